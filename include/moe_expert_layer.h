@@ -1,0 +1,210 @@
+/*
+ * moe_expert_layer.h - C ABI of an MI355X (gfx950) library for the forward pass of a
+ * Mixture-of-Experts expert layer on one GPU.
+ *
+ * The layer is the expert part of the EP-MC2 forward on the page "NPU Training Operators - MC2",
+ * section 执行路径 (execution path): count slots per expert (step 2), permute token rows into
+ * expert-contiguous order (step 6), grouped matmul with the gate/up weights (step 7), SwiGLU
+ * (step 8), grouped matmul with the down weights (step 9), and the probs-weighted unpermute
+ * (step 10), taken as one device's share with the cross-card All-to-All left out.  The operand set
+ * is mc2_fused_expert's on the page "MC2 通算融合" (hwcomputing.csdn.net), section 用法, without
+ * the communication group, in the order gate, up, down, plus the routing probabilities of step 10.
+ *
+ * Conventions for every entry point:
+ *   - Data pointers are DEVICE pointers unless a parameter says "host".  Shapes are row-major and
+ *     contiguous; "[A,B]" means A rows of B elements.
+ *   - Work is enqueued on `stream` (0 = the null stream) and the call returns without waiting
+ *     for it.  Buffers must stay alive, and must not be written by others, until that work ends.
+ *   - The caller allocates and frees all memory, including the workspace, whose size comes from the
+ *     matching *_workspace_size call.  The library never allocates device memory in these calls and
+ *     keeps no pointer after returning.  One workspace must not serve two calls in flight at once.
+ *   - Argument problems that the host can see (null pointers, bad sizes, unsupported dtype, a
+ *     workspace that is too small) return an error before anything is enqueued.  Problems only the
+ *     device can see (an expert id outside [0, E), a group expert outside [0, E)) are recorded in a
+ *     status word at the start of the workspace; moe_query_device_status reads it.  Such slots /
+ *     groups are skipped (they contribute nothing), like histc ignoring out-of-range values.
+ *   - No C++ exception crosses this interface.  moe_last_error() gives a thread-local message for the
+ *     last failing call on the calling thread.
+ *
+ * Storage formats (moe_problem.dtype):
+ *   MOE_F32         float32 x, weights, out; float32 intermediates.
+ *   MOE_BF16        bfloat16 x, weights, out; fp32 accumulation; the SwiGLU output h and the
+ *                   per-slot expert outputs are rounded to bfloat16 (round to nearest even).
+ *   MOE_MXFP8_E4M3  OCP-MX (Microscaling Formats v1.0): E4M3 element bytes with one E8M0 scale byte
+ *                   per 32 consecutive elements along the contraction axis; x_scale [T, H/32],
+ *                   wg_scale / wu_scale [E, H/32, F], wd_scale [E, F/32, H].  h is MX-encoded the same
+ *                   way along F before the down projection.  The output is bfloat16.  The MX format
+ *                   is the one named for the reference MC2 matmul on the page
+ *                   "MC2 通算融合架构总览", §1.
+ */
+#ifndef MOE_EXPERT_LAYER_H
+#define MOE_EXPERT_LAYER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARGUMENT = 1,       /* null pointer, non-positive size, k > E, ...            */
+    MOE_ERR_UNSUPPORTED = 2,            /* dtype or a size the kernels do not handle              */
+    MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+    MOE_ERR_EXPERT_ID_OUT_OF_RANGE = 4, /* device-side: some id was outside [0, E)                */
+    MOE_ERR_HIP = 5                     /* a HIP runtime call failed (message in moe_last_error)  */
+} moe_status;
+
+enum moe_dtype_code { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8_E4M3 = 2 };
+
+typedef struct moe_problem {
+    int64_t T;            /* tokens                                                              */
+    int64_t H;            /* hidden size                                                         */
+    int64_t F;            /* expert feed-forward size                                            */
+    int64_t E;            /* experts                                                             */
+    int64_t k;            /* experts per token (top-k), 1 <= k <= E                              */
+    int32_t dtype;        /* enum moe_dtype_code                                                 */
+    int32_t head_m_size;  /* 0: unchunked.  Otherwise the permuted rows are processed in chunks of
+                             this many rows (a multiple of 256), in chunk order, and each chunk's
+                             completion is counted in the workspace.  The M-axis split and its 512-row
+                             default are those of "MC2 通算融合架构总览", §6 切分策略; the result is
+                             bitwise identical to the unchunked one.                              */
+    uint32_t flags;       /* must be 0                                                           */
+    uint32_t reserved;    /* must be 0                                                           */
+} moe_problem;
+
+/* ---------------------------------------------------------------------------------------------
+ * Whole layer.
+ * ------------------------------------------------------------------------------------------- */
+
+/* Host only.  Workspace bytes needed by moe_expert_forward / moe_expert_forward_mx for `p`. */
+moe_status moe_workspace_size(const moe_problem* p, size_t* bytes /* host */);
+
+/* out[T,H] = sum_j probs[t,j] * FFN_{expert_ids[t,j]}(x[t]),
+ *   FFN_e(v) = (silu(v Wg[e]) * (v Wu[e])) Wd[e],   silu(z) = z / (1 + exp(-z)).
+ * dtype MOE_F32 or MOE_BF16 (x, weights and out in that dtype).
+ *   x          [T,H]           w_gate, w_up [E,H,F]        w_down [E,F,H]
+ *   expert_ids [T,k] int32     probs [T,k] float32         out [T,H]
+ * Steps (all on `stream`): route, permute, fc1 + SwiGLU, fc2, unpermute.  The k slots of a token
+ * are summed in j order with fp32 accumulation and one final rounding; no float atomics, so the
+ * output is deterministic. */
+moe_status moe_expert_forward(const moe_problem* p, const void* x, const void* w_gate,
+                              const void* w_up, const void* w_down, const int32_t* expert_ids,
+                              const float* probs, void* out, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/* The same layer on OCP-MX E4M3 inputs (dtype must be MOE_MXFP8_E4M3; H and F multiples of 128).
+ * Element bytes and scale bytes as described above; out is bfloat16 [T,H]. */
+moe_status moe_expert_forward_mx(const moe_problem* p, const uint8_t* x, const uint8_t* x_scale,
+                                 const uint8_t* w_gate, const uint8_t* wg_scale,
+                                 const uint8_t* w_up, const uint8_t* wu_scale,
+                                 const uint8_t* w_down, const uint8_t* wd_scale,
+                                 const int32_t* expert_ids, const float* probs, void* out_bf16,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Sub-steps (the same kernels the whole-layer calls use).
+ * ------------------------------------------------------------------------------------------- */
+
+/* Host only.  Workspace bytes for moe_route. */
+moe_status moe_route_workspace_size(int64_t T, int64_t k, int64_t E, size_t* bytes /* host */);
+
+/* Routing ("NPU Training Operators - MC2", 执行路径 step 2 and the index maps of steps 6 and 10).
+ * Slots are the flattened ids, s = t*k + j.
+ *   counts[E]    slots per expert (histc with E bins over [0, E); out-of-range ids not counted)
+ *   offsets[E+1] exclusive prefix sum of counts
+ *   perm[M]      permuted row p holds slot perm[p]; rows are grouped by ascending expert and,
+ *                inside an expert, by ascending slot (stable), M = T*k.  Entries past offsets[E]
+ *                (only when ids were out of range) are -1.
+ *   pos[M]       row of slot s (the inverse of perm), or -1 for an out-of-range id.
+ * Integer only; bit-exact and deterministic. */
+moe_status moe_route(const int32_t* expert_ids, int64_t T, int64_t k, int64_t E, int32_t* counts,
+                     int32_t* offsets, int32_t* perm, int32_t* pos, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/* Permute ("NPU Training Operators - MC2", 执行路径 step 6): x_perm[pos[s]] = x[s / k] for every
+ * slot with pos[s] >= 0.  Rows of p->H elements of p->dtype; for MOE_MXFP8_E4M3 the H/32 scale bytes
+ * of each row move with it (x_scale -> x_perm_scale; both NULL otherwise).  x_perm has T*k rows.
+ * A pure copy: bit-exact. */
+moe_status moe_permute(const moe_problem* p, const void* x, const uint8_t* x_scale,
+                       const int32_t* pos, void* x_perm, uint8_t* x_perm_scale, hipStream_t stream);
+
+/* Unpermute ("NPU Training Operators - MC2", 执行路径 step 10):
+ *   out[t] = sum_{j = 0..k-1, in order} probs[t,j] * y_perm[pos[t*k+j]]
+ * fp32 accumulation (fused multiply-add, starting from 0), one rounding to the output dtype; slots
+ * with pos < 0 are skipped.  y_perm [T*k, H] and out [T,H] are float32 for MOE_F32, bfloat16 for
+ * MOE_BF16 and MOE_MXFP8_E4M3. */
+moe_status moe_unpermute(const moe_problem* p, const void* y_perm, const int32_t* pos,
+                         const float* probs, void* out, hipStream_t stream);
+
+/* Host only.  Workspace bytes for moe_grouped_ffn / moe_grouped_ffn_mx with M rows in G groups. */
+moe_status moe_grouped_ffn_workspace_size(const moe_problem* p, int64_t M, int64_t G,
+                                          size_t* bytes /* host */);
+
+/* Grouped expert FFN on rows that are already grouped, as one expert-parallel rank receives them
+ * after the dispatch All-to-All ("NPU Training Operators - MC2", 执行路径 steps 5, 7-9): group g is
+ * rows [group_offsets[g], group_offsets[g+1]) and uses expert group_expert[g] (both device arrays,
+ * read only on the device, so the call never waits for the GPU).  Groups may be empty and several
+ * groups may share an expert.  y_rows[r] = FFN_{expert of r}(rows[r]); rows / y_rows are [M,H] in
+ * p->dtype (MOE_F32 or MOE_BF16).  p->T and p->k are ignored; p->E bounds group_expert. */
+moe_status moe_grouped_ffn(const moe_problem* p, const void* rows, int64_t M,
+                           const int32_t* group_offsets, const int32_t* group_expert, int64_t G,
+                           const void* w_gate, const void* w_up, const void* w_down, void* y_rows,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The same for OCP-MX rows (rows_scale [M, H/32]); y_rows is bfloat16 [M,H]. */
+moe_status moe_grouped_ffn_mx(const moe_problem* p, const uint8_t* rows, const uint8_t* rows_scale,
+                              int64_t M, const int32_t* group_offsets,
+                              const int32_t* group_expert, int64_t G, const uint8_t* w_gate,
+                              const uint8_t* wg_scale, const uint8_t* w_up,
+                              const uint8_t* wu_scale, const uint8_t* w_down,
+                              const uint8_t* wd_scale, void* y_rows, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/* OCP-MX encoder used on h inside the MX layer, exposed on its own: v [rows, cols] float32
+ * (cols a multiple of 32) -> codes [rows, cols] E4M3 bytes and scales [rows, cols/32] E8M0 bytes.
+ * Shared exponent floor(log2 max|block|) - 8 clamped to [-127, 127] (-127 for an all-zero block);
+ * elements v / 2^e rounded to nearest even on the E4M3 grid, saturated to +-448, sign kept.
+ * Integer arithmetic on the float32 bits: bit-exact and deterministic. */
+moe_status moe_mx_quantize(const float* v, int64_t rows, int64_t cols, uint8_t* codes,
+                           uint8_t* scales, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Status, errors, diagnostics.
+ * ------------------------------------------------------------------------------------------- */
+
+/* Waits for `stream`, then reads the device status word that the last call using `workspace`
+ * recorded (MOE_OK or MOE_ERR_EXPERT_ID_OUT_OF_RANGE) into *status (host). */
+moe_status moe_query_device_status(const void* workspace, hipStream_t stream,
+                                   int32_t* status /* host */);
+
+/* Per-chunk completion counters of the last chunked call using `workspace` (head_m_size > 0):
+ * after the call's work ends, counters (device, [num_chunks] int32, num_chunks = ceil(M /
+ * head_m_size)) hold the number of down-projection tiles finished in each chunk; tiles_per_chunk
+ * gives the expected totals.  Both are device pointers inside the workspace. */
+moe_status moe_chunk_counters(const moe_problem* p, void* workspace, size_t workspace_bytes,
+                              int64_t M, const int32_t** counters, const int32_t** tiles_per_chunk,
+                              int64_t* num_chunks /* host */);
+
+const char* moe_status_string(moe_status s);
+const char* moe_last_error(void);
+
+/* Kernel timing for profiling.  While enabled, every kernel the library enqueues is bracketed by
+ * two hipEvents recorded on the same stream.  moe_timing_collect waits for those events, adds
+ * each kernel's elapsed time to a per-name total, and copies up to `capacity` entries into the host
+ * arrays (name pointers stay valid for the life of the library).  Entries accumulate across calls
+ * until moe_timing_reset. */
+moe_status moe_timing_enable(int enable);
+moe_status moe_timing_collect(const char** names /* host */, double* total_ms /* host */,
+                              int64_t* launches /* host */, int capacity,
+                              int* count /* host */);
+moe_status moe_timing_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_EXPERT_LAYER_H */

@@ -1,0 +1,684 @@
+// C-ABI entry points of the MoE expert-layer library (declared in include/moe_expert_layer.h).
+// Host side only: argument checks, workspace carving, and the launch sequence on the caller's
+// stream.  Nothing here allocates device memory or waits for the GPU (except the explicitly
+// synchronous status / timing queries).
+#include "moe_expert_layer.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace moe {
+
+int bf16_fc1_cols_per_tile();
+int bf16_fc2_cols_per_tile();
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status s, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+moe_status hip_fail(hipError_t e, const char* what)
+{
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t elem_bytes(int dtype) { return dtype == MOE_F32 ? 4 : dtype == MOE_BF16 ? 2 : 1; }
+int64_t out_bytes(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
+
+int row_tile(int dtype) { return dtype == MOE_F32 ? kBmF32 : dtype == MOE_BF16 ? kBmBf16 : kBmMx; }
+
+// Column tiles of the down projection for the chunk counters (tasks per row tile).
+int fc2_col_tiles(int dtype, int64_t H)
+{
+    if (dtype == MOE_F32)
+        return static_cast<int>(ceil_div(H, 256));
+    return static_cast<int>(H / bf16_fc2_cols_per_tile());
+}
+
+// ------------------------------------------------------------------------------------- timing
+
+struct TimingRec {
+    const char* name;
+    hipEvent_t a, b;
+};
+
+struct Timing {
+    std::mutex mu;
+    bool enabled = false;
+    std::vector<TimingRec> pending;
+    std::vector<hipEvent_t> pool;
+    struct Total {
+        const char* name;   // a string literal of this file: valid for the life of the library
+        double ms;
+        int64_t n;
+    };
+    std::map<std::string, Total> totals;
+};
+
+Timing& timing()
+{
+    static Timing t;
+    return t;
+}
+
+hipEvent_t take_event(Timing& t)
+{
+    if (!t.pool.empty()) {
+        hipEvent_t e = t.pool.back();
+        t.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess)
+        return nullptr;
+    return e;
+}
+
+// Brackets one kernel launch with events when timing is enabled.
+class Timed {
+public:
+    Timed(hipStream_t s, const char* name) : s_(s), name_(name)
+    {
+        Timing& t = timing();
+        std::lock_guard<std::mutex> g(t.mu);
+        if (!t.enabled)
+            return;
+        a_ = take_event(t);
+        b_ = take_event(t);
+        if (a_ && b_)
+            hipEventRecord(a_, s_);
+    }
+    ~Timed()
+    {
+        if (!a_ || !b_)
+            return;
+        hipEventRecord(b_, s_);
+        Timing& t = timing();
+        std::lock_guard<std::mutex> g(t.mu);
+        t.pending.push_back({name_, a_, b_});
+    }
+
+private:
+    hipStream_t s_;
+    const char* name_;
+    hipEvent_t a_ = nullptr, b_ = nullptr;
+};
+
+#define LAUNCH(stream, name, call)                                   \
+    do {                                                             \
+        hipError_t err_;                                             \
+        {                                                            \
+            Timed timed_(stream, name);                              \
+            err_ = (call);                                           \
+        }                                                            \
+        if (err_ != hipSuccess)                                      \
+            return hip_fail(err_, name);                             \
+    } while (0)
+
+// ------------------------------------------------------------------------------------- checks
+
+moe_status check_problem(const moe_problem* p, bool need_tokens)
+{
+    if (p == nullptr)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "problem is null");
+    if (p->flags != 0 || p->reserved != 0)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "flags and reserved must be 0");
+    if (p->dtype != MOE_F32 && p->dtype != MOE_BF16 && p->dtype != MOE_MXFP8_E4M3)
+        return fail(MOE_ERR_UNSUPPORTED, "unknown dtype %d", p->dtype);
+    if (p->H <= 0 || p->F <= 0 || p->E <= 0)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "H, F and E must be positive");
+    if (p->E >= kMaxExperts)
+        return fail(MOE_ERR_UNSUPPORTED, "E = %lld exceeds %d", (long long)p->E, kMaxExperts - 1);
+    if (need_tokens) {
+        if (p->T < 0 || p->k <= 0)
+            return fail(MOE_ERR_INVALID_ARGUMENT, "T must be >= 0 and k >= 1");
+        if (p->k > p->E)
+            return fail(MOE_ERR_INVALID_ARGUMENT, "k = %lld exceeds E = %lld", (long long)p->k,
+                        (long long)p->E);
+        if (p->T * p->k > INT32_MAX)
+            return fail(MOE_ERR_UNSUPPORTED, "T * k exceeds int32 indexing");
+    }
+    if (p->head_m_size < 0 || p->head_m_size % kChunkAlign != 0)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "head_m_size must be 0 or a multiple of %d",
+                    kChunkAlign);
+    switch (p->dtype) {
+    case MOE_F32:
+        if (p->H % 4)
+            return fail(MOE_ERR_UNSUPPORTED, "float32 needs H %% 4 == 0");
+        break;
+    case MOE_BF16:
+        if (p->H % bf16_fc2_cols_per_tile() || p->F % 64 || p->F % bf16_fc1_cols_per_tile())
+            return fail(MOE_ERR_UNSUPPORTED, "bfloat16 needs H %% %d == 0 and F %% 64 == 0",
+                        bf16_fc2_cols_per_tile());
+        break;
+    default:
+        if (p->H % 128 || p->F % 128)
+            return fail(MOE_ERR_UNSUPPORTED, "MX needs H and F multiples of 128");
+        break;
+    }
+    if (p->H > INT32_MAX / 16 || p->F > INT32_MAX / 16)
+        return fail(MOE_ERR_UNSUPPORTED, "H or F too large");
+    return MOE_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------- layouts
+
+RouteLayout route_layout(int64_t T, int64_t k, int64_t E, size_t base)
+{
+    RouteLayout L;
+    L.status = 0;
+    L.nblocks = ceil_div(T * k, kRouteSlotsPerBlock);
+    size_t off = base == 0 ? kAlign : base;
+    L.block_counts = off;
+    off = align_up(off + sizeof(int32_t) * static_cast<size_t>(L.nblocks * (E + 1)));
+    L.total = off;
+    return L;
+}
+
+FfnLayout ffn_layout(int dtype, int64_t M, int64_t G, int64_t H, int64_t F, int64_t chunk,
+                     size_t base)
+{
+    (void)H;
+    FfnLayout L;
+    L.bm1 = L.bm2 = row_tile(dtype);
+    L.num_chunks = chunk > 0 ? std::max<int64_t>(1, ceil_div(M, chunk)) : 1;
+    L.max_tiles1 = max_mtiles(M, G, chunk, L.bm1);
+    L.max_tiles2 = max_mtiles(M, G, chunk, L.bm2);
+    size_t off = base;
+    L.status = 0;
+    if (base == 0)
+        off = kAlign;
+    L.tile_count = off;
+    off = align_up(off + 4 * sizeof(int32_t));
+    L.chunk_done = off;
+    off = align_up(off + sizeof(int32_t) * static_cast<size_t>(L.num_chunks));
+    L.chunk_tiles = off;
+    off = align_up(off + sizeof(int32_t) * static_cast<size_t>(L.num_chunks));
+    L.tiles1 = off;
+    off = align_up(off + sizeof(MTile) * static_cast<size_t>(L.max_tiles1));
+    L.tiles2 = L.tiles1;
+    if (L.bm2 != L.bm1) {
+        L.tiles2 = off;
+        off = align_up(off + sizeof(MTile) * static_cast<size_t>(L.max_tiles2));
+    }
+    L.h = off;
+    off = align_up(off + static_cast<size_t>(M * F * elem_bytes(dtype)));
+    L.h_scale = off;
+    if (dtype == MOE_MXFP8_E4M3)
+        off = align_up(off + static_cast<size_t>(M * (F / 32)));
+    L.total = off;
+    return L;
+}
+
+ForwardLayout forward_layout(int dtype, int64_t T, int64_t H, int64_t F, int64_t E, int64_t k,
+                             int64_t chunk)
+{
+    const int64_t M = T * k;
+    ForwardLayout L;
+    L.ffn = ffn_layout(dtype, M, E, H, F, chunk, 0);
+    size_t off = L.ffn.total;
+    L.route = route_layout(T, k, E, off);
+    off = L.route.total;
+    L.counts = off;
+    off = align_up(off + sizeof(int32_t) * static_cast<size_t>(E));
+    L.offsets = off;
+    off = align_up(off + sizeof(int32_t) * static_cast<size_t>(E + 1));
+    L.perm = off;
+    off = align_up(off + sizeof(int32_t) * static_cast<size_t>(M));
+    L.pos = off;
+    off = align_up(off + sizeof(int32_t) * static_cast<size_t>(M));
+    L.x_perm = off;
+    off = align_up(off + static_cast<size_t>(M * H * elem_bytes(dtype)));
+    L.x_perm_scale = off;
+    if (dtype == MOE_MXFP8_E4M3)
+        off = align_up(off + static_cast<size_t>(M * (H / 32)));
+    L.y_perm = off;
+    off = align_up(off + static_cast<size_t>(M * H * out_bytes(dtype)));
+    L.total = off;
+    return L;
+}
+
+const DeviceInfo& device_info()
+{
+    static std::mutex mu;
+    static std::map<int, DeviceInfo> cache;
+    int dev = 0;
+    hipGetDevice(&dev);
+    std::lock_guard<std::mutex> g(mu);
+    auto it = cache.find(dev);
+    if (it != cache.end())
+        return it->second;
+    DeviceInfo info{};
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cu <= 0)
+        cu = 256;
+    info.cu_count = (cu + 7) / 8 * 8;   // persistent grids are dealt evenly to the 8 XCDs
+    return cache.emplace(dev, info).first->second;
+}
+
+namespace {
+
+template <class T>
+T* at(void* ws, size_t off)
+{
+    return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// Route sub-sequence shared by moe_route and the forward.  Writes the status word at ws + 0.
+moe_status run_route(const int32_t* ids, int64_t T, int64_t k, int64_t E, int32_t* counts,
+                     int32_t* offsets, int32_t* perm, int32_t* pos, void* ws,
+                     const RouteLayout& L, hipStream_t s)
+{
+    const int64_t M = T * k;
+    int32_t* bc = at<int32_t>(ws, L.block_counts);
+    int32_t* status = at<int32_t>(ws, L.status);
+    if (M > 0)
+        LAUNCH(s, "route_count", launch_route_count(ids, M, E, bc, L.nblocks, s));
+    LAUNCH(s, "route_scan", launch_route_scan(bc, L.nblocks, E, M, counts, offsets, perm, status, s));
+    if (M > 0)
+        LAUNCH(s, "route_scatter", launch_route_scatter(ids, M, E, bc, L.nblocks, perm, pos, s));
+    return MOE_OK;
+}
+
+// fc1 + SwiGLU + fc2 over grouped rows; tiles are built from (offsets, group_expert).
+moe_status run_ffn(int dtype, const void* rows, const uint8_t* rows_scale, int64_t M,
+                   const int32_t* offsets, const int32_t* group_expert, int64_t G, int64_t E,
+                   int64_t H, int64_t F, int64_t head_m_size, const void* wg, const uint8_t* wgs,
+                   const void* wu, const uint8_t* wus, const void* wd, const uint8_t* wds,
+                   void* y, void* ws, const FfnLayout& L, bool write_status, hipStream_t s)
+{
+    (void)rows_scale; (void)wgs; (void)wus; (void)wds;
+    const int64_t chunk = head_m_size > 0 ? head_m_size : std::max<int64_t>(M, 1);
+    int32_t* status = at<int32_t>(ws, L.status);
+    int32_t* tcount = at<int32_t>(ws, L.tile_count);
+    MTile* tiles = at<MTile>(ws, L.tiles1);
+    int32_t* chunk_done = head_m_size > 0 ? at<int32_t>(ws, L.chunk_done) : nullptr;
+    int32_t* chunk_tiles = head_m_size > 0 ? at<int32_t>(ws, L.chunk_tiles) : nullptr;
+    LAUNCH(s, "build_tiles",
+           launch_build_tiles(offsets, group_expert, G, E, M, chunk, L.bm1, tiles, L.max_tiles1,
+                              tcount, chunk_tiles, chunk_done, L.num_chunks,
+                              fc2_col_tiles(dtype, H), status, write_status, s));
+    if (dtype == MOE_BF16) {
+        uint16_t* h = at<uint16_t>(ws, L.h);
+        LAUNCH(s, "fc1_bf16",
+               launch_fc1_bf16(static_cast<const uint16_t*>(rows), static_cast<const uint16_t*>(wg),
+                               static_cast<const uint16_t*>(wu), h, tiles, tcount, H, F, s));
+        LAUNCH(s, "fc2_bf16",
+               launch_fc2_bf16(h, static_cast<const uint16_t*>(wd), static_cast<uint16_t*>(y),
+                               tiles, tcount, H, F, chunk_done, s));
+    } else if (dtype == MOE_F32) {
+        float* h = at<float>(ws, L.h);
+        LAUNCH(s, "fc1_f32",
+               launch_fc1_f32(static_cast<const float*>(rows), static_cast<const float*>(wg),
+                              static_cast<const float*>(wu), h, tiles, tcount, H, F, s));
+        LAUNCH(s, "fc2_f32",
+               launch_fc2_f32(h, static_cast<const float*>(wd), static_cast<float*>(y), tiles,
+                              tcount, H, F, chunk_done, s));
+    } else {
+        return fail(MOE_ERR_UNSUPPORTED, "MX grouped GEMM is not available in this build");
+    }
+    return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+// ===================================================================================== C ABI
+
+MOE_API moe_status moe_workspace_size(const moe_problem* p, size_t* bytes)
+{
+    if (bytes == nullptr)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "bytes is null");
+    if (moe_status st = check_problem(p, true); st != MOE_OK)
+        return st;
+    *bytes = forward_layout(p->dtype, p->T, p->H, p->F, p->E, p->k, p->head_m_size).total;
+    return MOE_OK;
+}
+
+static moe_status forward_common(const moe_problem* p, const void* x, const uint8_t* x_scale,
+                                 const void* wg, const uint8_t* wgs, const void* wu,
+                                 const uint8_t* wus, const void* wd, const uint8_t* wds,
+                                 const int32_t* ids, const float* probs, void* out, void* ws,
+                                 size_t ws_bytes, hipStream_t s)
+{
+    const ForwardLayout L = forward_layout(p->dtype, p->T, p->H, p->F, p->E, p->k, p->head_m_size);
+    if (ws == nullptr || ws_bytes < L.total)
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", L.total,
+                    ws == nullptr ? size_t{0} : ws_bytes);
+    const int64_t T = p->T, k = p->k, M = T * k, H = p->H;
+    if (T > 0 && (x == nullptr || wg == nullptr || wu == nullptr || wd == nullptr ||
+                  ids == nullptr || probs == nullptr || out == nullptr))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "null data pointer");
+    int32_t* counts = at<int32_t>(ws, L.counts);
+    int32_t* offsets = at<int32_t>(ws, L.offsets);
+    int32_t* perm = at<int32_t>(ws, L.perm);
+    int32_t* pos = at<int32_t>(ws, L.pos);
+    if (moe_status st = run_route(ids, T, k, p->E, counts, offsets, perm, pos, ws, L.route, s);
+        st != MOE_OK)
+        return st;
+    if (M == 0)
+        return MOE_OK;
+    const int64_t eb = elem_bytes(p->dtype);
+    LAUNCH(s, "permute", launch_permute(x, pos, at<void>(ws, L.x_perm), T, k, M, H * eb, s));
+    if (p->dtype == MOE_MXFP8_E4M3)
+        LAUNCH(s, "permute_scale",
+               launch_permute(x_scale, pos, at<void>(ws, L.x_perm_scale), T, k, M, H / 32, s));
+    if (moe_status st = run_ffn(p->dtype, at<void>(ws, L.x_perm), at<uint8_t>(ws, L.x_perm_scale),
+                                M, offsets, nullptr, p->E, p->E, H, p->F, p->head_m_size, wg, wgs,
+                                wu, wus, wd, wds, at<void>(ws, L.y_perm), ws, L.ffn, false, s);
+        st != MOE_OK)
+        return st;
+    LAUNCH(s, "unpermute",
+           launch_unpermute(p->dtype == MOE_F32 ? 0 : 1, at<void>(ws, L.y_perm), pos, probs, out,
+                            T, k, M, H, s));
+    return MOE_OK;
+}
+
+MOE_API moe_status moe_expert_forward(const moe_problem* p, const void* x, const void* w_gate,
+                                      const void* w_up, const void* w_down,
+                                      const int32_t* expert_ids, const float* probs, void* out,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (moe_status st = check_problem(p, true); st != MOE_OK)
+        return st;
+    if (p->dtype == MOE_MXFP8_E4M3)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "MX inputs go through moe_expert_forward_mx");
+    return forward_common(p, x, nullptr, w_gate, nullptr, w_up, nullptr, w_down, nullptr,
+                          expert_ids, probs, out, workspace, workspace_bytes, stream);
+}
+
+MOE_API moe_status moe_expert_forward_mx(const moe_problem* p, const uint8_t* x,
+                                         const uint8_t* x_scale, const uint8_t* w_gate,
+                                         const uint8_t* wg_scale, const uint8_t* w_up,
+                                         const uint8_t* wu_scale, const uint8_t* w_down,
+                                         const uint8_t* wd_scale, const int32_t* expert_ids,
+                                         const float* probs, void* out_bf16, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream)
+{
+    if (moe_status st = check_problem(p, true); st != MOE_OK)
+        return st;
+    if (p->dtype != MOE_MXFP8_E4M3)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "moe_expert_forward_mx needs dtype MOE_MXFP8_E4M3");
+    if (p->T > 0 && (x_scale == nullptr || wg_scale == nullptr || wu_scale == nullptr ||
+                     wd_scale == nullptr))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "null scale pointer");
+    return forward_common(p, x, x_scale, w_gate, wg_scale, w_up, wu_scale, w_down, wd_scale,
+                          expert_ids, probs, out_bf16, workspace, workspace_bytes, stream);
+}
+
+MOE_API moe_status moe_route_workspace_size(int64_t T, int64_t k, int64_t E, size_t* bytes)
+{
+    if (bytes == nullptr || T < 0 || k <= 0 || E <= 0 || k > E)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "bad route sizes");
+    if (E >= kMaxExperts)
+        return fail(MOE_ERR_UNSUPPORTED, "E exceeds %d", kMaxExperts - 1);
+    *bytes = route_layout(T, k, E, 0).total;
+    return MOE_OK;
+}
+
+MOE_API moe_status moe_route(const int32_t* expert_ids, int64_t T, int64_t k, int64_t E,
+                             int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    size_t need = 0;
+    if (moe_status st = moe_route_workspace_size(T, k, E, &need); st != MOE_OK)
+        return st;
+    if (T * k > INT32_MAX)
+        return fail(MOE_ERR_UNSUPPORTED, "T * k exceeds int32 indexing");
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes", need);
+    if (counts == nullptr || offsets == nullptr ||
+        (T > 0 && (expert_ids == nullptr || perm == nullptr || pos == nullptr)))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+    return run_route(expert_ids, T, k, E, counts, offsets, perm, pos, workspace,
+                     route_layout(T, k, E, 0), stream);
+}
+
+MOE_API moe_status moe_permute(const moe_problem* p, const void* x, const uint8_t* x_scale,
+                               const int32_t* pos, void* x_perm, uint8_t* x_perm_scale,
+                               hipStream_t stream)
+{
+    if (moe_status st = check_problem(p, true); st != MOE_OK)
+        return st;
+    const int64_t M = p->T * p->k;
+    if (M == 0)
+        return MOE_OK;
+    if (x == nullptr || pos == nullptr || x_perm == nullptr)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+    const bool mx = p->dtype == MOE_MXFP8_E4M3;
+    if (mx && (x_scale == nullptr || x_perm_scale == nullptr))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "MX permute needs both scale pointers");
+    LAUNCH(stream, "permute",
+           launch_permute(x, pos, x_perm, p->T, p->k, M, p->H * elem_bytes(p->dtype), stream));
+    if (mx)
+        LAUNCH(stream, "permute_scale",
+               launch_permute(x_scale, pos, x_perm_scale, p->T, p->k, M, p->H / 32, stream));
+    return MOE_OK;
+}
+
+MOE_API moe_status moe_unpermute(const moe_problem* p, const void* y_perm, const int32_t* pos,
+                                 const float* probs, void* out, hipStream_t stream)
+{
+    if (moe_status st = check_problem(p, true); st != MOE_OK)
+        return st;
+    const int64_t M = p->T * p->k;
+    if (p->T == 0)
+        return MOE_OK;
+    if (y_perm == nullptr || pos == nullptr || probs == nullptr || out == nullptr)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+    LAUNCH(stream, "unpermute",
+           launch_unpermute(p->dtype == MOE_F32 ? 0 : 1, y_perm, pos, probs, out, p->T, p->k, M,
+                            p->H, stream));
+    return MOE_OK;
+}
+
+MOE_API moe_status moe_grouped_ffn_workspace_size(const moe_problem* p, int64_t M, int64_t G,
+                                                  size_t* bytes)
+{
+    if (bytes == nullptr || M < 0 || G <= 0 || M > INT32_MAX)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "bad grouped sizes");
+    if (moe_status st = check_problem(p, false); st != MOE_OK)
+        return st;
+    *bytes = ffn_layout(p->dtype, M, G, p->H, p->F, p->head_m_size, 0).total;
+    return MOE_OK;
+}
+
+static moe_status grouped_common(const moe_problem* p, const void* rows, const uint8_t* rows_scale,
+                                 int64_t M, const int32_t* group_offsets,
+                                 const int32_t* group_expert, int64_t G, const void* wg,
+                                 const uint8_t* wgs, const void* wu, const uint8_t* wus,
+                                 const void* wd, const uint8_t* wds, void* y, void* ws,
+                                 size_t ws_bytes, hipStream_t s)
+{
+    size_t need = 0;
+    if (moe_status st = moe_grouped_ffn_workspace_size(p, M, G, &need); st != MOE_OK)
+        return st;
+    if (ws == nullptr || ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes", need);
+    if (group_offsets == nullptr || group_expert == nullptr ||
+        (M > 0 && (rows == nullptr || wg == nullptr || wu == nullptr || wd == nullptr || y == nullptr)))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+    const FfnLayout L = ffn_layout(p->dtype, M, G, p->H, p->F, p->head_m_size, 0);
+    return run_ffn(p->dtype, rows, rows_scale, M, group_offsets, group_expert, G, p->E, p->H, p->F,
+                   p->head_m_size, wg, wgs, wu, wus, wd, wds, y, ws, L, true, s);
+}
+
+MOE_API moe_status moe_grouped_ffn(const moe_problem* p, const void* rows, int64_t M,
+                                   const int32_t* group_offsets, const int32_t* group_expert,
+                                   int64_t G, const void* w_gate, const void* w_up,
+                                   const void* w_down, void* y_rows, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream)
+{
+    if (p != nullptr && p->dtype == MOE_MXFP8_E4M3)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "MX rows go through moe_grouped_ffn_mx");
+    return grouped_common(p, rows, nullptr, M, group_offsets, group_expert, G, w_gate, nullptr,
+                          w_up, nullptr, w_down, nullptr, y_rows, workspace, workspace_bytes,
+                          stream);
+}
+
+MOE_API moe_status moe_grouped_ffn_mx(const moe_problem* p, const uint8_t* rows,
+                                      const uint8_t* rows_scale, int64_t M,
+                                      const int32_t* group_offsets, const int32_t* group_expert,
+                                      int64_t G, const uint8_t* w_gate, const uint8_t* wg_scale,
+                                      const uint8_t* w_up, const uint8_t* wu_scale,
+                                      const uint8_t* w_down, const uint8_t* wd_scale, void* y_rows,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (p == nullptr || p->dtype != MOE_MXFP8_E4M3)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "moe_grouped_ffn_mx needs dtype MOE_MXFP8_E4M3");
+    if (M > 0 && (rows_scale == nullptr || wg_scale == nullptr || wu_scale == nullptr ||
+                  wd_scale == nullptr))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "null scale pointer");
+    return grouped_common(p, rows, rows_scale, M, group_offsets, group_expert, G, w_gate, wg_scale,
+                          w_up, wu_scale, w_down, wd_scale, y_rows, workspace, workspace_bytes,
+                          stream);
+}
+
+MOE_API moe_status moe_mx_quantize(const float* v, int64_t rows, int64_t cols, uint8_t* codes,
+                                   uint8_t* scales, hipStream_t stream)
+{
+    if (rows < 0 || cols <= 0 || cols % 32 != 0 || rows * cols > (int64_t{1} << 40))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "cols must be a positive multiple of 32");
+    if (rows == 0)
+        return MOE_OK;
+    if (v == nullptr || codes == nullptr || scales == nullptr)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+    LAUNCH(stream, "mx_quantize", launch_mx_quantize(v, rows, cols, codes, scales, stream));
+    return MOE_OK;
+}
+
+MOE_API moe_status moe_query_device_status(const void* workspace, hipStream_t stream,
+                                           int32_t* status)
+{
+    if (workspace == nullptr || status == nullptr)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipStreamSynchronize");
+    e = hipMemcpy(status, workspace, sizeof(int32_t), hipMemcpyDeviceToHost);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipMemcpy");
+    return MOE_OK;
+}
+
+MOE_API moe_status moe_chunk_counters(const moe_problem* p, void* workspace,
+                                      size_t workspace_bytes, int64_t M,
+                                      const int32_t** counters, const int32_t** tiles_per_chunk,
+                                      int64_t* num_chunks)
+{
+    if (p == nullptr || workspace == nullptr || counters == nullptr || tiles_per_chunk == nullptr ||
+        num_chunks == nullptr || M < 0)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+    if (p->head_m_size <= 0)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "counters exist only in chunked mode");
+    // the counters sit at the start of both the forward and the grouped-FFN workspaces
+    const FfnLayout L = ffn_layout(p->dtype, M, 1, p->H, p->F, p->head_m_size, 0);
+    if (workspace_bytes < L.chunk_tiles + sizeof(int32_t) * static_cast<size_t>(L.num_chunks))
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+    *counters = at<const int32_t>(workspace, L.chunk_done);
+    *tiles_per_chunk = at<const int32_t>(workspace, L.chunk_tiles);
+    *num_chunks = L.num_chunks;
+    return MOE_OK;
+}
+
+MOE_API const char* moe_status_string(moe_status s)
+{
+    switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_EXPERT_ID_OUT_OF_RANGE: return "MOE_ERR_EXPERT_ID_OUT_OF_RANGE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    }
+    return "unknown moe_status";
+}
+
+MOE_API const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+MOE_API moe_status moe_timing_enable(int enable)
+{
+    Timing& t = timing();
+    std::lock_guard<std::mutex> g(t.mu);
+    t.enabled = enable != 0;
+    return MOE_OK;
+}
+
+MOE_API moe_status moe_timing_collect(const char** names, double* total_ms, int64_t* launches,
+                                      int capacity, int* count)
+{
+    Timing& t = timing();
+    std::lock_guard<std::mutex> g(t.mu);
+    for (TimingRec& r : t.pending) {
+        float ms = 0.0f;
+        hipError_t e = hipEventSynchronize(r.b);
+        if (e == hipSuccess)
+            e = hipEventElapsedTime(&ms, r.a, r.b);
+        if (e != hipSuccess)
+            return hip_fail(e, "timing events");
+        auto it = t.totals.find(r.name);
+        if (it == t.totals.end())
+            it = t.totals.emplace(r.name, Timing::Total{r.name, 0.0, 0}).first;
+        it->second.ms += ms;
+        it->second.n += 1;
+        t.pool.push_back(r.a);
+        t.pool.push_back(r.b);
+    }
+    t.pending.clear();
+    int n = 0;
+    for (auto& kv : t.totals) {
+        if (n < capacity) {
+            if (names)
+                names[n] = kv.second.name;
+            if (total_ms)
+                total_ms[n] = kv.second.ms;
+            if (launches)
+                launches[n] = kv.second.n;
+        }
+        ++n;
+    }
+    if (count)
+        *count = n;
+    return MOE_OK;
+}
+
+MOE_API moe_status moe_timing_reset(void)
+{
+    Timing& t = timing();
+    std::lock_guard<std::mutex> g(t.mu);
+    for (TimingRec& r : t.pending) {
+        hipEventSynchronize(r.b);
+        t.pool.push_back(r.a);
+        t.pool.push_back(r.b);
+    }
+    t.pending.clear();
+    t.totals.clear();
+    return MOE_OK;
+}

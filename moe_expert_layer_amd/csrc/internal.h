@@ -1,0 +1,143 @@
+// Host-side internals shared by the C-ABI layer (api.cpp) and the kernel launchers (*.hip).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// A tile of work for the grouped GEMMs: rows [row_begin, row_end) of the grouped activations all
+// use weights of `expert`; `chunk` is the M-axis chunk the rows belong to (0 when unchunked).
+struct MTile {
+    int expert;
+    int row_begin;
+    int row_end;
+    int chunk;
+};
+
+// ---------------------------------------------------------------------------------------------
+// Kernel configuration constants the host needs (tile shapes decide workspace sizes).
+// ---------------------------------------------------------------------------------------------
+constexpr int kRouteSlotsPerBlock = 2048;  // slots handled by one routing workgroup
+constexpr int kMaxExperts = 1024;          // routing LDS histograms are sized for this
+constexpr int kChunkAlign = 256;           // head_m_size must be a multiple of this
+constexpr size_t kAlign = 256;
+
+// Row-tile heights of the grouped GEMMs (the tile tables are built per height).
+constexpr int kBmBf16 = 128;
+constexpr int kBmF32 = 32;
+constexpr int kBmMx = 128;
+
+inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Upper bound on the number of row tiles for M rows in G groups, chunks of `chunk` rows
+// (chunk == 0: one chunk) and tile height bm: each group adds at most one partial tile and each
+// chunk boundary splits at most one more tile.
+inline int64_t max_mtiles(int64_t M, int64_t G, int64_t chunk, int bm)
+{
+    int64_t chunks = chunk > 0 ? ceil_div(M, chunk) : 1;
+    return ceil_div(M, bm) + G + chunks + 1;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Workspace layout.  Byte offsets from the workspace base; the status word is always at 0.
+// ---------------------------------------------------------------------------------------------
+struct RouteLayout {
+    size_t status = 0;        // int32 status word (+ padding)
+    size_t block_counts = 0;  // int32 [nblocks, E + 1]: per-block expert counts, last = invalid ids
+    size_t total = 0;
+    int64_t nblocks = 0;
+};
+
+struct FfnLayout {
+    size_t status = 0;
+    size_t tiles1 = 0, tiles2 = 0;     // MTile tables for fc1 / fc2 row-tile heights
+    size_t tile_count = 0;             // int32 [4]: fc1 tiles, fc2 tiles
+    size_t chunk_done = 0;             // int32 [num_chunks]: fc2 tiles finished per chunk
+    size_t chunk_tiles = 0;            // int32 [num_chunks]: fc2 tiles per chunk
+    size_t h = 0, h_scale = 0;         // SwiGLU output [M, F] (+ MX scales [M, F/32])
+    size_t total = 0;
+    int64_t max_tiles1 = 0, max_tiles2 = 0, num_chunks = 0;
+    int bm1 = 0, bm2 = 0;
+};
+
+struct ForwardLayout {
+    RouteLayout route;                 // offsets relative to the workspace base
+    FfnLayout ffn;                     // offsets relative to the workspace base
+    size_t counts = 0, offsets = 0, perm = 0, pos = 0;
+    size_t x_perm = 0, x_perm_scale = 0, y_perm = 0;
+    size_t total = 0;
+};
+
+RouteLayout route_layout(int64_t T, int64_t k, int64_t E, size_t base);
+FfnLayout ffn_layout(int dtype, int64_t M, int64_t G, int64_t H, int64_t F, int64_t chunk,
+                     size_t base);
+ForwardLayout forward_layout(int dtype, int64_t T, int64_t H, int64_t F, int64_t E, int64_t k,
+                             int64_t chunk);
+
+// ---------------------------------------------------------------------------------------------
+// Launchers (defined in the .hip files).  Each returns the hipError_t of its launch.
+// ---------------------------------------------------------------------------------------------
+struct DeviceInfo {
+    int cu_count;
+};
+const DeviceInfo& device_info();       // for the current device (cached)
+
+// route.hip
+hipError_t launch_route_count(const int32_t* ids, int64_t M, int64_t E, int32_t* block_counts,
+                              int64_t nblocks, hipStream_t s);
+hipError_t launch_route_scan(int32_t* block_counts, int64_t nblocks, int64_t E, int64_t M,
+                             int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* status,
+                             hipStream_t s);
+hipError_t launch_route_scatter(const int32_t* ids, int64_t M, int64_t E,
+                                const int32_t* block_counts, int64_t nblocks, int32_t* perm,
+                                int32_t* pos, hipStream_t s);
+// Builds the row-tile table: groups are rows [offsets[g], offsets[g+1]) (clamped into [0, M]) with expert
+// group_expert[g] (identity when null).  Writes tiles and *tile_count; when chunk_tiles is not
+// null also the expected (row tile x column tile) tasks per chunk (row tiles * col_tiles) and
+// zeroes chunk_done.  A non-empty group with an expert outside [0, E) is skipped and sets
+// *status; with write_status the status word is written either way.
+hipError_t launch_build_tiles(const int32_t* offsets, const int32_t* group_expert, int64_t G,
+                              int64_t E, int64_t M, int64_t chunk, int bm, MTile* tiles, int64_t max_tiles,
+                              int32_t* tile_count, int32_t* chunk_tiles, int32_t* chunk_done,
+                              int64_t num_chunks, int col_tiles, int32_t* status,
+                              bool write_status, hipStream_t s);
+
+// permute.hip
+// Slots whose pos is outside [0, M) are skipped.
+hipError_t launch_permute(const void* x, const int32_t* pos, void* x_perm, int64_t T, int64_t k,
+                          int64_t M, int64_t row_bytes, hipStream_t s);
+hipError_t launch_unpermute(int dtype, const void* y_perm, const int32_t* pos, const float* probs,
+                            void* out, int64_t T, int64_t k, int64_t M, int64_t H, hipStream_t s);
+
+// gemm_bf16.hip: grouped GEMMs on bf16 MFMA.  fc1: h = swiglu(A Wg, A Wu); fc2: y = h Wd.
+hipError_t launch_fc1_bf16(const uint16_t* A, const uint16_t* wg, const uint16_t* wu, uint16_t* h,
+                           const MTile* tiles, const int32_t* tile_count, int64_t H, int64_t F,
+                           hipStream_t s);
+hipError_t launch_fc2_bf16(const uint16_t* h, const uint16_t* wd, uint16_t* y, const MTile* tiles,
+                           const int32_t* tile_count, int64_t H, int64_t F, int32_t* chunk_done,
+                           hipStream_t s);
+
+// gemm_f32.hip: float32 grouped GEMMs (plain FMA).
+hipError_t launch_fc1_f32(const float* A, const float* wg, const float* wu, float* h,
+                          const MTile* tiles, const int32_t* tile_count, int64_t H, int64_t F,
+                          hipStream_t s);
+hipError_t launch_fc2_f32(const float* h, const float* wd, float* y, const MTile* tiles,
+                          const int32_t* tile_count, int64_t H, int64_t F, int32_t* chunk_done,
+                          hipStream_t s);
+
+// gemm_mx.hip: OCP-MX grouped GEMMs on scaled fp8 MFMA.
+hipError_t launch_fc1_mx(const uint8_t* A, const uint8_t* a_scale, const uint8_t* wg,
+                         const uint8_t* wg_scale, const uint8_t* wu, const uint8_t* wu_scale,
+                         uint8_t* h, uint8_t* h_scale, const MTile* tiles,
+                         const int32_t* tile_count, int64_t H, int64_t F, hipStream_t s);
+hipError_t launch_fc2_mx(const uint8_t* h, const uint8_t* h_scale, const uint8_t* wd,
+                         const uint8_t* wd_scale, uint16_t* y, const MTile* tiles,
+                         const int32_t* tile_count, int64_t H, int64_t F, int32_t* chunk_done,
+                         hipStream_t s);
+hipError_t launch_mx_quantize(const float* v, int64_t rows, int64_t cols, uint8_t* codes,
+                              uint8_t* scales, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,143 @@
+// Permute and unpermute for the MoE expert layer on gfx950 (HBM-bound data movement).
+//
+// permute   ("NPU Training Operators - MC2", 执行路径 step 6): x_perm[pos[s]] = x[s / k].
+//           Written as a scatter over tokens: each token row is read once and stored to its k
+//           permuted rows, so HBM traffic is exactly (1 + k) row transfers per token.
+// unpermute (step 10): out[t] = sum_j probs[t, j] * y_perm[pos[t*k + j]], j ascending, fp32
+//           fused multiply-add from 0 and one rounding; a gather, so no atomics and a
+//           deterministic result.
+// Both move 16-byte vectors; one workgroup walks whole rows so every access is coalesced.
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename V>
+__global__ __launch_bounds__(kThreads) void permute_kernel(const V* __restrict__ x,
+                                                           const int32_t* __restrict__ pos,
+                                                           V* __restrict__ x_perm, int64_t T,
+                                                           int k, int64_t M, int64_t row_vecs)
+{
+    for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+        const V* src = x + t * row_vecs;
+        const int32_t* tp = pos + t * k;
+        for (int64_t c = threadIdx.x; c < row_vecs; c += kThreads) {
+            const V v = src[c];
+            for (int j = 0; j < k; ++j) {
+                const int64_t p = tp[j];
+                if (p >= 0 && p < M)
+                    x_perm[p * row_vecs + c] = v;
+            }
+        }
+    }
+}
+
+// bfloat16 rows: 8 values per 16-byte vector.
+__global__ __launch_bounds__(kThreads) void unpermute_bf16_kernel(
+    const uint4* __restrict__ y, const int32_t* __restrict__ pos, const float* __restrict__ probs,
+    uint4* __restrict__ out, int64_t T, int k, int64_t M, int64_t row_vecs)
+{
+    for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+        const int32_t* tp = pos + t * k;
+        const float* pp = probs + t * k;
+        for (int64_t c = threadIdx.x; c < row_vecs; c += kThreads) {
+            float acc[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc[i] = 0.0f;
+            for (int j = 0; j < k; ++j) {
+                const int64_t p = tp[j];
+                if (p < 0 || p >= M)
+                    continue;
+                const float w = pp[j];
+                const uint4 v = y[p * row_vecs + c];
+                const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[2 * i] = fmaf(w, __uint_as_float(d[i] << 16), acc[2 * i]);
+                    acc[2 * i + 1] = fmaf(w, __uint_as_float(d[i] & 0xffff0000u), acc[2 * i + 1]);
+                }
+            }
+            uint4 o;
+            o.x = pack_bf16x2(acc[0], acc[1]);
+            o.y = pack_bf16x2(acc[2], acc[3]);
+            o.z = pack_bf16x2(acc[4], acc[5]);
+            o.w = pack_bf16x2(acc[6], acc[7]);
+            out[t * row_vecs + c] = o;
+        }
+    }
+}
+
+// float32 rows: 4 values per 16-byte vector.
+__global__ __launch_bounds__(kThreads) void unpermute_f32_kernel(
+    const float4* __restrict__ y, const int32_t* __restrict__ pos, const float* __restrict__ probs,
+    float4* __restrict__ out, int64_t T, int k, int64_t M, int64_t row_vecs)
+{
+    for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+        const int32_t* tp = pos + t * k;
+        const float* pp = probs + t * k;
+        for (int64_t c = threadIdx.x; c < row_vecs; c += kThreads) {
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int j = 0; j < k; ++j) {
+                const int64_t p = tp[j];
+                if (p < 0 || p >= M)
+                    continue;
+                const float w = pp[j];
+                const float4 v = y[p * row_vecs + c];
+                acc.x = fmaf(w, v.x, acc.x);
+                acc.y = fmaf(w, v.y, acc.y);
+                acc.z = fmaf(w, v.z, acc.z);
+                acc.w = fmaf(w, v.w, acc.w);
+            }
+            out[t * row_vecs + c] = acc;
+        }
+    }
+}
+
+unsigned grid_for_rows(int64_t rows)
+{
+    const int64_t cap = static_cast<int64_t>(device_info().cu_count) * 16;
+    return static_cast<unsigned>(rows < cap ? (rows > 0 ? rows : 1) : cap);
+}
+
+}  // namespace
+
+hipError_t launch_permute(const void* x, const int32_t* pos, void* x_perm, int64_t T, int64_t k,
+                          int64_t M, int64_t row_bytes, hipStream_t s)
+{
+    const dim3 grid(grid_for_rows(T)), block(kThreads);
+    if (row_bytes % 16 == 0)
+        permute_kernel<uint4><<<grid, block, 0, s>>>(static_cast<const uint4*>(x), pos,
+                                                      static_cast<uint4*>(x_perm), T,
+                                                      static_cast<int>(k), M, row_bytes / 16);
+    else if (row_bytes % 4 == 0)
+        permute_kernel<uint32_t><<<grid, block, 0, s>>>(static_cast<const uint32_t*>(x), pos,
+                                                          static_cast<uint32_t*>(x_perm), T,
+                                                          static_cast<int>(k), M, row_bytes / 4);
+    else
+        permute_kernel<uint8_t><<<grid, block, 0, s>>>(static_cast<const uint8_t*>(x), pos,
+                                                        static_cast<uint8_t*>(x_perm), T,
+                                                        static_cast<int>(k), M, row_bytes);
+    return hipGetLastError();
+}
+
+// dtype: 0 float32 rows (H % 4 == 0), otherwise bfloat16 rows (H % 8 == 0).
+hipError_t launch_unpermute(int dtype, const void* y_perm, const int32_t* pos, const float* probs,
+                            void* out, int64_t T, int64_t k, int64_t M, int64_t H, hipStream_t s)
+{
+    const dim3 grid(grid_for_rows(T)), block(kThreads);
+    if (dtype == 0)
+        unpermute_f32_kernel<<<grid, block, 0, s>>>(static_cast<const float4*>(y_perm), pos, probs,
+                                                     static_cast<float4*>(out), T,
+                                                     static_cast<int>(k), M, H / 4);
+    else
+        unpermute_bf16_kernel<<<grid, block, 0, s>>>(static_cast<const uint4*>(y_perm), pos,
+                                                      probs, static_cast<uint4*>(out), T,
+                                                      static_cast<int>(k), M, H / 8);
+    return hipGetLastError();
+}
+
+}  // namespace moe

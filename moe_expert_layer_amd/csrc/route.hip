@@ -1,0 +1,280 @@
+// Routing for the MoE expert layer on gfx950: per-expert counts, offsets, and the stable slot
+// permutation, plus the row-tile table the grouped GEMMs consume.
+//
+// The counting step is histc over the flattened expert ids with E bins on [0, E) ("NPU Training
+// Operators - MC2", 执行路径 step 2); ids outside [0, E) are left out of every bin, as histc does,
+// and flagged in the status word (section 迁移检查 requires ids in [0, E)).  The permutation orders
+// slots s = t*k + j by expert and, inside an expert, by s: the row layout permute (step 6) writes
+// and unpermute (step 10) reads back.
+//
+// Three launches, all integer and deterministic:
+//   count   one workgroup per 2048 slots: LDS histogram -> block_counts[b][e]
+//   scan    one workgroup: per expert, prefix over blocks; exclusive scan over experts -> offsets;
+//           block_counts becomes each block's first row per expert
+//   scatter one workgroup per 2048 slots, in rounds of 256 slots: a slot's rank among same-expert
+//           slots of its wave comes from ballots over the id bits; waves are ordered through LDS.
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kScanThreads = 1024;
+constexpr int kStatusOk = 0;
+constexpr int kStatusBadId = 4;   // MOE_ERR_EXPERT_ID_OUT_OF_RANGE
+
+__global__ __launch_bounds__(kThreads) void route_count_kernel(const int32_t* __restrict__ ids,
+                                                               int64_t M, int E,
+                                                               int32_t* __restrict__ block_counts)
+{
+    __shared__ int hist[kMaxExperts + 1];
+    for (int i = threadIdx.x; i <= E; i += kThreads)
+        hist[i] = 0;
+    __syncthreads();
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kRouteSlotsPerBlock;
+    for (int i = threadIdx.x; i < kRouteSlotsPerBlock; i += kThreads) {
+        const int64_t s = base + i;
+        if (s < M) {
+            const int id = ids[s];
+            atomicAdd(&hist[(id >= 0 && id < E) ? id : E], 1);
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i <= E; i += kThreads)
+        block_counts[static_cast<int64_t>(blockIdx.x) * (E + 1) + i] = hist[i];
+}
+
+// Inclusive scan of one value per thread over a 1024-thread workgroup (Hillis-Steele in LDS).
+__device__ int block_inclusive_scan(int v, int* buf /* [2][kScanThreads] */)
+{
+    int pin = 0;
+    buf[threadIdx.x] = v;
+    __syncthreads();
+    for (int off = 1; off < kScanThreads; off <<= 1) {
+        int x = buf[pin * kScanThreads + threadIdx.x];
+        if (threadIdx.x >= off)
+            x += buf[pin * kScanThreads + threadIdx.x - off];
+        buf[(1 - pin) * kScanThreads + threadIdx.x] = x;
+        __syncthreads();
+        pin ^= 1;
+    }
+    return buf[pin * kScanThreads + threadIdx.x];
+}
+
+__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
+    int32_t* __restrict__ block_counts, int nblocks, int E, int64_t M, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ status)
+{
+    __shared__ int buf[2 * kScanThreads];
+    __shared__ int total_valid;
+    const int e = threadIdx.x;           // E <= kMaxExperts == kScanThreads
+    int tot = 0;
+    if (e <= E) {
+        for (int b = 0; b < nblocks; ++b) {
+            int32_t* c = block_counts + static_cast<int64_t>(b) * (E + 1) + e;
+            const int v = *c;
+            *c = tot;
+            tot += v;
+        }
+    }
+    const int v = e < E ? tot : 0;
+    const int incl = block_inclusive_scan(v, buf);
+    const int excl = incl - v;
+    if (e < E) {
+        counts[e] = tot;
+        offsets[e] = excl;
+        for (int b = 0; b < nblocks; ++b)
+            block_counts[static_cast<int64_t>(b) * (E + 1) + e] += excl;
+    }
+    if (e == E - 1) {
+        offsets[E] = incl;
+        total_valid = incl;
+    }
+    if (e == E)
+        *status = tot > 0 ? kStatusBadId : kStatusOk;
+    __syncthreads();
+    // rows that no valid slot fills (only when some ids were out of range)
+    for (int64_t p = total_valid + threadIdx.x; p < M; p += kScanThreads)
+        perm[p] = -1;
+}
+
+__global__ __launch_bounds__(kThreads) void route_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t M, int E, int id_bits,
+    const int32_t* __restrict__ block_base, int32_t* __restrict__ perm, int32_t* __restrict__ pos)
+{
+    constexpr int kWaves = kThreads / 64;
+    __shared__ int running[kMaxExperts];
+    __shared__ int wave_cnt[kWaves][kMaxExperts];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    for (int e = threadIdx.x; e < E; e += kThreads) {
+        running[e] = block_base[static_cast<int64_t>(blockIdx.x) * (E + 1) + e];
+        for (int w = 0; w < kWaves; ++w)
+            wave_cnt[w][e] = 0;
+    }
+    __syncthreads();
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kRouteSlotsPerBlock;
+    for (int round = 0; round < kRouteSlotsPerBlock / kThreads; ++round) {
+        const int64_t s = base + round * kThreads + threadIdx.x;
+        const bool in_range = s < M;
+        const int id = in_range ? ids[s] : -1;
+        const bool ok = in_range && id >= 0 && id < E;
+        // peers: the lanes of this wave holding a valid slot with the same expert id
+        uint64_t peers = __ballot(ok);
+        for (int bit = 0; bit < id_bits; ++bit) {
+            const bool b = (id >> bit) & 1;
+            const uint64_t m = __ballot(b);
+            peers &= b ? m : ~m;
+        }
+        const int rank = __popcll(peers & lt_mask);
+        const int cnt = __popcll(peers);
+        if (ok && rank == cnt - 1)
+            wave_cnt[wave][id] = cnt;
+        __syncthreads();
+        if (ok) {
+            int p = running[id] + rank;
+            for (int w = 0; w < wave; ++w)
+                p += wave_cnt[w][id];
+            perm[p] = static_cast<int32_t>(s);
+            pos[s] = p;
+        } else if (in_range) {
+            pos[s] = -1;
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < E; e += kThreads) {
+            int add = 0;
+            for (int w = 0; w < kWaves; ++w) {
+                add += wave_cnt[w][e];
+                wave_cnt[w][e] = 0;
+            }
+            running[e] += add;
+        }
+        __syncthreads();
+    }
+}
+
+// Row-tile table.  Group g covers rows [offsets[g], offsets[g+1]) with expert group_expert[g]
+// (g itself when group_expert is null).  Each group is cut at chunk boundaries (multiples of
+// `chunk` rows) and each piece into tiles of at most bm rows.  Tiles are written in row order, so
+// the table is chunk-major.  One workgroup; groups are handled 1024 at a time.
+__global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ group_expert, int G, int E,
+    int64_t M, int64_t chunk, int bm, MTile* __restrict__ tiles, int max_tiles, int32_t* __restrict__ tile_count,
+    int32_t* __restrict__ chunk_tiles, int32_t* __restrict__ chunk_done, int num_chunks,
+    int col_tiles, int32_t* __restrict__ status, int write_status)
+{
+    __shared__ int buf[2 * kScanThreads];
+    __shared__ int carry;
+    __shared__ int bad;
+    if (threadIdx.x == 0) {
+        carry = 0;
+        bad = 0;
+    }
+    if (chunk_tiles != nullptr)
+        for (int c = threadIdx.x; c < num_chunks; c += kScanThreads) {
+            chunk_tiles[c] = 0;
+            chunk_done[c] = 0;
+        }
+    __syncthreads();
+    for (int g0 = 0; g0 < G; g0 += kScanThreads) {
+        const int g = g0 + threadIdx.x;
+        int64_t rb = 0, re = 0;
+        int ex = 0, n = 0;
+        if (g < G) {
+            // clamp into [0, M] so that malformed offsets can never address rows outside the buffers
+            rb = min(max(static_cast<int64_t>(offsets[g]), int64_t{0}), M);
+            re = min(max(static_cast<int64_t>(offsets[g + 1]), rb), M);
+            ex = group_expert ? group_expert[g] : g;
+            if (ex < 0 || ex >= E) {
+                if (re > rb)
+                    atomicOr(&bad, 1);
+                re = rb;   // skipped
+            }
+            for (int64_t r = rb; r < re;) {
+                const int64_t cend = min(re, (r / chunk + 1) * chunk);
+                n += static_cast<int>((cend - r + bm - 1) / bm);
+                r = cend;
+            }
+        }
+        const int incl = block_inclusive_scan(n, buf);
+        int t = carry + incl - n;
+        for (int64_t r = rb; r < re;) {
+            const int64_t cend = min(re, (r / chunk + 1) * chunk);
+            for (int64_t r0 = r; r0 < cend; r0 += bm) {
+                const int c = static_cast<int>(r0 / chunk);
+                if (t < max_tiles) {
+                    MTile mt;
+                    mt.expert = ex;
+                    mt.row_begin = static_cast<int>(r0);
+                    mt.row_end = static_cast<int>(min(cend, r0 + bm));
+                    mt.chunk = c;
+                    tiles[t] = mt;
+                }
+                if (chunk_tiles != nullptr && c < num_chunks)
+                    atomicAdd(&chunk_tiles[c], col_tiles);
+                ++t;
+            }
+            r = cend;
+        }
+        __syncthreads();
+        if (threadIdx.x == kScanThreads - 1)
+            carry += incl;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        tile_count[0] = min(carry, max_tiles);
+        if (write_status)
+            *status = bad ? kStatusBadId : kStatusOk;
+        else if (bad)
+            *status = kStatusBadId;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_route_count(const int32_t* ids, int64_t M, int64_t E, int32_t* block_counts,
+                              int64_t nblocks, hipStream_t s)
+{
+    route_count_kernel<<<dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, s>>>(
+        ids, M, static_cast<int>(E), block_counts);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_scan(int32_t* block_counts, int64_t nblocks, int64_t E, int64_t M,
+                             int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* status,
+                             hipStream_t s)
+{
+    route_scan_kernel<<<dim3(1), dim3(kScanThreads), 0, s>>>(
+        block_counts, static_cast<int>(nblocks), static_cast<int>(E), M, counts, offsets, perm,
+        status);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_scatter(const int32_t* ids, int64_t M, int64_t E,
+                                const int32_t* block_counts, int64_t nblocks, int32_t* perm,
+                                int32_t* pos, hipStream_t s)
+{
+    int bits = 0;
+    while ((int64_t{1} << bits) < E)
+        ++bits;
+    route_scatter_kernel<<<dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, s>>>(
+        ids, M, static_cast<int>(E), bits, block_counts, perm, pos);
+    return hipGetLastError();
+}
+
+hipError_t launch_build_tiles(const int32_t* offsets, const int32_t* group_expert, int64_t G,
+                              int64_t E, int64_t M, int64_t chunk, int bm, MTile* tiles, int64_t max_tiles,
+                              int32_t* tile_count, int32_t* chunk_tiles, int32_t* chunk_done,
+                              int64_t num_chunks, int col_tiles, int32_t* status,
+                              bool write_status, hipStream_t s)
+{
+    build_tiles_kernel<<<dim3(1), dim3(kScanThreads), 0, s>>>(
+        offsets, group_expert, static_cast<int>(G), static_cast<int>(E), M, chunk, bm, tiles,
+        static_cast<int>(max_tiles), tile_count, chunk_tiles, chunk_done,
+        static_cast<int>(num_chunks), col_tiles, status, write_status ? 1 : 0);
+    return hipGetLastError();
+}
+
+}  // namespace moe

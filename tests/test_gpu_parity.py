@@ -1,0 +1,274 @@
+"""GPU parity of the HIP path against the CPU oracle at sizes the oracle finishes in seconds.
+
+Every call goes through the C ABI (via the ctypes binding).  Bars: integer work (counts, offsets,
+perm, pos, permute bytes) bit-exact; float outputs within max|gpu - oracle| / max|oracle|
+<= 2e-2 for bfloat16 and 1e-5 for float32 (see the tolerance derivation in the design notes).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import devinputs as dv
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+mel = pytest.importorskip("moe_expert_layer_amd")
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "mxfp8": 6e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mel.library()
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------------------------------ route
+
+@pytest.mark.parametrize("T,k,E,seed", [(64, 2, 4, 0), (4096, 2, 8, 1), (8192, 8, 128, 2),
+                                         (16384, 4, 32, 3), (1, 1, 1, 4), (3000, 3, 1000, 5),
+                                         (2049, 1, 2, 6), (0, 2, 4, 7)])
+def test_route_bit_exact(T, k, E, seed):
+    rng = np.random.default_rng(seed)
+    ids = (np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32) if T
+           else np.zeros((0, k), np.int32))
+    counts, offsets, perm, pos, ws = mel.route(dv.tensor(ids), E)
+    oc, oo, op, opos = oracle.route(ids, E)
+    assert np.array_equal(dv.host(counts), oc)
+    assert np.array_equal(dv.host(offsets), oo)
+    assert np.array_equal(dv.host(perm), op)
+    assert np.array_equal(dv.host(pos), opos)
+    assert mel.device_status(ws) == 0
+
+
+def test_route_workload_routing_bit_exact():
+    for name in ("finegrained_bf16", "mxfp8"):
+        cfg = synth.WORKLOADS[name]
+        inp = synth.make_layer(T=cfg["T"], H=32, F=32, E=cfg["E"], k=cfg["k"], dtype="f32",
+                               routing=cfg["routing"],
+                               **{kk: cfg[kk] for kk in ("zipf_s", "n_zero") if kk in cfg})
+        counts, offsets, perm, pos, _ = mel.route(dv.tensor(inp.expert_ids), cfg["E"])
+        oc, oo, op, opos = oracle.route(inp.expert_ids, cfg["E"])
+        assert np.array_equal(dv.host(counts), oc) and np.array_equal(dv.host(offsets), oo)
+        assert np.array_equal(dv.host(perm), op) and np.array_equal(dv.host(pos), opos)
+
+
+def test_route_out_of_range_ids_flagged_and_dropped():
+    rng = np.random.default_rng(9)
+    T, k, E = 700, 2, 6
+    ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    bad = rng.choice(T * k, 25, replace=False)
+    ids.ravel()[bad[:10]] = E + 3
+    ids.ravel()[bad[10:]] = -1
+    counts, offsets, perm, pos, ws = mel.route(dv.tensor(ids), E)
+    assert mel.device_status(ws) == 4            # MOE_ERR_EXPERT_ID_OUT_OF_RANGE
+    flat = ids.ravel()
+    ok = (flat >= 0) & (flat < E)
+    assert np.array_equal(dv.host(counts), np.bincount(flat[ok], minlength=E))
+    valid_slots = np.flatnonzero(ok)
+    order = valid_slots[np.argsort(flat[ok], kind="stable")]
+    p = dv.host(perm)
+    assert np.array_equal(p[:ok.sum()], order)
+    assert np.all(p[ok.sum():] == -1)
+    ps = dv.host(pos)
+    assert np.all(ps[~ok] == -1)
+    assert np.array_equal(ps[order], np.arange(ok.sum()))
+
+
+# ------------------------------------------------------------------------------------------ permute / unpermute
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "mxfp8"])
+def test_permute_bit_exact(dtype):
+    inp = synth.make_layer(T=300, H=256, F=128, E=7, k=3, dtype=dtype)
+    _, _, perm, pos = oracle.route(inp.expert_ids, 7)
+    d = dv.layer(inp)
+    pos_d = dv.tensor(pos)
+    if dtype == "mxfp8":
+        xp, xsp = mel.permute(d.x, pos_d, 3, x_scale=d.x_scale)
+        assert np.array_equal(dv.host(xsp), oracle.permute(inp.x_scale, perm, 3))
+    else:
+        xp = mel.permute(d.x, pos_d, 3)
+    ref = oracle.permute(inp.x, perm, 3)
+    got = xp.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bf16" else dv.host(xp)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("dtype,k", [("bf16", 1), ("bf16", 2), ("bf16", 4), ("bf16", 8),
+                                     ("f32", 1), ("f32", 2)])
+def test_permute_unpermute_identity(dtype, k):
+    """With the expert step replaced by the identity, unpermute(permute(x)) with probs 1/k gives x
+    back bit for bit, and unit probs give k*x (power-of-two scalings and short exact sums)."""
+    T, H, E = 257, 128, 8
+    inp = synth.make_layer(T=T, H=H, F=64, E=E, k=k, dtype=dtype)
+    d = dv.layer(inp)
+    _, _, _, pos, _ = mel.route(d.expert_ids, E)
+    xp = mel.permute(d.x, pos, k)
+    x = dv.host(d.x)
+    probs = torch.full((T, k), 1.0 / k, dtype=torch.float32, device="cuda")
+    assert np.array_equal(dv.host(mel.unpermute(xp, pos, probs)), x)
+    if k in (2, 4, 8) or (dtype == "f32" and k == 2):
+        ones = torch.ones((T, k), dtype=torch.float32, device="cuda")
+        assert np.array_equal(dv.host(mel.unpermute(xp, pos, ones)), np.float32(k) * x)
+
+
+def test_unpermute_weighted_sum_matches_definition():
+    rng = np.random.default_rng(4)
+    T, k, H = 123, 4, 256
+    y = rng.standard_normal((T * k, H)).astype(np.float32)
+    perm = rng.permutation(T * k).astype(np.int32)
+    pos = np.empty_like(perm)
+    pos[perm] = np.arange(T * k, dtype=np.int32)
+    probs = rng.random((T, k)).astype(np.float32)
+    out = dv.host(mel.unpermute(dv.tensor(y), dv.tensor(pos), dv.tensor(probs)))
+    ref = np.zeros((T, H))
+    for j in range(k):
+        ref += probs[:, j:j + 1].astype(np.float64) * y[pos.reshape(T, k)[:, j]]
+    assert oracle.inf_norm_rel(out, ref) < 1e-6
+
+
+# ------------------------------------------------------------------------------------------ whole layer
+
+CASES = [
+    # name, dtype, T, H, F, E, k, routing kwargs
+    ("tiny_f32_full_shape", "f32", 64, 128, 256, 4, 2, {}),
+    ("f32_ragged", "f32", 75, 96, 160, 5, 2, {}),
+    ("bf16_mixtral_like", "bf16", 384, 256, 448, 8, 2, {}),
+    ("bf16_ragged_tail", "bf16", 333, 384, 192, 6, 2, {}),
+    ("bf16_finegrained_like", "bf16", 256, 256, 128, 32, 8,
+     {"routing": "zipf_gumbel", "zipf_s": 1.1, "n_zero": 4}),
+]
+
+
+@pytest.mark.parametrize("name,dtype,T,H,F,E,k,kw", CASES, ids=[c[0] for c in CASES])
+def test_forward_matches_oracle(name, dtype, T, H, F, E, k, kw):
+    inp = synth.make_layer(T=T, H=H, F=F, E=E, k=k, dtype=dtype, **kw)
+    ref, *_ = oracle.forward(inp)
+    d = dv.layer(inp)
+    out = dv.host(dv.forward(mel, d))
+    err = oracle.inf_norm_rel(out, ref)
+    print(f"{name}: inf-norm rel err {err:.3e}")
+    assert err <= TOL[dtype]
+    # determinism: a second call gives the same bits
+    out2 = dv.host(dv.forward(mel, d))
+    assert np.array_equal(out, out2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("head", [256, 512])
+def test_chunked_equals_unchunked(dtype, head):
+    inp = synth.make_layer(T=700, H=128, F=192, E=5, k=2, dtype=dtype, seed=3)
+    d = dv.layer(inp)
+    base = dv.host(dv.forward(mel, d, 0))
+    ws = torch.empty(mel.workspace_size(mel.problem(700, 128, 192, 5, 2,
+                                                    mel.F32 if dtype == "f32" else mel.BF16,
+                                                    head)), dtype=torch.uint8, device="cuda")
+    out = dv.host(dv.forward(mel, d, head, workspace=ws))
+    assert np.array_equal(out, base)
+    done, expected = mel.chunk_counters(ws, 1400, 128, 192, head,
+                                        mel.F32 if dtype == "f32" else mel.BF16)
+    torch.cuda.synchronize()
+    assert done.shape[0] == -(-1400 // head)
+    assert np.array_equal(dv.host(done), dv.host(expected)) and dv.host(expected).min() > 0
+
+
+def test_invariances_bitwise():
+    inp = synth.make_layer(T=200, H=128, F=128, E=6, k=2, dtype="bf16", seed=8)
+    d = dv.layer(inp)
+    base = dv.host(dv.forward(mel, d))
+    rng = np.random.default_rng(1)
+    tp = rng.permutation(200)
+    tpi = torch.from_numpy(tp).cuda()
+    d2 = dv.layer(inp)
+    d2.x, d2.expert_ids, d2.probs = (d.x[tpi].contiguous(), d.expert_ids[tpi].contiguous(),
+                                     d.probs[tpi].contiguous())
+    assert np.array_equal(dv.host(dv.forward(mel, d2)), base[tp])
+    rel = rng.permutation(6)
+    inv = torch.from_numpy(np.argsort(rel)).cuda()
+    d3 = dv.layer(inp)
+    d3.w_gate, d3.w_up, d3.w_down = d.w_gate[inv].contiguous(), d.w_up[inv].contiguous(), d.w_down[inv].contiguous()
+    d3.expert_ids = torch.from_numpy(rel.astype(np.int32)).cuda()[d.expert_ids.long()].contiguous()
+    assert np.array_equal(dv.host(dv.forward(mel, d3)), base)
+    d4 = dv.layer(inp)
+    d4.probs = d.probs * 2
+    out4 = dv.host(dv.forward(mel, d4))
+    # bf16 output: doubling is exact unless the doubled value leaves bf16's range (it cannot here)
+    assert np.array_equal(out4, 2 * base)
+
+
+def test_empty_and_degenerate():
+    # T = 0: nothing to do, call succeeds
+    inp = synth.make_layer(T=0, H=128, F=64, E=4, k=2, dtype="bf16")
+    d = dv.layer(inp)
+    out = dv.forward(mel, d)
+    assert out.shape == (0, 128)
+    # every token to one expert (the other experts empty), k = 1, E = 1
+    for E, k in ((3, 1), (1, 1)):
+        inp = synth.make_layer(T=130, H=128, F=64, E=E, k=k, dtype="bf16", seed=2)
+        inp.expert_ids[:] = E - 1
+        ref, *_ = oracle.forward(inp)
+        out = dv.host(dv.forward(mel, dv.layer(inp)))
+        assert oracle.inf_norm_rel(out, ref) <= TOL["bf16"]
+
+
+def test_forward_out_of_range_ids_flagged():
+    inp = synth.make_layer(T=100, H=128, F=64, E=4, k=2, dtype="bf16")
+    inp.expert_ids[5, 1] = 9
+    d = dv.layer(inp)
+    ws = torch.empty(mel.workspace_size(mel.problem(100, 128, 64, 4, 2, mel.BF16)),
+                     dtype=torch.uint8, device="cuda")
+    out = dv.host(dv.forward(mel, d, workspace=ws))
+    assert mel.device_status(ws) == 4
+    # the dropped slot contributes nothing: token 5 gets only its first expert's share
+    good = inp.expert_ids.copy()
+    good[5, 1] = 0
+    inp2 = synth.make_layer(T=100, H=128, F=64, E=4, k=2, dtype="bf16")
+    inp2.expert_ids = good
+    inp2.probs = inp.probs.copy()
+    inp2.probs[5, 1] = 0.0
+    ref, *_ = oracle.forward(inp2)
+    assert oracle.inf_norm_rel(out, ref) <= TOL["bf16"]
+
+
+def test_grouped_ffn_matches_oracle():
+    g = synth.make_grouped(rows=900, H=256, F=192, E_local=2, sources=8, zipf_s=1.2, seed=2)
+    ref = oracle.grouped_ffn(g)
+    y = mel.grouped_ffn(dv.tensor(g.rows), dv.tensor(g.group_offsets), dv.tensor(g.group_expert),
+                        dv.tensor(g.w_gate), dv.tensor(g.w_up), dv.tensor(g.w_down))
+    assert oracle.inf_norm_rel(dv.host(y), ref) <= TOL["bf16"]
+    y2 = mel.grouped_ffn(dv.tensor(g.rows), dv.tensor(g.group_offsets), dv.tensor(g.group_expert),
+                         dv.tensor(g.w_gate), dv.tensor(g.w_up), dv.tensor(g.w_down),
+                         head_m_size=256)
+    assert torch.equal(y, y2)
+
+
+def test_grouped_ffn_bad_group_expert_flagged():
+    g = synth.make_grouped(rows=300, H=128, F=64, E_local=2, sources=8, seed=3)
+    ge = g.group_expert.copy()
+    ge[3] = 7
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device="cuda")
+    mel.grouped_ffn(dv.tensor(g.rows), dv.tensor(g.group_offsets), dv.tensor(ge),
+                    dv.tensor(g.w_gate), dv.tensor(g.w_up), dv.tensor(g.w_down), workspace=ws)
+    assert mel.device_status(ws) == 4
+
+
+def test_mx_quantize_bit_exact():
+    rng = np.random.default_rng(12)
+    v = (rng.standard_normal((64, 256)) * np.exp2(rng.integers(-30, 30, (64, 1)))).astype(np.float32)
+    v[0] = 0.0
+    v[1, :32] = 1e-41                                   # float32 subnormals
+    vals = np.array([oracle.e4m3_value(c) for c in range(127)])
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)
+    v[2, :126] = np.resize(mids, 126)                    # ties, with a 448 anchor per block
+    v[2, ::32] = 448.0
+    v[3, :4] = [460.0, 464.0, 465.0, -0.0]
+    v[3, 4] = 448.0
+    codes, scales = mel.mx_quantize(dv.tensor(v))
+    q, s = oracle.mx_quantize(v.astype(np.float64))
+    assert np.array_equal(dv.host(scales), s)
+    assert np.array_equal(dv.host(codes), q)
