@@ -1,0 +1,221 @@
+"""Benchmark of the MoE expert-layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral_bf16]
+
+A step is one whole forward (route -> permute -> fc1 + SwiGLU -> fc2 -> unpermute) over one batch
+of seeded synthetic inputs already resident in HBM.  Before every timed step a 1 GiB buffer is
+overwritten so that neither the L2s nor the 256 MiB Infinity Cache hold operands of the previous
+step (the profiling rule of the page "MC2 通算融合架构总览", §8: flush L2 before every timed round).
+Each step is bracketed by HIP events on the stream the library launches on; the flush is outside
+the brackets.  A second pass of the same steps records every kernel of the library between events
+(moe_timing_*), which gives each kernel's average duration for the roofline figures.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": 2500.0, "mxfp8": 5000.0, "f32": 157.3}     # dense TFLOP/s, MI355X published
+HBM_PEAK_GBS = 8000.0
+METRIC = "MoE layer fwd tokens/s + grouped-GEMM % MFMA peak, Mixtral-shaped E=8 top-2"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def gemm_flops(M, H, F):
+    """Algorithmic FLOPs of the routed rows: fc1 gate + up (2 * 2MHF) and fc2 (2MHF)."""
+    return {"fc1": 4.0 * M * H * F, "fc2": 2.0 * M * H * F}
+
+
+def byte_model(inp, M):
+    """Algorithmic HBM bytes of the data-movement kernels (each row moved once per use)."""
+    T, H, k = inp.T, inp.H, inp.k
+    if inp.dtype == "mxfp8":
+        row = H + H // 32
+        return {"permute": (1 + k) * T * H + 4 * M, "permute_scale": (1 + k) * T * (H // 32),
+                "unpermute": k * T * H * 2 + T * H * 2 + 8 * M}
+    b = 4 if inp.dtype == "f32" else 2
+    return {"permute": (1 + k) * T * H * b + 4 * M, "unpermute": (k * T * H * b + T * H * b + 8 * M)}
+
+
+def cpu_baseline(inp, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of the same workload's tokens: the sample
+    doubles until one run takes at least half the budget (or covers every token)."""
+    import oracle
+    rng = np.random.default_rng(123)
+    order = rng.permutation(inp.T).astype(np.int32)
+    n = 8
+    while True:
+        t0 = time.perf_counter()
+        oracle.forward_tokens(inp, order[:n])
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 2 or n >= inp.T:
+            break
+        n = min(inp.T, max(2 * n, int(n * budget_s / 2 / max(dt, 1e-3))))
+    return {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} of {inp.T} tokens through the per-token definition (all k experts of each, "
+                      f"weights decoded per call), {dt:.1f} s, fp64"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_bf16")
+    ap.add_argument("--head-m-size", type=int, default=None,
+                    help="chunk rows for the reported mode (default: unchunked)")
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-chunked", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_expert_layer_amd as mel
+    import synth
+    from synth import device as dv
+
+    if not os.path.exists(mel.lib_path):
+        from moe_expert_layer_amd.build import build
+        build()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+
+    cfg = synth.WORKLOADS[args.workload]
+    if cfg["kind"] != "layer":
+        print("bench.py times whole-layer workloads", file=sys.stderr)
+        sys.exit(2)
+    log(f"generating {args.workload} inputs")
+    t0 = time.perf_counter()
+    inp = synth.make_workload(args.workload)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s; uploading")
+    d = dv.layer(inp, dev)
+    T, H, F, E, k = inp.T, inp.H, inp.F, inp.E, inp.k
+    M = T * k
+    head = args.head_m_size if args.head_m_size is not None else 0
+    code = {"f32": mel.F32, "bf16": mel.BF16, "mxfp8": mel.MXFP8}[inp.dtype]
+    ws = torch.empty(mel.workspace_size(mel.problem(T, H, F, E, k, code, max(head, 512))),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((T, H), dtype=torch.float32 if inp.dtype == "f32" else torch.bfloat16,
+                      device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def step(h):
+        if inp.dtype == "mxfp8":
+            mel.expert_forward_mx(d.x, d.x_scale, d.w_gate, d.wg_scale, d.w_up, d.wu_scale,
+                                  d.w_down, d.wd_scale, d.expert_ids, d.probs, head_m_size=h,
+                                  out=out, workspace=ws)
+        else:
+            mel.expert_forward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs,
+                               head_m_size=h, out=out, workspace=ws)
+
+    def timed(h, steps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        for a, b in ev:
+            if not args.no_flush:
+                flush.fill_(1)
+            a.record()
+            step(h)
+            b.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        return np.array([a.elapsed_time(b) for a, b in ev]), wall
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step(head)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps (head_m_size={head})")
+    ms, wall = timed(head, args.steps)
+    ms_per_step = float(ms.mean())
+    log(f"ms/step mean {ms_per_step:.3f} median {np.median(ms):.3f} p10 {np.percentile(ms, 10):.3f} "
+        f"p90 {np.percentile(ms, 90):.3f}")
+
+    # per-kernel durations, same steps, events around every kernel the library launches
+    mel.timing_reset()
+    mel.timing_enable(True)
+    for _ in range(args.steps):
+        if not args.no_flush:
+            flush.fill_(1)
+        step(head)
+    kern = mel.timing_collect()
+    mel.timing_enable(False)
+    kavg = {n: tot / cnt for n, (tot, cnt) in kern.items()}
+    log("kernel avg ms: " + ", ".join(f"{n}={v:.4f}" for n, v in sorted(kavg.items())))
+
+    fl = gemm_flops(M, H, F)
+    suffix = {"f32": "f32", "bf16": "bf16", "mxfp8": "mx"}[inp.dtype]
+    fc1_ms, fc2_ms = kavg.get(f"fc1_{suffix}", float("nan")), kavg.get(f"fc2_{suffix}", float("nan"))
+    gemm_tflops = (fl["fc1"] + fl["fc2"]) / ((fc1_ms + fc2_ms) * 1e-3) / 1e12
+    peak = PEAK[inp.dtype]
+    bytes_ = byte_model(inp, M)
+    dominant = max(kavg, key=kavg.get)
+    dom_flops = fl.get(dominant.split("_")[0]) if dominant.startswith("fc") else None
+    if dom_flops is not None:
+        achieved = dom_flops / (kavg[dominant] * 1e-3) / 1e12
+        roof = {"kernel": dominant, "bound": "mfma", "achieved": achieved, "peak": peak,
+                "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                "per_launch": f"{dom_flops:.4g} FLOP = 2*M*H*F per projection, M={M} routed rows"}
+    else:
+        gbs = bytes_[dominant] / (kavg[dominant] * 1e-3) / 1e9
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None}
+    hbm = {n: {"GB/s": bytes_[n] / (kavg[n] * 1e-3) / 1e9,
+               "frac": bytes_[n] / (kavg[n] * 1e-3) / 1e9 / HBM_PEAK_GBS}
+           for n in bytes_ if n in kavg}
+
+    result = {
+        "metric": METRIC, "value": T / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": inp.dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "T": T, "H": H, "F": F, "E": E, "k": k,
+                   "head_m_size": head, "routed_rows": M, "flush_bytes": 0 if args.no_flush else 1 << 30},
+        "gemm": {"tflops": gemm_tflops, "frac_of_peak": gemm_tflops / peak, "peak_tflops": peak,
+                 "fc1_ms": fc1_ms, "fc2_ms": fc2_ms},
+        "kernels_ms": kavg, "hbm": hbm, "roofline": roof,
+        "timing": {"median_ms": float(np.median(ms)), "p10_ms": float(np.percentile(ms, 10)),
+                   "p90_ms": float(np.percentile(ms, 90)),
+                   "wall_ms_per_step_incl_flush": wall * 1e3 / args.steps},
+    }
+
+    if not args.skip_chunked:
+        for _ in range(2):
+            step(512)
+        cms, _ = timed(512, args.steps)
+        result["chunked"] = {"head_m_size": 512, "ms_per_step": float(cms.mean()),
+                             "tokens_per_s": T / (float(cms.mean()) * 1e-3),
+                             "overhead_vs_unchunked": float(cms.mean()) / ms_per_step - 1.0}
+        log(f"chunked(512) ms/step {cms.mean():.3f}")
+
+    if not args.skip_cpu_baseline:
+        log(f"cpu baseline (~{args.cpu_seconds:.0f} s of oracle work)")
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        log(f"cpu baseline {result['cpu_baseline']['value']:.2f} tokens/s on "
+            f"{result['cpu_baseline']['cores']} threads")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

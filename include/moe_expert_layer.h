@@ -189,6 +189,13 @@ moe_status moe_chunk_counters(const moe_problem* p, void* workspace, size_t work
                               int64_t M, const int32_t** counters, const int32_t** tiles_per_chunk,
                               int64_t* num_chunks /* host */);
 
+/* Host only.  Byte offsets, inside the workspace of moe_grouped_ffn / moe_grouped_ffn_mx (M rows in G
+ * groups) or of moe_expert_forward / _mx (M = T*k, G = E), of the intermediate SwiGLU output h
+ * [M, F] (p->dtype elements; E4M3 bytes for MX) and, for MX, of its E8M0 scales [M, F/32].  After
+ * the call's work ends they hold that call's h, for inspection. */
+moe_status moe_intermediate_offsets(const moe_problem* p, int64_t M, int64_t G,
+                                    size_t* h_offset /* host */, size_t* h_scale_offset /* host */);
+
 const char* moe_status_string(moe_status s);
 const char* moe_last_error(void);
 

@@ -18,6 +18,7 @@ __all__ = [
     "MoeError", "library", "lib_path", "F32", "BF16", "MXFP8",
     "workspace_size", "expert_forward", "expert_forward_mx", "route", "permute", "unpermute",
     "grouped_ffn", "grouped_ffn_mx", "mx_quantize", "device_status", "chunk_counters",
+    "intermediate_h",
     "timing_enable", "timing_collect", "timing_reset",
 ]
 
@@ -48,7 +49,7 @@ class MoeError(RuntimeError):
 _SIGS = {
     "moe_workspace_size": [ctypes.POINTER(MoeProblem), ctypes.POINTER(ctypes.c_size_t)],
     "moe_expert_forward": [ctypes.POINTER(MoeProblem)] + [_P] * 8 + [ctypes.c_size_t, _P],
-    "moe_expert_forward_mx": [ctypes.POINTER(MoeProblem)] + [_P] * 13 + [ctypes.c_size_t, _P],
+    "moe_expert_forward_mx": [ctypes.POINTER(MoeProblem)] + [_P] * 12 + [ctypes.c_size_t, _P],
     "moe_route_workspace_size": [_I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
     "moe_route": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_permute": [ctypes.POINTER(MoeProblem), _P, _P, _P, _P, _P, _P],
@@ -63,6 +64,8 @@ _SIGS = {
     "moe_query_device_status": [_P, _P, ctypes.POINTER(ctypes.c_int32)],
     "moe_chunk_counters": [ctypes.POINTER(MoeProblem), _P, ctypes.c_size_t, _I64,
                            ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_I64)],
+    "moe_intermediate_offsets": [ctypes.POINTER(MoeProblem), _I64, _I64,
+                                 ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)],
     "moe_status_string": [ctypes.c_int],
     "moe_last_error": [],
     "moe_timing_enable": [ctypes.c_int],
@@ -332,6 +335,21 @@ def chunk_counters(workspace, M: int, H: int, F: int, head_m_size: int, dtype: i
     oc, ot = c.value - base, t.value - base
     nb = 4 * n.value
     return (workspace[oc:oc + nb].view(torch.int32), workspace[ot:ot + nb].view(torch.int32))
+
+
+def intermediate_h(workspace, M: int, G: int, H: int, F: int, E: int, dtype: int,
+                   head_m_size: int = 0):
+    """Views into `workspace` of the SwiGLU output h [M, F] (and MX scales [M, F/32], else None)
+    left there by the last grouped-FFN or forward call that used it."""
+    prob = problem(0, H, F, E, 1, dtype, head_m_size)
+    ho, so = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(library().moe_intermediate_offsets(ctypes.byref(prob), M, G, ctypes.byref(ho),
+                                              ctypes.byref(so)))
+    esz = {F32: 4, BF16: 2, MXFP8: 1}[dtype]
+    h = workspace[ho.value:ho.value + M * F * esz]
+    if dtype == MXFP8:
+        return h.view(M, F), workspace[so.value:so.value + M * (F // 32)].view(M, F // 32)
+    return h.view(torch.float32 if dtype == F32 else torch.bfloat16).view(M, F), None
 
 
 def timing_enable(on: bool = True):

@@ -23,6 +23,7 @@ namespace moe {
 
 int bf16_fc1_cols_per_tile();
 int bf16_fc2_cols_per_tile();
+int mx_fc2_cols_per_tile();
 
 namespace {
 
@@ -54,6 +55,8 @@ int fc2_col_tiles(int dtype, int64_t H)
 {
     if (dtype == MOE_F32)
         return static_cast<int>(ceil_div(H, 256));
+    if (dtype == MOE_MXFP8_E4M3)
+        return static_cast<int>(H / mx_fc2_cols_per_tile());
     return static_cast<int>(H / bf16_fc2_cols_per_tile());
 }
 
@@ -159,6 +162,8 @@ moe_status check_problem(const moe_problem* p, bool need_tokens)
                         (long long)p->E);
         if (p->T * p->k > INT32_MAX)
             return fail(MOE_ERR_UNSUPPORTED, "T * k exceeds int32 indexing");
+        if (p->dtype == MOE_MXFP8_E4M3 && p->T * p->k * std::max(p->H, p->F) > UINT32_MAX)
+            return fail(MOE_ERR_UNSUPPORTED, "MX needs T * k * max(H, F) < 2^32");
     }
     if (p->head_m_size < 0 || p->head_m_size % kChunkAlign != 0)
         return fail(MOE_ERR_INVALID_ARGUMENT, "head_m_size must be 0 or a multiple of %d",
@@ -312,7 +317,6 @@ moe_status run_ffn(int dtype, const void* rows, const uint8_t* rows_scale, int64
                    const void* wu, const uint8_t* wus, const void* wd, const uint8_t* wds,
                    void* y, void* ws, const FfnLayout& L, bool write_status, hipStream_t s)
 {
-    (void)rows_scale; (void)wgs; (void)wus; (void)wds;
     const int64_t chunk = head_m_size > 0 ? head_m_size : std::max<int64_t>(M, 1);
     int32_t* status = at<int32_t>(ws, L.status);
     int32_t* tcount = at<int32_t>(ws, L.tile_count);
@@ -340,7 +344,15 @@ moe_status run_ffn(int dtype, const void* rows, const uint8_t* rows_scale, int64
                launch_fc2_f32(h, static_cast<const float*>(wd), static_cast<float*>(y), tiles,
                               tcount, H, F, chunk_done, s));
     } else {
-        return fail(MOE_ERR_UNSUPPORTED, "MX grouped GEMM is not available in this build");
+        uint8_t* h = at<uint8_t>(ws, L.h);
+        uint8_t* hs = at<uint8_t>(ws, L.h_scale);
+        LAUNCH(s, "fc1_mx",
+               launch_fc1_mx(static_cast<const uint8_t*>(rows), rows_scale,
+                             static_cast<const uint8_t*>(wg), wgs, static_cast<const uint8_t*>(wu),
+                             wus, h, hs, tiles, tcount, H, F, s));
+        LAUNCH(s, "fc2_mx",
+               launch_fc2_mx(h, hs, static_cast<const uint8_t*>(wd), wds, static_cast<uint16_t*>(y),
+                             tiles, tcount, H, F, chunk_done, s));
     }
     return MOE_OK;
 }
@@ -506,6 +518,8 @@ MOE_API moe_status moe_grouped_ffn_workspace_size(const moe_problem* p, int64_t 
         return fail(MOE_ERR_INVALID_ARGUMENT, "bad grouped sizes");
     if (moe_status st = check_problem(p, false); st != MOE_OK)
         return st;
+    if (p->dtype == MOE_MXFP8_E4M3 && M * std::max(p->H, p->F) > UINT32_MAX)
+        return fail(MOE_ERR_UNSUPPORTED, "MX needs M * max(H, F) < 2^32");
     *bytes = ffn_layout(p->dtype, M, G, p->H, p->F, p->head_m_size, 0).total;
     return MOE_OK;
 }
@@ -605,6 +619,20 @@ MOE_API moe_status moe_chunk_counters(const moe_problem* p, void* workspace,
     *counters = at<const int32_t>(workspace, L.chunk_done);
     *tiles_per_chunk = at<const int32_t>(workspace, L.chunk_tiles);
     *num_chunks = L.num_chunks;
+    return MOE_OK;
+}
+
+MOE_API moe_status moe_intermediate_offsets(const moe_problem* p, int64_t M, int64_t G,
+                                            size_t* h_offset, size_t* h_scale_offset)
+{
+    if (h_offset == nullptr || h_scale_offset == nullptr || M < 0 || G <= 0)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "bad arguments");
+    if (moe_status st = check_problem(p, false); st != MOE_OK)
+        return st;
+    // the FFN block (and with it h) starts at the workspace base in both layouts
+    const FfnLayout L = ffn_layout(p->dtype, M, G, p->H, p->F, p->head_m_size, 0);
+    *h_offset = L.h;
+    *h_scale_offset = L.h_scale;
     return MOE_OK;
 }
 

@@ -195,11 +195,16 @@ def grouped_ffn(g, row_index=None) -> np.ndarray:
     offs = np.asarray(g.group_offsets, np.int64)
     row_expert = np.repeat(np.asarray(g.group_expert, np.int32), np.diff(offs))
     rows = g.rows
+    rows_scale = getattr(g, "rows_scale", None)
     if row_index is not None:
         row_index = np.asarray(row_index, np.int64)
         rows = rows[row_index]
         row_expert = row_expert[row_index]
-    return ffn_rows(g.dtype, rows, row_expert, g.w_gate, g.w_up, g.w_down)
+        if rows_scale is not None:
+            rows_scale = rows_scale[row_index]
+    return ffn_rows(g.dtype, rows, row_expert, g.w_gate, g.w_up, g.w_down, rows_scale=rows_scale,
+                    wg_scale=getattr(g, "wg_scale", None), wu_scale=getattr(g, "wu_scale", None),
+                    wd_scale=getattr(g, "wd_scale", None))
 
 
 def forward(inp, chunk: int = 0):

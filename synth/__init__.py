@@ -143,6 +143,10 @@ class GroupedInputs:
     w_gate: np.ndarray
     w_up: np.ndarray
     w_down: np.ndarray
+    rows_scale: np.ndarray | None = None   # mxfp8: [M, H/32]
+    wg_scale: np.ndarray | None = None
+    wu_scale: np.ndarray | None = None
+    wd_scale: np.ndarray | None = None
     meta: dict = field(default_factory=dict)
 
 
@@ -201,18 +205,23 @@ def make_layer(T: int, H: int, F: int, E: int, k: int, dtype: str = "bf16",
     ids, probs = _route(st[0], T, E, k, routing, **routing_kw)
     x, xs = _store(_normal_f32(st[1], (T, H), x_std), dtype, 1)
 
+    u8 = dtype == "mxfp8"
+    edt = {"f32": np.float32, "bf16": np.uint16, "mxfp8": np.uint8}[dtype]
+    mats = [np.empty((E, H, F), edt), np.empty((E, H, F), edt), np.empty((E, F, H), edt)]
+    scl = ([np.empty((E, H // 32, F), np.uint8), np.empty((E, H // 32, F), np.uint8),
+            np.empty((E, F // 32, H), np.uint8)] if u8 else [None, None, None])
+
     def one(job):
         which, e = job
-        rng = st[2 + which * E + e]
         shape = (H, F) if which < 2 else (F, H)
-        return _store(_normal_f32(rng, shape, w_std), dtype, 0)
+        q, sc = _store(_normal_f32(st[2 + which * E + e], shape, w_std), dtype, 0)
+        mats[which][e] = q
+        if u8:
+            scl[which][e] = sc
 
     jobs = [(w, e) for w in range(3) for e in range(E)]
     with ThreadPoolExecutor(_WORKERS) as ex:
-        res = list(ex.map(one, jobs))
-    mats = [np.stack([res[w * E + e][0] for e in range(E)]) for w in range(3)]
-    scl = [np.stack([res[w * E + e][1] for e in range(E)]) if dtype == "mxfp8" else None
-           for w in range(3)]
+        list(ex.map(one, jobs))
     return LayerInputs(T=T, H=H, F=F, E=E, k=k, dtype=dtype, x=x, w_gate=mats[0], w_up=mats[1],
                        w_down=mats[2], expert_ids=ids, probs=probs, x_scale=xs,
                        wg_scale=scl[0], wu_scale=scl[1], wd_scale=scl[2],
@@ -236,20 +245,23 @@ def make_grouped(rows: int, H: int, F: int, E_local: int = 2, sources: int = 8, 
     offs = np.zeros(G + 1, dtype=np.int64)
     offs[1:] = np.cumsum(counts.ravel())
     gexp = np.tile(np.arange(E_local, dtype=np.int32), sources)
-    x, _ = _store(_normal_f32(st[1], (rows, H), 1.0), dtype, 1)
+    x, xs = _store(_normal_f32(st[1], (rows, H), 1.0), dtype, 1)
 
     def one(job):
         which, e = job
         shape = (H, F) if which < 2 else (F, H)
-        return _store(_normal_f32(st[2 + which * E_local + e], shape, 0.02), dtype, 0)[0]
+        return _store(_normal_f32(st[2 + which * E_local + e], shape, 0.02), dtype, 0)
 
     jobs = [(w, e) for w in range(3) for e in range(E_local)]
     with ThreadPoolExecutor(_WORKERS) as ex:
         res = list(ex.map(one, jobs))
-    mats = [np.stack(res[w * E_local:(w + 1) * E_local]) for w in range(3)]
+    mats = [np.stack([r[0] for r in res[w * E_local:(w + 1) * E_local]]) for w in range(3)]
+    scl = [np.stack([r[1] for r in res[w * E_local:(w + 1) * E_local]]) if dtype == "mxfp8"
+           else None for w in range(3)]
     return GroupedInputs(H=H, F=F, E_local=E_local, sources=sources, dtype=dtype, rows=x,
                          group_offsets=offs.astype(np.int32), group_expert=gexp,
                          recv_counts=counts, w_gate=mats[0], w_up=mats[1], w_down=mats[2],
+                         rows_scale=xs, wg_scale=scl[0], wu_scale=scl[1], wd_scale=scl[2],
                          meta=dict(seed=seed, zipf_s=zipf_s))
 
 

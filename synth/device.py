@@ -1,4 +1,5 @@
-"""Move seeded synthetic inputs (numpy, from ``synth``) onto a GPU as torch tensors."""
+"""Move seeded synthetic inputs (numpy, from ``synth``) onto a GPU as torch tensors (torch is
+imported by the caller; this module only converts)."""
 from types import SimpleNamespace
 
 import numpy as np

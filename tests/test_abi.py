@@ -91,7 +91,7 @@ def test_forward_rejects_before_enqueue(mel):
                                 ctypes.c_void_p(0x1000), need, None)
     assert st == 1
     # MX entry with a non-MX problem and vice versa
-    st = lib.moe_expert_forward_mx(ctypes.byref(prob), *([None] * 12), None, 0, None)
+    st = lib.moe_expert_forward_mx(ctypes.byref(prob), *([None] * 12), 0, None)
     assert st == 1
     mx = mel.problem(64, 128, 256, 4, 2, mel.MXFP8)
     st = lib.moe_expert_forward(ctypes.byref(mx), *([None] * 8), 0, None)

@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import synth
-from tests import devinputs as dv
+from synth import device as dv
 
 pytestmark = pytest.mark.gpu
 
@@ -272,3 +272,83 @@ def test_mx_quantize_bit_exact():
     q, s = oracle.mx_quantize(v.astype(np.float64))
     assert np.array_equal(dv.host(scales), s)
     assert np.array_equal(dv.host(codes), q)
+
+
+# ------------------------------------------------------------------------------------------ MX-FP8
+
+def _dec_mx(codes, scales, axis):
+    v = torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).double().numpy()
+    return v * np.repeat(np.exp2(np.asarray(scales, np.float64) - 127), 32, axis=axis)
+
+
+def _mx_weights64(src):
+    return (_dec_mx(src.w_gate, src.wg_scale, 1), _dec_mx(src.w_up, src.wu_scale, 1),
+            _dec_mx(src.w_down, src.wd_scale, 1))
+
+
+@pytest.mark.parametrize("T,H,F,E,k", [(200, 256, 256, 6, 4), (333, 384, 128, 5, 2),
+                                       (96, 128, 384, 32, 4)])
+def test_mx_forward_matches_oracle(T, H, F, E, k):
+    inp = synth.make_layer(T=T, H=H, F=F, E=E, k=k, dtype="mxfp8", seed=T)
+    ref, *_ = oracle.forward(inp)
+    d = dv.layer(inp)
+    out = dv.host(dv.forward(mel, d))
+    err = oracle.inf_norm_rel(out, ref)
+    print(f"mx T={T} H={H} F={F}: inf-norm rel err {err:.3e}")
+    assert err <= TOL["mxfp8"]
+    assert np.array_equal(out, dv.host(dv.forward(mel, d)))
+
+
+def test_mx_h_encoding_agrees_with_oracle():
+    """fc1's MX-encoded SwiGLU output, read back from the workspace, against the oracle's encoding
+    of the exact h.  The scaled fp8 MFMA accumulates with less precision than fp32 (measured: up to
+    1.5e-5 of the sum of |terms|), so a few codes may land one step away; every other code and
+    nearly every block scale must match."""
+    T, H, F, E, k = 200, 256, 384, 4, 2
+    inp = synth.make_layer(T=T, H=H, F=F, E=E, k=k, dtype="mxfp8", seed=11)
+    counts, offs, perm, _ = oracle.route(inp.expert_ids, E)
+    xp, xps = oracle.permute(inp.x, perm, k), oracle.permute(inp.x_scale, perm, k)
+    M = T * k
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    mel.grouped_ffn_mx(dv.tensor(xp), dv.tensor(xps), dv.tensor(offs),
+                       dv.tensor(np.arange(E, dtype=np.int32)), dv.tensor(inp.w_gate),
+                       dv.tensor(inp.wg_scale), dv.tensor(inp.w_up), dv.tensor(inp.wu_scale),
+                       dv.tensor(inp.w_down), dv.tensor(inp.wd_scale), workspace=ws)
+    hq_d, hs_d = mel.intermediate_h(ws, M, E, H, F, E, mel.MXFP8)
+    hq, hs = dv.host(hq_d), dv.host(hs_d)
+    X = _dec_mx(xp, xps, 1)
+    Wg, Wu, _ = _mx_weights64(inp)
+    row_e = np.repeat(np.arange(E), counts)
+    h64 = np.empty((M, F))
+    for e in range(E):
+        rows = row_e == e
+        g, u = X[rows] @ Wg[e], X[rows] @ Wu[e]
+        h64[rows] = g / (1 + np.exp(-g)) * u
+    q64, s64 = oracle.mx_quantize(h64)
+    assert (hs == s64).mean() > 0.995
+    same_scale = np.repeat(hs == s64, 32, axis=1)
+    assert (hq == q64).mean() > 0.99
+    # value check: each decoded element is within the worst-case E4M3 rounding of its block (half a
+    # top-binade step is 1/16 of amax, saturation at 448 loses up to 1/8) of the exact h
+    amax = np.repeat(np.abs(h64).reshape(M, F // 32, 32).max(axis=2), 32, axis=1)
+    err = np.abs(_dec_mx(hq, hs, 1) - h64) / np.maximum(amax, 1e-30)
+    assert err.max() <= 0.125 + 1e-6
+    assert err.mean() < 4e-3
+
+
+def test_mx_chunked_equals_unchunked():
+    inp = synth.make_layer(T=600, H=256, F=256, E=7, k=2, dtype="mxfp8", seed=5)
+    d = dv.layer(inp)
+    base = dv.host(dv.forward(mel, d, 0))
+    assert np.array_equal(dv.host(dv.forward(mel, d, 256)), base)
+    assert np.array_equal(dv.host(dv.forward(mel, d, 512)), base)
+
+
+def test_mx_grouped_ffn_matches_oracle():
+    g = synth.make_grouped(rows=700, H=256, F=256, E_local=2, sources=8, dtype="mxfp8", seed=4)
+    ref = oracle.grouped_ffn(g)
+    y = mel.grouped_ffn_mx(dv.tensor(g.rows), dv.tensor(g.rows_scale), dv.tensor(g.group_offsets),
+                           dv.tensor(g.group_expert), dv.tensor(g.w_gate), dv.tensor(g.wg_scale),
+                           dv.tensor(g.w_up), dv.tensor(g.wu_scale), dv.tensor(g.w_down),
+                           dv.tensor(g.wd_scale))
+    assert oracle.inf_norm_rel(dv.host(y), ref) <= TOL["mxfp8"]
