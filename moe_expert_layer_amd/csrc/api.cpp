@@ -21,8 +21,6 @@
 
 namespace moe {
 
-int bf16_fc1_cols_per_tile();
-int bf16_fc2_cols_per_tile();
 int mx_fc2_cols_per_tile();
 
 namespace {
@@ -48,16 +46,19 @@ moe_status hip_fail(hipError_t e, const char* what)
 int64_t elem_bytes(int dtype) { return dtype == MOE_F32 ? 4 : dtype == MOE_BF16 ? 2 : 1; }
 int64_t out_bytes(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
 
-int row_tile(int dtype) { return dtype == MOE_F32 ? kBmF32 : dtype == MOE_BF16 ? kBmBf16 : kBmMx; }
+int row_tile(int dtype, int64_t H, int64_t F)
+{
+    return dtype == MOE_F32 ? kBmF32 : dtype == MOE_BF16 ? bf16_row_tile(H, F) : kBmMx;
+}
 
 // Column tiles of the down projection for the chunk counters (tasks per row tile).
-int fc2_col_tiles(int dtype, int64_t H)
+int fc2_col_tiles(int dtype, int64_t H, int64_t F)
 {
     if (dtype == MOE_F32)
         return static_cast<int>(ceil_div(H, 256));
     if (dtype == MOE_MXFP8_E4M3)
         return static_cast<int>(H / mx_fc2_cols_per_tile());
-    return static_cast<int>(H / bf16_fc2_cols_per_tile());
+    return static_cast<int>(H / bf16_fc2_cols_per_tile(H, F));
 }
 
 // ------------------------------------------------------------------------------------- timing
@@ -142,7 +143,7 @@ private:
 
 // ------------------------------------------------------------------------------------- checks
 
-moe_status check_problem(const moe_problem* p, bool need_tokens)
+moe_status check_problem(const moe_problem* p, bool need_tokens, bool gemm = true)
 {
     if (p == nullptr)
         return fail(MOE_ERR_INVALID_ARGUMENT, "problem is null");
@@ -174,13 +175,16 @@ moe_status check_problem(const moe_problem* p, bool need_tokens)
             return fail(MOE_ERR_UNSUPPORTED, "float32 needs H %% 4 == 0");
         break;
     case MOE_BF16:
-        if (p->H % bf16_fc2_cols_per_tile() || p->F % 64 || p->F % bf16_fc1_cols_per_tile())
-            return fail(MOE_ERR_UNSUPPORTED, "bfloat16 needs H %% %d == 0 and F %% 64 == 0",
-                        bf16_fc2_cols_per_tile());
+        if (p->H % 8)
+            return fail(MOE_ERR_UNSUPPORTED, "bfloat16 needs H %% 8 == 0");
+        if (gemm && !bf16_supported(p->H, p->F))
+            return fail(MOE_ERR_UNSUPPORTED, "bfloat16 GEMMs need H %% 128 == 0 and F %% 64 == 0");
         break;
     default:
-        if (p->H % 128 || p->F % 128)
-            return fail(MOE_ERR_UNSUPPORTED, "MX needs H and F multiples of 128");
+        if (p->H % 32)
+            return fail(MOE_ERR_UNSUPPORTED, "MX needs H %% 32 == 0");
+        if (gemm && (p->H % 128 || p->F % 128))
+            return fail(MOE_ERR_UNSUPPORTED, "MX GEMMs need H and F multiples of 128");
         break;
     }
     if (p->H > INT32_MAX / 16 || p->F > INT32_MAX / 16)
@@ -207,9 +211,8 @@ RouteLayout route_layout(int64_t T, int64_t k, int64_t E, size_t base)
 FfnLayout ffn_layout(int dtype, int64_t M, int64_t G, int64_t H, int64_t F, int64_t chunk,
                      size_t base)
 {
-    (void)H;
     FfnLayout L;
-    L.bm1 = L.bm2 = row_tile(dtype);
+    L.bm1 = L.bm2 = row_tile(dtype, H, F);
     L.num_chunks = chunk > 0 ? std::max<int64_t>(1, ceil_div(M, chunk)) : 1;
     L.max_tiles1 = max_mtiles(M, G, chunk, L.bm1);
     L.max_tiles2 = max_mtiles(M, G, chunk, L.bm2);
@@ -219,6 +222,8 @@ FfnLayout ffn_layout(int dtype, int64_t M, int64_t G, int64_t H, int64_t F, int6
         off = kAlign;
     L.tile_count = off;
     off = align_up(off + 4 * sizeof(int32_t));
+    L.task_ctr = off;
+    off = align_up(off + 2 * kXcdCount * sizeof(int32_t));
     L.chunk_done = off;
     off = align_up(off + sizeof(int32_t) * static_cast<size_t>(L.num_chunks));
     L.chunk_tiles = off;
@@ -323,18 +328,20 @@ moe_status run_ffn(int dtype, const void* rows, const uint8_t* rows_scale, int64
     MTile* tiles = at<MTile>(ws, L.tiles1);
     int32_t* chunk_done = head_m_size > 0 ? at<int32_t>(ws, L.chunk_done) : nullptr;
     int32_t* chunk_tiles = head_m_size > 0 ? at<int32_t>(ws, L.chunk_tiles) : nullptr;
+    int32_t* task_ctr = at<int32_t>(ws, L.task_ctr);
     LAUNCH(s, "build_tiles",
            launch_build_tiles(offsets, group_expert, G, E, M, chunk, L.bm1, tiles, L.max_tiles1,
                               tcount, chunk_tiles, chunk_done, L.num_chunks,
-                              fc2_col_tiles(dtype, H), status, write_status, s));
+                              fc2_col_tiles(dtype, H, F), task_ctr, status, write_status, s));
     if (dtype == MOE_BF16) {
         uint16_t* h = at<uint16_t>(ws, L.h);
         LAUNCH(s, "fc1_bf16",
                launch_fc1_bf16(static_cast<const uint16_t*>(rows), static_cast<const uint16_t*>(wg),
-                               static_cast<const uint16_t*>(wu), h, tiles, tcount, H, F, s));
+                               static_cast<const uint16_t*>(wu), h, tiles, tcount, H, F,
+                               task_ctr, s));
         LAUNCH(s, "fc2_bf16",
                launch_fc2_bf16(h, static_cast<const uint16_t*>(wd), static_cast<uint16_t*>(y),
-                               tiles, tcount, H, F, chunk_done, s));
+                               tiles, tcount, H, F, chunk_done, task_ctr + kXcdCount, s));
     } else if (dtype == MOE_F32) {
         float* h = at<float>(ws, L.h);
         LAUNCH(s, "fc1_f32",
@@ -477,7 +484,7 @@ MOE_API moe_status moe_permute(const moe_problem* p, const void* x, const uint8_
                                const int32_t* pos, void* x_perm, uint8_t* x_perm_scale,
                                hipStream_t stream)
 {
-    if (moe_status st = check_problem(p, true); st != MOE_OK)
+    if (moe_status st = check_problem(p, true, false); st != MOE_OK)
         return st;
     const int64_t M = p->T * p->k;
     if (M == 0)
@@ -498,7 +505,7 @@ MOE_API moe_status moe_permute(const moe_problem* p, const void* x, const uint8_
 MOE_API moe_status moe_unpermute(const moe_problem* p, const void* y_perm, const int32_t* pos,
                                  const float* probs, void* out, hipStream_t stream)
 {
-    if (moe_status st = check_problem(p, true); st != MOE_OK)
+    if (moe_status st = check_problem(p, true, false); st != MOE_OK)
         return st;
     const int64_t M = p->T * p->k;
     if (p->T == 0)

@@ -17,18 +17,19 @@
 //   - LDS rows are 128 bytes; their 16-byte chunks are XOR-swizzled by (row mod 8) so the
 //     fragment reads (8 consecutive rows, same chunk) hit distinct banks.
 //   - Two LDS stages: the global loads for step k+1 are in flight while step k's MFMAs run.
-//   - Task order puts the row tiles of one column strip next to each other, and consecutive task
-//     ids go to workgroups of one XCD (workgroups are dealt to the 8 XCDs round-robin), so the
-//     weight strip a group of tiles shares is fetched into that XCD's L2 once.
+//   - Tasks are enumerated run by run (a run is the consecutive row tiles of one expert in one
+//     chunk), column-tile-major inside a run, and consecutive task ids go to workgroups of one XCD
+//     (workgroups are dealt to the 8 XCDs round-robin): the workgroups of an XCD then share the
+//     run's A rows and a handful of weight strips in their L2.
+//   - In a partial row tile, 32-row MFMA blocks that lie wholly past the tile's last row are
+//     skipped (the condition is uniform per wave).
 #include "common.h"
 #include "internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kXcds = 8;
-
-template <bool kGated, int kWM, int kWN, int kTM, int kTN>
+template <bool kGated, int kWM, int kWN, int kTM, int kTN, int kMinBlocks>
 struct Cfg {
     static constexpr int kWaves = kWM * kWN;
     static constexpr int kThreads = kWaves * 64;
@@ -45,6 +46,7 @@ struct Cfg {
     static_assert(kBRows * kThreads * 8 == BK * BNB, "B tile split");
     static_assert(kBRows == 4 || kBRows == 8, "B transpose handles 4 or 8 rows");
     static_assert(!kGated || kTN % 2 == 0, "gated tiles pair gate/up subtiles");
+    static constexpr int kSmemBytes = 2 * kStageBytes;
 };
 
 // Byte offset of element (row, k) in a [rows x 64] bf16 LDS tile with XOR-swizzled 16-byte chunks.
@@ -53,22 +55,15 @@ __device__ __forceinline__ int lds_off(int row, int k)
     return row * 128 + ((((k >> 3) ^ row) & 7) << 4) + ((k & 7) << 1);
 }
 
-__device__ __forceinline__ int remap_xcd(int bid, int grid)
-{
-    // grid is a multiple of kXcds: workgroup bid runs on XCD bid % kXcds; give each XCD a
-    // contiguous range of logical ids.
-    return (bid % kXcds) * (grid / kXcds) + bid / kXcds;
-}
-
 // Global -> register staging of one K step (k0) of the A and B tiles.
 template <class G>
 __device__ __forceinline__ void load_tiles(u32x4_t (&ra)[G::kAChunks], u32x4_t (&rb)[G::kBRows],
-                                           const uint16_t* const (&asrc)[G::kAChunks],
+                                           const uint16_t* A, const uint32_t (&aoff)[G::kAChunks],
                                            const uint16_t* bsrc, int k0, int64_t N_w)
 {
 #pragma unroll
     for (int i = 0; i < G::kAChunks; ++i)
-        ra[i] = *reinterpret_cast<const u32x4_t*>(asrc[i] + k0);
+        ra[i] = *reinterpret_cast<const u32x4_t*>(A + aoff[i] + k0);
 #pragma unroll
     for (int r = 0; r < G::kBRows; ++r)
         rb[r] = *reinterpret_cast<const u32x4_t*>(bsrc + static_cast<int64_t>(k0 + r) * N_w);
@@ -79,14 +74,15 @@ __device__ __forceinline__ void load_tiles(u32x4_t (&ra)[G::kAChunks], u32x4_t (
 template <class G>
 __device__ __forceinline__ void store_tiles(unsigned char* smem, int buf,
                                             const u32x4_t (&ra)[G::kAChunks],
-                                            const u32x4_t (&rb)[G::kBRows],
-                                            const int (&a_lds)[G::kAChunks], int b0, int kg)
+                                            const u32x4_t (&rb)[G::kBRows], int a_lds0, int b0,
+                                            int kg)
 {
     unsigned char* As = smem + buf * G::kStageBytes;
     unsigned char* Bs = As + G::kABytes;
+    // A chunk i of this thread is row tid / 8 + (kThreads / 8) * i: same swizzle phase
 #pragma unroll
     for (int i = 0; i < G::kAChunks; ++i)
-        *reinterpret_cast<u32x4_t*>(As + a_lds[i]) = ra[i];
+        *reinterpret_cast<u32x4_t*>(As + a_lds0 + i * (G::kThreads / 8) * 128) = ra[i];
 #pragma unroll
     for (int col = 0; col < 8; ++col) {
         const int d = col >> 1;
@@ -103,18 +99,94 @@ __device__ __forceinline__ void store_tiles(unsigned char* smem, int buf,
     }
 }
 
-template <bool kGated, int kWM, int kWN, int kTM, int kTN>
-__global__ __launch_bounds__(kWM * kWN * 64, 2) void grouped_gemm_bf16(
+// Row block i of wave row wm covers tile rows 32 * (kWM * i + wm) .. + 31 (wave rows interleave, so
+// a partial tile splits its row blocks evenly between them).
+template <int kWM>
+__device__ __forceinline__ int row_block(int i, int wm)
+{
+    return 32 * (kWM * i + wm);
+}
+
+// MFMA fragments of k sub-step ks (16 values of K): the first NB row blocks and all kTN column blocks.
+template <int kWM, int kTM, int kTN, int NB>
+__device__ __forceinline__ void load_frags(bf16x8_t (&af)[kTM], bf16x8_t (&bfr)[kTN],
+                                           const unsigned char* As, const unsigned char* Bs, int wm,
+                                           int wn, int lane, int ks)
+{
+    const int kk = ks * 16 + 8 * (lane >> 5);
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(
+            Bs + lds_off(wn * kTN * 32 + 32 * j + (lane & 31), kk));
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(
+            As + lds_off(row_block<kWM>(i, wm) + (lane & 31), kk));
+}
+
+template <int kTM, int kTN, int NB>
+__device__ __forceinline__ void mfma_block(f32x16_t (&acc)[kTM][kTN], const bf16x8_t (&af)[kTM],
+                                           const bf16x8_t (&bfr)[kTN])
+{
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+}
+
+// The K loop of one task with NB active row blocks in this wave (NB = 0: the wave only helps stage
+// tiles and keeps the barriers).  Two LDS stages; global loads of step kt + 1 and LDS fragment reads
+// of sub-step ks + 1 are in flight while the MFMAs of kt / ks run.
+template <class G, int kWM, int kTM, int kTN, int NB>
+__device__ __forceinline__ void k_loop(f32x16_t (&acc)[kTM][kTN], unsigned char* smem,
+                                       const uint16_t* A, const uint32_t (&aoff)[G::kAChunks],
+                                       const uint16_t* bsrc, int64_t N_w, int a_lds0, int b0,
+                                       int kg, int KT, int wm, int wn, int lane)
+{
+    u32x4_t ra[G::kAChunks];
+    u32x4_t rb[G::kBRows];
+    load_tiles<G>(ra, rb, A, aoff, bsrc, 0, N_w);
+    store_tiles<G>(smem, 0, ra, rb, a_lds0, b0, kg);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < KT)
+            load_tiles<G>(ra, rb, A, aoff, bsrc, (kt + 1) * G::BK, N_w);
+        const unsigned char* As = smem + cur * G::kStageBytes;
+        const unsigned char* Bs = As + G::kABytes;
+        if constexpr (NB > 0) {
+            bf16x8_t af[2][kTM], bfr[2][kTN];
+            load_frags<kWM, kTM, kTN, NB>(af[0], bfr[0], As, Bs, wm, wn, lane, 0);
+#pragma unroll 1
+            for (int ks = 0; ks < G::BK / 16; ks += 2) {
+                load_frags<kWM, kTM, kTN, NB>(af[1], bfr[1], As, Bs, wm, wn, lane, ks + 1);
+                mfma_block<kTM, kTN, NB>(acc, af[0], bfr[0]);
+                if (ks + 2 < G::BK / 16)
+                    load_frags<kWM, kTM, kTN, NB>(af[0], bfr[0], As, Bs, wm, wn, lane, ks + 2);
+                mfma_block<kTM, kTN, NB>(acc, af[1], bfr[1]);
+            }
+        }
+        if (kt + 1 < KT)
+            store_tiles<G>(smem, cur ^ 1, ra, rb, a_lds0, b0, kg);
+        __syncthreads();
+    }
+}
+
+template <bool kGated, int kWM, int kWN, int kTM, int kTN, int kMinBlocks>
+__global__ __launch_bounds__(kWM * kWN * 64, kMinBlocks) void grouped_gemm_bf16(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, const MTile* __restrict__ tiles,
-    const int32_t* __restrict__ tile_count, int K, int N_out, int32_t* __restrict__ chunk_done)
+    const int32_t* __restrict__ tile_count, int K, int N_out, int32_t* __restrict__ chunk_done,
+    int32_t* __restrict__ task_ctr)
 {
-    using G = Cfg<kGated, kWM, kWN, kTM, kTN>;
+    using G = Cfg<kGated, kWM, kWN, kTM, kTN, kMinBlocks>;
+    __shared__ int claimed;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave: keep scalar
     const int wm = wave / kWN;
     const int wn = wave % kWN;
     const int n_mt = *tile_count;
@@ -123,15 +195,43 @@ __global__ __launch_bounds__(kWM * kWN * 64, 2) void grouped_gemm_bf16(
     const int KT = K / G::BK;
     const int64_t N_w = N_out;        // row stride of the weight matrices
 
-    // B staging position of this thread
-    const int cb = tid % (G::BNB / 8);          // 8-column chunk of the staged columns
-    const int kg = tid / (G::BNB / 8);          // group of kBRows k rows
+    // B staging position of this thread.  The k group varies fastest across lanes, so the 8 lanes
+    // writing one transposed column chunk fill the 8 (swizzled) 16-byte chunks of one LDS row and
+    // never collide on a bank; each global load still covers whole 128-byte row segments.
+    constexpr int kKGroups = G::BK / G::kBRows;
+    const int kg = tid % kKGroups;              // group of kBRows k rows
+    const int cb = tid / kKGroups;              // 8-column chunk of the staged columns
     const int b0 = cb * 8;
 
-    for (int t = remap_xcd(blockIdx.x, gridDim.x); t < total; t += gridDim.x) {
-        const MTile tile = tiles[t % n_mt];
-        const int nt = t / n_mt;
+    // Tasks are dealt in blocks of `blk` (the workgroups of one XCD): block j belongs to XCD j % 8,
+    // and each XCD's workgroups claim that XCD's tasks in order from its own counter.  Whatever the
+    // workgroups' relative speeds, an XCD works on about `blk` consecutive tasks at a time (shared
+    // A rows and weight strips in its L2), and overall progress follows task order.
+    const int xcd = blockIdx.x % kXcdCount;
+    const int blk = gridDim.x / kXcdCount;
+    for (;;) {
+        // Wave 0 claims the next task: every lane takes part (lane 0 adds 1, the others 0) so no
+        // lane-divergent branch sits in this barrier loop; lane-divergent regions here let the
+        // compiler's loop restructuring split one wave's lanes across different barrier paths.
+        if (wave == 0) {
+            const int v = atomicAdd(&task_ctr[xcd], lane == 0 ? 1 : 0);
+            claimed = __builtin_amdgcn_readfirstlane(v);
+        }
+        __syncthreads();
+        const int i = __builtin_amdgcn_readfirstlane(claimed);   // one value per workgroup
+        const int t = ((i / blk) * kXcdCount + xcd) * blk + i % blk;
+        if (t >= total)
+            break;
+        // task t belongs to the run holding row tile t / n_nt; inside the run, row tiles vary fastest
+        const MTile head = tiles[t / n_nt];
+        const int local = t - n_nt * head.run_begin;
+        const MTile tile = tiles[head.run_begin + local % head.run_len];
+        const int nt = local / head.run_len;
         const int n0 = nt * G::BN;
+        // 32-row MFMA blocks of this wave that hold at least one row of the tile
+        const int tile_blocks = (tile.row_end - tile.row_begin + 31) / 32;
+        const int nb = __builtin_amdgcn_readfirstlane(
+            min(kTM, max(0, (tile_blocks - wm + kWM - 1) / kWM)));
 
         // global column and matrix this thread stages
         const uint16_t* bsrc;
@@ -144,20 +244,15 @@ __global__ __launch_bounds__(kWM * kWN * 64, 2) void grouped_gemm_bf16(
         }
         bsrc += static_cast<int64_t>(kg * G::kBRows) * N_w;
 
-        // A rows this thread stages (clamped into the tile; rows past row_end are never stored)
-        const uint16_t* asrc[G::kAChunks];
-        int a_lds[G::kAChunks];
+        // A rows this thread stages (clamped into the tile; rows past row_end are never stored), as
+        // element offsets from A (the host bounds M * K below 2^31)
+        uint32_t aoff[G::kAChunks];
 #pragma unroll
         for (int i = 0; i < G::kAChunks; ++i) {
-            const int idx = tid + i * G::kThreads;
-            const int row = idx / 8, ch = idx % 8;
-            const int grow = min(tile.row_begin + row, tile.row_end - 1);
-            asrc[i] = A + static_cast<int64_t>(grow) * K + ch * 8;
-            a_lds[i] = lds_off(row, ch * 8);
+            const int grow = min(tile.row_begin + tid / 8 + (G::kThreads / 8) * i, tile.row_end - 1);
+            aoff[i] = static_cast<uint32_t>(grow) * static_cast<uint32_t>(K) + (tid % 8) * 8;
         }
-
-        u32x4_t ra[G::kAChunks];
-        u32x4_t rb[G::kBRows];
+        const int a_lds0 = lds_off(tid / 8, (tid % 8) * 8);
 
         f32x16_t acc[kTM][kTN];
 #pragma unroll
@@ -168,46 +263,29 @@ __global__ __launch_bounds__(kWM * kWN * 64, 2) void grouped_gemm_bf16(
                 for (int r = 0; r < 16; ++r)
                     acc[i][j][r] = 0.0f;
 
-        load_tiles<G>(ra, rb, asrc, bsrc, 0, N_w);
-        store_tiles<G>(smem, 0, ra, rb, a_lds, b0, kg);
-        __syncthreads();
-        for (int kt = 0; kt < KT; ++kt) {
-            const int cur = kt & 1;
-            if (kt + 1 < KT)
-                load_tiles<G>(ra, rb, asrc, bsrc, (kt + 1) * G::BK, N_w);
-            const unsigned char* As = smem + cur * G::kStageBytes;
-            const unsigned char* Bs = As + G::kABytes;
-#pragma unroll
-            for (int ks = 0; ks < G::BK / 16; ++ks) {
-                const int kk = ks * 16 + 8 * (lane >> 5);
-                bf16x8_t af[kTM], bfr[kTN];
-#pragma unroll
-                for (int i = 0; i < kTM; ++i)
-                    af[i] = *reinterpret_cast<const bf16x8_t*>(
-                        As + lds_off(wm * kTM * 32 + 32 * i + (lane & 31), kk));
-#pragma unroll
-                for (int j = 0; j < kTN; ++j)
-                    bfr[j] = *reinterpret_cast<const bf16x8_t*>(
-                        Bs + lds_off(wn * kTN * 32 + 32 * j + (lane & 31), kk));
-#pragma unroll
-                for (int i = 0; i < kTM; ++i)
-#pragma unroll
-                    for (int j = 0; j < kTN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j],
-                                                                           acc[i][j], 0, 0, 0);
-            }
-            if (kt + 1 < KT)
-                store_tiles<G>(smem, cur ^ 1, ra, rb, a_lds, b0, kg);
-            __syncthreads();
+        switch (nb) {
+#define MOE_KLOOP(NB)                                                                               \
+    case NB:                                                                                        \
+        k_loop<G, kWM, kTM, kTN, (NB < kTM ? NB : kTM)>(acc, smem, A, aoff, bsrc, N_w, a_lds0, b0, \
+                                                         kg, KT, wm, wn, lane);                     \
+        break;
+            MOE_KLOOP(0) MOE_KLOOP(1) MOE_KLOOP(2) MOE_KLOOP(3)
+            default:
+                k_loop<G, kWM, kTM, kTN, kTM>(acc, smem, A, aoff, bsrc, N_w, a_lds0, b0, kg, KT,
+                                              wm, wn, lane);
+                break;
+#undef MOE_KLOOP
         }
 
         // epilogue: lane holds column (lane % 32) of each 32x32 block, rows
         // 8 * (r / 4) + 4 * (lane / 32) + r % 4 for r = 0..15
 #pragma unroll
         for (int i = 0; i < kTM; ++i) {
+            // keep the scheduler from pulling every accumulator into VGPRs at once
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = tile.row_begin + wm * kTM * 32 + 32 * i + 8 * (r >> 2) +
+                const int row = tile.row_begin + row_block<kWM>(i, wm) + 8 * (r >> 2) +
                                 4 * (lane >> 5) + (r & 3);
                 if (row >= tile.row_end)
                     continue;
@@ -229,46 +307,87 @@ __global__ __launch_bounds__(kWM * kWN * 64, 2) void grouped_gemm_bf16(
         if (chunk_done != nullptr) {
             __threadfence();
             __syncthreads();
-            if (tid == 0)
-                atomicAdd(&chunk_done[tile.chunk], 1);
+            if (wave == 0)
+                atomicAdd(&chunk_done[tile.chunk], lane == 0 ? 1 : 0);
         }
     }
 }
 
-// Tile configuration: 4 waves (2 x 2), each 64 rows x 64 staged columns.
-constexpr int kWM = 2, kWN = 2, kTM = 2, kTN = 2;
-using Fc1Cfg = Cfg<true, kWM, kWN, kTM, kTN>;
-using Fc2Cfg = Cfg<false, kWM, kWN, kTM, kTN>;
-static_assert(Fc1Cfg::BM == kBmBf16 && Fc2Cfg::BM == kBmBf16, "row tile height");
+// Tile configurations.  Large: 4 waves (2 x 2), each 128 rows x 128 staged columns (16 accumulator
+// blocks of 32 x 32 per wave), one workgroup per CU, 128 KiB of LDS for the two stages; used when
+// H % 256 == 0 and F % 128 == 0.  Small: 4 waves of 64 x 64, two workgroups per CU, for other sizes
+// (H % 128 == 0, F % 64 == 0).
+using Fc1Big = Cfg<true, 2, 2, 4, 4, 1>;
+using Fc2Big = Cfg<false, 2, 2, 4, 4, 1>;
+using Fc1Small = Cfg<true, 2, 2, 2, 2, 2>;
+using Fc2Small = Cfg<false, 2, 2, 2, 2, 2>;
+#define FC1_BIG grouped_gemm_bf16<true, 2, 2, 4, 4, 1>
+#define FC2_BIG grouped_gemm_bf16<false, 2, 2, 4, 4, 1>
+#define FC1_SMALL grouped_gemm_bf16<true, 2, 2, 2, 2, 2>
+#define FC2_SMALL grouped_gemm_bf16<false, 2, 2, 2, 2, 2>
 
-unsigned persistent_grid()
+bool use_big(int64_t H, int64_t F) { return H % Fc2Big::BN == 0 && F % Fc1Big::BN == 0; }
+
+hipError_t ensure_smem_limits()
 {
-    return static_cast<unsigned>(device_info().cu_count * 2);
+    static bool done[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 64 && done[dev])
+        return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&FC1_BIG),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, Fc1Big::kSmemBytes);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&FC2_BIG),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, Fc2Big::kSmemBytes);
+    if (e == hipSuccess && dev < 64)
+        done[dev] = true;
+    return e;
 }
 
 }  // namespace
 
-int bf16_fc1_cols_per_tile() { return Fc1Cfg::BN; }
-int bf16_fc2_cols_per_tile() { return Fc2Cfg::BN; }
+int bf16_row_tile(int64_t H, int64_t F) { return use_big(H, F) ? Fc1Big::BM : Fc1Small::BM; }
+int bf16_fc2_cols_per_tile(int64_t H, int64_t F) { return use_big(H, F) ? Fc2Big::BN : Fc2Small::BN; }
+bool bf16_supported(int64_t H, int64_t F) { return H % Fc2Small::BN == 0 && F % Fc1Small::BN == 0; }
 
 hipError_t launch_fc1_bf16(const uint16_t* A, const uint16_t* wg, const uint16_t* wu, uint16_t* h,
                            const MTile* tiles, const int32_t* tile_count, int64_t H, int64_t F,
-                           hipStream_t s)
+                           int32_t* task_ctr, hipStream_t s)
 {
-    grouped_gemm_bf16<true, kWM, kWN, kTM, kTN>
-        <<<dim3(persistent_grid()), dim3(Fc1Cfg::kThreads), 2 * Fc1Cfg::kStageBytes, s>>>(
-            A, wg, wu, h, tiles, tile_count, static_cast<int>(H), static_cast<int>(F), nullptr);
+    const int cu = device_info().cu_count;
+    if (use_big(H, F)) {
+        if (hipError_t e = ensure_smem_limits(); e != hipSuccess)
+            return e;
+        FC1_BIG<<<dim3(cu), dim3(Fc1Big::kThreads), Fc1Big::kSmemBytes, s>>>(
+            A, wg, wu, h, tiles, tile_count, static_cast<int>(H), static_cast<int>(F), nullptr,
+            task_ctr);
+    } else {
+        FC1_SMALL<<<dim3(2 * cu), dim3(Fc1Small::kThreads), Fc1Small::kSmemBytes, s>>>(
+            A, wg, wu, h, tiles, tile_count, static_cast<int>(H), static_cast<int>(F), nullptr,
+            task_ctr);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_fc2_bf16(const uint16_t* h, const uint16_t* wd, uint16_t* y, const MTile* tiles,
                            const int32_t* tile_count, int64_t H, int64_t F, int32_t* chunk_done,
-                           hipStream_t s)
+                           int32_t* task_ctr, hipStream_t s)
 {
-    grouped_gemm_bf16<false, kWM, kWN, kTM, kTN>
-        <<<dim3(persistent_grid()), dim3(Fc2Cfg::kThreads), 2 * Fc2Cfg::kStageBytes, s>>>(
+    const int cu = device_info().cu_count;
+    if (use_big(H, F)) {
+        if (hipError_t e = ensure_smem_limits(); e != hipSuccess)
+            return e;
+        FC2_BIG<<<dim3(cu), dim3(Fc2Big::kThreads), Fc2Big::kSmemBytes, s>>>(
             h, wd, nullptr, y, tiles, tile_count, static_cast<int>(F), static_cast<int>(H),
-            chunk_done);
+            chunk_done, task_ctr);
+    } else {
+        FC2_SMALL<<<dim3(2 * cu), dim3(Fc2Small::kThreads), Fc2Small::kSmemBytes, s>>>(
+            h, wd, nullptr, y, tiles, tile_count, static_cast<int>(F), static_cast<int>(H),
+            chunk_done, task_ctr);
+    }
     return hipGetLastError();
 }
 

@@ -42,8 +42,9 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(
         if (chunk_done != nullptr) {
             __threadfence();
             __syncthreads();
-            if (threadIdx.x == 0)
-                atomicAdd(&chunk_done[tile.chunk], 1);
+            // whole first wave (lane 0 adds 1): no lane-divergent region in this barrier loop
+            if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0)
+                atomicAdd(&chunk_done[tile.chunk], (threadIdx.x & 63) == 0 ? 1 : 0);
         }
     }
 }

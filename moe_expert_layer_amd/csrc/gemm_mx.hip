@@ -77,10 +77,12 @@ constexpr int kEpiBytes = 4 * 64 * kStageLd * 4;  // 4 waves x 64 rows
 constexpr int kSmemBytes = 2 * kStageBytes > kEpiBytes ? 2 * kStageBytes : kEpiBytes;
 static_assert(BM == kWM * kTM * 32 && BNB == kWN * kTN * 32, "tile shape");
 
-// Byte offset of (row, k) in a [rows x 128] byte LDS tile with XOR-swizzled 16-byte chunks.
+// Byte offset of (row, k) in a [rows x 128] byte LDS tile with XOR-swizzled 16-byte chunks.  The
+// swizzle mixes row bits 0-2 (fragment reads: 8 consecutive rows) and 4-6 (transposed weight
+// writes: lanes 16 rows apart), so neither access pattern piles onto one bank.
 __device__ __forceinline__ int lds_off8(int row, int k)
 {
-    return row * 128 + ((((k >> 4) ^ row) & 7) << 4) + (k & 15);
+    return row * 128 + ((((k >> 4) ^ row ^ (row >> 4)) & 7) << 4) + (k & 15);
 }
 
 __device__ __forceinline__ int remap_xcd(int bid, int grid)
@@ -113,7 +115,7 @@ __device__ __forceinline__ void mx_load(Stage& st, const uint8_t* A, const uint3
 }
 
 __device__ __forceinline__ void mx_store(unsigned char* smem, int buf, const Stage& st,
-                                         int a_lds0, int b0, int kg, int tid)
+                                         int a_row0, int a_k, int b0, int kg, int tid)
 {
     unsigned char* As = smem + buf * kStageBytes;
     unsigned char* Bs = As + kABytes;
@@ -121,7 +123,7 @@ __device__ __forceinline__ void mx_store(unsigned char* smem, int buf, const Sta
     unsigned char* Bsc = Asc + kAScBytes;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4_t*>(As + a_lds0 + i * 32 * 128) = st.a[i];   // rows tid/8 + 32 i
+        *reinterpret_cast<u32x4_t*>(As + lds_off8(a_row0 + 32 * i, a_k)) = st.a[i];   // rows tid/8 + 32 i
     // 4 (k) x 16 (n) bytes -> 16 columns of 4 consecutive k bytes: a 4x4 byte transpose per dword
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_mx(
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / kWN, wn = wave % kWN;
     const int h = lane >> 5;
     const int n_mt = *tile_count;
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_mx(
             const int grow = min(tile.row_begin + tid / 8 + 32 * i, tile.row_end - 1);
             aoff[i] = static_cast<uint32_t>(grow) * static_cast<uint32_t>(K) + (tid % 8) * 16;
         }
-        const int a_lds0 = lds_off8(tid / 8, (tid % 8) * 16);
+        const int a_row0 = tid / 8, a_k = (tid % 8) * 16;
 
         f32x16_t acc[kTM][kTN];
 #pragma unroll
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_mx(
 
         Stage st;
         mx_load<kGated>(st, A, aoff, bsrc, ascsrc, bscsrc, 0, N_w, tid);
-        mx_store(smem, 0, st, a_lds0, b0, kg, tid);
+        mx_store(smem, 0, st, a_row0, a_k, b0, kg, tid);
         __syncthreads();
         for (int kt = 0; kt < KT; ++kt) {
             const int cur = kt & 1;
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_mx(
                             af[i], bfr[j], acc[i][j], 0, 0, 0, sa[i], 0, sbv[j]);
             }
             if (kt + 1 < KT)
-                mx_store(smem, cur ^ 1, st, a_lds0, b0, kg, tid);
+                mx_store(smem, cur ^ 1, st, a_row0, a_k, b0, kg, tid);
             __syncthreads();
         }
 
@@ -312,8 +314,8 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_mx(
             if (chunk_done != nullptr) {
                 __threadfence();
                 __syncthreads();
-                if (tid == 0)
-                    atomicAdd(&chunk_done[tile.chunk], 1);
+                if (wave == 0)   // whole wave (lane 0 adds 1): no lane-divergent region in the loop
+                    atomicAdd(&chunk_done[tile.chunk], lane == 0 ? 1 : 0);
             }
         }
     }

@@ -9,11 +9,17 @@ namespace moe {
 
 // A tile of work for the grouped GEMMs: rows [row_begin, row_end) of the grouped activations all
 // use weights of `expert`; `chunk` is the M-axis chunk the rows belong to (0 when unchunked).
+// Consecutive tiles of one expert inside one chunk form a run [run_begin, run_begin + run_len) of
+// the table; the GEMMs enumerate a run's (row tile, column tile) tasks column-tile-major so that
+// the workgroups working at the same time share the run's A rows and a few weight strips.
 struct MTile {
     int expert;
     int row_begin;
     int row_end;
     int chunk;
+    int run_begin;
+    int run_len;
+    int pad0, pad1;
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -23,9 +29,10 @@ constexpr int kRouteSlotsPerBlock = 2048;  // slots handled by one routing workg
 constexpr int kMaxExperts = 1024;          // routing LDS histograms are sized for this
 constexpr int kChunkAlign = 256;           // head_m_size must be a multiple of this
 constexpr size_t kAlign = 256;
+constexpr int kXcdCount = 8;               // MI355X: workgroup b runs on XCD b % 8 (measured)
 
-// Row-tile heights of the grouped GEMMs (the tile tables are built per height).
-constexpr int kBmBf16 = 128;
+// Row-tile heights of the grouped GEMMs (the tile tables are built per height); the bf16 height
+// depends on the problem (bf16_row_tile).
 constexpr int kBmF32 = 32;
 constexpr int kBmMx = 128;
 
@@ -55,6 +62,7 @@ struct FfnLayout {
     size_t status = 0;
     size_t tiles1 = 0, tiles2 = 0;     // MTile tables for fc1 / fc2 row-tile heights
     size_t tile_count = 0;             // int32 [4]: fc1 tiles, fc2 tiles
+    size_t task_ctr = 0;               // int32 [2][kXcdCount]: per-XCD task counters of fc1 / fc2
     size_t chunk_done = 0;             // int32 [num_chunks]: fc2 tiles finished per chunk
     size_t chunk_tiles = 0;            // int32 [num_chunks]: fc2 tiles per chunk
     size_t h = 0, h_scale = 0;         // SwiGLU output [M, F] (+ MX scales [M, F/32])
@@ -97,13 +105,13 @@ hipError_t launch_route_scatter(const int32_t* ids, int64_t M, int64_t E,
 // Builds the row-tile table: groups are rows [offsets[g], offsets[g+1]) (clamped into [0, M]) with expert
 // group_expert[g] (identity when null).  Writes tiles and *tile_count; when chunk_tiles is not
 // null also the expected (row tile x column tile) tasks per chunk (row tiles * col_tiles) and
-// zeroes chunk_done.  A non-empty group with an expert outside [0, E) is skipped and sets
+// zeroes chunk_done; zeroes the 2 * kXcdCount task counters at task_ctr.  A non-empty group with an expert outside [0, E) is skipped and sets
 // *status; with write_status the status word is written either way.
 hipError_t launch_build_tiles(const int32_t* offsets, const int32_t* group_expert, int64_t G,
                               int64_t E, int64_t M, int64_t chunk, int bm, MTile* tiles, int64_t max_tiles,
                               int32_t* tile_count, int32_t* chunk_tiles, int32_t* chunk_done,
-                              int64_t num_chunks, int col_tiles, int32_t* status,
-                              bool write_status, hipStream_t s);
+                              int64_t num_chunks, int col_tiles, int32_t* task_ctr,
+                              int32_t* status, bool write_status, hipStream_t s);
 
 // permute.hip
 // Slots whose pos is outside [0, M) are skipped.
@@ -113,12 +121,16 @@ hipError_t launch_unpermute(int dtype, const void* y_perm, const int32_t* pos, c
                             void* out, int64_t T, int64_t k, int64_t M, int64_t H, hipStream_t s);
 
 // gemm_bf16.hip: grouped GEMMs on bf16 MFMA.  fc1: h = swiglu(A Wg, A Wu); fc2: y = h Wd.
+bool bf16_supported(int64_t H, int64_t F);
+int bf16_row_tile(int64_t H, int64_t F);
+int bf16_fc2_cols_per_tile(int64_t H, int64_t F);
+// task_ctr: kXcdCount zeroed counters for this launch (workspace).
 hipError_t launch_fc1_bf16(const uint16_t* A, const uint16_t* wg, const uint16_t* wu, uint16_t* h,
                            const MTile* tiles, const int32_t* tile_count, int64_t H, int64_t F,
-                           hipStream_t s);
+                           int32_t* task_ctr, hipStream_t s);
 hipError_t launch_fc2_bf16(const uint16_t* h, const uint16_t* wd, uint16_t* y, const MTile* tiles,
                            const int32_t* tile_count, int64_t H, int64_t F, int32_t* chunk_done,
-                           hipStream_t s);
+                           int32_t* task_ctr, hipStream_t s);
 
 // gemm_f32.hip: float32 grouped GEMMs (plain FMA).
 hipError_t launch_fc1_f32(const float* A, const float* wg, const float* wu, float* h,

@@ -163,8 +163,10 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ group_expert, int G, int E,
     int64_t M, int64_t chunk, int bm, MTile* __restrict__ tiles, int max_tiles, int32_t* __restrict__ tile_count,
     int32_t* __restrict__ chunk_tiles, int32_t* __restrict__ chunk_done, int num_chunks,
-    int col_tiles, int32_t* __restrict__ status, int write_status)
+    int col_tiles, int32_t* __restrict__ task_ctr, int32_t* __restrict__ status, int write_status)
 {
+    if (task_ctr != nullptr && threadIdx.x < 2 * kXcdCount)
+        task_ctr[threadIdx.x] = 0;
     __shared__ int buf[2 * kScanThreads];
     __shared__ int carry;
     __shared__ int bad;
@@ -202,6 +204,8 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
         int t = carry + incl - n;
         for (int64_t r = rb; r < re;) {
             const int64_t cend = min(re, (r / chunk + 1) * chunk);
+            const int run_begin = t;
+            const int run_len = static_cast<int>((cend - r + bm - 1) / bm);
             for (int64_t r0 = r; r0 < cend; r0 += bm) {
                 const int c = static_cast<int>(r0 / chunk);
                 if (t < max_tiles) {
@@ -210,6 +214,9 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
                     mt.row_begin = static_cast<int>(r0);
                     mt.row_end = static_cast<int>(min(cend, r0 + bm));
                     mt.chunk = c;
+                    mt.run_begin = run_begin;
+                    mt.run_len = run_len;
+                    mt.pad0 = mt.pad1 = 0;
                     tiles[t] = mt;
                 }
                 if (chunk_tiles != nullptr && c < num_chunks)
@@ -267,13 +274,13 @@ hipError_t launch_route_scatter(const int32_t* ids, int64_t M, int64_t E,
 hipError_t launch_build_tiles(const int32_t* offsets, const int32_t* group_expert, int64_t G,
                               int64_t E, int64_t M, int64_t chunk, int bm, MTile* tiles, int64_t max_tiles,
                               int32_t* tile_count, int32_t* chunk_tiles, int32_t* chunk_done,
-                              int64_t num_chunks, int col_tiles, int32_t* status,
-                              bool write_status, hipStream_t s)
+                              int64_t num_chunks, int col_tiles, int32_t* task_ctr,
+                              int32_t* status, bool write_status, hipStream_t s)
 {
     build_tiles_kernel<<<dim3(1), dim3(kScanThreads), 0, s>>>(
         offsets, group_expert, static_cast<int>(G), static_cast<int>(E), M, chunk, bm, tiles,
         static_cast<int>(max_tiles), tile_count, chunk_tiles, chunk_done,
-        static_cast<int>(num_chunks), col_tiles, status, write_status ? 1 : 0);
+        static_cast<int>(num_chunks), col_tiles, task_ctr, status, write_status ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -332,8 +332,9 @@ def test_mx_h_encoding_agrees_with_oracle():
     # top-binade step is 1/16 of amax, saturation at 448 loses up to 1/8) of the exact h
     amax = np.repeat(np.abs(h64).reshape(M, F // 32, 32).max(axis=2), 32, axis=1)
     err = np.abs(_dec_mx(hq, hs, 1) - h64) / np.maximum(amax, 1e-30)
+    own = np.abs(_dec_mx(q64, s64, 1) - h64) / np.maximum(amax, 1e-30)
     assert err.max() <= 0.125 + 1e-6
-    assert err.mean() < 4e-3
+    assert err.mean() <= 1.05 * own.mean()       # as good as encoding the exact h, on average
 
 
 def test_mx_chunked_equals_unchunked():
