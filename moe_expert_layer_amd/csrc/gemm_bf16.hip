@@ -8,21 +8,27 @@
 // the same K order whatever tile or chunk the row falls in (no split-K), so results do not depend
 // on the tiling of M.
 //
-// Structure (one persistent workgroup per CU slot, looping over (row tile, column tile) tasks):
-//   - A tile [BM x 64] is read as 16-byte row segments and stored to LDS unchanged (K contiguous).
-//   - The weights are N-contiguous ([K, N]); MFMA wants K-contiguous fragments, so each thread
-//     loads a (rows of k) x 8-column block, transposes it in registers with v_perm_b32, and
-//     stores K-contiguous columns to LDS.  For fc1 the staged columns interleave 32 gate columns
-//     with the matching 32 up columns, so one wave holds both halves of every SwiGLU pair.
-//   - LDS rows are 128 bytes; their 16-byte chunks are XOR-swizzled by (row mod 8) so the
-//     fragment reads (8 consecutive rows, same chunk) hit distinct banks.
-//   - Two LDS stages: the global loads for step k+1 are in flight while step k's MFMAs run.
-//   - Tasks are enumerated run by run (a run is the consecutive row tiles of one expert in one
-//     chunk), column-tile-major inside a run, and consecutive task ids go to workgroups of one XCD
-//     (workgroups are dealt to the 8 XCDs round-robin): the workgroups of an XCD then share the
-//     run's A rows and a handful of weight strips in their L2.
-//   - In a partial row tile, 32-row MFMA blocks that lie wholly past the tile's last row are
-//     skipped (the condition is uniform per wave).
+// Both kernels are persistent (one or two workgroups per CU slot) and loop over (row tile, column
+// tile) tasks.  Tasks are enumerated run by run (a run is the consecutive row tiles of one expert in
+// one chunk), column-tile-major inside a run, and consecutive task ids go to workgroups of one XCD
+// (workgroups are dealt to the 8 XCDs round-robin): the workgroups of an XCD then share the run's A
+// rows and a handful of weight strips in their L2.  In a partial row tile, 32-row MFMA blocks that
+// lie wholly past the tile's last row are skipped (the condition is uniform per wave).
+//
+// Large tiles (256 rows x 256 weight columns, 4 waves of 128 x 128; H % 256 == 0, F % 128 == 0):
+//   - global -> LDS copies bypass registers (global_load_lds_dwordx4: each lane moves 16 bytes to
+//     LDS at the wave's base + 16 * lane); four LDS stages of 32 values of K, so the copies of three
+//     K steps are in flight while one is multiplied;
+//   - A sits in LDS as [256 rows][32 k] and is read as K-contiguous fragments (ds_read_b128);
+//   - the weights stay N-contiguous in LDS ([32 k][columns], one region per matrix) and are read
+//     with the transposing ds_read_b64_tr_b16, which hands every lane 4 consecutive k of one column;
+//   - 16-byte chunks are XOR-swizzled inside each LDS row (the copy lanes pick their global source
+//     to match), so fragment reads hit distinct banks;
+//   - the barrier that opens K step kt + 1 sits before the last 16 MFMAs of step kt, with the first
+//     fragments of step kt + 1 requested behind it, so neither barrier nor LDS latency idles the
+//     matrix cores.
+// Small tiles (128 x 128, two workgroups per CU, other sizes): register-staged copies, the weights
+// transposed in registers with v_perm_b32 and stored K-contiguous, two LDS stages.
 #include "common.h"
 #include "internal.h"
 
@@ -173,6 +179,77 @@ __device__ __forceinline__ void k_loop(f32x16_t (&acc)[kTM][kTN], unsigned char*
     }
 }
 
+// The workgroup's next task: wave 0 claims it (every lane takes part, lane 0 adds 1, the others 0,
+// so no lane-divergent branch sits in the barrier loop: lane-divergent regions there let the
+// compiler's loop restructuring split one wave's lanes across different barrier paths).  Tasks are
+// dealt in blocks of `blk` (the workgroups of one XCD): block j belongs to XCD j % 8, and each XCD's
+// workgroups claim that XCD's tasks in order from its own counter.  Whatever the workgroups'
+// relative speeds, an XCD works on about `blk` consecutive tasks at a time (shared A rows and
+// weight strips in its L2), and overall progress follows task order.
+__device__ __forceinline__ int claim_task(int* claimed, int32_t* task_ctr, int xcd, int blk, int wave,
+                                          int lane)
+{
+    if (wave == 0) {
+        const int v = atomicAdd(&task_ctr[xcd], lane == 0 ? 1 : 0);
+        *claimed = __builtin_amdgcn_readfirstlane(v);
+    }
+    __syncthreads();
+    const int i = __builtin_amdgcn_readfirstlane(*claimed);   // one value per workgroup
+    return ((i / blk) * kXcdCount + xcd) * blk + i % blk;
+}
+
+// Task t belongs to the run holding row tile t / n_nt; inside the run, row tiles vary fastest.
+__device__ __forceinline__ MTile decode_task(int t, int n_nt, const MTile* __restrict__ tiles, int& nt)
+{
+    const MTile head = tiles[t / n_nt];
+    const int local = t - n_nt * head.run_begin;
+    nt = local / head.run_len;
+    return tiles[head.run_begin + local % head.run_len];
+}
+
+// Writes the wave's accumulators.  Lane holds column (lane % 32) of each 32 x 32 block, rows
+// 8 * (r / 4) + 4 * (lane / 32) + r % 4 for r = 0..15.  Gated: blocks j and j + 1 are the gate and
+// up halves of output columns 32 * ((wn * kTN + j) / 2) ..
+template <bool kGated, int kWM, int kTM, int kTN>
+__device__ __forceinline__ void store_output(const f32x16_t (&acc)[kTM][kTN], uint16_t* __restrict__ C,
+                                             const MTile& tile, int n0, int N_out, int wm, int wn,
+                                             int lane)
+{
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+        // keep the scheduler from pulling every accumulator into VGPRs at once
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = tile.row_begin + row_block<kWM>(i, wm) + 8 * (r >> 2) + 4 * (lane >> 5) +
+                            (r & 3);
+            if (row >= tile.row_end)
+                continue;
+            uint16_t* crow = C + static_cast<int64_t>(row) * N_out;
+            if (kGated) {
+#pragma unroll
+                for (int j = 0; j < kTN; j += 2) {
+                    const int q = (wn * kTN + j) / 2;
+                    crow[n0 + 32 * q + (lane & 31)] = f32_to_bf16(swiglu(acc[i][j][r], acc[i][j + 1][r]));
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < kTN; ++j)
+                    crow[n0 + wn * kTN * 32 + 32 * j + (lane & 31)] = f32_to_bf16(acc[i][j][r]);
+            }
+        }
+    }
+}
+
+// Counts a finished fc2 tile for its chunk (the whole first wave takes part; see claim_task).
+__device__ __forceinline__ void count_done(int32_t* chunk_done, int chunk, int wave, int lane)
+{
+    __threadfence();
+    __syncthreads();
+    if (wave == 0)
+        atomicAdd(&chunk_done[chunk], lane == 0 ? 1 : 0);
+}
+
 template <bool kGated, int kWM, int kWN, int kTM, int kTN, int kMinBlocks>
 __global__ __launch_bounds__(kWM * kWN * 64, kMinBlocks) void grouped_gemm_bf16(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
@@ -203,30 +280,14 @@ __global__ __launch_bounds__(kWM * kWN * 64, kMinBlocks) void grouped_gemm_bf16(
     const int cb = tid / kKGroups;              // 8-column chunk of the staged columns
     const int b0 = cb * 8;
 
-    // Tasks are dealt in blocks of `blk` (the workgroups of one XCD): block j belongs to XCD j % 8,
-    // and each XCD's workgroups claim that XCD's tasks in order from its own counter.  Whatever the
-    // workgroups' relative speeds, an XCD works on about `blk` consecutive tasks at a time (shared
-    // A rows and weight strips in its L2), and overall progress follows task order.
     const int xcd = blockIdx.x % kXcdCount;
     const int blk = gridDim.x / kXcdCount;
     for (;;) {
-        // Wave 0 claims the next task: every lane takes part (lane 0 adds 1, the others 0) so no
-        // lane-divergent branch sits in this barrier loop; lane-divergent regions here let the
-        // compiler's loop restructuring split one wave's lanes across different barrier paths.
-        if (wave == 0) {
-            const int v = atomicAdd(&task_ctr[xcd], lane == 0 ? 1 : 0);
-            claimed = __builtin_amdgcn_readfirstlane(v);
-        }
-        __syncthreads();
-        const int i = __builtin_amdgcn_readfirstlane(claimed);   // one value per workgroup
-        const int t = ((i / blk) * kXcdCount + xcd) * blk + i % blk;
+        const int t = claim_task(&claimed, task_ctr, xcd, blk, wave, lane);
         if (t >= total)
             break;
-        // task t belongs to the run holding row tile t / n_nt; inside the run, row tiles vary fastest
-        const MTile head = tiles[t / n_nt];
-        const int local = t - n_nt * head.run_begin;
-        const MTile tile = tiles[head.run_begin + local % head.run_len];
-        const int nt = local / head.run_len;
+        int nt;
+        const MTile tile = decode_task(t, n_nt, tiles, nt);
         const int n0 = nt * G::BN;
         // 32-row MFMA blocks of this wave that hold at least one row of the tile
         const int tile_blocks = (tile.row_end - tile.row_begin + 31) / 32;
@@ -264,69 +325,272 @@ __global__ __launch_bounds__(kWM * kWN * 64, kMinBlocks) void grouped_gemm_bf16(
                     acc[i][j][r] = 0.0f;
 
         switch (nb) {
-#define MOE_KLOOP(NB)                                                                               \
-    case NB:                                                                                        \
-        k_loop<G, kWM, kTM, kTN, (NB < kTM ? NB : kTM)>(acc, smem, A, aoff, bsrc, N_w, a_lds0, b0, \
-                                                         kg, KT, wm, wn, lane);                     \
-        break;
-            MOE_KLOOP(0) MOE_KLOOP(1) MOE_KLOOP(2) MOE_KLOOP(3)
-            default:
-                k_loop<G, kWM, kTM, kTN, kTM>(acc, smem, A, aoff, bsrc, N_w, a_lds0, b0, kg, KT,
-                                              wm, wn, lane);
-                break;
-#undef MOE_KLOOP
+        case 0: k_loop<G, kWM, kTM, kTN, 0>(acc, smem, A, aoff, bsrc, N_w, a_lds0, b0, kg, KT, wm, wn, lane); break;
+        case 1: k_loop<G, kWM, kTM, kTN, 1>(acc, smem, A, aoff, bsrc, N_w, a_lds0, b0, kg, KT, wm, wn, lane); break;
+        default: k_loop<G, kWM, kTM, kTN, kTM>(acc, smem, A, aoff, bsrc, N_w, a_lds0, b0, kg, KT, wm, wn, lane); break;
         }
-
-        // epilogue: lane holds column (lane % 32) of each 32x32 block, rows
-        // 8 * (r / 4) + 4 * (lane / 32) + r % 4 for r = 0..15
-#pragma unroll
-        for (int i = 0; i < kTM; ++i) {
-            // keep the scheduler from pulling every accumulator into VGPRs at once
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = tile.row_begin + row_block<kWM>(i, wm) + 8 * (r >> 2) +
-                                4 * (lane >> 5) + (r & 3);
-                if (row >= tile.row_end)
-                    continue;
-                uint16_t* crow = C + static_cast<int64_t>(row) * N_out;
-                if (kGated) {
-#pragma unroll
-                    for (int j = 0; j < kTN; j += 2) {
-                        const int q = (wn * kTN + j) / 2;
-                        crow[n0 + 32 * q + (lane & 31)] =
-                            f32_to_bf16(swiglu(acc[i][j][r], acc[i][j + 1][r]));
-                    }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < kTN; ++j)
-                        crow[n0 + wn * kTN * 32 + 32 * j + (lane & 31)] = f32_to_bf16(acc[i][j][r]);
-                }
-            }
-        }
-        if (chunk_done != nullptr) {
-            __threadfence();
-            __syncthreads();
-            if (wave == 0)
-                atomicAdd(&chunk_done[tile.chunk], lane == 0 ? 1 : 0);
-        }
+        store_output<kGated, kWM, kTM, kTN>(acc, C, tile, n0, N_out, wm, wn, lane);
+        if (chunk_done != nullptr)
+            count_done(chunk_done, tile.chunk, wave, lane);
     }
 }
 
-// Tile configurations.  Large: 4 waves (2 x 2), each 128 rows x 128 staged columns (16 accumulator
-// blocks of 32 x 32 per wave), one workgroup per CU, 128 KiB of LDS for the two stages; used when
-// H % 256 == 0 and F % 128 == 0.  Small: 4 waves of 64 x 64, two workgroups per CU, for other sizes
-// (H % 128 == 0, F % 64 == 0).
-using Fc1Big = Cfg<true, 2, 2, 4, 4, 1>;
-using Fc2Big = Cfg<false, 2, 2, 4, 4, 1>;
+// ------------------------------------------------------------------------------------------------
+// Large tiles with LDS DMA
+
+namespace big {
+constexpr int kWM = 2, kWN = 2, kTM = 4, kTN = 4;
+constexpr int kThreads = kWM * kWN * 64;
+constexpr int BM = kWM * kTM * 32;                     // 256 rows
+constexpr int BNB = kWN * kTN * 32;                    // 256 weight columns
+constexpr int BK = 32;
+constexpr int kStages = 4;
+constexpr int kABytes = BM * BK * 2;                   // [256 rows][32 k], 64-byte rows
+constexpr int kBBytes = BK * BNB * 2;                  // [32 k][256 columns] over 1 or 2 matrices
+constexpr int kStageBytes = kABytes + kBBytes;
+constexpr int kSmemBytes = kStages * kStageBytes;      // 128 KiB
+constexpr int kACopies = kABytes / 1024 / 4;           // 1 KiB copies per wave per K step
+constexpr int kBCopies = kBBytes / 1024 / 4;
+constexpr int kCopies = kACopies + kBCopies;
+
+template <bool kGated>
+struct BLayout {
+    static constexpr int kMats = kGated ? 2 : 1;
+    static constexpr int kRowBytes = BNB / kMats * 2;   // one k row of one matrix: 256 or 512 bytes
+    static constexpr int kChunks = kRowBytes / 16;      // 16-byte chunks per row
+    static constexpr int kRowsPerCopy = 64 / kChunks;
+    static constexpr int kMatBytes = BK * kRowBytes;
+    static_assert(kChunks >= 16, "the k-row swizzle uses chunk bits 2..3");
+};
+
+// LDS DMA of 16 bytes per lane: lane i reads base + voff (bytes) and writes LDS byte address
+// lds + 16 * i.  `base` and `lds` must be wave-uniform.  M0 carries the LDS address; no compiled
+// code keeps a live value in M0 across this statement (LDS instructions on this target do not use
+// it).  The copies count in vmcnt like any other vector-memory load.
+__device__ __forceinline__ void lds_copy16(const void* base, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(base), "s"(lds) : "memory");
+}
+
+// Waits until at most n K steps of this wave's copies are still in flight.
+__device__ __forceinline__ void wait_copies(int n)
+{
+    static_assert(kCopies * 3 <= 63, "vmcnt range");
+    switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kCopies) : "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * kCopies) : "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(%0)" :: "n"(3 * kCopies) : "memory"); break;
+    }
+}
+
+// A: LDS row r (64 bytes = 4 chunks of 8 k) keeps logical chunk c at position c ^ ((r >> 2) & 3):
+// 16 consecutive rows read at one chunk then cover all 16 bank groups of 16 bytes.
+// B: k row kr keeps 16-byte chunk c at c ^ (4 * (kr & 3)): the four k rows of one transposing read
+// group land 64 bytes apart within each 256-byte bank window.
+//
+// Copy j of wave w moves A rows 16 * (kACopies * w + j) .. + 15 (4 lanes per row) and B copy
+// slot bi (kRowsPerCopy k rows of one matrix).  The per-lane global offsets below already apply the
+// swizzle; rows past the tile's last row re-read its last row (their results are never stored).
+template <bool kGated>
+__device__ __forceinline__ void issue_step(int step, uint32_t lds0, const uint16_t* At,
+                                           const uint32_t (&a_voff)[kACopies], const uint16_t* Bm,
+                                           const uint32_t (&b_voff)[kBCopies], int wave, int64_t N_w)
+{
+    using L = BLayout<kGated>;
+    const uint32_t st = lds0 + static_cast<uint32_t>((step % kStages) * kStageBytes);
+    const uint16_t* a = At + step * BK;
+#pragma unroll
+    for (int j = 0; j < kACopies; ++j)
+        lds_copy16(a, a_voff[j], st + (kACopies * wave + j) * 1024);
+    const int bi0 = kGated ? kBCopies * (wave & 1) : kBCopies * wave;
+    const uint32_t bst = st + kABytes + (kGated ? (wave >> 1) * L::kMatBytes : 0);
+#pragma unroll
+    for (int j = 0; j < kBCopies; ++j) {
+        const uint16_t* b = Bm + static_cast<int64_t>(step * BK + (bi0 + j) * L::kRowsPerCopy) * N_w;
+        lds_copy16(b, b_voff[j], bst + (bi0 + j) * 1024);
+    }
+}
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// Fragments of k sub-step ks (16 of the step's 32 k): A row blocks 0..NB-1 and all kTN weight
+// column blocks.  a_lane / b_lane[j] are the lane parts of the addresses (see the kernel).
+template <bool kGated, int NB>
+__device__ __forceinline__ void frags(bf16x8_t (&af)[kTM], bf16x8_t (&bfr)[kTN], uint32_t stage,
+                                      const uint32_t (&a_lane)[2], const uint32_t (&b_lane)[kTN],
+                                      int wm, int ks)
+{
+    using L = BLayout<kGated>;
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+        af[i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
+            stage + a_lane[ks] + row_block<kWM>(i, wm) * 64);
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) {
+        const uint32_t p = stage + kABytes + b_lane[j] + 16 * ks * L::kRowBytes;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<lds_i16x4_t*>(p));
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<lds_i16x4_t*>(p + 4 * L::kRowBytes));
+        bfr[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+}
+
+template <bool kGated, int NB>
+__device__ __forceinline__ void k_loop(f32x16_t (&acc)[kTM][kTN], uint32_t lds0, const uint16_t* At,
+                                       const uint32_t (&a_voff)[kACopies], const uint16_t* Bm,
+                                       const uint32_t (&b_voff)[kBCopies], const uint32_t (&a_lane)[2],
+                                       const uint32_t (&b_lane)[kTN], int64_t N_w, int KT, int wave,
+                                       int wm)
+{
+    const int pre = KT < kStages ? KT : kStages;
+    for (int s = 0; s < pre; ++s)
+        issue_step<kGated>(s, lds0, At, a_voff, Bm, b_voff, wave, N_w);
+    wait_copies(pre - 1);
+    __syncthreads();
+    bf16x8_t af[2][kTM], bfr[2][kTN];
+    if constexpr (NB > 0)
+        frags<kGated, NB>(af[0], bfr[0], lds0, a_lane, b_lane, wm, 0);
+    for (int kt = 0; kt < KT; ++kt) {
+        const uint32_t stage = lds0 + static_cast<uint32_t>((kt % kStages) * kStageBytes);
+        if constexpr (NB > 0) {
+            frags<kGated, NB>(af[1], bfr[1], stage, a_lane, b_lane, wm, 1);
+            mfma_block<kTM, kTN, NB>(acc, af[0], bfr[0]);
+        }
+        if (kt + 1 < KT) {
+            // step kt + 1 landed (this wave's copies, then everyone's), and every wave is done
+            // reading stage kt % kStages, which the copies of step kt + kStages now refill
+            wait_copies(min(2, KT - 2 - kt));
+            __syncthreads();
+            if (kt + kStages < KT)
+                issue_step<kGated>(kt + kStages, lds0, At, a_voff, Bm, b_voff, wave, N_w);
+            if constexpr (NB > 0)
+                frags<kGated, NB>(af[0], bfr[0],
+                                  lds0 + static_cast<uint32_t>(((kt + 1) % kStages) * kStageBytes),
+                                  a_lane, b_lane, wm, 0);
+        }
+        if constexpr (NB > 0)
+            mfma_block<kTM, kTN, NB>(acc, af[1], bfr[1]);
+    }
+}
+
+template <bool kGated>
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, const MTile* __restrict__ tiles,
+    const int32_t* __restrict__ tile_count, int K, int N_out, int32_t* __restrict__ chunk_done,
+    int32_t* __restrict__ task_ctr)
+{
+    using L = BLayout<kGated>;
+    constexpr int BN = kGated ? BNB / 2 : BNB;
+    // dynamic LDS: kStages stages, then the claimed-task word
+    extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
+    int* const claimed = reinterpret_cast<int*>(smem + kSmemBytes);
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) unsigned char*)(smem)));
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / kWN;
+    const int wn = wave % kWN;
+    const int n_mt = *tile_count;
+    const int n_nt = N_out / BN;
+    const int total = n_mt * n_nt;
+    const int KT = K / BK;
+    const int64_t N_w = N_out;
+
+    // copy sources, lane parts (bytes): B copy j covers k rows kRowsPerCopy * (bi0 + j) + lane / kChunks
+    uint32_t b_voff[kBCopies];
+#pragma unroll
+    for (int j = 0; j < kBCopies; ++j) {
+        const int bi = (kGated ? kBCopies * (wave & 1) : kBCopies * wave) + j;
+        const int kr = bi * L::kRowsPerCopy + lane / L::kChunks;
+        const int c = (lane % L::kChunks) ^ (4 * (kr & 3));
+        b_voff[j] = static_cast<uint32_t>(lane / L::kChunks) * static_cast<uint32_t>(N_out) * 2u +
+                    16u * c;
+    }
+    // fragment reads, lane parts (LDS bytes from the stage base)
+    uint32_t a_lane[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const int r = lane & 31;
+        a_lane[ks] = r * 64 + 16 * ((2 * ks + (lane >> 5)) ^ ((r >> 2) & 3));
+    }
+    uint32_t b_lane[kTN];
+    {
+        const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
+        const int kr = 8 * (g >> 1) + e;                       // + 16 ks + 4 for the upper half
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            const int m = kGated ? (j & 1) : 0;
+            const int col = (kGated ? 64 * wn + 32 * (j >> 1) : 128 * wn + 32 * j) + 16 * (g & 1) + 4 * q;
+            b_lane[j] = m * L::kMatBytes + kr * L::kRowBytes + 16 * ((col >> 3) ^ (4 * e)) + 2 * (col & 7);
+        }
+    }
+
+    const int xcd = blockIdx.x % kXcdCount;
+    const int blk = gridDim.x / kXcdCount;
+    for (;;) {
+        const int t = claim_task(claimed, task_ctr, xcd, blk, wave, lane);
+        if (t >= total)
+            break;
+        int nt;
+        const MTile tile = decode_task(t, n_nt, tiles, nt);
+        const int n0 = nt * BN;
+        const int rows = tile.row_end - tile.row_begin;
+        const int nb = __builtin_amdgcn_readfirstlane(
+            min(kTM, max(0, ((rows + 31) / 32 - wm + kWM - 1) / kWM)));
+
+        const uint16_t* At = A + static_cast<int64_t>(tile.row_begin) * K;
+        uint32_t a_voff[kACopies];
+#pragma unroll
+        for (int j = 0; j < kACopies; ++j) {
+            const int r = 16 * (kACopies * wave + j) + lane / 4;
+            const int c = (lane & 3) ^ ((r >> 2) & 3);
+            a_voff[j] = static_cast<uint32_t>(min(r, rows - 1)) * static_cast<uint32_t>(K) * 2u + 16u * c;
+        }
+        const uint16_t* Bm = (kGated && (wave >> 1) ? B1 : B0) +
+                             static_cast<int64_t>(tile.expert) * K * N_w + n0;
+
+        f32x16_t acc[kTM][kTN];
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+            for (int j = 0; j < kTN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[i][j][r] = 0.0f;
+
+        switch (nb) {
+        case 0: k_loop<kGated, 0>(acc, lds0, At, a_voff, Bm, b_voff, a_lane, b_lane, N_w, KT, wave, wm); break;
+        case 1: k_loop<kGated, 1>(acc, lds0, At, a_voff, Bm, b_voff, a_lane, b_lane, N_w, KT, wave, wm); break;
+        case 2: k_loop<kGated, 2>(acc, lds0, At, a_voff, Bm, b_voff, a_lane, b_lane, N_w, KT, wave, wm); break;
+        case 3: k_loop<kGated, 3>(acc, lds0, At, a_voff, Bm, b_voff, a_lane, b_lane, N_w, KT, wave, wm); break;
+        default: k_loop<kGated, 4>(acc, lds0, At, a_voff, Bm, b_voff, a_lane, b_lane, N_w, KT, wave, wm); break;
+        }
+        store_output<kGated, kWM, kTM, kTN>(acc, C, tile, n0, N_out, wm, wn, lane);
+        if (chunk_done != nullptr)
+            count_done(chunk_done, tile.chunk, wave, lane);
+    }
+}
+}  // namespace big
+
+// Tile configurations.  Large (LDS DMA, above): one workgroup per CU, used when H % 256 == 0 and
+// F % 128 == 0.  Small: 4 waves of 64 x 64, two workgroups per CU, two register-staged LDS stages,
+// for other sizes (H % 128 == 0, F % 64 == 0).
 using Fc1Small = Cfg<true, 2, 2, 2, 2, 2>;
 using Fc2Small = Cfg<false, 2, 2, 2, 2, 2>;
-#define FC1_BIG grouped_gemm_bf16<true, 2, 2, 4, 4, 1>
-#define FC2_BIG grouped_gemm_bf16<false, 2, 2, 4, 4, 1>
 #define FC1_SMALL grouped_gemm_bf16<true, 2, 2, 2, 2, 2>
 #define FC2_SMALL grouped_gemm_bf16<false, 2, 2, 2, 2, 2>
+constexpr int kBigFc1Cols = big::BNB / 2;    // output columns per fc1 task
+constexpr int kBigFc2Cols = big::BNB;        // output columns per fc2 task
+constexpr int kBigSmem = big::kSmemBytes + 16;
 
-bool use_big(int64_t H, int64_t F) { return H % Fc2Big::BN == 0 && F % Fc1Big::BN == 0; }
+bool use_big(int64_t H, int64_t F) { return H % kBigFc2Cols == 0 && F % kBigFc1Cols == 0; }
 
 hipError_t ensure_smem_limits()
 {
@@ -337,11 +601,11 @@ hipError_t ensure_smem_limits()
         return e;
     if (dev < 64 && done[dev])
         return hipSuccess;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&FC1_BIG),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, Fc1Big::kSmemBytes);
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&big::grouped_gemm_bf16_dma<true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kBigSmem);
     if (e == hipSuccess)
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&FC2_BIG),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, Fc2Big::kSmemBytes);
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&big::grouped_gemm_bf16_dma<false>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kBigSmem);
     if (e == hipSuccess && dev < 64)
         done[dev] = true;
     return e;
@@ -349,8 +613,8 @@ hipError_t ensure_smem_limits()
 
 }  // namespace
 
-int bf16_row_tile(int64_t H, int64_t F) { return use_big(H, F) ? Fc1Big::BM : Fc1Small::BM; }
-int bf16_fc2_cols_per_tile(int64_t H, int64_t F) { return use_big(H, F) ? Fc2Big::BN : Fc2Small::BN; }
+int bf16_row_tile(int64_t H, int64_t F) { return use_big(H, F) ? big::BM : Fc1Small::BM; }
+int bf16_fc2_cols_per_tile(int64_t H, int64_t F) { return use_big(H, F) ? kBigFc2Cols : Fc2Small::BN; }
 bool bf16_supported(int64_t H, int64_t F) { return H % Fc2Small::BN == 0 && F % Fc1Small::BN == 0; }
 
 hipError_t launch_fc1_bf16(const uint16_t* A, const uint16_t* wg, const uint16_t* wu, uint16_t* h,
@@ -361,7 +625,7 @@ hipError_t launch_fc1_bf16(const uint16_t* A, const uint16_t* wg, const uint16_t
     if (use_big(H, F)) {
         if (hipError_t e = ensure_smem_limits(); e != hipSuccess)
             return e;
-        FC1_BIG<<<dim3(cu), dim3(Fc1Big::kThreads), Fc1Big::kSmemBytes, s>>>(
+        big::grouped_gemm_bf16_dma<true><<<dim3(cu), dim3(big::kThreads), kBigSmem, s>>>(
             A, wg, wu, h, tiles, tile_count, static_cast<int>(H), static_cast<int>(F), nullptr,
             task_ctr);
     } else {
@@ -380,7 +644,7 @@ hipError_t launch_fc2_bf16(const uint16_t* h, const uint16_t* wd, uint16_t* y, c
     if (use_big(H, F)) {
         if (hipError_t e = ensure_smem_limits(); e != hipSuccess)
             return e;
-        FC2_BIG<<<dim3(cu), dim3(Fc2Big::kThreads), Fc2Big::kSmemBytes, s>>>(
+        big::grouped_gemm_bf16_dma<false><<<dim3(cu), dim3(big::kThreads), kBigSmem, s>>>(
             h, wd, nullptr, y, tiles, tile_count, static_cast<int>(F), static_cast<int>(H),
             chunk_done, task_ctr);
     } else {

@@ -142,6 +142,9 @@ CASES = [
     ("bf16_ragged_tail", "bf16", 333, 384, 192, 6, 2, {}),
     ("bf16_finegrained_like", "bf16", 256, 256, 128, 32, 8,
      {"routing": "zipf_gumbel", "zipf_s": 1.1, "n_zero": 4}),
+    # large-tile path (H % 256 == 0, F % 128 == 0): several K steps, column tiles and ragged tiles
+    ("bf16_large_tiles_ragged", "bf16", 700, 512, 384, 6, 2, {}),
+    ("bf16_large_tiles_deep_k", "bf16", 300, 1024, 640, 3, 2, {}),
 ]
 
 
@@ -161,19 +164,21 @@ def test_forward_matches_oracle(name, dtype, T, H, F, E, k, kw):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("head", [256, 512])
-def test_chunked_equals_unchunked(dtype, head):
-    inp = synth.make_layer(T=700, H=128, F=192, E=5, k=2, dtype=dtype, seed=3)
+@pytest.mark.parametrize("T,H,F", [(700, 128, 192), (1100, 256, 256)], ids=["small_tiles", "large_tiles"])
+def test_chunked_equals_unchunked(dtype, head, T, H, F):
+    if dtype == "f32" and H > 128:
+        pytest.skip("tile shapes are a bf16 matter")
+    inp = synth.make_layer(T=T, H=H, F=F, E=5, k=2, dtype=dtype, seed=3)
+    code = mel.F32 if dtype == "f32" else mel.BF16
     d = dv.layer(inp)
     base = dv.host(dv.forward(mel, d, 0))
-    ws = torch.empty(mel.workspace_size(mel.problem(700, 128, 192, 5, 2,
-                                                    mel.F32 if dtype == "f32" else mel.BF16,
-                                                    head)), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(mel.workspace_size(mel.problem(T, H, F, 5, 2, code, head)),
+                     dtype=torch.uint8, device="cuda")
     out = dv.host(dv.forward(mel, d, head, workspace=ws))
     assert np.array_equal(out, base)
-    done, expected = mel.chunk_counters(ws, 1400, 128, 192, head,
-                                        mel.F32 if dtype == "f32" else mel.BF16)
+    done, expected = mel.chunk_counters(ws, 2 * T, H, F, head, code)
     torch.cuda.synchronize()
-    assert done.shape[0] == -(-1400 // head)
+    assert done.shape[0] == -(-2 * T // head)
     assert np.array_equal(dv.host(done), dv.host(expected)) and dv.host(expected).min() > 0
 
 
