@@ -24,11 +24,8 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b)
 // float32 -> bfloat16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return static_cast<uint16_t>((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    // v_cvt_pk_bf16_f32: round to nearest even, NaN stays NaN
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
@@ -37,11 +34,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 }
 
 // SwiGLU ("NPU Training Operators - MC2", 执行路径 step 8): silu(g) * u with silu(z) = z / (1 + e^-z).
-// e^-z is computed as 2^(-z log2 e) on the hardware exp2 unit.
+// e^-z is computed as 2^(-z log2 e) on the hardware exp2 unit and the quotient through the hardware
+// reciprocal (1 ulp).
 __device__ __forceinline__ float swiglu(float g, float u)
 {
     const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
-    return g / (1.0f + e) * u;
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
 // floor(log2(a)) of a positive finite float, exact (handles subnormals).

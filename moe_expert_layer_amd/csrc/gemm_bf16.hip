@@ -29,6 +29,8 @@
 //     matrix cores.
 // Small tiles (128 x 128, two workgroups per CU, other sizes): register-staged copies, the weights
 // transposed in registers with v_perm_b32 and stored K-contiguous, two LDS stages.
+#include <utility>
+
 #include "common.h"
 #include "internal.h"
 
@@ -348,7 +350,10 @@ constexpr int kStages = 4;
 constexpr int kABytes = BM * BK * 2;                   // [256 rows][32 k], 64-byte rows
 constexpr int kBBytes = BK * BNB * 2;                  // [32 k][256 columns] over 1 or 2 matrices
 constexpr int kStageBytes = kABytes + kBBytes;
-constexpr int kSmemBytes = kStages * kStageBytes;      // 128 KiB
+constexpr int kRingBytes = kStages * kStageBytes;      // 128 KiB
+constexpr int kOutRows = 64;                           // epilogue staging: 64 rows x 64 columns
+constexpr int kOutWaveBytes = kOutRows * 128;          //   of bf16 per wave (8 KiB)
+constexpr int kSmemBytes = kRingBytes + 4 * kOutWaveBytes;   // 160 KiB, the whole LDS of a CU
 constexpr int kACopies = kABytes / 1024 / 4;           // 1 KiB copies per wave per K step
 constexpr int kBCopies = kBBytes / 1024 / 4;
 constexpr int kCopies = kACopies + kBCopies;
@@ -363,25 +368,29 @@ struct BLayout {
     static_assert(kChunks >= 16, "the k-row swizzle uses chunk bits 2..3");
 };
 
-// LDS DMA of 16 bytes per lane: lane i reads base + voff (bytes) and writes LDS byte address
-// lds + 16 * i.  `base` and `lds` must be wave-uniform.  M0 carries the LDS address; no compiled
-// code keeps a live value in M0 across this statement (LDS instructions on this target do not use
-// it).  The copies count in vmcnt like any other vector-memory load.
+// LDS DMA of 16 bytes per lane (global_load_lds_dwordx4): lane i reads base + voff (bytes) and
+// writes LDS byte address lds + 16 * i.  `base` and `lds` must be wave-uniform.  M0 carries the
+// LDS address; no compiled code keeps a live value in M0 across this statement (LDS instructions on
+// this target do not use it).  The copies count in vmcnt like any other vector-memory load, and
+// the waits for them are explicit (step_barrier).  Written as inline assembly: the compiler's own
+// form of this instruction makes every later LDS read wait for all copies in flight.
 __device__ __forceinline__ void lds_copy16(const void* base, uint32_t voff, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :: "v"(voff), "s"(base), "s"(lds) : "memory");
 }
 
-// Waits until at most n K steps of this wave's copies are still in flight.
-__device__ __forceinline__ void wait_copies(int n)
+// Waits until at most n K steps of this wave's copies are still in flight, and for this wave's LDS
+// reads, then joins the workgroup barrier.  One statement with a memory clobber: no memory
+// operation moves across it.
+__device__ __forceinline__ void step_barrier(int n)
 {
     static_assert(kCopies * 3 <= 63, "vmcnt range");
     switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kCopies) : "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * kCopies) : "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(%0)" :: "n"(3 * kCopies) : "memory"); break;
+    case 0: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(kCopies) : "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(2 * kCopies) : "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(3 * kCopies) : "memory"); break;
     }
 }
 
@@ -393,50 +402,169 @@ __device__ __forceinline__ void wait_copies(int n)
 // Copy j of wave w moves A rows 16 * (kACopies * w + j) .. + 15 (4 lanes per row) and B copy
 // slot bi (kRowsPerCopy k rows of one matrix).  The per-lane global offsets below already apply the
 // swizzle; rows past the tile's last row re-read its last row (their results are never stored).
+// Uniform addresses of this wave's copies of one K step (lane parts in a_voff / b_voff).
+struct StepCopies {
+    const uint16_t* a;     // A source of the step
+    const uint16_t* b;     // weight source of the wave's first B copy
+    uint32_t a_lds;        // LDS destination of the wave's first A copy
+    uint32_t b_lds;        // LDS destination of the wave's first B copy
+    bool on;
+};
+
 template <bool kGated>
-__device__ __forceinline__ void issue_step(int step, uint32_t lds0, const uint16_t* At,
-                                           const uint32_t (&a_voff)[kACopies], const uint16_t* Bm,
-                                           const uint32_t (&b_voff)[kBCopies], int wave, int64_t N_w)
+__device__ __forceinline__ StepCopies step_copies(int step, uint32_t lds0, const uint16_t* At,
+                                                  const uint16_t* Bm, int wave, int64_t N_w)
 {
     using L = BLayout<kGated>;
     const uint32_t st = lds0 + static_cast<uint32_t>((step % kStages) * kStageBytes);
-    const uint16_t* a = At + step * BK;
-#pragma unroll
-    for (int j = 0; j < kACopies; ++j)
-        lds_copy16(a, a_voff[j], st + (kACopies * wave + j) * 1024);
     const int bi0 = kGated ? kBCopies * (wave & 1) : kBCopies * wave;
-    const uint32_t bst = st + kABytes + (kGated ? (wave >> 1) * L::kMatBytes : 0);
-#pragma unroll
-    for (int j = 0; j < kBCopies; ++j) {
-        const uint16_t* b = Bm + static_cast<int64_t>(step * BK + (bi0 + j) * L::kRowsPerCopy) * N_w;
-        lds_copy16(b, b_voff[j], bst + (bi0 + j) * 1024);
+    StepCopies c;
+    c.a = At + step * BK;
+    c.a_lds = st + kACopies * wave * 1024;
+    c.b = Bm + static_cast<int64_t>(step * BK + bi0 * L::kRowsPerCopy) * N_w;
+    c.b_lds = st + kABytes + (kGated ? (wave >> 1) * L::kMatBytes : 0) + bi0 * 1024;
+    return c;
+}
+
+// Copy C (0 .. kCopies - 1) of a step: A copies first, then B copies.
+template <bool kGated, int C>
+__device__ __forceinline__ void copy_one(const StepCopies& s, const uint32_t (&a_voff)[kACopies],
+                                         const uint32_t (&b_voff)[kBCopies], int64_t N_w)
+{
+    if (!s.on) return;
+    if constexpr (C < kACopies) {
+        lds_copy16(s.a, a_voff[C], s.a_lds + C * 1024);
+    } else {
+        constexpr int j = C - kACopies;
+        lds_copy16(s.b + j * BLayout<kGated>::kRowsPerCopy * N_w, b_voff[j], s.b_lds + j * 1024);
     }
+}
+
+template <bool kGated, int C0, int... Is>
+__device__ __forceinline__ void copies_impl(std::integer_sequence<int, Is...>, const StepCopies& s,
+                                            const uint32_t (&a_voff)[kACopies],
+                                            const uint32_t (&b_voff)[kBCopies], int64_t N_w)
+{
+    (copy_one<kGated, C0 + Is>(s, a_voff, b_voff, N_w), ...);
+}
+
+// Copies C0 .. C1 - 1 of a step.
+template <bool kGated, int C0, int C1>
+__device__ __forceinline__ void copies(const StepCopies& s, const uint32_t (&a_voff)[kACopies],
+                                       const uint32_t (&b_voff)[kBCopies], int64_t N_w)
+{
+    copies_impl<kGated, C0>(std::make_integer_sequence<int, C1 - C0>{}, s, a_voff, b_voff, N_w);
 }
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-// Fragments of k sub-step ks (16 of the step's 32 k): A row blocks 0..NB-1 and all kTN weight
-// column blocks.  a_lane / b_lane[j] are the lane parts of the addresses (see the kernel).
-template <bool kGated, int NB>
-__device__ __forceinline__ void frags(bf16x8_t (&af)[kTM], bf16x8_t (&bfr)[kTN], uint32_t stage,
-                                      const uint32_t (&a_lane)[2], const uint32_t (&b_lane)[kTN],
-                                      int wm, int ks)
+// MFMA operands of one k sub-step (16 k): A row blocks and weight column blocks.
+struct Frags {
+    bf16x8_t a[kTM];
+    bf16x8_t b[kTN];
+    i16x4_t lo[kTN];       // first half of b[j] until its second half arrives
+};
+
+// Fragment read Q of a sub-step: Q = 2 j, 2 j + 1 are the two transposing reads (k 0..3, 4..7 of
+// the lane's 8) of weight block j; Q = 2 kTN + i is A row block i.  a_lane / b_lane[j] are the
+// lane parts of the addresses (see the kernel).
+template <bool kGated, int Q>
+__device__ __forceinline__ void read_one(Frags& f, uint32_t stage, const uint32_t (&a_lane)[2],
+                                         const uint32_t (&b_lane)[kTN], int wm, int ks)
 {
     using L = BLayout<kGated>;
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-        af[i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
+    if constexpr (Q < 2 * kTN) {
+        constexpr int j = Q / 2;
+        const uint32_t p = stage + kABytes + b_lane[j] + 16 * ks * L::kRowBytes + (Q % 2) * 4 * L::kRowBytes;
+        const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4_t*>(p));
+        if constexpr (Q % 2 == 0)
+            f.lo[j] = v;
+        else
+            f.b[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(f.lo[j], v, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+        constexpr int i = Q - 2 * kTN;
+        f.a[i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
             stage + a_lane[ks] + row_block<kWM>(i, wm) * 64);
-#pragma unroll
-    for (int j = 0; j < kTN; ++j) {
-        const uint32_t p = stage + kABytes + b_lane[j] + 16 * ks * L::kRowBytes;
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<lds_i16x4_t*>(p));
-        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<lds_i16x4_t*>(p + 4 * L::kRowBytes));
-        bfr[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
+}
+
+template <bool kGated, int Q0, int... Is>
+__device__ __forceinline__ void reads_impl(std::integer_sequence<int, Is...>, Frags& f, uint32_t stage,
+                                           const uint32_t (&a_lane)[2], const uint32_t (&b_lane)[kTN],
+                                           int wm, int ks)
+{
+    (read_one<kGated, Q0 + Is>(f, stage, a_lane, b_lane, wm, ks), ...);
+}
+
+template <bool kGated, int Q0, int Q1>
+__device__ __forceinline__ void reads(Frags& f, uint32_t stage, const uint32_t (&a_lane)[2],
+                                      const uint32_t (&b_lane)[kTN], int wm, int ks)
+{
+    reads_impl<kGated, Q0>(std::make_integer_sequence<int, Q1 - Q0>{}, f, stage, a_lane, b_lane, wm, ks);
+}
+
+// Everything a sub-step needs besides the fragments.
+struct SubstepCtx {
+    uint32_t stage;        // LDS stage whose fragments are read
+    int ks;                // sub-step of those fragments
+    StepCopies cp;         // copies issued during this sub-step (when NC > 0)
+};
+
+// Slot M of a sub-step: MFMA M (row block M / kTN, column block M % kTN), then this slot's share of
+// the next sub-step's fragment reads and of the step's copies.  Reads and copies are spread evenly
+// over the MFMAs, so the wave's in-order issue never stalls on a burst of memory instructions, and
+// no MFMA waits for a read issued just before it.
+template <bool kGated, int NB, int NC, int M>
+__device__ __forceinline__ void slot(f32x16_t (&acc)[kTM][kTN], const Frags& use, Frags& load,
+                                     const SubstepCtx& c, const uint32_t (&a_lane)[2],
+                                     const uint32_t (&b_lane)[kTN], const uint32_t (&a_voff)[kACopies],
+                                     const uint32_t (&b_voff)[kBCopies], int64_t N_w, int wm)
+{
+    constexpr int NM = NB * kTN, NR = 2 * kTN + NB;
+    acc[M / kTN][M % kTN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(use.a[M / kTN], use.b[M % kTN],
+                                                                    acc[M / kTN][M % kTN], 0, 0, 0);
+    reads<kGated, M * NR / NM, (M + 1) * NR / NM>(load, c.stage, a_lane, b_lane, wm, c.ks);
+    copies<kGated, M * NC / NM, (M + 1) * NC / NM>(c.cp, a_voff, b_voff, N_w);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool kGated, int NB, int NC, int... Ms>
+__device__ __forceinline__ void slots(std::integer_sequence<int, Ms...>, f32x16_t (&acc)[kTM][kTN],
+                                      const Frags& use, Frags& load, const SubstepCtx& c,
+                                      const uint32_t (&a_lane)[2], const uint32_t (&b_lane)[kTN],
+                                      const uint32_t (&a_voff)[kACopies],
+                                      const uint32_t (&b_voff)[kBCopies], int64_t N_w, int wm)
+{
+    (slot<kGated, NB, NC, Ms>(acc, use, load, c, a_lane, b_lane, a_voff, b_voff, N_w, wm), ...);
+}
+
+// One k sub-step: the NB * kTN MFMAs on `use`, the fragment reads of sub-step c.ks of c.stage into
+// `load`, and NC copies of c.cp.  A wave without MFMAs (NB = 0) only issues the copies.
+template <bool kGated, int NB, int NC>
+__device__ __forceinline__ void substep(f32x16_t (&acc)[kTM][kTN], const Frags& use, Frags& load,
+                                        const SubstepCtx& c, const uint32_t (&a_lane)[2],
+                                        const uint32_t (&b_lane)[kTN], const uint32_t (&a_voff)[kACopies],
+                                        const uint32_t (&b_voff)[kBCopies], int64_t N_w, int wm)
+{
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NB == 0)
+        copies<kGated, 0, NC>(c.cp, a_voff, b_voff, N_w);
+    else
+        slots<kGated, NB, NC>(std::make_integer_sequence<int, NB * kTN>{}, acc, use, load, c, a_lane,
+                              b_lane, a_voff, b_voff, N_w, wm);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Issues all copies of one K step (task prologue).
+template <bool kGated>
+__device__ __forceinline__ void issue_step(int step, uint32_t lds0, const uint16_t* At,
+                                           const uint32_t (&a_voff)[kACopies], const uint16_t* Bm,
+                                           const uint32_t (&b_voff)[kBCopies], int wave, int64_t N_w)
+{
+    StepCopies c = step_copies<kGated>(step, lds0, At, Bm, wave, N_w);
+    c.on = true;
+    copies<kGated, 0, kCopies>(c, a_voff, b_voff, N_w);
 }
 
 template <bool kGated, int NB>
@@ -446,34 +574,79 @@ __device__ __forceinline__ void k_loop(f32x16_t (&acc)[kTM][kTN], uint32_t lds0,
                                        const uint32_t (&b_lane)[kTN], int64_t N_w, int KT, int wave,
                                        int wm)
 {
-    const int pre = KT < kStages ? KT : kStages;
-    for (int s = 0; s < pre; ++s)
-        issue_step<kGated>(s, lds0, At, a_voff, Bm, b_voff, wave, N_w);
-    wait_copies(pre - 1);
-    __syncthreads();
-    bf16x8_t af[2][kTM], bfr[2][kTN];
+    // the caller issued the copies of steps 0 .. min(KT, kStages) - 1
+    step_barrier((KT < kStages ? KT : kStages) - 1);
+    Frags f0, f1;
+    SubstepCtx c{lds0, 0, {}};
     if constexpr (NB > 0)
-        frags<kGated, NB>(af[0], bfr[0], lds0, a_lane, b_lane, wm, 0);
+        reads<kGated, 0, 2 * kTN + NB>(f0, lds0, a_lane, b_lane, wm, 0);
     for (int kt = 0; kt < KT; ++kt) {
-        const uint32_t stage = lds0 + static_cast<uint32_t>((kt % kStages) * kStageBytes);
-        if constexpr (NB > 0) {
-            frags<kGated, NB>(af[1], bfr[1], stage, a_lane, b_lane, wm, 1);
-            mfma_block<kTM, kTN, NB>(acc, af[0], bfr[0]);
-        }
+        c.stage = lds0 + static_cast<uint32_t>((kt % kStages) * kStageBytes);
+        c.ks = 1;
+        substep<kGated, NB, 0>(acc, f0, f1, c, a_lane, b_lane, a_voff, b_voff, N_w, wm);
         if (kt + 1 < KT) {
             // step kt + 1 landed (this wave's copies, then everyone's), and every wave is done
-            // reading stage kt % kStages, which the copies of step kt + kStages now refill
-            wait_copies(min(2, KT - 2 - kt));
-            __syncthreads();
-            if (kt + kStages < KT)
-                issue_step<kGated>(kt + kStages, lds0, At, a_voff, Bm, b_voff, wave, N_w);
-            if constexpr (NB > 0)
-                frags<kGated, NB>(af[0], bfr[0],
-                                  lds0 + static_cast<uint32_t>(((kt + 1) % kStages) * kStageBytes),
-                                  a_lane, b_lane, wm, 0);
+            // reading stage kt % kStages, which the copies of step kt + kStages may now refill
+            step_barrier(min(2, KT - 2 - kt));
         }
-        if constexpr (NB > 0)
-            mfma_block<kTM, kTN, NB>(acc, af[1], bfr[1]);
+        // after the last step this reads a stale stage whose fragments are never used
+        c.stage = lds0 + static_cast<uint32_t>(((kt + 1) % kStages) * kStageBytes);
+        c.ks = 0;
+        c.cp = step_copies<kGated>(kt + kStages, lds0, At, Bm, wave, N_w);
+        c.cp.on = kt + kStages < KT;
+        substep<kGated, NB, kCopies>(acc, f1, f0, c, a_lane, b_lane, a_voff, b_voff, N_w, wm);
+    }
+}
+
+// Epilogue through LDS.  The wave's output (128 rows x 64 columns for fc1, 128 x 128 for fc2) goes
+// out in 64 x 64 pieces: the accumulators are written to the wave's staging area as bf16 (2-byte
+// LDS writes, rows of 128 bytes with 16-byte chunks XOR-swizzled by row), then read back as
+// 16-byte row chunks and stored to global memory 16 bytes per lane.  Only this wave touches its
+// area, and LDS operations of one wave complete in order, so no barrier is needed.
+template <bool kGated>
+__device__ __forceinline__ void store_output_staged(const f32x16_t (&acc)[kTM][kTN], uint16_t* __restrict__ C,
+                                                    const MTile& tile, int n0, int N_out, uint32_t stage,
+                                                    int wm, int wn, int lane)
+{
+    constexpr int kColPieces = kGated ? 1 : 2;     // 64-column pieces per wave
+#pragma unroll
+    for (int rp = 0; rp < kTM / 2; ++rp) {          // row blocks 2 rp, 2 rp + 1
+#pragma unroll
+        for (int cp = 0; cp < kColPieces; ++cp) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii) {
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float v;
+                        if constexpr (kGated) {
+                            const int j = 2 * jj;            // gate block j, up block j + 1
+                            v = swiglu(acc[2 * rp + ii][j][r], acc[2 * rp + ii][j + 1][r]);
+                        } else {
+                            v = acc[2 * rp + ii][2 * cp + jj][r];
+                        }
+                        const int row = 32 * ii + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                        const int col = 32 * jj + (lane & 31);
+                        const uint32_t a = stage + row * 128 + ((((col >> 3) ^ row) & 7) << 4) + 2 * (col & 7);
+                        *reinterpret_cast<__attribute__((address_space(3))) uint16_t*>(a) = f32_to_bf16(v);
+                    }
+                }
+            }
+            // 64 rows x 8 chunks of 16 bytes: lane reads chunk (lane % 8) of rows lane / 8 + 8 m
+            const int chunk = lane & 7;
+            const int col0 = kGated ? n0 + 64 * wn + 8 * chunk : n0 + 128 * wn + 64 * cp + 8 * chunk;
+#pragma unroll
+            for (int m = 0; m < kOutRows / 8; ++m) {
+                const int row = (lane >> 3) + 8 * m;
+                const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
+                    stage + row * 128 + (((chunk ^ row) & 7) << 4));
+                const int grow = tile.row_begin + 32 * (2 * (2 * rp + (row >> 5)) + wm) + (row & 31);
+                if (grow < tile.row_end)
+                    *reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(grow) * N_out + col0) = v;
+            }
+        }
     }
 }
 
@@ -486,9 +659,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
 {
     using L = BLayout<kGated>;
     constexpr int BN = kGated ? BNB / 2 : BNB;
-    // dynamic LDS: kStages stages, then the claimed-task word
+    // dynamic LDS: the kStages-stage ring, then each wave's epilogue staging area.  The claimed-task
+    // word sits at the start of wave 0's area: it is written by wave 0 only, read by every wave
+    // before any epilogue starts, and wave 0 overwrites it only after its own epilogue.
     extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
-    int* const claimed = reinterpret_cast<int*>(smem + kSmemBytes);
+    int* const claimed = reinterpret_cast<int*>(smem + kRingBytes);
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
         (__attribute__((address_space(3))) unsigned char*)(smem)));
 
@@ -534,27 +709,44 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
 
     const int xcd = blockIdx.x % kXcdCount;
     const int blk = gridDim.x / kXcdCount;
-    for (;;) {
-        const int t = claim_task(claimed, task_ctr, xcd, blk, wave, lane);
-        if (t >= total)
-            break;
-        int nt;
-        const MTile tile = decode_task(t, n_nt, tiles, nt);
-        const int n0 = nt * BN;
-        const int rows = tile.row_end - tile.row_begin;
-        const int nb = __builtin_amdgcn_readfirstlane(
-            min(kTM, max(0, ((rows + 31) / 32 - wm + kWM - 1) / kWM)));
 
-        const uint16_t* At = A + static_cast<int64_t>(tile.row_begin) * K;
-        uint32_t a_voff[kACopies];
+    // Task state.  The copies of a task's first K steps are issued before the previous task's
+    // epilogue, so the epilogue hides their latency.
+    MTile tile{};
+    int n0 = 0;
+    const uint16_t* At = A;
+    const uint16_t* Bm = B0;
+    uint32_t a_voff[kACopies];
+    auto setup = [&](int t) {
+        int nt;
+        tile = decode_task(t, n_nt, tiles, nt);
+        n0 = nt * BN;
+        const int rows = tile.row_end - tile.row_begin;
+        At = A + static_cast<int64_t>(tile.row_begin) * K;
 #pragma unroll
         for (int j = 0; j < kACopies; ++j) {
             const int r = 16 * (kACopies * wave + j) + lane / 4;
             const int c = (lane & 3) ^ ((r >> 2) & 3);
             a_voff[j] = static_cast<uint32_t>(min(r, rows - 1)) * static_cast<uint32_t>(K) * 2u + 16u * c;
         }
-        const uint16_t* Bm = (kGated && (wave >> 1) ? B1 : B0) +
-                             static_cast<int64_t>(tile.expert) * K * N_w + n0;
+        Bm = (kGated && (wave >> 1) ? B1 : B0) + static_cast<int64_t>(tile.expert) * K * N_w + n0;
+        const int pre = KT < kStages ? KT : kStages;
+        for (int st = 0; st < pre; ++st)
+            issue_step<kGated>(st, lds0, At, a_voff, Bm, b_voff, wave, N_w);
+    };
+
+    int t = claim_task(claimed, task_ctr, xcd, blk, wave, lane);
+    if (t < total)
+        setup(t);
+    while (t < total) {
+        // claim the following task now; the other waves read the claim after this task's barriers
+        if (wave == 0) {
+            const int v = atomicAdd(&task_ctr[xcd], lane == 0 ? 1 : 0);
+            *claimed = __builtin_amdgcn_readfirstlane(v);
+        }
+        const int rows = tile.row_end - tile.row_begin;
+        const int nb = __builtin_amdgcn_readfirstlane(
+            min(kTM, max(0, ((rows + 31) / 32 - wm + kWM - 1) / kWM)));
 
         f32x16_t acc[kTM][kTN];
 #pragma unroll
@@ -572,9 +764,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
         case 3: k_loop<kGated, 3>(acc, lds0, At, a_voff, Bm, b_voff, a_lane, b_lane, N_w, KT, wave, wm); break;
         default: k_loop<kGated, 4>(acc, lds0, At, a_voff, Bm, b_voff, a_lane, b_lane, N_w, KT, wave, wm); break;
         }
-        store_output<kGated, kWM, kTM, kTN>(acc, C, tile, n0, N_out, wm, wn, lane);
+        const MTile done = tile;
+        const int done_n0 = n0;
+        const int i = __builtin_amdgcn_readfirstlane(*claimed);
+        t = ((i / blk) * kXcdCount + xcd) * blk + i % blk;
+        // every wave is past its last read of this task's stages (and of the claim word)
+        __syncthreads();
+        if (t < total)
+            setup(t);
+        store_output_staged<kGated>(acc, C, done, done_n0, N_out, lds0 + kRingBytes + wave * kOutWaveBytes,
+                                     wm, wn, lane);
         if (chunk_done != nullptr)
-            count_done(chunk_done, tile.chunk, wave, lane);
+            count_done(chunk_done, done.chunk, wave, lane);
     }
 }
 }  // namespace big
@@ -588,7 +789,7 @@ using Fc2Small = Cfg<false, 2, 2, 2, 2, 2>;
 #define FC2_SMALL grouped_gemm_bf16<false, 2, 2, 2, 2, 2>
 constexpr int kBigFc1Cols = big::BNB / 2;    // output columns per fc1 task
 constexpr int kBigFc2Cols = big::BNB;        // output columns per fc2 task
-constexpr int kBigSmem = big::kSmemBytes + 16;
+constexpr int kBigSmem = big::kSmemBytes;
 
 bool use_big(int64_t H, int64_t F) { return H % kBigFc2Cols == 0 && F % kBigFc1Cols == 0; }
 
