@@ -15,7 +15,8 @@
 // rows and a handful of weight strips in their L2.  In a partial row tile, 32-row MFMA blocks that
 // lie wholly past the tile's last row are skipped (the condition is uniform per wave).
 //
-// Large tiles (256 rows x 256 weight columns, 4 waves of 128 x 128; H % 256 == 0, F % 128 == 0):
+// Large tiles (256 rows x 256 weight columns, 8 waves of 64 x 128, two per SIMD; H % 256 == 0,
+// F % 128 == 0):
 //   - global -> LDS copies bypass registers (global_load_lds_dwordx4: each lane moves 16 bytes to
 //     LDS at the wave's base + 16 * lane); four LDS stages of 32 values of K, so the copies of three
 //     K steps are in flight while one is multiplied;
@@ -24,9 +25,12 @@
 //     with the transposing ds_read_b64_tr_b16, which hands every lane 4 consecutive k of one column;
 //   - 16-byte chunks are XOR-swizzled inside each LDS row (the copy lanes pick their global source
 //     to match), so fragment reads hit distinct banks;
-//   - the barrier that opens K step kt + 1 sits before the last 16 MFMAs of step kt, with the first
-//     fragments of step kt + 1 requested behind it, so neither barrier nor LDS latency idles the
-//     matrix cores.
+//   - inside a k sub-step every MFMA is followed by its share of the next sub-step's fragment reads
+//     and of the copies, and the barrier that opens K step kt + 1 sits between the two sub-steps of
+//     step kt, so neither barrier nor LDS latency idles the matrix cores;
+//   - the workgroup claims its next task while working on the current one and issues that task's
+//     first copies before the current epilogue, which writes through a per-wave LDS staging area
+//     as 16-byte stores.
 // Small tiles (128 x 128, two workgroups per CU, other sizes): register-staged copies, the weights
 // transposed in registers with v_perm_b32 and stored K-contiguous, two LDS stages.
 #include <utility>
@@ -341,8 +345,9 @@ __global__ __launch_bounds__(kWM * kWN * 64, kMinBlocks) void grouped_gemm_bf16(
 // Large tiles with LDS DMA
 
 namespace big {
-constexpr int kWM = 2, kWN = 2, kTM = 4, kTN = 4;
-constexpr int kThreads = kWM * kWN * 64;
+constexpr int kWM = 4, kWN = 2, kTM = 2, kTN = 4;     // 8 waves (2 per SIMD), 64 x 128 each
+constexpr int kWaves = kWM * kWN;
+constexpr int kThreads = kWaves * 64;
 constexpr int BM = kWM * kTM * 32;                     // 256 rows
 constexpr int BNB = kWN * kTN * 32;                    // 256 weight columns
 constexpr int BK = 32;
@@ -351,11 +356,11 @@ constexpr int kABytes = BM * BK * 2;                   // [256 rows][32 k], 64-b
 constexpr int kBBytes = BK * BNB * 2;                  // [32 k][256 columns] over 1 or 2 matrices
 constexpr int kStageBytes = kABytes + kBBytes;
 constexpr int kRingBytes = kStages * kStageBytes;      // 128 KiB
-constexpr int kOutRows = 64;                           // epilogue staging: 64 rows x 64 columns
-constexpr int kOutWaveBytes = kOutRows * 128;          //   of bf16 per wave (8 KiB)
-constexpr int kSmemBytes = kRingBytes + 4 * kOutWaveBytes;   // 160 KiB, the whole LDS of a CU
-constexpr int kACopies = kABytes / 1024 / 4;           // 1 KiB copies per wave per K step
-constexpr int kBCopies = kBBytes / 1024 / 4;
+constexpr int kOutRows = 32;                           // epilogue staging: 32 rows x 64 columns
+constexpr int kOutWaveBytes = kOutRows * 128;          //   of bf16 per wave (4 KiB)
+constexpr int kSmemBytes = kRingBytes + kWaves * kOutWaveBytes;   // 160 KiB, the whole LDS of a CU
+constexpr int kACopies = kABytes / 1024 / kWaves;      // 1 KiB copies per wave per K step
+constexpr int kBCopies = kBBytes / 1024 / kWaves;
 constexpr int kCopies = kACopies + kBCopies;
 
 template <bool kGated>
@@ -417,12 +422,12 @@ __device__ __forceinline__ StepCopies step_copies(int step, uint32_t lds0, const
 {
     using L = BLayout<kGated>;
     const uint32_t st = lds0 + static_cast<uint32_t>((step % kStages) * kStageBytes);
-    const int bi0 = kGated ? kBCopies * (wave & 1) : kBCopies * wave;
+    const int bi0 = kGated ? kBCopies * (wave % (kWaves / 2)) : kBCopies * wave;
     StepCopies c;
     c.a = At + step * BK;
     c.a_lds = st + kACopies * wave * 1024;
     c.b = Bm + static_cast<int64_t>(step * BK + bi0 * L::kRowsPerCopy) * N_w;
-    c.b_lds = st + kABytes + (kGated ? (wave >> 1) * L::kMatBytes : 0) + bi0 * 1024;
+    c.b_lds = st + kABytes + (kGated ? (wave / (kWaves / 2)) * L::kMatBytes : 0) + bi0 * 1024;
     return c;
 }
 
@@ -598,8 +603,8 @@ __device__ __forceinline__ void k_loop(f32x16_t (&acc)[kTM][kTN], uint32_t lds0,
     }
 }
 
-// Epilogue through LDS.  The wave's output (128 rows x 64 columns for fc1, 128 x 128 for fc2) goes
-// out in 64 x 64 pieces: the accumulators are written to the wave's staging area as bf16 (2-byte
+// Epilogue through LDS.  The wave's output (64 rows x 64 columns for fc1, 64 x 128 for fc2) goes
+// out in 32 x 64 pieces: the accumulators are written to the wave's staging area as bf16 (2-byte
 // LDS writes, rows of 128 bytes with 16-byte chunks XOR-swizzled by row), then read back as
 // 16-byte row chunks and stored to global memory 16 bytes per lane.  Only this wave touches its
 // area, and LDS operations of one wave complete in order, so no barrier is needed.
@@ -610,31 +615,26 @@ __device__ __forceinline__ void store_output_staged(const f32x16_t (&acc)[kTM][k
 {
     constexpr int kColPieces = kGated ? 1 : 2;     // 64-column pieces per wave
 #pragma unroll
-    for (int rp = 0; rp < kTM / 2; ++rp) {          // row blocks 2 rp, 2 rp + 1
+    for (int i = 0; i < kTM; ++i) {                 // one 32-row block per piece
 #pragma unroll
         for (int cp = 0; cp < kColPieces; ++cp) {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int ii = 0; ii < 2; ++ii) {
+            for (int jj = 0; jj < 2; ++jj) {
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float v;
-                        if constexpr (kGated) {
-                            const int j = 2 * jj;            // gate block j, up block j + 1
-                            v = swiglu(acc[2 * rp + ii][j][r], acc[2 * rp + ii][j + 1][r]);
-                        } else {
-                            v = acc[2 * rp + ii][2 * cp + jj][r];
-                        }
-                        const int row = 32 * ii + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                        const int col = 32 * jj + (lane & 31);
-                        const uint32_t a = stage + row * 128 + ((((col >> 3) ^ row) & 7) << 4) + 2 * (col & 7);
-                        *reinterpret_cast<__attribute__((address_space(3))) uint16_t*>(a) = f32_to_bf16(v);
-                    }
+                for (int r = 0; r < 16; ++r) {
+                    float v;
+                    if constexpr (kGated)
+                        v = swiglu(acc[i][2 * jj][r], acc[i][2 * jj + 1][r]);   // gate, up blocks
+                    else
+                        v = acc[i][2 * cp + jj][r];
+                    const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    const int col = 32 * jj + (lane & 31);
+                    const uint32_t a = stage + row * 128 + ((((col >> 3) ^ row) & 7) << 4) + 2 * (col & 7);
+                    *reinterpret_cast<__attribute__((address_space(3))) uint16_t*>(a) = f32_to_bf16(v);
                 }
             }
-            // 64 rows x 8 chunks of 16 bytes: lane reads chunk (lane % 8) of rows lane / 8 + 8 m
+            // 32 rows x 8 chunks of 16 bytes: lane reads chunk (lane % 8) of rows lane / 8 + 8 m
             const int chunk = lane & 7;
             const int col0 = kGated ? n0 + 64 * wn + 8 * chunk : n0 + 128 * wn + 64 * cp + 8 * chunk;
 #pragma unroll
@@ -642,7 +642,7 @@ __device__ __forceinline__ void store_output_staged(const f32x16_t (&acc)[kTM][k
                 const int row = (lane >> 3) + 8 * m;
                 const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
                     stage + row * 128 + (((chunk ^ row) & 7) << 4));
-                const int grow = tile.row_begin + 32 * (2 * (2 * rp + (row >> 5)) + wm) + (row & 31);
+                const int grow = tile.row_begin + row_block<kWM>(i, wm) + row;
                 if (grow < tile.row_end)
                     *reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(grow) * N_out + col0) = v;
             }
@@ -682,7 +682,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
     uint32_t b_voff[kBCopies];
 #pragma unroll
     for (int j = 0; j < kBCopies; ++j) {
-        const int bi = (kGated ? kBCopies * (wave & 1) : kBCopies * wave) + j;
+        const int bi = (kGated ? kBCopies * (wave % (kWaves / 2)) : kBCopies * wave) + j;
         const int kr = bi * L::kRowsPerCopy + lane / L::kChunks;
         const int c = (lane % L::kChunks) ^ (4 * (kr & 3));
         b_voff[j] = static_cast<uint32_t>(lane / L::kChunks) * static_cast<uint32_t>(N_out) * 2u +
@@ -729,7 +729,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
             const int c = (lane & 3) ^ ((r >> 2) & 3);
             a_voff[j] = static_cast<uint32_t>(min(r, rows - 1)) * static_cast<uint32_t>(K) * 2u + 16u * c;
         }
-        Bm = (kGated && (wave >> 1) ? B1 : B0) + static_cast<int64_t>(tile.expert) * K * N_w + n0;
+        Bm = (kGated && wave >= kWaves / 2 ? B1 : B0) + static_cast<int64_t>(tile.expert) * K * N_w + n0;
         const int pre = KT < kStages ? KT : kStages;
         for (int st = 0; st < pre; ++st)
             issue_step<kGated>(st, lds0, At, a_voff, Bm, b_voff, wave, N_w);
@@ -760,9 +760,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
         switch (nb) {
         case 0: k_loop<kGated, 0>(acc, lds0, At, a_voff, Bm, b_voff, a_lane, b_lane, N_w, KT, wave, wm); break;
         case 1: k_loop<kGated, 1>(acc, lds0, At, a_voff, Bm, b_voff, a_lane, b_lane, N_w, KT, wave, wm); break;
-        case 2: k_loop<kGated, 2>(acc, lds0, At, a_voff, Bm, b_voff, a_lane, b_lane, N_w, KT, wave, wm); break;
-        case 3: k_loop<kGated, 3>(acc, lds0, At, a_voff, Bm, b_voff, a_lane, b_lane, N_w, KT, wave, wm); break;
-        default: k_loop<kGated, 4>(acc, lds0, At, a_voff, Bm, b_voff, a_lane, b_lane, N_w, KT, wave, wm); break;
+        default: k_loop<kGated, 2>(acc, lds0, At, a_voff, Bm, b_voff, a_lane, b_lane, N_w, KT, wave, wm); break;
         }
         const MTile done = tile;
         const int done_n0 = n0;
