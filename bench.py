@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"bf16": 2500.0, "mxfp8": 5000.0, "f32": 157.3}     # dense TFLOP/s, MI355X published
 HBM_PEAK_GBS = 8000.0
+CSRC = os.path.join(ROOT, "moe_expert_layer_amd", "csrc")
 METRIC = "MoE layer fwd tokens/s + grouped-GEMM % MFMA peak, Mixtral-shaped E=8 top-2"
 
 
@@ -48,6 +49,36 @@ def byte_model(inp, M):
                 "unpermute": k * T * H * 2 + T * H * 2 + 8 * M}
     b = 4 if inp.dtype == "f32" else 2
     return {"permute": (1 + k) * T * H * b + 4 * M, "unpermute": (k * T * H * b + T * H * b + 8 * M)}
+
+
+def kernel_source_digest(files) -> str:
+    """sha256 over the named kernel sources (and the shared headers), to tie counter figures to code."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in list(files) + ["common.h", "internal.h"]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when there is
+    none for this workload or the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    try:
+        if kv.get("source_digest") != kernel_source_digest(kv["sources"].split(",")):
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError, OSError):
+        return None
 
 
 def cpu_baseline(inp, budget_s: float):
@@ -81,6 +112,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-chunked", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (reference for HBM counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -142,6 +175,15 @@ def main():
         wall = time.perf_counter() - w0
         return np.array([a.elapsed_time(b) for a, b in ev]), wall
 
+    if args.copy_calibration_mib:
+        src = torch.ones(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {args.copy_calibration_mib} MiB done")
+        del src, dst
+
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         step(head)
@@ -175,12 +217,14 @@ def main():
     if dom_flops is not None:
         achieved = dom_flops / (kavg[dominant] * 1e-3) / 1e12
         roof = {"kernel": dominant, "bound": "mfma", "achieved": achieved, "peak": peak,
-                "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                "unit": "TFLOP/s", "frac": achieved / peak,
+                "traffic": measured_traffic(args.workload, dominant),
                 "per_launch": f"{dom_flops:.4g} FLOP = 2*M*H*F per projection, M={M} routed rows"}
     else:
         gbs = bytes_[dominant] / (kavg[dominant] * 1e-3) / 1e9
         roof = {"kernel": dominant, "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None}
+                "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                "traffic": measured_traffic(args.workload, dominant)}
     hbm = {n: {"GB/s": bytes_[n] / (kavg[n] * 1e-3) / 1e9,
                "frac": bytes_[n] / (kavg[n] * 1e-3) / 1e9 / HBM_PEAK_GBS}
            for n in bytes_ if n in kavg}
