@@ -613,36 +613,47 @@ __device__ __forceinline__ void store_output_staged(const f32x16_t (&acc)[kTM][k
                                                     const MTile& tile, int n0, int N_out, uint32_t stage,
                                                     int wm, int wn, int lane)
 {
-    constexpr int kColPieces = kGated ? 1 : 2;     // 64-column pieces per wave
+    constexpr int kOutCols = kGated ? 16 * kTN : 32 * kTN;       // the wave's output columns
+    constexpr int PC = kOutCols < 64 ? kOutCols : 64;           // piece columns
+    constexpr int PR = kOutWaveBytes / (2 * PC);                // piece rows (a multiple of 32)
+    constexpr int CPR = PC / 8;                                 // 16-byte chunks per staged row
+    constexpr int kSwz = CPR == 8 ? 0 : 2;                      // rows sharing a 256-byte bank window
+    static_assert(PR % 32 == 0 && (32 * kTM) % PR == 0, "pieces cover whole row blocks");
 #pragma unroll
-    for (int i = 0; i < kTM; ++i) {                 // one 32-row block per piece
+    for (int rp = 0; rp < 32 * kTM / PR; ++rp) {
 #pragma unroll
-        for (int cp = 0; cp < kColPieces; ++cp) {
+        for (int cp = 0; cp < kOutCols / PC; ++cp) {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
+            for (int ii = 0; ii < PR / 32; ++ii) {
+                const int i = rp * (PR / 32) + ii;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float v;
-                    if constexpr (kGated)
-                        v = swiglu(acc[i][2 * jj][r], acc[i][2 * jj + 1][r]);   // gate, up blocks
-                    else
-                        v = acc[i][2 * cp + jj][r];
-                    const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    const int col = 32 * jj + (lane & 31);
-                    const uint32_t a = stage + row * 128 + ((((col >> 3) ^ row) & 7) << 4) + 2 * (col & 7);
-                    *reinterpret_cast<__attribute__((address_space(3))) uint16_t*>(a) = f32_to_bf16(v);
+                for (int jj = 0; jj < PC / 32; ++jj) {
+                    const int ob = cp * (PC / 32) + jj;               // 32-column output block
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float v;
+                        if constexpr (kGated)
+                            v = swiglu(acc[i][2 * ob][r], acc[i][2 * ob + 1][r]);   // gate, up blocks
+                        else
+                            v = acc[i][ob][r];
+                        const int row = 32 * ii + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                        const int col = 32 * jj + (lane & 31);
+                        const uint32_t a = stage + row * (2 * PC) +
+                                           ((((col >> 3) ^ (row >> kSwz)) & (CPR - 1)) << 4) + 2 * (col & 7);
+                        *reinterpret_cast<__attribute__((address_space(3))) uint16_t*>(a) = f32_to_bf16(v);
+                    }
                 }
             }
-            // 32 rows x 8 chunks of 16 bytes: lane reads chunk (lane % 8) of rows lane / 8 + 8 m
-            const int chunk = lane & 7;
-            const int col0 = kGated ? n0 + 64 * wn + 8 * chunk : n0 + 128 * wn + 64 * cp + 8 * chunk;
+            // PR rows x CPR chunks of 16 bytes: lane reads chunk (lane % CPR) of rows lane / CPR + ..
+            const int chunk = lane % CPR;
+            const int col0 = n0 + kOutCols * wn + PC * cp + 8 * chunk;
 #pragma unroll
-            for (int m = 0; m < kOutRows / 8; ++m) {
-                const int row = (lane >> 3) + 8 * m;
+            for (int m = 0; m < PR * CPR / 64; ++m) {
+                const int row = lane / CPR + (64 / CPR) * m;
                 const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
-                    stage + row * 128 + (((chunk ^ row) & 7) << 4));
-                const int grow = tile.row_begin + row_block<kWM>(i, wm) + row;
+                    stage + row * (2 * PC) + (((chunk ^ (row >> kSwz)) & (CPR - 1)) << 4));
+                const int grow = tile.row_begin + row_block<kWM>(rp * (PR / 32) + row / 32, wm) + row % 32;
                 if (grow < tile.row_end)
                     *reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(grow) * N_out + col0) = v;
             }
@@ -702,7 +713,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
 #pragma unroll
         for (int j = 0; j < kTN; ++j) {
             const int m = kGated ? (j & 1) : 0;
-            const int col = (kGated ? 64 * wn + 32 * (j >> 1) : 128 * wn + 32 * j) + 16 * (g & 1) + 4 * q;
+            const int col = (kGated ? 16 * kTN * wn + 32 * (j >> 1) : 32 * kTN * wn + 32 * j) + 16 * (g & 1) + 4 * q;
             b_lane[j] = m * L::kMatBytes + kr * L::kRowBytes + 16 * ((col >> 3) ^ (4 * e)) + 2 * (col & 7);
         }
     }

@@ -157,8 +157,11 @@ __global__ __launch_bounds__(kThreads) void route_scatter_kernel(
 
 // Row-tile table.  Group g covers rows [offsets[g], offsets[g+1]) with expert group_expert[g]
 // (g itself when group_expert is null).  Each group is cut at chunk boundaries (multiples of
-// `chunk` rows) and each piece into tiles of at most bm rows.  Tiles are written in row order, so
-// the table is chunk-major.  One workgroup; groups are handled 1024 at a time.
+// `chunk` rows) and each piece into tiles of at most bm rows; a run is the tiles of one piece.
+// Chunked (num_chunks > 1): tiles in row order, so the table is chunk-major and chunks complete in
+// order.  Unchunked: first every group's full tiles (row order), then the partial tail tiles, each
+// its own run, so that the short tasks come last and even out the workgroups' finishing times.
+// One workgroup; groups are handled 1024 at a time.
 __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ group_expert, int G, int E,
     int64_t M, int64_t chunk, int bm, MTile* __restrict__ tiles, int max_tiles, int32_t* __restrict__ tile_count,
@@ -180,39 +183,43 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
             chunk_done[c] = 0;
         }
     __syncthreads();
-    for (int g0 = 0; g0 < G; g0 += kScanThreads) {
-        const int g = g0 + threadIdx.x;
-        int64_t rb = 0, re = 0;
-        int ex = 0, n = 0;
-        if (g < G) {
-            // clamp into [0, M] so that malformed offsets can never address rows outside the buffers
-            rb = min(max(static_cast<int64_t>(offsets[g]), int64_t{0}), M);
-            re = min(max(static_cast<int64_t>(offsets[g + 1]), rb), M);
-            ex = group_expert ? group_expert[g] : g;
-            if (ex < 0 || ex >= E) {
-                if (re > rb)
-                    atomicOr(&bad, 1);
-                re = rb;   // skipped
+    const bool tails_last = num_chunks <= 1;
+    for (int pass = 0; pass < (tails_last ? 2 : 1); ++pass) {
+        for (int g0 = 0; g0 < G; g0 += kScanThreads) {
+            const int g = g0 + threadIdx.x;
+            int64_t rb = 0, re = 0;
+            int ex = 0, n = 0;
+            if (g < G) {
+                // clamp into [0, M] so that malformed offsets can never address rows outside the buffers
+                rb = min(max(static_cast<int64_t>(offsets[g]), int64_t{0}), M);
+                re = min(max(static_cast<int64_t>(offsets[g + 1]), rb), M);
+                ex = group_expert ? group_expert[g] : g;
+                if (ex < 0 || ex >= E) {
+                    if (re > rb)
+                        atomicOr(&bad, 1);
+                    re = rb;   // skipped
+                }
+                if (!tails_last) {
+                    for (int64_t r = rb; r < re;) {
+                        const int64_t cend = min(re, (r / chunk + 1) * chunk);
+                        n += static_cast<int>((cend - r + bm - 1) / bm);
+                        r = cend;
+                    }
+                } else if (pass == 0) {
+                    n = static_cast<int>((re - rb) / bm);
+                } else {
+                    n = (re - rb) % bm != 0 ? 1 : 0;
+                }
             }
-            for (int64_t r = rb; r < re;) {
-                const int64_t cend = min(re, (r / chunk + 1) * chunk);
-                n += static_cast<int>((cend - r + bm - 1) / bm);
-                r = cend;
-            }
-        }
-        const int incl = block_inclusive_scan(n, buf);
-        int t = carry + incl - n;
-        for (int64_t r = rb; r < re;) {
-            const int64_t cend = min(re, (r / chunk + 1) * chunk);
-            const int run_begin = t;
-            const int run_len = static_cast<int>((cend - r + bm - 1) / bm);
-            for (int64_t r0 = r; r0 < cend; r0 += bm) {
+            const int incl = block_inclusive_scan(n, buf);
+            int t = carry + incl - n;
+            auto emit = [&](int64_t r0, int64_t r1, int run_begin, int run_len) {
                 const int c = static_cast<int>(r0 / chunk);
                 if (t < max_tiles) {
                     MTile mt;
                     mt.expert = ex;
                     mt.row_begin = static_cast<int>(r0);
-                    mt.row_end = static_cast<int>(min(cend, r0 + bm));
+                    mt.row_end = static_cast<int>(r1);
                     mt.chunk = c;
                     mt.run_begin = run_begin;
                     mt.run_len = run_len;
@@ -222,13 +229,28 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
                 if (chunk_tiles != nullptr && c < num_chunks)
                     atomicAdd(&chunk_tiles[c], col_tiles);
                 ++t;
+            };
+            if (!tails_last) {
+                for (int64_t r = rb; r < re;) {
+                    const int64_t cend = min(re, (r / chunk + 1) * chunk);
+                    const int run_begin = t;
+                    const int run_len = static_cast<int>((cend - r + bm - 1) / bm);
+                    for (int64_t r0 = r; r0 < cend; r0 += bm)
+                        emit(r0, min(cend, r0 + bm), run_begin, run_len);
+                    r = cend;
+                }
+            } else if (pass == 0) {
+                const int run_begin = t;
+                for (int i = 0; i < n; ++i)
+                    emit(rb + int64_t{i} * bm, rb + int64_t{i + 1} * bm, run_begin, n);
+            } else if (n != 0) {
+                emit(rb + (re - rb) / bm * bm, re, t, 1);
             }
-            r = cend;
+            __syncthreads();
+            if (threadIdx.x == kScanThreads - 1)
+                carry += incl;
+            __syncthreads();
         }
-        __syncthreads();
-        if (threadIdx.x == kScanThreads - 1)
-            carry += incl;
-        __syncthreads();
     }
     if (threadIdx.x == 0) {
         tile_count[0] = min(carry, max_tiles);
