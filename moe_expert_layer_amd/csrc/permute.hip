@@ -6,7 +6,10 @@
 // unpermute (step 10): out[t] = sum_j probs[t, j] * y_perm[pos[t*k + j]], j ascending, fp32
 //           fused multiply-add from 0 and one rounding; a gather, so no atomics and a
 //           deterministic result.
-// Both move 16-byte vectors; one workgroup walks whole rows so every access is coalesced.
+// Both move 16-byte vectors.  The flat kernels give every (token, 16-byte column) pair its own
+// thread, so a launch keeps as many independent loads in flight as the machine can hold; rows are
+// contiguous in the thread index, so every access is coalesced.  Grid-stride versions cover sizes
+// whose pair count does not fit 32 bits.
 #include "common.h"
 #include "internal.h"
 
@@ -33,6 +36,79 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const V* __restrict__
             }
         }
     }
+}
+
+// One thread per (token, 16-byte column): total = T * row_vecs < 2^31.
+template <typename V>
+__global__ __launch_bounds__(kThreads) void permute_flat_kernel(const V* __restrict__ x,
+                                                                const int32_t* __restrict__ pos,
+                                                                V* __restrict__ x_perm, int k,
+                                                                int64_t M, uint32_t row_vecs,
+                                                                uint32_t total)
+{
+    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+    if (i >= total)
+        return;
+    const uint32_t t = i / row_vecs;
+    const uint32_t c = i - t * row_vecs;
+    const V v = x[i];
+    const int32_t* tp = pos + static_cast<int64_t>(t) * k;
+    for (int j = 0; j < k; ++j) {
+        const int64_t p = tp[j];
+        if (p >= 0 && p < M)
+            x_perm[p * row_vecs + c] = v;
+    }
+}
+
+__device__ __forceinline__ void fma_bf16x8(float (&acc)[8], float w, const uint4& v)
+{
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(w, __uint_as_float(d[i] << 16), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(w, __uint_as_float(d[i] & 0xffff0000u), acc[2 * i + 1]);
+    }
+}
+
+// One thread per (token, 16-byte column) of the output.  The k rows are loaded before any is used
+// (k <= 8 in one batch), then summed in j order.
+__global__ __launch_bounds__(kThreads) void unpermute_bf16_flat_kernel(
+    const uint4* __restrict__ y, const int32_t* __restrict__ pos, const float* __restrict__ probs,
+    uint4* __restrict__ out, int k, int64_t M, uint32_t row_vecs, uint32_t total)
+{
+    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+    if (i >= total)
+        return;
+    const uint32_t t = i / row_vecs;
+    const uint32_t c = i - t * row_vecs;
+    const int32_t* tp = pos + static_cast<int64_t>(t) * k;
+    const float* pp = probs + static_cast<int64_t>(t) * k;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        acc[e] = 0.0f;
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        uint4 v[8];
+        float w[8];
+        bool ok[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t p = j0 + j < k ? tp[j0 + j] : -1;
+            ok[j] = p >= 0 && p < M;
+            w[j] = ok[j] ? pp[j0 + j] : 0.0f;
+            v[j] = ok[j] ? y[p * row_vecs + c] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (ok[j])
+                fma_bf16x8(acc, w[j], v[j]);
+    }
+    uint4 o;
+    o.x = pack_bf16x2(acc[0], acc[1]);
+    o.y = pack_bf16x2(acc[2], acc[3]);
+    o.z = pack_bf16x2(acc[4], acc[5]);
+    o.w = pack_bf16x2(acc[6], acc[7]);
+    out[i] = o;
 }
 
 // bfloat16 rows: 8 values per 16-byte vector.
@@ -108,7 +184,15 @@ unsigned grid_for_rows(int64_t rows)
 hipError_t launch_permute(const void* x, const int32_t* pos, void* x_perm, int64_t T, int64_t k,
                           int64_t M, int64_t row_bytes, hipStream_t s)
 {
-    const dim3 grid(grid_for_rows(T)), block(kThreads);
+    const dim3 block(kThreads);
+    if (row_bytes % 16 == 0 && T * (row_bytes / 16) < (int64_t{1} << 31)) {
+        const uint32_t total = static_cast<uint32_t>(T * (row_bytes / 16));
+        permute_flat_kernel<uint4><<<dim3((total + kThreads - 1) / kThreads), block, 0, s>>>(
+            static_cast<const uint4*>(x), pos, static_cast<uint4*>(x_perm), static_cast<int>(k), M,
+            static_cast<uint32_t>(row_bytes / 16), total);
+        return hipGetLastError();
+    }
+    const dim3 grid(grid_for_rows(T));
     if (row_bytes % 16 == 0)
         permute_kernel<uint4><<<grid, block, 0, s>>>(static_cast<const uint4*>(x), pos,
                                                       static_cast<uint4*>(x_perm), T,
@@ -129,6 +213,13 @@ hipError_t launch_unpermute(int dtype, const void* y_perm, const int32_t* pos, c
                             void* out, int64_t T, int64_t k, int64_t M, int64_t H, hipStream_t s)
 {
     const dim3 grid(grid_for_rows(T)), block(kThreads);
+    if (dtype != 0 && T * (H / 8) < (int64_t{1} << 31)) {
+        const uint32_t total = static_cast<uint32_t>(T * (H / 8));
+        unpermute_bf16_flat_kernel<<<dim3((total + kThreads - 1) / kThreads), block, 0, s>>>(
+            static_cast<const uint4*>(y_perm), pos, probs, static_cast<uint4*>(out),
+            static_cast<int>(k), M, static_cast<uint32_t>(H / 8), total);
+        return hipGetLastError();
+    }
     if (dtype == 0)
         unpermute_f32_kernel<<<grid, block, 0, s>>>(static_cast<const float4*>(y_perm), pos, probs,
                                                      static_cast<float4*>(out), T,
