@@ -55,7 +55,7 @@ def kernel_source_digest(files) -> str:
     """sha256 over the named kernel sources (and the shared headers), to tie counter figures to code."""
     import hashlib
     h = hashlib.sha256()
-    for f in list(files) + ["common.h", "internal.h"]:
+    for f in list(files) + ["common.h", "internal.h", "gemm_common.h"]:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

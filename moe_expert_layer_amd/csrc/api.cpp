@@ -21,7 +21,6 @@
 
 namespace moe {
 
-int mx_fc2_cols_per_tile();
 
 namespace {
 
@@ -48,7 +47,7 @@ int64_t out_bytes(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
 
 int row_tile(int dtype, int64_t H, int64_t F)
 {
-    return dtype == MOE_F32 ? kBmF32 : dtype == MOE_BF16 ? bf16_row_tile(H, F) : kBmMx;
+    return dtype == MOE_F32 ? kBmF32 : dtype == MOE_BF16 ? bf16_row_tile(H, F) : mx_row_tile(H, F);
 }
 
 // Column tiles of the down projection for the chunk counters (tasks per row tile).
@@ -57,7 +56,7 @@ int fc2_col_tiles(int dtype, int64_t H, int64_t F)
     if (dtype == MOE_F32)
         return static_cast<int>(ceil_div(H, 256));
     if (dtype == MOE_MXFP8_E4M3)
-        return static_cast<int>(H / mx_fc2_cols_per_tile());
+        return static_cast<int>(H / mx_fc2_cols_per_tile(H, F));
     return static_cast<int>(H / bf16_fc2_cols_per_tile(H, F));
 }
 
@@ -356,10 +355,10 @@ moe_status run_ffn(int dtype, const void* rows, const uint8_t* rows_scale, int64
         LAUNCH(s, "fc1_mx",
                launch_fc1_mx(static_cast<const uint8_t*>(rows), rows_scale,
                              static_cast<const uint8_t*>(wg), wgs, static_cast<const uint8_t*>(wu),
-                             wus, h, hs, tiles, tcount, H, F, s));
+                             wus, h, hs, tiles, tcount, H, F, task_ctr, s));
         LAUNCH(s, "fc2_mx",
                launch_fc2_mx(h, hs, static_cast<const uint8_t*>(wd), wds, static_cast<uint16_t*>(y),
-                             tiles, tcount, H, F, chunk_done, s));
+                             tiles, tcount, H, F, chunk_done, task_ctr + kXcdCount, s));
     }
     return MOE_OK;
 }

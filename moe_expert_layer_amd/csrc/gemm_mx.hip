@@ -16,6 +16,7 @@
 // the fp32 SwiGLU tile in LDS so each lane owns one (row, 32-column block), finds its amax, and
 // writes 32 E4M3 bytes plus one scale byte with the same integer encoder as the standalone kernel.
 #include "common.h"
+#include "gemm_common.h"
 #include "internal.h"
 
 namespace moe {
@@ -321,6 +322,493 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_mx(
     }
 }
 
+// ----------------------------------------------------------------------------------- large tiles
+//
+// 256 rows x 256 weight columns per task (8 waves of 64 x 128, two per SIMD), for H and F multiples
+// of 512.  The structure is the bfloat16 large-tile kernel's: global -> LDS copies
+// (global_load_lds_dwordx4) into a four-stage ring, three K steps in flight, tasks claimed per XCD,
+// the next task's first copies issued before the current epilogue.  A K step is 64 values (one
+// scaled MFMA): A [256 rows][64 bytes], weights [64 k][columns] N-contiguous.  Weight fragments come
+// from ds_read_b64_tr_b8 (measured: lane i of a 16-lane group receives byte e from source lane
+// 2e + i / 8, byte i % 8, so 16 source lanes reading 8 rows x 16 columns hand every lane 8
+// consecutive k of one column).  Block scales ride in their own two-slot LDS ring, one slot per 8
+// K steps (16 scale blocks): A scales [256 rows][16] and weight scales [16][columns].
+namespace big {
+
+constexpr int kWM = 4, kWN = 2, kTM = 2, kTN = 4;
+constexpr int kWaves = kWM * kWN;
+constexpr int kThreads = kWaves * 64;
+constexpr int BM = kWM * kTM * 32;                    // 256
+constexpr int BNB = kWN * kTN * 32;                   // 256
+constexpr int BK = 64;
+constexpr int kStages = 4;
+constexpr int kABytes = BM * BK;
+constexpr int kBBytes = BK * BNB;
+constexpr int kStageBytes = kABytes + kBBytes;        // 32 KiB
+constexpr int kRingBytes = kStages * kStageBytes;     // 128 KiB
+constexpr int kScaleSteps = 8;                        // K steps per scale slot (16 blocks of 32)
+constexpr int kAScBytes = BM * 16;                    // [256 rows][16 blocks]
+constexpr int kBScBytes = 16 * BNB;                   // [16 blocks][256 columns]
+constexpr int kScSlotBytes = kAScBytes + kBScBytes;
+constexpr int kScRing = kRingBytes;
+constexpr int kOutBase = kScRing + 2 * kScSlotBytes;  // 144 KiB
+constexpr int kOutWaveBytes = 2048;                   // epilogue staging per wave
+constexpr int kSmemBytes = kOutBase + kWaves * kOutWaveBytes;   // 160 KiB
+constexpr int kACopies = kABytes / 1024 / kWaves;     // 2
+constexpr int kBCopies = kBBytes / 1024 / kWaves;     // 2
+constexpr int kDataCopies = kACopies + kBCopies;
+static_assert(kSmemBytes <= 160 * 1024, "LDS");
+
+template <bool kGated>
+struct BLayout {
+    static constexpr int kMats = kGated ? 2 : 1;
+    static constexpr int kRowBytes = BNB / kMats;       // one k row of one matrix: 128 or 256 bytes
+    static constexpr int kChunks = kRowBytes / 16;
+    static constexpr int kRowsPerCopy = 64 / kChunks;
+    static constexpr int kMatBytes = BK * kRowBytes;
+};
+
+// 16-byte chunk position of logical chunk c in weight k row kr.  The transposing reads take 8
+// consecutive k rows x 2 neighbouring chunks per 32 lanes; the XOR keeps those 16 pieces in
+// distinct bank groups (rows of 256 bytes fill a bank window, rows of 128 bytes share one).
+template <bool kGated>
+__device__ __forceinline__ int bswz(int c, int kr)
+{
+    return BLayout<kGated>::kChunks == 16 ? c ^ ((kr & 7) << 1) : c ^ (((kr >> 1) & 3) << 1);
+}
+
+// Copies in flight after the group of step s: data copies, plus one scale copy per wave with
+// every eighth step.
+__device__ __forceinline__ int group_copies(int s, int KT)
+{
+    return s >= KT ? 0 : kDataCopies + (s % kScaleSteps == 0 ? 1 : 0);
+}
+
+// Waits until at most n copies of this wave are in flight and for its LDS reads, then joins the
+// workgroup barrier (one statement with a memory clobber).
+__device__ __forceinline__ void step_barrier(int n)
+{
+    switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 9: asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 12: asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 13: asm volatile("s_waitcnt vmcnt(13) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    }
+}
+
+// Per-task copy sources (uniform bases, per-lane byte offsets).
+struct TaskSrc {
+    const uint8_t* At;        // A rows of the tile
+    const uint8_t* Bm;        // this wave's weight matrix, expert and first column applied
+    const uint8_t* Asc;       // A scale rows of the tile
+    const uint8_t* Bsc;       // this wave's scale-copy matrix (waves >= 4), expert and column applied
+    uint32_t a_voff[kACopies];
+    uint32_t sc_voff;         // lane offset of this wave's scale copy
+};
+
+template <bool kGated>
+__device__ __forceinline__ void issue_copies(int step, uint32_t lds0, const TaskSrc& t,
+                                             const uint32_t (&b_voff)[kBCopies], int wave, int K,
+                                             int64_t N_w, bool on)
+{
+    using L = BLayout<kGated>;
+    if (!on)
+        return;
+    if (step % kScaleSteps == 0) {
+        const int blk = step / kScaleSteps;
+        const uint32_t slot = lds0 + kScRing + (blk & 1) * kScSlotBytes;
+        if (wave < 4) {
+            lds_copy16(t.Asc + 16 * blk, t.sc_voff, slot + wave * 1024);
+        } else {
+            const int c = wave - 4;
+            const int64_t kb0 = int64_t{16} * blk;
+            lds_copy16(t.Bsc + kb0 * N_w, t.sc_voff, slot + kAScBytes + c * 1024);
+        }
+    }
+    const uint32_t st = lds0 + static_cast<uint32_t>((step % kStages) * kStageBytes);
+#pragma unroll
+    for (int j = 0; j < kACopies; ++j)
+        lds_copy16(t.At + step * BK, t.a_voff[j], st + (kACopies * wave + j) * 1024);
+    const int bi0 = kGated ? kBCopies * (wave % (kWaves / 2)) : kBCopies * wave;
+    const uint32_t bst = st + kABytes + (kGated ? (wave / (kWaves / 2)) * L::kMatBytes : 0);
+#pragma unroll
+    for (int j = 0; j < kBCopies; ++j)
+        lds_copy16(t.Bm + (static_cast<int64_t>(step) * BK + (bi0 + j) * L::kRowsPerCopy) * N_w,
+                   b_voff[j], bst + (bi0 + j) * 1024);
+}
+
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
+
+__device__ __forceinline__ i32x8_t read_a(uint32_t p0, uint32_t p1)
+{
+    const u32x4_t lo = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(p0);
+    const u32x4_t hi = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(p1);
+    return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+template <int kRowBytes>
+__device__ __forceinline__ i32x8_t read_b(uint32_t p)
+{
+    const i32x2_t r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<lds_i32x2_t*>(p));
+    const i32x2_t r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<lds_i32x2_t*>(p + 8 * kRowBytes));
+    const i32x2_t r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<lds_i32x2_t*>(p + 32 * kRowBytes));
+    const i32x2_t r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<lds_i32x2_t*>(p + 40 * kRowBytes));
+    return i32x8_t{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+}
+
+__device__ __forceinline__ int read_u8(uint32_t p)
+{
+    return *reinterpret_cast<const __attribute__((address_space(3))) uint8_t*>(p);
+}
+
+// Lane parts of the fragment and scale addresses.
+struct LaneAddr {
+    uint32_t a0, a1;          // A chunks h and 2 + h of the lane's row (plus the row block)
+    uint32_t b[kTN];          // first transposing read of weight block j
+    uint32_t asc;             // A scale byte: row * 16 + h
+    uint32_t bsc[kTN];        // weight scale byte of block j: column + h * row bytes
+};
+
+struct MxFrags {
+    i32x8_t a[kTM];
+    int sa[kTM];
+};
+
+template <int NB>
+__device__ __forceinline__ void mfma_pair(f32x16_t (&acc)[kTM][kTN], const MxFrags& A, const i32x8_t (&b)[2],
+                                          const int (&sb)[2], int j0)
+{
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+            acc[i][j0 + jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                A.a[i], b[jj], acc[i][j0 + jj], 0, 0, 0, A.sa[i], 0, sb[jj]);
+}
+
+// One K step: the MFMAs of weight blocks 0-1 (fragments loaded during the previous step) while the
+// fragments of blocks 2-3 are read; the barrier; the MFMAs of blocks 2-3 while the next step's A and
+// blocks 0-1 fragments are read and the copies of step kt + 4 are issued.
+template <bool kGated, int NB>
+__device__ __forceinline__ void mx_step(f32x16_t (&acc)[kTM][kTN], const MxFrags& Acur, MxFrags& Anext,
+                                        i32x8_t (&b01)[2], int (&sb01)[2], i32x8_t (&b23)[2],
+                                        int (&sb23)[2], int kt, int KT, uint32_t lds0, const LaneAddr& la,
+                                        const TaskSrc& t, const uint32_t (&b_voff)[kBCopies],
+                                        int wave, int wm, int K, int64_t N_w)
+{
+    using L = BLayout<kGated>;
+    const uint32_t stage = lds0 + static_cast<uint32_t>((kt % kStages) * kStageBytes);
+    const uint32_t bst = stage + kABytes;
+    const uint32_t sc = lds0 + kScRing + ((kt / kScaleSteps) & 1) * kScSlotBytes;
+    const int kbl = 2 * (kt % kScaleSteps);
+    if constexpr (NB > 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        // blocks 2-3 of this step
+        b23[0] = read_b<L::kRowBytes>(bst + la.b[2]);
+        sb23[0] = read_u8(sc + kAScBytes + la.bsc[2] + kbl * L::kRowBytes);
+        b23[1] = read_b<L::kRowBytes>(bst + la.b[3]);
+        sb23[1] = read_u8(sc + kAScBytes + la.bsc[3] + kbl * L::kRowBytes);
+        mfma_pair<NB>(acc, Acur, b01, sb01, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (kt + 1 < KT)
+        step_barrier(group_copies(kt + 2, KT) + group_copies(kt + 3, KT));
+    {
+        // the next step's fragments (a stale stage after the last step: never used)
+        const int kn = kt + 1;
+        const uint32_t nstage = lds0 + static_cast<uint32_t>((kn % kStages) * kStageBytes);
+        const uint32_t nsc = lds0 + kScRing + ((kn / kScaleSteps) & 1) * kScSlotBytes;
+        const int nkbl = 2 * (kn % kScaleSteps);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_copies<kGated>(kt + kStages, lds0, t, b_voff, wave, K, N_w, kt + kStages < KT);
+        if constexpr (NB > 0) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                Anext.a[i] = read_a(nstage + la.a0 + row_block<kWM>(i, wm) * 64,
+                                    nstage + la.a1 + row_block<kWM>(i, wm) * 64);
+                Anext.sa[i] = read_u8(nsc + la.asc + row_block<kWM>(i, wm) * 16 + nkbl);
+            }
+            mfma_pair<NB>(acc, Acur, b23, sb23, 2);
+            b01[0] = read_b<L::kRowBytes>(nstage + kABytes + la.b[0]);
+            sb01[0] = read_u8(nsc + kAScBytes + la.bsc[0] + nkbl * L::kRowBytes);
+            b01[1] = read_b<L::kRowBytes>(nstage + kABytes + la.b[1]);
+            sb01[1] = read_u8(nsc + kAScBytes + la.bsc[1] + nkbl * L::kRowBytes);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <bool kGated, int NB>
+__device__ __forceinline__ void mx_k_loop(f32x16_t (&acc)[kTM][kTN], uint32_t lds0, const LaneAddr& la,
+                                          const TaskSrc& t, const uint32_t (&b_voff)[kBCopies], int KT,
+                                          int wave, int wm, int K, int64_t N_w)
+{
+    using L = BLayout<kGated>;
+    // the caller issued the groups of steps 0 .. 3
+    step_barrier(group_copies(1, KT) + group_copies(2, KT) + group_copies(3, KT));
+    MxFrags A0, A1;
+    i32x8_t b01[2], b23[2];
+    int sb01[2], sb23[2];
+    if constexpr (NB > 0) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            A0.a[i] = read_a(lds0 + la.a0 + row_block<kWM>(i, wm) * 64, lds0 + la.a1 + row_block<kWM>(i, wm) * 64);
+            A0.sa[i] = read_u8(lds0 + kScRing + la.asc + row_block<kWM>(i, wm) * 16);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            b01[jj] = read_b<L::kRowBytes>(lds0 + kABytes + la.b[jj]);
+            sb01[jj] = read_u8(lds0 + kScRing + kAScBytes + la.bsc[jj]);
+        }
+    }
+    for (int kt = 0; kt < KT; kt += 2) {
+        mx_step<kGated, NB>(acc, A0, A1, b01, sb01, b23, sb23, kt, KT, lds0, la, t, b_voff, wave, wm, K, N_w);
+        mx_step<kGated, NB>(acc, A1, A0, b01, sb01, b23, sb23, kt + 1, KT, lds0, la, t, b_voff, wave, wm, K, N_w);
+    }
+}
+
+// fc2 epilogue: bf16 rows through the wave's 2 KiB staging area in pieces of 16 rows x 64 columns.
+__device__ __forceinline__ void store_y(const f32x16_t (&acc)[kTM][kTN], uint16_t* __restrict__ C,
+                                        const MTile& tile, int n0, int N_out, uint32_t stage, int wm,
+                                        int wn, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int cp = 0; cp < 2; ++cp) {
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                    for (int rr = 0; rr < 8; ++rr) {
+                        const int r = 8 * half + rr;
+                        const int row = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);   // 0..15
+                        const int col = 32 * jj + (lane & 31);
+                        const uint32_t a = stage + row * 128 + ((((col >> 3) ^ row) & 7) << 4) + 2 * (col & 7);
+                        *reinterpret_cast<__attribute__((address_space(3))) uint16_t*>(a) =
+                            f32_to_bf16(acc[i][2 * cp + jj][r]);
+                    }
+                const int chunk = lane & 7;
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const int row = (lane >> 3) + 8 * m;
+                    const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
+                        stage + row * 128 + (((chunk ^ row) & 7) << 4));
+                    const int brow = 16 * half + row;          // row inside the 32-row block
+                    const int grow = tile.row_begin + row_block<kWM>(i, wm) + brow;
+                    if (grow < tile.row_end)
+                        *reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(grow) * N_out + n0 + 128 * wn +
+                                                    64 * cp + 8 * chunk) = v;
+                }
+            }
+}
+
+// fc1 epilogue: SwiGLU in fp32 into the staging area, 16 rows x 32 columns at a time (16-byte
+// chunks XOR-swizzled by row).  Four lanes share a row's 32-column block: each takes 8 values, the
+// block's largest magnitude is combined across the four, and each lane encodes its 8 values (OCP-MX,
+// the integer encoder) and stores 8 code bytes; the first of the four stores the scale byte.
+__device__ __forceinline__ uint32_t h_stage_off(int row, int col)
+{
+    return row * 128 + 16 * (((col >> 2) ^ row) & 7) + 4 * (col & 3);
+}
+
+__device__ __forceinline__ void store_h(const f32x16_t (&acc)[kTM][kTN], uint8_t* __restrict__ Cq,
+                                        uint8_t* __restrict__ Cq_sc, const MTile& tile, int n0,
+                                        int N_out, uint32_t stage, int wm, int wn, int lane)
+{
+    const int erow = lane >> 2;                   // row of the piece this lane encodes
+    const int eq = lane & 3;                      // its quarter of the 32 columns
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int ob = 0; ob < 2; ++ob) {      // output block: gate block 2 ob, up block 2 ob + 1
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int rr = 0; rr < 8; ++rr) {
+                    const int r = 8 * half + rr;
+                    const int row = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+                    *reinterpret_cast<__attribute__((address_space(3))) float*>(
+                        stage + h_stage_off(row, lane & 31)) = swiglu(acc[i][2 * ob][r], acc[i][2 * ob + 1][r]);
+                }
+                const f32x4_t x0 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(
+                    stage + h_stage_off(erow, 8 * eq));
+                const f32x4_t x1 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(
+                    stage + h_stage_off(erow, 8 * eq + 4));
+                uint32_t amax = 0;
+#pragma unroll
+                for (int z = 0; z < 4; ++z)
+                    amax = max(amax, max(__float_as_uint(x0[z]) & 0x7fffffffu, __float_as_uint(x1[z]) & 0x7fffffffu));
+                amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 1)));
+                amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 2)));
+                const int e = mx_shared_exponent(amax);
+                const uint32_t lo = e4m3_encode_scaled(x0[0], e) | (e4m3_encode_scaled(x0[1], e) << 8) |
+                                    (e4m3_encode_scaled(x0[2], e) << 16) | (e4m3_encode_scaled(x0[3], e) << 24);
+                const uint32_t hi = e4m3_encode_scaled(x1[0], e) | (e4m3_encode_scaled(x1[1], e) << 8) |
+                                    (e4m3_encode_scaled(x1[2], e) << 16) | (e4m3_encode_scaled(x1[3], e) << 24);
+                const int grow = tile.row_begin + row_block<kWM>(i, wm) + 16 * half + erow;
+                const int hcol = n0 + 64 * wn + 32 * ob;
+                if (grow < tile.row_end) {
+                    *reinterpret_cast<u32x2_t*>(Cq + static_cast<int64_t>(grow) * N_out + hcol + 8 * eq) =
+                        u32x2_t{lo, hi};
+                    if (eq == 0)
+                        Cq_sc[static_cast<int64_t>(grow) * (N_out / 32) + hcol / 32] = static_cast<uint8_t>(e + 127);
+                }
+            }
+}
+
+template <bool kGated>
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ A_sc,
+    const uint8_t* __restrict__ B0, const uint8_t* __restrict__ B0_sc,
+    const uint8_t* __restrict__ B1, const uint8_t* __restrict__ B1_sc,
+    uint8_t* __restrict__ Cq, uint8_t* __restrict__ Cq_sc, uint16_t* __restrict__ Cy,
+    const MTile* __restrict__ tiles, const int32_t* __restrict__ tile_count, int K, int N_out,
+    int32_t* __restrict__ chunk_done, int32_t* __restrict__ task_ctr)
+{
+    using L = BLayout<kGated>;
+    constexpr int BN = kGated ? BNB / 2 : BNB;
+    extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
+    int* const claimed = reinterpret_cast<int*>(smem + kOutBase);   // start of wave 0's staging
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) unsigned char*)(smem)));
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / kWN;
+    const int wn = wave % kWN;
+    const int h = lane >> 5;
+    const int n_mt = *tile_count;
+    const int n_nt = N_out / BN;
+    const int total = n_mt * n_nt;
+    const int KT = K / BK;
+    const int64_t N_w = N_out;
+    const int KS = K / 32;
+
+    // weight copy offsets (bytes): copy j covers k rows kRowsPerCopy * (bi0 + j) + lane / kChunks
+    uint32_t b_voff[kBCopies];
+#pragma unroll
+    for (int j = 0; j < kBCopies; ++j) {
+        const int bi = (kGated ? kBCopies * (wave % (kWaves / 2)) : kBCopies * wave) + j;
+        const int kr = bi * L::kRowsPerCopy + lane / L::kChunks;
+        const int c = bswz<kGated>(lane % L::kChunks, kr);
+        b_voff[j] = static_cast<uint32_t>(lane / L::kChunks) * static_cast<uint32_t>(N_out) + 16u * c;
+    }
+    // fragment and scale addresses (LDS bytes from the stage / scale-slot bases)
+    LaneAddr la;
+    {
+        const int r = lane & 31;
+        la.a0 = r * 64 + 16 * ((0 + h) ^ ((r >> 2) & 3));
+        la.a1 = r * 64 + 16 * ((2 + h) ^ ((r >> 2) & 3));
+        la.asc = r * 16 + h;
+        const int g = lane >> 4, sl = lane & 15;
+        const int hh = g >> 1;
+        const int kr = 16 * hh + (sl >> 1);                     // first read; + 8, + 32, + 40
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            const int m = kGated ? (j & 1) : 0;
+            const int cb = kGated ? 16 * kTN * wn + 32 * (j >> 1) : 32 * kTN * wn + 32 * j;
+            const int col = cb + 16 * (g & 1) + 8 * (sl & 1);
+            la.b[j] = m * L::kMatBytes + kr * L::kRowBytes + 16 * bswz<kGated>(col >> 4, kr) + (col & 15);
+            const int ocol = cb + (lane & 31);                  // this lane's output column of block j
+            la.bsc[j] = (kGated ? m * (kBScBytes / 2) : 0) + h * L::kRowBytes + ocol;
+        }
+    }
+
+    const int xcd = blockIdx.x % kXcdCount;
+    const int blk = gridDim.x / kXcdCount;
+    MTile tile{};
+    int n0 = 0;
+    TaskSrc src{};
+    auto setup = [&](int tk) {
+        int nt;
+        tile = decode_task(tk, n_nt, tiles, nt);
+        n0 = nt * BN;
+        const int rows = tile.row_end - tile.row_begin;
+        src.At = A + static_cast<int64_t>(tile.row_begin) * K;
+        src.Asc = A_sc + static_cast<int64_t>(tile.row_begin) * KS;
+#pragma unroll
+        for (int j = 0; j < kACopies; ++j) {
+            const int r = 16 * (kACopies * wave + j) + lane / 4;
+            const int c = (lane & 3) ^ ((r >> 2) & 3);
+            src.a_voff[j] = static_cast<uint32_t>(min(r, rows - 1)) * static_cast<uint32_t>(K) + 16u * c;
+        }
+        const int64_t eoff = static_cast<int64_t>(tile.expert) * K * N_w;
+        const int64_t esoff = static_cast<int64_t>(tile.expert) * KS * N_w;
+        src.Bm = (kGated && wave >= kWaves / 2 ? B1 : B0) + eoff + n0;
+        if (wave < 4) {
+            src.sc_voff = static_cast<uint32_t>(min(64 * wave + lane, rows - 1)) * static_cast<uint32_t>(KS);
+            src.Bsc = B0_sc;
+        } else {
+            const int c = wave - 4;
+            if (kGated) {
+                // scale copy c: matrix c / 2, block rows 8 (c % 2) .. + 7, 8 lanes per 128-byte row
+                src.Bsc = (c >= 2 ? B1_sc : B0_sc) + esoff + n0 + int64_t{8} * (c & 1) * N_w;
+                src.sc_voff = static_cast<uint32_t>(lane >> 3) * static_cast<uint32_t>(N_out) + 16u * (lane & 7);
+            } else {
+                // scale copy c: block rows 4 c .. + 3, 16 lanes per 256-byte row
+                src.Bsc = B0_sc + esoff + n0 + int64_t{4} * c * N_w;
+                src.sc_voff = static_cast<uint32_t>(lane >> 4) * static_cast<uint32_t>(N_out) + 16u * (lane & 15);
+            }
+        }
+        for (int st = 0; st < kStages; ++st)
+            issue_copies<kGated>(st, lds0, src, b_voff, wave, K, N_w, st < KT);
+    };
+
+    int t = claim_task(claimed, task_ctr, xcd, blk, wave, lane);
+    if (t < total)
+        setup(t);
+    while (t < total) {
+        if (wave == 0) {
+            const int v = atomicAdd(&task_ctr[xcd], lane == 0 ? 1 : 0);
+            *claimed = __builtin_amdgcn_readfirstlane(v);
+        }
+        const int rows = tile.row_end - tile.row_begin;
+        const int nb = __builtin_amdgcn_readfirstlane(
+            min(kTM, max(0, ((rows + 31) / 32 - wm + kWM - 1) / kWM)));
+        f32x16_t acc[kTM][kTN];
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+            for (int j = 0; j < kTN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[i][j][r] = 0.0f;
+        switch (nb) {
+        case 0: mx_k_loop<kGated, 0>(acc, lds0, la, src, b_voff, KT, wave, wm, K, N_w); break;
+        case 1: mx_k_loop<kGated, 1>(acc, lds0, la, src, b_voff, KT, wave, wm, K, N_w); break;
+        default: mx_k_loop<kGated, 2>(acc, lds0, la, src, b_voff, KT, wave, wm, K, N_w); break;
+        }
+        const MTile done = tile;
+        const int done_n0 = n0;
+        const int ci = __builtin_amdgcn_readfirstlane(*claimed);
+        t = ((ci / blk) * kXcdCount + xcd) * blk + ci % blk;
+        __syncthreads();
+        if (t < total)
+            setup(t);
+        const uint32_t stg = lds0 + kOutBase + wave * kOutWaveBytes;
+        if constexpr (kGated)
+            store_h(acc, Cq, Cq_sc, done, done_n0, N_out, stg, wm, wn, lane);
+        else
+            store_y(acc, Cy, done, done_n0, N_out, stg, wm, wn, lane);
+        if (chunk_done != nullptr)
+            count_done(chunk_done, done.chunk, wave, lane);
+    }
+}
+
+}  // namespace big
+
+bool mx_use_big(int64_t H, int64_t F) { return H % 512 == 0 && F % 512 == 0; }
+
 unsigned persistent_grid() { return static_cast<unsigned>(device_info().cu_count * 2); }
 
 hipError_t ensure_smem_limits()
@@ -337,6 +825,12 @@ hipError_t ensure_smem_limits()
     if (e == hipSuccess)
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_mx<false>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&big::grouped_gemm_mx_dma<true>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, big::kSmemBytes);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&big::grouped_gemm_mx_dma<false>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, big::kSmemBytes);
     if (e == hipSuccess && dev < 64)
         done[dev] = true;
     return e;
@@ -355,15 +849,23 @@ hipError_t launch_mx_quantize(const float* v, int64_t rows, int64_t cols, uint8_
     return hipGetLastError();
 }
 
-int mx_fc2_cols_per_tile() { return BNB; }
+int mx_fc2_cols_per_tile(int64_t H, int64_t F) { return mx_use_big(H, F) ? big::BNB : BNB; }
+int mx_row_tile(int64_t H, int64_t F) { return mx_use_big(H, F) ? big::BM : BM; }
 
 hipError_t launch_fc1_mx(const uint8_t* A, const uint8_t* a_scale, const uint8_t* wg,
                          const uint8_t* wg_scale, const uint8_t* wu, const uint8_t* wu_scale,
                          uint8_t* h, uint8_t* h_scale, const MTile* tiles,
-                         const int32_t* tile_count, int64_t H, int64_t F, hipStream_t s)
+                         const int32_t* tile_count, int64_t H, int64_t F, int32_t* task_ctr,
+                         hipStream_t s)
 {
     if (hipError_t e = ensure_smem_limits(); e != hipSuccess)
         return e;
+    if (mx_use_big(H, F)) {
+        big::grouped_gemm_mx_dma<true><<<dim3(device_info().cu_count), dim3(big::kThreads), big::kSmemBytes, s>>>(
+            A, a_scale, wg, wg_scale, wu, wu_scale, h, h_scale, nullptr, tiles, tile_count,
+            static_cast<int>(H), static_cast<int>(F), nullptr, task_ctr);
+        return hipGetLastError();
+    }
     grouped_gemm_mx<true><<<dim3(persistent_grid()), dim3(kThreads), kSmemBytes, s>>>(
         A, a_scale, wg, wg_scale, wu, wu_scale, h, h_scale, nullptr, tiles, tile_count,
         static_cast<int>(H), static_cast<int>(F), nullptr);
@@ -373,10 +875,16 @@ hipError_t launch_fc1_mx(const uint8_t* A, const uint8_t* a_scale, const uint8_t
 hipError_t launch_fc2_mx(const uint8_t* h, const uint8_t* h_scale, const uint8_t* wd,
                          const uint8_t* wd_scale, uint16_t* y, const MTile* tiles,
                          const int32_t* tile_count, int64_t H, int64_t F, int32_t* chunk_done,
-                         hipStream_t s)
+                         int32_t* task_ctr, hipStream_t s)
 {
     if (hipError_t e = ensure_smem_limits(); e != hipSuccess)
         return e;
+    if (mx_use_big(H, F)) {
+        big::grouped_gemm_mx_dma<false><<<dim3(device_info().cu_count), dim3(big::kThreads), big::kSmemBytes, s>>>(
+            h, h_scale, wd, wd_scale, nullptr, nullptr, nullptr, nullptr, y, tiles, tile_count,
+            static_cast<int>(F), static_cast<int>(H), chunk_done, task_ctr);
+        return hipGetLastError();
+    }
     grouped_gemm_mx<false><<<dim3(persistent_grid()), dim3(kThreads), kSmemBytes, s>>>(
         h, h_scale, wd, wd_scale, nullptr, nullptr, nullptr, nullptr, y, tiles, tile_count,
         static_cast<int>(F), static_cast<int>(H), chunk_done);

@@ -141,14 +141,19 @@ hipError_t launch_fc2_f32(const float* h, const float* wd, float* y, const MTile
                           hipStream_t s);
 
 // gemm_mx.hip: OCP-MX grouped GEMMs on scaled fp8 MFMA.
+// task_ctr: kXcdCount zeroed counters for this launch (used by the large-tile kernels).
 hipError_t launch_fc1_mx(const uint8_t* A, const uint8_t* a_scale, const uint8_t* wg,
                          const uint8_t* wg_scale, const uint8_t* wu, const uint8_t* wu_scale,
                          uint8_t* h, uint8_t* h_scale, const MTile* tiles,
-                         const int32_t* tile_count, int64_t H, int64_t F, hipStream_t s);
+                         const int32_t* tile_count, int64_t H, int64_t F, int32_t* task_ctr,
+                         hipStream_t s);
 hipError_t launch_fc2_mx(const uint8_t* h, const uint8_t* h_scale, const uint8_t* wd,
                          const uint8_t* wd_scale, uint16_t* y, const MTile* tiles,
                          const int32_t* tile_count, int64_t H, int64_t F, int32_t* chunk_done,
-                         hipStream_t s);
+                         int32_t* task_ctr, hipStream_t s);
+// MX tile shapes: 256 x 256 when H and F are multiples of 512, else 128 x 128.
+int mx_row_tile(int64_t H, int64_t F);
+int mx_fc2_cols_per_tile(int64_t H, int64_t F);
 hipError_t launch_mx_quantize(const float* v, int64_t rows, int64_t cols, uint8_t* codes,
                               uint8_t* scales, hipStream_t s);
 

@@ -292,7 +292,9 @@ def _mx_weights64(src):
 
 
 @pytest.mark.parametrize("T,H,F,E,k", [(200, 256, 256, 6, 4), (333, 384, 128, 5, 2),
-                                       (96, 128, 384, 32, 4)])
+                                       (96, 128, 384, 32, 4),
+                                       # large tiles (H, F multiples of 512): ragged tails, deep K
+                                       (300, 512, 512, 5, 2), (700, 1024, 512, 3, 2)])
 def test_mx_forward_matches_oracle(T, H, F, E, k):
     inp = synth.make_layer(T=T, H=H, F=F, E=E, k=k, dtype="mxfp8", seed=T)
     ref, *_ = oracle.forward(inp)
@@ -304,12 +306,13 @@ def test_mx_forward_matches_oracle(T, H, F, E, k):
     assert np.array_equal(out, dv.host(dv.forward(mel, d)))
 
 
-def test_mx_h_encoding_agrees_with_oracle():
+@pytest.mark.parametrize("T,H,F,E,k", [(200, 256, 384, 4, 2), (300, 512, 512, 3, 2)],
+                         ids=["small_tiles", "large_tiles"])
+def test_mx_h_encoding_agrees_with_oracle(T, H, F, E, k):
     """fc1's MX-encoded SwiGLU output, read back from the workspace, against the oracle's encoding
     of the exact h.  The scaled fp8 MFMA accumulates with less precision than fp32 (measured: up to
     1.5e-5 of the sum of |terms|), so a few codes may land one step away; every other code and
     nearly every block scale must match."""
-    T, H, F, E, k = 200, 256, 384, 4, 2
     inp = synth.make_layer(T=T, H=H, F=F, E=E, k=k, dtype="mxfp8", seed=11)
     counts, offs, perm, _ = oracle.route(inp.expert_ids, E)
     xp, xps = oracle.permute(inp.x, perm, k), oracle.permute(inp.x_scale, perm, k)
@@ -342,16 +345,18 @@ def test_mx_h_encoding_agrees_with_oracle():
     assert err.mean() <= 1.05 * own.mean()       # as good as encoding the exact h, on average
 
 
-def test_mx_chunked_equals_unchunked():
-    inp = synth.make_layer(T=600, H=256, F=256, E=7, k=2, dtype="mxfp8", seed=5)
+@pytest.mark.parametrize("T,H,F", [(600, 256, 256), (1100, 512, 512)], ids=["small_tiles", "large_tiles"])
+def test_mx_chunked_equals_unchunked(T, H, F):
+    inp = synth.make_layer(T=T, H=H, F=F, E=7, k=2, dtype="mxfp8", seed=5)
     d = dv.layer(inp)
     base = dv.host(dv.forward(mel, d, 0))
     assert np.array_equal(dv.host(dv.forward(mel, d, 256)), base)
     assert np.array_equal(dv.host(dv.forward(mel, d, 512)), base)
 
 
-def test_mx_grouped_ffn_matches_oracle():
-    g = synth.make_grouped(rows=700, H=256, F=256, E_local=2, sources=8, dtype="mxfp8", seed=4)
+@pytest.mark.parametrize("H,F", [(256, 256), (512, 512)], ids=["small_tiles", "large_tiles"])
+def test_mx_grouped_ffn_matches_oracle(H, F):
+    g = synth.make_grouped(rows=700, H=H, F=F, E_local=2, sources=8, dtype="mxfp8", seed=4)
     ref = oracle.grouped_ffn(g)
     y = mel.grouped_ffn_mx(dv.tensor(g.rows), dv.tensor(g.rows_scale), dv.tensor(g.group_offsets),
                            dv.tensor(g.group_expert), dv.tensor(g.w_gate), dv.tensor(g.wg_scale),
