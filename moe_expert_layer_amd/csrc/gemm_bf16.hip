@@ -555,7 +555,7 @@ __device__ __forceinline__ void k_loop(f32x16_t (&acc)[kTM][kTN], uint32_t lds0,
 template <bool kGated>
 __device__ __forceinline__ void store_output_staged(const f32x16_t (&acc)[kTM][kTN], uint16_t* __restrict__ C,
                                                     const MTile& tile, int n0, int N_out, uint32_t stage,
-                                                    int wm, int wn, int lane)
+                                                    int wm, int wn, int lane, bool through)
 {
     constexpr int kOutCols = kGated ? 16 * kTN : 32 * kTN;       // the wave's output columns
     constexpr int PC = kOutCols < 64 ? kOutCols : 64;           // piece columns
@@ -598,8 +598,13 @@ __device__ __forceinline__ void store_output_staged(const f32x16_t (&acc)[kTM][k
                 const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
                     stage + row * (2 * PC) + (((chunk ^ (row >> kSwz)) & (CPR - 1)) << 4));
                 const int grow = tile.row_begin + row_block<kWM>(rp * (PR / 32) + row / 32, wm) + row % 32;
-                if (grow < tile.row_end)
-                    *reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(grow) * N_out + col0) = v;
+                if (grow < tile.row_end) {
+                    uint16_t* dst = C + static_cast<int64_t>(grow) * N_out + col0;
+                    if (through)
+                        store16_through(dst, v);
+                    else
+                        *reinterpret_cast<u32x4_t*>(dst) = v;
+                }
             }
         }
     }
@@ -726,9 +731,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
         if (t < total)
             setup(t);
         store_output_staged<kGated>(acc, C, done, done_n0, N_out, lds0 + kRingBytes + wave * kOutWaveBytes,
-                                     wm, wn, lane);
+                                     wm, wn, lane, chunk_done != nullptr);
         if (chunk_done != nullptr)
-            count_done(chunk_done, done.chunk, wave, lane);
+            count_done_through(chunk_done, done.chunk, wave, lane);
     }
 }
 }  // namespace big

@@ -64,4 +64,22 @@ __device__ __forceinline__ void lds_copy16(const void* base, uint32_t voff, uint
                  :: "v"(voff), "s"(base), "s"(lds) : "memory");
 }
 
+// 16-byte store that writes through the L2 (sc0 sc1), for outputs whose completion other XCDs may
+// watch through the chunk counters.
+__device__ __forceinline__ void store16_through(void* p, u32x4_t v)
+{
+    asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" :: "v"(p), "v"(v) : "memory");
+}
+
+// Counts a finished tile whose outputs all went out with store16_through: every store of the
+// workgroup has completed (vmcnt), then one relaxed device-scope increment.  Unlike a device-scope
+// fence this writes back and invalidates nothing in the L2.
+__device__ __forceinline__ void count_done_through(int32_t* chunk_done, int chunk, int wave, int lane)
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (wave == 0)
+        atomicAdd(&chunk_done[chunk], lane == 0 ? 1 : 0);
+}
+
 }  // namespace moe

@@ -575,7 +575,7 @@ __device__ __forceinline__ void mx_k_loop(f32x16_t (&acc)[kTM][kTN], uint32_t ld
 // fc2 epilogue: bf16 rows through the wave's 2 KiB staging area in pieces of 16 rows x 64 columns.
 __device__ __forceinline__ void store_y(const f32x16_t (&acc)[kTM][kTN], uint16_t* __restrict__ C,
                                         const MTile& tile, int n0, int N_out, uint32_t stage, int wm,
-                                        int wn, int lane)
+                                        int wn, int lane, bool through)
 {
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
@@ -603,9 +603,13 @@ __device__ __forceinline__ void store_y(const f32x16_t (&acc)[kTM][kTN], uint16_
                         stage + row * 128 + (((chunk ^ row) & 7) << 4));
                     const int brow = 16 * half + row;          // row inside the 32-row block
                     const int grow = tile.row_begin + row_block<kWM>(i, wm) + brow;
-                    if (grow < tile.row_end)
-                        *reinterpret_cast<u32x4_t*>(C + static_cast<int64_t>(grow) * N_out + n0 + 128 * wn +
-                                                    64 * cp + 8 * chunk) = v;
+                    if (grow < tile.row_end) {
+                        uint16_t* dst = C + static_cast<int64_t>(grow) * N_out + n0 + 128 * wn + 64 * cp + 8 * chunk;
+                        if (through)
+                            store16_through(dst, v);
+                        else
+                            *reinterpret_cast<u32x4_t*>(dst) = v;
+                    }
                 }
             }
 }
@@ -799,9 +803,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
         if constexpr (kGated)
             store_h(acc, Cq, Cq_sc, done, done_n0, N_out, stg, wm, wn, lane);
         else
-            store_y(acc, Cy, done, done_n0, N_out, stg, wm, wn, lane);
+            store_y(acc, Cy, done, done_n0, N_out, stg, wm, wn, lane, chunk_done != nullptr);
         if (chunk_done != nullptr)
-            count_done(chunk_done, done.chunk, wave, lane);
+            count_done_through(chunk_done, done.chunk, wave, lane);
     }
 }
 

@@ -35,6 +35,8 @@ constexpr int kXcdCount = 8;               // MI355X: workgroup b runs on XCD b 
 // depends on the problem (bf16_row_tile).
 constexpr int kBmF32 = 32;
 constexpr int kBmMx = 128;
+// Chunked mode: consecutive chunks whose tiles of one expert form one run of tasks.
+constexpr int kChunkWindow = 4;
 
 inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

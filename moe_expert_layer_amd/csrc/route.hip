@@ -158,8 +158,9 @@ __global__ __launch_bounds__(kThreads) void route_scatter_kernel(
 // Row-tile table.  Group g covers rows [offsets[g], offsets[g+1]) with expert group_expert[g]
 // (g itself when group_expert is null).  Each group is cut at chunk boundaries (multiples of
 // `chunk` rows) and each piece into tiles of at most bm rows; a run is the tiles of one piece.
-// Chunked (num_chunks > 1): tiles in row order, so the table is chunk-major and chunks complete in
-// order.  Unchunked: first every group's full tiles (row order), then the partial tail tiles, each
+// Chunked (num_chunks > 1): tiles in row order (chunk-major); a run spans a group's tiles within a
+// window of kChunkWindow chunks, so the tasks sharing a weight strip stay together across the
+// window's chunks, and chunks complete in order window by window.  Unchunked: first every group's full tiles (row order), then the partial tail tiles, each
 // its own run, so that the short tasks come last and even out the workgroups' finishing times.
 // One workgroup; groups are handled 1024 at a time.
 __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
@@ -231,13 +232,24 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
                 ++t;
             };
             if (!tails_last) {
+                // a run: the group's tiles inside one window of kChunkWindow chunks
+                const int64_t win = chunk * kChunkWindow;
                 for (int64_t r = rb; r < re;) {
-                    const int64_t cend = min(re, (r / chunk + 1) * chunk);
+                    const int64_t wend = min(re, (r / win + 1) * win);
+                    int run_len = 0;
+                    for (int64_t q = r; q < wend;) {
+                        const int64_t cend = min(wend, (q / chunk + 1) * chunk);
+                        run_len += static_cast<int>((cend - q + bm - 1) / bm);
+                        q = cend;
+                    }
                     const int run_begin = t;
-                    const int run_len = static_cast<int>((cend - r + bm - 1) / bm);
-                    for (int64_t r0 = r; r0 < cend; r0 += bm)
-                        emit(r0, min(cend, r0 + bm), run_begin, run_len);
-                    r = cend;
+                    for (int64_t q = r; q < wend;) {
+                        const int64_t cend = min(wend, (q / chunk + 1) * chunk);
+                        for (int64_t r0 = q; r0 < cend; r0 += bm)
+                            emit(r0, min(cend, r0 + bm), run_begin, run_len);
+                        q = cend;
+                    }
+                    r = wend;
                 }
             } else if (pass == 0) {
                 const int run_begin = t;
