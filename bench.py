@@ -145,8 +145,8 @@ def main():
     M = T * k
     head = args.head_m_size if args.head_m_size is not None else 0
     code = {"f32": mel.F32, "bf16": mel.BF16, "mxfp8": mel.MXFP8}[inp.dtype]
-    ws = torch.empty(mel.workspace_size(mel.problem(T, H, F, E, k, code, max(head, 512))),
-                     dtype=torch.uint8, device=dev)
+    ws_bytes = max(mel.workspace_size(mel.problem(T, H, F, E, k, code, h)) for h in (head, 512))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty((T, H), dtype=torch.float32 if inp.dtype == "f32" else torch.bfloat16,
                       device=dev)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
