@@ -212,8 +212,24 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
                     n = (re - rb) % bm != 0 ? 1 : 0;
                 }
             }
-            const int incl = block_inclusive_scan(n, buf);
+            int incl = block_inclusive_scan(n, buf);
             int t = carry + incl - n;
+            if (tails_last && pass == 1 && G <= kScanThreads) {
+                // longest partial tiles first (all groups fit one pass): the rank of this group's
+                // tail among all tails, larger first, ties by group index
+                __shared__ int tail_rows[kScanThreads];
+                const int mine = n != 0 ? static_cast<int>((re - rb) % bm) : -1;
+                tail_rows[threadIdx.x] = mine;
+                __syncthreads();
+                int rank = 0;
+                for (int q = 0; q < G; ++q) {
+                    const int other = tail_rows[q];
+                    rank += (other > mine || (other == mine && q < g)) ? 1 : 0;
+                }
+                __syncthreads();
+                if (n != 0)
+                    t = carry + rank;
+            }
             auto emit = [&](int64_t r0, int64_t r1, int run_begin, int run_len) {
                 const int c = static_cast<int>(r0 / chunk);
                 if (t < max_tiles) {
