@@ -10,6 +10,10 @@ Each step is bracketed by HIP events on the stream the library launches on; the 
 the brackets.  A second pass of the same steps records every kernel of the library between events
 (moe_timing_*), which gives each kernel's average duration for the roofline figures.
 
+The flush reads the 1 GiB buffer by default (`--flush write` overwrites it instead): either way no
+operand of the previous step stays in the L2s or the Infinity Cache, but a write flush also leaves
+those caches full of dirty lines, whose write-back then lands on whichever kernel runs first.
+
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -52,10 +56,11 @@ def byte_model(inp, M):
 
 
 def kernel_source_digest(files) -> str:
-    """sha256 over the named kernel sources (and the shared headers), to tie counter figures to code."""
+    """sha256 over the named kernel sources, the shared headers and the tile-table builder (task
+    order changes the traffic), to tie counter figures to code."""
     import hashlib
     h = hashlib.sha256()
-    for f in list(files) + ["common.h", "internal.h", "gemm_common.h"]:
+    for f in list(files) + ["common.h", "internal.h", "gemm_common.h", "route.hip"]:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -109,6 +114,8 @@ def main():
     ap.add_argument("--head-m-size", type=int, default=None,
                     help="chunk rows for the reported mode (default: unchunked)")
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--flush", choices=["read", "write"], default="read",
+                    help="how the 1 GiB buffer evicts the caches between steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-chunked", action="store_true")
@@ -149,7 +156,16 @@ def main():
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty((T, H), dtype=torch.float32 if inp.dtype == "f32" else torch.bfloat16,
                       device=dev)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    flush_words = flush.view(torch.int32)
+
+    def do_flush():
+        if args.no_flush:
+            return
+        if args.flush == "write":
+            flush.fill_(1)
+        else:
+            flush_words.sum()
 
     def step(h):
         if inp.dtype == "mxfp8":
@@ -166,8 +182,7 @@ def main():
         torch.cuda.synchronize()
         w0 = time.perf_counter()
         for a, b in ev:
-            if not args.no_flush:
-                flush.fill_(1)
+            do_flush()
             a.record()
             step(h)
             b.record()
@@ -198,8 +213,7 @@ def main():
     mel.timing_reset()
     mel.timing_enable(True)
     for _ in range(args.steps):
-        if not args.no_flush:
-            flush.fill_(1)
+        do_flush()
         step(head)
     kern = mel.timing_collect()
     mel.timing_enable(False)
@@ -235,7 +249,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": inp.dtype, "data": "synthetic",
         "config": {"workload": args.workload, "T": T, "H": H, "F": F, "E": E, "k": k,
-                   "head_m_size": head, "routed_rows": M, "flush_bytes": 0 if args.no_flush else 1 << 30},
+                   "head_m_size": head, "routed_rows": M, "flush_bytes": 0 if args.no_flush else 1 << 30,
+                   "flush": "none" if args.no_flush else args.flush},
         "gemm": {"tflops": gemm_tflops, "frac_of_peak": gemm_tflops / peak, "peak_tflops": peak,
                  "fc1_ms": fc1_ms, "fc2_ms": fc2_ms},
         "kernels_ms": kavg, "hbm": hbm, "roofline": roof,
