@@ -310,8 +310,8 @@ constexpr int BK = 32;
 constexpr int kStages = 4;
 constexpr int kABytes = BM * BK * 2;                   // [256 rows][32 k], 64-byte rows
 constexpr int kBBytes = BK * BNB * 2;                  // [32 k][256 columns] over 1 or 2 matrices
-constexpr int kStageBytes = kABytes + kBBytes;
-constexpr int kRingBytes = kStages * kStageBytes;      // 128 KiB
+constexpr int kBRing = kStages * kABytes;             // the A parts of all stages, then the B parts
+constexpr int kRingBytes = kStages * (kABytes + kBBytes);   // 128 KiB
 constexpr int kOutRows = 32;                           // epilogue staging: 32 rows x 64 columns
 constexpr int kOutWaveBytes = kOutRows * 128;          //   of bf16 per wave (4 KiB)
 constexpr int kSmemBytes = kRingBytes + kWaves * kOutWaveBytes;   // 160 KiB, the whole LDS of a CU
@@ -329,18 +329,14 @@ struct BLayout {
     static_assert(kChunks >= 16, "the k-row swizzle uses chunk bits 2..3");
 };
 
-// Waits until at most n K steps of this wave's copies are still in flight, and for this wave's LDS
-// reads, then joins the workgroup barrier.  One statement with a memory clobber: no memory
-// operation moves across it.
-__device__ __forceinline__ void step_barrier(int n)
+// Waits until at most N of this wave's copies are still in flight, and for this wave's LDS reads,
+// then joins the workgroup barrier.  One statement with a memory clobber: no memory operation
+// moves across it.
+template <int N>
+__device__ __forceinline__ void step_barrier()
 {
-    static_assert(kCopies * 3 <= 63, "vmcnt range");
-    switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(kCopies) : "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(2 * kCopies) : "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(3 * kCopies) : "memory"); break;
-    }
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
 }
 
 // A: LDS row r (64 bytes = 4 chunks of 8 k) keeps logical chunk c at position c ^ ((r >> 2) & 3):
@@ -349,60 +345,49 @@ __device__ __forceinline__ void step_barrier(int n)
 // group land 64 bytes apart within each 256-byte bank window.
 //
 // Copy j of wave w moves A rows 16 * (kACopies * w + j) .. + 15 (4 lanes per row) and B copy
-// slot bi (kRowsPerCopy k rows of one matrix).  The per-lane global offsets below already apply the
-// swizzle; rows past the tile's last row re-read its last row (their results are never stored).
-// Uniform addresses of this wave's copies of one K step (lane parts in a_voff / b_voff).
-struct StepCopies {
-    const uint16_t* a;     // A source of the step
-    const uint16_t* b;     // weight source of the wave's first B copy
-    uint32_t a_lds;        // LDS destination of the wave's first A copy
-    uint32_t b_lds;        // LDS destination of the wave's first B copy
-    bool on;
+// slot bi (kRowsPerCopy k rows of one matrix).  The per-lane global offsets (a_voff, b_voff: the
+// lane's row and swizzled 16-byte chunk) stay fixed for a task; rows past the tile's last row
+// re-read its last row (their results are never stored).  A K step advances the two sources by BK
+// elements of A and BK weight rows.
+struct CopyCtx {
+    const uint16_t* a;     // A at the first k of the next step to fetch
+    const uint16_t* b;     // this wave's weight matrix at that step's first k row
+    uint32_t a_lds;        // LDS destination of the wave's first A copy in stage 0
+    uint32_t b_lds;        // LDS destination of the wave's first B copy in stage 0
 };
 
-template <bool kGated>
-__device__ __forceinline__ StepCopies step_copies(int step, uint32_t lds0, const uint16_t* At,
-                                                  const uint16_t* Bm, int wave, int64_t N_w)
+// Copy C (0 .. kCopies - 1) of a step into stage S: A copies first, then B copies.
+template <int S, int C>
+__device__ __forceinline__ void copy_one(const CopyCtx& s, const uint32_t (&a_voff)[kACopies],
+                                         const uint32_t (&b_voff)[kBCopies])
 {
-    using L = BLayout<kGated>;
-    const uint32_t st = lds0 + static_cast<uint32_t>((step % kStages) * kStageBytes);
-    const int bi0 = kGated ? kBCopies * (wave % (kWaves / 2)) : kBCopies * wave;
-    StepCopies c;
-    c.a = At + step * BK;
-    c.a_lds = st + kACopies * wave * 1024;
-    c.b = Bm + static_cast<int64_t>(step * BK + bi0 * L::kRowsPerCopy) * N_w;
-    c.b_lds = st + kABytes + (kGated ? (wave / (kWaves / 2)) * L::kMatBytes : 0) + bi0 * 1024;
-    return c;
+    if constexpr (C < kACopies)
+        lds_copy16(s.a, a_voff[C], s.a_lds + S * kABytes + C * 1024);
+    else
+        lds_copy16(s.b, b_voff[C - kACopies], s.b_lds + S * kBBytes + (C - kACopies) * 1024);
 }
 
-// Copy C (0 .. kCopies - 1) of a step: A copies first, then B copies.
-template <bool kGated, int C>
-__device__ __forceinline__ void copy_one(const StepCopies& s, const uint32_t (&a_voff)[kACopies],
-                                         const uint32_t (&b_voff)[kBCopies], int64_t N_w)
-{
-    if (!s.on) return;
-    if constexpr (C < kACopies) {
-        lds_copy16(s.a, a_voff[C], s.a_lds + C * 1024);
-    } else {
-        constexpr int j = C - kACopies;
-        lds_copy16(s.b + j * BLayout<kGated>::kRowsPerCopy * N_w, b_voff[j], s.b_lds + j * 1024);
-    }
-}
-
-template <bool kGated, int C0, int... Is>
-__device__ __forceinline__ void copies_impl(std::integer_sequence<int, Is...>, const StepCopies& s,
+template <int S, int C0, int... Is>
+__device__ __forceinline__ void copies_impl(std::integer_sequence<int, Is...>, const CopyCtx& s,
                                             const uint32_t (&a_voff)[kACopies],
-                                            const uint32_t (&b_voff)[kBCopies], int64_t N_w)
+                                            const uint32_t (&b_voff)[kBCopies])
 {
-    (copy_one<kGated, C0 + Is>(s, a_voff, b_voff, N_w), ...);
+    (copy_one<S, C0 + Is>(s, a_voff, b_voff), ...);
 }
 
-// Copies C0 .. C1 - 1 of a step.
-template <bool kGated, int C0, int C1>
-__device__ __forceinline__ void copies(const StepCopies& s, const uint32_t (&a_voff)[kACopies],
-                                       const uint32_t (&b_voff)[kBCopies], int64_t N_w)
+// Copies C0 .. C1 - 1 of a step into stage S.
+template <int S, int C0, int C1>
+__device__ __forceinline__ void copies(const CopyCtx& s, const uint32_t (&a_voff)[kACopies],
+                                       const uint32_t (&b_voff)[kBCopies])
 {
-    copies_impl<kGated, C0>(std::make_integer_sequence<int, C1 - C0>{}, s, a_voff, b_voff, N_w);
+    copies_impl<S, C0>(std::make_integer_sequence<int, C1 - C0>{}, s, a_voff, b_voff);
+}
+
+// Advances the copy sources by one K step.
+__device__ __forceinline__ void advance(CopyCtx& s, int64_t N_w)
+{
+    s.a += BK;
+    s.b += BK * N_w;
 }
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -415,136 +400,148 @@ struct Frags {
     i16x4_t lo[kTN];       // first half of b[j] until its second half arrives
 };
 
-// Fragment read Q of a sub-step: Q = 2 j, 2 j + 1 are the two transposing reads (k 0..3, 4..7 of
-// the lane's 8) of weight block j; Q = 2 kTN + i is A row block i.  a_lane / b_lane[j] are the
-// lane parts of the addresses (see the kernel).
-template <bool kGated, int Q>
-__device__ __forceinline__ void read_one(Frags& f, uint32_t stage, const uint32_t (&a_lane)[2],
-                                         const uint32_t (&b_lane)[kTN], int wm, int ks)
+// Fragment read Q of a sub-step (ks) of LDS stage S, in the order the next sub-step's MFMAs consume
+// them: Q = 0 is A row block 0, Q = 1 + 2 j, 2 + 2 j the two transposing reads (k 0..3, 4..7 of
+// the lane's 8) of weight block j, Q = 2 kTN + i (i >= 1) A row block i.  a_base[ks] / b_base[j]
+// are the lane's addresses in stage 0 (see the kernel); the stage, sub-step and block parts are
+// constants below 64 KiB that the LDS instructions take as immediate offsets.
+template <bool kGated, int S, int KS, int Q>
+__device__ __forceinline__ void read_one(Frags& f, const uint32_t (&a_base)[2], const uint32_t (&b_base)[kTN])
 {
     using L = BLayout<kGated>;
-    if constexpr (Q < 2 * kTN) {
-        constexpr int j = Q / 2;
-        const uint32_t p = stage + kABytes + b_lane[j] + 16 * ks * L::kRowBytes + (Q % 2) * 4 * L::kRowBytes;
+    if constexpr (Q >= 1 && Q <= 2 * kTN) {
+        constexpr int j = (Q - 1) / 2, h = (Q - 1) % 2;
+        const uint32_t p = b_base[j] + S * kBBytes + (16 * KS + 4 * h) * L::kRowBytes;
         const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4_t*>(p));
-        if constexpr (Q % 2 == 0)
+        if constexpr (h == 0)
             f.lo[j] = v;
         else
             f.b[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(f.lo[j], v, 0, 1, 2, 3, 4, 5, 6, 7));
     } else {
-        constexpr int i = Q - 2 * kTN;
+        constexpr int i = Q == 0 ? 0 : Q - 2 * kTN;
         f.a[i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
-            stage + a_lane[ks] + row_block<kWM>(i, wm) * 64);
+            a_base[KS] + S * kABytes + row_block<kWM>(i, 0) * 64);
     }
 }
 
-template <bool kGated, int Q0, int... Is>
-__device__ __forceinline__ void reads_impl(std::integer_sequence<int, Is...>, Frags& f, uint32_t stage,
-                                           const uint32_t (&a_lane)[2], const uint32_t (&b_lane)[kTN],
-                                           int wm, int ks)
+template <bool kGated, int S, int KS, int Q0, int... Is>
+__device__ __forceinline__ void reads_impl(std::integer_sequence<int, Is...>, Frags& f,
+                                           const uint32_t (&a_base)[2], const uint32_t (&b_base)[kTN])
 {
-    (read_one<kGated, Q0 + Is>(f, stage, a_lane, b_lane, wm, ks), ...);
+    (read_one<kGated, S, KS, Q0 + Is>(f, a_base, b_base), ...);
 }
 
-template <bool kGated, int Q0, int Q1>
-__device__ __forceinline__ void reads(Frags& f, uint32_t stage, const uint32_t (&a_lane)[2],
-                                      const uint32_t (&b_lane)[kTN], int wm, int ks)
+template <bool kGated, int S, int KS, int Q0, int Q1>
+__device__ __forceinline__ void reads(Frags& f, const uint32_t (&a_base)[2], const uint32_t (&b_base)[kTN])
 {
-    reads_impl<kGated, Q0>(std::make_integer_sequence<int, Q1 - Q0>{}, f, stage, a_lane, b_lane, wm, ks);
+    reads_impl<kGated, S, KS, Q0>(std::make_integer_sequence<int, Q1 - Q0>{}, f, a_base, b_base);
 }
 
-// Everything a sub-step needs besides the fragments.
-struct SubstepCtx {
-    uint32_t stage;        // LDS stage whose fragments are read
-    int ks;                // sub-step of those fragments
-    StepCopies cp;         // copies issued during this sub-step (when NC > 0)
+// Operands shared by the sub-steps of a K loop.
+struct LoopArgs {
+    const uint32_t (&a_base)[2];
+    const uint32_t (&b_base)[kTN];
+    const uint32_t (&a_voff)[kACopies];
+    const uint32_t (&b_voff)[kBCopies];
 };
 
 // Slot M of a sub-step: MFMA M (row block M / kTN, column block M % kTN), then this slot's share of
-// the next sub-step's fragment reads and of the step's copies.  Reads and copies are spread evenly
-// over the MFMAs, so the wave's in-order issue never stalls on a burst of memory instructions, and
-// no MFMA waits for a read issued just before it.
-template <bool kGated, int NB, int NC, int M>
+// the next sub-step's fragment reads (sub-step KS of stage SR) and of the step's copies (into stage
+// SC).  Reads and copies are spread evenly over the MFMAs, so the wave's in-order issue never
+// stalls on a burst of memory instructions, and no MFMA waits for a read issued just before it.
+template <bool kGated, int NB, int C0, int NC, int SR, int KS, int SC, int M>
 __device__ __forceinline__ void slot(f32x16_t (&acc)[kTM][kTN], const Frags& use, Frags& load,
-                                     const SubstepCtx& c, const uint32_t (&a_lane)[2],
-                                     const uint32_t (&b_lane)[kTN], const uint32_t (&a_voff)[kACopies],
-                                     const uint32_t (&b_voff)[kBCopies], int64_t N_w, int wm)
+                                     const CopyCtx& cp, const LoopArgs& g)
 {
     constexpr int NM = NB * kTN, NR = 2 * kTN + NB;
     acc[M / kTN][M % kTN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(use.a[M / kTN], use.b[M % kTN],
                                                                     acc[M / kTN][M % kTN], 0, 0, 0);
-    reads<kGated, M * NR / NM, (M + 1) * NR / NM>(load, c.stage, a_lane, b_lane, wm, c.ks);
-    copies<kGated, M * NC / NM, (M + 1) * NC / NM>(c.cp, a_voff, b_voff, N_w);
+    reads<kGated, SR, KS, M * NR / NM, (M + 1) * NR / NM>(load, g.a_base, g.b_base);
+    copies<SC, C0 + M * NC / NM, C0 + (M + 1) * NC / NM>(cp, g.a_voff, g.b_voff);
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool kGated, int NB, int NC, int... Ms>
+template <bool kGated, int NB, int C0, int NC, int SR, int KS, int SC, int... Ms>
 __device__ __forceinline__ void slots(std::integer_sequence<int, Ms...>, f32x16_t (&acc)[kTM][kTN],
-                                      const Frags& use, Frags& load, const SubstepCtx& c,
-                                      const uint32_t (&a_lane)[2], const uint32_t (&b_lane)[kTN],
-                                      const uint32_t (&a_voff)[kACopies],
-                                      const uint32_t (&b_voff)[kBCopies], int64_t N_w, int wm)
+                                      const Frags& use, Frags& load, const CopyCtx& cp,
+                                      const LoopArgs& g)
 {
-    (slot<kGated, NB, NC, Ms>(acc, use, load, c, a_lane, b_lane, a_voff, b_voff, N_w, wm), ...);
+    (slot<kGated, NB, C0, NC, SR, KS, SC, Ms>(acc, use, load, cp, g), ...);
 }
 
-// One k sub-step: the NB * kTN MFMAs on `use`, the fragment reads of sub-step c.ks of c.stage into
-// `load`, and NC copies of c.cp.  A wave without MFMAs (NB = 0) only issues the copies.
-template <bool kGated, int NB, int NC>
+// One k sub-step: the NB * kTN MFMAs on `use`, the fragment reads of sub-step KS of stage SR into
+// `load`, and copies C0 .. C0 + NC - 1 of cp's step into stage SC.  A wave without MFMAs (NB = 0)
+// only issues the copies.
+template <bool kGated, int NB, int C0, int NC, int SR, int KS, int SC>
 __device__ __forceinline__ void substep(f32x16_t (&acc)[kTM][kTN], const Frags& use, Frags& load,
-                                        const SubstepCtx& c, const uint32_t (&a_lane)[2],
-                                        const uint32_t (&b_lane)[kTN], const uint32_t (&a_voff)[kACopies],
-                                        const uint32_t (&b_voff)[kBCopies], int64_t N_w, int wm)
+                                        const CopyCtx& cp, const LoopArgs& g)
 {
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NB == 0)
-        copies<kGated, 0, NC>(c.cp, a_voff, b_voff, N_w);
+        copies<SC, C0, C0 + NC>(cp, g.a_voff, g.b_voff);
     else
-        slots<kGated, NB, NC>(std::make_integer_sequence<int, NB * kTN>{}, acc, use, load, c, a_lane,
-                              b_lane, a_voff, b_voff, N_w, wm);
+        slots<kGated, NB, C0, NC, SR, KS, SC>(std::make_integer_sequence<int, NB * kTN>{}, acc, use,
+                                              load, cp, g);
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Issues all copies of one K step (task prologue).
-template <bool kGated>
-__device__ __forceinline__ void issue_step(int step, uint32_t lds0, const uint16_t* At,
-                                           const uint32_t (&a_voff)[kACopies], const uint16_t* Bm,
-                                           const uint32_t (&b_voff)[kBCopies], int wave, int64_t N_w)
+// Issues copies C0 .. C1 - 1 of cp's step into stage S (task prologue).
+template <int S, int C0, int C1>
+__device__ __forceinline__ void issue(const CopyCtx& cp, const uint32_t (&a_voff)[kACopies],
+                                      const uint32_t (&b_voff)[kBCopies])
 {
-    StepCopies c = step_copies<kGated>(step, lds0, At, Bm, wave, N_w);
-    c.on = true;
-    copies<kGated, 0, kCopies>(c, a_voff, b_voff, N_w);
+    copies<S, C0, C1>(cp, a_voff, b_voff);
 }
 
-template <bool kGated, int NB>
-__device__ __forceinline__ void k_loop(f32x16_t (&acc)[kTM][kTN], uint32_t lds0, const uint16_t* At,
-                                       const uint32_t (&a_voff)[kACopies], const uint16_t* Bm,
-                                       const uint32_t (&b_voff)[kBCopies], const uint32_t (&a_lane)[2],
-                                       const uint32_t (&b_lane)[kTN], int64_t N_w, int KT, int wave,
-                                       int wm)
+// The copies of K step s go out in two halves: the A half during the second sub-step of step
+// s - kStages, the B half during the first sub-step of step s - kStages + 1, so every MFMA slot of
+// a step carries about the same number of copies.  Copies are issued in step order, so "step s has
+// landed" is "at most (the copies issued after it) are in flight".
+constexpr int kHalfA = kACopies;                  // copies 0 .. kHalfA - 1 of a step are its A half
+
+// K step kt (kt % kStages = S): sub-step 1 of stage S on the fragments of sub-step 0, with the B
+// half of step kt + kStages - 1 (into stage S - 1) when kCopyB; the barrier after which step kt + 1
+// has landed (at most W copies still in flight; no barrier for W < 0) and stage S is free; sub-step
+// 0 of stage S + 1 on the fragments of sub-step 1, with the A half of step kt + kStages (into
+// stage S) when kCopyA.
+template <bool kGated, int NB, int S, bool kCopyB, bool kCopyA, int W>
+__device__ __forceinline__ void k_step(f32x16_t (&acc)[kTM][kTN], Frags& f0, Frags& f1, CopyCtx& cp,
+                                       const LoopArgs& g, int64_t N_w)
 {
-    // the caller issued the copies of steps 0 .. min(KT, kStages) - 1
-    step_barrier((KT < kStages ? KT : kStages) - 1);
+    substep<kGated, NB, kHalfA, kCopyB ? kCopies - kHalfA : 0, S, 1, (S + kStages - 1) % kStages>(
+        acc, f0, f1, cp, g);
+    if constexpr (kCopyB)
+        advance(cp, N_w);
+    if constexpr (W >= 0)
+        step_barrier<W>();
+    // after the last step this reads a stale stage whose fragments are never used
+    substep<kGated, NB, 0, kCopyA ? kHalfA : 0, (S + 1) % kStages, 0, S>(acc, f1, f0, cp, g);
+}
+
+// The K loop of one task.  KT is a multiple of kStages (at least kStages); the caller issued the
+// copies of steps 0 .. kStages - 2 and the A half of step kStages - 1, and cp points at that step.
+// The body is unrolled over the kStages stages, so every LDS address is a lane base plus a
+// constant.
+template <bool kGated, int NB>
+__device__ __forceinline__ void k_loop(f32x16_t (&acc)[kTM][kTN], CopyCtx cp, const LoopArgs& g,
+                                       int64_t N_w, int KT)
+{
+    static_assert(kStages == 4, "the unrolled body below covers four stages");
+    constexpr int K2 = 2 * kCopies;
+    step_barrier<K2 + kHalfA>();                   // step 0 landed
     Frags f0, f1;
-    SubstepCtx c{lds0, 0, {}};
     if constexpr (NB > 0)
-        reads<kGated, 0, 2 * kTN + NB>(f0, lds0, a_lane, b_lane, wm, 0);
-    for (int kt = 0; kt < KT; ++kt) {
-        c.stage = lds0 + static_cast<uint32_t>((kt % kStages) * kStageBytes);
-        c.ks = 1;
-        substep<kGated, NB, 0>(acc, f0, f1, c, a_lane, b_lane, a_voff, b_voff, N_w, wm);
-        if (kt + 1 < KT) {
-            // step kt + 1 landed (this wave's copies, then everyone's), and every wave is done
-            // reading stage kt % kStages, which the copies of step kt + kStages may now refill
-            step_barrier(min(2, KT - 2 - kt));
-        }
-        // after the last step this reads a stale stage whose fragments are never used
-        c.stage = lds0 + static_cast<uint32_t>(((kt + 1) % kStages) * kStageBytes);
-        c.ks = 0;
-        c.cp = step_copies<kGated>(kt + kStages, lds0, At, Bm, wave, N_w);
-        c.cp.on = kt + kStages < KT;
-        substep<kGated, NB, kCopies>(acc, f1, f0, c, a_lane, b_lane, a_voff, b_voff, N_w, wm);
+        reads<kGated, 0, 0, 0, 2 * kTN + NB>(f0, g.a_base, g.b_base);
+    for (int kt = 0; kt < KT - kStages; kt += kStages) {
+        k_step<kGated, NB, 0, true, true, K2>(acc, f0, f1, cp, g, N_w);
+        k_step<kGated, NB, 1, true, true, K2>(acc, f0, f1, cp, g, N_w);
+        k_step<kGated, NB, 2, true, true, K2>(acc, f0, f1, cp, g, N_w);
+        k_step<kGated, NB, 3, true, true, K2>(acc, f0, f1, cp, g, N_w);
     }
+    k_step<kGated, NB, 0, true, false, K2>(acc, f0, f1, cp, g, N_w);
+    k_step<kGated, NB, 1, false, false, kCopies>(acc, f0, f1, cp, g, N_w);
+    k_step<kGated, NB, 2, false, false, 0>(acc, f0, f1, cp, g, N_w);
+    k_step<kGated, NB, 3, false, false, -1>(acc, f0, f1, cp, g, N_w);
 }
 
 // Epilogue through LDS.  The wave's output (64 rows x 64 columns for fc1, 64 x 128 for fc2) goes
@@ -638,24 +635,30 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
     const int KT = K / BK;
     const int64_t N_w = N_out;
 
-    // copy sources, lane parts (bytes): B copy j covers k rows kRowsPerCopy * (bi0 + j) + lane / kChunks
+    // copy sources, lane parts (bytes from the step's first weight row): B copy j covers k rows
+    // kRowsPerCopy * (bi0 + j) .. + kRowsPerCopy - 1, lane / kChunks within them
+    const int bi0 = kGated ? kBCopies * (wave % (kWaves / 2)) : kBCopies * wave;
     uint32_t b_voff[kBCopies];
 #pragma unroll
     for (int j = 0; j < kBCopies; ++j) {
-        const int bi = (kGated ? kBCopies * (wave % (kWaves / 2)) : kBCopies * wave) + j;
-        const int kr = bi * L::kRowsPerCopy + lane / L::kChunks;
+        const int kr = (bi0 + j) * L::kRowsPerCopy + lane / L::kChunks;
         const int c = (lane % L::kChunks) ^ (4 * (kr & 3));
-        b_voff[j] = static_cast<uint32_t>(lane / L::kChunks) * static_cast<uint32_t>(N_out) * 2u +
-                    16u * c;
+        b_voff[j] = static_cast<uint32_t>(kr) * static_cast<uint32_t>(N_out) * 2u + 16u * c;
     }
-    // fragment reads, lane parts (LDS bytes from the stage base)
-    uint32_t a_lane[2];
+    CopyCtx cp;
+    cp.a_lds = lds0 + kACopies * wave * 1024;
+    cp.b_lds = lds0 + kBRing + (kGated ? (wave / (kWaves / 2)) * L::kMatBytes : 0) + bi0 * 1024;
+    // fragment reads: the lane's LDS addresses in stage 0 (A: row block 0 of this wave, sub-step ks;
+    // B: weight block j, sub-step 0).  Each is hidden from the optimiser so that it stays one
+    // register and the constant parts of every read go into the instruction's offset field.
+    uint32_t a_base[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         const int r = lane & 31;
-        a_lane[ks] = r * 64 + 16 * ((2 * ks + (lane >> 5)) ^ ((r >> 2) & 3));
+        a_base[ks] = lds0 + row_block<kWM>(0, wm) * 64 + r * 64 + 16 * ((2 * ks + (lane >> 5)) ^ ((r >> 2) & 3));
+        asm volatile("" : "+v"(a_base[ks]));
     }
-    uint32_t b_lane[kTN];
+    uint32_t b_base[kTN];
     {
         const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
         const int kr = 8 * (g >> 1) + e;                       // + 16 ks + 4 for the upper half
@@ -663,7 +666,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
         for (int j = 0; j < kTN; ++j) {
             const int m = kGated ? (j & 1) : 0;
             const int col = (kGated ? 16 * kTN * wn + 32 * (j >> 1) : 32 * kTN * wn + 32 * j) + 16 * (g & 1) + 4 * q;
-            b_lane[j] = m * L::kMatBytes + kr * L::kRowBytes + 16 * ((col >> 3) ^ (4 * e)) + 2 * (col & 7);
+            b_base[j] = lds0 + kBRing + m * L::kMatBytes + kr * L::kRowBytes + 16 * ((col >> 3) ^ (4 * e)) +
+                        2 * (col & 7);
+            asm volatile("" : "+v"(b_base[j]));
         }
     }
 
@@ -674,25 +679,27 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
     // epilogue, so the epilogue hides their latency.
     MTile tile{};
     int n0 = 0;
-    const uint16_t* At = A;
-    const uint16_t* Bm = B0;
     uint32_t a_voff[kACopies];
     auto setup = [&](int t) {
         int nt;
         tile = decode_task(t, n_nt, tiles, nt);
         n0 = nt * BN;
         const int rows = tile.row_end - tile.row_begin;
-        At = A + static_cast<int64_t>(tile.row_begin) * K;
 #pragma unroll
         for (int j = 0; j < kACopies; ++j) {
             const int r = 16 * (kACopies * wave + j) + lane / 4;
             const int c = (lane & 3) ^ ((r >> 2) & 3);
             a_voff[j] = static_cast<uint32_t>(min(r, rows - 1)) * static_cast<uint32_t>(K) * 2u + 16u * c;
         }
-        Bm = (kGated && wave >= kWaves / 2 ? B1 : B0) + static_cast<int64_t>(tile.expert) * K * N_w + n0;
-        const int pre = KT < kStages ? KT : kStages;
-        for (int st = 0; st < pre; ++st)
-            issue_step<kGated>(st, lds0, At, a_voff, Bm, b_voff, wave, N_w);
+        cp.a = A + static_cast<int64_t>(tile.row_begin) * K;
+        cp.b = (kGated && wave >= kWaves / 2 ? B1 : B0) + static_cast<int64_t>(tile.expert) * K * N_w + n0;
+        issue<0, 0, kCopies>(cp, a_voff, b_voff);
+        advance(cp, N_w);
+        issue<1, 0, kCopies>(cp, a_voff, b_voff);
+        advance(cp, N_w);
+        issue<2, 0, kCopies>(cp, a_voff, b_voff);
+        advance(cp, N_w);
+        issue<3, 0, kHalfA>(cp, a_voff, b_voff);
     };
 
     int t = claim_task(claimed, task_ctr, xcd, blk, wave, lane);
@@ -717,10 +724,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
                 for (int r = 0; r < 16; ++r)
                     acc[i][j][r] = 0.0f;
 
+        const LoopArgs g{a_base, b_base, a_voff, b_voff};
         switch (nb) {
-        case 0: k_loop<kGated, 0>(acc, lds0, At, a_voff, Bm, b_voff, a_lane, b_lane, N_w, KT, wave, wm); break;
-        case 1: k_loop<kGated, 1>(acc, lds0, At, a_voff, Bm, b_voff, a_lane, b_lane, N_w, KT, wave, wm); break;
-        default: k_loop<kGated, 2>(acc, lds0, At, a_voff, Bm, b_voff, a_lane, b_lane, N_w, KT, wave, wm); break;
+        case 0: k_loop<kGated, 0>(acc, cp, g, N_w, KT); break;
+        case 1: k_loop<kGated, 1>(acc, cp, g, N_w, KT); break;
+        default: k_loop<kGated, 2>(acc, cp, g, N_w, KT); break;
         }
         const MTile done = tile;
         const int done_n0 = n0;
@@ -749,6 +757,7 @@ constexpr int kBigFc1Cols = big::BNB / 2;    // output columns per fc1 task
 constexpr int kBigFc2Cols = big::BNB;        // output columns per fc2 task
 constexpr int kBigSmem = big::kSmemBytes;
 
+// The large kernels run K loops of whole multiples of four steps (H / 32, F / 32).
 bool use_big(int64_t H, int64_t F) { return H % kBigFc2Cols == 0 && F % kBigFc1Cols == 0; }
 
 hipError_t ensure_smem_limits()
