@@ -344,8 +344,8 @@ constexpr int BK = 64;
 constexpr int kStages = 4;
 constexpr int kABytes = BM * BK;
 constexpr int kBBytes = BK * BNB;
-constexpr int kStageBytes = kABytes + kBBytes;        // 32 KiB
-constexpr int kRingBytes = kStages * kStageBytes;     // 128 KiB
+constexpr int kBRing = kStages * kABytes;            // the A parts of all stages, then the B parts
+constexpr int kRingBytes = kStages * (kABytes + kBBytes);   // 128 KiB
 constexpr int kScaleSteps = 8;                        // K steps per scale slot (16 blocks of 32)
 constexpr int kAScBytes = BM * 16;                    // [256 rows][16 blocks]
 constexpr int kBScBytes = 16 * BNB;                   // [16 blocks][256 columns]
@@ -377,68 +377,55 @@ __device__ __forceinline__ int bswz(int c, int kr)
     return BLayout<kGated>::kChunks == 16 ? c ^ ((kr & 7) << 1) : c ^ (((kr >> 1) & 3) << 1);
 }
 
-// Copies in flight after the group of step s: data copies, plus one scale copy per wave with
-// every eighth step.
-__device__ __forceinline__ int group_copies(int s, int KT)
+// Copies of K step s in flight: data copies, plus one scale copy per wave when s opens a scale
+// block (s % 8 == 0); none past the last step.
+constexpr int group_copies(int s_pos, bool exists)
 {
-    return s >= KT ? 0 : kDataCopies + (s % kScaleSteps == 0 ? 1 : 0);
+    return exists ? kDataCopies + (s_pos % kScaleSteps == 0 ? 1 : 0) : 0;
 }
 
-// Waits until at most n copies of this wave are in flight and for its LDS reads, then joins the
+// Waits until at most N copies of this wave are in flight and for its LDS reads, then joins the
 // workgroup barrier (one statement with a memory clobber).
-__device__ __forceinline__ void step_barrier(int n)
+template <int N>
+__device__ __forceinline__ void step_barrier()
 {
-    switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    case 5: asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    case 8: asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    case 9: asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    case 12: asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    case 13: asm volatile("s_waitcnt vmcnt(13) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    }
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
 }
 
-// Per-task copy sources (uniform bases, per-lane byte offsets).
-struct TaskSrc {
-    const uint8_t* At;        // A rows of the tile
-    const uint8_t* Bm;        // this wave's weight matrix, expert and first column applied
-    const uint8_t* Asc;       // A scale rows of the tile
-    const uint8_t* Bsc;       // this wave's scale-copy matrix (waves >= 4), expert and column applied
-    uint32_t a_voff[kACopies];
-    uint32_t sc_voff;         // lane offset of this wave's scale copy
+// Copy sources of the next step to fetch (uniform) and the LDS destinations of this wave's copies
+// in stage 0 / scale slot 0.  A step advances A by BK bytes and the weights by BK rows; a scale
+// block advances the scale source by sc_step bytes.
+struct MxCopy {
+    const uint8_t* a;
+    const uint8_t* b;
+    const uint8_t* sc;
+    int64_t sc_step;
+    uint32_t a_lds, b_lds, sc_lds;
 };
 
-template <bool kGated>
-__device__ __forceinline__ void issue_copies(int step, uint32_t lds0, const TaskSrc& t,
-                                             const uint32_t (&b_voff)[kBCopies], int wave, int K,
-                                             int64_t N_w, bool on)
+// The copies of one K step into stage S, with the scales of the block it opens into slot Q when
+// kScale.
+template <bool kScale, int S, int Q>
+__device__ __forceinline__ void mx_issue(const MxCopy& c, const uint32_t (&a_voff)[kACopies],
+                                         const uint32_t (&b_voff)[kBCopies], uint32_t sc_voff)
 {
-    using L = BLayout<kGated>;
-    if (!on)
-        return;
-    if (step % kScaleSteps == 0) {
-        const int blk = step / kScaleSteps;
-        const uint32_t slot = lds0 + kScRing + (blk & 1) * kScSlotBytes;
-        if (wave < 4) {
-            lds_copy16(t.Asc + 16 * blk, t.sc_voff, slot + wave * 1024);
-        } else {
-            const int c = wave - 4;
-            const int64_t kb0 = int64_t{16} * blk;
-            lds_copy16(t.Bsc + kb0 * N_w, t.sc_voff, slot + kAScBytes + c * 1024);
-        }
-    }
-    const uint32_t st = lds0 + static_cast<uint32_t>((step % kStages) * kStageBytes);
+    if constexpr (kScale)
+        lds_copy16(c.sc, sc_voff, c.sc_lds + Q * kScSlotBytes);
 #pragma unroll
     for (int j = 0; j < kACopies; ++j)
-        lds_copy16(t.At + step * BK, t.a_voff[j], st + (kACopies * wave + j) * 1024);
-    const int bi0 = kGated ? kBCopies * (wave % (kWaves / 2)) : kBCopies * wave;
-    const uint32_t bst = st + kABytes + (kGated ? (wave / (kWaves / 2)) * L::kMatBytes : 0);
+        lds_copy16(c.a, a_voff[j], c.a_lds + S * kABytes + j * 1024);
 #pragma unroll
     for (int j = 0; j < kBCopies; ++j)
-        lds_copy16(t.Bm + (static_cast<int64_t>(step) * BK + (bi0 + j) * L::kRowsPerCopy) * N_w,
-                   b_voff[j], bst + (bi0 + j) * 1024);
+        lds_copy16(c.b, b_voff[j], c.b_lds + S * kBBytes + j * 1024);
+}
+
+__device__ __forceinline__ void mx_advance(MxCopy& c, int64_t N_w, bool scale)
+{
+    c.a += BK;
+    c.b += BK * N_w;
+    if (scale)
+        c.sc += c.sc_step;
 }
 
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
@@ -467,12 +454,24 @@ __device__ __forceinline__ int read_u8(uint32_t p)
 }
 
 // Lane parts of the fragment and scale addresses.
+// The lane's LDS addresses in stage 0 / scale slot 0 (row block 0 of this wave, k step 0 of the
+// scale block).  Each is one register hidden from the optimiser, so the stage, slot, step and
+// block parts below are immediate offsets of the LDS instructions.
 struct LaneAddr {
-    uint32_t a0, a1;          // A chunks h and 2 + h of the lane's row (plus the row block)
+    uint32_t a0, a1;          // A chunks h and 2 + h of the lane's row
     uint32_t b[kTN];          // first transposing read of weight block j
     uint32_t asc;             // A scale byte: row * 16 + h
-    uint32_t bsc[kTN];        // weight scale byte of block j: column + h * row bytes
+    uint32_t bsc;             // weight scale byte of block 0: column + h * row bytes (block j at
+                              // the constant bsc_off<kGated>(j) from it)
 };
+
+// Offset of weight block j's scale bytes from block 0's (the lane's column moves by the block's
+// column base, and for the up matrix of fc1 by half a scale slot).
+template <bool kGated>
+constexpr int bsc_off(int j)
+{
+    return kGated ? (j & 1) * (kBScBytes / 2) + 32 * (j >> 1) : 32 * j;
+}
 
 struct MxFrags {
     i32x8_t a[kTM];
@@ -491,85 +490,128 @@ __device__ __forceinline__ void mfma_pair(f32x16_t (&acc)[kTM][kTN], const MxFra
                 A.a[i], b[jj], acc[i][j0 + jj], 0, 0, 0, A.sa[i], 0, sb[jj]);
 }
 
-// One K step: the MFMAs of weight blocks 0-1 (fragments loaded during the previous step) while the
-// fragments of blocks 2-3 are read; the barrier; the MFMAs of blocks 2-3 while the next step's A and
-// blocks 0-1 fragments are read and the copies of step kt + 4 are issued.
-template <bool kGated, int NB>
-__device__ __forceinline__ void mx_step(f32x16_t (&acc)[kTM][kTN], const MxFrags& Acur, MxFrags& Anext,
-                                        i32x8_t (&b01)[2], int (&sb01)[2], i32x8_t (&b23)[2],
-                                        int (&sb23)[2], int kt, int KT, uint32_t lds0, const LaneAddr& la,
-                                        const TaskSrc& t, const uint32_t (&b_voff)[kBCopies],
-                                        int wave, int wm, int K, int64_t N_w)
+// Fragments of K step position p (stage p % 4, scale slot P): A row blocks and their scales.
+template <int NB, int P, int p>
+__device__ __forceinline__ void read_a_frags(MxFrags& A, const LaneAddr& la)
 {
-    using L = BLayout<kGated>;
-    const uint32_t stage = lds0 + static_cast<uint32_t>((kt % kStages) * kStageBytes);
-    const uint32_t bst = stage + kABytes;
-    const uint32_t sc = lds0 + kScRing + ((kt / kScaleSteps) & 1) * kScSlotBytes;
-    const int kbl = 2 * (kt % kScaleSteps);
-    if constexpr (NB > 0) {
-        __builtin_amdgcn_sched_barrier(0);
-        // blocks 2-3 of this step
-        b23[0] = read_b<L::kRowBytes>(bst + la.b[2]);
-        sb23[0] = read_u8(sc + kAScBytes + la.bsc[2] + kbl * L::kRowBytes);
-        b23[1] = read_b<L::kRowBytes>(bst + la.b[3]);
-        sb23[1] = read_u8(sc + kAScBytes + la.bsc[3] + kbl * L::kRowBytes);
-        mfma_pair<NB>(acc, Acur, b01, sb01, 0);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    if (kt + 1 < KT)
-        step_barrier(group_copies(kt + 2, KT) + group_copies(kt + 3, KT));
-    {
-        // the next step's fragments (a stale stage after the last step: never used)
-        const int kn = kt + 1;
-        const uint32_t nstage = lds0 + static_cast<uint32_t>((kn % kStages) * kStageBytes);
-        const uint32_t nsc = lds0 + kScRing + ((kn / kScaleSteps) & 1) * kScSlotBytes;
-        const int nkbl = 2 * (kn % kScaleSteps);
-        __builtin_amdgcn_sched_barrier(0);
-        issue_copies<kGated>(kt + kStages, lds0, t, b_voff, wave, K, N_w, kt + kStages < KT);
-        if constexpr (NB > 0) {
+    constexpr int S = p % kStages;
 #pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                Anext.a[i] = read_a(nstage + la.a0 + row_block<kWM>(i, wm) * 64,
-                                    nstage + la.a1 + row_block<kWM>(i, wm) * 64);
-                Anext.sa[i] = read_u8(nsc + la.asc + row_block<kWM>(i, wm) * 16 + nkbl);
-            }
-            mfma_pair<NB>(acc, Acur, b23, sb23, 2);
-            b01[0] = read_b<L::kRowBytes>(nstage + kABytes + la.b[0]);
-            sb01[0] = read_u8(nsc + kAScBytes + la.bsc[0] + nkbl * L::kRowBytes);
-            b01[1] = read_b<L::kRowBytes>(nstage + kABytes + la.b[1]);
-            sb01[1] = read_u8(nsc + kAScBytes + la.bsc[1] + nkbl * L::kRowBytes);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < NB; ++i) {
+        A.a[i] = read_a(la.a0 + S * kABytes + row_block<kWM>(i, 0) * 64, la.a1 + S * kABytes + row_block<kWM>(i, 0) * 64);
+        A.sa[i] = read_u8(la.asc + P * kScSlotBytes + row_block<kWM>(i, 0) * 16 + 2 * p);
     }
 }
 
-template <bool kGated, int NB>
-__device__ __forceinline__ void mx_k_loop(f32x16_t (&acc)[kTM][kTN], uint32_t lds0, const LaneAddr& la,
-                                          const TaskSrc& t, const uint32_t (&b_voff)[kBCopies], int KT,
-                                          int wave, int wm, int K, int64_t N_w)
+// Weight blocks J0, J0 + 1 of K step position p and their scales.
+template <bool kGated, int P, int p, int J0>
+__device__ __forceinline__ void read_b_frags(i32x8_t (&b)[2], int (&sb)[2], const LaneAddr& la)
 {
     using L = BLayout<kGated>;
-    // the caller issued the groups of steps 0 .. 3
-    step_barrier(group_copies(1, KT) + group_copies(2, KT) + group_copies(3, KT));
+    constexpr int S = p % kStages;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        b[jj] = read_b<L::kRowBytes>(la.b[J0 + jj] + S * kBBytes);
+        sb[jj] = read_u8(la.bsc + bsc_off<kGated>(J0 + jj) + P * kScSlotBytes + 2 * p * L::kRowBytes);
+    }
+}
+
+// K step kt at position p of a 16-step unit (stage p % 4; scales of the 8-step block in slot
+// p / 8): the MFMAs of weight blocks 0-1 (fragments loaded during the previous step) while the
+// fragments of blocks 2-3 are read; the barrier after which step kt + 1 has landed (W copies may
+// stay in flight; none when W < 0); the copies of step kt + 4 (when kCopy); the next step's A and
+// blocks 0-1 fragments; the MFMAs of blocks 2-3.
+template <bool kGated, int NB, int p, bool kCopy, int W>
+__device__ __forceinline__ void mx_step(f32x16_t (&acc)[kTM][kTN], const MxFrags& Acur, MxFrags& Anext,
+                                        i32x8_t (&b01)[2], int (&sb01)[2], i32x8_t (&b23)[2],
+                                        int (&sb23)[2], const LaneAddr& la, MxCopy& cp,
+                                        const uint32_t (&a_voff)[kACopies],
+                                        const uint32_t (&b_voff)[kBCopies], uint32_t sc_voff, int64_t N_w)
+{
+    constexpr int P = p / kScaleSteps, q = p % kScaleSteps;                  // slot, step in block
+    constexpr int pn = (p + 1) % (2 * kScaleSteps);                          // the next step
+    constexpr int Pn = pn / kScaleSteps, qn = pn % kScaleSteps;
+    if constexpr (NB > 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        read_b_frags<kGated, P, q, 2>(b23, sb23, la);
+        mfma_pair<NB>(acc, Acur, b01, sb01, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (W >= 0)
+        step_barrier<W>();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kCopy) {
+        // step kt + 4 lands in this step's stage; it opens a scale block when q == 4 (other slot)
+        mx_issue<q == 4, p % kStages, 1 - P>(cp, a_voff, b_voff, sc_voff);
+        mx_advance(cp, N_w, q == 4);
+    }
+    if constexpr (NB > 0) {
+        // after the last step these read a stale stage whose fragments are never used
+        read_a_frags<NB, Pn, qn>(Anext, la);
+        mfma_pair<NB>(acc, Acur, b23, sb23, 2);
+        read_b_frags<kGated, Pn, qn, 0>(b01, sb01, la);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+constexpr int kUnit = 2 * kScaleSteps;    // steps per unrolled unit: four stages, two scale slots
+
+// Copies in flight at the barrier of the step at position p (steps kt + 2 and kt + 3; in the last
+// unit of a task, only those that exist).
+template <int p, bool kLast>
+constexpr int mx_wait()
+{
+    return group_copies(p + 2, !kLast || p + 2 < kUnit) + group_copies(p + 3, !kLast || p + 3 < kUnit);
+}
+
+// One unit of 16 K steps; in the last unit of a task, copies stop after position 11 and the last
+// step has no barrier.
+template <bool kGated, int NB, bool kLast, int... Ps>
+__device__ __forceinline__ void mx_unit_impl(std::integer_sequence<int, Ps...>, f32x16_t (&acc)[kTM][kTN],
+                                             MxFrags& A0, MxFrags& A1, i32x8_t (&b01)[2], int (&sb01)[2],
+                                             i32x8_t (&b23)[2], int (&sb23)[2], const LaneAddr& la,
+                                             MxCopy& cp, const uint32_t (&a_voff)[kACopies],
+                                             const uint32_t (&b_voff)[kBCopies], uint32_t sc_voff,
+                                             int64_t N_w)
+{
+    ((Ps % 2 == 0
+          ? mx_step<kGated, NB, Ps, !kLast || Ps + 4 < kUnit, kLast && Ps == kUnit - 1 ? -1 : mx_wait<Ps, kLast>()>(
+                acc, A0, A1, b01, sb01, b23, sb23, la, cp, a_voff, b_voff, sc_voff, N_w)
+          : mx_step<kGated, NB, Ps, !kLast || Ps + 4 < kUnit, kLast && Ps == kUnit - 1 ? -1 : mx_wait<Ps, kLast>()>(
+                acc, A1, A0, b01, sb01, b23, sb23, la, cp, a_voff, b_voff, sc_voff, N_w)),
+     ...);
+}
+
+template <bool kGated, int NB, bool kLast>
+__device__ __forceinline__ void mx_unit(f32x16_t (&acc)[kTM][kTN], MxFrags& A0, MxFrags& A1,
+                                        i32x8_t (&b01)[2], int (&sb01)[2], i32x8_t (&b23)[2],
+                                        int (&sb23)[2], const LaneAddr& la, MxCopy& cp,
+                                        const uint32_t (&a_voff)[kACopies],
+                                        const uint32_t (&b_voff)[kBCopies], uint32_t sc_voff, int64_t N_w)
+{
+    mx_unit_impl<kGated, NB, kLast>(std::make_integer_sequence<int, kUnit>{}, acc, A0, A1, b01, sb01, b23,
+                                    sb23, la, cp, a_voff, b_voff, sc_voff, N_w);
+}
+
+// The K loop of one task.  KT is a multiple of 16; the caller issued the copies of steps 0 .. 3
+// and cp points at step 4.  Every LDS address is a lane base plus a constant.
+template <bool kGated, int NB>
+__device__ __forceinline__ void mx_k_loop(f32x16_t (&acc)[kTM][kTN], const LaneAddr& la, MxCopy cp,
+                                          const uint32_t (&a_voff)[kACopies],
+                                          const uint32_t (&b_voff)[kBCopies], uint32_t sc_voff, int KT,
+                                          int64_t N_w)
+{
+    static_assert(kStages == 4 && kUnit % kStages == 0, "the unrolled unit below");
+    step_barrier<group_copies(1, true) + group_copies(2, true) + group_copies(3, true)>();   // step 0 landed
     MxFrags A0, A1;
     i32x8_t b01[2], b23[2];
     int sb01[2], sb23[2];
     if constexpr (NB > 0) {
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            A0.a[i] = read_a(lds0 + la.a0 + row_block<kWM>(i, wm) * 64, lds0 + la.a1 + row_block<kWM>(i, wm) * 64);
-            A0.sa[i] = read_u8(lds0 + kScRing + la.asc + row_block<kWM>(i, wm) * 16);
-        }
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            b01[jj] = read_b<L::kRowBytes>(lds0 + kABytes + la.b[jj]);
-            sb01[jj] = read_u8(lds0 + kScRing + kAScBytes + la.bsc[jj]);
-        }
+        read_a_frags<NB, 0, 0>(A0, la);
+        read_b_frags<kGated, 0, 0, 0>(b01, sb01, la);
     }
-    for (int kt = 0; kt < KT; kt += 2) {
-        mx_step<kGated, NB>(acc, A0, A1, b01, sb01, b23, sb23, kt, KT, lds0, la, t, b_voff, wave, wm, K, N_w);
-        mx_step<kGated, NB>(acc, A1, A0, b01, sb01, b23, sb23, kt + 1, KT, lds0, la, t, b_voff, wave, wm, K, N_w);
-    }
+    for (int kt = 0; kt < KT - kUnit; kt += kUnit)
+        mx_unit<kGated, NB, false>(acc, A0, A1, b01, sb01, b23, sb23, la, cp, a_voff, b_voff, sc_voff, N_w);
+    mx_unit<kGated, NB, true>(acc, A0, A1, b01, sb01, b23, sb23, la, cp, a_voff, b_voff, sc_voff, N_w);
 }
 
 // fc2 epilogue: bf16 rows through the wave's 2 KiB staging area in pieces of 16 rows x 64 columns.
@@ -698,22 +740,28 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
     const int64_t N_w = N_out;
     const int KS = K / 32;
 
-    // weight copy offsets (bytes): copy j covers k rows kRowsPerCopy * (bi0 + j) + lane / kChunks
+    // weight copy offsets (bytes from the step's first weight row): copy j covers k rows
+    // kRowsPerCopy * (bi0 + j) .. + kRowsPerCopy - 1, lane / kChunks within them
+    const int bi0 = kGated ? kBCopies * (wave % (kWaves / 2)) : kBCopies * wave;
     uint32_t b_voff[kBCopies];
 #pragma unroll
     for (int j = 0; j < kBCopies; ++j) {
-        const int bi = (kGated ? kBCopies * (wave % (kWaves / 2)) : kBCopies * wave) + j;
-        const int kr = bi * L::kRowsPerCopy + lane / L::kChunks;
+        const int kr = (bi0 + j) * L::kRowsPerCopy + lane / L::kChunks;
         const int c = bswz<kGated>(lane % L::kChunks, kr);
-        b_voff[j] = static_cast<uint32_t>(lane / L::kChunks) * static_cast<uint32_t>(N_out) + 16u * c;
+        b_voff[j] = static_cast<uint32_t>(kr) * static_cast<uint32_t>(N_out) + 16u * c;
     }
-    // fragment and scale addresses (LDS bytes from the stage / scale-slot bases)
+    MxCopy cp{};
+    cp.a_lds = lds0 + kACopies * wave * 1024;
+    cp.b_lds = lds0 + kBRing + (kGated ? (wave / (kWaves / 2)) * L::kMatBytes : 0) + bi0 * 1024;
+    cp.sc_lds = lds0 + kScRing + (wave < 4 ? wave * 1024 : kAScBytes + (wave - 4) * 1024);
+    // fragment and scale addresses (see LaneAddr)
     LaneAddr la;
     {
         const int r = lane & 31;
-        la.a0 = r * 64 + 16 * ((0 + h) ^ ((r >> 2) & 3));
-        la.a1 = r * 64 + 16 * ((2 + h) ^ ((r >> 2) & 3));
-        la.asc = r * 16 + h;
+        const uint32_t rb = row_block<kWM>(0, wm);
+        la.a0 = lds0 + rb * 64 + r * 64 + 16 * ((0 + h) ^ ((r >> 2) & 3));
+        la.a1 = lds0 + rb * 64 + r * 64 + 16 * ((2 + h) ^ ((r >> 2) & 3));
+        la.asc = lds0 + kScRing + rb * 16 + r * 16 + h;
         const int g = lane >> 4, sl = lane & 15;
         const int hh = g >> 1;
         const int kr = 16 * hh + (sl >> 1);                     // first read; + 8, + 32, + 40
@@ -722,50 +770,63 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
             const int m = kGated ? (j & 1) : 0;
             const int cb = kGated ? 16 * kTN * wn + 32 * (j >> 1) : 32 * kTN * wn + 32 * j;
             const int col = cb + 16 * (g & 1) + 8 * (sl & 1);
-            la.b[j] = m * L::kMatBytes + kr * L::kRowBytes + 16 * bswz<kGated>(col >> 4, kr) + (col & 15);
-            const int ocol = cb + (lane & 31);                  // this lane's output column of block j
-            la.bsc[j] = (kGated ? m * (kBScBytes / 2) : 0) + h * L::kRowBytes + ocol;
+            la.b[j] = lds0 + kBRing + m * L::kMatBytes + kr * L::kRowBytes + 16 * bswz<kGated>(col >> 4, kr) + (col & 15);
         }
+        // block 0's scale column: the wave's first output column plus the lane's
+        la.bsc = lds0 + kScRing + kAScBytes + h * L::kRowBytes + (kGated ? 16 * kTN * wn : 32 * kTN * wn) + (lane & 31);
+        asm volatile("" : "+v"(la.a0), "+v"(la.a1), "+v"(la.asc), "+v"(la.bsc));
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+            asm volatile("" : "+v"(la.b[j]));
     }
 
     const int xcd = blockIdx.x % kXcdCount;
     const int blk = gridDim.x / kXcdCount;
     MTile tile{};
     int n0 = 0;
-    TaskSrc src{};
+    uint32_t a_voff[kACopies];
+    uint32_t sc_voff = 0;
     auto setup = [&](int tk) {
         int nt;
         tile = decode_task(tk, n_nt, tiles, nt);
         n0 = nt * BN;
         const int rows = tile.row_end - tile.row_begin;
-        src.At = A + static_cast<int64_t>(tile.row_begin) * K;
-        src.Asc = A_sc + static_cast<int64_t>(tile.row_begin) * KS;
 #pragma unroll
         for (int j = 0; j < kACopies; ++j) {
             const int r = 16 * (kACopies * wave + j) + lane / 4;
             const int c = (lane & 3) ^ ((r >> 2) & 3);
-            src.a_voff[j] = static_cast<uint32_t>(min(r, rows - 1)) * static_cast<uint32_t>(K) + 16u * c;
+            a_voff[j] = static_cast<uint32_t>(min(r, rows - 1)) * static_cast<uint32_t>(K) + 16u * c;
         }
         const int64_t eoff = static_cast<int64_t>(tile.expert) * K * N_w;
         const int64_t esoff = static_cast<int64_t>(tile.expert) * KS * N_w;
-        src.Bm = (kGated && wave >= kWaves / 2 ? B1 : B0) + eoff + n0;
+        cp.a = A + static_cast<int64_t>(tile.row_begin) * K;
+        cp.b = (kGated && wave >= kWaves / 2 ? B1 : B0) + eoff + n0;
         if (wave < 4) {
-            src.sc_voff = static_cast<uint32_t>(min(64 * wave + lane, rows - 1)) * static_cast<uint32_t>(KS);
-            src.Bsc = B0_sc;
+            // A scale rows 64 wave .. + 63, 16 blocks (one scale block) per lane
+            cp.sc = A_sc + static_cast<int64_t>(tile.row_begin) * KS;
+            cp.sc_step = 16;
+            sc_voff = static_cast<uint32_t>(min(64 * wave + lane, rows - 1)) * static_cast<uint32_t>(KS);
         } else {
             const int c = wave - 4;
+            cp.sc_step = int64_t{16} * N_w;
             if (kGated) {
                 // scale copy c: matrix c / 2, block rows 8 (c % 2) .. + 7, 8 lanes per 128-byte row
-                src.Bsc = (c >= 2 ? B1_sc : B0_sc) + esoff + n0 + int64_t{8} * (c & 1) * N_w;
-                src.sc_voff = static_cast<uint32_t>(lane >> 3) * static_cast<uint32_t>(N_out) + 16u * (lane & 7);
+                cp.sc = (c >= 2 ? B1_sc : B0_sc) + esoff + n0 + int64_t{8} * (c & 1) * N_w;
+                sc_voff = static_cast<uint32_t>(lane >> 3) * static_cast<uint32_t>(N_out) + 16u * (lane & 7);
             } else {
                 // scale copy c: block rows 4 c .. + 3, 16 lanes per 256-byte row
-                src.Bsc = B0_sc + esoff + n0 + int64_t{4} * c * N_w;
-                src.sc_voff = static_cast<uint32_t>(lane >> 4) * static_cast<uint32_t>(N_out) + 16u * (lane & 15);
+                cp.sc = B0_sc + esoff + n0 + int64_t{4} * c * N_w;
+                sc_voff = static_cast<uint32_t>(lane >> 4) * static_cast<uint32_t>(N_out) + 16u * (lane & 15);
             }
         }
-        for (int st = 0; st < kStages; ++st)
-            issue_copies<kGated>(st, lds0, src, b_voff, wave, K, N_w, st < KT);
+        mx_issue<true, 0, 0>(cp, a_voff, b_voff, sc_voff);
+        mx_advance(cp, N_w, true);
+        mx_issue<false, 1, 0>(cp, a_voff, b_voff, sc_voff);
+        mx_advance(cp, N_w, false);
+        mx_issue<false, 2, 0>(cp, a_voff, b_voff, sc_voff);
+        mx_advance(cp, N_w, false);
+        mx_issue<false, 3, 0>(cp, a_voff, b_voff, sc_voff);
+        mx_advance(cp, N_w, false);
     };
 
     int t = claim_task(claimed, task_ctr, xcd, blk, wave, lane);
@@ -788,9 +849,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
                 for (int r = 0; r < 16; ++r)
                     acc[i][j][r] = 0.0f;
         switch (nb) {
-        case 0: mx_k_loop<kGated, 0>(acc, lds0, la, src, b_voff, KT, wave, wm, K, N_w); break;
-        case 1: mx_k_loop<kGated, 1>(acc, lds0, la, src, b_voff, KT, wave, wm, K, N_w); break;
-        default: mx_k_loop<kGated, 2>(acc, lds0, la, src, b_voff, KT, wave, wm, K, N_w); break;
+        case 0: mx_k_loop<kGated, 0>(acc, la, cp, a_voff, b_voff, sc_voff, KT, N_w); break;
+        case 1: mx_k_loop<kGated, 1>(acc, la, cp, a_voff, b_voff, sc_voff, KT, N_w); break;
+        default: mx_k_loop<kGated, 2>(acc, la, cp, a_voff, b_voff, sc_voff, KT, N_w); break;
         }
         const MTile done = tile;
         const int done_n0 = n0;
@@ -811,7 +872,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
 
 }  // namespace big
 
-bool mx_use_big(int64_t H, int64_t F) { return H % 512 == 0 && F % 512 == 0; }
+// The large kernels run K loops of whole 16-step units (H / 64, F / 64 multiples of 16).
+bool mx_use_big(int64_t H, int64_t F) { return H % 1024 == 0 && F % 1024 == 0; }
 
 unsigned persistent_grid() { return static_cast<unsigned>(device_info().cu_count * 2); }
 

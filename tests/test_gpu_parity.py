@@ -293,8 +293,10 @@ def _mx_weights64(src):
 
 @pytest.mark.parametrize("T,H,F,E,k", [(200, 256, 256, 6, 4), (333, 384, 128, 5, 2),
                                        (96, 128, 384, 32, 4),
-                                       # large tiles (H, F multiples of 512): ragged tails, deep K
-                                       (300, 512, 512, 5, 2), (700, 1024, 512, 3, 2)])
+                                       (300, 512, 512, 5, 2),
+                                       # large tiles (H, F multiples of 1024): ragged tails, K loops
+                                       # of one and of several 16-step units
+                                       (300, 1024, 2048, 5, 2), (700, 2048, 1024, 3, 2)])
 def test_mx_forward_matches_oracle(T, H, F, E, k):
     inp = synth.make_layer(T=T, H=H, F=F, E=E, k=k, dtype="mxfp8", seed=T)
     ref, *_ = oracle.forward(inp)
@@ -306,7 +308,7 @@ def test_mx_forward_matches_oracle(T, H, F, E, k):
     assert np.array_equal(out, dv.host(dv.forward(mel, d)))
 
 
-@pytest.mark.parametrize("T,H,F,E,k", [(200, 256, 384, 4, 2), (300, 512, 512, 3, 2)],
+@pytest.mark.parametrize("T,H,F,E,k", [(200, 256, 384, 4, 2), (300, 1024, 1024, 3, 2)],
                          ids=["small_tiles", "large_tiles"])
 def test_mx_h_encoding_agrees_with_oracle(T, H, F, E, k):
     """fc1's MX-encoded SwiGLU output, read back from the workspace, against the oracle's encoding
@@ -345,7 +347,7 @@ def test_mx_h_encoding_agrees_with_oracle(T, H, F, E, k):
     assert err.mean() <= 1.05 * own.mean()       # as good as encoding the exact h, on average
 
 
-@pytest.mark.parametrize("T,H,F", [(600, 256, 256), (1100, 512, 512)], ids=["small_tiles", "large_tiles"])
+@pytest.mark.parametrize("T,H,F", [(600, 256, 256), (1100, 1024, 1024)], ids=["small_tiles", "large_tiles"])
 def test_mx_chunked_equals_unchunked(T, H, F):
     inp = synth.make_layer(T=T, H=H, F=F, E=7, k=2, dtype="mxfp8", seed=5)
     d = dv.layer(inp)
@@ -354,7 +356,7 @@ def test_mx_chunked_equals_unchunked(T, H, F):
     assert np.array_equal(dv.host(dv.forward(mel, d, 512)), base)
 
 
-@pytest.mark.parametrize("H,F", [(256, 256), (512, 512)], ids=["small_tiles", "large_tiles"])
+@pytest.mark.parametrize("H,F", [(256, 256), (1024, 1024)], ids=["small_tiles", "large_tiles"])
 def test_mx_grouped_ffn_matches_oracle(H, F):
     g = synth.make_grouped(rows=700, H=H, F=F, E_local=2, sources=8, dtype="mxfp8", seed=4)
     ref = oracle.grouped_ffn(g)
