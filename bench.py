@@ -157,7 +157,7 @@ def main():
     out = torch.empty((T, H), dtype=torch.float32 if inp.dtype == "f32" else torch.bfloat16,
                       device=dev)
     flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
-    flush_words = flush.view(torch.int32)
+    flush_words = flush.view(torch.float32)     # summed as float: no widening copy of the buffer
 
     def do_flush():
         if args.no_flush:
