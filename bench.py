@@ -119,6 +119,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-chunked", action="store_true")
+    ap.add_argument("--separate-permute", action="store_true",
+                    help="run the permute step as its own kernel instead of inside fc1's row loads")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (reference for HBM counters)")
     args = ap.parse_args()
@@ -171,10 +173,11 @@ def main():
         if inp.dtype == "mxfp8":
             mel.expert_forward_mx(d.x, d.x_scale, d.w_gate, d.wg_scale, d.w_up, d.wu_scale,
                                   d.w_down, d.wd_scale, d.expert_ids, d.probs, head_m_size=h,
-                                  out=out, workspace=ws)
+                                  out=out, workspace=ws, separate_permute=args.separate_permute)
         else:
             mel.expert_forward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs,
-                               head_m_size=h, out=out, workspace=ws)
+                               head_m_size=h, out=out, workspace=ws,
+                               separate_permute=args.separate_permute)
 
     def timed(h, steps):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -250,7 +253,8 @@ def main():
         "dtype": inp.dtype, "data": "synthetic",
         "config": {"workload": args.workload, "T": T, "H": H, "F": F, "E": E, "k": k,
                    "head_m_size": head, "routed_rows": M, "flush_bytes": 0 if args.no_flush else 1 << 30,
-                   "flush": "none" if args.no_flush else args.flush},
+                   "flush": "none" if args.no_flush else args.flush,
+                   "permute": "separate kernel" if args.separate_permute else "inside fc1 where the large tiles serve"},
         "gemm": {"tflops": gemm_tflops, "frac_of_peak": gemm_tflops / peak, "peak_tflops": peak,
                  "fc1_ms": fc1_ms, "fc2_ms": fc2_ms},
         "kernels_ms": kavg, "hbm": hbm, "roofline": roof,

@@ -132,8 +132,11 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise ValueError(f"unsupported dtype {t.dtype} (float32 or bfloat16; MX uses the *_mx calls)")
 
 
-def problem(T, H, F, E, k, dtype, head_m_size=0) -> MoeProblem:
-    return MoeProblem(int(T), int(H), int(F), int(E), int(k), int(dtype), int(head_m_size), 0, 0)
+FLAG_SEPARATE_PERMUTE = 1    # run the permute step as a kernel of its own (see the C header)
+
+
+def problem(T, H, F, E, k, dtype, head_m_size=0, flags=0) -> MoeProblem:
+    return MoeProblem(int(T), int(H), int(F), int(E), int(k), int(dtype), int(head_m_size), int(flags), 0)
 
 
 def workspace_size(prob: MoeProblem) -> int:
@@ -154,7 +157,7 @@ def _workspace(nbytes: int, device, workspace):
 # ---------------------------------------------------------------------------------------------- layer
 
 def expert_forward(x, w_gate, w_up, w_down, expert_ids, probs, head_m_size: int = 0, out=None,
-                   workspace=None):
+                   workspace=None, separate_permute: bool = False):
     """out[T,H] = sum_j probs[t,j] * FFN_{expert_ids[t,j]}(x[t]) for float32 or bfloat16 inputs."""
     dt = _dtype_code(x)
     T, H = x.shape
@@ -167,7 +170,7 @@ def expert_forward(x, w_gate, w_up, w_down, expert_ids, probs, head_m_size: int 
     _need(w_down, "w_down", x.dtype, (E, F, H), dev)
     _need(expert_ids, "expert_ids", torch.int32, (T, k), dev)
     _need(probs, "probs", torch.float32, (T, k), dev)
-    prob = problem(T, H, F, E, k, dt, head_m_size)
+    prob = problem(T, H, F, E, k, dt, head_m_size, FLAG_SEPARATE_PERMUTE if separate_permute else 0)
     ws = _workspace(workspace_size(prob), dev, workspace)
     if out is None:
         out = torch.empty((T, H), dtype=x.dtype, device=dev)
@@ -179,7 +182,8 @@ def expert_forward(x, w_gate, w_up, w_down, expert_ids, probs, head_m_size: int 
 
 
 def expert_forward_mx(x, x_scale, w_gate, wg_scale, w_up, wu_scale, w_down, wd_scale, expert_ids,
-                      probs, head_m_size: int = 0, out=None, workspace=None):
+                      probs, head_m_size: int = 0, out=None, workspace=None,
+                      separate_permute: bool = False):
     """The same layer on OCP-MX E4M3 bytes (uint8 tensors) with E8M0 block scales; bf16 output."""
     T, H = x.shape
     E, _, F = w_gate.shape
@@ -196,7 +200,7 @@ def expert_forward_mx(x, x_scale, w_gate, wg_scale, w_up, wu_scale, w_down, wd_s
     _need(wd_scale, "wd_scale", u8, (E, F // 32, H), dev)
     _need(expert_ids, "expert_ids", torch.int32, (T, k), dev)
     _need(probs, "probs", torch.float32, (T, k), dev)
-    prob = problem(T, H, F, E, k, MXFP8, head_m_size)
+    prob = problem(T, H, F, E, k, MXFP8, head_m_size, FLAG_SEPARATE_PERMUTE if separate_permute else 0)
     ws = _workspace(workspace_size(prob), dev, workspace)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)

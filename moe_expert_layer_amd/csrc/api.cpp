@@ -146,8 +146,8 @@ moe_status check_problem(const moe_problem* p, bool need_tokens, bool gemm = tru
 {
     if (p == nullptr)
         return fail(MOE_ERR_INVALID_ARGUMENT, "problem is null");
-    if (p->flags != 0 || p->reserved != 0)
-        return fail(MOE_ERR_INVALID_ARGUMENT, "flags and reserved must be 0");
+    if ((p->flags & ~static_cast<uint32_t>(MOE_FLAG_SEPARATE_PERMUTE)) != 0 || p->reserved != 0)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "unknown flags, or reserved not 0");
     if (p->dtype != MOE_F32 && p->dtype != MOE_BF16 && p->dtype != MOE_MXFP8_E4M3)
         return fail(MOE_ERR_UNSUPPORTED, "unknown dtype %d", p->dtype);
     if (p->H <= 0 || p->F <= 0 || p->E <= 0)
@@ -314,12 +314,25 @@ moe_status run_route(const int32_t* ids, int64_t T, int64_t k, int64_t E, int32_
     return MOE_OK;
 }
 
-// fc1 + SwiGLU + fc2 over grouped rows; tiles are built from (offsets, group_expert).
+// Whether fc1 can read the permuted rows straight from x through perm (the permute step folded
+// into its row copies): the 256-row-tile kernels, with x addressable by 32-bit byte offsets.
+bool fc1_gathers(int dtype, int64_t T, int64_t H, int64_t F)
+{
+    if (dtype == MOE_BF16)
+        return bf16_row_tile(H, F) == 256 && T * H * 2 < (int64_t{1} << 32);
+    if (dtype == MOE_MXFP8_E4M3)
+        return mx_row_tile(H, F) == 256 && T * H < (int64_t{1} << 32);
+    return false;
+}
+
+// fc1 + SwiGLU + fc2 over grouped rows; tiles are built from (offsets, group_expert).  gather
+// (may be null, see fc1_gathers): permuted row p is row gather[p] / gather_k of `rows`.
 moe_status run_ffn(int dtype, const void* rows, const uint8_t* rows_scale, int64_t M,
                    const int32_t* offsets, const int32_t* group_expert, int64_t G, int64_t E,
                    int64_t H, int64_t F, int64_t head_m_size, const void* wg, const uint8_t* wgs,
                    const void* wu, const uint8_t* wus, const void* wd, const uint8_t* wds,
-                   void* y, void* ws, const FfnLayout& L, bool write_status, hipStream_t s)
+                   void* y, void* ws, const FfnLayout& L, bool write_status, hipStream_t s,
+                   const int32_t* gather = nullptr, int gather_k = 1)
 {
     const int64_t chunk = head_m_size > 0 ? head_m_size : std::max<int64_t>(M, 1);
     int32_t* status = at<int32_t>(ws, L.status);
@@ -337,7 +350,7 @@ moe_status run_ffn(int dtype, const void* rows, const uint8_t* rows_scale, int64
         LAUNCH(s, "fc1_bf16",
                launch_fc1_bf16(static_cast<const uint16_t*>(rows), static_cast<const uint16_t*>(wg),
                                static_cast<const uint16_t*>(wu), h, tiles, tcount, H, F,
-                               task_ctr, s));
+                               task_ctr, gather, gather_k, s));
         LAUNCH(s, "fc2_bf16",
                launch_fc2_bf16(h, static_cast<const uint16_t*>(wd), static_cast<uint16_t*>(y),
                                tiles, tcount, H, F, chunk_done, task_ctr + kXcdCount, s));
@@ -355,7 +368,7 @@ moe_status run_ffn(int dtype, const void* rows, const uint8_t* rows_scale, int64
         LAUNCH(s, "fc1_mx",
                launch_fc1_mx(static_cast<const uint8_t*>(rows), rows_scale,
                              static_cast<const uint8_t*>(wg), wgs, static_cast<const uint8_t*>(wu),
-                             wus, h, hs, tiles, tcount, H, F, task_ctr, s));
+                             wus, h, hs, tiles, tcount, H, F, task_ctr, gather, gather_k, s));
         LAUNCH(s, "fc2_mx",
                launch_fc2_mx(h, hs, static_cast<const uint8_t*>(wd), wds, static_cast<uint16_t*>(y),
                              tiles, tcount, H, F, chunk_done, task_ctr + kXcdCount, s));
@@ -404,13 +417,22 @@ static moe_status forward_common(const moe_problem* p, const void* x, const uint
     if (M == 0)
         return MOE_OK;
     const int64_t eb = elem_bytes(p->dtype);
-    LAUNCH(s, "permute", launch_permute(x, pos, at<void>(ws, L.x_perm), T, k, M, H * eb, s));
-    if (p->dtype == MOE_MXFP8_E4M3)
-        LAUNCH(s, "permute_scale",
-               launch_permute(x_scale, pos, at<void>(ws, L.x_perm_scale), T, k, M, H / 32, s));
-    if (moe_status st = run_ffn(p->dtype, at<void>(ws, L.x_perm), at<uint8_t>(ws, L.x_perm_scale),
-                                M, offsets, nullptr, p->E, p->E, H, p->F, p->head_m_size, wg, wgs,
-                                wu, wus, wd, wds, at<void>(ws, L.y_perm), ws, L.ffn, false, s);
+    // The permute step runs inside fc1 (row copies gathered through perm) unless the caller asks
+    // for it as a kernel of its own or the small-tile kernels serve these sizes.
+    const bool fused = (p->flags & MOE_FLAG_SEPARATE_PERMUTE) == 0 && fc1_gathers(p->dtype, T, H, p->F);
+    const void* rows = x;
+    const uint8_t* rows_scale = x_scale;
+    if (!fused) {
+        LAUNCH(s, "permute", launch_permute(x, pos, at<void>(ws, L.x_perm), T, k, M, H * eb, s));
+        if (p->dtype == MOE_MXFP8_E4M3)
+            LAUNCH(s, "permute_scale",
+                   launch_permute(x_scale, pos, at<void>(ws, L.x_perm_scale), T, k, M, H / 32, s));
+        rows = at<void>(ws, L.x_perm);
+        rows_scale = at<uint8_t>(ws, L.x_perm_scale);
+    }
+    if (moe_status st = run_ffn(p->dtype, rows, rows_scale, M, offsets, nullptr, p->E, p->E, H, p->F,
+                                p->head_m_size, wg, wgs, wu, wus, wd, wds, at<void>(ws, L.y_perm), ws,
+                                L.ffn, false, s, fused ? perm : nullptr, static_cast<int>(k));
         st != MOE_OK)
         return st;
     LAUNCH(s, "unpermute",

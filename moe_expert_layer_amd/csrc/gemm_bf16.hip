@@ -518,17 +518,20 @@ __device__ __forceinline__ void k_step(f32x16_t (&acc)[kTM][kTN], Frags& f0, Fra
     substep<kGated, NB, 0, kCopyA ? kHalfA : 0, (S + 1) % kStages, 0, S>(acc, f1, f0, cp, g);
 }
 
+// Copies a task's setup leaves in flight once its step 0 has landed (steps 1, 2 and the A half of
+// step 3).
+constexpr int kTopWait = 2 * kCopies + kHalfA;
+
 // The K loop of one task.  KT is a multiple of kStages (at least kStages); the caller issued the
-// copies of steps 0 .. kStages - 2 and the A half of step kStages - 1, and cp points at that step.
-// The body is unrolled over the kStages stages, so every LDS address is a lane base plus a
-// constant.
+// copies of steps 0 .. kStages - 2 and the A half of step kStages - 1, cp points at that step, and
+// the caller has waited for step 0 (step_barrier<kTopWait>).  The body is unrolled over the kStages
+// stages, so every LDS address is a lane base plus a constant.
 template <bool kGated, int NB>
 __device__ __forceinline__ void k_loop(f32x16_t (&acc)[kTM][kTN], CopyCtx cp, const LoopArgs& g,
                                        int64_t N_w, int KT)
 {
     static_assert(kStages == 4, "the unrolled body below covers four stages");
     constexpr int K2 = 2 * kCopies;
-    step_barrier<K2 + kHalfA>();                   // step 0 landed
     Frags f0, f1;
     if constexpr (NB > 0)
         reads<kGated, 0, 0, 0, 2 * kTN + NB>(f0, g.a_base, g.b_base);
@@ -607,12 +610,14 @@ __device__ __forceinline__ void store_output_staged(const f32x16_t (&acc)[kTM][k
     }
 }
 
+// gather (fc1 only, may be null): permuted row p of A is row gather[p] / gather_k of the matrix
+// A points at (the permute step folded into the row copies); null: row p of A.
 template <bool kGated>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, const MTile* __restrict__ tiles,
     const int32_t* __restrict__ tile_count, int K, int N_out, int32_t* __restrict__ chunk_done,
-    int32_t* __restrict__ task_ctr)
+    int32_t* __restrict__ task_ctr, const int32_t* __restrict__ gather, int gather_k)
 {
     using L = BLayout<kGated>;
     constexpr int BN = kGated ? BNB / 2 : BNB;
@@ -680,6 +685,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
     MTile tile{};
     int n0 = 0;
     uint32_t a_voff[kACopies];
+    // Gathered fc1 rows: the slot-list entries of this lane's A copy rows for the next task, loaded
+    // one task ahead (during the previous task's K loop) and first used in setup, so that nothing
+    // waits for them.
+    int gsrc[kACopies] = {};
+    auto fetch_rows = [&](int t) {
+        if (gather == nullptr)
+            return;
+        int nt;
+        const MTile tl = decode_task(t, n_nt, tiles, nt);
+#pragma unroll
+        for (int j = 0; j < kACopies; ++j) {
+            const int r = 16 * (kACopies * wave + j) + lane / 4;
+            gsrc[j] = gather[tl.row_begin + min(r, tl.row_end - tl.row_begin - 1)];   // used in setup
+        }
+    };
     auto setup = [&](int t) {
         int nt;
         tile = decode_task(t, n_nt, tiles, nt);
@@ -689,9 +709,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
         for (int j = 0; j < kACopies; ++j) {
             const int r = 16 * (kACopies * wave + j) + lane / 4;
             const int c = (lane & 3) ^ ((r >> 2) & 3);
-            a_voff[j] = static_cast<uint32_t>(min(r, rows - 1)) * static_cast<uint32_t>(K) * 2u + 16u * c;
+            const int src = gather != nullptr ? gsrc[j] / gather_k : min(r, rows - 1);
+            a_voff[j] = static_cast<uint32_t>(src) * static_cast<uint32_t>(K) * 2u + 16u * c;
         }
-        cp.a = A + static_cast<int64_t>(tile.row_begin) * K;
+        cp.a = gather != nullptr ? A : A + static_cast<int64_t>(tile.row_begin) * K;
         cp.b = (kGated && wave >= kWaves / 2 ? B1 : B0) + static_cast<int64_t>(tile.expert) * K * N_w + n0;
         issue<0, 0, kCopies>(cp, a_voff, b_voff);
         advance(cp, N_w);
@@ -703,8 +724,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
     };
 
     int t = claim_task(claimed, task_ctr, xcd, blk, wave, lane);
-    if (t < total)
+    if (t < total) {
+        fetch_rows(t);
         setup(t);
+    }
     while (t < total) {
         // claim the following task now; the other waves read the claim after this task's barriers
         if (wave == 0) {
@@ -724,6 +747,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
                 for (int r = 0; r < 16; ++r)
                     acc[i][j][r] = 0.0f;
 
+        // step 0 has landed; past this barrier every wave sees the claim of the following task,
+        // whose gathered source rows are loaded now and used after this task's K loop
+        step_barrier<kTopWait>();
+        const int i = __builtin_amdgcn_readfirstlane(*claimed);
+        const int t_next = ((i / blk) * kXcdCount + xcd) * blk + i % blk;
+        if (t_next < total)
+            fetch_rows(t_next);
         const LoopArgs g{a_base, b_base, a_voff, b_voff};
         switch (nb) {
         case 0: k_loop<kGated, 0>(acc, cp, g, N_w, KT); break;
@@ -732,8 +762,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
         }
         const MTile done = tile;
         const int done_n0 = n0;
-        const int i = __builtin_amdgcn_readfirstlane(*claimed);
-        t = ((i / blk) * kXcdCount + xcd) * blk + i % blk;
+        t = t_next;
         // every wave is past its last read of this task's stages (and of the claim word)
         __syncthreads();
         if (t < total)
@@ -787,15 +816,17 @@ bool bf16_supported(int64_t H, int64_t F) { return H % Fc2Small::BN == 0 && F % 
 
 hipError_t launch_fc1_bf16(const uint16_t* A, const uint16_t* wg, const uint16_t* wu, uint16_t* h,
                            const MTile* tiles, const int32_t* tile_count, int64_t H, int64_t F,
-                           int32_t* task_ctr, hipStream_t s)
+                           int32_t* task_ctr, const int32_t* gather, int gather_k, hipStream_t s)
 {
     const int cu = device_info().cu_count;
+    if (gather != nullptr && !use_big(H, F))
+        return hipErrorInvalidValue;              // only the large-tile kernel gathers rows
     if (use_big(H, F)) {
         if (hipError_t e = ensure_smem_limits(); e != hipSuccess)
             return e;
         big::grouped_gemm_bf16_dma<true><<<dim3(cu), dim3(big::kThreads), kBigSmem, s>>>(
             A, wg, wu, h, tiles, tile_count, static_cast<int>(H), static_cast<int>(F), nullptr,
-            task_ctr);
+            task_ctr, gather, gather_k);
     } else {
         FC1_SMALL<<<dim3(2 * cu), dim3(Fc1Small::kThreads), Fc1Small::kSmemBytes, s>>>(
             A, wg, wu, h, tiles, tile_count, static_cast<int>(H), static_cast<int>(F), nullptr,
@@ -814,7 +845,7 @@ hipError_t launch_fc2_bf16(const uint16_t* h, const uint16_t* wd, uint16_t* y, c
             return e;
         big::grouped_gemm_bf16_dma<false><<<dim3(cu), dim3(big::kThreads), kBigSmem, s>>>(
             h, wd, nullptr, y, tiles, tile_count, static_cast<int>(F), static_cast<int>(H),
-            chunk_done, task_ctr);
+            chunk_done, task_ctr, nullptr, 1);
     } else {
         FC2_SMALL<<<dim3(2 * cu), dim3(Fc2Small::kThreads), Fc2Small::kSmemBytes, s>>>(
             h, wd, nullptr, y, tiles, tile_count, static_cast<int>(F), static_cast<int>(H),

@@ -31,6 +31,7 @@ __device__ __forceinline__ int claim_task(int* claimed, int32_t* task_ctr, int x
     }
     __syncthreads();
     const int i = __builtin_amdgcn_readfirstlane(*claimed);   // one value per workgroup
+    __syncthreads();                                          // read by all before wave 0 reuses it
     return ((i / blk) * kXcdCount + xcd) * blk + i % blk;
 }
 

@@ -592,8 +592,12 @@ __device__ __forceinline__ void mx_unit(f32x16_t (&acc)[kTM][kTN], MxFrags& A0, 
                                     sb23, la, cp, a_voff, b_voff, sc_voff, N_w);
 }
 
-// The K loop of one task.  KT is a multiple of 16; the caller issued the copies of steps 0 .. 3
-// and cp points at step 4.  Every LDS address is a lane base plus a constant.
+// Copies a task's setup leaves in flight once its step 0 has landed (steps 1 .. 3).
+constexpr int kTopWait = group_copies(1, true) + group_copies(2, true) + group_copies(3, true);
+
+// The K loop of one task.  KT is a multiple of 16; the caller issued the copies of steps 0 .. 3,
+// cp points at step 4, and the caller has waited for step 0 (step_barrier<kTopWait>).  Every LDS
+// address is a lane base plus a constant.
 template <bool kGated, int NB>
 __device__ __forceinline__ void mx_k_loop(f32x16_t (&acc)[kTM][kTN], const LaneAddr& la, MxCopy cp,
                                           const uint32_t (&a_voff)[kACopies],
@@ -601,7 +605,6 @@ __device__ __forceinline__ void mx_k_loop(f32x16_t (&acc)[kTM][kTN], const LaneA
                                           int64_t N_w)
 {
     static_assert(kStages == 4 && kUnit % kStages == 0, "the unrolled unit below");
-    step_barrier<group_copies(1, true) + group_copies(2, true) + group_copies(3, true)>();   // step 0 landed
     MxFrags A0, A1;
     i32x8_t b01[2], b23[2];
     int sb01[2], sb23[2];
@@ -718,8 +721,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
     const uint8_t* __restrict__ B1, const uint8_t* __restrict__ B1_sc,
     uint8_t* __restrict__ Cq, uint8_t* __restrict__ Cq_sc, uint16_t* __restrict__ Cy,
     const MTile* __restrict__ tiles, const int32_t* __restrict__ tile_count, int K, int N_out,
-    int32_t* __restrict__ chunk_done, int32_t* __restrict__ task_ctr)
+    int32_t* __restrict__ chunk_done, int32_t* __restrict__ task_ctr, const int32_t* __restrict__ gather,
+    int gather_k)
 {
+    // gather (fc1 only, may be null): permuted row p of A (and of its scales) is row
+    // gather[p] / gather_k of the matrices A and A_sc point at; null: row p.
     using L = BLayout<kGated>;
     constexpr int BN = kGated ? BNB / 2 : BNB;
     extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
@@ -786,6 +792,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
     int n0 = 0;
     uint32_t a_voff[kACopies];
     uint32_t sc_voff = 0;
+    // Gathered fc1 rows: the slot-list entries of this lane's A copy rows and A scale row for the
+    // next task, loaded one task ahead (during the previous task's K loop) and first used in setup.
+    int gsrc[kACopies + 1] = {};
+    auto fetch_rows = [&](int tk) {
+        if (gather == nullptr)
+            return;
+        int nt;
+        const MTile tl = decode_task(tk, n_nt, tiles, nt);
+        const int last = tl.row_end - tl.row_begin - 1;
+#pragma unroll
+        for (int j = 0; j < kACopies; ++j)
+            gsrc[j] = gather[tl.row_begin + min(16 * (kACopies * wave + j) + lane / 4, last)];
+        if (wave < 4)
+            gsrc[kACopies] = gather[tl.row_begin + min(64 * wave + lane, last)];
+    };
     auto setup = [&](int tk) {
         int nt;
         tile = decode_task(tk, n_nt, tiles, nt);
@@ -795,17 +816,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
         for (int j = 0; j < kACopies; ++j) {
             const int r = 16 * (kACopies * wave + j) + lane / 4;
             const int c = (lane & 3) ^ ((r >> 2) & 3);
-            a_voff[j] = static_cast<uint32_t>(min(r, rows - 1)) * static_cast<uint32_t>(K) + 16u * c;
+            const int src = gather != nullptr ? gsrc[j] / gather_k : min(r, rows - 1);
+            a_voff[j] = static_cast<uint32_t>(src) * static_cast<uint32_t>(K) + 16u * c;
         }
         const int64_t eoff = static_cast<int64_t>(tile.expert) * K * N_w;
         const int64_t esoff = static_cast<int64_t>(tile.expert) * KS * N_w;
-        cp.a = A + static_cast<int64_t>(tile.row_begin) * K;
+        cp.a = gather != nullptr ? A : A + static_cast<int64_t>(tile.row_begin) * K;
         cp.b = (kGated && wave >= kWaves / 2 ? B1 : B0) + eoff + n0;
         if (wave < 4) {
             // A scale rows 64 wave .. + 63, 16 blocks (one scale block) per lane
-            cp.sc = A_sc + static_cast<int64_t>(tile.row_begin) * KS;
+            const int src = gather != nullptr ? gsrc[kACopies] / gather_k : min(64 * wave + lane, rows - 1);
+            cp.sc = gather != nullptr ? A_sc : A_sc + static_cast<int64_t>(tile.row_begin) * KS;
             cp.sc_step = 16;
-            sc_voff = static_cast<uint32_t>(min(64 * wave + lane, rows - 1)) * static_cast<uint32_t>(KS);
+            sc_voff = static_cast<uint32_t>(src) * static_cast<uint32_t>(KS);
         } else {
             const int c = wave - 4;
             cp.sc_step = int64_t{16} * N_w;
@@ -830,8 +853,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
     };
 
     int t = claim_task(claimed, task_ctr, xcd, blk, wave, lane);
-    if (t < total)
+    if (t < total) {
+        fetch_rows(t);
         setup(t);
+    }
     while (t < total) {
         if (wave == 0) {
             const int v = atomicAdd(&task_ctr[xcd], lane == 0 ? 1 : 0);
@@ -848,6 +873,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     acc[i][j][r] = 0.0f;
+        // step 0 has landed; past this barrier every wave sees the claim of the following task,
+        // whose gathered source rows are loaded now and used after this task's K loop
+        step_barrier<kTopWait>();
+        const int ci = __builtin_amdgcn_readfirstlane(*claimed);
+        const int t_next = ((ci / blk) * kXcdCount + xcd) * blk + ci % blk;
+        if (t_next < total)
+            fetch_rows(t_next);
         switch (nb) {
         case 0: mx_k_loop<kGated, 0>(acc, la, cp, a_voff, b_voff, sc_voff, KT, N_w); break;
         case 1: mx_k_loop<kGated, 1>(acc, la, cp, a_voff, b_voff, sc_voff, KT, N_w); break;
@@ -855,8 +887,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
         }
         const MTile done = tile;
         const int done_n0 = n0;
-        const int ci = __builtin_amdgcn_readfirstlane(*claimed);
-        t = ((ci / blk) * kXcdCount + xcd) * blk + ci % blk;
+        t = t_next;
         __syncthreads();
         if (t < total)
             setup(t);
@@ -922,14 +953,16 @@ hipError_t launch_fc1_mx(const uint8_t* A, const uint8_t* a_scale, const uint8_t
                          const uint8_t* wg_scale, const uint8_t* wu, const uint8_t* wu_scale,
                          uint8_t* h, uint8_t* h_scale, const MTile* tiles,
                          const int32_t* tile_count, int64_t H, int64_t F, int32_t* task_ctr,
-                         hipStream_t s)
+                         const int32_t* gather, int gather_k, hipStream_t s)
 {
     if (hipError_t e = ensure_smem_limits(); e != hipSuccess)
         return e;
+    if (gather != nullptr && !mx_use_big(H, F))
+        return hipErrorInvalidValue;              // only the large-tile kernel gathers rows
     if (mx_use_big(H, F)) {
         big::grouped_gemm_mx_dma<true><<<dim3(device_info().cu_count), dim3(big::kThreads), big::kSmemBytes, s>>>(
             A, a_scale, wg, wg_scale, wu, wu_scale, h, h_scale, nullptr, tiles, tile_count,
-            static_cast<int>(H), static_cast<int>(F), nullptr, task_ctr);
+            static_cast<int>(H), static_cast<int>(F), nullptr, task_ctr, gather, gather_k);
         return hipGetLastError();
     }
     grouped_gemm_mx<true><<<dim3(persistent_grid()), dim3(kThreads), kSmemBytes, s>>>(
@@ -948,7 +981,7 @@ hipError_t launch_fc2_mx(const uint8_t* h, const uint8_t* h_scale, const uint8_t
     if (mx_use_big(H, F)) {
         big::grouped_gemm_mx_dma<false><<<dim3(device_info().cu_count), dim3(big::kThreads), big::kSmemBytes, s>>>(
             h, h_scale, wd, wd_scale, nullptr, nullptr, nullptr, nullptr, y, tiles, tile_count,
-            static_cast<int>(F), static_cast<int>(H), chunk_done, task_ctr);
+            static_cast<int>(F), static_cast<int>(H), chunk_done, task_ctr, nullptr, 1);
         return hipGetLastError();
     }
     grouped_gemm_mx<false><<<dim3(persistent_grid()), dim3(kThreads), kSmemBytes, s>>>(

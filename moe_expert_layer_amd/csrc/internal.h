@@ -126,10 +126,11 @@ hipError_t launch_unpermute(int dtype, const void* y_perm, const int32_t* pos, c
 bool bf16_supported(int64_t H, int64_t F);
 int bf16_row_tile(int64_t H, int64_t F);
 int bf16_fc2_cols_per_tile(int64_t H, int64_t F);
-// task_ctr: kXcdCount zeroed counters for this launch (workspace).
+// task_ctr: kXcdCount zeroed counters for this launch (workspace).  gather (may be null; only
+// with 256-row tiles): permuted row p of A is row gather[p] / gather_k of A.
 hipError_t launch_fc1_bf16(const uint16_t* A, const uint16_t* wg, const uint16_t* wu, uint16_t* h,
                            const MTile* tiles, const int32_t* tile_count, int64_t H, int64_t F,
-                           int32_t* task_ctr, hipStream_t s);
+                           int32_t* task_ctr, const int32_t* gather, int gather_k, hipStream_t s);
 hipError_t launch_fc2_bf16(const uint16_t* h, const uint16_t* wd, uint16_t* y, const MTile* tiles,
                            const int32_t* tile_count, int64_t H, int64_t F, int32_t* chunk_done,
                            int32_t* task_ctr, hipStream_t s);
@@ -148,12 +149,12 @@ hipError_t launch_fc1_mx(const uint8_t* A, const uint8_t* a_scale, const uint8_t
                          const uint8_t* wg_scale, const uint8_t* wu, const uint8_t* wu_scale,
                          uint8_t* h, uint8_t* h_scale, const MTile* tiles,
                          const int32_t* tile_count, int64_t H, int64_t F, int32_t* task_ctr,
-                         hipStream_t s);
+                         const int32_t* gather, int gather_k, hipStream_t s);
 hipError_t launch_fc2_mx(const uint8_t* h, const uint8_t* h_scale, const uint8_t* wd,
                          const uint8_t* wd_scale, uint16_t* y, const MTile* tiles,
                          const int32_t* tile_count, int64_t H, int64_t F, int32_t* chunk_done,
                          int32_t* task_ctr, hipStream_t s);
-// MX tile shapes: 256 x 256 when H and F are multiples of 512, else 128 x 128.
+// MX tile shapes: 256 x 256 when H and F are multiples of 1024, else 128 x 128.
 int mx_row_tile(int64_t H, int64_t F);
 int mx_fc2_cols_per_tile(int64_t H, int64_t F);
 hipError_t launch_mx_quantize(const float* v, int64_t rows, int64_t cols, uint8_t* codes,

@@ -24,13 +24,15 @@ def layer(inp, device="cuda"):
         expert_ids=tensor(inp.expert_ids, device), probs=tensor(inp.probs, device))
 
 
-def forward(mel, d, head_m_size=0, workspace=None):
+def forward(mel, d, head_m_size=0, workspace=None, separate_permute=False):
     if d.x.dtype == torch.uint8:
         return mel.expert_forward_mx(d.x, d.x_scale, d.w_gate, d.wg_scale, d.w_up, d.wu_scale,
                                      d.w_down, d.wd_scale, d.expert_ids, d.probs,
-                                     head_m_size=head_m_size, workspace=workspace)
+                                     head_m_size=head_m_size, workspace=workspace,
+                                     separate_permute=separate_permute)
     return mel.expert_forward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs,
-                              head_m_size=head_m_size, workspace=workspace)
+                              head_m_size=head_m_size, workspace=workspace,
+                              separate_permute=separate_permute)
 
 
 def host(t):

@@ -61,7 +61,8 @@ def _status(mel, prob):
     (dict(T=64, H=7168, F=2000, E=32, k=4, dtype=2), 2),       # MX: multiples of 128
     (dict(T=64, H=128, F=256, E=4, k=2, dtype=1, head_m_size=300), 1),
     (dict(T=64, H=128, F=256, E=4, k=2, dtype=1, head_m_size=512), 0),
-    (dict(T=64, H=128, F=256, E=4, k=2, dtype=0, flags=1), 1),
+    (dict(T=64, H=128, F=256, E=4, k=2, dtype=0, flags=1), 0),      # MOE_FLAG_SEPARATE_PERMUTE
+    (dict(T=64, H=128, F=256, E=4, k=2, dtype=0, flags=2), 1),      # unknown flag bit
 ])
 def test_problem_validation(mel, kw, expected):
     kw = dict(kw)

@@ -62,8 +62,11 @@ def _layer_case(name, n_edge_experts, n_random):
     # the benchmark's launch configuration, unchunked and chunked by 512 rows: identical bits
     out = dv.forward(mel, d, 0, workspace=_workspace(inp, 0))
     out512 = dv.forward(mel, d, 512, workspace=_workspace(inp, 512))
+    # and with the permute step as a kernel of its own instead of inside fc1's row copies
+    sep = dv.forward(mel, d, 0, workspace=_workspace(inp, 0), separate_permute=True)
     torch.cuda.synchronize()
     assert torch.equal(out, out512)
+    assert torch.equal(out, sep)
 
     rng = np.random.default_rng(7)
     nonempty = [e for e in range(inp.E) if counts[e] > 0]

@@ -221,6 +221,23 @@ def test_empty_and_degenerate():
         assert oracle.inf_norm_rel(out, ref) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("dtype,T,H,F", [("bf16", 700, 512, 384), ("bf16", 333, 256, 192),
+                                         ("mxfp8", 500, 1024, 1024), ("mxfp8", 300, 512, 512)],
+                         ids=["bf16_large", "bf16_small", "mx_large", "mx_small"])
+def test_permute_fused_into_fc1_is_bitwise_the_separate_kernel(dtype, T, H, F):
+    """The default forward reads fc1's rows from x through the slot list (large tiles); the
+    separate-permute flag runs the permute kernel first.  Same bits, unchunked and chunked; the
+    small-tile sizes take the separate kernel either way."""
+    inp = synth.make_layer(T=T, H=H, F=F, E=6, k=3, dtype=dtype, seed=21)
+    d = dv.layer(inp)
+    for head in (0, 512):
+        fused = dv.host(dv.forward(mel, d, head))
+        separate = dv.host(dv.forward(mel, d, head, separate_permute=True))
+        assert np.array_equal(fused, separate)
+    ref, *_ = oracle.forward(inp)
+    assert oracle.inf_norm_rel(fused, ref) <= TOL[dtype]
+
+
 def test_forward_out_of_range_ids_flagged():
     inp = synth.make_layer(T=100, H=128, F=64, E=4, k=2, dtype="bf16")
     inp.expert_ids[5, 1] = 9
