@@ -315,9 +315,12 @@ constexpr int kRingBytes = kStages * (kABytes + kBBytes);   // 128 KiB
 constexpr int kOutRows = 32;                           // epilogue staging: 32 rows x 64 columns
 constexpr int kOutWaveBytes = kOutRows * 128;          //   of bf16 per wave (4 KiB)
 constexpr int kSmemBytes = kRingBytes + kWaves * kOutWaveBytes;   // 160 KiB, the whole LDS of a CU
-constexpr int kACopies = kABytes / 1024 / kWaves;      // 1 KiB copies per wave per K step
-constexpr int kBCopies = kBBytes / 1024 / kWaves;
-constexpr int kCopies = kACopies + kBCopies;
+// A moves in pairs of K steps (rows of 128 bytes, whole cache lines): two pair stages of 32 KiB
+// fill the A half of the ring.  The weights move per K step through the four B stages.
+constexpr int kAPairBytes = 2 * kABytes;               // [256 rows][64 k]
+constexpr int kACopies = kAPairBytes / 1024 / kWaves;  // 1 KiB copies per wave per pair (4)
+constexpr int kBCopies = kBBytes / 1024 / kWaves;      // per wave per K step (2)
+static_assert(kACopies == 4 && kBCopies == 2, "the copy schedule below");
 
 template <bool kGated>
 struct BLayout {
@@ -339,55 +342,66 @@ __device__ __forceinline__ void step_barrier()
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
 }
 
-// A: LDS row r (64 bytes = 4 chunks of 8 k) keeps logical chunk c at position c ^ ((r >> 2) & 3):
-// 16 consecutive rows read at one chunk then cover all 16 bank groups of 16 bytes.
-// B: k row kr keeps 16-byte chunk c at c ^ (4 * (kr & 3)): the four k rows of one transposing read
-// group land 64 bytes apart within each 256-byte bank window.
+// A: LDS row r of a pair stage (128 bytes = 8 chunks of 8 k) keeps logical chunk c at position
+// c ^ ((r >> 1) & 7): the 16 rows one read instruction serves per chunk cover all 16 bank groups
+// of 16 bytes.  B: k row kr keeps 16-byte chunk c at c ^ (4 * (kr & 3)): the four k rows of one
+// transposing read group land 64 bytes apart within each 256-byte bank window.
 //
-// Copy j of wave w moves A rows 16 * (kACopies * w + j) .. + 15 (4 lanes per row) and B copy
-// slot bi (kRowsPerCopy k rows of one matrix).  The per-lane global offsets (a_voff, b_voff: the
-// lane's row and swizzled 16-byte chunk) stay fixed for a task; rows past the tile's last row
-// re-read its last row (their results are never stored).  A K step advances the two sources by BK
-// elements of A and BK weight rows.
+// A copy j of wave w moves pair rows 32 w + 8 j .. + 7 (8 lanes per 128-byte row); B copy j moves
+// slot bi0 + j (kRowsPerCopy k rows of one matrix).  The per-lane global offsets (a_voff, b_voff:
+// the lane's row and swizzled 16-byte chunk) stay fixed for a task; rows past the tile's last row
+// re-read its last row (their results are never stored).  Sources advance by 64 elements of A per
+// pair and BK weight rows per K step.
 struct CopyCtx {
-    const uint16_t* a;     // A at the first k of the next step to fetch
-    const uint16_t* b;     // this wave's weight matrix at that step's first k row
-    uint32_t a_lds;        // LDS destination of the wave's first A copy in stage 0
-    uint32_t b_lds;        // LDS destination of the wave's first B copy in stage 0
+    const uint16_t* a;     // A at the first k of the next pair to fetch
+    const uint16_t* b;     // this wave's weight matrix at the next step's first k row
+    uint32_t a_lds;        // LDS destination of the wave's first A copy in pair stage 0
+    uint32_t b_lds;        // LDS destination of the wave's first B copy in B stage 0
 };
 
-// Copy C (0 .. kCopies - 1) of a step into stage S: A copies first, then B copies.
-template <int S, int C>
+// What a sub-step copies: nothing, the weights of one step, the second half of a pair's A, or the
+// weights of one step and then the first half of a pair's A.
+enum CopySet { kNone = 0, kB = 1, kA2 = 2, kBA1 = 3 };
+template <int CS>
+constexpr int set_size() { return CS == kNone ? 0 : CS == kBA1 ? 4 : 2; }
+
+// Copy C of copy set CS: weights into B stage SB, A into pair stage QA.
+template <int CS, int SB, int QA, int C>
 __device__ __forceinline__ void copy_one(const CopyCtx& s, const uint32_t (&a_voff)[kACopies],
                                          const uint32_t (&b_voff)[kBCopies])
 {
-    if constexpr (C < kACopies)
-        lds_copy16(s.a, a_voff[C], s.a_lds + S * kABytes + C * 1024);
-    else
-        lds_copy16(s.b, b_voff[C - kACopies], s.b_lds + S * kBBytes + (C - kACopies) * 1024);
+    if constexpr (CS == kA2) {
+        lds_copy16(s.a, a_voff[2 + C], s.a_lds + QA * kAPairBytes + (2 + C) * 1024);
+    } else if constexpr (C < kBCopies) {
+        lds_copy16(s.b, b_voff[C], s.b_lds + SB * kBBytes + C * 1024);
+    } else {
+        lds_copy16(s.a, a_voff[C - kBCopies], s.a_lds + QA * kAPairBytes + (C - kBCopies) * 1024);
+    }
 }
 
-template <int S, int C0, int... Is>
+template <int CS, int SB, int QA, int C0, int... Is>
 __device__ __forceinline__ void copies_impl(std::integer_sequence<int, Is...>, const CopyCtx& s,
                                             const uint32_t (&a_voff)[kACopies],
                                             const uint32_t (&b_voff)[kBCopies])
 {
-    (copy_one<S, C0 + Is>(s, a_voff, b_voff), ...);
+    (copy_one<CS, SB, QA, C0 + Is>(s, a_voff, b_voff), ...);
 }
 
-// Copies C0 .. C1 - 1 of a step into stage S.
-template <int S, int C0, int C1>
+// Copies C0 .. C1 - 1 of copy set CS.
+template <int CS, int SB, int QA, int C0, int C1>
 __device__ __forceinline__ void copies(const CopyCtx& s, const uint32_t (&a_voff)[kACopies],
                                        const uint32_t (&b_voff)[kBCopies])
 {
-    copies_impl<S, C0>(std::make_integer_sequence<int, C1 - C0>{}, s, a_voff, b_voff);
+    copies_impl<CS, SB, QA, C0>(std::make_integer_sequence<int, C1 - C0>{}, s, a_voff, b_voff);
 }
 
-// Advances the copy sources by one K step.
-__device__ __forceinline__ void advance(CopyCtx& s, int64_t N_w)
+// All four A copies of a pair into pair stage QA (task prologue).
+template <int QA>
+__device__ __forceinline__ void issue_pair(const CopyCtx& s, const uint32_t (&a_voff)[kACopies])
 {
-    s.a += BK;
-    s.b += BK * N_w;
+#pragma unroll
+    for (int j = 0; j < kACopies; ++j)
+        lds_copy16(s.a, a_voff[j], s.a_lds + QA * kAPairBytes + j * 1024);
 }
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -400,13 +414,13 @@ struct Frags {
     i16x4_t lo[kTN];       // first half of b[j] until its second half arrives
 };
 
-// Fragment read Q of a sub-step (ks) of LDS stage S, in the order the next sub-step's MFMAs consume
-// them: Q = 0 is A row block 0, Q = 1 + 2 j, 2 + 2 j the two transposing reads (k 0..3, 4..7 of
-// the lane's 8) of weight block j, Q = 2 kTN + i (i >= 1) A row block i.  a_base[ks] / b_base[j]
-// are the lane's addresses in stage 0 (see the kernel); the stage, sub-step and block parts are
-// constants below 64 KiB that the LDS instructions take as immediate offsets.
+// Fragment read Q of sub-step KS of K step position S (B stage S, pair stage S / 2, pair half
+// S % 2), in the order the next sub-step's MFMAs consume them: Q = 0 is A row block 0, Q = 1 + 2 j,
+// 2 + 2 j the two transposing reads (k 0..3, 4..7 of the lane's 8) of weight block j, Q = 2 kTN + i
+// (i >= 1) A row block i.  a_base[h][ks] / b_base[j] are the lane's addresses in stage 0; the stage,
+// sub-step and block parts are constants below 64 KiB, immediate offsets of the LDS instructions.
 template <bool kGated, int S, int KS, int Q>
-__device__ __forceinline__ void read_one(Frags& f, const uint32_t (&a_base)[2], const uint32_t (&b_base)[kTN])
+__device__ __forceinline__ void read_one(Frags& f, const uint32_t (&a_base)[2][2], const uint32_t (&b_base)[kTN])
 {
     using L = BLayout<kGated>;
     if constexpr (Q >= 1 && Q <= 2 * kTN) {
@@ -420,129 +434,126 @@ __device__ __forceinline__ void read_one(Frags& f, const uint32_t (&a_base)[2], 
     } else {
         constexpr int i = Q == 0 ? 0 : Q - 2 * kTN;
         f.a[i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
-            a_base[KS] + S * kABytes + row_block<kWM>(i, 0) * 64);
+            a_base[S % 2][KS] + (S / 2) * kAPairBytes + kWM * 32 * 128 * i);
     }
 }
 
 template <bool kGated, int S, int KS, int Q0, int... Is>
 __device__ __forceinline__ void reads_impl(std::integer_sequence<int, Is...>, Frags& f,
-                                           const uint32_t (&a_base)[2], const uint32_t (&b_base)[kTN])
+                                           const uint32_t (&a_base)[2][2], const uint32_t (&b_base)[kTN])
 {
     (read_one<kGated, S, KS, Q0 + Is>(f, a_base, b_base), ...);
 }
 
 template <bool kGated, int S, int KS, int Q0, int Q1>
-__device__ __forceinline__ void reads(Frags& f, const uint32_t (&a_base)[2], const uint32_t (&b_base)[kTN])
+__device__ __forceinline__ void reads(Frags& f, const uint32_t (&a_base)[2][2], const uint32_t (&b_base)[kTN])
 {
     reads_impl<kGated, S, KS, Q0>(std::make_integer_sequence<int, Q1 - Q0>{}, f, a_base, b_base);
 }
 
 // Operands shared by the sub-steps of a K loop.
 struct LoopArgs {
-    const uint32_t (&a_base)[2];
+    const uint32_t (&a_base)[2][2];
     const uint32_t (&b_base)[kTN];
     const uint32_t (&a_voff)[kACopies];
     const uint32_t (&b_voff)[kBCopies];
 };
 
 // Slot M of a sub-step: MFMA M (row block M / kTN, column block M % kTN), then this slot's share of
-// the next sub-step's fragment reads (sub-step KS of stage SR) and of the step's copies (into stage
-// SC).  Reads and copies are spread evenly over the MFMAs, so the wave's in-order issue never
-// stalls on a burst of memory instructions, and no MFMA waits for a read issued just before it.
-template <bool kGated, int NB, int C0, int NC, int SR, int KS, int SC, int M>
+// the next sub-step's fragment reads (sub-step KS of step position SR) and of the sub-step's copies
+// (copy set CS into B stage SB / pair stage QA).  Reads and copies are spread evenly over the
+// MFMAs, so the wave's in-order issue never stalls on a burst of memory instructions, and no MFMA
+// waits for a read issued just before it.
+template <bool kGated, int NB, int CS, int SB, int QA, int SR, int KS, int M>
 __device__ __forceinline__ void slot(f32x16_t (&acc)[kTM][kTN], const Frags& use, Frags& load,
                                      const CopyCtx& cp, const LoopArgs& g)
 {
-    constexpr int NM = NB * kTN, NR = 2 * kTN + NB;
+    constexpr int NM = NB * kTN, NR = 2 * kTN + NB, NC = set_size<CS>();
     acc[M / kTN][M % kTN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(use.a[M / kTN], use.b[M % kTN],
                                                                     acc[M / kTN][M % kTN], 0, 0, 0);
     reads<kGated, SR, KS, M * NR / NM, (M + 1) * NR / NM>(load, g.a_base, g.b_base);
-    copies<SC, C0 + M * NC / NM, C0 + (M + 1) * NC / NM>(cp, g.a_voff, g.b_voff);
+    copies<CS, SB, QA, M * NC / NM, (M + 1) * NC / NM>(cp, g.a_voff, g.b_voff);
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool kGated, int NB, int C0, int NC, int SR, int KS, int SC, int... Ms>
+template <bool kGated, int NB, int CS, int SB, int QA, int SR, int KS, int... Ms>
 __device__ __forceinline__ void slots(std::integer_sequence<int, Ms...>, f32x16_t (&acc)[kTM][kTN],
                                       const Frags& use, Frags& load, const CopyCtx& cp,
                                       const LoopArgs& g)
 {
-    (slot<kGated, NB, C0, NC, SR, KS, SC, Ms>(acc, use, load, cp, g), ...);
+    (slot<kGated, NB, CS, SB, QA, SR, KS, Ms>(acc, use, load, cp, g), ...);
 }
 
-// One k sub-step: the NB * kTN MFMAs on `use`, the fragment reads of sub-step KS of stage SR into
-// `load`, and copies C0 .. C0 + NC - 1 of cp's step into stage SC.  A wave without MFMAs (NB = 0)
-// only issues the copies.
-template <bool kGated, int NB, int C0, int NC, int SR, int KS, int SC>
+// One k sub-step: the NB * kTN MFMAs on `use`, the fragment reads of sub-step KS of step position
+// SR into `load`, and the copies of set CS.  A wave without MFMAs (NB = 0) only issues the copies.
+template <bool kGated, int NB, int CS, int SB, int QA, int SR, int KS>
 __device__ __forceinline__ void substep(f32x16_t (&acc)[kTM][kTN], const Frags& use, Frags& load,
                                         const CopyCtx& cp, const LoopArgs& g)
 {
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NB == 0)
-        copies<SC, C0, C0 + NC>(cp, g.a_voff, g.b_voff);
+        copies<CS, SB, QA, 0, set_size<CS>()>(cp, g.a_voff, g.b_voff);
     else
-        slots<kGated, NB, C0, NC, SR, KS, SC>(std::make_integer_sequence<int, NB * kTN>{}, acc, use,
+        slots<kGated, NB, CS, SB, QA, SR, KS>(std::make_integer_sequence<int, NB * kTN>{}, acc, use,
                                               load, cp, g);
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Issues copies C0 .. C1 - 1 of cp's step into stage S (task prologue).
-template <int S, int C0, int C1>
-__device__ __forceinline__ void issue(const CopyCtx& cp, const uint32_t (&a_voff)[kACopies],
-                                      const uint32_t (&b_voff)[kBCopies])
-{
-    copies<S, C0, C1>(cp, a_voff, b_voff);
-}
+// Copy schedule.  The weights of K step s go out during the second sub-step of step s - 4 (into
+// the B stage step s - 4 has just freed).  The A of pair p (steps 2p, 2p + 1) goes out in two
+// halves, during the second sub-step of step 2p - 3 and the first sub-step of step 2p - 2 (into the
+// pair stage pair p - 2 has just freed).  Copies are issued in a fixed order, so "what step t + 1
+// needs has landed" is "at most N copies are in flight", N counted from that order: 8 at the
+// barrier of an even step, 2 at that of an odd one (fewer near the end of the task).
+constexpr int kWaitEven = 8, kWaitOdd = 2;
 
-// The copies of K step s go out in two halves: the A half during the second sub-step of step
-// s - kStages, the B half during the first sub-step of step s - kStages + 1, so every MFMA slot of
-// a step carries about the same number of copies.  Copies are issued in step order, so "step s has
-// landed" is "at most (the copies issued after it) are in flight".
-constexpr int kHalfA = kACopies;                  // copies 0 .. kHalfA - 1 of a step are its A half
-
-// K step kt (kt % kStages = S): sub-step 1 of stage S on the fragments of sub-step 0, with the B
-// half of step kt + kStages - 1 (into stage S - 1) when kCopyB; the barrier after which step kt + 1
-// has landed (at most W copies still in flight; no barrier for W < 0) and stage S is free; sub-step
-// 0 of stage S + 1 on the fragments of sub-step 1, with the A half of step kt + kStages (into
-// stage S) when kCopyA.
-template <bool kGated, int NB, int S, bool kCopyB, bool kCopyA, int W>
+// K step t (t % 4 = S): sub-step 1 of step t on the fragments of sub-step 0, with the second A half
+// of pair t / 2 + 1 when t is even and kCopyA2; the barrier after which step t + 1 has landed (at
+// most W copies in flight; none for W < 0) and step t's stages are free; sub-step 0 of step t + 1
+// on the fragments of sub-step 1, with the weights of step t + 4 (and, t odd, the first A half of
+// pair (t + 3) / 2) when kCopyB.
+template <bool kGated, int NB, int S, bool kCopyA2, bool kCopyB, int W>
 __device__ __forceinline__ void k_step(f32x16_t (&acc)[kTM][kTN], Frags& f0, Frags& f1, CopyCtx& cp,
                                        const LoopArgs& g, int64_t N_w)
 {
-    substep<kGated, NB, kHalfA, kCopyB ? kCopies - kHalfA : 0, S, 1, (S + kStages - 1) % kStages>(
-        acc, f0, f1, cp, g);
-    if constexpr (kCopyB)
-        advance(cp, N_w);
+    constexpr int CS1 = S % 2 == 0 && kCopyA2 ? kA2 : kNone;
+    constexpr int CS2 = !kCopyB ? kNone : S % 2 == 0 ? kB : kBA1;
+    constexpr int Qnext = (S / 2 + 1) % 2;                    // pair stage of pair t / 2 + 1
+    substep<kGated, NB, CS1, 0, Qnext, S, 1>(acc, f0, f1, cp, g);
+    if constexpr (CS1 == kA2)
+        cp.a += 64;                                           // the next pair's A
     if constexpr (W >= 0)
         step_barrier<W>();
     // after the last step this reads a stale stage whose fragments are never used
-    substep<kGated, NB, 0, kCopyA ? kHalfA : 0, (S + 1) % kStages, 0, S>(acc, f1, f0, cp, g);
+    substep<kGated, NB, CS2, S, S / 2, (S + 1) % kStages, 0>(acc, f1, f0, cp, g);
+    if constexpr (kCopyB)
+        cp.b += BK * N_w;
 }
 
-// Copies a task's setup leaves in flight once its step 0 has landed (steps 1, 2 and the A half of
-// step 3).
-constexpr int kTopWait = 2 * kCopies + kHalfA;
+// The K loop of one task.  KT is a multiple of kStages (at least kStages); the caller issued A
+// pair 0, the weights of steps 0 .. 3 and the first A half of pair 1, in that order, cp points at
+// pair 1 and at step 4's weights, and the caller has waited for step 0 (step_barrier<kTopWait>).
+// The body is unrolled over the four B stages (two pair stages), so every LDS address is a lane
+// base plus a constant.
+constexpr int kTopWait = 3 * kBCopies + 2;            // weights of steps 1 .. 3, first half of pair 1
 
-// The K loop of one task.  KT is a multiple of kStages (at least kStages); the caller issued the
-// copies of steps 0 .. kStages - 2 and the A half of step kStages - 1, cp points at that step, and
-// the caller has waited for step 0 (step_barrier<kTopWait>).  The body is unrolled over the kStages
-// stages, so every LDS address is a lane base plus a constant.
 template <bool kGated, int NB>
 __device__ __forceinline__ void k_loop(f32x16_t (&acc)[kTM][kTN], CopyCtx cp, const LoopArgs& g,
                                        int64_t N_w, int KT)
 {
     static_assert(kStages == 4, "the unrolled body below covers four stages");
-    constexpr int K2 = 2 * kCopies;
     Frags f0, f1;
     if constexpr (NB > 0)
         reads<kGated, 0, 0, 0, 2 * kTN + NB>(f0, g.a_base, g.b_base);
     for (int kt = 0; kt < KT - kStages; kt += kStages) {
-        k_step<kGated, NB, 0, true, true, K2>(acc, f0, f1, cp, g, N_w);
-        k_step<kGated, NB, 1, true, true, K2>(acc, f0, f1, cp, g, N_w);
-        k_step<kGated, NB, 2, true, true, K2>(acc, f0, f1, cp, g, N_w);
-        k_step<kGated, NB, 3, true, true, K2>(acc, f0, f1, cp, g, N_w);
+        k_step<kGated, NB, 0, true, true, kWaitEven>(acc, f0, f1, cp, g, N_w);
+        k_step<kGated, NB, 1, true, true, kWaitOdd>(acc, f0, f1, cp, g, N_w);
+        k_step<kGated, NB, 2, true, true, kWaitEven>(acc, f0, f1, cp, g, N_w);
+        k_step<kGated, NB, 3, true, true, kWaitOdd>(acc, f0, f1, cp, g, N_w);
     }
-    k_step<kGated, NB, 0, true, false, K2>(acc, f0, f1, cp, g, N_w);
-    k_step<kGated, NB, 1, false, false, kCopies>(acc, f0, f1, cp, g, N_w);
+    // the last four steps: only the second A half of the last pair is still to be copied
+    k_step<kGated, NB, 0, true, false, kWaitEven>(acc, f0, f1, cp, g, N_w);
+    k_step<kGated, NB, 1, false, false, 0>(acc, f0, f1, cp, g, N_w);
     k_step<kGated, NB, 2, false, false, 0>(acc, f0, f1, cp, g, N_w);
     k_step<kGated, NB, 3, false, false, -1>(acc, f0, f1, cp, g, N_w);
 }
@@ -656,13 +667,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
     // fragment reads: the lane's LDS addresses in stage 0 (A: row block 0 of this wave, sub-step ks;
     // B: weight block j, sub-step 0).  Each is hidden from the optimiser so that it stays one
     // register and the constant parts of every read go into the instruction's offset field.
-    uint32_t a_base[2];
+    uint32_t a_base[2][2];                                    // [pair half][sub-step]
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        const int r = lane & 31;
-        a_base[ks] = lds0 + row_block<kWM>(0, wm) * 64 + r * 64 + 16 * ((2 * ks + (lane >> 5)) ^ ((r >> 2) & 3));
-        asm volatile("" : "+v"(a_base[ks]));
-    }
+    for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int r = lane & 31;
+            a_base[hp][ks] = lds0 + row_block<kWM>(0, wm) * 128 + r * 128 +
+                             16 * ((4 * hp + 2 * ks + (lane >> 5)) ^ ((r >> 1) & 7));
+            asm volatile("" : "+v"(a_base[hp][ks]));
+        }
     uint32_t b_base[kTN];
     {
         const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
@@ -696,7 +710,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
         const MTile tl = decode_task(t, n_nt, tiles, nt);
 #pragma unroll
         for (int j = 0; j < kACopies; ++j) {
-            const int r = 16 * (kACopies * wave + j) + lane / 4;
+            const int r = 32 * wave + 8 * j + lane / 8;
             gsrc[j] = gather[tl.row_begin + min(r, tl.row_end - tl.row_begin - 1)];   // used in setup
         }
     };
@@ -707,20 +721,25 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
         const int rows = tile.row_end - tile.row_begin;
 #pragma unroll
         for (int j = 0; j < kACopies; ++j) {
-            const int r = 16 * (kACopies * wave + j) + lane / 4;
-            const int c = (lane & 3) ^ ((r >> 2) & 3);
+            const int r = 32 * wave + 8 * j + lane / 8;
+            const int c = (lane & 7) ^ ((r >> 1) & 7);
             const int src = gather != nullptr ? gsrc[j] / gather_k : min(r, rows - 1);
             a_voff[j] = static_cast<uint32_t>(src) * static_cast<uint32_t>(K) * 2u + 16u * c;
         }
         cp.a = gather != nullptr ? A : A + static_cast<int64_t>(tile.row_begin) * K;
         cp.b = (kGated && wave >= kWaves / 2 ? B1 : B0) + static_cast<int64_t>(tile.expert) * K * N_w + n0;
-        issue<0, 0, kCopies>(cp, a_voff, b_voff);
-        advance(cp, N_w);
-        issue<1, 0, kCopies>(cp, a_voff, b_voff);
-        advance(cp, N_w);
-        issue<2, 0, kCopies>(cp, a_voff, b_voff);
-        advance(cp, N_w);
-        issue<3, 0, kHalfA>(cp, a_voff, b_voff);
+        // A pair 0, the weights of steps 0 .. 3, the first half of A pair 1 (k_loop's order)
+        issue_pair<0>(cp, a_voff);
+        cp.a += 64;
+        copies<kB, 0, 0, 0, kBCopies>(cp, a_voff, b_voff);
+        cp.b += BK * N_w;
+        copies<kB, 1, 0, 0, kBCopies>(cp, a_voff, b_voff);
+        cp.b += BK * N_w;
+        copies<kB, 2, 0, 0, kBCopies>(cp, a_voff, b_voff);
+        cp.b += BK * N_w;
+        copies<kB, 3, 0, 0, kBCopies>(cp, a_voff, b_voff);
+        cp.b += BK * N_w;
+        copies<kBA1, 0, 1, kBCopies, kBCopies + 2>(cp, a_voff, b_voff);
     };
 
     int t = claim_task(claimed, task_ctr, xcd, blk, wave, lane);
