@@ -354,9 +354,11 @@ constexpr int kScRing = kRingBytes;
 constexpr int kOutBase = kScRing + 2 * kScSlotBytes;  // 144 KiB
 constexpr int kOutWaveBytes = 2048;                   // epilogue staging per wave
 constexpr int kSmemBytes = kOutBase + kWaves * kOutWaveBytes;   // 160 KiB
-constexpr int kACopies = kABytes / 1024 / kWaves;     // 2
+// A moves in pairs of K steps (rows of 128 bytes, whole cache lines): two pair stages of 32 KiB
+// fill the A half of the ring.  The weights move per K step through the four B stages.
+constexpr int kAPairBytes = 2 * kABytes;              // [256 rows][128 k]
+constexpr int kACopies = kAPairBytes / 1024 / kWaves; // per wave per pair (4)
 constexpr int kBCopies = kBBytes / 1024 / kWaves;     // 2
-constexpr int kDataCopies = kACopies + kBCopies;
 static_assert(kSmemBytes <= 160 * 1024, "LDS");
 
 template <bool kGated>
@@ -377,12 +379,6 @@ __device__ __forceinline__ int bswz(int c, int kr)
     return BLayout<kGated>::kChunks == 16 ? c ^ ((kr & 7) << 1) : c ^ (((kr >> 1) & 3) << 1);
 }
 
-// Copies of K step s in flight: data copies, plus one scale copy per wave when s opens a scale
-// block (s % 8 == 0); none past the last step.
-constexpr int group_copies(int s_pos, bool exists)
-{
-    return exists ? kDataCopies + (s_pos % kScaleSteps == 0 ? 1 : 0) : 0;
-}
 
 // Waits until at most N copies of this wave are in flight and for its LDS reads, then joins the
 // workgroup barrier (one statement with a memory clobber).
@@ -393,9 +389,9 @@ __device__ __forceinline__ void step_barrier()
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
 }
 
-// Copy sources of the next step to fetch (uniform) and the LDS destinations of this wave's copies
-// in stage 0 / scale slot 0.  A step advances A by BK bytes and the weights by BK rows; a scale
-// block advances the scale source by sc_step bytes.
+// Copy sources (uniform) and the LDS destinations of this wave's copies in stage 0 / pair stage 0
+// / scale slot 0: A at the next pair to fetch (a pair advances it by 2 BK bytes), the weights at
+// the next step (BK rows per step), the scales at the next block (sc_step bytes per block).
 struct MxCopy {
     const uint8_t* a;
     const uint8_t* b;
@@ -404,28 +400,29 @@ struct MxCopy {
     uint32_t a_lds, b_lds, sc_lds;
 };
 
-// The copies of one K step into stage S, with the scales of the block it opens into slot Q when
-// kScale.
-template <bool kScale, int S, int Q>
-__device__ __forceinline__ void mx_issue(const MxCopy& c, const uint32_t (&a_voff)[kACopies],
-                                         const uint32_t (&b_voff)[kBCopies], uint32_t sc_voff)
+// The copies of one K step: the scales of the block it opens into slot Q when kScale, its weights
+// into B stage SB, and the A of a pair into pair stage QA when QA >= 0 (in that order); each
+// source then moves on.
+template <bool kScale, int Q, int SB, int QA>
+__device__ __forceinline__ void mx_issue(MxCopy& c, const uint32_t (&a_voff)[kACopies],
+                                         const uint32_t (&b_voff)[kBCopies], uint32_t sc_voff, int64_t N_w)
 {
-    if constexpr (kScale)
+    if constexpr (kScale) {
         lds_copy16(c.sc, sc_voff, c.sc_lds + Q * kScSlotBytes);
-#pragma unroll
-    for (int j = 0; j < kACopies; ++j)
-        lds_copy16(c.a, a_voff[j], c.a_lds + S * kABytes + j * 1024);
-#pragma unroll
-    for (int j = 0; j < kBCopies; ++j)
-        lds_copy16(c.b, b_voff[j], c.b_lds + S * kBBytes + j * 1024);
-}
-
-__device__ __forceinline__ void mx_advance(MxCopy& c, int64_t N_w, bool scale)
-{
-    c.a += BK;
-    c.b += BK * N_w;
-    if (scale)
         c.sc += c.sc_step;
+    }
+    if constexpr (SB >= 0) {
+#pragma unroll
+        for (int j = 0; j < kBCopies; ++j)
+            lds_copy16(c.b, b_voff[j], c.b_lds + SB * kBBytes + j * 1024);
+        c.b += BK * N_w;
+    }
+    if constexpr (QA >= 0) {
+#pragma unroll
+        for (int j = 0; j < kACopies; ++j)
+            lds_copy16(c.a, a_voff[j], c.a_lds + QA * kAPairBytes + j * 1024);
+        c.a += 2 * BK;
+    }
 }
 
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
@@ -458,7 +455,7 @@ __device__ __forceinline__ int read_u8(uint32_t p)
 // scale block).  Each is one register hidden from the optimiser, so the stage, slot, step and
 // block parts below are immediate offsets of the LDS instructions.
 struct LaneAddr {
-    uint32_t a0, a1;          // A chunks h and 2 + h of the lane's row
+    uint32_t a[2][2];         // A, pair half hp: chunks 4 hp + h and 4 hp + 2 + h of the lane's row
     uint32_t b[kTN];          // first transposing read of weight block j
     uint32_t asc;             // A scale byte: row * 16 + h
     uint32_t bsc;             // weight scale byte of block 0: column + h * row bytes (block j at
@@ -494,10 +491,12 @@ __device__ __forceinline__ void mfma_pair(f32x16_t (&acc)[kTM][kTN], const MxFra
 template <int NB, int P, int p>
 __device__ __forceinline__ void read_a_frags(MxFrags& A, const LaneAddr& la)
 {
-    constexpr int S = p % kStages;
+    constexpr int S = p % kStages;                // pair stage S / 2, pair half S % 2
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-        A.a[i] = read_a(la.a0 + S * kABytes + row_block<kWM>(i, 0) * 64, la.a1 + S * kABytes + row_block<kWM>(i, 0) * 64);
+        constexpr int kRowBlock = kWM * 32 * 128;
+        A.a[i] = read_a(la.a[S % 2][0] + (S / 2) * kAPairBytes + i * kRowBlock,
+                        la.a[S % 2][1] + (S / 2) * kAPairBytes + i * kRowBlock);
         A.sa[i] = read_u8(la.asc + P * kScSlotBytes + row_block<kWM>(i, 0) * 16 + 2 * p);
     }
 }
@@ -515,12 +514,31 @@ __device__ __forceinline__ void read_b_frags(i32x8_t (&b)[2], int (&sb)[2], cons
     }
 }
 
-// K step kt at position p of a 16-step unit (stage p % 4; scales of the 8-step block in slot
-// p / 8): the MFMAs of weight blocks 0-1 (fragments loaded during the previous step) while the
-// fragments of blocks 2-3 are read; the barrier after which step kt + 1 has landed (W copies may
-// stay in flight; none when W < 0); the copies of step kt + 4 (when kCopy); the next step's A and
-// blocks 0-1 fragments; the MFMAs of blocks 2-3.
-template <bool kGated, int NB, int p, bool kCopy, int W>
+// Copy schedule.  After the barrier of step t: the scales of the block step t + 4 opens (when it
+// opens one), the weights of step t + 4 (into the B stage step t has just freed) and, t odd, the A
+// of pair (t + 3) / 2 (into the pair stage pair (t - 1) / 2 has just freed), in that order.  Copies
+// are issued in a fixed order, so "what step t + 1 needs has landed" is "at most N copies are in
+// flight", counted from that order: at an odd step, the weights of step t + 3 and any scales
+// issued with them (none near the end of the task); at an even step, what step t + 1 needs was
+// already complete at the previous barrier except for a task's first step, where 8 is exact.
+constexpr bool scale_at(int u) { return u % kScaleSteps == 4; }   // step u issues scales
+template <int p, bool kLast>
+constexpr int mx_wait()
+{
+    if (p % 2 == 0)
+        return 2 * kBCopies + kACopies;
+    const bool w = !kLast || p + 3 < 2 * kScaleSteps;             // step t + 3 exists
+    const bool sc = scale_at(p - 1) && (!kLast || p + 3 < 2 * kScaleSteps);
+    return (w ? kBCopies : 0) + (sc ? 1 : 0);
+}
+
+// K step kt at position p of a 16-step unit (stage p % 4, pair stage p % 4 / 2; scales of the
+// 8-step block in slot p / 8): the MFMAs of weight blocks 0-1 (fragments loaded during the
+// previous step) while the fragments of blocks 2-3 are read; the barrier after which step kt + 1
+// has landed (W copies may stay in flight; none when W < 0); the copies (weights and scales of
+// step kt + 4 when kCopyB, A of pair (kt + 3) / 2 when kCopyA); the next step's A and blocks 0-1
+// fragments; the MFMAs of blocks 2-3.
+template <bool kGated, int NB, int p, bool kCopyB, bool kCopyA, int W>
 __device__ __forceinline__ void mx_step(f32x16_t (&acc)[kTM][kTN], const MxFrags& Acur, MxFrags& Anext,
                                         i32x8_t (&b01)[2], int (&sb01)[2], i32x8_t (&b23)[2],
                                         int (&sb23)[2], const LaneAddr& la, MxCopy& cp,
@@ -539,11 +557,8 @@ __device__ __forceinline__ void mx_step(f32x16_t (&acc)[kTM][kTN], const MxFrags
     if constexpr (W >= 0)
         step_barrier<W>();
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kCopy) {
-        // step kt + 4 lands in this step's stage; it opens a scale block when q == 4 (other slot)
-        mx_issue<q == 4, p % kStages, 1 - P>(cp, a_voff, b_voff, sc_voff);
-        mx_advance(cp, N_w, q == 4);
-    }
+    mx_issue<kCopyB && q == 4, 1 - P, kCopyB ? p % kStages : -1, kCopyA ? ((p + 3) / 2) % 2 : -1>(
+        cp, a_voff, b_voff, sc_voff, N_w);
     if constexpr (NB > 0) {
         // after the last step these read a stale stage whose fragments are never used
         read_a_frags<NB, Pn, qn>(Anext, la);
@@ -555,16 +570,8 @@ __device__ __forceinline__ void mx_step(f32x16_t (&acc)[kTM][kTN], const MxFrags
 
 constexpr int kUnit = 2 * kScaleSteps;    // steps per unrolled unit: four stages, two scale slots
 
-// Copies in flight at the barrier of the step at position p (steps kt + 2 and kt + 3; in the last
-// unit of a task, only those that exist).
-template <int p, bool kLast>
-constexpr int mx_wait()
-{
-    return group_copies(p + 2, !kLast || p + 2 < kUnit) + group_copies(p + 3, !kLast || p + 3 < kUnit);
-}
-
-// One unit of 16 K steps; in the last unit of a task, copies stop after position 11 and the last
-// step has no barrier.
+// One unit of 16 K steps; in the last unit of a task, the weight copies stop after position 11,
+// the A copies after position 11, and the last step has no barrier.
 template <bool kGated, int NB, bool kLast, int... Ps>
 __device__ __forceinline__ void mx_unit_impl(std::integer_sequence<int, Ps...>, f32x16_t (&acc)[kTM][kTN],
                                              MxFrags& A0, MxFrags& A1, i32x8_t (&b01)[2], int (&sb01)[2],
@@ -574,9 +581,11 @@ __device__ __forceinline__ void mx_unit_impl(std::integer_sequence<int, Ps...>, 
                                              int64_t N_w)
 {
     ((Ps % 2 == 0
-          ? mx_step<kGated, NB, Ps, !kLast || Ps + 4 < kUnit, kLast && Ps == kUnit - 1 ? -1 : mx_wait<Ps, kLast>()>(
+          ? mx_step<kGated, NB, Ps, !kLast || Ps + 4 < kUnit, Ps % 2 == 1 && (!kLast || Ps + 3 < kUnit),
+                    kLast && Ps == kUnit - 1 ? -1 : mx_wait<Ps, kLast>()>(
                 acc, A0, A1, b01, sb01, b23, sb23, la, cp, a_voff, b_voff, sc_voff, N_w)
-          : mx_step<kGated, NB, Ps, !kLast || Ps + 4 < kUnit, kLast && Ps == kUnit - 1 ? -1 : mx_wait<Ps, kLast>()>(
+          : mx_step<kGated, NB, Ps, !kLast || Ps + 4 < kUnit, Ps % 2 == 1 && (!kLast || Ps + 3 < kUnit),
+                    kLast && Ps == kUnit - 1 ? -1 : mx_wait<Ps, kLast>()>(
                 acc, A1, A0, b01, sb01, b23, sb23, la, cp, a_voff, b_voff, sc_voff, N_w)),
      ...);
 }
@@ -592,12 +601,14 @@ __device__ __forceinline__ void mx_unit(f32x16_t (&acc)[kTM][kTN], MxFrags& A0, 
                                     sb23, la, cp, a_voff, b_voff, sc_voff, N_w);
 }
 
-// Copies a task's setup leaves in flight once its step 0 has landed (steps 1 .. 3).
-constexpr int kTopWait = group_copies(1, true) + group_copies(2, true) + group_copies(3, true);
+// Copies a task's setup leaves in flight once its step 0 has landed: the weights of steps 1 .. 3
+// and A pair 1.
+constexpr int kTopWait = 3 * kBCopies + kACopies;
 
-// The K loop of one task.  KT is a multiple of 16; the caller issued the copies of steps 0 .. 3,
-// cp points at step 4, and the caller has waited for step 0 (step_barrier<kTopWait>).  Every LDS
-// address is a lane base plus a constant.
+// The K loop of one task.  KT is a multiple of 16; the caller issued the scales of block 0, A pair
+// 0, the weights of steps 0 .. 3 and A pair 1 (in that order), cp points at pair 2, step 4 and
+// block 1, and the caller has waited for step 0 (step_barrier<kTopWait>).  Every LDS address is a
+// lane base plus a constant.
 template <bool kGated, int NB>
 __device__ __forceinline__ void mx_k_loop(f32x16_t (&acc)[kTM][kTN], const LaneAddr& la, MxCopy cp,
                                           const uint32_t (&a_voff)[kACopies],
@@ -765,8 +776,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
     {
         const int r = lane & 31;
         const uint32_t rb = row_block<kWM>(0, wm);
-        la.a0 = lds0 + rb * 64 + r * 64 + 16 * ((0 + h) ^ ((r >> 2) & 3));
-        la.a1 = lds0 + rb * 64 + r * 64 + 16 * ((2 + h) ^ ((r >> 2) & 3));
+        // A pair rows of 128 bytes keep logical chunk c at c ^ ((r >> 1) & 7)
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp) {
+            la.a[hp][0] = lds0 + rb * 128 + r * 128 + 16 * ((4 * hp + h) ^ ((r >> 1) & 7));
+            la.a[hp][1] = lds0 + rb * 128 + r * 128 + 16 * ((4 * hp + 2 + h) ^ ((r >> 1) & 7));
+        }
         la.asc = lds0 + kScRing + rb * 16 + r * 16 + h;
         const int g = lane >> 4, sl = lane & 15;
         const int hh = g >> 1;
@@ -780,7 +795,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
         }
         // block 0's scale column: the wave's first output column plus the lane's
         la.bsc = lds0 + kScRing + kAScBytes + h * L::kRowBytes + (kGated ? 16 * kTN * wn : 32 * kTN * wn) + (lane & 31);
-        asm volatile("" : "+v"(la.a0), "+v"(la.a1), "+v"(la.asc), "+v"(la.bsc));
+        asm volatile("" : "+v"(la.a[0][0]), "+v"(la.a[0][1]), "+v"(la.a[1][0]), "+v"(la.a[1][1]),
+                          "+v"(la.asc), "+v"(la.bsc));
 #pragma unroll
         for (int j = 0; j < kTN; ++j)
             asm volatile("" : "+v"(la.b[j]));
@@ -803,7 +819,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
         const int last = tl.row_end - tl.row_begin - 1;
 #pragma unroll
         for (int j = 0; j < kACopies; ++j)
-            gsrc[j] = gather[tl.row_begin + min(16 * (kACopies * wave + j) + lane / 4, last)];
+            gsrc[j] = gather[tl.row_begin + min(32 * wave + 8 * j + lane / 8, last)];
         if (wave < 4)
             gsrc[kACopies] = gather[tl.row_begin + min(64 * wave + lane, last)];
     };
@@ -814,8 +830,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
         const int rows = tile.row_end - tile.row_begin;
 #pragma unroll
         for (int j = 0; j < kACopies; ++j) {
-            const int r = 16 * (kACopies * wave + j) + lane / 4;
-            const int c = (lane & 3) ^ ((r >> 2) & 3);
+            const int r = 32 * wave + 8 * j + lane / 8;           // 8 lanes per 128-byte pair row
+            const int c = (lane & 7) ^ ((r >> 1) & 7);
             const int src = gather != nullptr ? gsrc[j] / gather_k : min(r, rows - 1);
             a_voff[j] = static_cast<uint32_t>(src) * static_cast<uint32_t>(K) + 16u * c;
         }
@@ -842,14 +858,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
                 sc_voff = static_cast<uint32_t>(lane >> 4) * static_cast<uint32_t>(N_out) + 16u * (lane & 15);
             }
         }
-        mx_issue<true, 0, 0>(cp, a_voff, b_voff, sc_voff);
-        mx_advance(cp, N_w, true);
-        mx_issue<false, 1, 0>(cp, a_voff, b_voff, sc_voff);
-        mx_advance(cp, N_w, false);
-        mx_issue<false, 2, 0>(cp, a_voff, b_voff, sc_voff);
-        mx_advance(cp, N_w, false);
-        mx_issue<false, 3, 0>(cp, a_voff, b_voff, sc_voff);
-        mx_advance(cp, N_w, false);
+        // scales of block 0 and A pair 0, the weights of steps 0 .. 3, A pair 1 (mx_k_loop's order)
+        mx_issue<true, 0, -1, 0>(cp, a_voff, b_voff, sc_voff, N_w);
+        mx_issue<false, 0, 0, -1>(cp, a_voff, b_voff, sc_voff, N_w);
+        mx_issue<false, 0, 1, -1>(cp, a_voff, b_voff, sc_voff, N_w);
+        mx_issue<false, 0, 2, -1>(cp, a_voff, b_voff, sc_voff, N_w);
+        mx_issue<false, 0, 3, -1>(cp, a_voff, b_voff, sc_voff, N_w);
+        mx_issue<false, 0, -1, 1>(cp, a_voff, b_voff, sc_voff, N_w);
     };
 
     int t = claim_task(claimed, task_ctr, xcd, blk, wave, lane);
