@@ -119,6 +119,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-chunked", action="store_true")
+    ap.add_argument("--skip-router", action="store_true")
     ap.add_argument("--separate-permute", action="store_true",
                     help="run the permute step as its own kernel instead of inside fc1's row loads")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -262,6 +263,28 @@ def main():
                    "p90_ms": float(np.percentile(ms, 90)),
                    "wall_ms_per_step_incl_flush": wall * 1e3 / args.steps},
     }
+
+    # the router in front of the layer (top-k gate over this workload's logits), timed on its own:
+    # the layer's step starts from expert ids, as the benchmark's metric does
+    if not args.skip_router:
+        kw = {key: cfg[key] for key in ("zipf_s", "n_zero") if key in cfg}
+        logits = torch.from_numpy(
+            synth.make_logits(T, E, cfg.get("routing", "normal_logits"), seed=0, **kw)).to(dev)
+        for _ in range(3):
+            mel.router_topk(logits, k)
+        torch.cuda.synchronize()
+        mel.timing_reset()
+        mel.timing_enable(True)
+        for _ in range(args.steps):
+            do_flush()
+            mel.router_topk(logits, k)
+        rk = mel.timing_collect()
+        mel.timing_enable(False)
+        r_ms = rk["router"][0] / rk["router"][1]
+        r_bytes = T * E * 4 + T * k * 8
+        result["router"] = {"ms": r_ms, "bytes": r_bytes, "GB/s": r_bytes / (r_ms * 1e-3) / 1e9,
+                            "frac": r_bytes / (r_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        log(f"router {r_ms * 1e3:.1f} us ({r_bytes / (r_ms * 1e-3) / 1e9:.0f} GB/s)")
 
     if not args.skip_chunked:
         for _ in range(2):

@@ -171,6 +171,18 @@ moe_status moe_grouped_ffn_mx(const moe_problem* p, const uint8_t* rows, const u
                               const uint8_t* wd_scale, void* y_rows, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
+/* Router in front of the layer: the gate's top-k.  logits [T, E] float32 (E <= 1024) ->
+ * expert_ids [T, k] int32 and probs [T, k] float32 (1 <= k <= min(E, 64)), ready for
+ * moe_expert_forward.  The gate is the first step of the step breakdown on the page "MC2 通算融合";
+ * the router top-k distribution is one of the checks listed on the page "NPU Training Operators -
+ * MC2" (验证项).  Per token: the k largest logits in descending order, equal logits taken in
+ * ascending expert id; probs[t, j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k selected
+ * (the softmax over all E renormalised over the k), float32 arithmetic.  Logits must not be NaN and
+ * each token's largest logit must be finite (-inf logits are taken last, with probability 0).
+ * Errors: MOE_ERR_INVALID_ARGUMENT for bad sizes or null pointers (nothing enqueued). */
+moe_status moe_router_topk(const float* logits, int64_t T, int64_t E, int64_t k,
+                           int32_t* expert_ids, float* probs, hipStream_t stream);
+
 /* OCP-MX encoder used on h inside the MX layer, exposed on its own: v [rows, cols] float32
  * (cols a multiple of 32) -> codes [rows, cols] E4M3 bytes and scales [rows, cols/32] E8M0 bytes.
  * Shared exponent floor(log2 max|block|) - 8 clamped to [-127, 127] (-127 for an all-zero block);

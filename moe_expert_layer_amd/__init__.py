@@ -61,6 +61,7 @@ _SIGS = {
     "moe_grouped_ffn_mx": [ctypes.POINTER(MoeProblem), _P, _P, _I64, _P, _P, _I64, _P, _P, _P,
                            _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_mx_quantize": [_P, _I64, _I64, _P, _P, _P],
+    "moe_router_topk": [_P, _I64, _I64, _I64, _P, _P, _P],
     "moe_query_device_status": [_P, _P, ctypes.POINTER(ctypes.c_int32)],
     "moe_chunk_counters": [ctypes.POINTER(MoeProblem), _P, ctypes.c_size_t, _I64,
                            ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_I64)],
@@ -308,6 +309,16 @@ def grouped_ffn_mx(rows, rows_scale, group_offsets, group_expert, w_gate, wg_sca
         _ptr(group_expert), G, _ptr(w_gate), _ptr(wg_scale), _ptr(w_up), _ptr(wu_scale),
         _ptr(w_down), _ptr(wd_scale), _ptr(out), _ptr(ws), ws.numel(), _stream(rows)))
     return out
+
+
+def router_topk(logits, k: int):
+    """Top-k gate: float32 logits [T, E] -> (expert_ids int32 [T, k], probs float32 [T, k])."""
+    _need(logits, "logits", torch.float32)
+    T, E = logits.shape
+    ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    probs = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check(library().moe_router_topk(_ptr(logits), T, E, k, _ptr(ids), _ptr(probs), _stream(logits)))
+    return ids, probs
 
 
 def mx_quantize(v):

@@ -16,7 +16,8 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libmoe_expert_layer.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm_f32.hip", "gemm_bf16.hip", "gemm_mx.hip"]
+SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm_f32.hip", "gemm_bf16.hip", "gemm_mx.hip",
+           "router.hip"]
 HEADERS = ["common.h", "internal.h", "gemm_common.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

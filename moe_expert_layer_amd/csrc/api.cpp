@@ -616,6 +616,21 @@ MOE_API moe_status moe_mx_quantize(const float* v, int64_t rows, int64_t cols, u
     return MOE_OK;
 }
 
+MOE_API moe_status moe_router_topk(const float* logits, int64_t T, int64_t E, int64_t k,
+                                   int32_t* expert_ids, float* probs, hipStream_t stream)
+{
+    if (T < 0 || E < 1 || E > 1024 || k < 1 || k > E || k > 64)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "need T >= 0, 1 <= E <= 1024, 1 <= k <= min(E, 64)");
+    if (T * E > (int64_t{1} << 40))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "T * E too large");
+    if (T == 0)
+        return MOE_OK;
+    if (logits == nullptr || expert_ids == nullptr || probs == nullptr)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+    LAUNCH(stream, "router", launch_router(logits, T, E, k, expert_ids, probs, stream));
+    return MOE_OK;
+}
+
 MOE_API moe_status moe_query_device_status(const void* workspace, hipStream_t stream,
                                            int32_t* status)
 {

@@ -157,6 +157,9 @@ hipError_t launch_fc2_mx(const uint8_t* h, const uint8_t* h_scale, const uint8_t
 // MX tile shapes: 256 x 256 when H and F are multiples of 1024, else 128 x 128.
 int mx_row_tile(int64_t H, int64_t F);
 int mx_fc2_cols_per_tile(int64_t H, int64_t F);
+// router.hip: top-k gate over float32 logits [T, E] (E <= 1024, k <= min(E, 64)).
+hipError_t launch_router(const float* logits, int64_t T, int64_t E, int64_t k, int32_t* ids,
+                         float* probs, hipStream_t s);
 hipError_t launch_mx_quantize(const float* v, int64_t rows, int64_t cols, uint8_t* codes,
                               uint8_t* scales, hipStream_t s);
 

@@ -51,6 +51,8 @@ def _load():
             P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
             lib.oracle_route.argtypes = [P, I64, I64, I64, P, P, P, P]
             lib.oracle_route.restype = I32
+            lib.oracle_router.argtypes = [P, I64, I64, I64, P, P]
+            lib.oracle_router.restype = None
             lib.oracle_permute.argtypes = [P, I64, P, I64, I64, P]
             lib.oracle_permute.restype = None
             lib.oracle_ffn_rows.argtypes = [I32, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P]
@@ -152,6 +154,19 @@ def route(expert_ids, E: int):
     if rc != 0:
         raise OracleError("expert id out of range")
     return counts, offsets, perm, pos
+
+
+def router(logits, k: int):
+    """Top-k gate: (expert_ids int32 [T, k] in descending logit order, ties to the lower id;
+    probs float64 [T, k] = softmax over the k selected logits) for float32 logits [T, E]."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    ids = np.empty((T, k), np.int32)
+    probs = np.empty((T, k), np.float64)
+    _load().oracle_router(_p(logits), T, E, k, _p(ids), _p(probs))
+    return ids, probs
 
 
 def permute(x, perm, k: int) -> np.ndarray:

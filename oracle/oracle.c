@@ -409,6 +409,40 @@ int oracle_forward_tokens(int dtype, int64_t T, int64_t H, int64_t F, int64_t E,
     return rc;
 }
 
+/* ------------------------------------------------------------------------------------------------
+ * Router in front of the path: the gate's top-k (the "Gate 计算" step of the step breakdown on the
+ * page "MC2 通算融合"; the router top-k distribution is one of the checks listed on the page "NPU
+ * Training Operators - MC2").  Reading taken: the k experts with the largest logits, in descending
+ * logit order, ties broken towards the lower expert id; the probability of each is the softmax over
+ * the k selected logits, which equals the softmax over all E experts renormalised over the k.
+ * Per token: k passes of a plain scan for the largest not yet taken logit (strictly greater wins,
+ * so the first of equal logits is kept), then exp(l_j - l_max) / sum_i exp(l_i - l_max) in double.
+ * Logits must not be NaN, and the largest logit of a token must be finite.
+ * ---------------------------------------------------------------------------------------------- */
+void oracle_router(const float* logits, int64_t T, int64_t E, int64_t k, int32_t* ids, double* probs)
+{
+    char* taken = (char*)malloc(E > 0 ? (size_t)E : 1);
+    for (int64_t t = 0; t < T; ++t) {
+        const float* l = logits + t * E;
+        memset(taken, 0, (size_t)E);
+        for (int64_t j = 0; j < k; ++j) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; ++e)
+                if (!taken[e] && (best < 0 || l[e] > l[best]))
+                    best = e;
+            taken[best] = 1;
+            ids[t * k + j] = (int32_t)best;
+        }
+        const double m = (double)l[ids[t * k]];
+        double sum = 0.0;
+        for (int64_t j = 0; j < k; ++j)
+            sum += exp((double)l[ids[t * k + j]] - m);
+        for (int64_t j = 0; j < k; ++j)
+            probs[t * k + j] = exp((double)l[ids[t * k + j]] - m) / sum;
+    }
+    free(taken);
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

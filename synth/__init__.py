@@ -173,9 +173,8 @@ def _store(v: np.ndarray, dtype: str, mx_axis: int | None):
     raise ValueError(dtype)
 
 
-def _route(rng: np.random.Generator, T: int, E: int, k: int, routing: str, **kw):
-    """Router draw: expert_ids = top-k of the logits (descending, ties -> lower id);
-    probs = softmax over the k selected logits (fp64), stored as float32."""
+def _logits(rng: np.random.Generator, T: int, E: int, routing: str, **kw) -> np.ndarray:
+    """Router logits [T, E] (float64) of the named distribution."""
     if routing == "normal_logits":
         logits = rng.standard_normal((T, E))
     elif routing == "zipf_gumbel":
@@ -189,6 +188,13 @@ def _route(rng: np.random.Generator, T: int, E: int, k: int, routing: str, **kw)
         logits = logw[None, :] + rng.gumbel(size=(T, E))
     else:
         raise ValueError(routing)
+    return logits
+
+
+def _route(rng: np.random.Generator, T: int, E: int, k: int, routing: str, **kw):
+    """Router draw: expert_ids = top-k of the logits (descending, ties -> lower id);
+    probs = softmax over the k selected logits (fp64), stored as float32."""
+    logits = _logits(rng, T, E, routing, **kw)
     order = np.argsort(-logits, axis=1, kind="stable")[:, :k]
     sel = np.take_along_axis(logits, order, axis=1)
     z = np.exp(sel - sel.max(axis=1, keepdims=True))
@@ -263,6 +269,13 @@ def make_grouped(rows: int, H: int, F: int, E_local: int = 2, sources: int = 8, 
                          recv_counts=counts, w_gate=mats[0], w_up=mats[1], w_down=mats[2],
                          rows_scale=xs, wg_scale=scl[0], wu_scale=scl[1], wd_scale=scl[2],
                          meta=dict(seed=seed, zipf_s=zipf_s))
+
+
+def make_logits(T: int, E: int, routing: str = "normal_logits", seed: int = 0, **routing_kw) -> np.ndarray:
+    """The router logits behind make_layer(T=T, E=E, routing=routing, seed=seed, ...), as float32
+    (the same stream, so top-k of these gives that layer's expert_ids)."""
+    st = _streams(seed, 2 + 3 * E)
+    return _logits(st[0], T, E, routing, **routing_kw).astype(np.float32)
 
 
 def make_workload(name: str, seed: int = 0, **override):
