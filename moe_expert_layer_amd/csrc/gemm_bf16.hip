@@ -320,7 +320,8 @@ constexpr int kSmemBytes = kRingBytes + kWaves * kOutWaveBytes;   // 160 KiB, th
 constexpr int kAPairBytes = 2 * kABytes;               // [256 rows][64 k]
 constexpr int kACopies = kAPairBytes / 1024 / kWaves;  // 1 KiB copies per wave per pair (4)
 constexpr int kBCopies = kBBytes / 1024 / kWaves;      // per wave per K step (2)
-static_assert(kACopies == 4 && kBCopies == 2, "the copy schedule below");
+constexpr int kAHalf = kACopies / 2;                   // A copies per half pair
+static_assert(kACopies % 2 == 0 && kACopies * kWaves * 1024 == kAPairBytes, "whole copies");
 
 template <bool kGated>
 struct BLayout {
@@ -363,7 +364,7 @@ struct CopyCtx {
 // weights of one step and then the first half of a pair's A.
 enum CopySet { kNone = 0, kB = 1, kA2 = 2, kBA1 = 3 };
 template <int CS>
-constexpr int set_size() { return CS == kNone ? 0 : CS == kBA1 ? 4 : 2; }
+constexpr int set_size() { return CS == kNone ? 0 : CS == kBA1 ? kBCopies + kAHalf : CS == kB ? kBCopies : kAHalf; }
 
 // Copy C of copy set CS: weights into B stage SB, A into pair stage QA.
 template <int CS, int SB, int QA, int C>
@@ -371,7 +372,7 @@ __device__ __forceinline__ void copy_one(const CopyCtx& s, const uint32_t (&a_vo
                                          const uint32_t (&b_voff)[kBCopies])
 {
     if constexpr (CS == kA2) {
-        lds_copy16(s.a, a_voff[2 + C], s.a_lds + QA * kAPairBytes + (2 + C) * 1024);
+        lds_copy16(s.a, a_voff[kAHalf + C], s.a_lds + QA * kAPairBytes + (kAHalf + C) * 1024);
     } else if constexpr (C < kBCopies) {
         lds_copy16(s.b, b_voff[C], s.b_lds + SB * kBBytes + C * 1024);
     } else {
@@ -505,19 +506,26 @@ __device__ __forceinline__ void substep(f32x16_t (&acc)[kTM][kTN], const Frags& 
 // pair stage pair p - 2 has just freed).  Copies are issued in a fixed order, so "what step t + 1
 // needs has landed" is "at most N copies are in flight", N counted from that order: 8 at the
 // barrier of an even step, 2 at that of an odd one (fewer near the end of the task).
-constexpr int kWaitEven = 8, kWaitOdd = 2;
+//
+// A wave whose 32 A rows all lie past the tile's last row (a partial tile) copies no A at all: its
+// copies are the weights alone, and the step t + 1 weights have landed once at most the weights of
+// steps t + 2 and t + 3 are in flight, at every barrier.
+template <bool kA>
+constexpr int wait_even() { return kA ? 2 * kBCopies + kACopies : 2 * kBCopies; }
+template <bool kA>
+constexpr int wait_odd() { return kA ? kBCopies : 2 * kBCopies; }
 
 // K step t (t % 4 = S): sub-step 1 of step t on the fragments of sub-step 0, with the second A half
 // of pair t / 2 + 1 when t is even and kCopyA2; the barrier after which step t + 1 has landed (at
 // most W copies in flight; none for W < 0) and step t's stages are free; sub-step 0 of step t + 1
 // on the fragments of sub-step 1, with the weights of step t + 4 (and, t odd, the first A half of
-// pair (t + 3) / 2) when kCopyB.
-template <bool kGated, int NB, int S, bool kCopyA2, bool kCopyB, int W>
+// pair (t + 3) / 2) when kCopyB.  kA = false: the wave copies no A.
+template <bool kGated, int NB, bool kA, int S, bool kCopyA2, bool kCopyB, int W>
 __device__ __forceinline__ void k_step(f32x16_t (&acc)[kTM][kTN], Frags& f0, Frags& f1, CopyCtx& cp,
                                        const LoopArgs& g, int64_t N_w)
 {
-    constexpr int CS1 = S % 2 == 0 && kCopyA2 ? kA2 : kNone;
-    constexpr int CS2 = !kCopyB ? kNone : S % 2 == 0 ? kB : kBA1;
+    constexpr int CS1 = kA && S % 2 == 0 && kCopyA2 ? kA2 : kNone;
+    constexpr int CS2 = !kCopyB ? kNone : S % 2 == 0 || !kA ? kB : kBA1;
     constexpr int Qnext = (S / 2 + 1) % 2;                    // pair stage of pair t / 2 + 1
     substep<kGated, NB, CS1, 0, Qnext, S, 1>(acc, f0, f1, cp, g);
     if constexpr (CS1 == kA2)
@@ -531,31 +539,33 @@ __device__ __forceinline__ void k_step(f32x16_t (&acc)[kTM][kTN], Frags& f0, Fra
 }
 
 // The K loop of one task.  KT is a multiple of kStages (at least kStages); the caller issued A
-// pair 0, the weights of steps 0 .. 3 and the first A half of pair 1, in that order, cp points at
-// pair 1 and at step 4's weights, and the caller has waited for step 0 (step_barrier<kTopWait>).
-// The body is unrolled over the four B stages (two pair stages), so every LDS address is a lane
-// base plus a constant.
-constexpr int kTopWait = 3 * kBCopies + 2;            // weights of steps 1 .. 3, first half of pair 1
+// pair 0, the weights of steps 0 .. 3 and the first A half of pair 1, in that order (kA = false:
+// the weights alone), cp points at pair 1 and at step 4's weights, and the caller has waited for
+// step 0 (step_barrier<top_wait<kA>()>).  The body is unrolled over the four B stages (two pair
+// stages), so every LDS address is a lane base plus a constant.
+template <bool kA>
+constexpr int top_wait() { return kA ? 3 * kBCopies + kAHalf : 3 * kBCopies; }   // steps 1 .. 3 (+ A)
 
-template <bool kGated, int NB>
+template <bool kGated, int NB, bool kA>
 __device__ __forceinline__ void k_loop(f32x16_t (&acc)[kTM][kTN], CopyCtx cp, const LoopArgs& g,
                                        int64_t N_w, int KT)
 {
     static_assert(kStages == 4, "the unrolled body below covers four stages");
+    constexpr int WE = wait_even<kA>(), WO = wait_odd<kA>();
     Frags f0, f1;
     if constexpr (NB > 0)
         reads<kGated, 0, 0, 0, 2 * kTN + NB>(f0, g.a_base, g.b_base);
     for (int kt = 0; kt < KT - kStages; kt += kStages) {
-        k_step<kGated, NB, 0, true, true, kWaitEven>(acc, f0, f1, cp, g, N_w);
-        k_step<kGated, NB, 1, true, true, kWaitOdd>(acc, f0, f1, cp, g, N_w);
-        k_step<kGated, NB, 2, true, true, kWaitEven>(acc, f0, f1, cp, g, N_w);
-        k_step<kGated, NB, 3, true, true, kWaitOdd>(acc, f0, f1, cp, g, N_w);
+        k_step<kGated, NB, kA, 0, true, true, WE>(acc, f0, f1, cp, g, N_w);
+        k_step<kGated, NB, kA, 1, true, true, WO>(acc, f0, f1, cp, g, N_w);
+        k_step<kGated, NB, kA, 2, true, true, WE>(acc, f0, f1, cp, g, N_w);
+        k_step<kGated, NB, kA, 3, true, true, WO>(acc, f0, f1, cp, g, N_w);
     }
     // the last four steps: only the second A half of the last pair is still to be copied
-    k_step<kGated, NB, 0, true, false, kWaitEven>(acc, f0, f1, cp, g, N_w);
-    k_step<kGated, NB, 1, false, false, 0>(acc, f0, f1, cp, g, N_w);
-    k_step<kGated, NB, 2, false, false, 0>(acc, f0, f1, cp, g, N_w);
-    k_step<kGated, NB, 3, false, false, -1>(acc, f0, f1, cp, g, N_w);
+    k_step<kGated, NB, kA, 0, true, false, WE>(acc, f0, f1, cp, g, N_w);
+    k_step<kGated, NB, kA, 1, false, false, 0>(acc, f0, f1, cp, g, N_w);
+    k_step<kGated, NB, kA, 2, false, false, 0>(acc, f0, f1, cp, g, N_w);
+    k_step<kGated, NB, kA, 3, false, false, -1>(acc, f0, f1, cp, g, N_w);
 }
 
 // Epilogue through LDS.  The wave's output (64 rows x 64 columns for fc1, 64 x 128 for fc2) goes
@@ -710,7 +720,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
         const MTile tl = decode_task(t, n_nt, tiles, nt);
 #pragma unroll
         for (int j = 0; j < kACopies; ++j) {
-            const int r = 32 * wave + 8 * j + lane / 8;
+            const int r = 8 * (kACopies * wave + j) + lane / 8;
             gsrc[j] = gather[tl.row_begin + min(r, tl.row_end - tl.row_begin - 1)];   // used in setup
         }
     };
@@ -721,15 +731,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
         const int rows = tile.row_end - tile.row_begin;
 #pragma unroll
         for (int j = 0; j < kACopies; ++j) {
-            const int r = 32 * wave + 8 * j + lane / 8;
+            const int r = 8 * (kACopies * wave + j) + lane / 8;
             const int c = (lane & 7) ^ ((r >> 1) & 7);
             const int src = gather != nullptr ? gsrc[j] / gather_k : min(r, rows - 1);
             a_voff[j] = static_cast<uint32_t>(src) * static_cast<uint32_t>(K) * 2u + 16u * c;
         }
         cp.a = gather != nullptr ? A : A + static_cast<int64_t>(tile.row_begin) * K;
         cp.b = (kGated && wave >= kWaves / 2 ? B1 : B0) + static_cast<int64_t>(tile.expert) * K * N_w + n0;
-        // A pair 0, the weights of steps 0 .. 3, the first half of A pair 1 (k_loop's order)
-        issue_pair<0>(cp, a_voff);
+        // A pair 0, the weights of steps 0 .. 3, the first half of A pair 1 (k_loop's order); a wave
+        // whose A rows all lie past the tile's end copies the weights alone
+        const bool a_on = 32 * wave < rows;
+        if (a_on)
+            issue_pair<0>(cp, a_voff);
         cp.a += 64;
         copies<kB, 0, 0, 0, kBCopies>(cp, a_voff, b_voff);
         cp.b += BK * N_w;
@@ -739,7 +752,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
         cp.b += BK * N_w;
         copies<kB, 3, 0, 0, kBCopies>(cp, a_voff, b_voff);
         cp.b += BK * N_w;
-        copies<kBA1, 0, 1, kBCopies, kBCopies + 2>(cp, a_voff, b_voff);
+        if (a_on)
+            copies<kBA1, 0, 1, kBCopies, kBCopies + kAHalf>(cp, a_voff, b_voff);
     };
 
     int t = claim_task(claimed, task_ctr, xcd, blk, wave, lane);
@@ -756,6 +770,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
         const int rows = tile.row_end - tile.row_begin;
         const int nb = __builtin_amdgcn_readfirstlane(
             min(kTM, max(0, ((rows + 31) / 32 - wm + kWM - 1) / kWM)));
+        // the wave copies A rows 32 wave .. + 31, row block `wave`; row block v is used by wave row
+        // v % kWM, so a wave that copies no A has at most one row block (nb <= 1) and a wave without
+        // row blocks copies no A
+        const int a_on = __builtin_amdgcn_readfirstlane(32 * wave < rows ? 1 : 0);
 
         f32x16_t acc[kTM][kTN];
 #pragma unroll
@@ -768,17 +786,23 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
 
         // step 0 has landed; past this barrier every wave sees the claim of the following task,
         // whose gathered source rows are loaded now and used after this task's K loop
-        step_barrier<kTopWait>();
+        if (a_on)
+            step_barrier<top_wait<true>()>();
+        else
+            step_barrier<top_wait<false>()>();
         const int i = __builtin_amdgcn_readfirstlane(*claimed);
         const int t_next = ((i / blk) * kXcdCount + xcd) * blk + i % blk;
         if (t_next < total)
             fetch_rows(t_next);
         const LoopArgs g{a_base, b_base, a_voff, b_voff};
-        switch (nb) {
-        case 0: k_loop<kGated, 0>(acc, cp, g, N_w, KT); break;
-        case 1: k_loop<kGated, 1>(acc, cp, g, N_w, KT); break;
-        default: k_loop<kGated, 2>(acc, cp, g, N_w, KT); break;
-        }
+        if (nb == 0)
+            k_loop<kGated, 0, false>(acc, cp, g, N_w, KT);
+        else if (nb == 1 && !a_on)
+            k_loop<kGated, 1, false>(acc, cp, g, N_w, KT);
+        else if (nb == 1)
+            k_loop<kGated, 1, true>(acc, cp, g, N_w, KT);
+        else
+            k_loop<kGated, kTM, true>(acc, cp, g, N_w, KT);
         const MTile done = tile;
         const int done_n0 = n0;
         t = t_next;
