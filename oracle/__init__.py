@@ -1,4 +1,4 @@
-"""CPU oracle for the MoE expert-layer forward (ctypes wrapper around ``oracle.c``).
+"""CPU oracle for the MoE expert layer, forward and backward (ctypes wrapper around ``oracle.c``).
 
 TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the CPU-baseline leg of
 the benchmark.  Nothing in the HIP library imports or calls it, and it imports nothing from the HIP
@@ -61,6 +61,12 @@ def _load():
             lib.oracle_forward.restype = I32
             lib.oracle_forward_tokens.argtypes = ([I32] + [I64] * 5 + [P] * 11 + [I64, P])
             lib.oracle_forward_tokens.restype = I32
+            lib.oracle_backward.argtypes = [I32] + [I64] * 5 + [P] * 12
+            lib.oracle_backward.restype = I32
+            lib.oracle_backward_tokens.argtypes = [I32] + [I64] * 5 + [P] * 8 + [I64, P, P]
+            lib.oracle_backward_tokens.restype = I32
+            lib.oracle_wgrad_entries.argtypes = [I32] + [I64] * 5 + [P] * 7 + [I64] + [P] * 6
+            lib.oracle_wgrad_entries.restype = I32
             lib.oracle_mx_quantize.argtypes = [P, I64, P, P]
             lib.oracle_mx_quantize.restype = None
             lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
@@ -259,6 +265,63 @@ def forward_tokens(inp, tokens) -> np.ndarray:
     if rc != 0:
         raise OracleError("oracle_forward_tokens rejected its inputs")
     return out
+
+
+# ---------------------------------------------------------------------------------------------- backward
+
+def _bwd_args(inp, dout):
+    if inp.dtype not in ("f32", "bf16"):
+        raise ValueError("the backward oracle takes float32 or bfloat16 storage")
+    dout = _c(dout)
+    if dout.dtype != inp.x.dtype or dout.shape != (inp.T, inp.H):
+        raise ValueError("dout must be [T, H] in the storage format of x")
+    return (DTYPES[inp.dtype], inp.T, inp.H, inp.F, inp.E, inp.k, _c(inp.x), _c(inp.w_gate),
+            _c(inp.w_up), _c(inp.w_down), _c(inp.expert_ids, np.int32), _c(inp.probs, np.float32),
+            dout)
+
+
+def backward(inp, dout):
+    """Gradients of sum(dout * out) for the layer of ``inp`` (float32 / bfloat16 storage), all fp64:
+    (dx [T,H], dw_gate [E,H,F], dw_up [E,H,F], dw_down [E,F,H], dprobs [T,k])."""
+    a = _bwd_args(inp, dout)
+    _, T, H, F, E, k = a[:6]
+    dx = np.empty((T, H), np.float64)
+    dwg = np.empty((E, H, F), np.float64)
+    dwu = np.empty((E, H, F), np.float64)
+    dwd = np.empty((E, F, H), np.float64)
+    dprobs = np.empty((T, k), np.float64)
+    rc = _load().oracle_backward(*a[:6], *[_p(v) for v in a[6:]], _p(dx), _p(dwg), _p(dwu),
+                                 _p(dwd), _p(dprobs))
+    if rc != 0:
+        raise OracleError("oracle_backward rejected its inputs")
+    return dx, dwg, dwu, dwd, dprobs
+
+
+def backward_tokens(inp, dout, tokens):
+    """(dx rows [n, H], dprobs rows [n, k]) of the listed tokens, fp64."""
+    a = _bwd_args(inp, dout)
+    tokens = _c(tokens, np.int32)
+    n = tokens.shape[0]
+    dx = np.empty((n, inp.H), np.float64)
+    dprobs = np.empty((n, inp.k), np.float64)
+    rc = _load().oracle_backward_tokens(*a[:6], *[_p(v) for v in a[6:]], _p(tokens), n, _p(dx),
+                                        _p(dprobs))
+    if rc != 0:
+        raise OracleError("oracle_backward_tokens rejected its inputs")
+    return dx, dprobs
+
+
+def wgrad_entries(inp, dout, e, f, h):
+    """Entries (dWg[e,h,f], dWu[e,h,f], dWd[e,f,h]) for index arrays e, f, h, fp64."""
+    a = _bwd_args(inp, dout)
+    e, f, h = (_c(np.atleast_1d(v), np.int32) for v in (e, f, h))
+    n = e.shape[0]
+    out = [np.empty(n, np.float64) for _ in range(3)]
+    rc = _load().oracle_wgrad_entries(*a[:6], *[_p(v) for v in a[6:]], n, _p(e), _p(f), _p(h),
+                                      *[_p(o) for o in out])
+    if rc != 0:
+        raise OracleError("oracle_wgrad_entries rejected its inputs")
+    return tuple(out)
 
 
 def inf_norm_rel(a, ref) -> float:

@@ -451,3 +451,266 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* ------------------------------------------------------------------------------------------------
+ * Backward of the layer: the gradients of the scalar L = sum_{t,h} dout[t,h] * out[t,h] with
+ * respect to x, the three weight stacks and the routing probabilities, for given routing.  The
+ * page "NPU Training Operators - MC2" wraps the forward and the backward of each step in its fused
+ * ops, and its 验证项 list the fc1 / fc2 gradients among the checks.  Written from the chain rule
+ * on the forward's definition (steps 6-10), per slot s = t*k + j with expert e = ids[s]:
+ *   g = x_t Wg[e], u = x_t Wu[e], sg = sigmoid(g), a = g sg u, y = a Wd[e]
+ *   dprobs[s]  = <dout_t, y>
+ *   dy         = probs[s] dout_t
+ *   da         = dy Wd[e]^T                      (sum over h)
+ *   dg         = da u sg (1 + g (1 - sg))       (d silu(g) / dg = sg + g sg (1 - sg))
+ *   du         = da g sg
+ *   dx_t      += dg Wg[e]^T + du Wu[e]^T         (sum over f; the k slots of t added in j order)
+ *   dWd[e]    += a^T dy,  dWg[e] += x_t^T dg,  dWu[e] += x_t^T du   (slots in ascending s)
+ * Inputs in storage format (float32 or bfloat16; dout in the same format), widened exactly to
+ * double; every sum is a double sum in ascending index order.  Outputs double:
+ * dx [T, H], dwg / dwu [E, H, F], dwd [E, F, H], dprobs [T, k].  Returns 0, or -1 for a bad id or
+ * an unsupported dtype.
+ * ---------------------------------------------------------------------------------------------- */
+static double sigmoid_d(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+/* Forward and backward quantities of one slot whose weights are decoded (wg, wu [H, F], wd [F, H]):
+ * g, u, a (F), da (F) from x row xr and the scaled output gradient dy (H); y (H). */
+static void slot_chain(int64_t H, int64_t F, const double* xr, const double* dr, double w,
+                       const double* wg, const double* wu, const double* wd, double* g, double* u,
+                       double* a, double* y, double* dy, double* da, double* dprob)
+{
+    for (int64_t f = 0; f < F; ++f) {
+        double gs = 0.0, us = 0.0;
+        for (int64_t h = 0; h < H; ++h) {
+            gs += xr[h] * wg[h * F + f];
+            us += xr[h] * wu[h * F + f];
+        }
+        g[f] = gs;
+        u[f] = us;
+        a[f] = gs * sigmoid_d(gs) * us;
+    }
+    double dp = 0.0;
+    for (int64_t h = 0; h < H; ++h) {
+        double ys = 0.0;
+        for (int64_t f = 0; f < F; ++f)
+            ys += a[f] * wd[f * H + h];
+        y[h] = ys;
+        dp += dr[h] * ys;
+        dy[h] = w * dr[h];
+    }
+    *dprob = dp;
+    for (int64_t f = 0; f < F; ++f) {
+        double s = 0.0;
+        for (int64_t h = 0; h < H; ++h)
+            s += dy[h] * wd[f * H + h];
+        da[f] = s;
+    }
+}
+
+int oracle_backward(int dtype, int64_t T, int64_t H, int64_t F, int64_t E, int64_t k,
+                    const void* x, const void* w_gate, const void* w_up, const void* w_down,
+                    const int32_t* ids, const float* probs, const void* dout, double* dx,
+                    double* dwg, double* dwu, double* dwd, double* dprobs)
+{
+    const int64_t M = T * k;
+    const int64_t esz = dtype == O_F32 ? 4 : 2;
+    double *xd, *dd, *wg, *wu, *wd, *dxp, *g, *u, *a, *y, *dy, *da, *dg, *du;
+    if (dtype != O_F32 && dtype != O_BF16)
+        return -1;
+    for (int64_t s = 0; s < M; ++s)
+        if (ids[s] < 0 || ids[s] >= E)
+            return -1;
+    xd = (double*)malloc(sizeof(double) * (size_t)(T * H + 1));
+    dd = (double*)malloc(sizeof(double) * (size_t)(T * H + 1));
+    wg = (double*)malloc(sizeof(double) * (size_t)(H * F));
+    wu = (double*)malloc(sizeof(double) * (size_t)(H * F));
+    wd = (double*)malloc(sizeof(double) * (size_t)(F * H));
+    dxp = (double*)calloc((size_t)(M * H + 1), sizeof(double));
+    g = (double*)malloc(sizeof(double) * (size_t)F);
+    u = (double*)malloc(sizeof(double) * (size_t)F);
+    a = (double*)malloc(sizeof(double) * (size_t)F);
+    da = (double*)malloc(sizeof(double) * (size_t)F);
+    dg = (double*)malloc(sizeof(double) * (size_t)F);
+    du = (double*)malloc(sizeof(double) * (size_t)F);
+    y = (double*)malloc(sizeof(double) * (size_t)H);
+    dy = (double*)malloc(sizeof(double) * (size_t)H);
+    decode_matrix(dtype, x, NULL, T, H, 0, xd);
+    decode_matrix(dtype, dout, NULL, T, H, 0, dd);
+    for (int64_t e = 0; e < E; ++e) {
+        double* gwg = dwg + e * H * F;
+        double* gwu = dwu + e * H * F;
+        double* gwd = dwd + e * F * H;
+        memset(gwg, 0, sizeof(double) * (size_t)(H * F));
+        memset(gwu, 0, sizeof(double) * (size_t)(H * F));
+        memset(gwd, 0, sizeof(double) * (size_t)(F * H));
+        decode_matrix(dtype, (const char*)w_gate + e * H * F * esz, NULL, H, F, 1, wg);
+        decode_matrix(dtype, (const char*)w_up + e * H * F * esz, NULL, H, F, 1, wu);
+        decode_matrix(dtype, (const char*)w_down + e * F * H * esz, NULL, F, H, 1, wd);
+        for (int64_t s = 0; s < M; ++s) {
+            if (ids[s] != e)
+                continue;
+            const double* xr = xd + (s / k) * H;
+            slot_chain(H, F, xr, dd + (s / k) * H, (double)probs[s], wg, wu, wd, g, u, a, y, dy,
+                       da, &dprobs[s]);
+            for (int64_t f = 0; f < F; ++f) {
+                const double sg = sigmoid_d(g[f]);
+                dg[f] = da[f] * u[f] * sg * (1.0 + g[f] * (1.0 - sg));
+                du[f] = da[f] * g[f] * sg;
+            }
+            for (int64_t h = 0; h < H; ++h) {
+                double acc = 0.0;
+                for (int64_t f = 0; f < F; ++f)
+                    acc += dg[f] * wg[h * F + f] + du[f] * wu[h * F + f];
+                dxp[s * H + h] = acc;
+            }
+            for (int64_t f = 0; f < F; ++f)
+                for (int64_t h = 0; h < H; ++h)
+                    gwd[f * H + h] += a[f] * dy[h];
+            for (int64_t h = 0; h < H; ++h)
+                for (int64_t f = 0; f < F; ++f) {
+                    gwg[h * F + f] += xr[h] * dg[f];
+                    gwu[h * F + f] += xr[h] * du[f];
+                }
+        }
+    }
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < k; ++j)
+                acc += dxp[(t * k + j) * H + h];
+            dx[t * H + h] = acc;
+        }
+    free(xd); free(dd); free(wg); free(wu); free(wd); free(dxp);
+    free(g); free(u); free(a); free(da); free(dg); free(du); free(y); free(dy);
+    return 0;
+}
+
+/* The same gradients for a list of tokens only: dx[tokens[i]] and dprobs[tokens[i], :], computed
+ * per slot exactly as in oracle_backward (used where the whole backward would take too long on a
+ * CPU).  Outputs double dx_rows [ntok, H], dprobs_rows [ntok, k]. */
+int oracle_backward_tokens(int dtype, int64_t T, int64_t H, int64_t F, int64_t E, int64_t k,
+                           const void* x, const void* w_gate, const void* w_up, const void* w_down,
+                           const int32_t* ids, const float* probs, const void* dout,
+                           const int32_t* tokens, int64_t ntok, double* dx_rows,
+                           double* dprobs_rows)
+{
+    const int64_t esz = dtype == O_F32 ? 4 : 2;
+    int rc = 0;
+    int64_t i;
+    if (dtype != O_F32 && dtype != O_BF16)
+        return -1;
+    for (i = 0; i < ntok; ++i) {
+        if (tokens[i] < 0 || tokens[i] >= T)
+            return -1;
+        for (int64_t j = 0; j < k; ++j)
+            if (ids[tokens[i] * k + j] < 0 || ids[tokens[i] * k + j] >= E)
+                return -1;
+    }
+#pragma omp parallel for schedule(dynamic)
+    for (i = 0; i < ntok; ++i) {
+        const int64_t t = tokens[i];
+        double* xr = (double*)malloc(sizeof(double) * (size_t)H);
+        double* dr = (double*)malloc(sizeof(double) * (size_t)H);
+        double* wg = (double*)malloc(sizeof(double) * (size_t)(H * F));
+        double* wu = (double*)malloc(sizeof(double) * (size_t)(H * F));
+        double* wd = (double*)malloc(sizeof(double) * (size_t)(F * H));
+        double* g = (double*)malloc(sizeof(double) * (size_t)F);
+        double* u = (double*)malloc(sizeof(double) * (size_t)F);
+        double* a = (double*)malloc(sizeof(double) * (size_t)F);
+        double* da = (double*)malloc(sizeof(double) * (size_t)F);
+        double* y = (double*)malloc(sizeof(double) * (size_t)H);
+        double* dy = (double*)malloc(sizeof(double) * (size_t)H);
+        double* dxp = (double*)malloc(sizeof(double) * (size_t)(k * H));
+        decode_matrix(dtype, (const char*)x + t * H * esz, NULL, 1, H, 0, xr);
+        decode_matrix(dtype, (const char*)dout + t * H * esz, NULL, 1, H, 0, dr);
+        for (int64_t j = 0; j < k; ++j) {
+            const int64_t s = t * k + j, e = ids[s];
+            decode_matrix(dtype, (const char*)w_gate + e * H * F * esz, NULL, H, F, 1, wg);
+            decode_matrix(dtype, (const char*)w_up + e * H * F * esz, NULL, H, F, 1, wu);
+            decode_matrix(dtype, (const char*)w_down + e * F * H * esz, NULL, F, H, 1, wd);
+            slot_chain(H, F, xr, dr, (double)probs[s], wg, wu, wd, g, u, a, y, dy, da,
+                       &dprobs_rows[i * k + j]);
+            for (int64_t h = 0; h < H; ++h) {
+                double acc = 0.0;
+                for (int64_t f = 0; f < F; ++f) {
+                    const double sg = sigmoid_d(g[f]);
+                    acc += da[f] * u[f] * sg * (1.0 + g[f] * (1.0 - sg)) * wg[h * F + f] +
+                           da[f] * g[f] * sg * wu[h * F + f];
+                }
+                dxp[j * H + h] = acc;
+            }
+        }
+        for (int64_t h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < k; ++j)
+                acc += dxp[j * H + h];
+            dx_rows[i * H + h] = acc;
+        }
+        free(xr); free(dr); free(wg); free(wu); free(wd); free(g); free(u); free(a); free(da);
+        free(y); free(dy); free(dxp);
+    }
+    return rc;
+}
+
+/* Single entries of the weight gradients: for entry i with (e, f, h) = (ent_e[i], ent_f[i],
+ * ent_h[i]), dwg_out[i] = dWg[e][h][f], dwu_out[i] = dWu[e][h][f], dwd_out[i] = dWd[e][f][h], each
+ * the sum over the slots of expert e in ascending s, as in oracle_backward, but with only column f
+ * of g, u and da evaluated per slot. */
+int oracle_wgrad_entries(int dtype, int64_t T, int64_t H, int64_t F, int64_t E, int64_t k,
+                         const void* x, const void* w_gate, const void* w_up, const void* w_down,
+                         const int32_t* ids, const float* probs, const void* dout, int64_t nent,
+                         const int32_t* ent_e, const int32_t* ent_f, const int32_t* ent_h,
+                         double* dwg_out, double* dwu_out, double* dwd_out)
+{
+    const int64_t M = T * k;
+    const int64_t esz = dtype == O_F32 ? 4 : 2;
+    int64_t i;
+    if (dtype != O_F32 && dtype != O_BF16)
+        return -1;
+    for (i = 0; i < nent; ++i)
+        if (ent_e[i] < 0 || ent_e[i] >= E || ent_f[i] < 0 || ent_f[i] >= F || ent_h[i] < 0 ||
+            ent_h[i] >= H)
+            return -1;
+#pragma omp parallel for schedule(dynamic)
+    for (i = 0; i < nent; ++i) {
+        const int64_t e = ent_e[i], f = ent_f[i], hh = ent_h[i];
+        double* wgc = (double*)malloc(sizeof(double) * (size_t)H);   /* column f of Wg[e] */
+        double* wuc = (double*)malloc(sizeof(double) * (size_t)H);
+        double* wdr = (double*)malloc(sizeof(double) * (size_t)H);   /* row f of Wd[e] */
+        double* xr = (double*)malloc(sizeof(double) * (size_t)H);
+        double* dr = (double*)malloc(sizeof(double) * (size_t)H);
+        double sg_acc = 0.0, su_acc = 0.0, sd_acc = 0.0;
+        for (int64_t h = 0; h < H; ++h) {
+            wgc[h] = dtype == O_F32 ? (double)((const float*)w_gate)[(e * H + h) * F + f]
+                                    : oracle_bf16_value(((const uint16_t*)w_gate)[(e * H + h) * F + f]);
+            wuc[h] = dtype == O_F32 ? (double)((const float*)w_up)[(e * H + h) * F + f]
+                                    : oracle_bf16_value(((const uint16_t*)w_up)[(e * H + h) * F + f]);
+            wdr[h] = dtype == O_F32 ? (double)((const float*)w_down)[(e * F + f) * H + h]
+                                    : oracle_bf16_value(((const uint16_t*)w_down)[(e * F + f) * H + h]);
+        }
+        for (int64_t s = 0; s < M; ++s) {
+            if (ids[s] != e)
+                continue;
+            const int64_t t = s / k;
+            double g = 0.0, u = 0.0, da = 0.0;
+            decode_matrix(dtype, (const char*)x + t * H * esz, NULL, 1, H, 0, xr);
+            decode_matrix(dtype, (const char*)dout + t * H * esz, NULL, 1, H, 0, dr);
+            for (int64_t h = 0; h < H; ++h) {
+                g += xr[h] * wgc[h];
+                u += xr[h] * wuc[h];
+            }
+            const double w = (double)probs[s];
+            for (int64_t h = 0; h < H; ++h)
+                da += w * dr[h] * wdr[h];
+            const double sg = sigmoid_d(g);
+            sg_acc += xr[hh] * (da * u * sg * (1.0 + g * (1.0 - sg)));
+            su_acc += xr[hh] * (da * g * sg);
+            sd_acc += (g * sg * u) * (w * dr[hh]);
+        }
+        dwg_out[i] = sg_acc;
+        dwu_out[i] = su_acc;
+        dwd_out[i] = sd_acc;
+        free(wgc); free(wuc); free(wdr); free(xr); free(dr);
+    }
+    return 0;
+}

@@ -31,7 +31,7 @@ import numpy as np
 
 __all__ = [
     "WORKLOADS", "LayerInputs", "GroupedInputs", "make_layer", "make_grouped",
-    "make_workload", "to_bf16_bits", "bf16_bits_to_f32", "mx_encode_blocks",
+    "make_workload", "make_dout", "to_bf16_bits", "bf16_bits_to_f32", "mx_encode_blocks",
 ]
 
 # The five workloads: sizes, dtypes and routing structure (dims are the full sizes).
@@ -269,6 +269,17 @@ def make_grouped(rows: int, H: int, F: int, E_local: int = 2, sources: int = 8, 
                          recv_counts=counts, w_gate=mats[0], w_up=mats[1], w_down=mats[2],
                          rows_scale=xs, wg_scale=scl[0], wu_scale=scl[1], wd_scale=scl[2],
                          meta=dict(seed=seed, zipf_s=zipf_s))
+
+
+def make_dout(inp: LayerInputs, std: float = 1.0) -> np.ndarray:
+    """Output gradient [T, H] for the backward of ``inp``'s layer, in x's storage format (float32 or
+    bfloat16 bits): float32 normals times ``std`` from the stream after the layer's own streams."""
+    if inp.dtype not in ("f32", "bf16"):
+        raise ValueError("the backward takes float32 or bfloat16 storage")
+    seed = inp.meta.get("seed", 0)
+    rng = _streams(seed, 3 + 3 * inp.E)[-1]
+    v, _ = _store(_normal_f32(rng, (inp.T, inp.H), std), inp.dtype, None)
+    return v
 
 
 def make_logits(T: int, E: int, routing: str = "normal_logits", seed: int = 0, **routing_kw) -> np.ndarray:
