@@ -1,6 +1,6 @@
 /*
- * moe_expert_layer.h - C ABI of an MI355X (gfx950) library for the forward pass of a
- * Mixture-of-Experts expert layer on one GPU.
+ * moe_expert_layer.h - C ABI of an MI355X (gfx950) library for the forward and backward passes of
+ * a Mixture-of-Experts expert layer on one GPU.
  *
  * The layer is the expert part of the EP-MC2 forward on the page "NPU Training Operators - MC2",
  * section 执行路径 (execution path): count slots per expert (step 2), permute token rows into
@@ -111,6 +111,38 @@ moe_status moe_expert_forward_mx(const moe_problem* p, const uint8_t* x, const u
                                  const uint8_t* w_down, const uint8_t* wd_scale,
                                  const int32_t* expert_ids, const float* probs, void* out_bf16,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Backward of the layer.
+ * ------------------------------------------------------------------------------------------- */
+
+/* Host only.  Workspace bytes needed by moe_expert_backward for `p`. */
+moe_status moe_backward_workspace_size(const moe_problem* p, size_t* bytes /* host */);
+
+/* Gradients of L = sum_{t,h} dout[t,h] * out[t,h] for moe_expert_forward's layer with the same
+ * inputs and routing.  The page "NPU Training Operators - MC2" wraps forward and backward of each
+ * step of 执行路径 in its fused ops and lists the fc1 / fc2 gradients among its checks (验证项).
+ * Per slot s = t*k + j with expert e = expert_ids[t,j], g = x[t] Wg[e], u = x[t] Wu[e],
+ * sg = sigmoid(g), h = g sg u (silu(g) u):
+ *   dprobs[t,j] = <dout[t], h Wd[e]>
+ *   da          = probs[t,j] * dout[t] Wd[e]^T
+ *   dg          = da u sg (1 + g (1 - sg)),   du = da g sg
+ *   dx[t]       = sum_j (dg Wg[e]^T + du Wu[e]^T), the k slots added in j order
+ *   dw_down[e]  = sum over the slots of expert e of h^T (probs[t,j] dout[t])
+ *   dw_gate[e]  = sum over the slots of expert e of x[t]^T dg,   dw_up[e] likewise with du
+ * dtype MOE_BF16 only; H and F multiples of 128; head_m_size 0; flags ignored.
+ *   x [T,H], w_gate / w_up [E,H,F], w_down [E,F,H] bfloat16; expert_ids [T,k] int32;
+ *   probs [T,k] float32; dout [T,H] bfloat16
+ *   dx [T,H] bfloat16; dw_gate / dw_up [E,H,F], dw_down [E,F,H], dprobs [T,k] float32
+ * g and u are recomputed from x (nothing is kept from a forward call).  g, u, dg, du, probs * h and
+ * each slot's dx row are rounded to bfloat16; every gradient element is one fp32 sum in a fixed
+ * order (no float atomics), so the results are deterministic.  Experts that receive no slot get zero
+ * weight gradients; slots with an out-of-range id are skipped (dprobs 0) and flag the status word. */
+moe_status moe_expert_backward(const moe_problem* p, const void* x, const void* w_gate,
+                               const void* w_up, const void* w_down, const int32_t* expert_ids,
+                               const float* probs, const void* dout, void* dx, float* dw_gate,
+                               float* dw_up, float* dw_down, float* dprobs, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Sub-steps (the same kernels the whole-layer calls use).

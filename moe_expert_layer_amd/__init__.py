@@ -1,4 +1,4 @@
-"""MI355X (gfx950) MoE expert-layer forward: Python binding over the C ABI in
+"""MI355X (gfx950) MoE expert layer, forward and backward: Python binding over the C ABI in
 ``include/moe_expert_layer.h``.
 
 Every step of the layer runs in the HIP library (``libmoe_expert_layer.so``, built in-tree by
@@ -16,7 +16,8 @@ import torch
 
 __all__ = [
     "MoeError", "library", "lib_path", "F32", "BF16", "MXFP8",
-    "workspace_size", "expert_forward", "expert_forward_mx", "route", "permute", "unpermute",
+    "workspace_size", "expert_forward", "expert_forward_mx", "backward_workspace_size",
+    "expert_backward", "route", "permute", "unpermute",
     "grouped_ffn", "grouped_ffn_mx", "mx_quantize", "device_status", "chunk_counters",
     "intermediate_h",
     "timing_enable", "timing_collect", "timing_reset",
@@ -50,6 +51,8 @@ _SIGS = {
     "moe_workspace_size": [ctypes.POINTER(MoeProblem), ctypes.POINTER(ctypes.c_size_t)],
     "moe_expert_forward": [ctypes.POINTER(MoeProblem)] + [_P] * 8 + [ctypes.c_size_t, _P],
     "moe_expert_forward_mx": [ctypes.POINTER(MoeProblem)] + [_P] * 12 + [ctypes.c_size_t, _P],
+    "moe_backward_workspace_size": [ctypes.POINTER(MoeProblem), ctypes.POINTER(ctypes.c_size_t)],
+    "moe_expert_backward": [ctypes.POINTER(MoeProblem)] + [_P] * 13 + [ctypes.c_size_t, _P],
     "moe_route_workspace_size": [_I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
     "moe_route": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_permute": [ctypes.POINTER(MoeProblem), _P, _P, _P, _P, _P, _P],
@@ -180,6 +183,41 @@ def expert_forward(x, w_gate, w_up, w_down, expert_ids, probs, head_m_size: int 
                                         _ptr(w_down), _ptr(expert_ids), _ptr(probs), _ptr(out),
                                         _ptr(ws), ws.numel(), _stream(x)))
     return out
+
+
+def backward_workspace_size(prob: MoeProblem) -> int:
+    n = ctypes.c_size_t()
+    _check(library().moe_backward_workspace_size(ctypes.byref(prob), ctypes.byref(n)))
+    return n.value
+
+
+def expert_backward(x, w_gate, w_up, w_down, expert_ids, probs, dout, workspace=None):
+    """Gradients of sum(dout * out) for expert_forward's bfloat16 layer:
+    (dx bf16 [T,H], dw_gate f32 [E,H,F], dw_up f32 [E,H,F], dw_down f32 [E,F,H], dprobs f32 [T,k])."""
+    T, H = x.shape
+    E, _, F = w_gate.shape
+    k = expert_ids.shape[1]
+    dev = x.device
+    bf = torch.bfloat16
+    _need(x, "x", bf, (T, H))
+    _need(w_gate, "w_gate", bf, (E, H, F), dev)
+    _need(w_up, "w_up", bf, (E, H, F), dev)
+    _need(w_down, "w_down", bf, (E, F, H), dev)
+    _need(expert_ids, "expert_ids", torch.int32, (T, k), dev)
+    _need(probs, "probs", torch.float32, (T, k), dev)
+    _need(dout, "dout", bf, (T, H), dev)
+    prob = problem(T, H, F, E, k, BF16)
+    ws = _workspace(backward_workspace_size(prob), dev, workspace)
+    dx = torch.empty((T, H), dtype=bf, device=dev)
+    dwg = torch.empty((E, H, F), dtype=torch.float32, device=dev)
+    dwu = torch.empty((E, H, F), dtype=torch.float32, device=dev)
+    dwd = torch.empty((E, F, H), dtype=torch.float32, device=dev)
+    dprobs = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _check(library().moe_expert_backward(ctypes.byref(prob), _ptr(x), _ptr(w_gate), _ptr(w_up),
+                                         _ptr(w_down), _ptr(expert_ids), _ptr(probs), _ptr(dout),
+                                         _ptr(dx), _ptr(dwg), _ptr(dwu), _ptr(dwd), _ptr(dprobs),
+                                         _ptr(ws), ws.numel(), _stream(x)))
+    return dx, dwg, dwu, dwd, dprobs
 
 
 def expert_forward_mx(x, x_scale, w_gate, wg_scale, w_up, wu_scale, w_down, wd_scale, expert_ids,

@@ -17,7 +17,7 @@ LIB_NAME = "libmoe_expert_layer.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm_f32.hip", "gemm_bf16.hip", "gemm_mx.hip",
-           "router.hip"]
+           "router.hip", "gemm_bwd.hip"]
 HEADERS = ["common.h", "internal.h", "gemm_common.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

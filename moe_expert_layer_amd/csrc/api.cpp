@@ -473,6 +473,161 @@ MOE_API moe_status moe_expert_forward_mx(const moe_problem* p, const uint8_t* x,
                           expert_ids, probs, out_bf16, workspace, workspace_bytes, stream);
 }
 
+// ------------------------------------------------------------------------------------- backward
+
+namespace moe {
+namespace {
+
+struct BackwardLayout {
+    RouteLayout route;
+    size_t counts = 0, offsets = 0, perm = 0, pos = 0, tile_count = 0, task_ctr = 0;
+    size_t tiles_r = 0, tiles_d = 0, prow = 0, partial = 0;
+    size_t x_perm = 0, dout_perm = 0, g = 0, u = 0, dgu = 0, hp = 0, dx_perm = 0, total = 0;
+    int64_t max_tiles_r = 0, max_tiles_d = 0;
+    int bm_r = 0;
+};
+
+// g and u are recomputed with the plain grouped GEMM (K = H, N = F), whose row tiles are bm_r
+// high; the backward's own GEMMs use 128-row tiles.
+BackwardLayout backward_layout(int64_t T, int64_t H, int64_t F, int64_t E, int64_t k)
+{
+    const int64_t M = T * k;
+    BackwardLayout L;
+    L.route = route_layout(T, k, E, 0);
+    size_t off = L.route.total;
+    auto take = [&off](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    };
+    const auto n = [](int64_t v) { return static_cast<size_t>(v); };
+    L.counts = take(4 * n(E));
+    L.offsets = take(4 * n(E + 1));
+    L.perm = take(4 * n(M));
+    L.pos = take(4 * n(M));
+    L.tile_count = take(4 * sizeof(int32_t));
+    L.task_ctr = take(2 * kXcdCount * sizeof(int32_t));
+    L.bm_r = bf16_row_tile(F, H);
+    L.max_tiles_r = max_mtiles(M, E, 0, L.bm_r);
+    L.max_tiles_d = max_mtiles(M, E, 0, kBmBwd);
+    L.tiles_r = take(sizeof(MTile) * n(L.max_tiles_r));
+    L.tiles_d = L.bm_r == kBmBwd ? L.tiles_r : take(sizeof(MTile) * n(L.max_tiles_d));
+    L.prow = take(4 * n(M));
+    L.partial = take(4 * n(M) * n(F / 64));
+    L.x_perm = take(2 * n(M) * n(H));
+    L.dout_perm = take(2 * n(M) * n(H));
+    L.g = take(2 * n(M) * n(F));
+    L.u = take(2 * n(M) * n(F));
+    L.dgu = take(4 * n(M) * n(F));
+    L.hp = take(2 * n(M) * n(F));
+    L.dx_perm = take(2 * n(M) * n(H));
+    L.total = off;
+    return L;
+}
+
+moe_status check_backward(const moe_problem* p)
+{
+    if (moe_status st = check_problem(p, true); st != MOE_OK)
+        return st;
+    if (p->dtype != MOE_BF16)
+        return fail(MOE_ERR_UNSUPPORTED, "the backward takes bfloat16 (dtype MOE_BF16) only");
+    if (p->head_m_size != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "the backward is unchunked (head_m_size must be 0)");
+    if (!bwd_supported(p->H, p->F) || !bf16_supported(p->F, p->H))
+        return fail(MOE_ERR_UNSUPPORTED, "the backward needs H and F multiples of 128");
+    if (p->T * p->k * 2 * p->F > INT32_MAX)
+        return fail(MOE_ERR_UNSUPPORTED, "the backward needs T * k * 2F < 2^31");
+    return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+MOE_API moe_status moe_backward_workspace_size(const moe_problem* p, size_t* bytes)
+{
+    if (bytes == nullptr)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "bytes is null");
+    if (moe_status st = check_backward(p); st != MOE_OK)
+        return st;
+    *bytes = backward_layout(p->T, p->H, p->F, p->E, p->k).total;
+    return MOE_OK;
+}
+
+MOE_API moe_status moe_expert_backward(const moe_problem* p, const void* x, const void* w_gate,
+                                       const void* w_up, const void* w_down,
+                                       const int32_t* expert_ids, const float* probs,
+                                       const void* dout, void* dx, float* dw_gate, float* dw_up,
+                                       float* dw_down, float* dprobs, void* ws, size_t ws_bytes,
+                                       hipStream_t s)
+{
+    if (moe_status st = check_backward(p); st != MOE_OK)
+        return st;
+    const int64_t T = p->T, H = p->H, F = p->F, E = p->E, k = p->k, M = T * k;
+    const BackwardLayout L = backward_layout(T, H, F, E, k);
+    if (ws == nullptr || ws_bytes < L.total)
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", L.total,
+                    ws == nullptr ? size_t{0} : ws_bytes);
+    if (w_gate == nullptr || w_up == nullptr || w_down == nullptr || dw_gate == nullptr ||
+        dw_up == nullptr || dw_down == nullptr)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "null weight or weight-gradient pointer");
+    if (T > 0 && (x == nullptr || expert_ids == nullptr || probs == nullptr || dout == nullptr ||
+                  dx == nullptr || dprobs == nullptr))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "null data pointer");
+    int32_t* counts = at<int32_t>(ws, L.counts);
+    int32_t* offsets = at<int32_t>(ws, L.offsets);
+    int32_t* perm = at<int32_t>(ws, L.perm);
+    int32_t* pos = at<int32_t>(ws, L.pos);
+    if (moe_status st = run_route(expert_ids, T, k, E, counts, offsets, perm, pos, ws, L.route, s);
+        st != MOE_OK)
+        return st;
+    const auto* wg = static_cast<const uint16_t*>(w_gate);
+    const auto* wu = static_cast<const uint16_t*>(w_up);
+    const auto* wd = static_cast<const uint16_t*>(w_down);
+    uint16_t* x_perm = at<uint16_t>(ws, L.x_perm);
+    uint16_t* dout_perm = at<uint16_t>(ws, L.dout_perm);
+    uint16_t* dgu = at<uint16_t>(ws, L.dgu);
+    uint16_t* hp = at<uint16_t>(ws, L.hp);
+    if (M > 0) {
+        int32_t* status = at<int32_t>(ws, L.route.status);
+        int32_t* tcount = at<int32_t>(ws, L.tile_count);
+        int32_t* task_ctr = at<int32_t>(ws, L.task_ctr);
+        MTile* tiles_r = at<MTile>(ws, L.tiles_r);
+        MTile* tiles_d = at<MTile>(ws, L.tiles_d);
+        uint16_t* g = at<uint16_t>(ws, L.g);
+        uint16_t* u = at<uint16_t>(ws, L.u);
+        uint16_t* dx_perm = at<uint16_t>(ws, L.dx_perm);
+        float* prow = at<float>(ws, L.prow);
+        float* partial = at<float>(ws, L.partial);
+        LAUNCH(s, "permute", launch_permute(x, pos, x_perm, T, k, M, H * 2, s));
+        LAUNCH(s, "permute", launch_permute(dout, pos, dout_perm, T, k, M, H * 2, s));
+        LAUNCH(s, "build_tiles",
+               launch_build_tiles(offsets, nullptr, E, E, M, M, L.bm_r, tiles_r, L.max_tiles_r,
+                                  tcount, nullptr, nullptr, 1, 0, task_ctr, status, false, s));
+        if (L.tiles_d != L.tiles_r)
+            LAUNCH(s, "build_tiles",
+                   launch_build_tiles(offsets, nullptr, E, E, M, M, kBmBwd, tiles_d, L.max_tiles_d,
+                                      tcount + 1, nullptr, nullptr, 1, 0, nullptr, status, false, s));
+        const int32_t* tcount_d = L.tiles_d != L.tiles_r ? tcount + 1 : tcount;
+        // g = x_perm Wg[e], u = x_perm Wu[e]: the plain grouped GEMM with K = H and N = F
+        LAUNCH(s, "recompute_g", launch_fc2_bf16(x_perm, wg, g, tiles_r, tcount, F, H, nullptr, task_ctr, s));
+        LAUNCH(s, "recompute_u",
+               launch_fc2_bf16(x_perm, wu, u, tiles_r, tcount, F, H, nullptr, task_ctr + kXcdCount, s));
+        LAUNCH(s, "row_probs", launch_row_probs(perm, probs, prow, M, s));
+        LAUNCH(s, "dgrad_down",
+               launch_dgrad_down(dout_perm, wd, g, u, prow, dgu, hp, partial, tiles_d, tcount_d,
+                                 L.max_tiles_d, H, F, s));
+        LAUNCH(s, "dprobs", launch_dprobs(partial, pos, dprobs, M, F, s));
+        LAUNCH(s, "dgrad_gate_up",
+               launch_dgrad_gate_up(dgu, wg, wu, dx_perm, tiles_d, tcount_d, L.max_tiles_d, H, F, s));
+        LAUNCH(s, "unpermute", launch_unpermute(1, dx_perm, pos, nullptr, dx, T, k, M, H, s));
+    }
+    // weight gradients (an expert without rows gets zeros)
+    LAUNCH(s, "wgrad_down", launch_wgrad(hp, F, dout_perm, H, offsets, E, F, H, dw_down, s));
+    LAUNCH(s, "wgrad_gate", launch_wgrad(x_perm, H, dgu, 2 * F, offsets, E, H, F, dw_gate, s));
+    LAUNCH(s, "wgrad_up", launch_wgrad(x_perm, H, dgu + F, 2 * F, offsets, E, H, F, dw_up, s));
+    return MOE_OK;
+}
+
 MOE_API moe_status moe_route_workspace_size(int64_t T, int64_t k, int64_t E, size_t* bytes)
 {
     if (bytes == nullptr || T < 0 || k <= 0 || E <= 0 || k > E)

@@ -1,0 +1,488 @@
+// Grouped GEMMs of the expert layer's backward on gfx950 MFMA (bf16 operands, fp32 accumulation
+// on v_mfma_f32_32x32x16_bf16).  The page "NPU Training Operators - MC2" wraps forward and backward
+// of every step of 执行路径 in its fused ops; its 验证项 list the fc1 / fc2 gradients among the
+// checks.  With the permuted rows p (expert e(p)), the forward's g = x Wg, u = x Wu and the routing
+// probability w(p) of the slot behind row p:
+//
+//   down dgrad (N = F):  d[p, f] = sum_h dout_perm[p, h] Wd[e][f, h]          (dout Wd^T)
+//       epilogue: sg = sigmoid(g), h = g sg u, dh = w d,
+//                 dg = dh u sg (1 + g (1 - sg)), du = dh g sg   -> dgu [M, 2F] = [dg | du]
+//                 hp = w h                                      -> hp [M, F]
+//                 sum over the wave's 64 columns of h d          -> dprobs partial [M, F / 64]
+//   gate/up dgrad (N = H): dx_perm[p, h] = sum_f dg[p, f] Wg[e][h, f] + du[p, f] Wu[e][h, f]
+//   weight gradients (per expert, K = the expert's rows, in ascending p):
+//       dWd[e][f, h] = sum_p hp[p, f] dout_perm[p, h]
+//       dWg[e][h, f] = sum_p x_perm[p, h] dg[p, f],   dWu likewise with du
+//
+// Tiles of 128 x 128 outputs, 4 waves of 64 x 64 (2 x 2 MFMA blocks of 32 x 32), K steps of 64,
+// two LDS stages filled through registers, two workgroups per CU.  In LDS both operands are
+// K-contiguous rows of 64 values with XOR-swizzled 16-byte chunks, read as 16-byte fragments.
+//   - dgrad: both operands are K-contiguous in memory (activation rows; weight rows of Wd[e] as
+//     [F][H], of Wg[e] / Wu[e] as [H][F]) and are copied as they are;
+//   - weight gradients: both operands are rows over K (activations [M][cols]); each thread loads 4
+//     consecutive rows of 8 columns and transposes them in registers (v_perm_b32) into 8 columns of
+//     4 consecutive k; rows past the expert's last row load as zero.
+// Every output element sums its whole contraction in one workgroup in a fixed order, so results
+// are deterministic.  Tasks: dgrad over (row tile, column tile) of the row-tile table, weight
+// gradients over (expert, column tile of the gradient's rows, column tile of its columns) in groups
+// of 8 row tiles; consecutive tasks go to one XCD (workgroup b runs on XCD b % 8), so the
+// workgroups of an XCD share operand strips in its L2.
+#include "common.h"
+#include "gemm_common.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWM = 2, kWN = 2, kTM = 2, kTN = 2;
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int kTileBytes = BM * BK * 2;        // one operand, one stage: 16 KiB
+constexpr int kStageBytes = 2 * kTileBytes;
+constexpr int kSmemBytes = 2 * kStageBytes;    // 64 KiB
+
+enum Epi { kEpiDown = 0, kEpiGateUp = 1, kEpiWgrad = 2 };
+
+// Byte offset of element (row, k) in a [128 rows][64 k] bf16 tile, 16-byte chunks XOR-swizzled by row.
+__device__ __forceinline__ int tile_off(int row, int k)
+{
+    return row * 128 + ((((k >> 3) ^ row) & 7) << 4) + ((k & 7) << 1);
+}
+
+__device__ __forceinline__ float sigmoid_f(float z)
+{
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+}
+
+struct BwdArgs {
+    // A: dgrad, K-contiguous rows (row stride lda); weight gradients, rows over K (stride lda)
+    const uint16_t* a;
+    int64_t lda;
+    // B: dgrad, weight rows of expert e at b0 + e * b_estride + n * ldb (k < kseg) and
+    // b1 + e * b_estride + n * ldb (k >= kseg); weight gradients, rows over K at b0 (stride ldb)
+    const uint16_t* b0;
+    const uint16_t* b1;
+    int64_t ldb;
+    int64_t b_estride;
+    int kseg;
+    int K;                        // dgrad contraction length
+    int N;                        // output columns
+    int Mo;                       // weight gradients: output rows
+    const MTile* tiles;           // dgrad row tiles (128 rows)
+    const int32_t* tile_count;
+    const int32_t* offsets;       // weight gradients: expert e owns rows [offsets[e], offsets[e+1])
+    int E;
+    void* c;                      // dgu (down dgrad), dx_perm (gate/up dgrad), dW (fp32)
+    const uint16_t* g;            // down dgrad: recomputed g, u [M, F]; row weights w(p)
+    const uint16_t* u;
+    const float* prow;
+    uint16_t* hp;                 // down dgrad: w h [M, F]
+    float* partial;               // down dgrad: [M, F / 64]
+};
+
+// Register staging of one K step.  K-contiguous operand: 4 chunks of 16 bytes, rows tid / 8 + 32 i,
+// k chunk tid % 8.  Rows over K: 4 rows (4 (tid % 16) + r) of the 8 columns 8 (tid / 16) ...
+struct Stage {
+    u32x4_t a[4];
+    u32x4_t b[4];
+};
+
+template <int kEpi>
+struct Src {
+    // dgrad: per chunk row pointers (k = 0 of segment 0 and of segment 1)
+    const uint16_t* a_row[4];
+    const uint16_t* b_row0[4];
+    const uint16_t* b_row1[4];
+    // weight gradients: column chunk pointers at the expert's first row, rows available
+    const uint16_t* a_col;
+    const uint16_t* b_col;
+    int kend;
+};
+
+template <int kEpi>
+__device__ __forceinline__ void load_step(Stage& st, const Src<kEpi>& s, const BwdArgs& g, int k0,
+                                          int tid)
+{
+    if constexpr (kEpi != kEpiWgrad) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            st.a[i] = *reinterpret_cast<const u32x4_t*>(s.a_row[i] + k0);
+            const uint16_t* bp = k0 < g.kseg ? s.b_row0[i] + k0 : s.b_row1[i] + (k0 - g.kseg);
+            st.b[i] = *reinterpret_cast<const u32x4_t*>(bp);
+        }
+    } else {
+        const int kk = k0 + 4 * (tid % 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const bool ok = kk + r < s.kend;
+            const u32x4_t z = {0u, 0u, 0u, 0u};
+            st.a[r] = ok ? *reinterpret_cast<const u32x4_t*>(s.a_col + static_cast<int64_t>(kk + r) * g.lda) : z;
+            st.b[r] = ok ? *reinterpret_cast<const u32x4_t*>(s.b_col + static_cast<int64_t>(kk + r) * g.ldb) : z;
+        }
+    }
+}
+
+// 4 rows x 8 columns (r[row] holds the row's 8 values) -> 8 columns of 4 consecutive k
+__device__ __forceinline__ void store_transposed(unsigned char* T, const u32x4_t (&r)[4], int c0, int k0)
+{
+#pragma unroll
+    for (int col = 0; col < 8; ++col) {
+        const int d = col >> 1;
+        const uint32_t sel = (col & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t w0 = __builtin_amdgcn_perm(r[1][d], r[0][d], sel);
+        const uint32_t w1 = __builtin_amdgcn_perm(r[3][d], r[2][d], sel);
+        *reinterpret_cast<u32x2_t*>(T + tile_off(c0 + col, k0)) = u32x2_t{w0, w1};
+    }
+}
+
+template <int kEpi>
+__device__ __forceinline__ void store_step(unsigned char* smem, int buf, const Stage& st, int tid)
+{
+    unsigned char* As = smem + buf * kStageBytes;
+    unsigned char* Bs = As + kTileBytes;
+    if constexpr (kEpi != kEpiWgrad) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int off = tile_off(tid / 8 + 32 * i, 8 * (tid % 8));
+            *reinterpret_cast<u32x4_t*>(As + off) = st.a[i];
+            *reinterpret_cast<u32x4_t*>(Bs + off) = st.b[i];
+        }
+    } else {
+        store_transposed(As, st.a, 8 * (tid / 16), 4 * (tid % 16));
+        store_transposed(Bs, st.b, 8 * (tid / 16), 4 * (tid % 16));
+    }
+}
+
+__device__ __forceinline__ void load_frags(bf16x8_t (&af)[kTM], bf16x8_t (&bf)[kTN],
+                                           const unsigned char* As, const unsigned char* Bs, int wm,
+                                           int wn, int lane, int ks)
+{
+    const int kk = ks * 16 + 8 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(As + tile_off(32 * (kWM * i + wm) + (lane & 31), kk));
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+        bf[j] = *reinterpret_cast<const bf16x8_t*>(Bs + tile_off(64 * wn + 32 * j + (lane & 31), kk));
+}
+
+__device__ __forceinline__ void mfmas(f32x16_t (&acc)[kTM][kTN], const bf16x8_t (&af)[kTM],
+                                      const bf16x8_t (&bf)[kTN])
+{
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+}
+
+// The K loop: KT steps of 64; the global loads of step kt + 1 and the fragment reads of sub-step
+// ks + 1 are in flight while the MFMAs of kt / ks run.
+template <int kEpi>
+__device__ __forceinline__ void k_loop(f32x16_t (&acc)[kTM][kTN], unsigned char* smem,
+                                       const Src<kEpi>& s, const BwdArgs& g, int KT, int tid,
+                                       int wm, int wn, int lane)
+{
+    if (KT <= 0)
+        return;
+    Stage st;
+    load_step<kEpi>(st, s, g, 0, tid);
+    store_step<kEpi>(smem, 0, st, tid);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < KT)
+            load_step<kEpi>(st, s, g, (kt + 1) * BK, tid);
+        const unsigned char* As = smem + cur * kStageBytes;
+        const unsigned char* Bs = As + kTileBytes;
+        bf16x8_t af[2][kTM], bf[2][kTN];
+        load_frags(af[0], bf[0], As, Bs, wm, wn, lane, 0);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ks += 2) {
+            load_frags(af[1], bf[1], As, Bs, wm, wn, lane, ks + 1);
+            mfmas(acc, af[0], bf[0]);
+            if (ks + 2 < BK / 16)
+                load_frags(af[0], bf[0], As, Bs, wm, wn, lane, ks + 2);
+            mfmas(acc, af[1], bf[1]);
+        }
+        if (kt + 1 < KT)
+            store_step<kEpi>(smem, cur ^ 1, st, tid);
+        __syncthreads();
+    }
+}
+
+// Task t of this workgroup (consecutive tasks on one XCD), or -1.
+__device__ __forceinline__ int task_of_block(int total)
+{
+    const int per = (total + kXcdCount - 1) / kXcdCount;
+    const int b = blockIdx.x;
+    const int local = b / kXcdCount;
+    const int t = (b % kXcdCount) * per + local;
+    return local < per && t < total ? t : -1;
+}
+
+template <int kEpi>
+__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_bwd(BwdArgs g)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / kWN;
+    const int wn = wave % kWN;
+    const int n_nt = g.N / BN;
+
+    Src<kEpi> s{};
+    MTile tile{};
+    int n0 = 0, m0 = 0, e = 0, KT = 0;
+    if constexpr (kEpi != kEpiWgrad) {
+        const int total = *g.tile_count * n_nt;
+        const int t = task_of_block(total);
+        if (t < 0)
+            return;
+        int nt;
+        tile = decode_task(t, n_nt, g.tiles, nt);
+        n0 = nt * BN;
+        e = tile.expert;
+        KT = g.K / BK;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = tid / 8 + 32 * i;
+            const int row = min(tile.row_begin + r, tile.row_end - 1);   // rows past the end: never stored
+            const int c = 8 * (tid % 8);
+            s.a_row[i] = g.a + static_cast<int64_t>(row) * g.lda + c;
+            const int64_t boff = static_cast<int64_t>(e) * g.b_estride + static_cast<int64_t>(n0 + r) * g.ldb + c;
+            s.b_row0[i] = g.b0 + boff;
+            s.b_row1[i] = g.b1 + boff;
+        }
+    } else {
+        const int n_mt = g.Mo / BM;
+        const int per_e = n_mt * n_nt;
+        const int t = task_of_block(per_e * g.E);
+        if (t < 0)
+            return;
+        e = t / per_e;
+        const int tl = t - e * per_e;
+        constexpr int kGroup = 8;                                   // row tiles per group
+        const int grp = tl / (kGroup * n_nt);
+        const int first = grp * kGroup;
+        const int gsz = min(kGroup, n_mt - first);
+        const int idx = tl - grp * kGroup * n_nt;
+        m0 = (first + idx % gsz) * BM;
+        n0 = (idx / gsz) * BN;
+        const int k_begin = g.offsets[e];
+        s.kend = g.offsets[e + 1] - k_begin;
+        KT = (s.kend + BK - 1) / BK;
+        const int c = 8 * (tid / 16);
+        s.a_col = g.a + static_cast<int64_t>(k_begin) * g.lda + m0 + c;
+        s.b_col = g.b0 + static_cast<int64_t>(k_begin) * g.ldb + n0 + c;
+    }
+
+    f32x16_t acc[kTM][kTN];
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[i][j][r] = 0.0f;
+    k_loop<kEpi>(acc, smem, s, g, KT, tid, wm, wn, lane);
+
+    // Lane holds column lane % 32 of each 32 x 32 block, rows 8 (r / 4) + 4 (lane / 32) + r % 4.
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int lrow = 32 * (kWM * i + wm) + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if constexpr (kEpi == kEpiWgrad) {
+                float* C = static_cast<float*>(g.c) + (static_cast<int64_t>(e) * g.Mo + m0 + lrow) * g.N;
+#pragma unroll
+                for (int j = 0; j < kTN; ++j)
+                    C[n0 + 64 * wn + 32 * j + (lane & 31)] = acc[i][j][r];
+            } else if constexpr (kEpi == kEpiGateUp) {
+                const int p = tile.row_begin + lrow;
+                if (p < tile.row_end) {
+                    uint16_t* C = static_cast<uint16_t*>(g.c) + static_cast<int64_t>(p) * g.N;
+#pragma unroll
+                    for (int j = 0; j < kTN; ++j)
+                        C[n0 + 64 * wn + 32 * j + (lane & 31)] = f32_to_bf16(acc[i][j][r]);
+                }
+            } else {
+                const int p = tile.row_begin + lrow;
+                const bool live = p < tile.row_end;
+                const int F = g.N;
+                float part = 0.0f;
+                if (live) {
+                    const float w = g.prow[p];
+                    const int64_t rowF = static_cast<int64_t>(p) * F;
+                    uint16_t* dgu = static_cast<uint16_t*>(g.c) + 2 * rowF;
+#pragma unroll
+                    for (int j = 0; j < kTN; ++j) {
+                        const int f = n0 + 64 * wn + 32 * j + (lane & 31);
+                        const float gv = bf16_to_f32(g.g[rowF + f]);
+                        const float uv = bf16_to_f32(g.u[rowF + f]);
+                        const float d = acc[i][j][r];
+                        const float sg = sigmoid_f(gv);
+                        const float hv = gv * sg * uv;
+                        part += hv * d;
+                        const float dh = w * d;
+                        dgu[f] = f32_to_bf16(dh * uv * sg * (1.0f + gv * (1.0f - sg)));
+                        dgu[F + f] = f32_to_bf16(dh * gv * sg);
+                        g.hp[rowF + f] = f32_to_bf16(w * hv);
+                    }
+                }
+                // sum over the 32 lanes that share this row (every lane takes part)
+#pragma unroll
+                for (int off = 16; off >= 1; off >>= 1)
+                    part += __shfl_xor(part, off);
+                if (live && (lane & 31) == 0)
+                    g.partial[static_cast<int64_t>(p) * (F / 64) + n0 / 64 + wn] = part;
+            }
+        }
+    }
+}
+
+constexpr int kSmallThreads = 256;
+
+// w(p) = probs of the slot behind permuted row p (0 for rows past the valid ones).
+__global__ __launch_bounds__(kSmallThreads) void row_probs_kernel(const int32_t* __restrict__ perm,
+                                                                  const float* __restrict__ probs,
+                                                                  float* __restrict__ prow, int64_t M)
+{
+    const int64_t p = static_cast<int64_t>(blockIdx.x) * kSmallThreads + threadIdx.x;
+    if (p < M) {
+        const int32_t slot = perm[p];          // -1 past the valid rows (out-of-range ids)
+        prow[p] = slot >= 0 ? probs[slot] : 0.0f;
+    }
+}
+
+// dprobs[s] = sum over q ascending of partial[pos[s]][q] (0 for a slot with pos < 0).
+__global__ __launch_bounds__(kSmallThreads) void dprobs_kernel(const float* __restrict__ partial,
+                                                               const int32_t* __restrict__ pos,
+                                                               float* __restrict__ dprobs, int64_t M, int nq)
+{
+    const int64_t s = static_cast<int64_t>(blockIdx.x) * kSmallThreads + threadIdx.x;
+    if (s >= M)
+        return;
+    const int32_t p = pos[s];
+    if (p < 0 || p >= M) {                     // slot with an out-of-range id: skipped
+        dprobs[s] = 0.0f;
+        return;
+    }
+    const float* row = partial + static_cast<int64_t>(p) * nq;
+    float acc = 0.0f;
+    for (int q = 0; q < nq; ++q)
+        acc += row[q];
+    dprobs[s] = acc;
+}
+
+template <int kEpi>
+hipError_t launch_bwd(const BwdArgs& a, int64_t total_bound, hipStream_t s)
+{
+    static bool done[64] = {};
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess)
+        return e;
+    if (dev >= 64 || !done[dev]) {
+        if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_bwd<kEpi>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
+            e != hipSuccess)
+            return e;
+        if (dev < 64)
+            done[dev] = true;
+    }
+    if (total_bound <= 0)
+        return hipSuccess;
+    const int64_t blocks = (total_bound + kXcdCount - 1) / kXcdCount * kXcdCount;
+    if (blocks >= (int64_t{1} << 31))
+        return hipErrorInvalidValue;
+    grouped_gemm_bwd<kEpi><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), kSmemBytes, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool bwd_supported(int64_t H, int64_t F) { return H % BN == 0 && F % BN == 0; }
+
+hipError_t launch_row_probs(const int32_t* perm, const float* probs, float* prow, int64_t M, hipStream_t s)
+{
+    if (M <= 0)
+        return hipSuccess;
+    row_probs_kernel<<<dim3(static_cast<unsigned>((M + kSmallThreads - 1) / kSmallThreads)),
+                       dim3(kSmallThreads), 0, s>>>(perm, probs, prow, M);
+    return hipGetLastError();
+}
+
+hipError_t launch_dgrad_down(const uint16_t* dout_perm, const uint16_t* wd, const uint16_t* g,
+                             const uint16_t* u, const float* prow, uint16_t* dgu, uint16_t* hp,
+                             float* partial, const MTile* tiles, const int32_t* tile_count,
+                             int64_t max_tiles, int64_t H, int64_t F, hipStream_t s)
+{
+    BwdArgs a{};
+    a.a = dout_perm;
+    a.lda = H;
+    a.b0 = a.b1 = wd;
+    a.ldb = H;
+    a.b_estride = F * H;
+    a.K = a.kseg = static_cast<int>(H);
+    a.N = static_cast<int>(F);
+    a.tiles = tiles;
+    a.tile_count = tile_count;
+    a.c = dgu;
+    a.g = g;
+    a.u = u;
+    a.prow = prow;
+    a.hp = hp;
+    a.partial = partial;
+    return launch_bwd<kEpiDown>(a, max_tiles * (F / BN), s);
+}
+
+hipError_t launch_dprobs(const float* partial, const int32_t* pos, float* dprobs, int64_t M, int64_t F,
+                         hipStream_t s)
+{
+    if (M <= 0)
+        return hipSuccess;
+    dprobs_kernel<<<dim3(static_cast<unsigned>((M + kSmallThreads - 1) / kSmallThreads)),
+                    dim3(kSmallThreads), 0, s>>>(partial, pos, dprobs, M, static_cast<int>(F / 64));
+    return hipGetLastError();
+}
+
+hipError_t launch_dgrad_gate_up(const uint16_t* dgu, const uint16_t* wg, const uint16_t* wu,
+                                uint16_t* dx_perm, const MTile* tiles, const int32_t* tile_count,
+                                int64_t max_tiles, int64_t H, int64_t F, hipStream_t s)
+{
+    BwdArgs a{};
+    a.a = dgu;
+    a.lda = 2 * F;
+    a.b0 = wg;
+    a.b1 = wu;
+    a.ldb = F;
+    a.b_estride = H * F;
+    a.kseg = static_cast<int>(F);
+    a.K = static_cast<int>(2 * F);
+    a.N = static_cast<int>(H);
+    a.tiles = tiles;
+    a.tile_count = tile_count;
+    a.c = dx_perm;
+    return launch_bwd<kEpiGateUp>(a, max_tiles * (H / BN), s);
+}
+
+hipError_t launch_wgrad(const uint16_t* a_rows, int64_t lda, const uint16_t* b_rows, int64_t ldb,
+                        const int32_t* offsets, int64_t E, int64_t Mo, int64_t No, float* dw,
+                        hipStream_t s)
+{
+    BwdArgs a{};
+    a.a = a_rows;
+    a.lda = lda;
+    a.b0 = a.b1 = b_rows;
+    a.ldb = ldb;
+    a.Mo = static_cast<int>(Mo);
+    a.N = static_cast<int>(No);
+    a.offsets = offsets;
+    a.E = static_cast<int>(E);
+    a.c = dw;
+    return launch_bwd<kEpiWgrad>(a, E * (Mo / BM) * (No / BN), s);
+}
+
+}  // namespace moe

@@ -119,6 +119,7 @@ hipError_t launch_build_tiles(const int32_t* offsets, const int32_t* group_exper
 // Slots whose pos is outside [0, M) are skipped.
 hipError_t launch_permute(const void* x, const int32_t* pos, void* x_perm, int64_t T, int64_t k,
                           int64_t M, int64_t row_bytes, hipStream_t s);
+// probs null: every weight is 1 (the plain sum of a token's k rows).
 hipError_t launch_unpermute(int dtype, const void* y_perm, const int32_t* pos, const float* probs,
                             void* out, int64_t T, int64_t k, int64_t M, int64_t H, hipStream_t s);
 
@@ -157,6 +158,29 @@ hipError_t launch_fc2_mx(const uint8_t* h, const uint8_t* h_scale, const uint8_t
 // MX tile shapes: 256 x 256 when H and F are multiples of 1024, else 128 x 128.
 int mx_row_tile(int64_t H, int64_t F);
 int mx_fc2_cols_per_tile(int64_t H, int64_t F);
+// gemm_bwd.hip: the backward's grouped GEMMs (bf16, 128-row tiles; H and F multiples of 128).
+bool bwd_supported(int64_t H, int64_t F);
+constexpr int kBmBwd = 128;
+// prow[p] = probs[perm[p]]
+hipError_t launch_row_probs(const int32_t* perm, const float* probs, float* prow, int64_t M,
+                            hipStream_t s);
+// d = dout_perm Wd^T with the SwiGLU backward in the epilogue: dgu [M, 2F] = [dg | du], hp [M, F]
+// = w h, partial [M, F / 64] (per 64 columns: sum of h d)
+hipError_t launch_dgrad_down(const uint16_t* dout_perm, const uint16_t* wd, const uint16_t* g,
+                             const uint16_t* u, const float* prow, uint16_t* dgu, uint16_t* hp,
+                             float* partial, const MTile* tiles, const int32_t* tile_count,
+                             int64_t max_tiles, int64_t H, int64_t F, hipStream_t s);
+// dprobs[s] = sum of partial[pos[s]][0 .. F / 64)
+hipError_t launch_dprobs(const float* partial, const int32_t* pos, float* dprobs, int64_t M,
+                         int64_t F, hipStream_t s);
+// dx_perm = dg Wg^T + du Wu^T
+hipError_t launch_dgrad_gate_up(const uint16_t* dgu, const uint16_t* wg, const uint16_t* wu,
+                                uint16_t* dx_perm, const MTile* tiles, const int32_t* tile_count,
+                                int64_t max_tiles, int64_t H, int64_t F, hipStream_t s);
+// dw[e] [Mo, No] (fp32) = sum over the rows p of expert e of a_rows[p, :Mo]^T b_rows[p, :No]
+hipError_t launch_wgrad(const uint16_t* a_rows, int64_t lda, const uint16_t* b_rows, int64_t ldb,
+                        const int32_t* offsets, int64_t E, int64_t Mo, int64_t No, float* dw,
+                        hipStream_t s);
 // router.hip: top-k gate over float32 logits [T, E] (E <= 1024, k <= min(E, 64)).
 hipError_t launch_router(const float* logits, int64_t T, int64_t E, int64_t k, int32_t* ids,
                          float* probs, hipStream_t s);

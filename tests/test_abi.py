@@ -118,3 +118,32 @@ def test_status_strings(mel):
     names = [lib.moe_status_string(i).decode() for i in range(6)]
     assert names == ["MOE_OK", "MOE_ERR_INVALID_ARGUMENT", "MOE_ERR_UNSUPPORTED",
                      "MOE_ERR_WORKSPACE_TOO_SMALL", "MOE_ERR_EXPERT_ID_OUT_OF_RANGE", "MOE_ERR_HIP"]
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(T=64, H=128, F=256, E=4, k=2, dtype=1), 0),
+    (dict(T=0, H=128, F=256, E=4, k=2, dtype=1), 0),
+    (dict(T=64, H=128, F=256, E=4, k=2, dtype=0), 2),          # the backward is bf16 only
+    (dict(T=64, H=128, F=256, E=4, k=2, dtype=2), 2),
+    (dict(T=64, H=128, F=192, E=4, k=2, dtype=1), 2),          # F % 128
+    (dict(T=64, H=4096, F=14336, E=8, k=2, dtype=1), 0),
+    (dict(T=64, H=128, F=256, E=4, k=2, dtype=1, head_m_size=256), 2),   # unchunked only
+])
+def test_backward_validation(mel, kw, expected):
+    prob = mel.problem(**kw)
+    n = ctypes.c_size_t()
+    assert mel.library().moe_backward_workspace_size(ctypes.byref(prob), ctypes.byref(n)) == expected
+    if expected == 0:
+        assert n.value > 0
+
+
+def test_backward_rejects_before_enqueue(mel):
+    lib = mel.library()
+    prob = mel.problem(64, 128, 256, 4, 2, mel.BF16)
+    n = ctypes.c_size_t()
+    assert lib.moe_backward_workspace_size(ctypes.byref(prob), ctypes.byref(n)) == 0
+    st = lib.moe_expert_backward(ctypes.byref(prob), *([None] * 13), 0, None)
+    assert st == 3 and b"workspace" in lib.moe_last_error()
+    st = lib.moe_expert_backward(ctypes.byref(prob), *([None] * 12), ctypes.c_void_p(0x1000),
+                                 n.value, None)
+    assert st == 1

@@ -1,0 +1,148 @@
+"""Parity of the layer's backward (bf16) with the oracle's fp64 gradients.
+
+Small layers are compared whole: dx, dw_gate, dw_up, dw_down and dprobs each within 2e-2 inf-norm
+relative error (the bf16 bar; g, u, dg, du, probs * h and the per-slot dx rows are bf16 on the GPU,
+the oracle keeps everything in double).  At the workloads' full sizes the oracle computes sampled
+tokens (dx rows, dprobs) and sampled weight-gradient entries one by one; samples include the tokens
+and the weight columns at tile edges.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_layer_amd as mel
+import oracle
+import synth
+from synth import device as dv
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    mel.library()
+    oracle.build()
+
+
+def _gpu_backward(inp, dout):
+    d = dv.layer(inp)
+    dd = dv.tensor(dout)
+    res = mel.expert_backward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs, dd)
+    torch.cuda.synchronize()
+    return [dv.host(t) for t in res]
+
+
+def _compare(gpu, ref, names=("dx", "dw_gate", "dw_up", "dw_down", "dprobs")):
+    for name, a, r in zip(names, gpu, ref):
+        err = oracle.inf_norm_rel(a, r)
+        print(f"    {name}: inf-norm rel {err:.2e}", flush=True)
+        assert np.all(np.isfinite(a)), name
+        assert err <= TOL, (name, err)
+
+
+CASES = [
+    # T, H, F, E, k, routing kwargs: several row tiles with ragged tails, several column tiles
+    (300, 256, 384, 6, 2, {}),
+    # fine-grained shape: many experts, some empty (zero weight gradients), k = 4
+    (200, 128, 256, 16, 4, dict(routing="zipf_gumbel", zipf_s=1.1, n_zero=3)),
+    # one token, one expert slot
+    (1, 128, 128, 2, 1, {}),
+    # k = E: every token uses every expert
+    (40, 128, 256, 3, 3, {}),
+]
+
+
+@pytest.mark.parametrize("T,H,F,E,k,kw", CASES)
+def test_backward_matches_oracle(T, H, F, E, k, kw):
+    print(f"[backward] T={T} H={H} F={F} E={E} k={k} {kw}", flush=True)
+    inp = synth.make_layer(T=T, H=H, F=F, E=E, k=k, dtype="bf16", seed=T + E, **kw)
+    dout = synth.make_dout(inp)
+    gpu = _gpu_backward(inp, dout)
+    ref = oracle.backward(inp, dout)
+    _compare(gpu, ref)
+    counts = np.bincount(inp.expert_ids.ravel(), minlength=E)
+    for e in np.flatnonzero(counts == 0):
+        assert np.all(gpu[1][e] == 0) and np.all(gpu[2][e] == 0) and np.all(gpu[3][e] == 0)
+
+
+def test_backward_is_deterministic():
+    inp = synth.make_layer(T=257, H=256, F=256, E=5, k=2, dtype="bf16", seed=11)
+    dout = synth.make_dout(inp)
+    a = _gpu_backward(inp, dout)
+    b = _gpu_backward(inp, dout)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint32) if x.dtype == np.float32 else x,
+                              y.view(np.uint32) if y.dtype == np.float32 else y)
+
+
+def test_backward_without_tokens_zeroes_the_weight_gradients():
+    inp = synth.make_layer(T=4, H=128, F=128, E=3, k=1, dtype="bf16", seed=2)
+    d = dv.layer(inp)
+    x = d.x[:0]
+    ids = d.expert_ids[:0]
+    probs = d.probs[:0]
+    dout = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    dx, dwg, dwu, dwd, dprobs = mel.expert_backward(x, d.w_gate, d.w_up, d.w_down, ids, probs, dout)
+    torch.cuda.synchronize()
+    assert dx.shape == (0, 128) and dprobs.shape == (0, 1)
+    for t in (dwg, dwu, dwd):
+        assert torch.count_nonzero(t).item() == 0
+
+
+def test_backward_zero_probability_slot():
+    """probs 0 on slot 1 of every token: dx and the weight gradients equal those of the k = 1 layer
+    within the tolerance, dprobs of the zero slots is still <dout, y>."""
+    inp = synth.make_layer(T=150, H=128, F=256, E=4, k=2, dtype="bf16", seed=5)
+    inp.probs[:, 1] = 0.0
+    dout = synth.make_dout(inp)
+    gpu = _gpu_backward(inp, dout)
+    ref = oracle.backward(inp, dout)
+    _compare(gpu, ref)
+
+
+def test_backward_rejects_other_dtypes():
+    inp = synth.make_layer(T=8, H=128, F=128, E=2, k=1, dtype="f32", seed=0)
+    d = dv.layer(inp)
+    dout = torch.zeros((8, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        mel.expert_backward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs, dout)
+
+
+def _edge_columns(n, rng, n_random, tile=128):
+    cols = {0, n - 1, tile - 1, tile, n - tile}
+    cols.update(int(c) for c in rng.choice(n, size=n_random, replace=False))
+    return np.array(sorted(c for c in cols if 0 <= c < n))
+
+
+@pytest.mark.parametrize("name,n_tokens,n_entries", [("mixtral_bf16", 6, 24),
+                                                     ("finegrained_bf16", 8, 32)])
+def test_backward_full_size_sampled(name, n_tokens, n_entries):
+    print(f"[backward-full] {name}: generating inputs", flush=True)
+    inp = synth.make_workload(name)
+    dout = synth.make_dout(inp)
+    print(f"[backward-full] {name}: T={inp.T} H={inp.H} F={inp.F} E={inp.E} k={inp.k}", flush=True)
+    dx, dwg, dwu, dwd, dprobs = _gpu_backward(inp, dout)
+    rng = np.random.default_rng(0)
+    counts, offsets, perm, pos = oracle.route(inp.expert_ids, inp.E)
+    # tokens owning the first / last row of the largest experts, and random ones
+    big = np.argsort(-counts)[:2]
+    toks = {int(perm[offsets[e]]) // inp.k for e in big} | {int(perm[offsets[e + 1] - 1]) // inp.k for e in big}
+    toks.update(int(t) for t in rng.choice(inp.T, size=n_tokens, replace=False))
+    toks = np.array(sorted(toks), np.int32)
+    print(f"[backward-full] {name}: oracle on {len(toks)} tokens", flush=True)
+    ref_dx, ref_dp = oracle.backward_tokens(inp, dout, toks)
+    _compare([dx[toks], dprobs[toks]], [ref_dx, ref_dp], names=("dx rows", "dprobs rows"))
+    # weight-gradient entries: experts with rows, columns at tile edges and random
+    live = np.flatnonzero(counts > 0)
+    e = rng.choice(live, size=n_entries)
+    f = rng.choice(_edge_columns(inp.F, rng, 8), size=n_entries)
+    h = rng.choice(_edge_columns(inp.H, rng, 8), size=n_entries)
+    print(f"[backward-full] {name}: oracle on {n_entries} weight-gradient entries", flush=True)
+    rg, ru, rd = oracle.wgrad_entries(inp, dout, e, f, h)
+    _compare([dwg[e, h, f], dwu[e, h, f], dwd[e, f, h]], [rg, ru, rd],
+             names=("dw_gate entries", "dw_up entries", "dw_down entries"))
+    empty = np.flatnonzero(counts == 0)
+    for ee in empty:
+        assert np.all(dwg[ee] == 0) and np.all(dwu[ee] == 0) and np.all(dwd[ee] == 0)
