@@ -14,6 +14,10 @@ The flush reads the 1 GiB buffer by default (`--flush write` overwrites it inste
 operand of the previous step stays in the L2s or the Infinity Cache, but a write flush also leaves
 those caches full of dirty lines, whose write-back then lands on whichever kernel runs first.
 
+Beside the step, and outside its figures: the router in front of the layer and, for the bfloat16
+workloads, the layer's backward (gradients of x, the three weight stacks and probs, with g and u
+recomputed), each timed on its own with the same flush.
+
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -120,6 +124,7 @@ def main():
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-chunked", action="store_true")
     ap.add_argument("--skip-router", action="store_true")
+    ap.add_argument("--skip-backward", action="store_true")
     ap.add_argument("--separate-permute", action="store_true",
                     help="run the permute step as its own kernel instead of inside fc1's row loads")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -285,6 +290,56 @@ def main():
         result["router"] = {"ms": r_ms, "bytes": r_bytes, "GB/s": r_bytes / (r_ms * 1e-3) / 1e9,
                             "frac": r_bytes / (r_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         log(f"router {r_ms * 1e3:.1f} us ({r_bytes / (r_ms * 1e-3) / 1e9:.0f} GB/s)")
+
+    # the layer's backward (bf16 workloads): gradients of sum(dout * out) for x, the three weight
+    # stacks and probs, g and u recomputed inside; timed on its own like the router
+    if not args.skip_backward and inp.dtype == "bf16":
+        dout = dv.tensor(synth.make_dout(inp), dev)
+        bws = torch.empty(mel.backward_workspace_size(mel.problem(T, H, F, E, k, mel.BF16)),
+                          dtype=torch.uint8, device=dev)
+
+        def bstep():
+            return mel.expert_backward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs, dout,
+                                       workspace=bws)
+
+        for _ in range(2):
+            bstep()
+        torch.cuda.synchronize()
+        bsteps = max(3, args.steps // 2)
+        bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(bsteps)]
+        for a, b in bev:
+            do_flush()
+            a.record()
+            bstep()
+            b.record()
+        torch.cuda.synchronize()
+        bms = np.array([a.elapsed_time(b) for a, b in bev])
+        mel.timing_reset()
+        mel.timing_enable(True)
+        for _ in range(bsteps):
+            do_flush()
+            bstep()
+        bk = mel.timing_collect()
+        mel.timing_enable(False)
+        bkavg = {n: tot / cnt for n, (tot, cnt) in bk.items()}
+        grad_flops = 12.0 * M * H * F            # dgrad down + gate/up, wgrad down + gate/up
+        rec_flops = 4.0 * M * H * F              # g and u recomputed
+        gemm_names = ("recompute_g", "recompute_u", "dgrad_down", "dgrad_gate_up", "wgrad_down",
+                      "wgrad_gate", "wgrad_up")
+        gemm_ms = sum(bkavg.get(n, 0.0) for n in gemm_names)
+        b_mean = float(bms.mean())
+        result["backward"] = {
+            "ms": b_mean, "median_ms": float(np.median(bms)), "steps": bsteps,
+            "tokens_per_s": T / (b_mean * 1e-3),
+            "gemm_tflops": (grad_flops + rec_flops) / (gemm_ms * 1e-3) / 1e12,
+            "gemm_frac_of_peak": (grad_flops + rec_flops) / (gemm_ms * 1e-3) / 1e12 / peak,
+            "flops": {"gradients": grad_flops, "recompute": rec_flops},
+            "kernels_ms": bkavg,
+        }
+        log(f"backward ms/step {b_mean:.3f}; kernel avg ms: " +
+            ", ".join(f"{n}={v:.4f}" for n, v in sorted(bkavg.items())))
+        del bws, dout
 
     if not args.skip_chunked:
         for _ in range(2):
