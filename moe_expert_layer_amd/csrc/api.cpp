@@ -609,9 +609,9 @@ MOE_API moe_status moe_expert_backward(const moe_problem* p, const void* x, cons
                                       tcount + 1, nullptr, nullptr, 1, 0, nullptr, status, false, s));
         const int32_t* tcount_d = L.tiles_d != L.tiles_r ? tcount + 1 : tcount;
         // g = x_perm Wg[e], u = x_perm Wu[e]: the plain grouped GEMM with K = H and N = F
-        LAUNCH(s, "recompute_g", launch_fc2_bf16(x_perm, wg, g, tiles_r, tcount, F, H, nullptr, task_ctr, s));
+        LAUNCH(s, "recompute_g", launch_recompute_bf16(x_perm, wg, g, tiles_r, tcount, H, F, task_ctr, s));
         LAUNCH(s, "recompute_u",
-               launch_fc2_bf16(x_perm, wu, u, tiles_r, tcount, F, H, nullptr, task_ctr + kXcdCount, s));
+               launch_recompute_bf16(x_perm, wu, u, tiles_r, tcount, H, F, task_ctr + kXcdCount, s));
         LAUNCH(s, "row_probs", launch_row_probs(perm, probs, prow, M, s));
         LAUNCH(s, "dgrad_down",
                launch_dgrad_down(dout_perm, wd, g, u, prow, dgu, hp, partial, tiles_d, tcount_d,

@@ -633,7 +633,9 @@ __device__ __forceinline__ void store_output_staged(const f32x16_t (&acc)[kTM][k
 
 // gather (fc1 only, may be null): permuted row p of A is row gather[p] / gather_k of the matrix
 // A points at (the permute step folded into the row copies); null: row p of A.
-template <bool kGated>
+// kRole only separates launches in profiles: 0 for the forward, 1 for the backward's recompute of g
+// and u (the same code).
+template <bool kGated, int kRole = 0>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, const MTile* __restrict__ tiles,
@@ -846,6 +848,9 @@ hipError_t ensure_smem_limits()
     if (e == hipSuccess)
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(&big::grouped_gemm_bf16_dma<false>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kBigSmem);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&big::grouped_gemm_bf16_dma<false, 1>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kBigSmem);
     if (e == hipSuccess && dev < 64)
         done[dev] = true;
     return e;
@@ -893,6 +898,25 @@ hipError_t launch_fc2_bf16(const uint16_t* h, const uint16_t* wd, uint16_t* y, c
         FC2_SMALL<<<dim3(2 * cu), dim3(Fc2Small::kThreads), Fc2Small::kSmemBytes, s>>>(
             h, wd, nullptr, y, tiles, tile_count, static_cast<int>(F), static_cast<int>(H),
             chunk_done, task_ctr);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_recompute_bf16(const uint16_t* A, const uint16_t* w, uint16_t* C, const MTile* tiles,
+                                 const int32_t* tile_count, int64_t K, int64_t N, int32_t* task_ctr,
+                                 hipStream_t s)
+{
+    const int cu = device_info().cu_count;
+    if (use_big(N, K)) {
+        if (hipError_t e = ensure_smem_limits(); e != hipSuccess)
+            return e;
+        big::grouped_gemm_bf16_dma<false, 1><<<dim3(cu), dim3(big::kThreads), kBigSmem, s>>>(
+            A, w, nullptr, C, tiles, tile_count, static_cast<int>(K), static_cast<int>(N), nullptr,
+            task_ctr, nullptr, 1);
+    } else {
+        FC2_SMALL<<<dim3(2 * cu), dim3(Fc2Small::kThreads), Fc2Small::kSmemBytes, s>>>(
+            A, w, nullptr, C, tiles, tile_count, static_cast<int>(K), static_cast<int>(N), nullptr,
+            task_ctr);
     }
     return hipGetLastError();
 }

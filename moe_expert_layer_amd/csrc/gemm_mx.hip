@@ -531,6 +531,15 @@ constexpr int mx_wait()
     const bool sc = scale_at(p - 1) && (!kLast || p + 3 < 2 * kScaleSteps);
     return (w ? kBCopies : 0) + (sc ? 1 : 0);
 }
+// A wave whose A rows all lie past the tile's last row copies no A: step t + 1 has landed once at
+// most the weights of steps t + 2 and t + 3 are in flight (scales issued among them are not
+// counted, which only makes the wait longer).
+template <int p, bool kLast>
+constexpr int mx_wait_no_a()
+{
+    constexpr int kUnitSteps = 2 * kScaleSteps;
+    return (!kLast || p + 2 < kUnitSteps ? kBCopies : 0) + (!kLast || p + 3 < kUnitSteps ? kBCopies : 0);
+}
 
 // K step kt at position p of a 16-step unit (stage p % 4, pair stage p % 4 / 2; scales of the
 // 8-step block in slot p / 8): the MFMAs of weight blocks 0-1 (fragments loaded during the
@@ -571,8 +580,8 @@ __device__ __forceinline__ void mx_step(f32x16_t (&acc)[kTM][kTN], const MxFrags
 constexpr int kUnit = 2 * kScaleSteps;    // steps per unrolled unit: four stages, two scale slots
 
 // One unit of 16 K steps; in the last unit of a task, the weight copies stop after position 11,
-// the A copies after position 11, and the last step has no barrier.
-template <bool kGated, int NB, bool kLast, int... Ps>
+// the A copies after position 11, and the last step has no barrier.  kA = false: no A copies.
+template <bool kGated, int NB, bool kLast, bool kA, int... Ps>
 __device__ __forceinline__ void mx_unit_impl(std::integer_sequence<int, Ps...>, f32x16_t (&acc)[kTM][kTN],
                                              MxFrags& A0, MxFrags& A1, i32x8_t (&b01)[2], int (&sb01)[2],
                                              i32x8_t (&b23)[2], int (&sb23)[2], const LaneAddr& la,
@@ -581,35 +590,39 @@ __device__ __forceinline__ void mx_unit_impl(std::integer_sequence<int, Ps...>, 
                                              int64_t N_w)
 {
     ((Ps % 2 == 0
-          ? mx_step<kGated, NB, Ps, !kLast || Ps + 4 < kUnit, Ps % 2 == 1 && (!kLast || Ps + 3 < kUnit),
-                    kLast && Ps == kUnit - 1 ? -1 : mx_wait<Ps, kLast>()>(
+          ? mx_step<kGated, NB, Ps, !kLast || Ps + 4 < kUnit,
+                    kA && Ps % 2 == 1 && (!kLast || Ps + 3 < kUnit),
+                    kLast && Ps == kUnit - 1 ? -1 : kA ? mx_wait<Ps, kLast>() : mx_wait_no_a<Ps, kLast>()>(
                 acc, A0, A1, b01, sb01, b23, sb23, la, cp, a_voff, b_voff, sc_voff, N_w)
-          : mx_step<kGated, NB, Ps, !kLast || Ps + 4 < kUnit, Ps % 2 == 1 && (!kLast || Ps + 3 < kUnit),
-                    kLast && Ps == kUnit - 1 ? -1 : mx_wait<Ps, kLast>()>(
+          : mx_step<kGated, NB, Ps, !kLast || Ps + 4 < kUnit,
+                    kA && Ps % 2 == 1 && (!kLast || Ps + 3 < kUnit),
+                    kLast && Ps == kUnit - 1 ? -1 : kA ? mx_wait<Ps, kLast>() : mx_wait_no_a<Ps, kLast>()>(
                 acc, A1, A0, b01, sb01, b23, sb23, la, cp, a_voff, b_voff, sc_voff, N_w)),
      ...);
 }
 
-template <bool kGated, int NB, bool kLast>
+template <bool kGated, int NB, bool kLast, bool kA>
 __device__ __forceinline__ void mx_unit(f32x16_t (&acc)[kTM][kTN], MxFrags& A0, MxFrags& A1,
                                         i32x8_t (&b01)[2], int (&sb01)[2], i32x8_t (&b23)[2],
                                         int (&sb23)[2], const LaneAddr& la, MxCopy& cp,
                                         const uint32_t (&a_voff)[kACopies],
                                         const uint32_t (&b_voff)[kBCopies], uint32_t sc_voff, int64_t N_w)
 {
-    mx_unit_impl<kGated, NB, kLast>(std::make_integer_sequence<int, kUnit>{}, acc, A0, A1, b01, sb01, b23,
-                                    sb23, la, cp, a_voff, b_voff, sc_voff, N_w);
+    mx_unit_impl<kGated, NB, kLast, kA>(std::make_integer_sequence<int, kUnit>{}, acc, A0, A1, b01, sb01,
+                                        b23, sb23, la, cp, a_voff, b_voff, sc_voff, N_w);
 }
 
 // Copies a task's setup leaves in flight once its step 0 has landed: the weights of steps 1 .. 3
-// and A pair 1.
-constexpr int kTopWait = 3 * kBCopies + kACopies;
+// and A pair 1 (kA = false: the weights alone).
+template <bool kA>
+constexpr int top_wait() { return kA ? 3 * kBCopies + kACopies : 3 * kBCopies; }
 
 // The K loop of one task.  KT is a multiple of 16; the caller issued the scales of block 0, A pair
 // 0, the weights of steps 0 .. 3 and A pair 1 (in that order), cp points at pair 2, step 4 and
-// block 1, and the caller has waited for step 0 (step_barrier<kTopWait>).  Every LDS address is a
-// lane base plus a constant.
-template <bool kGated, int NB>
+// block 1, and the caller has waited for step 0 (step_barrier<top_wait<kA>()>).  kA = false: the
+// wave copies no A (its rows all lie past the tile's end).  Every LDS address is a lane base plus a
+// constant.
+template <bool kGated, int NB, bool kA>
 __device__ __forceinline__ void mx_k_loop(f32x16_t (&acc)[kTM][kTN], const LaneAddr& la, MxCopy cp,
                                           const uint32_t (&a_voff)[kACopies],
                                           const uint32_t (&b_voff)[kBCopies], uint32_t sc_voff, int KT,
@@ -624,8 +637,8 @@ __device__ __forceinline__ void mx_k_loop(f32x16_t (&acc)[kTM][kTN], const LaneA
         read_b_frags<kGated, 0, 0, 0>(b01, sb01, la);
     }
     for (int kt = 0; kt < KT - kUnit; kt += kUnit)
-        mx_unit<kGated, NB, false>(acc, A0, A1, b01, sb01, b23, sb23, la, cp, a_voff, b_voff, sc_voff, N_w);
-    mx_unit<kGated, NB, true>(acc, A0, A1, b01, sb01, b23, sb23, la, cp, a_voff, b_voff, sc_voff, N_w);
+        mx_unit<kGated, NB, false, kA>(acc, A0, A1, b01, sb01, b23, sb23, la, cp, a_voff, b_voff, sc_voff, N_w);
+    mx_unit<kGated, NB, true, kA>(acc, A0, A1, b01, sb01, b23, sb23, la, cp, a_voff, b_voff, sc_voff, N_w);
 }
 
 // fc2 epilogue: bf16 rows through the wave's 2 KiB staging area in pieces of 16 rows x 64 columns.
@@ -858,13 +871,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
                 sc_voff = static_cast<uint32_t>(lane >> 4) * static_cast<uint32_t>(N_out) + 16u * (lane & 15);
             }
         }
-        // scales of block 0 and A pair 0, the weights of steps 0 .. 3, A pair 1 (mx_k_loop's order)
-        mx_issue<true, 0, -1, 0>(cp, a_voff, b_voff, sc_voff, N_w);
+        // scales of block 0 and A pair 0, the weights of steps 0 .. 3, A pair 1 (mx_k_loop's order);
+        // a wave whose A rows all lie past the tile's end copies the scales and the weights alone
+        // (the A source still moves on by the two pairs)
+        if (32 * wave < rows)
+            mx_issue<true, 0, -1, 0>(cp, a_voff, b_voff, sc_voff, N_w);
+        else
+            mx_issue<true, 0, -1, -1>(cp, a_voff, b_voff, sc_voff, N_w);
         mx_issue<false, 0, 0, -1>(cp, a_voff, b_voff, sc_voff, N_w);
         mx_issue<false, 0, 1, -1>(cp, a_voff, b_voff, sc_voff, N_w);
         mx_issue<false, 0, 2, -1>(cp, a_voff, b_voff, sc_voff, N_w);
         mx_issue<false, 0, 3, -1>(cp, a_voff, b_voff, sc_voff, N_w);
-        mx_issue<false, 0, -1, 1>(cp, a_voff, b_voff, sc_voff, N_w);
+        if (32 * wave < rows)
+            mx_issue<false, 0, -1, 1>(cp, a_voff, b_voff, sc_voff, N_w);
+        else
+            cp.a += 4 * BK;
     };
 
     int t = claim_task(claimed, task_ctr, xcd, blk, wave, lane);
@@ -880,6 +901,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
         const int rows = tile.row_end - tile.row_begin;
         const int nb = __builtin_amdgcn_readfirstlane(
             min(kTM, max(0, ((rows + 31) / 32 - wm + kWM - 1) / kWM)));
+        // the wave copies A rows 32 wave .. + 31 (row block `wave`, used by wave row wave % kWM):
+        // a wave that copies no A has at most one row block, a wave without row blocks copies none
+        const int a_on = __builtin_amdgcn_readfirstlane(32 * wave < rows ? 1 : 0);
         f32x16_t acc[kTM][kTN];
 #pragma unroll
         for (int i = 0; i < kTM; ++i)
@@ -890,16 +914,22 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
                     acc[i][j][r] = 0.0f;
         // step 0 has landed; past this barrier every wave sees the claim of the following task,
         // whose gathered source rows are loaded now and used after this task's K loop
-        step_barrier<kTopWait>();
+        if (a_on)
+            step_barrier<top_wait<true>()>();
+        else
+            step_barrier<top_wait<false>()>();
         const int ci = __builtin_amdgcn_readfirstlane(*claimed);
         const int t_next = ((ci / blk) * kXcdCount + xcd) * blk + ci % blk;
         if (t_next < total)
             fetch_rows(t_next);
-        switch (nb) {
-        case 0: mx_k_loop<kGated, 0>(acc, la, cp, a_voff, b_voff, sc_voff, KT, N_w); break;
-        case 1: mx_k_loop<kGated, 1>(acc, la, cp, a_voff, b_voff, sc_voff, KT, N_w); break;
-        default: mx_k_loop<kGated, 2>(acc, la, cp, a_voff, b_voff, sc_voff, KT, N_w); break;
-        }
+        if (nb == 0)
+            mx_k_loop<kGated, 0, false>(acc, la, cp, a_voff, b_voff, sc_voff, KT, N_w);
+        else if (nb == 1 && !a_on)
+            mx_k_loop<kGated, 1, false>(acc, la, cp, a_voff, b_voff, sc_voff, KT, N_w);
+        else if (nb == 1)
+            mx_k_loop<kGated, 1, true>(acc, la, cp, a_voff, b_voff, sc_voff, KT, N_w);
+        else
+            mx_k_loop<kGated, 2, true>(acc, la, cp, a_voff, b_voff, sc_voff, KT, N_w);
         const MTile done = tile;
         const int done_n0 = n0;
         t = t_next;
