@@ -478,11 +478,14 @@ MOE_API moe_status moe_expert_forward_mx(const moe_problem* p, const uint8_t* x,
 namespace moe {
 namespace {
 
+constexpr size_t kWgradZeroBytes = 1024;    // zero rows the weight-gradient copies read past an expert
+
 struct BackwardLayout {
     RouteLayout route;
     size_t counts = 0, offsets = 0, perm = 0, pos = 0, tile_count = 0, task_ctr = 0;
     size_t tiles_r = 0, tiles_d = 0, prow = 0, partial = 0;
-    size_t x_perm = 0, dout_perm = 0, g = 0, u = 0, dgu = 0, hp = 0, dx_perm = 0, total = 0;
+    size_t x_perm = 0, dout_perm = 0, g = 0, u = 0, dgu = 0, hp = 0, dx_perm = 0;
+    size_t wgrad_ctr = 0, zero = 0, total = 0;   // last: the zero rows sit above every source row
     int64_t max_tiles_r = 0, max_tiles_d = 0;
     int bm_r = 0;
 };
@@ -521,6 +524,11 @@ BackwardLayout backward_layout(int64_t T, int64_t H, int64_t F, int64_t E, int64
     L.dgu = take(4 * n(M) * n(F));
     L.hp = take(2 * n(M) * n(F));
     L.dx_perm = take(2 * n(M) * n(H));
+    L.wgrad_ctr = take(3 * kXcdCount * sizeof(int32_t));
+    // a weight-gradient copy source starts at most one row (plus its column offset) past the end
+    // of its buffer; the zero rows must lie above every such start
+    take(n(std::max(2 * H, 4 * F)));
+    L.zero = take(kWgradZeroBytes);
     L.total = off;
     return L;
 }
@@ -580,6 +588,13 @@ MOE_API moe_status moe_expert_backward(const moe_problem* p, const void* x, cons
     if (moe_status st = run_route(expert_ids, T, k, E, counts, offsets, perm, pos, ws, L.route, s);
         st != MOE_OK)
         return st;
+    // the weight-gradient kernels' task counters and zero rows (one contiguous region)
+    LAUNCH(s, "zero_fill",
+           launch_zero_i32(at<int32_t>(ws, L.wgrad_ctr),
+                           static_cast<int64_t>((L.zero + kWgradZeroBytes - L.wgrad_ctr) / 4), s));
+    const bool dma_ok = L.total < (size_t{1} << 32);       // zero rows within 32-bit copy offsets
+    const uint16_t* zero = dma_ok ? at<uint16_t>(ws, L.zero) : nullptr;
+    int32_t* wctr = at<int32_t>(ws, L.wgrad_ctr);
     const auto* wg = static_cast<const uint16_t*>(w_gate);
     const auto* wu = static_cast<const uint16_t*>(w_up);
     const auto* wd = static_cast<const uint16_t*>(w_down);
@@ -622,9 +637,12 @@ MOE_API moe_status moe_expert_backward(const moe_problem* p, const void* x, cons
         LAUNCH(s, "unpermute", launch_unpermute(1, dx_perm, pos, nullptr, dx, T, k, M, H, s));
     }
     // weight gradients (an expert without rows gets zeros)
-    LAUNCH(s, "wgrad_down", launch_wgrad(hp, F, dout_perm, H, offsets, E, F, H, dw_down, s));
-    LAUNCH(s, "wgrad_gate", launch_wgrad(x_perm, H, dgu, 2 * F, offsets, E, H, F, dw_gate, s));
-    LAUNCH(s, "wgrad_up", launch_wgrad(x_perm, H, dgu + F, 2 * F, offsets, E, H, F, dw_up, s));
+    LAUNCH(s, "wgrad_down",
+           launch_wgrad(hp, F, dout_perm, H, offsets, E, F, H, dw_down, zero, wctr, s));
+    LAUNCH(s, "wgrad_gate",
+           launch_wgrad(x_perm, H, dgu, 2 * F, offsets, E, H, F, dw_gate, zero, wctr + kXcdCount, s));
+    LAUNCH(s, "wgrad_up",
+           launch_wgrad(x_perm, H, dgu + F, 2 * F, offsets, E, H, F, dw_up, zero, wctr + 2 * kXcdCount, s));
     return MOE_OK;
 }
 

@@ -27,6 +27,8 @@
 // gradients over (expert, column tile of the gradient's rows, column tile of its columns) in groups
 // of 8 row tiles; consecutive tasks go to one XCD (workgroup b runs on XCD b % 8), so the
 // workgroups of an XCD share operand strips in its L2.
+#include <utility>
+
 #include "common.h"
 #include "gemm_common.h"
 #include "internal.h"
@@ -343,6 +345,344 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_bwd(BwdArgs g)
     }
 }
 
+// ------------------------------------------------------------------------------------------------
+// Weight gradients with LDS DMA (gradient tiles of 256 x 256; Mo and No multiples of 256).
+//
+// Both operands are activation rows over K (the expert's rows), so both take the path the forward's
+// large-tile kernel uses for its weights: four LDS stages of 32 k rows each ([32][256] bf16, 512-byte
+// rows, 16-byte chunks XOR-swizzled by c ^ 4 (kr & 3)), filled by global_load_lds_dwordx4 (no
+// staging registers) and read with the transposing ds_read_b64_tr_b16, which hands each lane 4
+// consecutive k of one column: an MFMA operand fragment from two reads.  Each K step every wave
+// issues 2 copies of A rows and 2 of B rows for step t + 4 right after the barrier of step t, so at
+// every barrier "step t + 1 has landed" is "at most 8 copies in flight".  A copy lane whose row lies
+// past the expert's last row reads a zeroed buffer instead (its offset from the copy's base is the
+// buffer's distance), and the K loop runs whole groups of four steps, so no row is masked in the
+// arithmetic.  8 waves of 64 x 128 (2 x 4 blocks of 32 x 32), one persistent workgroup per CU,
+// tasks (expert, gradient row tile, column tile) claimed per XCD; the next task's first copies go
+// out before the current task's fp32 stores.
+namespace tn {
+
+constexpr int kWM = 4, kWN = 2, kTM = 2, kTN = 4;
+constexpr int kWaves = kWM * kWN;
+constexpr int kThreads = kWaves * 64;
+constexpr int BM = kWM * kTM * 32;                 // 256 gradient rows
+constexpr int BN = kWN * kTN * 32;                 // 256 gradient columns
+constexpr int BK = 32;
+constexpr int kStages = 4;
+constexpr int kRowBytes = BM * 2;                  // one k row of a stage
+constexpr int kStageBytes = BK * kRowBytes;        // 16 KiB
+constexpr int kBRing = kStages * kStageBytes;      // A stages in the first 64 KiB, B in the next
+constexpr int kSmemBytes = 2 * kBRing + 256;       // + the claimed-task word
+constexpr int kCopies = kStageBytes / 1024 / kWaves;   // 1 KiB copies per operand, wave and step (2)
+constexpr int kStepCopies = 2 * kCopies;
+constexpr int kGroup = 8;                          // gradient row tiles per task group
+static_assert(BM == BN, "one stage layout serves both operands");
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+template <int N>
+__device__ __forceinline__ void step_barrier()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
+struct Frags {
+    bf16x8_t a[kTM];
+    bf16x8_t b[kTN];
+    i16x4_t alo[kTM];
+    i16x4_t blo[kTN];
+};
+
+// Running copy state: sources at the next step's first row (columns m0 / n0), rows of the expert
+// left from there, and the zero buffer's byte distance from each source.
+struct Copy {
+    const uint16_t* a;
+    const uint16_t* b;
+    int rem;
+    uint32_t za, zb;
+    uint32_t a_lds, b_lds;
+};
+
+// Fixed per lane: copy j moves stage rows 2 (kCopies wave + j) + lane / 32, chunk position lane % 32.
+struct Lane {
+    uint32_t a_voff[kCopies], b_voff[kCopies], c16[kCopies];
+    int krl[kCopies];
+    uint32_t a_base[kTM], b_base[kTN];        // fragment-read addresses in stage 0
+};
+
+template <int C>
+__device__ __forceinline__ void copy_one(const Copy& cp, const Lane& ln, int SB)
+{
+    constexpr int j = C % kCopies;
+    if constexpr (C < kCopies) {
+        const uint32_t v = ln.krl[j] < cp.rem ? ln.a_voff[j] : cp.za + ln.c16[j];
+        lds_copy16(cp.a, v, cp.a_lds + SB * kStageBytes + j * 1024);
+    } else {
+        const uint32_t v = ln.krl[j] < cp.rem ? ln.b_voff[j] : cp.zb + ln.c16[j];
+        lds_copy16(cp.b, v, cp.b_lds + SB * kStageBytes + j * 1024);
+    }
+}
+
+// The sources move on by one step while rows of the expert remain; after its last row they stay
+// (every copy then reads the zero rows), so a source never passes the zero rows above it.
+__device__ __forceinline__ void advance(Copy& cp, int64_t lda, int64_t ldb)
+{
+    cp.rem -= BK;
+    if (cp.rem > 0) {
+        cp.a += BK * lda;
+        cp.b += BK * ldb;
+        cp.za -= static_cast<uint32_t>(BK * lda * 2);
+        cp.zb -= static_cast<uint32_t>(BK * ldb * 2);
+    }
+}
+
+// Fragment read Q of sub-step KS of stage S, in the order the MFMAs consume them: Q 0-1 the two
+// halves of A block 0, then two per weight block j, then two per A block i >= 1.
+template <int S, int KS, int Q>
+__device__ __forceinline__ void read_one(Frags& f, const Lane& ln)
+{
+    constexpr int kB0 = 2, kB1 = 2 + 2 * kTN;
+    constexpr bool isB = Q >= kB0 && Q < kB1;
+    constexpr int h = Q % 2;
+    constexpr int idx = isB ? (Q - kB0) / 2 : (Q < kB0 ? 0 : 1 + (Q - kB1) / 2);
+    const uint32_t p = (isB ? ln.b_base[idx] : ln.a_base[idx]) + S * kStageBytes + (16 * KS + 4 * h) * kRowBytes;
+    const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4_t*>(p));
+    if constexpr (isB) {
+        if constexpr (h == 0)
+            f.blo[idx] = v;
+        else
+            f.b[idx] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(f.blo[idx], v, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+        if constexpr (h == 0)
+            f.alo[idx] = v;
+        else
+            f.a[idx] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(f.alo[idx], v, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+}
+
+template <int S, int KS, int Q0, int... Is>
+__device__ __forceinline__ void reads_impl(std::integer_sequence<int, Is...>, Frags& f, const Lane& ln)
+{
+    (read_one<S, KS, Q0 + Is>(f, ln), ...);
+}
+
+template <int S, int KS, int Q0, int Q1>
+__device__ __forceinline__ void reads(Frags& f, const Lane& ln)
+{
+    reads_impl<S, KS, Q0>(std::make_integer_sequence<int, Q1 - Q0>{}, f, ln);
+}
+
+template <int C0, int... Is>
+__device__ __forceinline__ void copies_impl(std::integer_sequence<int, Is...>, const Copy& cp,
+                                            const Lane& ln, int SB)
+{
+    (copy_one<C0 + Is>(cp, ln, SB), ...);
+}
+
+template <int C0, int C1>
+__device__ __forceinline__ void copies(const Copy& cp, const Lane& ln, int SB)
+{
+    copies_impl<C0>(std::make_integer_sequence<int, C1 - C0>{}, cp, ln, SB);
+}
+
+// Slot M of a sub-step: MFMA M, then its share of the next fragment reads and of the copies.
+template <int NC, int SB, int SR, int KS, int M>
+__device__ __forceinline__ void slot(f32x16_t (&acc)[kTM][kTN], const Frags& use, Frags& load,
+                                     const Copy& cp, const Lane& ln)
+{
+    constexpr int NM = kTM * kTN, NR = 2 * (kTM + kTN);
+    acc[M / kTN][M % kTN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(use.a[M / kTN], use.b[M % kTN],
+                                                                    acc[M / kTN][M % kTN], 0, 0, 0);
+    reads<SR, KS, M * NR / NM, (M + 1) * NR / NM>(load, ln);
+    copies<M * NC / NM, (M + 1) * NC / NM>(cp, ln, SB);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int NC, int SB, int SR, int KS, int... Ms>
+__device__ __forceinline__ void slots(std::integer_sequence<int, Ms...>, f32x16_t (&acc)[kTM][kTN],
+                                      const Frags& use, Frags& load, const Copy& cp, const Lane& ln)
+{
+    (slot<NC, SB, SR, KS, Ms>(acc, use, load, cp, ln), ...);
+}
+
+// K step t (stage S): the MFMAs of sub-step 0 while sub-step 1's fragments are read; the barrier
+// after which step t + 1 has landed (at most W copies in flight; none for W < 0); the MFMAs of
+// sub-step 1 while step t + 1's first fragments are read and (kCopy) step t + 4's copies go into
+// the stage step t has freed.
+template <int S, bool kCopy, int W>
+__device__ __forceinline__ void k_step(f32x16_t (&acc)[kTM][kTN], Frags& f0, Frags& f1, Copy& cp,
+                                       const Lane& ln, int64_t lda, int64_t ldb)
+{
+    __builtin_amdgcn_sched_barrier(0);
+    slots<0, 0, S, 1>(std::make_integer_sequence<int, kTM * kTN>{}, acc, f0, f1, cp, ln);
+    if constexpr (W >= 0)
+        step_barrier<W>();
+    __builtin_amdgcn_sched_barrier(0);
+    slots<kCopy ? kStepCopies : 0, S, (S + 1) % kStages, 0>(std::make_integer_sequence<int, kTM * kTN>{},
+                                                             acc, f1, f0, cp, ln);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kCopy)
+        advance(cp, lda, ldb);
+}
+
+constexpr int kTopWait = 3 * kStepCopies;       // steps 1 .. 3 may still be in flight
+
+// The K loop of one task: KT a multiple of 4 (at least 4); the caller issued steps 0 .. 3 and
+// waited for step 0 (step_barrier<kTopWait>); cp is at step 4.
+__device__ __forceinline__ void k_loop(f32x16_t (&acc)[kTM][kTN], Copy cp, const Lane& ln, int KT,
+                                       int64_t lda, int64_t ldb)
+{
+    constexpr int W = 2 * kStepCopies;
+    Frags f0, f1;
+    reads<0, 0, 0, 2 * (kTM + kTN)>(f0, ln);
+    for (int kt = 0; kt < KT - kStages; kt += kStages) {
+        k_step<0, true, W>(acc, f0, f1, cp, ln, lda, ldb);
+        k_step<1, true, W>(acc, f0, f1, cp, ln, lda, ldb);
+        k_step<2, true, W>(acc, f0, f1, cp, ln, lda, ldb);
+        k_step<3, true, W>(acc, f0, f1, cp, ln, lda, ldb);
+    }
+    k_step<0, false, W>(acc, f0, f1, cp, ln, lda, ldb);
+    k_step<1, false, kStepCopies>(acc, f0, f1, cp, ln, lda, ldb);
+    k_step<2, false, 0>(acc, f0, f1, cp, ln, lda, ldb);
+    k_step<3, false, -1>(acc, f0, f1, cp, ln, lda, ldb);
+}
+
+struct WgradArgs {
+    const uint16_t* a;       // rows over K: [rows][>= Mo], row stride lda
+    const uint16_t* b;       // [rows][>= No], row stride ldb
+    int64_t lda, ldb;
+    const int32_t* offsets;  // expert e owns rows [offsets[e], offsets[e + 1])
+    const uint16_t* zero;    // >= 512 zero bytes at or above (source end + one source row)
+    float* c;                // [E][Mo][No]
+    int E, Mo, No;
+    int32_t* task_ctr;       // kXcdCount zeroed counters
+};
+
+__global__ __launch_bounds__(kThreads, 1) void wgrad_dma(WgradArgs g)
+{
+    extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
+    int* const claimed = reinterpret_cast<int*>(smem + 2 * kBRing);
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) unsigned char*)(smem)));
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / kWN;
+    const int wn = wave % kWN;
+    const int n_mt = g.Mo / BM, n_nt = g.No / BN;
+    const int per_e = n_mt * n_nt;
+    const int total = per_e * g.E;
+
+    Lane ln;
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j) {
+        const int kr = 2 * (kCopies * wave + j) + lane / 32;
+        const int c = (lane & 31) ^ (4 * (kr & 3));
+        ln.krl[j] = kr;
+        ln.c16[j] = 16u * c;
+        ln.a_voff[j] = static_cast<uint32_t>(kr) * static_cast<uint32_t>(g.lda) * 2u + 16u * c;
+        ln.b_voff[j] = static_cast<uint32_t>(kr) * static_cast<uint32_t>(g.ldb) * 2u + 16u * c;
+    }
+    {
+        const int gq = lane >> 4, e4 = (lane >> 2) & 3, q = lane & 3;
+        const int kr = 8 * (gq >> 1) + e4;
+#pragma unroll
+        for (int i = 0; i < kTM; ++i) {
+            const int col = 32 * (kWM * i + wm) + 16 * (gq & 1) + 4 * q;
+            ln.a_base[i] = lds0 + kr * kRowBytes + 16 * ((col >> 3) ^ (4 * e4)) + 2 * (col & 7);
+            asm volatile("" : "+v"(ln.a_base[i]));
+        }
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            const int col = 32 * kTN * wn + 32 * j + 16 * (gq & 1) + 4 * q;
+            ln.b_base[j] = lds0 + kBRing + kr * kRowBytes + 16 * ((col >> 3) ^ (4 * e4)) + 2 * (col & 7);
+            asm volatile("" : "+v"(ln.b_base[j]));
+        }
+    }
+    Copy cp;
+    cp.a_lds = lds0 + kCopies * wave * 1024;
+    cp.b_lds = lds0 + kBRing + kCopies * wave * 1024;
+
+    const int xcd = blockIdx.x % kXcdCount;
+    const int blk = gridDim.x / kXcdCount;
+    int e = 0, m0 = 0, n0 = 0, KT = 0;
+    auto setup = [&](int t) {
+        e = t / per_e;
+        const int tl = t - e * per_e;
+        const int grp = tl / (kGroup * n_nt);
+        const int first = grp * kGroup;
+        const int gsz = min(kGroup, n_mt - first);
+        const int idx = tl - grp * kGroup * n_nt;
+        m0 = (first + idx % gsz) * BM;
+        n0 = (idx / gsz) * BN;
+        const int k_begin = g.offsets[e];
+        const int cnt = g.offsets[e + 1] - k_begin;
+        KT = max(kStages, (cnt + kStages * BK - 1) / (kStages * BK) * kStages);
+        cp.a = g.a + static_cast<int64_t>(k_begin) * g.lda + m0;
+        cp.b = g.b + static_cast<int64_t>(k_begin) * g.ldb + n0;
+        cp.rem = cnt;
+        cp.za = static_cast<uint32_t>(reinterpret_cast<const char*>(g.zero) - reinterpret_cast<const char*>(cp.a));
+        cp.zb = static_cast<uint32_t>(reinterpret_cast<const char*>(g.zero) - reinterpret_cast<const char*>(cp.b));
+#pragma unroll
+        for (int S = 0; S < kStages; ++S) {
+            copies<0, kStepCopies>(cp, ln, S);
+            advance(cp, g.lda, g.ldb);
+        }
+    };
+
+    int t = claim_task(claimed, g.task_ctr, xcd, blk, wave, lane);
+    if (t < total)
+        setup(t);
+    while (t < total) {
+        if (wave == 0) {
+            const int v = atomicAdd(&g.task_ctr[xcd], lane == 0 ? 1 : 0);
+            *claimed = __builtin_amdgcn_readfirstlane(v);
+        }
+        f32x16_t acc[kTM][kTN];
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+            for (int j = 0; j < kTN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[i][j][r] = 0.0f;
+        step_barrier<kTopWait>();
+        const int ci = __builtin_amdgcn_readfirstlane(*claimed);
+        const int t_next = ((ci / blk) * kXcdCount + xcd) * blk + ci % blk;
+        k_loop(acc, cp, ln, KT, g.lda, g.ldb);
+        const int de = e, dm0 = m0, dn0 = n0;
+        t = t_next;
+        // every wave is past its last read of this task's stages (and of the claim word)
+        __syncthreads();
+        if (t < total)
+            setup(t);
+        float* C = g.c + static_cast<int64_t>(de) * g.Mo * g.No;
+#pragma unroll
+        for (int i = 0; i < kTM; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = dm0 + 32 * (kWM * i + wm) + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                float* crow = C + static_cast<int64_t>(row) * g.No + dn0 + 32 * kTN * wn + (lane & 31);
+#pragma unroll
+                for (int j = 0; j < kTN; ++j)
+                    crow[32 * j] = acc[i][j][r];
+            }
+        }
+    }
+}
+
+}  // namespace tn
+
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* __restrict__ p, int n)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n)
+        p[i] = 0;
+}
+
 constexpr int kSmallThreads = 256;
 
 // w(p) = probs of the slot behind permuted row p (0 for rows past the valid ones).
@@ -468,10 +808,39 @@ hipError_t launch_dgrad_gate_up(const uint16_t* dgu, const uint16_t* wg, const u
     return launch_bwd<kEpiGateUp>(a, max_tiles * (H / BN), s);
 }
 
+bool wgrad_dma_fits(int64_t Mo, int64_t No) { return Mo % tn::BM == 0 && No % tn::BN == 0; }
+
+hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s)
+{
+    if (n <= 0)
+        return hipSuccess;
+    zero_i32_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s>>>(p, static_cast<int>(n));
+    return hipGetLastError();
+}
+
 hipError_t launch_wgrad(const uint16_t* a_rows, int64_t lda, const uint16_t* b_rows, int64_t ldb,
                         const int32_t* offsets, int64_t E, int64_t Mo, int64_t No, float* dw,
-                        hipStream_t s)
+                        const uint16_t* zero, int32_t* task_ctr, hipStream_t s)
 {
+    if (zero != nullptr && task_ctr != nullptr && wgrad_dma_fits(Mo, No)) {
+        static bool done[64] = {};
+        int dev = 0;
+        if (hipError_t e = hipGetDevice(&dev); e != hipSuccess)
+            return e;
+        if (dev >= 64 || !done[dev]) {
+            if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&tn::wgrad_dma),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                   tn::kSmemBytes);
+                e != hipSuccess)
+                return e;
+            if (dev < 64)
+                done[dev] = true;
+        }
+        tn::WgradArgs a{a_rows, b_rows, lda, ldb, offsets, zero, dw, static_cast<int>(E),
+                        static_cast<int>(Mo), static_cast<int>(No), task_ctr};
+        tn::wgrad_dma<<<dim3(device_info().cu_count), dim3(tn::kThreads), tn::kSmemBytes, s>>>(a);
+        return hipGetLastError();
+    }
     BwdArgs a{};
     a.a = a_rows;
     a.lda = lda;

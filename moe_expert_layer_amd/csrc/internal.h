@@ -184,10 +184,16 @@ hipError_t launch_dprobs(const float* partial, const int32_t* pos, float* dprobs
 hipError_t launch_dgrad_gate_up(const uint16_t* dgu, const uint16_t* wg, const uint16_t* wu,
                                 uint16_t* dx_perm, const MTile* tiles, const int32_t* tile_count,
                                 int64_t max_tiles, int64_t H, int64_t F, hipStream_t s);
-// dw[e] [Mo, No] (fp32) = sum over the rows p of expert e of a_rows[p, :Mo]^T b_rows[p, :No]
+// dw[e] [Mo, No] (fp32) = sum over the rows p of expert e of a_rows[p, :Mo]^T b_rows[p, :No].
+// With zero (>= 512 zero bytes at least one source row above the end of both sources, less than
+// 4 GiB above their starts) and task_ctr
+// (kXcdCount zeroed counters), Mo and No multiples of 256: the LDS-DMA kernel; otherwise the
+// register-staged one.
+bool wgrad_dma_fits(int64_t Mo, int64_t No);
 hipError_t launch_wgrad(const uint16_t* a_rows, int64_t lda, const uint16_t* b_rows, int64_t ldb,
                         const int32_t* offsets, int64_t E, int64_t Mo, int64_t No, float* dw,
-                        hipStream_t s);
+                        const uint16_t* zero, int32_t* task_ctr, hipStream_t s);
+hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s);
 // router.hip: top-k gate over float32 logits [T, E] (E <= 1024, k <= min(E, 64)).
 hipError_t launch_router(const float* logits, int64_t T, int64_t E, int64_t k, int32_t* ids,
                          float* probs, hipStream_t s);

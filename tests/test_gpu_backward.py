@@ -51,6 +51,10 @@ CASES = [
     (1, 128, 128, 2, 1, {}),
     # k = E: every token uses every expert
     (40, 128, 256, 3, 3, {}),
+    # H and F multiples of 256: the weight gradients take the LDS-DMA kernel (ragged expert rows,
+    # several row / column tiles)
+    (300, 256, 512, 5, 2, {}),
+    (260, 512, 256, 16, 4, dict(routing="zipf_gumbel", zipf_s=1.1, n_zero=4)),
 ]
 
 
@@ -77,18 +81,32 @@ def test_backward_is_deterministic():
                               y.view(np.uint32) if y.dtype == np.float32 else y)
 
 
-def test_backward_without_tokens_zeroes_the_weight_gradients():
-    inp = synth.make_layer(T=4, H=128, F=128, E=3, k=1, dtype="bf16", seed=2)
+@pytest.mark.parametrize("H,F", [(128, 128), (256, 512)])
+def test_backward_without_tokens_zeroes_the_weight_gradients(H, F):
+    inp = synth.make_layer(T=4, H=H, F=F, E=3, k=1, dtype="bf16", seed=2)
     d = dv.layer(inp)
     x = d.x[:0]
     ids = d.expert_ids[:0]
     probs = d.probs[:0]
-    dout = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    dout = torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
     dx, dwg, dwu, dwd, dprobs = mel.expert_backward(x, d.w_gate, d.w_up, d.w_down, ids, probs, dout)
     torch.cuda.synchronize()
-    assert dx.shape == (0, 128) and dprobs.shape == (0, 1)
+    assert dx.shape == (0, H) and dprobs.shape == (0, 1)
     for t in (dwg, dwu, dwd):
         assert torch.count_nonzero(t).item() == 0
+
+
+def test_backward_one_busy_expert():
+    """Every slot on expert 0: the later experts own no rows (their row range starts at the end of
+    the permuted rows) and get zero weight gradients."""
+    inp = synth.make_layer(T=200, H=256, F=256, E=4, k=1, dtype="bf16", seed=4)
+    inp.expert_ids[:] = 0
+    dout = synth.make_dout(inp)
+    gpu = _gpu_backward(inp, dout)
+    ref = oracle.backward(inp, dout)
+    _compare(gpu, ref)
+    for e in (1, 2, 3):
+        assert np.all(gpu[1][e] == 0) and np.all(gpu[2][e] == 0) and np.all(gpu[3][e] == 0)
 
 
 def test_backward_zero_probability_slot():
