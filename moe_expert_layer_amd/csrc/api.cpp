@@ -487,7 +487,7 @@ struct BackwardLayout {
     size_t x_perm = 0, dout_perm = 0, g = 0, u = 0, dgu = 0, hp = 0, dx_perm = 0;
     size_t wgrad_ctr = 0, zero = 0, total = 0;   // last: the zero rows sit above every source row
     int64_t max_tiles_r = 0, max_tiles_d = 0;
-    int bm_r = 0;
+    int bm_r = 0, bm_d = 0;
 };
 
 // g and u are recomputed with the plain grouped GEMM (K = H, N = F), whose row tiles are bm_r
@@ -512,9 +512,10 @@ BackwardLayout backward_layout(int64_t T, int64_t H, int64_t F, int64_t E, int64
     L.task_ctr = take(2 * kXcdCount * sizeof(int32_t));
     L.bm_r = bf16_row_tile(F, H);
     L.max_tiles_r = max_mtiles(M, E, 0, L.bm_r);
-    L.max_tiles_d = max_mtiles(M, E, 0, kBmBwd);
+    L.bm_d = dgrad_row_tile(M, H, F);
+    L.max_tiles_d = max_mtiles(M, E, 0, L.bm_d);
     L.tiles_r = take(sizeof(MTile) * n(L.max_tiles_r));
-    L.tiles_d = L.bm_r == kBmBwd ? L.tiles_r : take(sizeof(MTile) * n(L.max_tiles_d));
+    L.tiles_d = L.bm_r == L.bm_d ? L.tiles_r : take(sizeof(MTile) * n(L.max_tiles_d));
     L.prow = take(4 * n(M));
     L.partial = take(4 * n(M) * n(F / 64));
     L.x_perm = take(2 * n(M) * n(H));
@@ -524,7 +525,7 @@ BackwardLayout backward_layout(int64_t T, int64_t H, int64_t F, int64_t E, int64
     L.dgu = take(4 * n(M) * n(F));
     L.hp = take(2 * n(M) * n(F));
     L.dx_perm = take(2 * n(M) * n(H));
-    L.wgrad_ctr = take(3 * kXcdCount * sizeof(int32_t));
+    L.wgrad_ctr = take(5 * kXcdCount * sizeof(int32_t));     // 3 weight gradients, 2 dgrads
     // a weight-gradient copy source starts at most one row (plus its column offset) past the end
     // of its buffer; the zero rows must lie above every such start
     take(n(std::max(2 * H, 4 * F)));
@@ -620,7 +621,7 @@ MOE_API moe_status moe_expert_backward(const moe_problem* p, const void* x, cons
                                   tcount, nullptr, nullptr, 1, 0, task_ctr, status, false, s));
         if (L.tiles_d != L.tiles_r)
             LAUNCH(s, "build_tiles",
-                   launch_build_tiles(offsets, nullptr, E, E, M, M, kBmBwd, tiles_d, L.max_tiles_d,
+                   launch_build_tiles(offsets, nullptr, E, E, M, M, L.bm_d, tiles_d, L.max_tiles_d,
                                       tcount + 1, nullptr, nullptr, 1, 0, nullptr, status, false, s));
         const int32_t* tcount_d = L.tiles_d != L.tiles_r ? tcount + 1 : tcount;
         // g = x_perm Wg[e], u = x_perm Wu[e]: the plain grouped GEMM with K = H and N = F
@@ -630,10 +631,11 @@ MOE_API moe_status moe_expert_backward(const moe_problem* p, const void* x, cons
         LAUNCH(s, "row_probs", launch_row_probs(perm, probs, prow, M, s));
         LAUNCH(s, "dgrad_down",
                launch_dgrad_down(dout_perm, wd, g, u, prow, dgu, hp, partial, tiles_d, tcount_d,
-                                 L.max_tiles_d, H, F, s));
-        LAUNCH(s, "dprobs", launch_dprobs(partial, pos, dprobs, M, F, s));
+                                 L.max_tiles_d, M, H, F, wctr + 3 * kXcdCount, s));
+        LAUNCH(s, "dprobs", launch_dprobs(partial, pos, dprobs, M, dprobs_partials(M, H, F), s));
         LAUNCH(s, "dgrad_gate_up",
-               launch_dgrad_gate_up(dgu, wg, wu, dx_perm, tiles_d, tcount_d, L.max_tiles_d, H, F, s));
+               launch_dgrad_gate_up(dgu, wg, wu, dx_perm, tiles_d, tcount_d, L.max_tiles_d, M, H, F,
+                                    wctr + 4 * kXcdCount, s));
         LAUNCH(s, "unpermute", launch_unpermute(1, dx_perm, pos, nullptr, dx, T, k, M, H, s));
     }
     // weight gradients (an expert without rows gets zeros)

@@ -676,6 +676,327 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_dma(WgradArgs g)
 
 }  // namespace tn
 
+// ------------------------------------------------------------------------------------------------
+// dgrads with LDS DMA (256 x 256 tiles over the 256-row tile table; N a multiple of 256, K of 128).
+//
+// Both operands are K-contiguous rows (activation rows of the tile, weight rows of the expert), so
+// each K step of 32 moves [256 rows][32 k] of each into a four-stage ring: 64-byte rows, 16-byte
+// chunk c of row r at position c ^ ((r >> 2) & 3), so the 16 rows one fragment read serves per
+// chunk cover all 16 bank groups; fragments are single ds_read_b128.  Copy schedule, waits, task
+// claiming and the overlap of the next task's first copies with the epilogue are those of the
+// weight-gradient kernel above.  Rows past a partial tile's end re-read its last row and are never
+// stored.  The gate/up dgrad's weight source switches from Wg[e] to Wu[e] at k = F.
+namespace nt {
+
+constexpr int kWM = 4, kWN = 2, kTM = 2, kTN = 4;
+constexpr int kWaves = kWM * kWN;
+constexpr int kThreads = kWaves * 64;
+constexpr int BM = kWM * kTM * 32;                 // 256 rows (the tile table's height)
+constexpr int BN = kWN * kTN * 32;                 // 256 output columns
+constexpr int BK = 32;
+constexpr int kStages = 4;
+constexpr int kRowBytes = BK * 2;                  // 64
+constexpr int kStageBytes = BM * kRowBytes;        // 16 KiB per operand
+constexpr int kBRing = kStages * kStageBytes;      // A stages in the first 64 KiB, B in the next
+constexpr int kSmemBytes = 2 * kBRing + 256;
+constexpr int kCopies = kStageBytes / 1024 / kWaves;   // 2: rows 16 (2 wave + j) .. + 15
+constexpr int kStepCopies = 2 * kCopies;
+static_assert(BM == BN, "one stage layout serves both operands");
+
+using tn::step_barrier;
+
+struct Frags {
+    bf16x8_t a[kTM];
+    bf16x8_t b[kTN];
+};
+
+struct Copy {
+    const uint16_t* a;       // A at the next step's first k (row offsets in a_voff)
+    const uint16_t* b;       // the expert's weights at the next step's first k
+    const uint16_t* b1;      // segment 1's weights at k = kseg
+    int step, kseg_steps;    // next step to copy; the step at which the weights switch to b1
+    uint32_t a_lds, b_lds;
+};
+
+struct Lane {
+    uint32_t a_voff[kCopies], b_voff[kCopies];
+    uint32_t a_base[2], b_base[2];     // fragment-read addresses in stage 0 for sub-steps 0, 1
+};
+
+template <int C>
+__device__ __forceinline__ void copy_one(const Copy& cp, const Lane& ln, int SB)
+{
+    constexpr int j = C % kCopies;
+    if constexpr (C < kCopies)
+        lds_copy16(cp.a, ln.a_voff[j], cp.a_lds + SB * kStageBytes + j * 1024);
+    else
+        lds_copy16(cp.b, ln.b_voff[j], cp.b_lds + SB * kStageBytes + j * 1024);
+}
+
+__device__ __forceinline__ void advance(Copy& cp)
+{
+    cp.a += BK;
+    ++cp.step;
+    cp.b = cp.step == cp.kseg_steps ? cp.b1 : cp.b + BK;
+}
+
+// Read Q of sub-step KS of stage S: A block 0, weight blocks 0 .. kTN - 1, then A blocks 1 ...
+template <int S, int KS, int Q>
+__device__ __forceinline__ void read_one(Frags& f, const Lane& ln)
+{
+    using LdsV = const __attribute__((address_space(3))) bf16x8_t;
+    if constexpr (Q >= 1 && Q <= kTN) {
+        constexpr int j = Q - 1;
+        f.b[j] = *reinterpret_cast<LdsV*>(ln.b_base[KS] + S * kStageBytes + j * 32 * kRowBytes);
+    } else {
+        constexpr int i = Q == 0 ? 0 : Q - kTN;
+        f.a[i] = *reinterpret_cast<LdsV*>(ln.a_base[KS] + S * kStageBytes + i * kWM * 32 * kRowBytes);
+    }
+}
+
+template <int S, int KS, int Q0, int... Is>
+__device__ __forceinline__ void reads_impl(std::integer_sequence<int, Is...>, Frags& f, const Lane& ln)
+{
+    (read_one<S, KS, Q0 + Is>(f, ln), ...);
+}
+
+template <int S, int KS, int Q0, int Q1>
+__device__ __forceinline__ void reads(Frags& f, const Lane& ln)
+{
+    reads_impl<S, KS, Q0>(std::make_integer_sequence<int, Q1 - Q0>{}, f, ln);
+}
+
+template <int C0, int... Is>
+__device__ __forceinline__ void copies_impl(std::integer_sequence<int, Is...>, const Copy& cp,
+                                            const Lane& ln, int SB)
+{
+    (copy_one<C0 + Is>(cp, ln, SB), ...);
+}
+
+template <int C0, int C1>
+__device__ __forceinline__ void copies(const Copy& cp, const Lane& ln, int SB)
+{
+    copies_impl<C0>(std::make_integer_sequence<int, C1 - C0>{}, cp, ln, SB);
+}
+
+template <int NC, int SB, int SR, int KS, int M>
+__device__ __forceinline__ void slot(f32x16_t (&acc)[kTM][kTN], const Frags& use, Frags& load,
+                                     const Copy& cp, const Lane& ln)
+{
+    constexpr int NM = kTM * kTN, NR = kTM + kTN;
+    acc[M / kTN][M % kTN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(use.a[M / kTN], use.b[M % kTN],
+                                                                    acc[M / kTN][M % kTN], 0, 0, 0);
+    reads<SR, KS, M * NR / NM, (M + 1) * NR / NM>(load, ln);
+    copies<M * NC / NM, (M + 1) * NC / NM>(cp, ln, SB);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int NC, int SB, int SR, int KS, int... Ms>
+__device__ __forceinline__ void slots(std::integer_sequence<int, Ms...>, f32x16_t (&acc)[kTM][kTN],
+                                      const Frags& use, Frags& load, const Copy& cp, const Lane& ln)
+{
+    (slot<NC, SB, SR, KS, Ms>(acc, use, load, cp, ln), ...);
+}
+
+template <int S, bool kCopy, int W>
+__device__ __forceinline__ void k_step(f32x16_t (&acc)[kTM][kTN], Frags& f0, Frags& f1, Copy& cp,
+                                       const Lane& ln)
+{
+    __builtin_amdgcn_sched_barrier(0);
+    slots<0, 0, S, 1>(std::make_integer_sequence<int, kTM * kTN>{}, acc, f0, f1, cp, ln);
+    if constexpr (W >= 0)
+        step_barrier<W>();
+    __builtin_amdgcn_sched_barrier(0);
+    slots<kCopy ? kStepCopies : 0, S, (S + 1) % kStages, 0>(std::make_integer_sequence<int, kTM * kTN>{},
+                                                             acc, f1, f0, cp, ln);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kCopy)
+        advance(cp);
+}
+
+constexpr int kTopWait = 3 * kStepCopies;
+
+__device__ __forceinline__ void k_loop(f32x16_t (&acc)[kTM][kTN], Copy cp, const Lane& ln, int KT)
+{
+    constexpr int W = 2 * kStepCopies;
+    Frags f0, f1;
+    reads<0, 0, 0, kTM + kTN>(f0, ln);
+    for (int kt = 0; kt < KT - kStages; kt += kStages) {
+        k_step<0, true, W>(acc, f0, f1, cp, ln);
+        k_step<1, true, W>(acc, f0, f1, cp, ln);
+        k_step<2, true, W>(acc, f0, f1, cp, ln);
+        k_step<3, true, W>(acc, f0, f1, cp, ln);
+    }
+    k_step<0, false, W>(acc, f0, f1, cp, ln);
+    k_step<1, false, kStepCopies>(acc, f0, f1, cp, ln);
+    k_step<2, false, 0>(acc, f0, f1, cp, ln);
+    k_step<3, false, -1>(acc, f0, f1, cp, ln);
+}
+
+template <int kEpi>
+__global__ __launch_bounds__(kThreads, 1) void dgrad_dma(BwdArgs g, int32_t* __restrict__ task_ctr)
+{
+    extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
+    int* const claimed = reinterpret_cast<int*>(smem + 2 * kBRing);
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) unsigned char*)(smem)));
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / kWN;
+    const int wn = wave % kWN;
+    const int n_nt = g.N / BN;
+    const int total = *g.tile_count * n_nt;
+    const int KT = g.K / BK;
+
+    Lane ln;
+    {
+        const int r = lane & 31;
+        const int swz = (r >> 2) & 3;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int pos = (2 * ks + (lane >> 5)) ^ swz;
+            ln.a_base[ks] = lds0 + (32 * wm + r) * kRowBytes + 16 * pos;
+            ln.b_base[ks] = lds0 + kBRing + (32 * kTN * wn + r) * kRowBytes + 16 * pos;
+            asm volatile("" : "+v"(ln.a_base[ks]));
+            asm volatile("" : "+v"(ln.b_base[ks]));
+        }
+    }
+    uint32_t c16[kCopies];
+    int crow[kCopies];
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j) {
+        crow[j] = 16 * (kCopies * wave + j) + lane / 4;
+        c16[j] = 16u * static_cast<uint32_t>((lane & 3) ^ ((crow[j] >> 2) & 3));
+    }
+    Copy cp;
+    cp.a_lds = lds0 + kCopies * wave * 1024;
+    cp.b_lds = lds0 + kBRing + kCopies * wave * 1024;
+    cp.kseg_steps = g.kseg / BK;
+
+    const int xcd = blockIdx.x % kXcdCount;
+    const int blk = gridDim.x / kXcdCount;
+    MTile tile{};
+    int n0 = 0;
+    auto setup = [&](int t) {
+        int nt;
+        tile = decode_task(t, n_nt, g.tiles, nt);
+        n0 = nt * BN;
+        const int last = tile.row_end - 1;
+#pragma unroll
+        for (int j = 0; j < kCopies; ++j) {
+            const int row = min(tile.row_begin + crow[j], last);
+            ln.a_voff[j] = static_cast<uint32_t>(row) * static_cast<uint32_t>(g.lda) * 2u + c16[j];
+            ln.b_voff[j] = static_cast<uint32_t>(n0 + crow[j]) * static_cast<uint32_t>(g.ldb) * 2u + c16[j];
+        }
+        const int64_t eoff = static_cast<int64_t>(tile.expert) * g.b_estride;
+        cp.a = g.a;
+        cp.b = g.b0 + eoff;
+        cp.b1 = g.b1 + eoff;
+        cp.step = 0;
+#pragma unroll
+        for (int S = 0; S < kStages; ++S) {
+            copies<0, kStepCopies>(cp, ln, S);
+            advance(cp);
+        }
+    };
+
+    int t = claim_task(claimed, task_ctr, xcd, blk, wave, lane);
+    if (t < total)
+        setup(t);
+    while (t < total) {
+        if (wave == 0) {
+            const int v = atomicAdd(&task_ctr[xcd], lane == 0 ? 1 : 0);
+            *claimed = __builtin_amdgcn_readfirstlane(v);
+        }
+        f32x16_t acc[kTM][kTN];
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+            for (int j = 0; j < kTN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[i][j][r] = 0.0f;
+        step_barrier<kTopWait>();
+        const int ci = __builtin_amdgcn_readfirstlane(*claimed);
+        const int t_next = ((ci / blk) * kXcdCount + xcd) * blk + ci % blk;
+        k_loop(acc, cp, ln, KT);
+        const MTile done = tile;
+        const int dn0 = n0;
+        t = t_next;
+        __syncthreads();
+        if (t < total)
+            setup(t);
+        // Lane holds column lane % 32 of each 32 x 32 block, rows 8 (r / 4) + 4 (lane / 32) + r % 4.
+#pragma unroll
+        for (int i = 0; i < kTM; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int p = done.row_begin + 32 * (kWM * i + wm) + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const bool live = p < done.row_end;
+                const int col0 = dn0 + 32 * kTN * wn + (lane & 31);
+                if constexpr (kEpi == kEpiGateUp) {
+                    if (live) {
+                        uint16_t* C = static_cast<uint16_t*>(g.c) + static_cast<int64_t>(p) * g.N + col0;
+#pragma unroll
+                        for (int j = 0; j < kTN; ++j)
+                            C[32 * j] = f32_to_bf16(acc[i][j][r]);
+                    }
+                } else {
+                    const int F = g.N;
+                    float part = 0.0f;
+                    if (live) {
+                        const float w = g.prow[p];
+                        const int64_t rowF = static_cast<int64_t>(p) * F;
+                        uint16_t* dgu = static_cast<uint16_t*>(g.c) + 2 * rowF;
+#pragma unroll
+                        for (int j = 0; j < kTN; ++j) {
+                            const int f = col0 + 32 * j;
+                            const float gv = bf16_to_f32(g.g[rowF + f]);
+                            const float uv = bf16_to_f32(g.u[rowF + f]);
+                            const float d = acc[i][j][r];
+                            const float sg = sigmoid_f(gv);
+                            const float hv = gv * sg * uv;
+                            part += hv * d;
+                            const float dh = w * d;
+                            dgu[f] = f32_to_bf16(dh * uv * sg * (1.0f + gv * (1.0f - sg)));
+                            dgu[F + f] = f32_to_bf16(dh * gv * sg);
+                            g.hp[rowF + f] = f32_to_bf16(w * hv);
+                        }
+                    }
+#pragma unroll
+                    for (int off = 16; off >= 1; off >>= 1)
+                        part += __shfl_xor(part, off);
+                    if (live && (lane & 31) == 0)
+                        g.partial[static_cast<int64_t>(p) * (F / 128) + dn0 / 128 + wn] = part;
+                }
+            }
+        }
+    }
+}
+
+template <int kEpi>
+hipError_t launch(const BwdArgs& a, int32_t* task_ctr, hipStream_t s)
+{
+    static bool done[64] = {};
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess)
+        return e;
+    if (dev >= 64 || !done[dev]) {
+        if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dgrad_dma<kEpi>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
+            e != hipSuccess)
+            return e;
+        if (dev < 64)
+            done[dev] = true;
+    }
+    dgrad_dma<kEpi><<<dim3(device_info().cu_count), dim3(kThreads), kSmemBytes, s>>>(a, task_ctr);
+    return hipGetLastError();
+}
+
+}  // namespace nt
+
 __global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* __restrict__ p, int n)
 {
     const int i = blockIdx.x * 256 + threadIdx.x;
@@ -754,10 +1075,22 @@ hipError_t launch_row_probs(const int32_t* perm, const float* probs, float* prow
     return hipGetLastError();
 }
 
+bool dgrad_dma_fits(int64_t M, int64_t H, int64_t F)
+{
+    const int64_t row_elems = H > 2 * F ? H : 2 * F;          // the wider activation row (dout or dgu)
+    return H % nt::BN == 0 && F % nt::BN == 0 && H % (nt::kStages * nt::BK) == 0 &&
+           M * row_elems * 2 < (int64_t{1} << 32) && F * H * 2 < (int64_t{1} << 32);
+}
+
+int dgrad_row_tile(int64_t M, int64_t H, int64_t F) { return dgrad_dma_fits(M, H, F) ? nt::BM : BM; }
+
+int dprobs_partials(int64_t M, int64_t H, int64_t F) { return static_cast<int>(F / (dgrad_dma_fits(M, H, F) ? 128 : 64)); }
+
 hipError_t launch_dgrad_down(const uint16_t* dout_perm, const uint16_t* wd, const uint16_t* g,
                              const uint16_t* u, const float* prow, uint16_t* dgu, uint16_t* hp,
                              float* partial, const MTile* tiles, const int32_t* tile_count,
-                             int64_t max_tiles, int64_t H, int64_t F, hipStream_t s)
+                             int64_t max_tiles, int64_t M, int64_t H, int64_t F, int32_t* task_ctr,
+                             hipStream_t s)
 {
     BwdArgs a{};
     a.a = dout_perm;
@@ -775,22 +1108,25 @@ hipError_t launch_dgrad_down(const uint16_t* dout_perm, const uint16_t* wd, cons
     a.prow = prow;
     a.hp = hp;
     a.partial = partial;
+    if (dgrad_dma_fits(M, H, F))
+        return nt::launch<kEpiDown>(a, task_ctr, s);
     return launch_bwd<kEpiDown>(a, max_tiles * (F / BN), s);
 }
 
-hipError_t launch_dprobs(const float* partial, const int32_t* pos, float* dprobs, int64_t M, int64_t F,
+hipError_t launch_dprobs(const float* partial, const int32_t* pos, float* dprobs, int64_t M, int nq,
                          hipStream_t s)
 {
     if (M <= 0)
         return hipSuccess;
     dprobs_kernel<<<dim3(static_cast<unsigned>((M + kSmallThreads - 1) / kSmallThreads)),
-                    dim3(kSmallThreads), 0, s>>>(partial, pos, dprobs, M, static_cast<int>(F / 64));
+                    dim3(kSmallThreads), 0, s>>>(partial, pos, dprobs, M, nq);
     return hipGetLastError();
 }
 
 hipError_t launch_dgrad_gate_up(const uint16_t* dgu, const uint16_t* wg, const uint16_t* wu,
                                 uint16_t* dx_perm, const MTile* tiles, const int32_t* tile_count,
-                                int64_t max_tiles, int64_t H, int64_t F, hipStream_t s)
+                                int64_t max_tiles, int64_t M, int64_t H, int64_t F, int32_t* task_ctr,
+                                hipStream_t s)
 {
     BwdArgs a{};
     a.a = dgu;
@@ -805,6 +1141,8 @@ hipError_t launch_dgrad_gate_up(const uint16_t* dgu, const uint16_t* wg, const u
     a.tiles = tiles;
     a.tile_count = tile_count;
     a.c = dx_perm;
+    if (dgrad_dma_fits(M, H, F))
+        return nt::launch<kEpiGateUp>(a, task_ctr, s);
     return launch_bwd<kEpiGateUp>(a, max_tiles * (H / BN), s);
 }
 

@@ -167,23 +167,31 @@ int mx_row_tile(int64_t H, int64_t F);
 int mx_fc2_cols_per_tile(int64_t H, int64_t F);
 // gemm_bwd.hip: the backward's grouped GEMMs (bf16, 128-row tiles; H and F multiples of 128).
 bool bwd_supported(int64_t H, int64_t F);
-constexpr int kBmBwd = 128;
 // prow[p] = probs[perm[p]]
 hipError_t launch_row_probs(const int32_t* perm, const float* probs, float* prow, int64_t M,
                             hipStream_t s);
+// The dgrads run on LDS DMA with 256-row tiles when dgrad_dma_fits (H, F multiples of 256, 32-bit
+// row offsets), else register-staged with 128-row tiles; dgrad_row_tile gives the tile table's
+// height they need and dprobs_partials the partial sums per row (F / 128 or F / 64).
+bool dgrad_dma_fits(int64_t M, int64_t H, int64_t F);
+int dgrad_row_tile(int64_t M, int64_t H, int64_t F);
+int dprobs_partials(int64_t M, int64_t H, int64_t F);
 // d = dout_perm Wd^T with the SwiGLU backward in the epilogue: dgu [M, 2F] = [dg | du], hp [M, F]
-// = w h, partial [M, F / 64] (per 64 columns: sum of h d)
+// = w h, partial [M, dprobs_partials] (sums of h d over consecutive column groups).  task_ctr:
+// kXcdCount zeroed counters (used by the DMA kernel).
 hipError_t launch_dgrad_down(const uint16_t* dout_perm, const uint16_t* wd, const uint16_t* g,
                              const uint16_t* u, const float* prow, uint16_t* dgu, uint16_t* hp,
                              float* partial, const MTile* tiles, const int32_t* tile_count,
-                             int64_t max_tiles, int64_t H, int64_t F, hipStream_t s);
-// dprobs[s] = sum of partial[pos[s]][0 .. F / 64)
-hipError_t launch_dprobs(const float* partial, const int32_t* pos, float* dprobs, int64_t M,
-                         int64_t F, hipStream_t s);
+                             int64_t max_tiles, int64_t M, int64_t H, int64_t F, int32_t* task_ctr,
+                             hipStream_t s);
+// dprobs[s] = sum of partial[pos[s]][0 .. nq)
+hipError_t launch_dprobs(const float* partial, const int32_t* pos, float* dprobs, int64_t M, int nq,
+                         hipStream_t s);
 // dx_perm = dg Wg^T + du Wu^T
 hipError_t launch_dgrad_gate_up(const uint16_t* dgu, const uint16_t* wg, const uint16_t* wu,
                                 uint16_t* dx_perm, const MTile* tiles, const int32_t* tile_count,
-                                int64_t max_tiles, int64_t H, int64_t F, hipStream_t s);
+                                int64_t max_tiles, int64_t M, int64_t H, int64_t F, int32_t* task_ctr,
+                                hipStream_t s);
 // dw[e] [Mo, No] (fp32) = sum over the rows p of expert e of a_rows[p, :Mo]^T b_rows[p, :No].
 // With zero (>= 512 zero bytes at least one source row above the end of both sources, less than
 // 4 GiB above their starts) and task_ctr
