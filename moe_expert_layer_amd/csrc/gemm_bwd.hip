@@ -928,48 +928,82 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_dma(BwdArgs g, int32_t* __r
         if (t < total)
             setup(t);
         // Lane holds column lane % 32 of each 32 x 32 block, rows 8 (r / 4) + 4 (lane / 32) + r % 4.
+        const int col0 = dn0 + 32 * kTN * wn + (lane & 31);
 #pragma unroll
         for (int i = 0; i < kTM; ++i) {
             __builtin_amdgcn_sched_barrier(0);
+            const int pbase = done.row_begin + 32 * (kWM * i + wm) + 4 * (lane >> 5);
+            if constexpr (kEpi == kEpiGateUp) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int p = done.row_begin + 32 * (kWM * i + wm) + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const bool live = p < done.row_end;
-                const int col0 = dn0 + 32 * kTN * wn + (lane & 31);
-                if constexpr (kEpi == kEpiGateUp) {
-                    if (live) {
+                for (int r = 0; r < 16; ++r) {
+                    const int p = pbase + 8 * (r >> 2) + (r & 3);
+                    if (p < done.row_end) {
                         uint16_t* C = static_cast<uint16_t*>(g.c) + static_cast<int64_t>(p) * g.N + col0;
 #pragma unroll
                         for (int j = 0; j < kTN; ++j)
                             C[32 * j] = f32_to_bf16(acc[i][j][r]);
                     }
-                } else {
-                    const int F = g.N;
-                    float part = 0.0f;
-                    if (live) {
-                        const float w = g.prow[p];
-                        const int64_t rowF = static_cast<int64_t>(p) * F;
-                        uint16_t* dgu = static_cast<uint16_t*>(g.c) + 2 * rowF;
+                }
+            } else {
+                const int F = g.N;
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    float part[4];
+                    // rows 8 rb + .. + 3 of the lane: every g, u and weight they need is loaded before
+                    // any is used (rows past the tile's end read its last row and store nothing)
+                    uint16_t gq[4][kTN], uq[4][kTN];
+                    float wq[4];
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int pc = min(pbase + 8 * rb + rr, done.row_end - 1);
+                        const int64_t rowF = static_cast<int64_t>(pc) * F;
+                        wq[rr] = g.prow[pc];
 #pragma unroll
                         for (int j = 0; j < kTN; ++j) {
-                            const int f = col0 + 32 * j;
-                            const float gv = bf16_to_f32(g.g[rowF + f]);
-                            const float uv = bf16_to_f32(g.u[rowF + f]);
-                            const float d = acc[i][j][r];
-                            const float sg = sigmoid_f(gv);
-                            const float hv = gv * sg * uv;
-                            part += hv * d;
-                            const float dh = w * d;
-                            dgu[f] = f32_to_bf16(dh * uv * sg * (1.0f + gv * (1.0f - sg)));
-                            dgu[F + f] = f32_to_bf16(dh * gv * sg);
-                            g.hp[rowF + f] = f32_to_bf16(w * hv);
+                            gq[rr][j] = g.g[rowF + col0 + 32 * j];
+                            uq[rr][j] = g.u[rowF + col0 + 32 * j];
                         }
                     }
 #pragma unroll
-                    for (int off = 16; off >= 1; off >>= 1)
-                        part += __shfl_xor(part, off);
-                    if (live && (lane & 31) == 0)
-                        g.partial[static_cast<int64_t>(p) * (F / 128) + dn0 / 128 + wn] = part;
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int r = 4 * rb + rr;
+                        const int p = pbase + 8 * rb + rr;
+                        const bool live = p < done.row_end;   // r = 4 rb + rr: row 8 rb + rr
+                        const int64_t rowF = static_cast<int64_t>(p) * F;
+                        uint16_t* dgu = static_cast<uint16_t*>(g.c) + 2 * rowF;
+                        float pt = 0.0f;
+#pragma unroll
+                        for (int j = 0; j < kTN; ++j) {
+                            const int f = col0 + 32 * j;
+                            const float gv = bf16_to_f32(gq[rr][j]);
+                            const float uv = bf16_to_f32(uq[rr][j]);
+                            const float d = acc[i][j][r];
+                            const float sg = sigmoid_f(gv);
+                            const float hv = gv * sg * uv;
+                            pt += hv * d;
+                            const float dh = wq[rr] * d;
+                            if (live) {
+                                dgu[f] = f32_to_bf16(dh * uv * sg * (1.0f + gv * (1.0f - sg)));
+                                dgu[F + f] = f32_to_bf16(dh * gv * sg);
+                                g.hp[rowF + f] = f32_to_bf16(wq[rr] * hv);
+                            }
+                        }
+                        part[rr] = pt;
+                    }
+                    // each row's sum over the wave's 128 columns (32 lanes hold one row each)
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+                        for (int off = 16; off >= 1; off >>= 1)
+                            part[rr] += __shfl_xor(part[rr], off);
+                    if ((lane & 31) == 0) {
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) {
+                            const int p = pbase + 8 * rb + rr;
+                            if (p < done.row_end)
+                                g.partial[static_cast<int64_t>(p) * (F / 128) + dn0 / 128 + wn] = part[rr];
+                        }
+                    }
                 }
             }
         }
