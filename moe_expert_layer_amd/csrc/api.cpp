@@ -524,7 +524,7 @@ BackwardLayout backward_layout(int64_t T, int64_t H, int64_t F, int64_t E, int64
     L.u = take(2 * n(M) * n(F));
     L.dgu = take(4 * n(M) * n(F));
     L.hp = take(2 * n(M) * n(F));
-    L.dx_perm = take(2 * n(M) * n(H));
+    L.dx_perm = take(2 * 4 * n(M) * n(H));   // each slot's dx row: two fp32 parts, or bf16
     L.wgrad_ctr = take(5 * kXcdCount * sizeof(int32_t));     // 3 weight gradients, 2 dgrads
     // a weight-gradient copy source starts at most one row (plus its column offset) past the end
     // of its buffer; the zero rows must lie above every such start
@@ -611,7 +611,7 @@ MOE_API moe_status moe_expert_backward(const moe_problem* p, const void* x, cons
         MTile* tiles_d = at<MTile>(ws, L.tiles_d);
         uint16_t* g = at<uint16_t>(ws, L.g);
         uint16_t* u = at<uint16_t>(ws, L.u);
-        uint16_t* dx_perm = at<uint16_t>(ws, L.dx_perm);
+        void* dx_rows = at<void>(ws, L.dx_perm);
         float* prow = at<float>(ws, L.prow);
         float* partial = at<float>(ws, L.partial);
         LAUNCH(s, "permute", launch_permute(x, pos, x_perm, T, k, M, H * 2, s));
@@ -634,9 +634,11 @@ MOE_API moe_status moe_expert_backward(const moe_problem* p, const void* x, cons
                                  L.max_tiles_d, M, H, F, wctr + 3 * kXcdCount, s));
         LAUNCH(s, "dprobs", launch_dprobs(partial, pos, dprobs, M, dprobs_partials(M, H, F), s));
         LAUNCH(s, "dgrad_gate_up",
-               launch_dgrad_gate_up(dgu, wg, wu, dx_perm, tiles_d, tcount_d, L.max_tiles_d, M, H, F,
+               launch_dgrad_gate_up(dgu, wg, wu, dx_rows, tiles_d, tcount_d, L.max_tiles_d, M, H, F,
                                     wctr + 4 * kXcdCount, s));
-        LAUNCH(s, "unpermute", launch_unpermute(1, dx_perm, pos, nullptr, dx, T, k, M, H, s));
+        LAUNCH(s, "sum_slots",
+               launch_sum_slot_rows(dx_rows, dgrad_gate_up_parts(M, H, F), pos,
+                                    static_cast<uint16_t*>(dx), T, k, M, H, s));
     }
     // weight gradients (an expert without rows gets zeros)
     LAUNCH(s, "wgrad_down",

@@ -833,7 +833,10 @@ __device__ __forceinline__ void k_loop(f32x16_t (&acc)[kTM][kTN], Copy cp, const
     k_step<3, false, -1>(acc, f0, f1, cp, ln);
 }
 
-template <int kEpi>
+// kParts (gate/up only): 1, one pass over k < 2F storing bf16 rows; 2, tasks [0, T0) take dg Wg^T
+// and tasks [T0, 2 T0) du Wu^T, each storing an fp32 part (twice the tasks, for problems with
+// too few 256 x 256 tiles to keep every CU busy to the end).
+template <int kEpi, int kParts>
 __global__ __launch_bounds__(kThreads, 1) void dgrad_dma(BwdArgs g, int32_t* __restrict__ task_ctr)
 {
     extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
@@ -846,8 +849,9 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_dma(BwdArgs g, int32_t* __r
     const int wm = wave / kWN;
     const int wn = wave % kWN;
     const int n_nt = g.N / BN;
-    const int total = *g.tile_count * n_nt;
-    const int KT = g.K / BK;
+    const int T0 = *g.tile_count * n_nt;
+    const int total = kParts * T0;
+    const int KT = (kParts == 2 ? g.kseg : g.K) / BK;
 
     Lane ln;
     {
@@ -872,15 +876,16 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_dma(BwdArgs g, int32_t* __r
     Copy cp;
     cp.a_lds = lds0 + kCopies * wave * 1024;
     cp.b_lds = lds0 + kBRing + kCopies * wave * 1024;
-    cp.kseg_steps = g.kseg / BK;
+    cp.kseg_steps = kParts == 2 ? KT : g.kseg / BK;      // parts: one weight matrix per task
 
     const int xcd = blockIdx.x % kXcdCount;
     const int blk = gridDim.x / kXcdCount;
     MTile tile{};
-    int n0 = 0;
+    int n0 = 0, part = 0;
     auto setup = [&](int t) {
         int nt;
-        tile = decode_task(t, n_nt, g.tiles, nt);
+        part = t >= T0 ? 1 : 0;
+        tile = decode_task(t - part * T0, n_nt, g.tiles, nt);
         n0 = nt * BN;
         const int last = tile.row_end - 1;
 #pragma unroll
@@ -890,8 +895,8 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_dma(BwdArgs g, int32_t* __r
             ln.b_voff[j] = static_cast<uint32_t>(n0 + crow[j]) * static_cast<uint32_t>(g.ldb) * 2u + c16[j];
         }
         const int64_t eoff = static_cast<int64_t>(tile.expert) * g.b_estride;
-        cp.a = g.a;
-        cp.b = g.b0 + eoff;
+        cp.a = g.a + part * g.kseg;
+        cp.b = (part ? g.b1 : g.b0) + eoff;
         cp.b1 = g.b1 + eoff;
         cp.step = 0;
 #pragma unroll
@@ -922,7 +927,7 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_dma(BwdArgs g, int32_t* __r
         const int t_next = ((ci / blk) * kXcdCount + xcd) * blk + ci % blk;
         k_loop(acc, cp, ln, KT);
         const MTile done = tile;
-        const int dn0 = n0;
+        const int dn0 = n0, dpart = part;
         t = t_next;
         __syncthreads();
         if (t < total)
@@ -938,10 +943,17 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_dma(BwdArgs g, int32_t* __r
                 for (int r = 0; r < 16; ++r) {
                     const int p = pbase + 8 * (r >> 2) + (r & 3);
                     if (p < done.row_end) {
-                        uint16_t* C = static_cast<uint16_t*>(g.c) + static_cast<int64_t>(p) * g.N + col0;
+                        if constexpr (kParts == 2) {
+                            float* C = static_cast<float*>(g.c) + (static_cast<int64_t>(dpart) * g.Mo + p) * g.N + col0;
 #pragma unroll
-                        for (int j = 0; j < kTN; ++j)
-                            C[32 * j] = f32_to_bf16(acc[i][j][r]);
+                            for (int j = 0; j < kTN; ++j)
+                                C[32 * j] = acc[i][j][r];
+                        } else {
+                            uint16_t* C = static_cast<uint16_t*>(g.c) + static_cast<int64_t>(p) * g.N + col0;
+#pragma unroll
+                            for (int j = 0; j < kTN; ++j)
+                                C[32 * j] = f32_to_bf16(acc[i][j][r]);
+                        }
                     }
                 }
             } else {
@@ -1010,7 +1022,7 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_dma(BwdArgs g, int32_t* __r
     }
 }
 
-template <int kEpi>
+template <int kEpi, int kParts>
 hipError_t launch(const BwdArgs& a, int32_t* task_ctr, hipStream_t s)
 {
     static bool done[64] = {};
@@ -1018,14 +1030,14 @@ hipError_t launch(const BwdArgs& a, int32_t* task_ctr, hipStream_t s)
     if (hipError_t e = hipGetDevice(&dev); e != hipSuccess)
         return e;
     if (dev >= 64 || !done[dev]) {
-        if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dgrad_dma<kEpi>),
+        if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dgrad_dma<kEpi, kParts>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, kSmemBytes);
             e != hipSuccess)
             return e;
         if (dev < 64)
             done[dev] = true;
     }
-    dgrad_dma<kEpi><<<dim3(device_info().cu_count), dim3(kThreads), kSmemBytes, s>>>(a, task_ctr);
+    dgrad_dma<kEpi, kParts><<<dim3(device_info().cu_count), dim3(kThreads), kSmemBytes, s>>>(a, task_ctr);
     return hipGetLastError();
 }
 
@@ -1039,6 +1051,46 @@ __global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* __restrict__ p, 
 }
 
 constexpr int kSmallThreads = 256;
+
+// dx[t] = sum over j (in order) of row pos[t k + j]: fp32 rows as part0 + part1 (part1 may be
+// null), or bf16 rows (kParts 0).  One thread per (token, 4 columns).
+template <int kParts>
+__global__ __launch_bounds__(kSmallThreads) void sum_slot_rows_kernel(
+    const void* __restrict__ rows, const int32_t* __restrict__ pos, uint2* __restrict__ dx, int k,
+    int64_t M, uint32_t row_vecs, uint32_t total)
+{
+    const uint32_t i = blockIdx.x * kSmallThreads + threadIdx.x;
+    if (i >= total)
+        return;
+    const uint32_t t = i / row_vecs;
+    const uint32_t c = i - t * row_vecs;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+        const int64_t p = pos[static_cast<int64_t>(t) * k + j];
+        if (p < 0 || p >= M)
+            continue;
+        float4 v;
+        if constexpr (kParts == 0) {
+            const uint2 b = static_cast<const uint2*>(rows)[p * row_vecs + c];
+            v = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u),
+                            __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xffff0000u));
+        } else {
+            v = static_cast<const float4*>(rows)[p * row_vecs + c];
+            if constexpr (kParts == 2) {
+                const float4 w = static_cast<const float4*>(rows)[(M + p) * row_vecs + c];
+                v.x += w.x;
+                v.y += w.y;
+                v.z += w.z;
+                v.w += w.w;
+            }
+        }
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    dx[i] = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+}
 
 // w(p) = probs of the slot behind permuted row p (0 for rows past the valid ones).
 __global__ __launch_bounds__(kSmallThreads) void row_probs_kernel(const int32_t* __restrict__ perm,
@@ -1143,7 +1195,7 @@ hipError_t launch_dgrad_down(const uint16_t* dout_perm, const uint16_t* wd, cons
     a.hp = hp;
     a.partial = partial;
     if (dgrad_dma_fits(M, H, F))
-        return nt::launch<kEpiDown>(a, task_ctr, s);
+        return nt::launch<kEpiDown, 1>(a, task_ctr, s);
     return launch_bwd<kEpiDown>(a, max_tiles * (F / BN), s);
 }
 
@@ -1157,8 +1209,18 @@ hipError_t launch_dprobs(const float* partial, const int32_t* pos, float* dprobs
     return hipGetLastError();
 }
 
+// Split into two parts when one pass has fewer than 3 tasks per CU (the last round of equal tasks
+// would leave most CUs idle); the fp32 parts cost their extra traffic only then.
+int dgrad_gate_up_parts(int64_t M, int64_t H, int64_t F)
+{
+    if (!dgrad_dma_fits(M, H, F))
+        return 1;
+    const int64_t tasks = ceil_div(M, nt::BM) * (H / nt::BN);
+    return tasks < 3 * int64_t{device_info().cu_count} ? 2 : 1;
+}
+
 hipError_t launch_dgrad_gate_up(const uint16_t* dgu, const uint16_t* wg, const uint16_t* wu,
-                                uint16_t* dx_perm, const MTile* tiles, const int32_t* tile_count,
+                                void* dx_rows, const MTile* tiles, const int32_t* tile_count,
                                 int64_t max_tiles, int64_t M, int64_t H, int64_t F, int32_t* task_ctr,
                                 hipStream_t s)
 {
@@ -1172,12 +1234,34 @@ hipError_t launch_dgrad_gate_up(const uint16_t* dgu, const uint16_t* wg, const u
     a.kseg = static_cast<int>(F);
     a.K = static_cast<int>(2 * F);
     a.N = static_cast<int>(H);
+    a.Mo = static_cast<int>(M);
     a.tiles = tiles;
     a.tile_count = tile_count;
-    a.c = dx_perm;
+    a.c = dx_rows;
+    if (dgrad_gate_up_parts(M, H, F) == 2)
+        return nt::launch<kEpiGateUp, 2>(a, task_ctr, s);
     if (dgrad_dma_fits(M, H, F))
-        return nt::launch<kEpiGateUp>(a, task_ctr, s);
+        return nt::launch<kEpiGateUp, 1>(a, task_ctr, s);
     return launch_bwd<kEpiGateUp>(a, max_tiles * (H / BN), s);
+}
+
+hipError_t launch_sum_slot_rows(const void* rows, int parts, const int32_t* pos, uint16_t* dx,
+                                int64_t T, int64_t k, int64_t M, int64_t H, hipStream_t s)
+{
+    const int64_t total = T * (H / 4);
+    if (total <= 0)
+        return hipSuccess;
+    if (total >= (int64_t{1} << 31))
+        return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>((total + kSmallThreads - 1) / kSmallThreads)), block(kSmallThreads);
+    const int kk = static_cast<int>(k);
+    const uint32_t rv = static_cast<uint32_t>(H / 4), tt = static_cast<uint32_t>(total);
+    uint2* out = reinterpret_cast<uint2*>(dx);
+    if (parts == 2)
+        sum_slot_rows_kernel<2><<<grid, block, 0, s>>>(rows, pos, out, kk, M, rv, tt);
+    else
+        sum_slot_rows_kernel<0><<<grid, block, 0, s>>>(rows, pos, out, kk, M, rv, tt);
+    return hipGetLastError();
 }
 
 bool wgrad_dma_fits(int64_t Mo, int64_t No) { return Mo % tn::BM == 0 && No % tn::BN == 0; }

@@ -119,7 +119,6 @@ hipError_t launch_build_tiles(const int32_t* offsets, const int32_t* group_exper
 // Slots whose pos is outside [0, M) are skipped.
 hipError_t launch_permute(const void* x, const int32_t* pos, void* x_perm, int64_t T, int64_t k,
                           int64_t M, int64_t row_bytes, hipStream_t s);
-// probs null: every weight is 1 (the plain sum of a token's k rows).
 hipError_t launch_unpermute(int dtype, const void* y_perm, const int32_t* pos, const float* probs,
                             void* out, int64_t T, int64_t k, int64_t M, int64_t H, hipStream_t s);
 
@@ -187,11 +186,18 @@ hipError_t launch_dgrad_down(const uint16_t* dout_perm, const uint16_t* wd, cons
 // dprobs[s] = sum of partial[pos[s]][0 .. nq)
 hipError_t launch_dprobs(const float* partial, const int32_t* pos, float* dprobs, int64_t M, int nq,
                          hipStream_t s);
-// dx_perm = dg Wg^T + du Wu^T
+// Each slot's dx row dg Wg^T + du Wu^T: with dgrad_gate_up_parts(M, H, F) == 2, as two fp32 parts
+// [M, H] at dx_rows (dg Wg^T) and dx_rows + M H floats (du Wu^T), computed as separate tasks for an
+// even spread over the CUs when one pass has few tasks; otherwise as bf16 rows [M, H].
+int dgrad_gate_up_parts(int64_t M, int64_t H, int64_t F);
 hipError_t launch_dgrad_gate_up(const uint16_t* dgu, const uint16_t* wg, const uint16_t* wu,
-                                uint16_t* dx_perm, const MTile* tiles, const int32_t* tile_count,
+                                void* dx_rows, const MTile* tiles, const int32_t* tile_count,
                                 int64_t max_tiles, int64_t M, int64_t H, int64_t F, int32_t* task_ctr,
                                 hipStream_t s);
+// dx[t] = bf16(sum over j in order of row pos[t k + j]), the rows as launch_dgrad_gate_up left them
+// (parts 2: fp32 part 0 + part 1 per slot; otherwise bf16); slots with pos outside [0, M) skipped.
+hipError_t launch_sum_slot_rows(const void* rows, int parts, const int32_t* pos, uint16_t* dx,
+                                int64_t T, int64_t k, int64_t M, int64_t H, hipStream_t s);
 // dw[e] [Mo, No] (fp32) = sum over the rows p of expert e of a_rows[p, :Mo]^T b_rows[p, :No].
 // With zero (>= 512 zero bytes at least one source row above the end of both sources, less than
 // 4 GiB above their starts) and task_ctr

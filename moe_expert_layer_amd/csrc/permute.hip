@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void unpermute_bf16_flat_kernel(
     const uint32_t t = i / row_vecs;
     const uint32_t c = i - t * row_vecs;
     const int32_t* tp = pos + static_cast<int64_t>(t) * k;
-    const float* pp = probs != nullptr ? probs + static_cast<int64_t>(t) * k : nullptr;
+    const float* pp = probs + static_cast<int64_t>(t) * k;
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void unpermute_bf16_flat_kernel(
         for (int j = 0; j < 8; ++j) {
             const int64_t p = j0 + j < k ? tp[j0 + j] : -1;
             ok[j] = p >= 0 && p < M;
-            w[j] = ok[j] ? (probs != nullptr ? pp[j0 + j] : 1.0f) : 0.0f;
+            w[j] = ok[j] ? pp[j0 + j] : 0.0f;
             v[j] = ok[j] ? y[p * row_vecs + c] : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void unpermute_bf16_kernel(
 {
     for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
         const int32_t* tp = pos + t * k;
-        const float* pp = probs != nullptr ? probs + t * k : nullptr;
+        const float* pp = probs + t * k;
         for (int64_t c = threadIdx.x; c < row_vecs; c += kThreads) {
             float acc[8];
 #pragma unroll
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void unpermute_bf16_kernel(
                 const int64_t p = tp[j];
                 if (p < 0 || p >= M)
                     continue;
-                const float w = pp != nullptr ? pp[j] : 1.0f;
+                const float w = pp[j];
                 const uint4 v = y[p * row_vecs + c];
                 const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -154,14 +154,14 @@ __global__ __launch_bounds__(kThreads) void unpermute_f32_kernel(
 {
     for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
         const int32_t* tp = pos + t * k;
-        const float* pp = probs != nullptr ? probs + t * k : nullptr;
+        const float* pp = probs + t * k;
         for (int64_t c = threadIdx.x; c < row_vecs; c += kThreads) {
             float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
             for (int j = 0; j < k; ++j) {
                 const int64_t p = tp[j];
                 if (p < 0 || p >= M)
                     continue;
-                const float w = pp != nullptr ? pp[j] : 1.0f;
+                const float w = pp[j];
                 const float4 v = y[p * row_vecs + c];
                 acc.x = fmaf(w, v.x, acc.x);
                 acc.y = fmaf(w, v.y, acc.y);
