@@ -134,9 +134,10 @@ moe_status moe_backward_workspace_size(const moe_problem* p, size_t* bytes /* ho
  *   x [T,H], w_gate / w_up [E,H,F], w_down [E,F,H] bfloat16; expert_ids [T,k] int32;
  *   probs [T,k] float32; dout [T,H] bfloat16
  *   dx [T,H] bfloat16; dw_gate / dw_up [E,H,F], dw_down [E,F,H], dprobs [T,k] float32
- * g and u are recomputed from x (nothing is kept from a forward call).  g, u, dg, du, probs * h and
- * each slot's dx row are rounded to bfloat16; every gradient element is one fp32 sum in a fixed
- * order (no float atomics), so the results are deterministic.  Experts that receive no slot get zero
+ * g and u are recomputed from x (nothing is kept from a forward call).  g, u, dg, du and probs * h
+ * are rounded to bfloat16, and so is each slot's dx row, except on problems with few 256-row tiles,
+ * where dg Wg^T and du Wu^T run as separate tasks and stay fp32 until the per-token sum.  Every
+ * gradient element is an fp32 sum in a fixed order (no float atomics): deterministic.  Experts that receive no slot get zero
  * weight gradients; slots with an out-of-range id are skipped (dprobs 0) and flag the status word. */
 moe_status moe_expert_backward(const moe_problem* p, const void* x, const void* w_gate,
                                const void* w_up, const void* w_down, const int32_t* expert_ids,

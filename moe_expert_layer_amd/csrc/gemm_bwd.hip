@@ -447,7 +447,12 @@ __device__ __forceinline__ void read_one(Frags& f, const Lane& ln)
     constexpr bool isB = Q >= kB0 && Q < kB1;
     constexpr int h = Q % 2;
     constexpr int idx = isB ? (Q - kB0) / 2 : (Q < kB0 ? 0 : 1 + (Q - kB1) / 2);
-    const uint32_t p = (isB ? ln.b_base[idx] : ln.a_base[idx]) + S * kStageBytes + (16 * KS + 4 * h) * kRowBytes;
+    uint32_t base;
+    if constexpr (isB)
+        base = ln.b_base[idx];
+    else
+        base = ln.a_base[idx];
+    const uint32_t p = base + S * kStageBytes + (16 * KS + 4 * h) * kRowBytes;
     const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4_t*>(p));
     if constexpr (isB) {
         if constexpr (h == 0)
@@ -1052,44 +1057,66 @@ __global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* __restrict__ p, 
 
 constexpr int kSmallThreads = 256;
 
-// dx[t] = sum over j (in order) of row pos[t k + j]: fp32 rows as part0 + part1 (part1 may be
-// null), or bf16 rows (kParts 0).  One thread per (token, 4 columns).
+// dx[t] = sum over j (in order) of row pos[t k + j]: fp32 rows as part 0 + part 1 (kParts 2) or
+// bf16 rows (kParts 0).  One thread per (token, 16 bytes of each source row: 8 bf16 or 4 fp32
+// columns); bf16 rows are loaded 8 at a time before any is added.
 template <int kParts>
 __global__ __launch_bounds__(kSmallThreads) void sum_slot_rows_kernel(
-    const void* __restrict__ rows, const int32_t* __restrict__ pos, uint2* __restrict__ dx, int k,
+    const void* __restrict__ rows, const int32_t* __restrict__ pos, uint16_t* __restrict__ dx, int k,
     int64_t M, uint32_t row_vecs, uint32_t total)
 {
+    constexpr int kCols = kParts == 0 ? 8 : 4;
     const uint32_t i = blockIdx.x * kSmallThreads + threadIdx.x;
     if (i >= total)
         return;
     const uint32_t t = i / row_vecs;
     const uint32_t c = i - t * row_vecs;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-        const int64_t p = pos[static_cast<int64_t>(t) * k + j];
-        if (p < 0 || p >= M)
-            continue;
-        float4 v;
-        if constexpr (kParts == 0) {
-            const uint2 b = static_cast<const uint2*>(rows)[p * row_vecs + c];
-            v = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u),
-                            __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xffff0000u));
-        } else {
-            v = static_cast<const float4*>(rows)[p * row_vecs + c];
-            if constexpr (kParts == 2) {
-                const float4 w = static_cast<const float4*>(rows)[(M + p) * row_vecs + c];
-                v.x += w.x;
-                v.y += w.y;
-                v.z += w.z;
-                v.w += w.w;
+    float acc[kCols];
+#pragma unroll
+    for (int e = 0; e < kCols; ++e)
+        acc[e] = 0.0f;
+    if constexpr (kParts == 2) {
+        // few slots per token where the parts are used: one row at a time
+        for (int j = 0; j < k; ++j) {
+            const int64_t p = pos[static_cast<int64_t>(t) * k + j];
+            if (p < 0 || p >= M)
+                continue;
+            const float4 a = static_cast<const float4*>(rows)[p * row_vecs + c];
+            const float4 b = static_cast<const float4*>(rows)[(M + p) * row_vecs + c];
+            acc[0] += a.x + b.x;
+            acc[1] += a.y + b.y;
+            acc[2] += a.z + b.z;
+            acc[3] += a.w + b.w;
+        }
+    }
+    for (int j0 = 0; kParts == 0 && j0 < k; j0 += 8) {
+        float v[8][kCols];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t p = j0 + j < k ? pos[static_cast<int64_t>(t) * k + j0 + j] : -1;
+            const bool ok = p >= 0 && p < M;
+            const int64_t at = (ok ? p : 0) * row_vecs + c;
+            if constexpr (kParts == 0) {
+                const uint4 b = ok ? static_cast<const uint4*>(rows)[at] : make_uint4(0, 0, 0, 0);
+                const uint32_t d[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[j][2 * e] = __uint_as_float(d[e] << 16);
+                    v[j][2 * e + 1] = __uint_as_float(d[e] & 0xffff0000u);
+                }
             }
         }
-        acc.x += v.x;
-        acc.y += v.y;
-        acc.z += v.z;
-        acc.w += v.w;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int e = 0; e < kCols; ++e)
+                acc[e] += v[j][e];                // skipped slots add 0 exactly
     }
-    dx[i] = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+    if constexpr (kCols == 8)
+        reinterpret_cast<uint4*>(dx)[i] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                                     pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+    else
+        reinterpret_cast<uint2*>(dx)[i] = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
 }
 
 // w(p) = probs of the slot behind permuted row p (0 for rows past the valid ones).
@@ -1248,19 +1275,19 @@ hipError_t launch_dgrad_gate_up(const uint16_t* dgu, const uint16_t* wg, const u
 hipError_t launch_sum_slot_rows(const void* rows, int parts, const int32_t* pos, uint16_t* dx,
                                 int64_t T, int64_t k, int64_t M, int64_t H, hipStream_t s)
 {
-    const int64_t total = T * (H / 4);
+    const int64_t cols = parts == 2 ? 4 : 8;                 // columns per thread
+    const int64_t total = T * (H / cols);
     if (total <= 0)
         return hipSuccess;
     if (total >= (int64_t{1} << 31))
         return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>((total + kSmallThreads - 1) / kSmallThreads)), block(kSmallThreads);
     const int kk = static_cast<int>(k);
-    const uint32_t rv = static_cast<uint32_t>(H / 4), tt = static_cast<uint32_t>(total);
-    uint2* out = reinterpret_cast<uint2*>(dx);
+    const uint32_t rv = static_cast<uint32_t>(H / cols), tt = static_cast<uint32_t>(total);
     if (parts == 2)
-        sum_slot_rows_kernel<2><<<grid, block, 0, s>>>(rows, pos, out, kk, M, rv, tt);
+        sum_slot_rows_kernel<2><<<grid, block, 0, s>>>(rows, pos, dx, kk, M, rv, tt);
     else
-        sum_slot_rows_kernel<0><<<grid, block, 0, s>>>(rows, pos, out, kk, M, rv, tt);
+        sum_slot_rows_kernel<0><<<grid, block, 0, s>>>(rows, pos, dx, kk, M, rv, tt);
     return hipGetLastError();
 }
 
