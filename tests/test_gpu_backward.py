@@ -164,3 +164,28 @@ def test_backward_full_size_sampled(name, n_tokens, n_entries):
     empty = np.flatnonzero(counts == 0)
     for ee in empty:
         assert np.all(dwg[ee] == 0) and np.all(dwu[ee] == 0) and np.all(dwd[ee] == 0)
+
+
+def test_backward_out_of_range_ids_skipped_and_flagged():
+    """Slots whose expert id lies outside [0, E) are skipped (dprobs 0, nothing in dx or the weight
+    gradients) and set the status word; every other gradient is that of the layer in which those
+    slots carry probability 0 (and any valid id)."""
+    inp = synth.make_layer(T=200, H=256, F=256, E=4, k=2, dtype="bf16", seed=12)
+    bad = np.zeros(inp.expert_ids.shape, bool)
+    bad[::7, 1] = True
+    bad[3::11, 0] = True
+    ids_bad = inp.expert_ids.copy()
+    ids_bad[bad] = np.where(np.arange(bad.sum()) % 2 == 0, 4, -1)
+    dout = synth.make_dout(inp)
+    d = dv.layer(inp)
+    ws = torch.empty(mel.backward_workspace_size(mel.problem(inp.T, inp.H, inp.F, inp.E, inp.k, mel.BF16)),
+                     dtype=torch.uint8, device="cuda")
+    res = mel.expert_backward(d.x, d.w_gate, d.w_up, d.w_down, dv.tensor(ids_bad), d.probs,
+                              dv.tensor(dout), workspace=ws)
+    assert mel.device_status(ws) == 4                 # MOE_ERR_EXPERT_ID_OUT_OF_RANGE
+    gpu = [dv.host(t) for t in res]
+    inp.probs = np.where(bad, np.float32(0.0), inp.probs).astype(np.float32)
+    ref = oracle.backward(inp, dout)
+    _compare(gpu[:4], ref[:4], names=("dx", "dw_gate", "dw_up", "dw_down"))
+    assert np.all(gpu[4][bad] == 0)
+    assert oracle.inf_norm_rel(gpu[4][~bad], ref[4][~bad]) <= TOL
