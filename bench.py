@@ -109,6 +109,118 @@ def cpu_baseline(inp, budget_s: float):
                       f"weights decoded per call), {dt:.1f} s, fp64"}
 
 
+def cpu_baseline_grouped(g, budget_s: float):
+    """The oracle on a bounded sample of one EP rank's received rows (doubling as above)."""
+    import oracle
+    M = int(g.group_offsets[-1])
+    rng = np.random.default_rng(123)
+    order = rng.permutation(M)
+    n = 8
+    while True:
+        t0 = time.perf_counter()
+        oracle.grouped_ffn(g, row_index=np.sort(order[:n]))
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 2 or n >= M:
+            break
+        n = min(M, max(2 * n, int(n * budget_s / 2 / max(dt, 1e-3))))
+    return {"value": n / dt, "unit": "rows/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} of {M} received rows through their experts (weights decoded per call), "
+                      f"{dt:.1f} s, fp64"}
+
+
+def bench_grouped(args, torch, mel, synth, dv, dev):
+    """One EP rank's share: the grouped FFN over rows as the dispatch All-to-All delivers them
+    (source-major groups of 2 local experts); a step is one moe_grouped_ffn call, the metric rows/s."""
+    g = synth.make_workload(args.workload)
+    M, H = g.rows.shape
+    F, G = g.F, g.group_expert.shape[0]
+    head = args.head_m_size if args.head_m_size is not None else 0
+    rows = dv.tensor(g.rows, dev)
+    offs, gexp = dv.tensor(g.group_offsets, dev), dv.tensor(g.group_expert, dev)
+    wg, wu, wd = (dv.tensor(w, dev) for w in (g.w_gate, g.w_up, g.w_down))
+    ws = torch.empty(max(mel.grouped_ffn_workspace_size(mel.problem(0, H, F, g.E_local, 1, mel.BF16, h), M, G)
+                         for h in (head, 512)), dtype=torch.uint8, device=dev)
+    out = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev).view(torch.float32)
+    if args.copy_calibration_mib:
+        src = torch.ones(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
+
+    def step(h):
+        mel.grouped_ffn(rows, offs, gexp, wg, wu, wd, head_m_size=h, workspace=ws, out=out)
+
+    for _ in range(args.warmup):
+        step(head)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for a, b in ev:
+        if not args.no_flush:
+            flush.sum()
+        a.record()
+        step(head)
+        b.record()
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    mel.timing_reset()
+    mel.timing_enable(True)
+    for _ in range(args.steps):
+        if not args.no_flush:
+            flush.sum()
+        step(head)
+    kern = mel.timing_collect()
+    mel.timing_enable(False)
+    kavg = {n: tot / cnt for n, (tot, cnt) in kern.items()}
+    ms_per_step = float(ms.mean())
+    log(f"ms/step mean {ms_per_step:.3f} median {np.median(ms):.3f}; kernel avg ms: " +
+        ", ".join(f"{n}={v:.4f}" for n, v in sorted(kavg.items())))
+    fl = gemm_flops(M, H, F)
+    fc1_ms, fc2_ms = kavg["fc1_bf16"], kavg["fc2_bf16"]
+    peak = PEAK["bf16"]
+    achieved = fl["fc1"] / (fc1_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC, "value": M / (ms_per_step * 1e-3), "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "rows": M, "H": H, "F": F, "local_experts": g.E_local,
+                   "sources": g.sources, "groups": G, "head_m_size": head,
+                   "flush": "none" if args.no_flush else "read"},
+        "gemm": {"tflops": (fl["fc1"] + fl["fc2"]) / ((fc1_ms + fc2_ms) * 1e-3) / 1e12,
+                 "frac_of_peak": (fl["fc1"] + fl["fc2"]) / ((fc1_ms + fc2_ms) * 1e-3) / 1e12 / peak,
+                 "peak_tflops": peak, "fc1_ms": fc1_ms, "fc2_ms": fc2_ms},
+        "kernels_ms": kavg,
+        "roofline": {"kernel": "fc1_bf16", "bound": "mfma", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": measured_traffic(args.workload, "fc1_bf16"),
+                     "per_launch": f"{fl['fc1']:.4g} FLOP = 4*M*H*F, M={M} received rows"},
+        "timing": {"median_ms": float(np.median(ms)), "p10_ms": float(np.percentile(ms, 10)),
+                   "p90_ms": float(np.percentile(ms, 90))},
+    }
+    if not args.skip_chunked:
+        for _ in range(2):
+            step(512)
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in cev:
+            if not args.no_flush:
+                flush.sum()
+            a.record()
+            step(512)
+            b.record()
+        torch.cuda.synchronize()
+        cms = float(np.mean([a.elapsed_time(b) for a, b in cev]))
+        result["chunked"] = {"head_m_size": 512, "ms_per_step": cms, "rows_per_s": M / (cms * 1e-3),
+                             "overhead_vs_unchunked": cms / ms_per_step - 1.0}
+        log(f"chunked(512) ms/step {cms:.3f}")
+    if not args.skip_cpu_baseline:
+        log(f"cpu baseline (~{args.cpu_seconds:.0f} s of oracle work)")
+        result["cpu_baseline"] = cpu_baseline_grouped(g, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,9 +260,9 @@ def main():
     dev = torch.device("cuda", 0)
 
     cfg = synth.WORKLOADS[args.workload]
-    if cfg["kind"] != "layer":
-        print("bench.py times whole-layer workloads", file=sys.stderr)
-        sys.exit(2)
+    if cfg["kind"] == "grouped":
+        bench_grouped(args, torch, mel, synth, dv, dev)
+        return
     log(f"generating {args.workload} inputs")
     t0 = time.perf_counter()
     inp = synth.make_workload(args.workload)

@@ -18,7 +18,7 @@ __all__ = [
     "MoeError", "library", "lib_path", "F32", "BF16", "MXFP8",
     "workspace_size", "expert_forward", "expert_forward_mx", "backward_workspace_size",
     "expert_backward", "route", "permute", "unpermute",
-    "grouped_ffn", "grouped_ffn_mx", "mx_quantize", "device_status", "chunk_counters",
+    "grouped_ffn_workspace_size", "grouped_ffn", "grouped_ffn_mx", "mx_quantize", "device_status", "chunk_counters",
     "intermediate_h",
     "timing_enable", "timing_collect", "timing_reset",
 ]
@@ -302,6 +302,12 @@ def unpermute(y_perm, pos, probs, F: int = 128, E: int | None = None):
     _check(library().moe_unpermute(ctypes.byref(prob), _ptr(y_perm), _ptr(pos), _ptr(probs),
                                    _ptr(out), _stream(y_perm)))
     return out
+
+
+def grouped_ffn_workspace_size(prob: MoeProblem, M: int, G: int) -> int:
+    n = ctypes.c_size_t()
+    _check(library().moe_grouped_ffn_workspace_size(ctypes.byref(prob), M, G, ctypes.byref(n)))
+    return n.value
 
 
 def grouped_ffn(rows, group_offsets, group_expert, w_gate, w_up, w_down, head_m_size: int = 0,
