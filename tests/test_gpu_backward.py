@@ -55,6 +55,8 @@ CASES = [
     # several row / column tiles)
     (300, 256, 512, 5, 2, {}),
     (260, 512, 256, 16, 4, dict(routing="zipf_gumbel", zipf_s=1.1, n_zero=4)),
+    # the most experts the routing takes: one or no row per expert, every tile partial
+    (128, 256, 256, 1023, 8, {}),
 ]
 
 

@@ -145,6 +145,8 @@ CASES = [
     # large-tile path (H % 256 == 0, F % 128 == 0): several K steps, column tiles and ragged tiles
     ("bf16_large_tiles_ragged", "bf16", 700, 512, 384, 6, 2, {}),
     ("bf16_large_tiles_deep_k", "bf16", 300, 1024, 640, 3, 2, {}),
+    # the most experts the routing takes: most experts empty or with one row, every tile partial
+    ("bf16_many_experts", "bf16", 128, 256, 256, 1023, 8, {}),
 ]
 
 
