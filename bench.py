@@ -451,7 +451,36 @@ def main():
         }
         log(f"backward ms/step {b_mean:.3f}; kernel avg ms: " +
             ", ".join(f"{n}={v:.4f}" for n, v in sorted(bkavg.items())))
-        del bws, dout
+        # training pair: the forward that keeps g and u, and the backward that takes them
+        saved = torch.empty((2, M, F), dtype=torch.bfloat16, device=dev)
+
+        def fstep():
+            mel.expert_forward_train(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs, out=out,
+                                     saved_gu=saved, workspace=ws)
+
+        def bstep_saved():
+            return mel.expert_backward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs, dout,
+                                       workspace=bws, saved_gu=saved)
+
+        pair = {}
+        for name, fn in (("forward_train_ms", fstep), ("backward_saved_gu_ms", bstep_saved)):
+            fn()
+            torch.cuda.synchronize()
+            pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(bsteps)]
+            for a, b in pev:
+                do_flush()
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            pair[name] = float(np.mean([a.elapsed_time(b) for a, b in pev]))
+        pair["step_ms"] = pair["forward_train_ms"] + pair["backward_saved_gu_ms"]
+        pair["tokens_per_s"] = T / (pair["step_ms"] * 1e-3)
+        result["backward"]["training_pair"] = pair
+        log(f"forward keeping g, u {pair['forward_train_ms']:.3f} ms + backward on them "
+            f"{pair['backward_saved_gu_ms']:.3f} ms")
+        del bws, dout, saved
 
     if not args.skip_chunked:
         for _ in range(2):

@@ -103,6 +103,17 @@ moe_status moe_expert_forward(const moe_problem* p, const void* x, const void* w
                               const float* probs, void* out, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
+/* moe_expert_forward (dtype MOE_BF16 only) that also keeps what the backward would recompute: the
+ * gate and up values g = x Wg[e], u = x Wu[e] of every routed slot, as bfloat16 in
+ * saved_gu [2, T*k, F] (g rows, then u rows; row p is the p-th slot in expert order, the row order of
+ * moe_route's perm).  Pass saved_gu to moe_expert_backward with the same inputs and routing to skip
+ * its recomputation; the gradients are then bitwise those of the recomputing call.  The output is
+ * bitwise that of moe_expert_forward.  Workspace: moe_workspace_size. */
+moe_status moe_expert_forward_train(const moe_problem* p, const void* x, const void* w_gate,
+                                    const void* w_up, const void* w_down, const int32_t* expert_ids,
+                                    const float* probs, void* out, void* saved_gu, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
 /* The same layer on OCP-MX E4M3 inputs (dtype must be MOE_MXFP8_E4M3; H and F multiples of 128).
  * Element bytes and scale bytes as described above; out is bfloat16 [T,H]. */
 moe_status moe_expert_forward_mx(const moe_problem* p, const uint8_t* x, const uint8_t* x_scale,
@@ -133,17 +144,18 @@ moe_status moe_backward_workspace_size(const moe_problem* p, size_t* bytes /* ho
  * dtype MOE_BF16 only; H and F multiples of 128; head_m_size 0; flags ignored.
  *   x [T,H], w_gate / w_up [E,H,F], w_down [E,F,H] bfloat16; expert_ids [T,k] int32;
  *   probs [T,k] float32; dout [T,H] bfloat16
+ *   saved_gu: NULL, or the g and u that moe_expert_forward_train kept for the same inputs
  *   dx [T,H] bfloat16; dw_gate / dw_up [E,H,F], dw_down [E,F,H], dprobs [T,k] float32
- * g and u are recomputed from x (nothing is kept from a forward call).  g, u, dg, du and probs * h
+ * Without saved_gu, g and u are recomputed from x.  g, u, dg, du and probs * h
  * are rounded to bfloat16, and so is each slot's dx row, except on problems with few 256-row tiles,
  * where dg Wg^T and du Wu^T run as separate tasks and stay fp32 until the per-token sum.  Every
  * gradient element is an fp32 sum in a fixed order (no float atomics): deterministic.  Experts that receive no slot get zero
  * weight gradients; slots with an out-of-range id are skipped (dprobs 0) and flag the status word. */
 moe_status moe_expert_backward(const moe_problem* p, const void* x, const void* w_gate,
                                const void* w_up, const void* w_down, const int32_t* expert_ids,
-                               const float* probs, const void* dout, void* dx, float* dw_gate,
-                               float* dw_up, float* dw_down, float* dprobs, void* workspace,
-                               size_t workspace_bytes, hipStream_t stream);
+                               const float* probs, const void* dout, const void* saved_gu, void* dx,
+                               float* dw_gate, float* dw_up, float* dw_down, float* dprobs,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Sub-steps (the same kernels the whole-layer calls use).

@@ -16,8 +16,8 @@ import torch
 
 __all__ = [
     "MoeError", "library", "lib_path", "F32", "BF16", "MXFP8",
-    "workspace_size", "expert_forward", "expert_forward_mx", "backward_workspace_size",
-    "expert_backward", "route", "permute", "unpermute",
+    "workspace_size", "expert_forward", "expert_forward_mx", "expert_forward_train",
+    "backward_workspace_size", "expert_backward", "route", "permute", "unpermute",
     "grouped_ffn_workspace_size", "grouped_ffn", "grouped_ffn_mx", "mx_quantize", "device_status", "chunk_counters",
     "intermediate_h",
     "timing_enable", "timing_collect", "timing_reset",
@@ -52,7 +52,8 @@ _SIGS = {
     "moe_expert_forward": [ctypes.POINTER(MoeProblem)] + [_P] * 8 + [ctypes.c_size_t, _P],
     "moe_expert_forward_mx": [ctypes.POINTER(MoeProblem)] + [_P] * 12 + [ctypes.c_size_t, _P],
     "moe_backward_workspace_size": [ctypes.POINTER(MoeProblem), ctypes.POINTER(ctypes.c_size_t)],
-    "moe_expert_backward": [ctypes.POINTER(MoeProblem)] + [_P] * 13 + [ctypes.c_size_t, _P],
+    "moe_expert_backward": [ctypes.POINTER(MoeProblem)] + [_P] * 14 + [ctypes.c_size_t, _P],
+    "moe_expert_forward_train": [ctypes.POINTER(MoeProblem)] + [_P] * 9 + [ctypes.c_size_t, _P],
     "moe_route_workspace_size": [_I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
     "moe_route": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_permute": [ctypes.POINTER(MoeProblem), _P, _P, _P, _P, _P, _P],
@@ -191,9 +192,40 @@ def backward_workspace_size(prob: MoeProblem) -> int:
     return n.value
 
 
-def expert_backward(x, w_gate, w_up, w_down, expert_ids, probs, dout, workspace=None):
+def expert_forward_train(x, w_gate, w_up, w_down, expert_ids, probs, out=None, saved_gu=None,
+                        workspace=None):
+    """expert_forward (bfloat16) that also returns g and u of every routed slot, bf16 [2, T*k, F],
+    for expert_backward(..., saved_gu=...).  Returns (out, saved_gu)."""
+    T, H = x.shape
+    E, _, F = w_gate.shape
+    k = expert_ids.shape[1]
+    dev = x.device
+    bf = torch.bfloat16
+    _need(x, "x", bf, (T, H))
+    _need(w_gate, "w_gate", bf, (E, H, F), dev)
+    _need(w_up, "w_up", bf, (E, H, F), dev)
+    _need(w_down, "w_down", bf, (E, F, H), dev)
+    _need(expert_ids, "expert_ids", torch.int32, (T, k), dev)
+    _need(probs, "probs", torch.float32, (T, k), dev)
+    prob = problem(T, H, F, E, k, BF16)
+    ws = _workspace(workspace_size(prob), dev, workspace)
+    if out is None:
+        out = torch.empty((T, H), dtype=bf, device=dev)
+    if saved_gu is None:
+        saved_gu = torch.empty((2, T * k, F), dtype=bf, device=dev)
+    _need(out, "out", bf, (T, H), dev)
+    _need(saved_gu, "saved_gu", bf, (2, T * k, F), dev)
+    _check(library().moe_expert_forward_train(ctypes.byref(prob), _ptr(x), _ptr(w_gate), _ptr(w_up),
+                                              _ptr(w_down), _ptr(expert_ids), _ptr(probs), _ptr(out),
+                                              _ptr(saved_gu), _ptr(ws), ws.numel(), _stream(x)))
+    return out, saved_gu
+
+
+def expert_backward(x, w_gate, w_up, w_down, expert_ids, probs, dout, workspace=None,
+                    saved_gu=None):
     """Gradients of sum(dout * out) for expert_forward's bfloat16 layer:
-    (dx bf16 [T,H], dw_gate f32 [E,H,F], dw_up f32 [E,H,F], dw_down f32 [E,F,H], dprobs f32 [T,k])."""
+    (dx bf16 [T,H], dw_gate f32 [E,H,F], dw_up f32 [E,H,F], dw_down f32 [E,F,H], dprobs f32 [T,k]).
+    saved_gu: g and u from expert_forward_train on the same inputs (skips their recomputation)."""
     T, H = x.shape
     E, _, F = w_gate.shape
     k = expert_ids.shape[1]
@@ -206,6 +238,8 @@ def expert_backward(x, w_gate, w_up, w_down, expert_ids, probs, dout, workspace=
     _need(expert_ids, "expert_ids", torch.int32, (T, k), dev)
     _need(probs, "probs", torch.float32, (T, k), dev)
     _need(dout, "dout", bf, (T, H), dev)
+    if saved_gu is not None:
+        _need(saved_gu, "saved_gu", bf, (2, T * k, F), dev)
     prob = problem(T, H, F, E, k, BF16)
     ws = _workspace(backward_workspace_size(prob), dev, workspace)
     dx = torch.empty((T, H), dtype=bf, device=dev)
@@ -215,7 +249,8 @@ def expert_backward(x, w_gate, w_up, w_down, expert_ids, probs, dout, workspace=
     dprobs = torch.empty((T, k), dtype=torch.float32, device=dev)
     _check(library().moe_expert_backward(ctypes.byref(prob), _ptr(x), _ptr(w_gate), _ptr(w_up),
                                          _ptr(w_down), _ptr(expert_ids), _ptr(probs), _ptr(dout),
-                                         _ptr(dx), _ptr(dwg), _ptr(dwu), _ptr(dwd), _ptr(dprobs),
+                                         _ptr(saved_gu), _ptr(dx), _ptr(dwg), _ptr(dwu), _ptr(dwd),
+                                         _ptr(dprobs),
                                          _ptr(ws), ws.numel(), _stream(x)))
     return dx, dwg, dwu, dwd, dprobs
 

@@ -332,7 +332,7 @@ moe_status run_ffn(int dtype, const void* rows, const uint8_t* rows_scale, int64
                    int64_t H, int64_t F, int64_t head_m_size, const void* wg, const uint8_t* wgs,
                    const void* wu, const uint8_t* wus, const void* wd, const uint8_t* wds,
                    void* y, void* ws, const FfnLayout& L, bool write_status, hipStream_t s,
-                   const int32_t* gather = nullptr, int gather_k = 1)
+                   const int32_t* gather = nullptr, int gather_k = 1, uint16_t* save_gu = nullptr)
 {
     const int64_t chunk = head_m_size > 0 ? head_m_size : std::max<int64_t>(M, 1);
     int32_t* status = at<int32_t>(ws, L.status);
@@ -350,7 +350,8 @@ moe_status run_ffn(int dtype, const void* rows, const uint8_t* rows_scale, int64
         LAUNCH(s, "fc1_bf16",
                launch_fc1_bf16(static_cast<const uint16_t*>(rows), static_cast<const uint16_t*>(wg),
                                static_cast<const uint16_t*>(wu), h, tiles, tcount, H, F,
-                               task_ctr, gather, gather_k, s));
+                               task_ctr, gather, gather_k, save_gu,
+                               save_gu != nullptr ? save_gu + M * F : nullptr, s));
         LAUNCH(s, "fc2_bf16",
                launch_fc2_bf16(h, static_cast<const uint16_t*>(wd), static_cast<uint16_t*>(y),
                                tiles, tcount, H, F, chunk_done, task_ctr + kXcdCount, s));
@@ -397,7 +398,7 @@ static moe_status forward_common(const moe_problem* p, const void* x, const uint
                                  const void* wg, const uint8_t* wgs, const void* wu,
                                  const uint8_t* wus, const void* wd, const uint8_t* wds,
                                  const int32_t* ids, const float* probs, void* out, void* ws,
-                                 size_t ws_bytes, hipStream_t s)
+                                 size_t ws_bytes, hipStream_t s, void* saved_gu = nullptr)
 {
     const ForwardLayout L = forward_layout(p->dtype, p->T, p->H, p->F, p->E, p->k, p->head_m_size);
     if (ws == nullptr || ws_bytes < L.total)
@@ -432,7 +433,8 @@ static moe_status forward_common(const moe_problem* p, const void* x, const uint
     }
     if (moe_status st = run_ffn(p->dtype, rows, rows_scale, M, offsets, nullptr, p->E, p->E, H, p->F,
                                 p->head_m_size, wg, wgs, wu, wus, wd, wds, at<void>(ws, L.y_perm), ws,
-                                L.ffn, false, s, fused ? perm : nullptr, static_cast<int>(k));
+                                L.ffn, false, s, fused ? perm : nullptr, static_cast<int>(k),
+                                static_cast<uint16_t*>(saved_gu));
         st != MOE_OK)
         return st;
     LAUNCH(s, "unpermute",
@@ -452,6 +454,22 @@ MOE_API moe_status moe_expert_forward(const moe_problem* p, const void* x, const
         return fail(MOE_ERR_INVALID_ARGUMENT, "MX inputs go through moe_expert_forward_mx");
     return forward_common(p, x, nullptr, w_gate, nullptr, w_up, nullptr, w_down, nullptr,
                           expert_ids, probs, out, workspace, workspace_bytes, stream);
+}
+
+MOE_API moe_status moe_expert_forward_train(const moe_problem* p, const void* x, const void* w_gate,
+                                            const void* w_up, const void* w_down,
+                                            const int32_t* expert_ids, const float* probs, void* out,
+                                            void* saved_gu, void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream)
+{
+    if (moe_status st = check_problem(p, true); st != MOE_OK)
+        return st;
+    if (p->dtype != MOE_BF16)
+        return fail(MOE_ERR_UNSUPPORTED, "saving g and u for the backward takes bfloat16 only");
+    if (p->T > 0 && saved_gu == nullptr)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "saved_gu is null");
+    return forward_common(p, x, nullptr, w_gate, nullptr, w_up, nullptr, w_down, nullptr,
+                          expert_ids, probs, out, workspace, workspace_bytes, stream, saved_gu);
 }
 
 MOE_API moe_status moe_expert_forward_mx(const moe_problem* p, const uint8_t* x,
@@ -565,9 +583,9 @@ MOE_API moe_status moe_backward_workspace_size(const moe_problem* p, size_t* byt
 MOE_API moe_status moe_expert_backward(const moe_problem* p, const void* x, const void* w_gate,
                                        const void* w_up, const void* w_down,
                                        const int32_t* expert_ids, const float* probs,
-                                       const void* dout, void* dx, float* dw_gate, float* dw_up,
-                                       float* dw_down, float* dprobs, void* ws, size_t ws_bytes,
-                                       hipStream_t s)
+                                       const void* dout, const void* saved_gu, void* dx,
+                                       float* dw_gate, float* dw_up, float* dw_down, float* dprobs,
+                                       void* ws, size_t ws_bytes, hipStream_t s)
 {
     if (moe_status st = check_backward(p); st != MOE_OK)
         return st;
@@ -609,8 +627,9 @@ MOE_API moe_status moe_expert_backward(const moe_problem* p, const void* x, cons
         int32_t* task_ctr = at<int32_t>(ws, L.task_ctr);
         MTile* tiles_r = at<MTile>(ws, L.tiles_r);
         MTile* tiles_d = at<MTile>(ws, L.tiles_d);
-        uint16_t* g = at<uint16_t>(ws, L.g);
-        uint16_t* u = at<uint16_t>(ws, L.u);
+        // g and u: as the forward saved them (same routing, so the same permuted rows), or recomputed
+        const uint16_t* g = saved_gu != nullptr ? static_cast<const uint16_t*>(saved_gu) : at<uint16_t>(ws, L.g);
+        const uint16_t* u = saved_gu != nullptr ? g + M * F : at<uint16_t>(ws, L.u);
         void* dx_rows = at<void>(ws, L.dx_perm);
         float* prow = at<float>(ws, L.prow);
         float* partial = at<float>(ws, L.partial);
@@ -625,9 +644,12 @@ MOE_API moe_status moe_expert_backward(const moe_problem* p, const void* x, cons
                                       tcount + 1, nullptr, nullptr, 1, 0, nullptr, status, false, s));
         const int32_t* tcount_d = L.tiles_d != L.tiles_r ? tcount + 1 : tcount;
         // g = x_perm Wg[e], u = x_perm Wu[e]: the plain grouped GEMM with K = H and N = F
-        LAUNCH(s, "recompute_g", launch_recompute_bf16(x_perm, wg, g, tiles_r, tcount, H, F, task_ctr, s));
-        LAUNCH(s, "recompute_u",
-               launch_recompute_bf16(x_perm, wu, u, tiles_r, tcount, H, F, task_ctr + kXcdCount, s));
+        if (saved_gu == nullptr) {
+            LAUNCH(s, "recompute_g", launch_recompute_bf16(x_perm, wg, at<uint16_t>(ws, L.g), tiles_r,
+                                                           tcount, H, F, task_ctr, s));
+            LAUNCH(s, "recompute_u", launch_recompute_bf16(x_perm, wu, at<uint16_t>(ws, L.u), tiles_r,
+                                                           tcount, H, F, task_ctr + kXcdCount, s));
+        }
         LAUNCH(s, "row_probs", launch_row_probs(perm, probs, prow, M, s));
         LAUNCH(s, "dgrad_down",
                launch_dgrad_down(dout_perm, wd, g, u, prow, dgu, hp, partial, tiles_d, tcount_d,

@@ -184,7 +184,8 @@ __device__ __forceinline__ void k_loop(f32x16_t (&acc)[kTM][kTN], unsigned char*
 template <bool kGated, int kWM, int kTM, int kTN>
 __device__ __forceinline__ void store_output(const f32x16_t (&acc)[kTM][kTN], uint16_t* __restrict__ C,
                                              const MTile& tile, int n0, int N_out, int wm, int wn,
-                                             int lane)
+                                             int lane, uint16_t* __restrict__ save_g,
+                                             uint16_t* __restrict__ save_u)
 {
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
@@ -201,7 +202,12 @@ __device__ __forceinline__ void store_output(const f32x16_t (&acc)[kTM][kTN], ui
 #pragma unroll
                 for (int j = 0; j < kTN; j += 2) {
                     const int q = (wn * kTN + j) / 2;
+                    const int64_t at = static_cast<int64_t>(row) * N_out + n0 + 32 * q + (lane & 31);
                     crow[n0 + 32 * q + (lane & 31)] = f32_to_bf16(swiglu(acc[i][j][r], acc[i][j + 1][r]));
+                    if (save_g != nullptr) {
+                        save_g[at] = f32_to_bf16(acc[i][j][r]);
+                        save_u[at] = f32_to_bf16(acc[i][j + 1][r]);
+                    }
                 }
             } else {
 #pragma unroll
@@ -217,7 +223,7 @@ __global__ __launch_bounds__(kWM * kWN * 64, kMinBlocks) void grouped_gemm_bf16(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, const MTile* __restrict__ tiles,
     const int32_t* __restrict__ tile_count, int K, int N_out, int32_t* __restrict__ chunk_done,
-    int32_t* __restrict__ task_ctr)
+    int32_t* __restrict__ task_ctr, uint16_t* __restrict__ save_g, uint16_t* __restrict__ save_u)
 {
     using G = Cfg<kGated, kWM, kWN, kTM, kTN, kMinBlocks>;
     __shared__ int claimed;
@@ -291,7 +297,7 @@ __global__ __launch_bounds__(kWM * kWN * 64, kMinBlocks) void grouped_gemm_bf16(
         case 1: k_loop<G, kWM, kTM, kTN, 1>(acc, smem, A, aoff, bsrc, N_w, a_lds0, b0, kg, KT, wm, wn, lane); break;
         default: k_loop<G, kWM, kTM, kTN, kTM>(acc, smem, A, aoff, bsrc, N_w, a_lds0, b0, kg, KT, wm, wn, lane); break;
         }
-        store_output<kGated, kWM, kTM, kTN>(acc, C, tile, n0, N_out, wm, wn, lane);
+        store_output<kGated, kWM, kTM, kTN>(acc, C, tile, n0, N_out, wm, wn, lane, save_g, save_u);
         if (chunk_done != nullptr)
             count_done(chunk_done, tile.chunk, wave, lane);
     }
@@ -573,7 +579,9 @@ __device__ __forceinline__ void k_loop(f32x16_t (&acc)[kTM][kTN], CopyCtx cp, co
 // LDS writes, rows of 128 bytes with 16-byte chunks XOR-swizzled by row), then read back as
 // 16-byte row chunks and stored to global memory 16 bytes per lane.  Only this wave touches its
 // area, and LDS operations of one wave complete in order, so no barrier is needed.
-template <bool kGated>
+// kVal (fc1): 0 the SwiGLU output h, 1 the gate values g, 2 the up values u (the last two saved for
+// the backward, same layout as h).
+template <bool kGated, int kVal = 0>
 __device__ __forceinline__ void store_output_staged(const f32x16_t (&acc)[kTM][kTN], uint16_t* __restrict__ C,
                                                     const MTile& tile, int n0, int N_out, uint32_t stage,
                                                     int wm, int wn, int lane, bool through)
@@ -598,8 +606,10 @@ __device__ __forceinline__ void store_output_staged(const f32x16_t (&acc)[kTM][k
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         float v;
-                        if constexpr (kGated)
+                        if constexpr (kGated && kVal == 0)
                             v = swiglu(acc[i][2 * ob][r], acc[i][2 * ob + 1][r]);   // gate, up blocks
+                        else if constexpr (kGated)
+                            v = acc[i][2 * ob + kVal - 1][r];
                         else
                             v = acc[i][ob][r];
                         const int row = 32 * ii + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -640,7 +650,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, const MTile* __restrict__ tiles,
     const int32_t* __restrict__ tile_count, int K, int N_out, int32_t* __restrict__ chunk_done,
-    int32_t* __restrict__ task_ctr, const int32_t* __restrict__ gather, int gather_k)
+    int32_t* __restrict__ task_ctr, const int32_t* __restrict__ gather, int gather_k,
+    uint16_t* __restrict__ save_g, uint16_t* __restrict__ save_u)
 {
     using L = BLayout<kGated>;
     constexpr int BN = kGated ? BNB / 2 : BNB;
@@ -814,6 +825,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
             setup(t);
         store_output_staged<kGated>(acc, C, done, done_n0, N_out, lds0 + kRingBytes + wave * kOutWaveBytes,
                                      wm, wn, lane, chunk_done != nullptr);
+        if constexpr (kGated) {
+            if (save_g != nullptr) {
+                store_output_staged<kGated, 1>(acc, save_g, done, done_n0, N_out,
+                                               lds0 + kRingBytes + wave * kOutWaveBytes, wm, wn, lane,
+                                               chunk_done != nullptr);
+                store_output_staged<kGated, 2>(acc, save_u, done, done_n0, N_out,
+                                               lds0 + kRingBytes + wave * kOutWaveBytes, wm, wn, lane,
+                                               chunk_done != nullptr);
+            }
+        }
         if (chunk_done != nullptr)
             count_done_through(chunk_done, done.chunk, wave, lane);
     }
@@ -864,7 +885,8 @@ bool bf16_supported(int64_t H, int64_t F) { return H % Fc2Small::BN == 0 && F % 
 
 hipError_t launch_fc1_bf16(const uint16_t* A, const uint16_t* wg, const uint16_t* wu, uint16_t* h,
                            const MTile* tiles, const int32_t* tile_count, int64_t H, int64_t F,
-                           int32_t* task_ctr, const int32_t* gather, int gather_k, hipStream_t s)
+                           int32_t* task_ctr, const int32_t* gather, int gather_k, uint16_t* save_g,
+                           uint16_t* save_u, hipStream_t s)
 {
     const int cu = device_info().cu_count;
     if (gather != nullptr && !use_big(H, F))
@@ -874,11 +896,11 @@ hipError_t launch_fc1_bf16(const uint16_t* A, const uint16_t* wg, const uint16_t
             return e;
         big::grouped_gemm_bf16_dma<true><<<dim3(cu), dim3(big::kThreads), kBigSmem, s>>>(
             A, wg, wu, h, tiles, tile_count, static_cast<int>(H), static_cast<int>(F), nullptr,
-            task_ctr, gather, gather_k);
+            task_ctr, gather, gather_k, save_g, save_u);
     } else {
         FC1_SMALL<<<dim3(2 * cu), dim3(Fc1Small::kThreads), Fc1Small::kSmemBytes, s>>>(
             A, wg, wu, h, tiles, tile_count, static_cast<int>(H), static_cast<int>(F), nullptr,
-            task_ctr);
+            task_ctr, save_g, save_u);
     }
     return hipGetLastError();
 }
@@ -893,11 +915,11 @@ hipError_t launch_fc2_bf16(const uint16_t* h, const uint16_t* wd, uint16_t* y, c
             return e;
         big::grouped_gemm_bf16_dma<false><<<dim3(cu), dim3(big::kThreads), kBigSmem, s>>>(
             h, wd, nullptr, y, tiles, tile_count, static_cast<int>(F), static_cast<int>(H),
-            chunk_done, task_ctr, nullptr, 1);
+            chunk_done, task_ctr, nullptr, 1, nullptr, nullptr);
     } else {
         FC2_SMALL<<<dim3(2 * cu), dim3(Fc2Small::kThreads), Fc2Small::kSmemBytes, s>>>(
             h, wd, nullptr, y, tiles, tile_count, static_cast<int>(F), static_cast<int>(H),
-            chunk_done, task_ctr);
+            chunk_done, task_ctr, nullptr, nullptr);
     }
     return hipGetLastError();
 }
@@ -912,11 +934,11 @@ hipError_t launch_recompute_bf16(const uint16_t* A, const uint16_t* w, uint16_t*
             return e;
         big::grouped_gemm_bf16_dma<false, 1><<<dim3(cu), dim3(big::kThreads), kBigSmem, s>>>(
             A, w, nullptr, C, tiles, tile_count, static_cast<int>(K), static_cast<int>(N), nullptr,
-            task_ctr, nullptr, 1);
+            task_ctr, nullptr, 1, nullptr, nullptr);
     } else {
         FC2_SMALL<<<dim3(2 * cu), dim3(Fc2Small::kThreads), Fc2Small::kSmemBytes, s>>>(
             A, w, nullptr, C, tiles, tile_count, static_cast<int>(K), static_cast<int>(N), nullptr,
-            task_ctr);
+            task_ctr, nullptr, nullptr);
     }
     return hipGetLastError();
 }

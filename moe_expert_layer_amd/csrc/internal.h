@@ -127,10 +127,12 @@ bool bf16_supported(int64_t H, int64_t F);
 int bf16_row_tile(int64_t H, int64_t F);
 int bf16_fc2_cols_per_tile(int64_t H, int64_t F);
 // task_ctr: kXcdCount zeroed counters for this launch (workspace).  gather (may be null; only
-// with 256-row tiles): permuted row p of A is row gather[p] / gather_k of A.
+// with 256-row tiles): permuted row p of A is row gather[p] / gather_k of A.  save_g / save_u (both
+// null or both set): also store the gate and up values g, u as bf16 [M, F], the layout of h.
 hipError_t launch_fc1_bf16(const uint16_t* A, const uint16_t* wg, const uint16_t* wu, uint16_t* h,
                            const MTile* tiles, const int32_t* tile_count, int64_t H, int64_t F,
-                           int32_t* task_ctr, const int32_t* gather, int gather_k, hipStream_t s);
+                           int32_t* task_ctr, const int32_t* gather, int gather_k, uint16_t* save_g,
+                           uint16_t* save_u, hipStream_t s);
 hipError_t launch_fc2_bf16(const uint16_t* h, const uint16_t* wd, uint16_t* y, const MTile* tiles,
                            const int32_t* tile_count, int64_t H, int64_t F, int32_t* chunk_done,
                            int32_t* task_ctr, hipStream_t s);

@@ -142,8 +142,16 @@ def test_backward_rejects_before_enqueue(mel):
     prob = mel.problem(64, 128, 256, 4, 2, mel.BF16)
     n = ctypes.c_size_t()
     assert lib.moe_backward_workspace_size(ctypes.byref(prob), ctypes.byref(n)) == 0
-    st = lib.moe_expert_backward(ctypes.byref(prob), *([None] * 13), 0, None)
+    st = lib.moe_expert_backward(ctypes.byref(prob), *([None] * 14), 0, None)
     assert st == 3 and b"workspace" in lib.moe_last_error()
-    st = lib.moe_expert_backward(ctypes.byref(prob), *([None] * 12), ctypes.c_void_p(0x1000),
+    st = lib.moe_expert_backward(ctypes.byref(prob), *([None] * 13), ctypes.c_void_p(0x1000),
                                  n.value, None)
     assert st == 1
+    # saving g and u: bf16 only, and saved_gu must be given
+    need = mel.workspace_size(prob)
+    st = lib.moe_expert_forward_train(ctypes.byref(prob), *([None] * 8), ctypes.c_void_p(0x1000),
+                                      need, None)
+    assert st == 1 and b"saved_gu" in lib.moe_last_error()
+    f32 = mel.problem(64, 128, 256, 4, 2, mel.F32)
+    st = lib.moe_expert_forward_train(ctypes.byref(f32), *([None] * 9), 0, None)
+    assert st == 2

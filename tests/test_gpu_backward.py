@@ -191,3 +191,38 @@ def test_backward_out_of_range_ids_skipped_and_flagged():
     _compare(gpu[:4], ref[:4], names=("dx", "dw_gate", "dw_up", "dw_down"))
     assert np.all(gpu[4][bad] == 0)
     assert oracle.inf_norm_rel(gpu[4][~bad], ref[4][~bad]) <= TOL
+
+
+@pytest.mark.parametrize("T,H,F,E,k", [(300, 384, 256, 6, 2), (300, 256, 512, 5, 2), (700, 512, 256, 8, 2)],
+                         ids=["small_tiles", "large_tiles", "large_tiles_gathered"])
+def test_saved_gate_up_values_are_those_recomputed(T, H, F, E, k):
+    """expert_forward_train's output is bitwise expert_forward's; the backward on its saved g and u
+    is bitwise the backward that recomputes them."""
+    inp = synth.make_layer(T=T, H=H, F=F, E=E, k=k, dtype="bf16", seed=T + H)
+    dout = dv.tensor(synth.make_dout(inp))
+    d = dv.layer(inp)
+    out = mel.expert_forward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs)
+    out_t, saved = mel.expert_forward_train(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs)
+    assert torch.equal(out, out_t)
+    a = mel.expert_backward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs, dout)
+    b = mel.expert_backward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs, dout,
+                            saved_gu=saved)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_saved_gate_up_values_full_size():
+    print("[backward-saved] mixtral_bf16: generating inputs", flush=True)
+    inp = synth.make_workload("mixtral_bf16")
+    d = dv.layer(inp)
+    dout = dv.tensor(synth.make_dout(inp))
+    out = mel.expert_forward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs)
+    out_t, saved = mel.expert_forward_train(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs)
+    assert torch.equal(out, out_t)
+    a = mel.expert_backward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs, dout)
+    b = mel.expert_backward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs, dout,
+                            saved_gu=saved)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
