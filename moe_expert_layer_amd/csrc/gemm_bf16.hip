@@ -33,6 +33,7 @@
 //     as 16-byte stores.
 // Small tiles (128 x 128, two workgroups per CU, other sizes): register-staged copies, the weights
 // transposed in registers with v_perm_b32 and stored K-contiguous, two LDS stages.
+#include <atomic>
 #include <utility>
 
 #include "common.h"
@@ -857,7 +858,7 @@ bool use_big(int64_t H, int64_t F) { return H % kBigFc2Cols == 0 && F % kBigFc1C
 
 hipError_t ensure_smem_limits()
 {
-    static bool done[64] = {};
+    static std::atomic<bool> done[64];    // per device: the attribute is set
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)

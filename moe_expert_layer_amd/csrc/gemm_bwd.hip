@@ -27,6 +27,7 @@
 // gradients over (expert, column tile of the gradient's rows, column tile of its columns) in groups
 // of 8 row tiles; consecutive tasks go to one XCD (workgroup b runs on XCD b % 8), so the
 // workgroups of an XCD share operand strips in its L2.
+#include <atomic>
 #include <utility>
 
 #include "common.h"
@@ -1030,7 +1031,7 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_dma(BwdArgs g, int32_t* __r
 template <int kEpi, int kParts>
 hipError_t launch(const BwdArgs& a, int32_t* task_ctr, hipStream_t s)
 {
-    static bool done[64] = {};
+    static std::atomic<bool> done[64];    // per device: the attribute is set
     int dev = 0;
     if (hipError_t e = hipGetDevice(&dev); e != hipSuccess)
         return e;
@@ -1154,7 +1155,7 @@ __global__ __launch_bounds__(kSmallThreads) void dprobs_kernel(const float* __re
 template <int kEpi>
 hipError_t launch_bwd(const BwdArgs& a, int64_t total_bound, hipStream_t s)
 {
-    static bool done[64] = {};
+    static std::atomic<bool> done[64];    // per device: the attribute is set
     int dev = 0;
     if (hipError_t e = hipGetDevice(&dev); e != hipSuccess)
         return e;
@@ -1306,7 +1307,7 @@ hipError_t launch_wgrad(const uint16_t* a_rows, int64_t lda, const uint16_t* b_r
                         const uint16_t* zero, int32_t* task_ctr, hipStream_t s)
 {
     if (zero != nullptr && task_ctr != nullptr && wgrad_dma_fits(Mo, No)) {
-        static bool done[64] = {};
+        static std::atomic<bool> done[64];    // per device: the attribute is set
         int dev = 0;
         if (hipError_t e = hipGetDevice(&dev); e != hipSuccess)
             return e;

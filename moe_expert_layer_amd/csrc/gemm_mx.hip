@@ -15,6 +15,8 @@
 // into K-contiguous LDS rows, two LDS stages, XOR-swizzled 16-byte chunks.  The fc1 epilogue stages
 // the fp32 SwiGLU tile in LDS so each lane owns one (row, 32-column block), finds its amax, and
 // writes 32 E4M3 bytes plus one scale byte with the same integer encoder as the standalone kernel.
+#include <atomic>
+
 #include "common.h"
 #include "gemm_common.h"
 #include "internal.h"
@@ -955,7 +957,7 @@ unsigned persistent_grid() { return static_cast<unsigned>(device_info().cu_count
 
 hipError_t ensure_smem_limits()
 {
-    static bool done[64] = {};
+    static std::atomic<bool> done[64];    // per device: the attribute is set
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
