@@ -45,37 +45,57 @@ __global__ __launch_bounds__(kThreads) void route_count_kernel(const int32_t* __
         block_counts[static_cast<int64_t>(blockIdx.x) * (E + 1) + i] = hist[i];
 }
 
-// Inclusive scan of one value per thread over a 1024-thread workgroup (Hillis-Steele in LDS).
-__device__ int block_inclusive_scan(int v, int* buf /* [2][kScanThreads] */)
+// Inclusive scan of one value per thread over a 1024-thread workgroup: a scan inside each wave by
+// shuffles, the 16 wave totals scanned by wave 0, then each wave adds the totals of the waves before
+// it.  Two barriers; buf needs 32 ints, and a following call only writes entries this one has
+// finished reading.
+__device__ int block_inclusive_scan(int v, int* buf)
 {
-    int pin = 0;
-    buf[threadIdx.x] = v;
-    __syncthreads();
-    for (int off = 1; off < kScanThreads; off <<= 1) {
-        int x = buf[pin * kScanThreads + threadIdx.x];
-        if (threadIdx.x >= off)
-            x += buf[pin * kScanThreads + threadIdx.x - off];
-        buf[(1 - pin) * kScanThreads + threadIdx.x] = x;
-        __syncthreads();
-        pin ^= 1;
+    constexpr int kWaves = kScanThreads / 64;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(v, off);
+        if (lane >= off)
+            v += y;
     }
-    return buf[pin * kScanThreads + threadIdx.x];
+    if (lane == 63)
+        buf[wave] = v;
+    __syncthreads();
+    if (wave == 0) {
+        int w = lane < kWaves ? buf[lane] : 0;
+#pragma unroll
+        for (int off = 1; off < kWaves; off <<= 1) {
+            const int y = __shfl_up(w, off);
+            if (lane >= off)
+                w += y;
+        }
+        if (lane < kWaves)
+            buf[kWaves + lane] = w;
+    }
+    __syncthreads();
+    return wave > 0 ? v + buf[kWaves + wave - 1] : v;
 }
 
 __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
     int32_t* __restrict__ block_counts, int nblocks, int E, int64_t M, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ status)
 {
-    __shared__ int buf[2 * kScanThreads];
+    __shared__ int buf[2 * (kScanThreads / 64)];
     __shared__ int total_valid;
     const int e = threadIdx.x;           // E <= kMaxExperts == kScanThreads
+    constexpr int kBatch = 8;            // block counts loaded per batch, all before any is used
     int tot = 0;
     if (e <= E) {
-        for (int b = 0; b < nblocks; ++b) {
-            int32_t* c = block_counts + static_cast<int64_t>(b) * (E + 1) + e;
-            const int v = *c;
-            *c = tot;
-            tot += v;
+        for (int b0 = 0; b0 < nblocks; b0 += kBatch) {
+            int v[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                v[j] = b0 + j < nblocks ? block_counts[static_cast<int64_t>(b0 + j) * (E + 1) + e] : 0;
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                tot += v[j];
         }
     }
     const int v = e < E ? tot : 0;
@@ -84,8 +104,20 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
     if (e < E) {
         counts[e] = tot;
         offsets[e] = excl;
-        for (int b = 0; b < nblocks; ++b)
-            block_counts[static_cast<int64_t>(b) * (E + 1) + e] += excl;
+        // each block's count becomes the block's first row for the expert
+        int run = excl;
+        for (int b0 = 0; b0 < nblocks; b0 += kBatch) {
+            int c[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                c[j] = b0 + j < nblocks ? block_counts[static_cast<int64_t>(b0 + j) * (E + 1) + e] : 0;
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                if (b0 + j < nblocks) {
+                    block_counts[static_cast<int64_t>(b0 + j) * (E + 1) + e] = run;
+                    run += c[j];
+                }
+        }
     }
     if (e == E - 1) {
         offsets[E] = incl;
@@ -171,7 +203,7 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
 {
     if (task_ctr != nullptr && threadIdx.x < 2 * kXcdCount)
         task_ctr[threadIdx.x] = 0;
-    __shared__ int buf[2 * kScanThreads];
+    __shared__ int buf[2 * (kScanThreads / 64)];
     __shared__ int carry;
     __shared__ int bad;
     if (threadIdx.x == 0) {
@@ -222,6 +254,7 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
                 tail_rows[threadIdx.x] = mine;
                 __syncthreads();
                 int rank = 0;
+#pragma unroll 8
                 for (int q = 0; q < G; ++q) {
                     const int other = tail_rows[q];
                     rank += (other > mine || (other == mine && q < g)) ? 1 : 0;
