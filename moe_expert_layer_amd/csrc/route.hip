@@ -239,9 +239,9 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
                         r = cend;
                     }
                 } else if (pass == 0) {
-                    n = static_cast<int>((re - rb) / bm);
+                    n = static_cast<int>(re - rb) / bm;
                 } else {
-                    n = (re - rb) % bm != 0 ? 1 : 0;
+                    n = static_cast<int>(re - rb) % bm != 0 ? 1 : 0;
                 }
             }
             int incl = block_inclusive_scan(n, buf);
@@ -250,21 +250,24 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
                 // longest partial tiles first (all groups fit one pass): the rank of this group's
                 // tail among all tails, larger first, ties by group index
                 __shared__ int tail_rows[kScanThreads];
-                const int mine = n != 0 ? static_cast<int>((re - rb) % bm) : -1;
+                const int mine = n != 0 ? static_cast<int>(re - rb) % bm : -1;
                 tail_rows[threadIdx.x] = mine;
                 __syncthreads();
                 int rank = 0;
+                if (n != 0) {                     // groups without a tail skip the count
 #pragma unroll 8
-                for (int q = 0; q < G; ++q) {
-                    const int other = tail_rows[q];
-                    rank += (other > mine || (other == mine && q < g)) ? 1 : 0;
+                    for (int q = 0; q < G; ++q) {
+                        const int other = tail_rows[q];
+                        rank += (other > mine || (other == mine && q < g)) ? 1 : 0;
+                    }
                 }
                 __syncthreads();
                 if (n != 0)
                     t = carry + rank;
             }
-            auto emit = [&](int64_t r0, int64_t r1, int run_begin, int run_len) {
-                const int c = static_cast<int>(r0 / chunk);
+            // c: the tile's chunk (0 unchunked), computed once per chunk piece by the caller, since a
+            // 64-bit division is a long software sequence
+            auto emit = [&](int64_t r0, int64_t r1, int run_begin, int run_len, int c) {
                 if (t < max_tiles) {
                     MTile mt;
                     mt.expert = ex;
@@ -293,9 +296,10 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
                     }
                     const int run_begin = t;
                     for (int64_t q = r; q < wend;) {
-                        const int64_t cend = min(wend, (q / chunk + 1) * chunk);
+                        const int64_t c = q / chunk;
+                        const int64_t cend = min(wend, (c + 1) * chunk);
                         for (int64_t r0 = q; r0 < cend; r0 += bm)
-                            emit(r0, min(cend, r0 + bm), run_begin, run_len);
+                            emit(r0, min(cend, r0 + bm), run_begin, run_len, static_cast<int>(c));
                         q = cend;
                     }
                     r = wend;
@@ -303,9 +307,9 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
             } else if (pass == 0) {
                 const int run_begin = t;
                 for (int i = 0; i < n; ++i)
-                    emit(rb + int64_t{i} * bm, rb + int64_t{i + 1} * bm, run_begin, n);
+                    emit(rb + int64_t{i} * bm, rb + int64_t{i + 1} * bm, run_begin, n, 0);
             } else if (n != 0) {
-                emit(rb + (re - rb) / bm * bm, re, t, 1);
+                emit(rb + static_cast<int>(re - rb) / bm * bm, re, t, 1, 0);
             }
             __syncthreads();
             if (threadIdx.x == kScanThreads - 1)
