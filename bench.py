@@ -70,10 +70,10 @@ def kernel_source_digest(files) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary, or None when there is
-    none for this workload or the kernel sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+def _profile_summary(workload: str, kernel: str, what: str):
+    """key = value pairs of the committed counter summary profiles/<kernel>_<workload>_<what>.txt,
+    or None when there is none or the kernel sources changed since its counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_{what}.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -81,13 +81,37 @@ def measured_traffic(workload: str, kernel: str):
         for line in fh:
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
-                kv[k.strip()] = v.strip()
+                kv[k.strip()] = v.split("#", 1)[0].strip()
     try:
         if kv.get("source_digest") != kernel_source_digest(kv["sources"].split(",")):
             return None
-        return float(kv["hbm_bytes_per_launch"])
-    except (KeyError, ValueError, OSError):
+    except (KeyError, OSError):
         return None
+    return kv
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when there is
+    none for this workload or the kernel sources changed since the counters were taken."""
+    kv = _profile_summary(workload, kernel, "traffic")
+    try:
+        return float(kv["hbm_bytes_per_launch"]) if kv else None
+    except (KeyError, ValueError):
+        return None
+
+
+def measured_clock(workload: str, kernel: str, achieved: float, peak: float):
+    """The shader clock and matrix-core busy fraction that a counter run of the same kernel saw,
+    and the live figure against the peak scaled to that clock (the chip is power-limited below the
+    2.4 GHz the published peaks assume).  Empty when no current summary exists."""
+    kv = _profile_summary(workload, kernel, "clock")
+    try:
+        sclk = float(kv["sclk_mhz_median"])
+        return {"sclk_mhz": sclk, "peak_at_sclk": peak * sclk / 2400.0,
+                "frac_at_sclk": achieved / (peak * sclk / 2400.0),
+                "mfma_busy": float(kv["mfma_busy_median"])}
+    except (TypeError, KeyError, ValueError):
+        return {}
 
 
 def cpu_baseline(inp, budget_s: float):
@@ -195,7 +219,8 @@ def bench_grouped(args, torch, mel, synth, dv, dev):
         "roofline": {"kernel": "fc1_bf16", "bound": "mfma", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": measured_traffic(args.workload, "fc1_bf16"),
-                     "per_launch": f"{fl['fc1']:.4g} FLOP = 4*M*H*F, M={M} received rows"},
+                     "per_launch": f"{fl['fc1']:.4g} FLOP = 4*M*H*F, M={M} received rows",
+                     **measured_clock(args.workload, "fc1_bf16", achieved, peak)},
         "timing": {"median_ms": float(np.median(ms)), "p10_ms": float(np.percentile(ms, 10)),
                    "p90_ms": float(np.percentile(ms, 90))},
     }
@@ -354,7 +379,8 @@ def main():
         roof = {"kernel": dominant, "bound": "mfma", "achieved": achieved, "peak": peak,
                 "unit": "TFLOP/s", "frac": achieved / peak,
                 "traffic": measured_traffic(args.workload, dominant),
-                "per_launch": f"{dom_flops:.4g} FLOP = 2*M*H*F per projection, M={M} routed rows"}
+                "per_launch": f"{dom_flops:.4g} FLOP = 2*M*H*F per projection, M={M} routed rows",
+                **measured_clock(args.workload, dominant, achieved, peak)}
     else:
         gbs = bytes_[dominant] / (kavg[dominant] * 1e-3) / 1e9
         roof = {"kernel": dominant, "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
