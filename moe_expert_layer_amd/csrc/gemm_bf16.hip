@@ -365,23 +365,33 @@ struct CopyCtx {
     const uint16_t* b;     // this wave's weight matrix at the next step's first k row
     uint32_t a_lds;        // LDS destination of the wave's first A copy in pair stage 0
     uint32_t b_lds;        // LDS destination of the wave's first B copy in B stage 0
+    bool b_on;             // half-width task: this lane's weight chunk lies in the task's columns
 };
 
 // What a sub-step copies: nothing, the weights of one step, the second half of a pair's A, or the
-// weights of one step and then the first half of a pair's A.
-enum CopySet { kNone = 0, kB = 1, kA2 = 2, kBA1 = 3 };
+// weights of one step and then the first half of a pair's A.  kHalfW marks the weight copies of a
+// half-width task (only the lanes with b_on copy).
+enum CopySet { kNone = 0, kB = 1, kA2 = 2, kBA1 = 3, kHalfW = 4 };
 template <int CS>
-constexpr int set_size() { return CS == kNone ? 0 : CS == kBA1 ? kBCopies + kAHalf : CS == kB ? kBCopies : kAHalf; }
+constexpr int set_size()
+{
+    return (CS & 3) == kNone ? 0 : (CS & 3) == kBA1 ? kBCopies + kAHalf : (CS & 3) == kB ? kBCopies : kAHalf;
+}
 
 // Copy C of copy set CS: weights into B stage SB, A into pair stage QA.
 template <int CS, int SB, int QA, int C>
 __device__ __forceinline__ void copy_one(const CopyCtx& s, const uint32_t (&a_voff)[kACopies],
                                          const uint32_t (&b_voff)[kBCopies])
 {
-    if constexpr (CS == kA2) {
+    if constexpr ((CS & 3) == kA2) {
         lds_copy16(s.a, a_voff[kAHalf + C], s.a_lds + QA * kAPairBytes + (kAHalf + C) * 1024);
     } else if constexpr (C < kBCopies) {
-        lds_copy16(s.b, b_voff[C], s.b_lds + SB * kBBytes + C * 1024);
+        if constexpr ((CS & kHalfW) != 0) {
+            if (s.b_on)
+                lds_copy16(s.b, b_voff[C], s.b_lds + SB * kBBytes + C * 1024);
+        } else {
+            lds_copy16(s.b, b_voff[C], s.b_lds + SB * kBBytes + C * 1024);
+        }
     } else {
         lds_copy16(s.a, a_voff[C - kBCopies], s.a_lds + QA * kAPairBytes + (C - kBCopies) * 1024);
     }
@@ -527,12 +537,12 @@ constexpr int wait_odd() { return kA ? kBCopies : 2 * kBCopies; }
 // most W copies in flight; none for W < 0) and step t's stages are free; sub-step 0 of step t + 1
 // on the fragments of sub-step 1, with the weights of step t + 4 (and, t odd, the first A half of
 // pair (t + 3) / 2) when kCopyB.  kA = false: the wave copies no A.
-template <bool kGated, int NB, bool kA, int S, bool kCopyA2, bool kCopyB, int W>
+template <bool kGated, int NB, bool kA, bool kHalf, int S, bool kCopyA2, bool kCopyB, int W>
 __device__ __forceinline__ void k_step(f32x16_t (&acc)[kTM][kTN], Frags& f0, Frags& f1, CopyCtx& cp,
                                        const LoopArgs& g, int64_t N_w)
 {
     constexpr int CS1 = kA && S % 2 == 0 && kCopyA2 ? kA2 : kNone;
-    constexpr int CS2 = !kCopyB ? kNone : S % 2 == 0 || !kA ? kB : kBA1;
+    constexpr int CS2 = !kCopyB ? kNone : (S % 2 == 0 || !kA ? kB : kBA1) | (kHalf ? kHalfW : 0);
     constexpr int Qnext = (S / 2 + 1) % 2;                    // pair stage of pair t / 2 + 1
     substep<kGated, NB, CS1, 0, Qnext, S, 1>(acc, f0, f1, cp, g);
     if constexpr (CS1 == kA2)
@@ -553,7 +563,7 @@ __device__ __forceinline__ void k_step(f32x16_t (&acc)[kTM][kTN], Frags& f0, Fra
 template <bool kA>
 constexpr int top_wait() { return kA ? 3 * kBCopies + kAHalf : 3 * kBCopies; }   // steps 1 .. 3 (+ A)
 
-template <bool kGated, int NB, bool kA>
+template <bool kGated, int NB, bool kA, bool kHalf>
 __device__ __forceinline__ void k_loop(f32x16_t (&acc)[kTM][kTN], CopyCtx cp, const LoopArgs& g,
                                        int64_t N_w, int KT)
 {
@@ -563,16 +573,16 @@ __device__ __forceinline__ void k_loop(f32x16_t (&acc)[kTM][kTN], CopyCtx cp, co
     if constexpr (NB > 0)
         reads<kGated, 0, 0, 0, 2 * kTN + NB>(f0, g.a_base, g.b_base);
     for (int kt = 0; kt < KT - kStages; kt += kStages) {
-        k_step<kGated, NB, kA, 0, true, true, WE>(acc, f0, f1, cp, g, N_w);
-        k_step<kGated, NB, kA, 1, true, true, WO>(acc, f0, f1, cp, g, N_w);
-        k_step<kGated, NB, kA, 2, true, true, WE>(acc, f0, f1, cp, g, N_w);
-        k_step<kGated, NB, kA, 3, true, true, WO>(acc, f0, f1, cp, g, N_w);
+        k_step<kGated, NB, kA, kHalf, 0, true, true, WE>(acc, f0, f1, cp, g, N_w);
+        k_step<kGated, NB, kA, kHalf, 1, true, true, WO>(acc, f0, f1, cp, g, N_w);
+        k_step<kGated, NB, kA, kHalf, 2, true, true, WE>(acc, f0, f1, cp, g, N_w);
+        k_step<kGated, NB, kA, kHalf, 3, true, true, WO>(acc, f0, f1, cp, g, N_w);
     }
     // the last four steps: only the second A half of the last pair is still to be copied
-    k_step<kGated, NB, kA, 0, true, false, WE>(acc, f0, f1, cp, g, N_w);
-    k_step<kGated, NB, kA, 1, false, false, 0>(acc, f0, f1, cp, g, N_w);
-    k_step<kGated, NB, kA, 2, false, false, 0>(acc, f0, f1, cp, g, N_w);
-    k_step<kGated, NB, kA, 3, false, false, -1>(acc, f0, f1, cp, g, N_w);
+    k_step<kGated, NB, kA, kHalf, 0, true, false, WE>(acc, f0, f1, cp, g, N_w);
+    k_step<kGated, NB, kA, kHalf, 1, false, false, 0>(acc, f0, f1, cp, g, N_w);
+    k_step<kGated, NB, kA, kHalf, 2, false, false, 0>(acc, f0, f1, cp, g, N_w);
+    k_step<kGated, NB, kA, kHalf, 3, false, false, -1>(acc, f0, f1, cp, g, N_w);
 }
 
 // Epilogue through LDS.  The wave's output (64 rows x 64 columns for fc1, 64 x 128 for fc2) goes
@@ -671,7 +681,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
     const int wn = wave % kWN;
     const int n_mt = *tile_count;
     const int n_nt = N_out / BN;
-    const int total = n_mt * n_nt;
+    // Half-width tasks (non-gated, unchunked tables): the table ends in its short partial tiles (at
+    // most 64 rows, each its own run), whose tasks stream the whole weight strip for a few rows; each
+    // of their column tiles becomes two tasks of BN / 2 columns, so the launch's last tasks spread
+    // over twice as many CUs.  tile_count[2] holds the number of tiles before that suffix.
+    const int n_full = !kGated && chunk_done == nullptr ? min(max(tile_count[2], 0), n_mt) : n_mt;
+    const int t_full = n_full * n_nt;
+    const int total = t_full + 2 * (n_mt - n_full) * n_nt;
     const int KT = K / BK;
     const int64_t N_w = N_out;
 
@@ -722,6 +738,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
     // epilogue, so the epilogue hides their latency.
     MTile tile{};
     int n0 = 0;
+    bool half = false;                                        // a half-width task (see n_full)
+    // task t: its row tile, first output column and width
+    auto decode = [&](int t, int& col0, bool& is_half) -> MTile {
+        if (t < t_full) {
+            int nt;
+            const MTile tl = decode_task(t, n_nt, tiles, nt);
+            col0 = nt * BN;
+            is_half = false;
+            return tl;
+        }
+        const int r = (t - t_full) % (2 * n_nt);
+        col0 = (r >> 1) * BN + (r & 1) * (BN / 2);
+        is_half = true;
+        return tiles[n_full + (t - t_full) / (2 * n_nt)];
+    };
     uint32_t a_voff[kACopies];
     // Gathered fc1 rows: the slot-list entries of this lane's A copy rows for the next task, loaded
     // one task ahead (during the previous task's K loop) and first used in setup, so that nothing
@@ -730,8 +761,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
     auto fetch_rows = [&](int t) {
         if (gather == nullptr)
             return;
-        int nt;
-        const MTile tl = decode_task(t, n_nt, tiles, nt);
+        int c0;
+        bool hf;
+        const MTile tl = decode(t, c0, hf);
 #pragma unroll
         for (int j = 0; j < kACopies; ++j) {
             const int r = 8 * (kACopies * wave + j) + lane / 8;
@@ -739,9 +771,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
         }
     };
     auto setup = [&](int t) {
-        int nt;
-        tile = decode_task(t, n_nt, tiles, nt);
-        n0 = nt * BN;
+        tile = decode(t, n0, half);
+        // the weight chunks of the task's columns: chunk c of a 512-byte row holds columns 8c ..
+        // 8c + 7, and copy lanes 0 .. 15 (32 .. 47) take chunks 0 .. 15 whatever the swizzle
+        cp.b_on = !half || (lane & 16) == 0;
         const int rows = tile.row_end - tile.row_begin;
 #pragma unroll
         for (int j = 0; j < kACopies; ++j) {
@@ -758,14 +791,25 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
         if (a_on)
             issue_pair<0>(cp, a_voff);
         cp.a += 64;
-        copies<kB, 0, 0, 0, kBCopies>(cp, a_voff, b_voff);
-        cp.b += BK * N_w;
-        copies<kB, 1, 0, 0, kBCopies>(cp, a_voff, b_voff);
-        cp.b += BK * N_w;
-        copies<kB, 2, 0, 0, kBCopies>(cp, a_voff, b_voff);
-        cp.b += BK * N_w;
-        copies<kB, 3, 0, 0, kBCopies>(cp, a_voff, b_voff);
-        cp.b += BK * N_w;
+        if (!kGated && half) {
+            copies<kB | kHalfW, 0, 0, 0, kBCopies>(cp, a_voff, b_voff);
+            cp.b += BK * N_w;
+            copies<kB | kHalfW, 1, 0, 0, kBCopies>(cp, a_voff, b_voff);
+            cp.b += BK * N_w;
+            copies<kB | kHalfW, 2, 0, 0, kBCopies>(cp, a_voff, b_voff);
+            cp.b += BK * N_w;
+            copies<kB | kHalfW, 3, 0, 0, kBCopies>(cp, a_voff, b_voff);
+            cp.b += BK * N_w;
+        } else {
+            copies<kB, 0, 0, 0, kBCopies>(cp, a_voff, b_voff);
+            cp.b += BK * N_w;
+            copies<kB, 1, 0, 0, kBCopies>(cp, a_voff, b_voff);
+            cp.b += BK * N_w;
+            copies<kB, 2, 0, 0, kBCopies>(cp, a_voff, b_voff);
+            cp.b += BK * N_w;
+            copies<kB, 3, 0, 0, kBCopies>(cp, a_voff, b_voff);
+            cp.b += BK * N_w;
+        }
         if (a_on)
             copies<kBA1, 0, 1, kBCopies, kBCopies + kAHalf>(cp, a_voff, b_voff);
     };
@@ -782,8 +826,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
             *claimed = __builtin_amdgcn_readfirstlane(v);
         }
         const int rows = tile.row_end - tile.row_begin;
+        // a half-width task leaves the second column half (wave column 1) without work
+        const bool half_task = __builtin_amdgcn_readfirstlane(half ? 1 : 0) != 0;
         const int nb = __builtin_amdgcn_readfirstlane(
-            min(kTM, max(0, ((rows + 31) / 32 - wm + kWM - 1) / kWM)));
+            half_task && wn == 1 ? 0 : min(kTM, max(0, ((rows + 31) / 32 - wm + kWM - 1) / kWM)));
         // the wave copies A rows 32 wave .. + 31, row block `wave`; row block v is used by wave row
         // v % kWM, so a wave that copies no A has at most one row block (nb <= 1) and a wave without
         // row blocks copies no A
@@ -809,23 +855,44 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
         if (t_next < total)
             fetch_rows(t_next);
         const LoopArgs g{a_base, b_base, a_voff, b_voff};
-        if (nb == 0)
-            k_loop<kGated, 0, false>(acc, cp, g, N_w, KT);
-        else if (nb == 1 && !a_on)
-            k_loop<kGated, 1, false>(acc, cp, g, N_w, KT);
-        else if (nb == 1)
-            k_loop<kGated, 1, true>(acc, cp, g, N_w, KT);
-        else
-            k_loop<kGated, kTM, true>(acc, cp, g, N_w, KT);
+        bool ran = false;
+        if constexpr (!kGated) {
+            if (half_task) {
+                // the waves of column half 1 copy A rows for the others but compute nothing
+                if (nb == 0 && !a_on)
+                    k_loop<kGated, 0, false, true>(acc, cp, g, N_w, KT);
+                else if (nb == 0)
+                    k_loop<kGated, 0, true, true>(acc, cp, g, N_w, KT);
+                else if (nb == 1 && !a_on)
+                    k_loop<kGated, 1, false, true>(acc, cp, g, N_w, KT);
+                else if (nb == 1)
+                    k_loop<kGated, 1, true, true>(acc, cp, g, N_w, KT);
+                else
+                    k_loop<kGated, kTM, true, true>(acc, cp, g, N_w, KT);
+                ran = true;
+            }
+        }
+        if (!ran) {
+            if (nb == 0)
+                k_loop<kGated, 0, false, false>(acc, cp, g, N_w, KT);
+            else if (nb == 1 && !a_on)
+                k_loop<kGated, 1, false, false>(acc, cp, g, N_w, KT);
+            else if (nb == 1)
+                k_loop<kGated, 1, true, false>(acc, cp, g, N_w, KT);
+            else
+                k_loop<kGated, kTM, true, false>(acc, cp, g, N_w, KT);
+        }
         const MTile done = tile;
         const int done_n0 = n0;
+        const bool done_skip = half_task && wn == 1;          // columns of the other half task
         t = t_next;
         // every wave is past its last read of this task's stages (and of the claim word)
         __syncthreads();
         if (t < total)
             setup(t);
-        store_output_staged<kGated>(acc, C, done, done_n0, N_out, lds0 + kRingBytes + wave * kOutWaveBytes,
-                                     wm, wn, lane, chunk_done != nullptr);
+        if (!done_skip)
+            store_output_staged<kGated>(acc, C, done, done_n0, N_out, lds0 + kRingBytes + wave * kOutWaveBytes,
+                                         wm, wn, lane, chunk_done != nullptr);
         if constexpr (kGated) {
             if (save_g != nullptr) {
                 store_output_staged<kGated, 1>(acc, save_g, done, done_n0, N_out,

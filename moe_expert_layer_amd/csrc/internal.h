@@ -63,7 +63,7 @@ struct RouteLayout {
 struct FfnLayout {
     size_t status = 0;
     size_t tiles1 = 0, tiles2 = 0;     // MTile tables for fc1 / fc2 row-tile heights
-    size_t tile_count = 0;             // int32 [4]: fc1 tiles, fc2 tiles
+    size_t tile_count = 0;             // int32 [4]: [0] tiles in the table, [2] tiles before its short tails
     size_t task_ctr = 0;               // int32 [2][kXcdCount]: per-XCD task counters of fc1 / fc2
     size_t chunk_done = 0;             // int32 [num_chunks]: fc2 tiles finished per chunk
     size_t chunk_tiles = 0;            // int32 [num_chunks]: fc2 tiles per chunk
@@ -105,7 +105,9 @@ hipError_t launch_route_scatter(const int32_t* ids, int64_t M, int64_t E,
                                 const int32_t* block_counts, int64_t nblocks, int32_t* perm,
                                 int32_t* pos, hipStream_t s);
 // Builds the row-tile table: groups are rows [offsets[g], offsets[g+1]) (clamped into [0, M]) with expert
-// group_expert[g] (identity when null).  Writes tiles and *tile_count; when chunk_tiles is not
+// group_expert[g] (identity when null).  Writes tiles, tile_count[0] (their number) and tile_count[2]
+// (how many precede the suffix of short partial tiles, at most 64 rows, that an unchunked table with
+// sorted tails ends in; all of them otherwise); when chunk_tiles is not
 // null also the expected (row tile x column tile) tasks per chunk (row tiles * col_tiles) and
 // zeroes chunk_done; zeroes the 2 * kXcdCount task counters at task_ctr.  A non-empty group with an expert outside [0, E) is skipped and sets
 // *status; with write_status the status word is written either way.

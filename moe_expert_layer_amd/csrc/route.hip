@@ -23,6 +23,10 @@ constexpr int kThreads = 256;
 constexpr int kScanThreads = 1024;
 constexpr int kStatusOk = 0;
 constexpr int kStatusBadId = 4;   // MOE_ERR_EXPERT_ID_OUT_OF_RANGE
+// Partial tiles of at most this many rows are the ones the non-gated GEMM runs as two half-width
+// tasks: their time is the weight stream, which halves; for taller tiles the A rows that both halves
+// copy cost more than the split gains.
+constexpr int kHalfWidthMaxRows = 64;
 
 __global__ __launch_bounds__(kThreads) void route_count_kernel(const int32_t* __restrict__ ids,
                                                                int64_t M, int E,
@@ -206,9 +210,13 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
     __shared__ int buf[2 * (kScanThreads / 64)];
     __shared__ int carry;
     __shared__ int bad;
+    __shared__ int full_tiles;
+    __shared__ int tall_tails;        // partial tiles above kHalfWidthMaxRows rows (sorted tables)
     if (threadIdx.x == 0) {
         carry = 0;
         bad = 0;
+        full_tiles = 0;
+        tall_tails = 0;
     }
     if (chunk_tiles != nullptr)
         for (int c = threadIdx.x; c < num_chunks; c += kScanThreads) {
@@ -218,6 +226,8 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
     __syncthreads();
     const bool tails_last = num_chunks <= 1;
     for (int pass = 0; pass < (tails_last ? 2 : 1); ++pass) {
+        if (pass == 1 && threadIdx.x == 0)
+            full_tiles = carry;                   // read by thread 0 only, after the last barrier
         for (int g0 = 0; g0 < G; g0 += kScanThreads) {
             const int g = g0 + threadIdx.x;
             int64_t rb = 0, re = 0;
@@ -252,6 +262,8 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
                 __shared__ int tail_rows[kScanThreads];
                 const int mine = n != 0 ? static_cast<int>(re - rb) % bm : -1;
                 tail_rows[threadIdx.x] = mine;
+                if (mine > kHalfWidthMaxRows)
+                    atomicAdd(&tall_tails, 1);
                 __syncthreads();
                 int rank = 0;
                 if (n != 0) {                     // groups without a tail skip the count
@@ -319,6 +331,11 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
     }
     if (threadIdx.x == 0) {
         tile_count[0] = min(carry, max_tiles);
+        // tile_count[2]: how many tiles lead the table before the short partial tiles (rows <=
+        // kHalfWidthMaxRows) that the non-gated GEMM splits into half-width tasks.  Only an unchunked
+        // table whose tails were sorted (longest first, one pass over the groups) has such a suffix.
+        const bool sorted_tails = tails_last && G <= kScanThreads;
+        tile_count[2] = sorted_tails ? min(full_tiles + tall_tails, max_tiles) : min(carry, max_tiles);
         if (write_status)
             *status = bad ? kStatusBadId : kStatusOk;
         else if (bad)
