@@ -4,6 +4,8 @@ Every call goes through the C ABI (via the ctypes binding).  Bars: integer work 
 perm, pos, permute bytes) bit-exact; float outputs within max|gpu - oracle| / max|oracle|
 <= 2e-2 for bfloat16 and 1e-5 for float32 (see the tolerance derivation in the design notes).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -182,6 +184,41 @@ def test_chunked_equals_unchunked(dtype, head, T, H, F):
     torch.cuda.synchronize()
     assert done.shape[0] == -(-2 * T // head)
     assert np.array_equal(dv.host(done), dv.host(expected)) and dv.host(expected).min() > 0
+
+
+def _layer_with_counts(counts, H, F, seed=11):
+    """A bfloat16 k = 1 layer whose experts receive exactly `counts` tokens (seeded token order and
+    routing weights; x and weights from the common generator)."""
+    T, E = int(sum(counts)), len(counts)
+    inp = synth.make_layer(T=T, H=H, F=F, E=E, k=1, dtype="bf16", seed=seed)
+    rng = np.random.default_rng(seed)
+    ids = rng.permutation(np.repeat(np.arange(E, dtype=np.int32), counts)).reshape(T, 1)
+    probs = rng.uniform(0.5, 1.0, size=(T, 1)).astype(np.float32)
+    return dataclasses.replace(inp, expert_ids=ids.astype(np.int32), probs=probs)
+
+
+def test_short_partial_tiles_half_width_tasks():
+    """Last row tiles of 1, 44 and 64 rows and an expert with one 64-row tile (the down projection
+    runs their column tiles as two half-width tasks) beside a 65-row one (kept whole) and an empty
+    expert: the output matches the oracle, is bitwise the chunked one (chunked tables never split),
+    and the backward that recomputes g and u (same kernel, same split) is bitwise the one that takes
+    the forward's saved values."""
+    inp = _layer_with_counts([257, 300, 320, 321, 0, 64], H=512, F=256)
+    ref, *_ = oracle.forward(inp)
+    d = dv.layer(inp)
+    out = dv.host(dv.forward(mel, d, 0))
+    err = oracle.inf_norm_rel(out, ref)
+    print(f"short tails: inf-norm rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+    assert np.array_equal(dv.host(dv.forward(mel, d, 512)), out)
+    dout = dv.tensor(synth.make_dout(inp))
+    _, saved = mel.expert_forward_train(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs)
+    a = mel.expert_backward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs, dout)
+    b = mel.expert_backward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs, dout,
+                            saved_gu=saved)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
 
 
 def test_invariances_bitwise():
