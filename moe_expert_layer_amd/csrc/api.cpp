@@ -110,20 +110,33 @@ public:
             return;
         a_ = take_event(t);
         b_ = take_event(t);
-        if (a_ && b_)
-            hipEventRecord(a_, s_);
+        if (!a_ || !b_ || hipEventRecord(a_, s_) != hipSuccess)
+            release(t);                           // timing is best effort: this launch goes untimed
     }
     ~Timed()
     {
         if (!a_ || !b_)
             return;
-        hipEventRecord(b_, s_);
+        const bool ok = hipEventRecord(b_, s_) == hipSuccess;
         Timing& t = timing();
         std::lock_guard<std::mutex> g(t.mu);
-        t.pending.push_back({name_, a_, b_});
+        if (ok)
+            t.pending.push_back({name_, a_, b_});
+        else
+            release(t);
     }
 
 private:
+    // gives the events back to the pool (t.mu held); the launch is then not timed
+    void release(Timing& t)
+    {
+        if (a_)
+            t.pool.push_back(a_);
+        if (b_)
+            t.pool.push_back(b_);
+        a_ = b_ = nullptr;
+    }
+
     hipStream_t s_;
     const char* name_;
     hipEvent_t a_ = nullptr, b_ = nullptr;
@@ -276,7 +289,8 @@ const DeviceInfo& device_info()
     static std::mutex mu;
     static std::map<int, DeviceInfo> cache;
     int dev = 0;
-    hipGetDevice(&dev);
+    if (hipGetDevice(&dev) != hipSuccess)
+        dev = 0;                                  // no current device: the launch itself will fail
     std::lock_guard<std::mutex> g(mu);
     auto it = cache.find(dev);
     if (it != cache.end())
@@ -944,7 +958,7 @@ MOE_API moe_status moe_timing_reset(void)
     Timing& t = timing();
     std::lock_guard<std::mutex> g(t.mu);
     for (TimingRec& r : t.pending) {
-        hipEventSynchronize(r.b);
+        (void)hipEventSynchronize(r.b);           // the events are recycled either way
         t.pool.push_back(r.a);
         t.pool.push_back(r.b);
     }
