@@ -308,6 +308,24 @@ def test_grouped_ffn_matches_oracle():
     assert torch.equal(y, y2)
 
 
+def test_grouped_ffn_short_groups_large_tiles():
+    """Source-major groups of 257, 44, 64, 0, 65 and 300 rows at large-tile sizes: partial tiles of 1,
+    44 and 64 rows run as half-width down-projection tasks, the 65-row one whole; the output matches
+    the oracle and is bitwise the chunked one."""
+    sizes = [257, 44, 64, 0, 65, 300]
+    g = synth.make_grouped(rows=sum(sizes), H=512, F=256, E_local=2, sources=3, seed=5)
+    g = dataclasses.replace(g, group_offsets=np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32),
+                            recv_counts=np.asarray(sizes, np.int64).reshape(3, 2))
+    ref = oracle.grouped_ffn(g)
+    args = (dv.tensor(g.rows), dv.tensor(g.group_offsets), dv.tensor(g.group_expert),
+            dv.tensor(g.w_gate), dv.tensor(g.w_up), dv.tensor(g.w_down))
+    y = mel.grouped_ffn(*args)
+    err = oracle.inf_norm_rel(dv.host(y), ref)
+    print(f"short groups: inf-norm rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+    assert torch.equal(y, mel.grouped_ffn(*args, head_m_size=256))
+
+
 def test_grouped_ffn_bad_group_expert_flagged():
     g = synth.make_grouped(rows=300, H=128, F=64, E_local=2, sources=8, seed=3)
     ge = g.group_expert.copy()
