@@ -2,7 +2,9 @@
 
 Every call goes through the C ABI (via the ctypes binding).  Bars: integer work (counts, offsets,
 perm, pos, permute bytes) bit-exact; float outputs within max|gpu - oracle| / max|oracle|
-<= 2e-2 for bfloat16 and 1e-5 for float32 (see the tolerance derivation in the design notes).
+<= 2e-2 for bfloat16 and 6e-2 for MX-FP8 (the stated bars) and 1e-5 for float32 (fp32 accumulation
+over at most 14336 products of N(0,1) and N(0,0.02) values keeps that error near 1e-6; 1e-5 leaves
+a tenfold margin).
 """
 import dataclasses
 
