@@ -67,6 +67,14 @@ enum moe_dtype_code { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8_E4M3 = 2 };
  * on x_perm instead; the result is bitwise the same either way. */
 #define MOE_FLAG_SEPARATE_PERMUTE 1u
 
+/* The chunk height that "MC2 通算融合架构总览", §6 (切分策略) uses for its M-axis split: the
+ * recommended moe_problem.head_m_size for a chunked call (0 still means unchunked). */
+#define MOE_DEFAULT_HEAD_M_SIZE 512
+
+/* Largest H and F the library accepts (MOE_ERR_UNSUPPORTED beyond): the grouped GEMMs address a
+ * row tile's operands by 32-bit offsets from the tile's first row. */
+#define MOE_MAX_HIDDEN (1 << 22)
+
 typedef struct moe_problem {
     int64_t T;            /* tokens                                                              */
     int64_t H;            /* hidden size                                                         */
@@ -77,7 +85,8 @@ typedef struct moe_problem {
     int32_t head_m_size;  /* 0: unchunked.  Otherwise the permuted rows are processed in chunks of
                              this many rows (a multiple of 256), in chunk order, and each chunk's
                              completion is counted in the workspace.  The M-axis split and its 512-row
-                             default are those of "MC2 通算融合架构总览", §6 切分策略; the result is
+                             default (MOE_DEFAULT_HEAD_M_SIZE, the value to pass for the pages' chunked
+                             mode) are those of "MC2 通算融合架构总览", §6 切分策略; the result is
                              bitwise identical to the unchunked one.                              */
     uint32_t flags;       /* 0, or MOE_FLAG_SEPARATE_PERMUTE                                     */
     uint32_t reserved;    /* must be 0                                                           */
@@ -235,6 +244,19 @@ moe_status moe_router_topk(const float* logits, int64_t T, int64_t E, int64_t k,
  * Integer arithmetic on the float32 bits: bit-exact and deterministic. */
 moe_status moe_mx_quantize(const float* v, int64_t rows, int64_t cols, uint8_t* codes,
                            uint8_t* scales, hipStream_t stream);
+
+/* The encoder of the MX layer's fc1 epilogue (the SwiGLU output h -> E4M3 codes and E8M0 block
+ * scales along F, "MC2 通算融合架构总览", §1 and §5), run by the same device code as inside the
+ * grouped GEMM (the staging through LDS, the block maximum combined across lanes, the encoding and
+ * the stores) but on caller-supplied float32 values in place of the SwiGLU output, so that the
+ * epilogue can be checked exactly against a reference encoder.  v [rows, cols] float32 -> codes
+ * [rows, cols] and scales [rows, cols/32], with moe_mx_quantize's rule.  large_tiles != 0: the
+ * epilogue of the 256-row-tile kernel (cols a multiple of 128; the one serving H and F multiples of
+ * 1024), else that of the 128-row-tile kernel (cols a multiple of 64).  rows * cols <= 2^28.
+ * Errors: MOE_ERR_INVALID_ARGUMENT for bad sizes or null pointers (nothing enqueued). */
+moe_status moe_mx_fc1_epilogue_encode(const float* v, int64_t rows, int64_t cols,
+                                      int32_t large_tiles, uint8_t* codes, uint8_t* scales,
+                                      hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Status, errors, diagnostics.

@@ -18,7 +18,8 @@ __all__ = [
     "MoeError", "library", "lib_path", "F32", "BF16", "MXFP8",
     "workspace_size", "expert_forward", "expert_forward_mx", "expert_forward_train",
     "backward_workspace_size", "expert_backward", "route", "permute", "unpermute",
-    "grouped_ffn_workspace_size", "grouped_ffn", "grouped_ffn_mx", "mx_quantize", "device_status", "chunk_counters",
+    "grouped_ffn_workspace_size", "grouped_ffn", "grouped_ffn_mx", "mx_quantize",
+    "mx_fc1_epilogue_encode", "device_status", "chunk_counters",
     "intermediate_h",
     "timing_enable", "timing_collect", "timing_reset",
 ]
@@ -65,6 +66,7 @@ _SIGS = {
     "moe_grouped_ffn_mx": [ctypes.POINTER(MoeProblem), _P, _P, _I64, _P, _P, _I64, _P, _P, _P,
                            _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_mx_quantize": [_P, _I64, _I64, _P, _P, _P],
+    "moe_mx_fc1_epilogue_encode": [_P, _I64, _I64, ctypes.c_int32, _P, _P, _P],
     "moe_router_topk": [_P, _I64, _I64, _I64, _P, _P, _P],
     "moe_query_device_status": [_P, _P, ctypes.POINTER(ctypes.c_int32)],
     "moe_chunk_counters": [ctypes.POINTER(MoeProblem), _P, ctypes.c_size_t, _I64,
@@ -304,26 +306,34 @@ def route(expert_ids, E: int, workspace=None):
     return counts, offsets, perm, pos, ws
 
 
-def permute(x, pos, k: int, E: int | None = None, x_scale=None, F: int = 128):
-    """x_perm[pos[s]] = x[s // k].  x float32 / bfloat16, or uint8 MX codes with x_scale."""
+def permute(x, pos, k: int, E: int | None = None, x_scale=None, F: int = 128, x_perm=None,
+            x_perm_scale=None):
+    """x_perm[pos[s]] = x[s // k].  x float32 / bfloat16, or uint8 MX codes with x_scale.  The
+    outputs are allocated unless given."""
     T, H = x.shape
     mx = x.dtype == torch.uint8
     dt = MXFP8 if mx else _dtype_code(x)
     _need(x, "x")
     _need(pos, "pos", torch.int32, (T * k,), x.device)
     prob = problem(T, H, F, E if E is not None else k, k, dt)
-    x_perm = torch.empty((T * k, H), dtype=x.dtype, device=x.device)
+    if x_perm is None:
+        x_perm = torch.empty((T * k, H), dtype=x.dtype, device=x.device)
+    _need(x_perm, "x_perm", x.dtype, (T * k, H), x.device)
     xs_perm = None
     if mx:
         _need(x_scale, "x_scale", torch.uint8, (T, H // 32), x.device)
-        xs_perm = torch.empty((T * k, H // 32), dtype=torch.uint8, device=x.device)
+        xs_perm = x_perm_scale
+        if xs_perm is None:
+            xs_perm = torch.empty((T * k, H // 32), dtype=torch.uint8, device=x.device)
+        _need(xs_perm, "x_perm_scale", torch.uint8, (T * k, H // 32), x.device)
     _check(library().moe_permute(ctypes.byref(prob), _ptr(x), _ptr(x_scale), _ptr(pos),
                                  _ptr(x_perm), _ptr(xs_perm), _stream(x)))
     return (x_perm, xs_perm) if mx else x_perm
 
 
-def unpermute(y_perm, pos, probs, F: int = 128, E: int | None = None):
-    """out[t] = sum_j probs[t,j] * y_perm[pos[t*k+j]] (float32 or bfloat16 rows)."""
+def unpermute(y_perm, pos, probs, F: int = 128, E: int | None = None, out=None):
+    """out[t] = sum_j probs[t,j] * y_perm[pos[t*k+j]] (float32 or bfloat16 rows); out is allocated
+    unless given."""
     T, k = probs.shape
     M, H = y_perm.shape
     dt = _dtype_code(y_perm)
@@ -333,7 +343,9 @@ def unpermute(y_perm, pos, probs, F: int = 128, E: int | None = None):
     if M != T * k:
         raise ValueError("y_perm must have T*k rows")
     prob = problem(T, H, F, E if E is not None else k, k, dt)
-    out = torch.empty((T, H), dtype=y_perm.dtype, device=y_perm.device)
+    if out is None:
+        out = torch.empty((T, H), dtype=y_perm.dtype, device=y_perm.device)
+    _need(out, "out", y_perm.dtype, (T, H), y_perm.device)
     _check(library().moe_unpermute(ctypes.byref(prob), _ptr(y_perm), _ptr(pos), _ptr(probs),
                                    _ptr(out), _stream(y_perm)))
     return out
@@ -407,6 +419,18 @@ def mx_quantize(v):
     codes = torch.empty((rows, cols), dtype=torch.uint8, device=v.device)
     scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=v.device)
     _check(library().moe_mx_quantize(_ptr(v), rows, cols, _ptr(codes), _ptr(scales), _stream(v)))
+    return codes, scales
+
+
+def mx_fc1_epilogue_encode(v, large_tiles: bool = True):
+    """The MX fc1 epilogue's encoder (the GEMM's own device code) on float32 v [rows, cols] in place
+    of the SwiGLU output -> (codes uint8 [rows, cols], scales uint8 [rows, cols/32])."""
+    _need(v, "v", torch.float32)
+    rows, cols = v.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=v.device)
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=v.device)
+    _check(library().moe_mx_fc1_epilogue_encode(_ptr(v), rows, cols, 1 if large_tiles else 0,
+                                                _ptr(codes), _ptr(scales), _stream(v)))
     return codes, scales
 
 

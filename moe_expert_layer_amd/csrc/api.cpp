@@ -199,8 +199,10 @@ moe_status check_problem(const moe_problem* p, bool need_tokens, bool gemm = tru
             return fail(MOE_ERR_UNSUPPORTED, "MX GEMMs need H and F multiples of 128");
         break;
     }
-    if (p->H > INT32_MAX / 16 || p->F > INT32_MAX / 16)
-        return fail(MOE_ERR_UNSUPPORTED, "H or F too large");
+    // the GEMMs address a row tile's operands by 32-bit offsets from its first row (at most 256
+    // rows of K elements, 32 weight rows of N), which this bound keeps below 2^31 bytes
+    if (p->H > MOE_MAX_HIDDEN || p->F > MOE_MAX_HIDDEN)
+        return fail(MOE_ERR_UNSUPPORTED, "H and F must be at most %d", MOE_MAX_HIDDEN);
     return MOE_OK;
 }
 
@@ -829,6 +831,24 @@ MOE_API moe_status moe_mx_quantize(const float* v, int64_t rows, int64_t cols, u
     return MOE_OK;
 }
 
+MOE_API moe_status moe_mx_fc1_epilogue_encode(const float* v, int64_t rows, int64_t cols,
+                                              int32_t large_tiles, uint8_t* codes, uint8_t* scales,
+                                              hipStream_t stream)
+{
+    const int64_t bn = large_tiles ? 128 : 64;
+    if (rows < 0 || cols <= 0 || cols % bn != 0 || rows * cols > (int64_t{1} << 28))
+        return fail(MOE_ERR_INVALID_ARGUMENT,
+                    "need rows >= 0, cols a positive multiple of %lld and rows * cols <= 2^28",
+                    static_cast<long long>(bn));
+    if (rows == 0)
+        return MOE_OK;
+    if (v == nullptr || codes == nullptr || scales == nullptr)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+    LAUNCH(stream, "mx_epilogue_probe",
+           launch_mx_epilogue_probe(v, rows, cols, large_tiles != 0, codes, scales, stream));
+    return MOE_OK;
+}
+
 MOE_API moe_status moe_router_topk(const float* logits, int64_t T, int64_t E, int64_t k,
                                    int32_t* expert_ids, float* probs, hipStream_t stream)
 {
@@ -966,3 +986,4 @@ MOE_API moe_status moe_timing_reset(void)
     t.totals.clear();
     return MOE_OK;
 }
+

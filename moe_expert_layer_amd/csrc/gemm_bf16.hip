@@ -275,12 +275,14 @@ __global__ __launch_bounds__(kWM * kWN * 64, kMinBlocks) void grouped_gemm_bf16(
         bsrc += static_cast<int64_t>(kg * G::kBRows) * N_w;
 
         // A rows this thread stages (clamped into the tile; rows past row_end are never stored), as
-        // element offsets from A (the host bounds M * K below 2^31)
+        // element offsets from the tile's first row: below BM * K, which the host keeps under 2^31
+        // (K <= 2^22), whatever the number of rows M
+        const uint16_t* A_tile = A + static_cast<int64_t>(tile.row_begin) * K;
         uint32_t aoff[G::kAChunks];
 #pragma unroll
         for (int i = 0; i < G::kAChunks; ++i) {
-            const int grow = min(tile.row_begin + tid / 8 + (G::kThreads / 8) * i, tile.row_end - 1);
-            aoff[i] = static_cast<uint32_t>(grow) * static_cast<uint32_t>(K) + (tid % 8) * 8;
+            const int trow = min(tid / 8 + (G::kThreads / 8) * i, tile.row_end - 1 - tile.row_begin);
+            aoff[i] = static_cast<uint32_t>(trow) * static_cast<uint32_t>(K) + (tid % 8) * 8;
         }
         const int a_lds0 = lds_off(tid / 8, (tid % 8) * 8);
 
@@ -294,9 +296,9 @@ __global__ __launch_bounds__(kWM * kWN * 64, kMinBlocks) void grouped_gemm_bf16(
                     acc[i][j][r] = 0.0f;
 
         switch (nb) {
-        case 0: k_loop<G, kWM, kTM, kTN, 0>(acc, smem, A, aoff, bsrc, N_w, a_lds0, b0, kg, KT, wm, wn, lane); break;
-        case 1: k_loop<G, kWM, kTM, kTN, 1>(acc, smem, A, aoff, bsrc, N_w, a_lds0, b0, kg, KT, wm, wn, lane); break;
-        default: k_loop<G, kWM, kTM, kTN, kTM>(acc, smem, A, aoff, bsrc, N_w, a_lds0, b0, kg, KT, wm, wn, lane); break;
+        case 0: k_loop<G, kWM, kTM, kTN, 0>(acc, smem, A_tile, aoff, bsrc, N_w, a_lds0, b0, kg, KT, wm, wn, lane); break;
+        case 1: k_loop<G, kWM, kTM, kTN, 1>(acc, smem, A_tile, aoff, bsrc, N_w, a_lds0, b0, kg, KT, wm, wn, lane); break;
+        default: k_loop<G, kWM, kTM, kTN, kTM>(acc, smem, A_tile, aoff, bsrc, N_w, a_lds0, b0, kg, KT, wm, wn, lane); break;
         }
         store_output<kGated, kWM, kTM, kTN>(acc, C, tile, n0, N_out, wm, wn, lane, save_g, save_u);
         if (chunk_done != nullptr)

@@ -149,6 +149,56 @@ __device__ __forceinline__ void mx_store(unsigned char* smem, int buf, const Sta
         *reinterpret_cast<u32x4_t*>(Bsc + (tid / 8) * BNB + (tid % 8) * 16) = st.bsc;
 }
 
+// fc1 epilogue of the 128-row tiles: the wave's 64 rows x 32 output columns go in fp32 into its LDS
+// stage [64 rows][32 columns] (padded rows), then one lane per row encodes its 32-column block.
+// kSwiGLU: the value of output (row, column) is swiglu(gate accumulator, up accumulator) (the GEMM);
+// otherwise the gate accumulator itself (the encoder probe, which loads caller values there).  All
+// threads of the workgroup call it (two workgroup barriers).
+template <bool kSwiGLU>
+__device__ __forceinline__ void store_h_small(const f32x16_t (&acc)[kTM][kTN], unsigned char* smem,
+                                              uint8_t* __restrict__ Cq, uint8_t* __restrict__ Cq_sc,
+                                              const MTile& tile, int n0, int N_out, int wave, int lane)
+{
+    const int wm = wave / kWN, wn = wave % kWN;
+    const int h = lane >> 5;
+    float* stage = reinterpret_cast<float*>(smem) + wave * 64 * kStageLd;
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+            stage[row * kStageLd + (lane & 31)] = kSwiGLU ? swiglu(acc[i][0][r], acc[i][1][r]) : acc[i][0][r];
+        }
+    __syncthreads();
+    const int grow = tile.row_begin + wm * kTM * 32 + lane;
+    if (grow < tile.row_end) {
+        const f32x4_t* src = reinterpret_cast<const f32x4_t*>(stage + lane * kStageLd);
+        f32x4_t x[8];
+        uint32_t amax = 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            x[q] = src[q];
+#pragma unroll
+            for (int z = 0; z < 4; ++z)
+                amax = max(amax, __float_as_uint(x[q][z]) & 0x7fffffffu);
+        }
+        const int e = mx_shared_exponent(amax);
+        u32x4_t out[2];
+#pragma unroll
+        for (int w = 0; w < 8; ++w)
+            out[w / 4][w % 4] = e4m3_encode_scaled(x[w][0], e) |
+                                (e4m3_encode_scaled(x[w][1], e) << 8) |
+                                (e4m3_encode_scaled(x[w][2], e) << 16) |
+                                (e4m3_encode_scaled(x[w][3], e) << 24);
+        const int hcol = n0 + 32 * wn;         // this wave's 32 output columns
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(Cq + static_cast<int64_t>(grow) * N_out + hcol);
+        dst[0] = out[0];
+        dst[1] = out[1];
+        Cq_sc[static_cast<int64_t>(grow) * (N_out / 32) + hcol / 32] = static_cast<uint8_t>(e + 127);
+    }
+    __syncthreads();
+}
+
 template <bool kGated>
 __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_mx(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ A_sc,
@@ -262,45 +312,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_mx(
         }
 
         if constexpr (kGated) {
-            // SwiGLU in fp32 into this wave's LDS stage [64 rows][32 columns] (padded rows), then
-            // one lane per row encodes its 32-column block.
-            float* stage = reinterpret_cast<float*>(smem) + wave * 64 * kStageLd;
-#pragma unroll
-            for (int i = 0; i < kTM; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                    stage[row * kStageLd + (lane & 31)] = swiglu(acc[i][0][r], acc[i][1][r]);
-                }
-            __syncthreads();
-            const int grow = tile.row_begin + wm * kTM * 32 + lane;
-            if (grow < tile.row_end) {
-                const f32x4_t* src = reinterpret_cast<const f32x4_t*>(stage + lane * kStageLd);
-                f32x4_t x[8];
-                uint32_t amax = 0;
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    x[q] = src[q];
-#pragma unroll
-                    for (int z = 0; z < 4; ++z)
-                        amax = max(amax, __float_as_uint(x[q][z]) & 0x7fffffffu);
-                }
-                const int e = mx_shared_exponent(amax);
-                u32x4_t out[2];
-#pragma unroll
-                for (int w = 0; w < 8; ++w)
-                    out[w / 4][w % 4] = e4m3_encode_scaled(x[w][0], e) |
-                                        (e4m3_encode_scaled(x[w][1], e) << 8) |
-                                        (e4m3_encode_scaled(x[w][2], e) << 16) |
-                                        (e4m3_encode_scaled(x[w][3], e) << 24);
-                const int hcol = n0 + 32 * wn;         // this wave's 32 output columns
-                u32x4_t* dst = reinterpret_cast<u32x4_t*>(Cq + static_cast<int64_t>(grow) * N_out + hcol);
-                dst[0] = out[0];
-                dst[1] = out[1];
-                Cq_sc[static_cast<int64_t>(grow) * (N_out / 32) + hcol / 32] =
-                    static_cast<uint8_t>(e + 127);
-            }
-            __syncthreads();
+            store_h_small<true>(acc, smem, Cq, Cq_sc, tile, n0, N_out, wave, lane);
         } else {
 #pragma unroll
             for (int i = 0; i < kTM; ++i)
@@ -694,6 +706,9 @@ __device__ __forceinline__ uint32_t h_stage_off(int row, int col)
     return row * 128 + 16 * (((col >> 2) ^ row) & 7) + 4 * (col & 3);
 }
 
+// kSwiGLU: the value of output (row, column) is swiglu(gate accumulator, up accumulator) (the GEMM);
+// otherwise the gate accumulator itself (the encoder probe, which loads caller values there).
+template <bool kSwiGLU>
 __device__ __forceinline__ void store_h(const f32x16_t (&acc)[kTM][kTN], uint8_t* __restrict__ Cq,
                                         uint8_t* __restrict__ Cq_sc, const MTile& tile, int n0,
                                         int N_out, uint32_t stage, int wm, int wn, int lane)
@@ -712,7 +727,8 @@ __device__ __forceinline__ void store_h(const f32x16_t (&acc)[kTM][kTN], uint8_t
                     const int r = 8 * half + rr;
                     const int row = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
                     *reinterpret_cast<__attribute__((address_space(3))) float*>(
-                        stage + h_stage_off(row, lane & 31)) = swiglu(acc[i][2 * ob][r], acc[i][2 * ob + 1][r]);
+                        stage + h_stage_off(row, lane & 31)) =
+                        kSwiGLU ? swiglu(acc[i][2 * ob][r], acc[i][2 * ob + 1][r]) : acc[i][2 * ob][r];
                 }
                 const f32x4_t x0 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(
                     stage + h_stage_off(erow, 8 * eq));
@@ -940,7 +956,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
             setup(t);
         const uint32_t stg = lds0 + kOutBase + wave * kOutWaveBytes;
         if constexpr (kGated)
-            store_h(acc, Cq, Cq_sc, done, done_n0, N_out, stg, wm, wn, lane);
+            store_h<true>(acc, Cq, Cq_sc, done, done_n0, N_out, stg, wm, wn, lane);
         else
             store_y(acc, Cy, done, done_n0, N_out, stg, wm, wn, lane, chunk_done != nullptr);
         if (chunk_done != nullptr)
@@ -948,7 +964,79 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
     }
 }
 
+// The fc1 epilogue's encoder on caller values: workgroup (x, y) takes output columns [128 x, 128 x +
+// 128) and rows [256 y, 256 y + 256) of v [rows, cols], puts each value in the gate accumulator
+// register that holds that output in the GEMM (32 x 32 block layout: lane column lane % 32, rows
+// 8 (r / 4) + 4 (lane / 32) + r % 4), and runs store_h on them without the SwiGLU.
+__global__ __launch_bounds__(kThreads, 1) void mx_epilogue_probe(const float* __restrict__ v, int rows,
+                                                                 int cols, uint8_t* __restrict__ codes,
+                                                                 uint8_t* __restrict__ scales)
+{
+    __shared__ __attribute__((aligned(256))) unsigned char stg[kWaves * kOutWaveBytes];
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) unsigned char*)(stg)));
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / kWN, wn = wave % kWN;
+    MTile tile{};
+    tile.row_begin = static_cast<int>(blockIdx.y) * BM;
+    tile.row_end = min(rows, tile.row_begin + BM);
+    const int n0 = static_cast<int>(blockIdx.x) * (BNB / 2);
+    f32x16_t acc[kTM][kTN];
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[i][j][r] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = tile.row_begin + row_block<kWM>(i, wm) + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const int col = n0 + 64 * wn + 32 * ob + (lane & 31);
+                acc[i][2 * ob][r] = row < tile.row_end ? v[static_cast<int64_t>(row) * cols + col] : 0.0f;
+            }
+    store_h<false>(acc, codes, scales, tile, n0, cols, lds0 + wave * kOutWaveBytes, wm, wn, lane);
+}
+
 }  // namespace big
+
+// The 128-row-tile fc1 epilogue's encoder on caller values (see big::mx_epilogue_probe): workgroup
+// (x, y) takes output columns [64 x, 64 x + 64) and rows [128 y, 128 y + 128).
+__global__ __launch_bounds__(kThreads) void mx_epilogue_probe_small(const float* __restrict__ v, int rows,
+                                                                    int cols, uint8_t* __restrict__ codes,
+                                                                    uint8_t* __restrict__ scales)
+{
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kEpiBytes];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / kWN, wn = wave % kWN;
+    MTile tile{};
+    tile.row_begin = static_cast<int>(blockIdx.y) * BM;
+    tile.row_end = min(rows, tile.row_begin + BM);
+    const int n0 = static_cast<int>(blockIdx.x) * (BNB / 2);
+    f32x16_t acc[kTM][kTN];
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[i][j][r] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = tile.row_begin + wm * kTM * 32 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int col = n0 + 32 * wn + (lane & 31);
+            acc[i][0][r] = row < tile.row_end ? v[static_cast<int64_t>(row) * cols + col] : 0.0f;
+        }
+    store_h_small<false>(acc, smem, codes, scales, tile, n0, cols, wave, lane);
+}
 
 // The large kernels run K loops of whole 16-step units (H / 64, F / 64 multiples of 16).
 bool mx_use_big(int64_t H, int64_t F) { return H % 1024 == 0 && F % 1024 == 0; }
@@ -990,6 +1078,25 @@ hipError_t launch_mx_quantize(const float* v, int64_t rows, int64_t cols, uint8_
     const int64_t cap = static_cast<int64_t>(device_info().cu_count) * 8;
     mx_quantize_kernel<<<dim3(static_cast<unsigned>(want < cap ? (want > 0 ? want : 1) : cap)),
                          dim3(kThreads), 0, s>>>(v, nblocks, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_epilogue_probe(const float* v, int64_t rows, int64_t cols, bool large_tiles,
+                                   uint8_t* codes, uint8_t* scales, hipStream_t s)
+{
+    const int bn = large_tiles ? big::BNB / 2 : BNB / 2;
+    const int bm = large_tiles ? big::BM : BM;
+    if (rows <= 0)
+        return hipSuccess;
+    if (cols % bn != 0 || rows * cols > (int64_t{1} << 28))
+        return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(cols / bn), static_cast<unsigned>(ceil_div(rows, bm)));
+    if (large_tiles)
+        big::mx_epilogue_probe<<<grid, dim3(big::kThreads), 0, s>>>(v, static_cast<int>(rows),
+                                                                    static_cast<int>(cols), codes, scales);
+    else
+        mx_epilogue_probe_small<<<grid, dim3(kThreads), 0, s>>>(v, static_cast<int>(rows),
+                                                                static_cast<int>(cols), codes, scales);
     return hipGetLastError();
 }
 

@@ -217,5 +217,10 @@ hipError_t launch_router(const float* logits, int64_t T, int64_t E, int64_t k, i
                          float* probs, hipStream_t s);
 hipError_t launch_mx_quantize(const float* v, int64_t rows, int64_t cols, uint8_t* codes,
                               uint8_t* scales, hipStream_t s);
+// The MX fc1 epilogue's encoder (large_tiles: the 256-row kernel's, else the 128-row kernel's) on
+// float32 values v [rows, cols] in place of the SwiGLU output; cols a multiple of 128 (64), rows * cols
+// <= 2^28.
+hipError_t launch_mx_epilogue_probe(const float* v, int64_t rows, int64_t cols, bool large_tiles,
+                                   uint8_t* codes, uint8_t* scales, hipStream_t s);
 
 }  // namespace moe

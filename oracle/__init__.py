@@ -324,6 +324,21 @@ def wgrad_entries(inp, dout, e, f, h):
     return tuple(out)
 
 
+def row_inf_norm_rel(a, ref) -> float:
+    """max over rows r of max |a_r - ref_r| / max |ref_r| (rows whose reference is all zero count
+    their absolute error): the per-token form of inf_norm_rel, so that a wrong row with small
+    outputs cannot hide under the largest row of the tensor."""
+    a = np.asarray(a, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return 0.0
+    a = a.reshape(ref.shape[0], -1)
+    ref = ref.reshape(ref.shape[0], -1)
+    num = np.max(np.abs(a - ref), axis=1)
+    den = np.max(np.abs(ref), axis=1)
+    return float(np.max(np.where(den > 0, num / np.where(den > 0, den, 1.0), num)))
+
+
 def inf_norm_rel(a, ref) -> float:
     """max |a - ref| / max |ref| over the whole tensor (the comparison metric for float outputs)."""
     a = np.asarray(a, np.float64)

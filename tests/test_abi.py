@@ -63,6 +63,11 @@ def _status(mel, prob):
     (dict(T=64, H=128, F=256, E=4, k=2, dtype=1, head_m_size=512), 0),
     (dict(T=64, H=128, F=256, E=4, k=2, dtype=0, flags=1), 0),      # MOE_FLAG_SEPARATE_PERMUTE
     (dict(T=64, H=128, F=256, E=4, k=2, dtype=0, flags=2), 1),      # unknown flag bit
+    # H and F at most 2^22: the GEMMs' 32-bit offsets from a row tile's first row
+    (dict(T=64, H=1 << 22, F=256, E=4, k=2, dtype=1), 0),
+    (dict(T=64, H=(1 << 22) + 128, F=256, E=4, k=2, dtype=1), 2),
+    (dict(T=64, H=128, F=(1 << 22) + 64, E=4, k=2, dtype=1), 2),
+    (dict(T=64, H=(1 << 22) + 128, F=256, E=4, k=2, dtype=2), 2),
 ])
 def test_problem_validation(mel, kw, expected):
     kw = dict(kw)

@@ -161,8 +161,10 @@ def test_forward_matches_oracle(name, dtype, T, H, F, E, k, kw):
     d = dv.layer(inp)
     out = dv.host(dv.forward(mel, d))
     err = oracle.inf_norm_rel(out, ref)
-    print(f"{name}: inf-norm rel err {err:.3e}")
+    row_err = oracle.row_inf_norm_rel(out, ref)
+    print(f"{name}: inf-norm rel err {err:.3e}, worst token {row_err:.3e}")
     assert err <= TOL[dtype]
+    assert row_err <= TOL[dtype]       # per token, against that token's own largest output
     # determinism: a second call gives the same bits
     out2 = dv.host(dv.forward(mel, d))
     assert np.array_equal(out, out2)
@@ -304,6 +306,7 @@ def test_grouped_ffn_matches_oracle():
     y = mel.grouped_ffn(dv.tensor(g.rows), dv.tensor(g.group_offsets), dv.tensor(g.group_expert),
                         dv.tensor(g.w_gate), dv.tensor(g.w_up), dv.tensor(g.w_down))
     assert oracle.inf_norm_rel(dv.host(y), ref) <= TOL["bf16"]
+    assert oracle.row_inf_norm_rel(dv.host(y), ref) <= TOL["bf16"]
     y2 = mel.grouped_ffn(dv.tensor(g.rows), dv.tensor(g.group_offsets), dv.tensor(g.group_expert),
                          dv.tensor(g.w_gate), dv.tensor(g.w_up), dv.tensor(g.w_down),
                          head_m_size=256)
@@ -355,6 +358,44 @@ def test_mx_quantize_bit_exact():
     assert np.array_equal(dv.host(codes), q)
 
 
+def _encoder_cases(rows, cols, seed):
+    """float32 values that exercise the OCP-MX encoder: magnitudes spread over 60 binades per row,
+    an all-zero row, subnormal blocks, E4M3 rounding midpoints (ties to even) with a 448 anchor per
+    block, values just past the saturation point, negative zeros and a negative block."""
+    rng = np.random.default_rng(seed)
+    v = (rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-30, 30, (rows, 1)))).astype(np.float32)
+    v[0] = 0.0
+    v[1, :32] = 1e-41
+    vals = np.array([oracle.e4m3_value(c) for c in range(127)])
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)
+    n_mid = -(-mids.size // cols)                       # rows holding the 126 midpoints
+    flat = v[2:2 + n_mid].reshape(-1)
+    flat[:mids.size] = mids
+    flat[::32] = 448.0                                  # the anchor that fixes each block's scale
+    r = 2 + n_mid
+    v[r, :4] = [460.0, 464.0, 465.0, -0.0]
+    v[r, 4] = 448.0
+    v[r + 1] = -np.abs(v[r + 1])
+    v[r + 2, :32] = -0.0
+    return v
+
+
+@pytest.mark.parametrize("large,rows,cols", [(True, 300, 384), (True, 256, 128), (True, 37, 256),
+                                             (False, 300, 192), (False, 128, 64), (False, 37, 128)],
+                         ids=["large_ragged", "large_one_tile", "large_short", "small_ragged",
+                              "small_one_tile", "small_short"])
+def test_mx_fc1_epilogue_encoder_bit_exact(large, rows, cols):
+    """fc1's MX epilogue (the GEMM kernels' own device code: accumulator registers -> LDS staging ->
+    block maximum across lanes -> integer encoder -> stores) fed float32 values the host knows
+    exactly, in place of the SwiGLU output: every code and every block scale equals the oracle's
+    encoding of the same values, including ragged row tiles."""
+    v = _encoder_cases(rows, cols, seed=rows + cols)
+    codes, scales = mel.mx_fc1_epilogue_encode(dv.tensor(v), large_tiles=large)
+    q, sc = oracle.mx_quantize(v.astype(np.float64))
+    assert np.array_equal(dv.host(scales), sc)
+    assert np.array_equal(dv.host(codes), q)
+
+
 # ------------------------------------------------------------------------------------------ MX-FP8
 
 def _dec_mx(codes, scales, axis):
@@ -379,18 +420,32 @@ def test_mx_forward_matches_oracle(T, H, F, E, k):
     d = dv.layer(inp)
     out = dv.host(dv.forward(mel, d))
     err = oracle.inf_norm_rel(out, ref)
-    print(f"mx T={T} H={H} F={F}: inf-norm rel err {err:.3e}")
+    row_err = oracle.row_inf_norm_rel(out, ref)
+    print(f"mx T={T} H={H} F={F}: inf-norm rel err {err:.3e}, worst token {row_err:.3e}")
     assert err <= TOL["mxfp8"]
+    assert row_err <= TOL["mxfp8"]
     assert np.array_equal(out, dv.host(dv.forward(mel, d)))
+
+
+def _e4m3_codes(v):
+    """E4M3 codes of float64 values already divided by their block scale (round to nearest even,
+    saturated to +-448), through torch's float8_e4m3fn conversion; used only to classify which
+    codes the GPU's accumulation error can move, never as the expected codes themselves."""
+    t = torch.from_numpy(np.clip(v, -448.0, 448.0).astype(np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
 @pytest.mark.parametrize("T,H,F,E,k", [(200, 256, 384, 4, 2), (300, 1024, 1024, 3, 2)],
                          ids=["small_tiles", "large_tiles"])
 def test_mx_h_encoding_agrees_with_oracle(T, H, F, E, k):
     """fc1's MX-encoded SwiGLU output, read back from the workspace, against the oracle's encoding
-    of the exact h.  The scaled fp8 MFMA accumulates with less precision than fp32 (measured: up to
-    1.5e-5 of the sum of |terms|), so a few codes may land one step away; every other code and
-    nearly every block scale must match."""
+    of the exact h.  The GPU's g and u carry the scaled fp8 MFMA's accumulation error (measured: at
+    most 1.5e-5 of the sum of |terms|; 6e-5 is assumed here) and the SwiGLU its hardware exp2 and
+    reciprocal (2e-6 relative assumed), which bounds how far the GPU's h can sit from the exact one.
+    Every block whose scale no h within that bound can change must carry the oracle's scale, and in
+    such blocks every code that no h within the bound can change must be the oracle's code; the
+    codes and scales left undecided must stay a small fraction (the encoder itself is checked
+    bit-exactly on exact inputs by test_mx_fc1_epilogue_encoder_bit_exact)."""
     inp = synth.make_layer(T=T, H=H, F=F, E=E, k=k, dtype="mxfp8", seed=11)
     counts, offs, perm, _ = oracle.route(inp.expert_ids, E)
     xp, xps = oracle.permute(inp.x, perm, k), oracle.permute(inp.x_scale, perm, k)
@@ -406,21 +461,46 @@ def test_mx_h_encoding_agrees_with_oracle(T, H, F, E, k):
     Wg, Wu, _ = _mx_weights64(inp)
     row_e = np.repeat(np.arange(E), counts)
     h64 = np.empty((M, F))
+    bound = np.empty((M, F))
     for e in range(E):
         rows = row_e == e
         g, u = X[rows] @ Wg[e], X[rows] @ Wu[e]
-        h64[rows] = g / (1 + np.exp(-g)) * u
+        sg, su = np.abs(X[rows]) @ np.abs(Wg[e]), np.abs(X[rows]) @ np.abs(Wu[e])
+        sig = 1.0 / (1.0 + np.exp(-g))
+        h64[rows] = g * sig * u
+        dh_dg = np.abs(sig * (1.0 + g * (1.0 - sig)) * u)
+        dh_du = np.abs(g * sig)
+        bound[rows] = 6e-5 * (dh_dg * sg + dh_du * su) + 2e-6 * np.abs(h64[rows])
     q64, s64 = oracle.mx_quantize(h64)
-    assert (hs == s64).mean() > 0.995
-    same_scale = np.repeat(hs == s64, 32, axis=1)
-    assert (hq == q64).mean() > 0.99
+
+    blocks = lambda a: a.reshape(M, F // 32, 32)
+    lo = np.maximum(np.abs(h64) - bound, 0.0)
+    hi = np.abs(h64) + bound
+    # the scale exponent floor(log2 amax) - 8 of any h within the bound lies between these two
+    e_lo = np.floor(np.log2(np.maximum(blocks(lo).max(axis=2), 1e-300)))
+    e_hi = np.floor(np.log2(np.maximum(blocks(hi).max(axis=2), 1e-300)))
+    nz = blocks(lo).max(axis=2) > 0
+    scale_decided = (e_lo == e_hi) & nz & (e_hi - 8 >= -127) & (e_hi - 8 <= 127)
+    assert np.array_equal(hs[scale_decided], s64[scale_decided])
+    # codes in blocks with a decided scale: decided when both ends of the bound encode alike
+    sc = np.repeat(np.exp2(s64.astype(np.float64) - 127), 32, axis=1)
+    c_lo, c_hi = _e4m3_codes((h64 - bound) / sc), _e4m3_codes((h64 + bound) / sc)
+    code_decided = np.repeat(scale_decided, 32, axis=1) & (c_lo == c_hi) & (c_lo == q64)
+    assert np.array_equal(hq[code_decided], q64[code_decided])
+    und_s = 1.0 - scale_decided[nz].mean()
+    und_c = 1.0 - code_decided.mean()
+    mis_s, mis_c = (hs != s64).mean(), (hq != q64).mean()
+    print(f"h encoding: undecided scales {und_s:.2e}, undecided codes {und_c:.2e}; mismatches: "
+          f"scales {mis_s:.2e}, codes {mis_c:.2e}")
+    # the bound leaves 0.2-0.6% of the scales and 12-20% of the codes undecided at these shapes
+    # (computed from the oracle's h alone); more would make the exact comparison above vacuous
+    assert und_s < 1e-2 and und_c < 0.3
+    assert mis_s < 5e-3 and mis_c < 1e-2
     # value check: each decoded element is within the worst-case E4M3 rounding of its block (half a
     # top-binade step is 1/16 of amax, saturation at 448 loses up to 1/8) of the exact h
     amax = np.repeat(np.abs(h64).reshape(M, F // 32, 32).max(axis=2), 32, axis=1)
     err = np.abs(_dec_mx(hq, hs, 1) - h64) / np.maximum(amax, 1e-30)
-    own = np.abs(_dec_mx(q64, s64, 1) - h64) / np.maximum(amax, 1e-30)
     assert err.max() <= 0.125 + 1e-6
-    assert err.mean() <= 1.05 * own.mean()       # as good as encoding the exact h, on average
 
 
 @pytest.mark.parametrize("T,H,F", [(600, 256, 256), (1100, 1024, 1024)], ids=["small_tiles", "large_tiles"])
@@ -441,3 +521,4 @@ def test_mx_grouped_ffn_matches_oracle(H, F):
                            dv.tensor(g.w_up), dv.tensor(g.wu_scale), dv.tensor(g.w_down),
                            dv.tensor(g.wd_scale))
     assert oracle.inf_norm_rel(dv.host(y), ref) <= TOL["mxfp8"]
+    assert oracle.row_inf_norm_rel(dv.host(y), ref) <= TOL["mxfp8"]

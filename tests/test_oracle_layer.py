@@ -188,3 +188,14 @@ def test_grouped_rows_source_major():
     assert oracle.inf_norm_rel(y, ref) < RTOL
     sub = np.array([299, 0, 150])
     assert np.array_equal(oracle.grouped_ffn(g, sub), y[sub])
+
+
+def test_row_inf_norm_rel_is_taken_per_row():
+    """The per-token metric: each row's error against that row's own largest reference value (a
+    zero row counts its absolute error), so a small row's 10% error is not hidden by a large row."""
+    ref = np.array([[10.0, -1.0], [0.1, 0.05], [0.0, 0.0]])
+    a = ref + np.array([[0.1, 0.0], [0.0, -0.01], [0.0, 0.002]])
+    assert oracle.row_inf_norm_rel(a, ref) == pytest.approx(0.1)
+    assert oracle.inf_norm_rel(a, ref) == pytest.approx(0.01)
+    assert oracle.row_inf_norm_rel(ref, ref) == 0.0
+    assert oracle.row_inf_norm_rel(np.zeros((0, 4)), np.zeros((0, 4))) == 0.0
