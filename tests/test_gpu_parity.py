@@ -495,7 +495,8 @@ def test_mx_h_encoding_agrees_with_oracle(T, H, F, E, k):
     # the bound leaves 0.2-0.6% of the scales and 12-20% of the codes undecided at these shapes
     # (computed from the oracle's h alone); more would make the exact comparison above vacuous
     assert und_s < 1e-2 and und_c < 0.3
-    assert mis_s < 5e-3 and mis_c < 1e-2
+    # measured: no scale and 0.17% of the codes differ (all of them undecided ones)
+    assert mis_s < 1e-3 and mis_c < 5e-3
     # value check: each decoded element is within the worst-case E4M3 rounding of its block (half a
     # top-binade step is 1/16 of amax, saturation at 448 loses up to 1/8) of the exact h
     amax = np.repeat(np.abs(h64).reshape(M, F // 32, 32).max(axis=2), 32, axis=1)
