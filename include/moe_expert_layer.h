@@ -186,6 +186,22 @@ moe_status moe_route(const int32_t* expert_ids, int64_t T, int64_t k, int64_t E,
                      int32_t* offsets, int32_t* perm, int32_t* pos, void* workspace,
                      size_t workspace_bytes, hipStream_t stream);
 
+/* moe_route for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the same kernels and results, with the
+ * routing scratch (a status word and per-block expert histograms) in a static device array of
+ * 256 B + 4 MiB that the library holds on each GPU it runs on until the process ends.  Nothing is
+ * allocated and no workspace is passed; inputs and outputs are as for moe_route.
+ * Limit: ceil(T*k / 2048) * (E + 1) <= 2^20 (e.g. any T*k < 2^31 for E = 8, T*k <= 2M slots for
+ * E = 1023); larger problems return MOE_ERR_UNSUPPORTED with nothing enqueued.
+ * Every call on one GPU uses that GPU's single scratch array: calls that overlap in time on one GPU
+ * (on different streams or host threads) race and must be serialised by the caller.  The kernels
+ * write every scratch word they read within the same call, so nothing needs clearing between calls.
+ * Out-of-range ids are dropped as in moe_route; with no workspace status word, offsets[E] < T*k is
+ * the sign that some were. */
+moe_status moe_route_noalloc(const int32_t* expert_ids, int64_t T, int64_t k, int64_t E,
+                             int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos,
+                             hipStream_t stream);
+
 /* Permute ("NPU Training Operators - MC2", 执行路径 step 6): x_perm[pos[s]] = x[s / k] for every
  * slot with pos[s] >= 0.  Rows of p->H elements of p->dtype; for MOE_MXFP8_E4M3 the H/32 scale bytes
  * of each row move with it (x_scale -> x_perm_scale; both NULL otherwise).  x_perm has T*k rows.

@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "MoeError", "library", "lib_path", "F32", "BF16", "MXFP8",
     "workspace_size", "expert_forward", "expert_forward_mx", "expert_forward_train",
-    "backward_workspace_size", "expert_backward", "route", "permute", "unpermute",
+    "backward_workspace_size", "expert_backward", "route", "route_noalloc", "permute", "unpermute",
     "grouped_ffn_workspace_size", "grouped_ffn", "grouped_ffn_mx", "mx_quantize",
     "mx_fc1_epilogue_encode", "device_status", "chunk_counters",
     "intermediate_h",
@@ -57,6 +57,7 @@ _SIGS = {
     "moe_expert_forward_train": [ctypes.POINTER(MoeProblem)] + [_P] * 9 + [ctypes.c_size_t, _P],
     "moe_route_workspace_size": [_I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
     "moe_route": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "moe_route_noalloc": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P],
     "moe_permute": [ctypes.POINTER(MoeProblem), _P, _P, _P, _P, _P, _P],
     "moe_unpermute": [ctypes.POINTER(MoeProblem), _P, _P, _P, _P, _P],
     "moe_grouped_ffn_workspace_size": [ctypes.POINTER(MoeProblem), _I64, _I64,
@@ -304,6 +305,24 @@ def route(expert_ids, E: int, workspace=None):
     _check(library().moe_route(_ptr(expert_ids), T, k, E, _ptr(counts), _ptr(offsets), _ptr(perm),
                                _ptr(pos), _ptr(ws), ws.numel(), _stream(expert_ids)))
     return counts, offsets, perm, pos, ws
+
+
+def route_noalloc(expert_ids, E: int, out=None):
+    """moe_route without a workspace (the library's static per-GPU scratch): (counts[E],
+    offsets[E+1], perm[M], pos[M]).  `out` may hold those four int32 tensors to write into."""
+    _need(expert_ids, "expert_ids", torch.int32)
+    T, k = expert_ids.shape
+    dev = expert_ids.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    if out is None:
+        out = (torch.empty(E, **i32), torch.empty(E + 1, **i32), torch.empty(T * k, **i32),
+               torch.empty(T * k, **i32))
+    for t, n, name in zip(out, (E, E + 1, T * k, T * k), ("counts", "offsets", "perm", "pos")):
+        _need(t, name, torch.int32, (n,), dev)
+    counts, offsets, perm, pos = out
+    _check(library().moe_route_noalloc(_ptr(expert_ids), T, k, E, _ptr(counts), _ptr(offsets),
+                                       _ptr(perm), _ptr(pos), _stream(expert_ids)))
+    return counts, offsets, perm, pos
 
 
 def permute(x, pos, k: int, E: int | None = None, x_scale=None, F: int = 128, x_perm=None,

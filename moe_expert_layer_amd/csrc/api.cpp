@@ -4,6 +4,7 @@
 // synchronous status / timing queries).
 #include "moe_expert_layer.h"
 
+#include <hip/hip_runtime.h>     // __device__ data: the allocation-free route's scratch
 #include <hip/hip_runtime_api.h>
 
 #include <cstdarg>
@@ -987,3 +988,69 @@ MOE_API moe_status moe_timing_reset(void)
     return MOE_OK;
 }
 
+// ------------------------------------------------------------------- allocation-free routing
+
+namespace moe {
+namespace {
+
+// The route's scratch (status word, then per-block expert histograms) for callers that cannot
+// allocate: a file-scope device array, one copy per GPU, kept until the process ends.
+constexpr size_t kNoAllocScratchBytes = kAlign + (size_t{4} << 20);
+
+}  // namespace
+}  // namespace moe
+
+static __device__ __align__(256) unsigned char scratch[moe::kNoAllocScratchBytes];
+
+namespace moe {
+namespace {
+
+// Device address of this GPU's copy of `scratch`.  In host code the array's name is a host-side
+// stand-in, not a device address, so the address is looked up once per device (with that device
+// current) and only the looked-up pointer is ever handed to kernels.
+moe_status noalloc_scratch(void** out)
+{
+    static std::mutex mu;
+    static std::map<int, void*> ptrs;
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> g(mu);
+    auto it = ptrs.find(dev);
+    if (it == ptrs.end()) {
+        void* p = nullptr;
+        if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess)
+            return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        it = ptrs.emplace(dev, p).first;
+    }
+    *out = it->second;
+    return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+MOE_API moe_status moe_route_noalloc(const int32_t* expert_ids, int64_t T, int64_t k, int64_t E,
+                                     int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos,
+                                     hipStream_t stream)
+{
+    size_t need = 0;
+    if (moe_status st = moe_route_workspace_size(T, k, E, &need); st != MOE_OK)
+        return st;
+    if (T * k > INT32_MAX)
+        return fail(MOE_ERR_UNSUPPORTED, "T * k exceeds int32 indexing");
+    if (need > kNoAllocScratchBytes)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "ceil(T*k / %d) * (E + 1) block counts need %zu bytes; the static scratch holds %zu",
+                    kRouteSlotsPerBlock, need, kNoAllocScratchBytes);
+    if (counts == nullptr || offsets == nullptr ||
+        (T > 0 && (expert_ids == nullptr || perm == nullptr || pos == nullptr)))
+        return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+    void* ws = nullptr;
+    if (moe_status st = noalloc_scratch(&ws); st != MOE_OK)
+        return st;
+    // every scratch byte the kernels read is written earlier in the same call (route_count fills
+    // each block's histogram row, route_scan the status word): nothing needs clearing
+    return run_route(expert_ids, T, k, E, counts, offsets, perm, pos, ws, route_layout(T, k, E, 0),
+                     stream);
+}

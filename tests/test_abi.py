@@ -160,3 +160,14 @@ def test_backward_rejects_before_enqueue(mel):
     f32 = mel.problem(64, 128, 256, 4, 2, mel.F32)
     st = lib.moe_expert_forward_train(ctypes.byref(f32), *([None] * 9), 0, None)
     assert st == 2
+
+
+def test_route_noalloc_rejects_before_touching_the_gpu(mel):
+    """The allocation-free route checks sizes against its static scratch (4 MiB of block counts)
+    and its arguments on the host, before any HIP call."""
+    lib = mel.library()
+    # 1026 routing blocks x 1024 counts: beyond the scratch
+    assert lib.moe_route_noalloc(None, 2048 * 1025 + 1, 1, 1023, None, None, None, None, None) == 2
+    assert b"scratch" in lib.moe_last_error()
+    assert lib.moe_route_noalloc(None, 16, 3, 2, None, None, None, None, None) == 1     # k > E
+    assert lib.moe_route_noalloc(None, 16, 2, 8, None, None, None, None, None) == 1     # null outputs
