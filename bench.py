@@ -16,7 +16,11 @@ those caches full of dirty lines, whose write-back then lands on whichever kerne
 
 Beside the step, and outside its figures: the router in front of the layer and, for the bfloat16
 workloads, the layer's backward (gradients of x, the three weight stacks and probs, with g and u
-recomputed), each timed on its own with the same flush.
+recomputed), each timed on its own with the same flush; the permute and unpermute kernels on their
+own, launched back to back from a captured HIP graph over rotating copies of their operands that
+together outgrow the Infinity Cache (so neither the host's launch gap nor a warm cache enters their
+rates); and, when the headline is the Mixtral layer, compact runs of the other three workloads (one
+EP rank's grouped FFN, the fine-grained layer, the MX-FP8 layer) under the key "workloads".
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -152,10 +156,86 @@ def cpu_baseline_grouped(g, budget_s: float):
                       f"{dt:.1f} s, fp64"}
 
 
-def bench_grouped(args, torch, mel, synth, dv, dev):
+def graph_rate(torch, launches, sets, flush, repeats=3):
+    """Mean duration of one launch when `launches` (callables, one per buffer set) run back to back
+    from a captured HIP graph, several rounds over the sets: no host launch gap between kernels, and
+    since the sets together outgrow the 256 MiB Infinity Cache, no launch finds its operands cached.
+    The cache flush runs before each replay, outside the events."""
+    for fn in launches:
+        fn()
+    torch.cuda.synchronize()
+    rounds = max(2, -(-16 // len(launches)))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        for _ in range(rounds):
+            for fn in launches:
+                fn()
+    torch.cuda.synchronize()
+    n = rounds * len(launches)
+    times = []
+    for _ in range(repeats):
+        flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) / n)
+    del g
+    return float(np.median(times)), n, sets
+
+
+def movement_rates(torch, mel, inp, d, dev, flush, bytes_):
+    """permute (the standalone kernel; the forward folds it into fc1 where it can) and unpermute on
+    their own, timed by graph_rate over rotating copies of their operands."""
+    T, H, k, E = inp.T, inp.H, inp.k, inp.E
+    M = T * k
+    _, _, _, pos, _ = mel.route(d.expert_ids, E)
+    mx = inp.dtype == "mxfp8"
+    ydt = torch.float32 if inp.dtype == "f32" else torch.bfloat16
+    out = {}
+    # permute: x (and scales) in, x_perm (and scales) out
+    set_bytes = bytes_["permute"] + bytes_.get("permute_scale", 0)
+    S = max(2, -(-(768 << 20) // set_bytes))
+    xs = [d.x.clone() for _ in range(S)]
+    xss = [d.x_scale.clone() for _ in range(S)] if mx else [None] * S
+    xp = [torch.empty((M, H), dtype=d.x.dtype, device=dev) for _ in range(S)]
+    xps = [torch.empty((M, H // 32), dtype=torch.uint8, device=dev) for _ in range(S)] if mx else [None] * S
+    launches = [lambda i=i: mel.permute(xs[i], pos, k, E=E, x_scale=xss[i], x_perm=xp[i],
+                                        x_perm_scale=xps[i]) for i in range(S)]
+    ms, n, _ = graph_rate(torch, launches, S, flush)
+    ref = mel.permute(xs[0], pos, k, E=E, x_scale=xss[0])
+    ok = torch.equal(ref[0] if mx else ref, xp[0])
+    out["permute"] = {"us": ms * 1e3, "bytes": set_bytes, "GB/s": set_bytes / (ms * 1e-3) / 1e9,
+                      "frac": set_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "launches": n,
+                      "buffer_sets": S, "graph_equals_eager": bool(ok)}
+    del xs, xss, xp, xps
+    # unpermute: y_perm in, out out
+    ub = bytes_["unpermute"]
+    S = max(2, -(-(768 << 20) // ub))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    ys = [torch.randn((M, H), generator=gen, device=dev).to(ydt) for _ in range(S)]
+    os_ = [torch.empty((T, H), dtype=ydt, device=dev) for _ in range(S)]
+    launches = [lambda i=i: mel.unpermute(ys[i], pos, d.probs, E=E, out=os_[i]) for i in range(S)]
+    ms, n, _ = graph_rate(torch, launches, S, flush)
+    ok = torch.equal(mel.unpermute(ys[0], pos, d.probs, E=E), os_[0])
+    out["unpermute"] = {"us": ms * 1e3, "bytes": ub, "GB/s": ub / (ms * 1e-3) / 1e9,
+                        "frac": ub / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "launches": n,
+                        "buffer_sets": S, "graph_equals_eager": bool(ok)}
+    del ys, os_
+    torch.cuda.synchronize()
+    log("standalone: " + ", ".join(f"{k_} {v['us']:.1f} us {v['GB/s']:.0f} GB/s ({100 * v['frac']:.0f}%)"
+                                   for k_, v in out.items()))
+    return out
+
+
+def bench_grouped(args, torch, mel, synth, dv, dev, name=None, compact=False):
     """One EP rank's share: the grouped FFN over rows as the dispatch All-to-All delivers them
-    (source-major groups of 2 local experts); a step is one moe_grouped_ffn call, the metric rows/s."""
-    g = synth.make_workload(args.workload)
+    (source-major groups of 2 local experts); a step is one moe_grouped_ffn call, the metric rows/s.
+    Returns the result dict (compact: no oracle baseline)."""
+    name = name or args.workload
+    g = synth.make_workload(name)
     M, H = g.rows.shape
     F, G = g.F, g.group_expert.shape[0]
     head = args.head_m_size if args.head_m_size is not None else 0
@@ -166,7 +246,7 @@ def bench_grouped(args, torch, mel, synth, dv, dev):
                          for h in (head, 512)), dtype=torch.uint8, device=dev)
     out = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
     flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev).view(torch.float32)
-    if args.copy_calibration_mib:
+    if args.copy_calibration_mib and not compact:
         src = torch.ones(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
         torch.empty_like(src).copy_(src)
         torch.cuda.synchronize()
@@ -209,7 +289,7 @@ def bench_grouped(args, torch, mel, synth, dv, dev):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "rows": M, "H": H, "F": F, "local_experts": g.E_local,
+        "config": {"workload": name, "rows": M, "H": H, "F": F, "local_experts": g.E_local,
                    "sources": g.sources, "groups": G, "head_m_size": head,
                    "flush": "none" if args.no_flush else "read"},
         "gemm": {"tflops": (fl["fc1"] + fl["fc2"]) / ((fc1_ms + fc2_ms) * 1e-3) / 1e12,
@@ -218,9 +298,9 @@ def bench_grouped(args, torch, mel, synth, dv, dev):
         "kernels_ms": kavg,
         "roofline": {"kernel": "fc1_bf16", "bound": "mfma", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": measured_traffic(args.workload, "fc1_bf16"),
+                     "traffic": measured_traffic(name, "fc1_bf16"),
                      "per_launch": f"{fl['fc1']:.4g} FLOP = 4*M*H*F, M={M} received rows",
-                     **measured_clock(args.workload, "fc1_bf16", achieved, peak)},
+                     **measured_clock(name, "fc1_bf16", achieved, peak)},
         "timing": {"median_ms": float(np.median(ms)), "p10_ms": float(np.percentile(ms, 10)),
                    "p90_ms": float(np.percentile(ms, 90))},
     }
@@ -240,10 +320,107 @@ def bench_grouped(args, torch, mel, synth, dv, dev):
         result["chunked"] = {"head_m_size": 512, "ms_per_step": cms, "rows_per_s": M / (cms * 1e-3),
                              "overhead_vs_unchunked": cms / ms_per_step - 1.0}
         log(f"chunked(512) ms/step {cms:.3f}")
-    if not args.skip_cpu_baseline:
+    if not args.skip_cpu_baseline and not compact:
         log(f"cpu baseline (~{args.cpu_seconds:.0f} s of oracle work)")
         result["cpu_baseline"] = cpu_baseline_grouped(g, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+    del rows, offs, gexp, wg, wu, wd, ws, out, flush
+    torch.cuda.empty_cache()
+    return result
+
+
+def expert_roofline_ms(inp, counts, peak_tflops):
+    """Attainable GEMM time by a per-expert roofline: each expert is bound by its FLOPs at the MFMA
+    peak or by its bytes (its three weight matrices once, its rows into and out of both
+    projections) at the HBM peak, whichever is larger; summed over the experts."""
+    H, F = inp.H, inp.F
+    eb = 1 if inp.dtype == "mxfp8" else 2
+    t = 0.0
+    for m in counts:
+        m = float(m)
+        if m == 0:
+            continue
+        flops = 6.0 * m * H * F
+        byts = 3.0 * H * F * eb + m * (H * eb + 2 * F * eb + H * 2)
+        t += max(flops / (peak_tflops * 1e12), byts / (HBM_PEAK_GBS * 1e9))
+    return t * 1e3
+
+
+def compact_layer(args, torch, mel, synth, dv, dev, name, flush):
+    """A layer workload beside the headline: mean step time unchunked and chunked by 512 rows, the
+    GEMMs' rate from per-kernel events, and the standalone permute / unpermute rates."""
+    log(f"[{name}] generating inputs")
+    inp = synth.make_workload(name)
+    d = dv.layer(inp)
+    T, H, F, E, k = inp.T, inp.H, inp.F, inp.E, inp.k
+    M = T * k
+    code = {"f32": mel.F32, "bf16": mel.BF16, "mxfp8": mel.MXFP8}[inp.dtype]
+    ws = torch.empty(max(mel.workspace_size(mel.problem(T, H, F, E, k, code, h)) for h in (0, 512)),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    def step(h):
+        if inp.dtype == "mxfp8":
+            mel.expert_forward_mx(d.x, d.x_scale, d.w_gate, d.wg_scale, d.w_up, d.wu_scale,
+                                  d.w_down, d.wd_scale, d.expert_ids, d.probs, head_m_size=h,
+                                  out=out, workspace=ws)
+        else:
+            mel.expert_forward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs,
+                               head_m_size=h, out=out, workspace=ws)
+
+    steps = min(args.steps, 10)
+    for _ in range(3):
+        step(0)
+    modes = {}
+    for h in (0, 512):
+        step(h)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            flush()
+            a.record()
+            step(h)
+            b.record()
+        torch.cuda.synchronize()
+        modes[h] = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    mel.timing_reset()
+    mel.timing_enable(True)
+    for _ in range(steps):
+        flush()
+        step(0)
+    kern = mel.timing_collect()
+    mel.timing_enable(False)
+    kavg = {n: tot / cnt for n, (tot, cnt) in kern.items()}
+    suffix = {"bf16": "bf16", "mxfp8": "mx"}[inp.dtype]
+    fl = gemm_flops(M, H, F)
+    fc1_ms, fc2_ms = kavg[f"fc1_{suffix}"], kavg[f"fc2_{suffix}"]
+    peak = PEAK[inp.dtype]
+    tflops = (fl["fc1"] + fl["fc2"]) / ((fc1_ms + fc2_ms) * 1e-3) / 1e12
+    counts = np.bincount(inp.expert_ids.ravel(), minlength=E)
+    bound_ms = expert_roofline_ms(inp, counts, peak)
+    bytes_ = byte_model(inp, M)
+    res = {
+        "config": {"T": T, "H": H, "F": F, "E": E, "k": k, "dtype": inp.dtype, "routed_rows": M},
+        "ms_per_step": modes[0], "tokens_per_s": T / (modes[0] * 1e-3),
+        "chunked_512": {"ms_per_step": modes[512], "tokens_per_s": T / (modes[512] * 1e-3)},
+        "gemm": {"tflops": tflops, "frac_of_peak": tflops / peak, "peak_tflops": peak,
+                 "fc1_ms": fc1_ms, "fc2_ms": fc2_ms,
+                 "expert_roofline_ms": bound_ms,
+                 "frac_of_expert_roofline": bound_ms / (fc1_ms + fc2_ms)},
+        "kernels_ms": kavg,
+        "hbm_in_step": {n: {"GB/s": bytes_[n] / (kavg[n] * 1e-3) / 1e9,
+                            "frac": bytes_[n] / (kavg[n] * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                        for n in bytes_ if n in kavg},
+        "hbm_standalone": movement_rates(torch, mel, inp, d, dev, flush, bytes_),
+    }
+    log(f"[{name}] ms/step {modes[0]:.3f} (chunked {modes[512]:.3f}); GEMMs {tflops:.0f} TFLOP/s "
+        f"({100 * tflops / peak:.1f}% of peak, {100 * bound_ms / (fc1_ms + fc2_ms):.0f}% of the per-expert roofline)")
+    del d, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
+EXTRA_WORKLOADS = ("ep_rank_bf16", "finegrained_bf16", "mxfp8")
 
 
 def main():
@@ -266,6 +443,10 @@ def main():
                     help="run the permute step as its own kernel instead of inside fc1's row loads")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (reference for HBM counters)")
+    ap.add_argument("--skip-workloads", action="store_true",
+                    help="leave out the compact runs of the other workloads beside the Mixtral headline")
+    ap.add_argument("--skip-standalone", action="store_true",
+                    help="leave out the standalone permute / unpermute rates")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -286,7 +467,7 @@ def main():
 
     cfg = synth.WORKLOADS[args.workload]
     if cfg["kind"] == "grouped":
-        bench_grouped(args, torch, mel, synth, dv, dev)
+        print(json.dumps(bench_grouped(args, torch, mel, synth, dv, dev)), flush=True)
         return
     log(f"generating {args.workload} inputs")
     t0 = time.perf_counter()
@@ -517,11 +698,30 @@ def main():
                              "overhead_vs_unchunked": float(cms.mean()) / ms_per_step - 1.0}
         log(f"chunked(512) ms/step {cms.mean():.3f}")
 
+    if not args.skip_standalone and inp.dtype != "f32":
+        result["hbm_standalone"] = movement_rates(torch, mel, inp, d, dev, do_flush, bytes_)
+
     if not args.skip_cpu_baseline:
         log(f"cpu baseline (~{args.cpu_seconds:.0f} s of oracle work)")
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
         log(f"cpu baseline {result['cpu_baseline']['value']:.2f} tokens/s on "
             f"{result['cpu_baseline']['cores']} threads")
+
+    # the other workloads, compactly, beside the headline (same flush, no oracle baseline)
+    if args.workload == "mixtral_bf16" and not args.skip_workloads:
+        del d, ws, out
+        torch.cuda.empty_cache()
+        result["workloads"] = {}
+        for name in EXTRA_WORKLOADS:
+            if synth.WORKLOADS[name]["kind"] == "grouped":
+                log(f"[{name}] grouped FFN")
+                r = bench_grouped(args, torch, mel, synth, dv, dev, name=name, compact=True)
+                result["workloads"][name] = {k_: r[k_] for k_ in ("value", "unit", "ms_per_step",
+                                                                  "config", "gemm", "chunked",
+                                                                  "kernels_ms") if k_ in r}
+            else:
+                result["workloads"][name] = compact_layer(args, torch, mel, synth, dv, dev, name,
+                                                          do_flush)
     print(json.dumps(result), flush=True)
 
 
