@@ -399,6 +399,42 @@ def compact_layer(args, torch, mel, synth, dv, dev, name, flush):
     counts = np.bincount(inp.expert_ids.ravel(), minlength=E)
     bound_ms = expert_roofline_ms(inp, counts, peak)
     bytes_ = byte_model(inp, M)
+    from_bf16 = None
+    if inp.dtype == "mxfp8":
+        # the same layer fed the bfloat16 x, encoded by the library on its way into the gather
+        xb = dv.tensor(inp.x_bf16, dev)
+        wsq = torch.empty(mel.workspace_size(mel.problem(T, H, F, E, k, code, 0, mel.FLAG_QUANTIZE_X)),
+                          dtype=torch.uint8, device=dev)
+
+        def qstep():
+            mel.expert_forward_mx(xb, None, d.w_gate, d.wg_scale, d.w_up, d.wu_scale, d.w_down,
+                                  d.wd_scale, d.expert_ids, d.probs, out=out, workspace=wsq)
+
+        qstep()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            flush()
+            a.record()
+            qstep()
+            b.record()
+        torch.cuda.synchronize()
+        qms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        mel.timing_reset()
+        mel.timing_enable(True)
+        for _ in range(steps):
+            flush()
+            qstep()
+        qk = mel.timing_collect()
+        mel.timing_enable(False)
+        enc_ms = qk["mx_encode_x"][0] / qk["mx_encode_x"][1]
+        enc_bytes = T * H * 2 + T * H + T * (H // 32)
+        from_bf16 = {"ms_per_step": qms, "tokens_per_s": T / (qms * 1e-3),
+                     "mx_encode_x_us": enc_ms * 1e3,
+                     "mx_encode_x_GB/s": enc_bytes / (enc_ms * 1e-3) / 1e9}
+        log(f"[{name}] from bf16 x: ms/step {qms:.3f}, encode {enc_ms * 1e3:.1f} us")
+        del xb, wsq
     res = {
         "config": {"T": T, "H": H, "F": F, "E": E, "k": k, "dtype": inp.dtype, "routed_rows": M},
         "ms_per_step": modes[0], "tokens_per_s": T / (modes[0] * 1e-3),
@@ -413,6 +449,8 @@ def compact_layer(args, torch, mel, synth, dv, dev, name, flush):
                         for n in bytes_ if n in kavg},
         "hbm_standalone": movement_rates(torch, mel, inp, d, dev, flush, bytes_),
     }
+    if from_bf16 is not None:
+        res["from_bf16_x"] = from_bf16
     log(f"[{name}] ms/step {modes[0]:.3f} (chunked {modes[512]:.3f}); GEMMs {tflops:.0f} TFLOP/s "
         f"({100 * tflops / peak:.1f}% of peak, {100 * bound_ms / (fc1_ms + fc2_ms):.0f}% of the per-expert roofline)")
     del d, ws, out
@@ -447,6 +485,8 @@ def main():
                     help="leave out the compact runs of the other workloads beside the Mixtral headline")
     ap.add_argument("--skip-standalone", action="store_true",
                     help="leave out the standalone permute / unpermute rates")
+    ap.add_argument("--mx-from-bf16", action="store_true",
+                    help="MX workloads: feed the bfloat16 x and let the library encode it (MOE_FLAG_QUANTIZE_X)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -478,7 +518,9 @@ def main():
     M = T * k
     head = args.head_m_size if args.head_m_size is not None else 0
     code = {"f32": mel.F32, "bf16": mel.BF16, "mxfp8": mel.MXFP8}[inp.dtype]
-    ws_bytes = max(mel.workspace_size(mel.problem(T, H, F, E, k, code, h)) for h in (head, 512))
+    qflag = mel.FLAG_QUANTIZE_X if (inp.dtype == "mxfp8" and args.mx_from_bf16) else 0
+    ws_bytes = max(mel.workspace_size(mel.problem(T, H, F, E, k, code, h, qflag)) for h in (head, 512))
+    xb16 = dv.tensor(inp.x_bf16, dev) if qflag else None
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty((T, H), dtype=torch.float32 if inp.dtype == "f32" else torch.bfloat16,
                       device=dev)
@@ -495,9 +537,10 @@ def main():
 
     def step(h):
         if inp.dtype == "mxfp8":
-            mel.expert_forward_mx(d.x, d.x_scale, d.w_gate, d.wg_scale, d.w_up, d.wu_scale,
-                                  d.w_down, d.wd_scale, d.expert_ids, d.probs, head_m_size=h,
-                                  out=out, workspace=ws, separate_permute=args.separate_permute)
+            mel.expert_forward_mx(xb16 if qflag else d.x, None if qflag else d.x_scale, d.w_gate,
+                                  d.wg_scale, d.w_up, d.wu_scale, d.w_down, d.wd_scale,
+                                  d.expert_ids, d.probs, head_m_size=h, out=out, workspace=ws,
+                                  separate_permute=args.separate_permute)
         else:
             mel.expert_forward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs,
                                head_m_size=h, out=out, workspace=ws,
@@ -579,7 +622,8 @@ def main():
         "config": {"workload": args.workload, "T": T, "H": H, "F": F, "E": E, "k": k,
                    "head_m_size": head, "routed_rows": M, "flush_bytes": 0 if args.no_flush else 1 << 30,
                    "flush": "none" if args.no_flush else args.flush,
-                   "permute": "separate kernel" if args.separate_permute else "inside fc1 where the large tiles serve"},
+                   "permute": "separate kernel" if args.separate_permute else "inside fc1 where the large tiles serve",
+                   **({"x": "bfloat16, MX-encoded by the library"} if qflag else {})},
         "gemm": {"tflops": gemm_tflops, "frac_of_peak": gemm_tflops / peak, "peak_tflops": peak,
                  "fc1_ms": fc1_ms, "fc2_ms": fc2_ms},
         "kernels_ms": kavg, "hbm": hbm, "roofline": roof,

@@ -67,6 +67,15 @@ enum moe_dtype_code { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8_E4M3 = 2 };
  * on x_perm instead; the result is bitwise the same either way. */
 #define MOE_FLAG_SEPARATE_PERMUTE 1u
 
+/* moe_problem.flags, MX problems only: x is bfloat16 [T,H] and the library encodes it to OCP-MX
+ * (E4M3 codes, one E8M0 scale per 32 elements along H, the rule of moe_mx_quantize) on its way into
+ * the gather of 执行路径 step 6 ("NPU Training Operators - MC2"; the MX matmul of
+ * "MC2 通算融合架构总览", §1): once per token into the workspace when the first grouped GEMM gathers
+ * its rows from x itself, or straight into the permuted rows when the permute runs as its own step
+ * (MOE_FLAG_SEPARATE_PERMUTE, or sizes the large tiles do not serve).  moe_workspace_size accounts
+ * for the token-order buffer; moe_quantized_x_offsets says where the codes are left. */
+#define MOE_FLAG_QUANTIZE_X 2u
+
 /* The chunk height that "MC2 通算融合架构总览", §6 (切分策略) uses for its M-axis split: the
  * recommended moe_problem.head_m_size for a chunked call (0 still means unchunked). */
 #define MOE_DEFAULT_HEAD_M_SIZE 512
@@ -88,7 +97,7 @@ typedef struct moe_problem {
                              default (MOE_DEFAULT_HEAD_M_SIZE, the value to pass for the pages' chunked
                              mode) are those of "MC2 通算融合架构总览", §6 切分策略; the result is
                              bitwise identical to the unchunked one.                              */
-    uint32_t flags;       /* 0, or MOE_FLAG_SEPARATE_PERMUTE                                     */
+    uint32_t flags;       /* 0, or MOE_FLAG_SEPARATE_PERMUTE and / or MOE_FLAG_QUANTIZE_X        */
     uint32_t reserved;    /* must be 0                                                           */
 } moe_problem;
 
@@ -124,7 +133,10 @@ moe_status moe_expert_forward_train(const moe_problem* p, const void* x, const v
                                     size_t workspace_bytes, hipStream_t stream);
 
 /* The same layer on OCP-MX E4M3 inputs (dtype must be MOE_MXFP8_E4M3; H and F multiples of 128).
- * Element bytes and scale bytes as described above; out is bfloat16 [T,H]. */
+ * Element bytes and scale bytes as described above; out is bfloat16 [T,H].
+ * With MOE_FLAG_QUANTIZE_X in p->flags, x points to bfloat16 activations [T,H] instead and x_scale
+ * must be NULL: the library encodes x itself (see the flag).  The encoding is bit-exact, so the
+ * output is bitwise that of a call on the host-encoded x. */
 moe_status moe_expert_forward_mx(const moe_problem* p, const uint8_t* x, const uint8_t* x_scale,
                                  const uint8_t* w_gate, const uint8_t* wg_scale,
                                  const uint8_t* w_up, const uint8_t* wu_scale,
@@ -290,6 +302,13 @@ moe_status moe_query_device_status(const void* workspace, hipStream_t stream,
 moe_status moe_chunk_counters(const moe_problem* p, void* workspace, size_t workspace_bytes,
                               int64_t M, const int32_t** counters, const int32_t** tiles_per_chunk,
                               int64_t* num_chunks /* host */);
+
+/* Host only.  For a forward with MOE_FLAG_QUANTIZE_X: where in the workspace the call leaves the
+ * encoded x.  *permuted = 0: token order ([T, H] codes + [T, H/32] scales), when the first grouped
+ * GEMM gathers its rows itself; *permuted = 1: the T*k permuted rows (the layout of moe_permute),
+ * when the permute runs as its own step.  Valid after the call's work ends. */
+moe_status moe_quantized_x_offsets(const moe_problem* p, size_t* codes_offset /* host */,
+                                   size_t* scales_offset /* host */, int32_t* permuted /* host */);
 
 /* Host only.  Byte offsets, inside the workspace of moe_grouped_ffn / moe_grouped_ffn_mx (M rows in G
  * groups) or of moe_expert_forward / _mx (M = T*k, G = E), of the intermediate SwiGLU output h

@@ -20,7 +20,7 @@ __all__ = [
     "backward_workspace_size", "expert_backward", "route", "route_noalloc", "permute", "unpermute",
     "grouped_ffn_workspace_size", "grouped_ffn", "grouped_ffn_mx", "mx_quantize",
     "mx_fc1_epilogue_encode", "device_status", "chunk_counters",
-    "intermediate_h",
+    "intermediate_h", "quantized_x",
     "timing_enable", "timing_collect", "timing_reset",
 ]
 
@@ -72,6 +72,8 @@ _SIGS = {
     "moe_query_device_status": [_P, _P, ctypes.POINTER(ctypes.c_int32)],
     "moe_chunk_counters": [ctypes.POINTER(MoeProblem), _P, ctypes.c_size_t, _I64,
                            ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_I64)],
+    "moe_quantized_x_offsets": [ctypes.POINTER(MoeProblem), ctypes.POINTER(ctypes.c_size_t),
+                                ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_int32)],
     "moe_intermediate_offsets": [ctypes.POINTER(MoeProblem), _I64, _I64,
                                  ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)],
     "moe_status_string": [ctypes.c_int],
@@ -141,6 +143,7 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 FLAG_SEPARATE_PERMUTE = 1    # run the permute step as a kernel of its own (see the C header)
+FLAG_QUANTIZE_X = 2          # MX problem with bfloat16 x, encoded by the library (see the C header)
 
 
 def problem(T, H, F, E, k, dtype, head_m_size=0, flags=0) -> MoeProblem:
@@ -261,14 +264,22 @@ def expert_backward(x, w_gate, w_up, w_down, expert_ids, probs, dout, workspace=
 def expert_forward_mx(x, x_scale, w_gate, wg_scale, w_up, wu_scale, w_down, wd_scale, expert_ids,
                       probs, head_m_size: int = 0, out=None, workspace=None,
                       separate_permute: bool = False):
-    """The same layer on OCP-MX E4M3 bytes (uint8 tensors) with E8M0 block scales; bf16 output."""
+    """The same layer on OCP-MX E4M3 bytes (uint8 tensors) with E8M0 block scales; bf16 output.
+    A bfloat16 x with x_scale None is encoded by the library on its way into the gather
+    (MOE_FLAG_QUANTIZE_X)."""
     T, H = x.shape
     E, _, F = w_gate.shape
     k = expert_ids.shape[1]
     dev = x.device
     u8 = torch.uint8
-    _need(x, "x", u8, (T, H))
-    _need(x_scale, "x_scale", u8, (T, H // 32), dev)
+    quantize_x = x.dtype == torch.bfloat16
+    if quantize_x:
+        if x_scale is not None:
+            raise ValueError("a bfloat16 x is encoded by the library: pass x_scale=None")
+        _need(x, "x", torch.bfloat16, (T, H))
+    else:
+        _need(x, "x", u8, (T, H))
+        _need(x_scale, "x_scale", u8, (T, H // 32), dev)
     _need(w_gate, "w_gate", u8, (E, H, F), dev)
     _need(wg_scale, "wg_scale", u8, (E, H // 32, F), dev)
     _need(w_up, "w_up", u8, (E, H, F), dev)
@@ -277,7 +288,8 @@ def expert_forward_mx(x, x_scale, w_gate, wg_scale, w_up, wu_scale, w_down, wd_s
     _need(wd_scale, "wd_scale", u8, (E, F // 32, H), dev)
     _need(expert_ids, "expert_ids", torch.int32, (T, k), dev)
     _need(probs, "probs", torch.float32, (T, k), dev)
-    prob = problem(T, H, F, E, k, MXFP8, head_m_size, FLAG_SEPARATE_PERMUTE if separate_permute else 0)
+    flags = (FLAG_SEPARATE_PERMUTE if separate_permute else 0) | (FLAG_QUANTIZE_X if quantize_x else 0)
+    prob = problem(T, H, F, E, k, MXFP8, head_m_size, flags)
     ws = _workspace(workspace_size(prob), dev, workspace)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
@@ -472,6 +484,21 @@ def chunk_counters(workspace, M: int, H: int, F: int, head_m_size: int, dtype: i
     oc, ot = c.value - base, t.value - base
     nb = 4 * n.value
     return (workspace[oc:oc + nb].view(torch.int32), workspace[ot:ot + nb].view(torch.int32))
+
+
+def quantized_x(workspace, T: int, H: int, F: int, E: int, k: int, head_m_size: int = 0,
+                separate_permute: bool = False):
+    """Views into `workspace` of the encoded x that a forward with a bfloat16 x left there:
+    (codes uint8 [rows, H], scales uint8 [rows, H/32], permuted), in token order (rows = T,
+    permuted False) or in the permuted row order (rows = T*k, permuted True)."""
+    flags = FLAG_QUANTIZE_X | (FLAG_SEPARATE_PERMUTE if separate_permute else 0)
+    prob = problem(T, H, F, E, k, MXFP8, head_m_size, flags)
+    co, so, pm = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int32()
+    _check(library().moe_quantized_x_offsets(ctypes.byref(prob), ctypes.byref(co), ctypes.byref(so),
+                                             ctypes.byref(pm)))
+    rows = T * k if pm.value else T
+    return (workspace[co.value:co.value + rows * H].view(rows, H),
+            workspace[so.value:so.value + rows * (H // 32)].view(rows, H // 32), bool(pm.value))
 
 
 def intermediate_h(workspace, M: int, G: int, H: int, F: int, E: int, dtype: int,

@@ -160,10 +160,13 @@ moe_status check_problem(const moe_problem* p, bool need_tokens, bool gemm = tru
 {
     if (p == nullptr)
         return fail(MOE_ERR_INVALID_ARGUMENT, "problem is null");
-    if ((p->flags & ~static_cast<uint32_t>(MOE_FLAG_SEPARATE_PERMUTE)) != 0 || p->reserved != 0)
+    if ((p->flags & ~static_cast<uint32_t>(MOE_FLAG_SEPARATE_PERMUTE | MOE_FLAG_QUANTIZE_X)) != 0 ||
+        p->reserved != 0)
         return fail(MOE_ERR_INVALID_ARGUMENT, "unknown flags, or reserved not 0");
     if (p->dtype != MOE_F32 && p->dtype != MOE_BF16 && p->dtype != MOE_MXFP8_E4M3)
         return fail(MOE_ERR_UNSUPPORTED, "unknown dtype %d", p->dtype);
+    if ((p->flags & MOE_FLAG_QUANTIZE_X) != 0 && p->dtype != MOE_MXFP8_E4M3)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "MOE_FLAG_QUANTIZE_X needs dtype MOE_MXFP8_E4M3");
     if (p->H <= 0 || p->F <= 0 || p->E <= 0)
         return fail(MOE_ERR_INVALID_ARGUMENT, "H, F and E must be positive");
     if (p->E >= kMaxExperts)
@@ -260,7 +263,7 @@ FfnLayout ffn_layout(int dtype, int64_t M, int64_t G, int64_t H, int64_t F, int6
 }
 
 ForwardLayout forward_layout(int dtype, int64_t T, int64_t H, int64_t F, int64_t E, int64_t k,
-                             int64_t chunk)
+                             int64_t chunk, bool quantize_x)
 {
     const int64_t M = T * k;
     ForwardLayout L;
@@ -283,6 +286,13 @@ ForwardLayout forward_layout(int dtype, int64_t T, int64_t H, int64_t F, int64_t
         off = align_up(off + static_cast<size_t>(M * (H / 32)));
     L.y_perm = off;
     off = align_up(off + static_cast<size_t>(M * H * out_bytes(dtype)));
+    L.x_q = off;
+    L.x_q_scale = off;
+    if (quantize_x) {
+        off = align_up(off + static_cast<size_t>(T * H));
+        L.x_q_scale = off;
+        off = align_up(off + static_cast<size_t>(T * (H / 32)));
+    }
     L.total = off;
     return L;
 }
@@ -407,7 +417,8 @@ MOE_API moe_status moe_workspace_size(const moe_problem* p, size_t* bytes)
         return fail(MOE_ERR_INVALID_ARGUMENT, "bytes is null");
     if (moe_status st = check_problem(p, true); st != MOE_OK)
         return st;
-    *bytes = forward_layout(p->dtype, p->T, p->H, p->F, p->E, p->k, p->head_m_size).total;
+    *bytes = forward_layout(p->dtype, p->T, p->H, p->F, p->E, p->k, p->head_m_size,
+                            (p->flags & MOE_FLAG_QUANTIZE_X) != 0).total;
     return MOE_OK;
 }
 
@@ -417,7 +428,9 @@ static moe_status forward_common(const moe_problem* p, const void* x, const uint
                                  const int32_t* ids, const float* probs, void* out, void* ws,
                                  size_t ws_bytes, hipStream_t s, void* saved_gu = nullptr)
 {
-    const ForwardLayout L = forward_layout(p->dtype, p->T, p->H, p->F, p->E, p->k, p->head_m_size);
+    const bool quantize_x = (p->flags & MOE_FLAG_QUANTIZE_X) != 0;
+    const ForwardLayout L = forward_layout(p->dtype, p->T, p->H, p->F, p->E, p->k, p->head_m_size,
+                                           quantize_x);
     if (ws == nullptr || ws_bytes < L.total)
         return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", L.total,
                     ws == nullptr ? size_t{0} : ws_bytes);
@@ -440,7 +453,24 @@ static moe_status forward_common(const moe_problem* p, const void* x, const uint
     const bool fused = (p->flags & MOE_FLAG_SEPARATE_PERMUTE) == 0 && fc1_gathers(p->dtype, T, H, p->F);
     const void* rows = x;
     const uint8_t* rows_scale = x_scale;
-    if (!fused) {
+    if (quantize_x) {
+        // bfloat16 x is MX-encoded on its way into the gather: once per token, into the workspace,
+        // when fc1 gathers the rows itself; otherwise straight into the permuted rows
+        const auto* xb = static_cast<const uint16_t*>(x);
+        if (fused) {
+            LAUNCH(s, "mx_encode_x",
+                   launch_mx_encode_bf16_rows(xb, T, H, nullptr, k, M, at<uint8_t>(ws, L.x_q),
+                                              at<uint8_t>(ws, L.x_q_scale), s));
+            rows = at<void>(ws, L.x_q);
+            rows_scale = at<uint8_t>(ws, L.x_q_scale);
+        } else {
+            LAUNCH(s, "mx_encode_permute",
+                   launch_mx_encode_bf16_rows(xb, T, H, pos, k, M, at<uint8_t>(ws, L.x_perm),
+                                              at<uint8_t>(ws, L.x_perm_scale), s));
+            rows = at<void>(ws, L.x_perm);
+            rows_scale = at<uint8_t>(ws, L.x_perm_scale);
+        }
+    } else if (!fused) {
         LAUNCH(s, "permute", launch_permute(x, pos, at<void>(ws, L.x_perm), T, k, M, H * eb, s));
         if (p->dtype == MOE_MXFP8_E4M3)
             LAUNCH(s, "permute_scale",
@@ -501,8 +531,11 @@ MOE_API moe_status moe_expert_forward_mx(const moe_problem* p, const uint8_t* x,
         return st;
     if (p->dtype != MOE_MXFP8_E4M3)
         return fail(MOE_ERR_INVALID_ARGUMENT, "moe_expert_forward_mx needs dtype MOE_MXFP8_E4M3");
-    if (p->T > 0 && (x_scale == nullptr || wg_scale == nullptr || wu_scale == nullptr ||
-                     wd_scale == nullptr))
+    const bool quantize_x = (p->flags & MOE_FLAG_QUANTIZE_X) != 0;
+    if (quantize_x && x_scale != nullptr)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "with MOE_FLAG_QUANTIZE_X, x is bfloat16 and x_scale must be null");
+    if (p->T > 0 && ((!quantize_x && x_scale == nullptr) || wg_scale == nullptr ||
+                     wu_scale == nullptr || wd_scale == nullptr))
         return fail(MOE_ERR_INVALID_ARGUMENT, "null scale pointer");
     return forward_common(p, x, x_scale, w_gate, wg_scale, w_up, wu_scale, w_down, wd_scale,
                           expert_ids, probs, out_bf16, workspace, workspace_bytes, stream);
@@ -896,6 +929,23 @@ MOE_API moe_status moe_chunk_counters(const moe_problem* p, void* workspace,
     *counters = at<const int32_t>(workspace, L.chunk_done);
     *tiles_per_chunk = at<const int32_t>(workspace, L.chunk_tiles);
     *num_chunks = L.num_chunks;
+    return MOE_OK;
+}
+
+MOE_API moe_status moe_quantized_x_offsets(const moe_problem* p, size_t* codes_offset,
+                                           size_t* scales_offset, int32_t* permuted)
+{
+    if (codes_offset == nullptr || scales_offset == nullptr || permuted == nullptr)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+    if (moe_status st = check_problem(p, true); st != MOE_OK)
+        return st;
+    if ((p->flags & MOE_FLAG_QUANTIZE_X) == 0)
+        return fail(MOE_ERR_INVALID_ARGUMENT, "the problem does not set MOE_FLAG_QUANTIZE_X");
+    const ForwardLayout L = forward_layout(p->dtype, p->T, p->H, p->F, p->E, p->k, p->head_m_size, true);
+    const bool fused = (p->flags & MOE_FLAG_SEPARATE_PERMUTE) == 0 && fc1_gathers(p->dtype, p->T, p->H, p->F);
+    *codes_offset = fused ? L.x_q : L.x_perm;
+    *scales_offset = fused ? L.x_q_scale : L.x_perm_scale;
+    *permuted = fused ? 0 : 1;
     return MOE_OK;
 }
 

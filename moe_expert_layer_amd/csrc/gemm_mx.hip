@@ -63,6 +63,66 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(const float* __re
     }
 }
 
+// bfloat16 activation rows -> OCP-MX, on the way into the gather.  One thread per (token, block of
+// 32 along H): the block's 64 bytes are widened exactly to float32, the shared exponent comes from
+// the largest magnitude, every element is encoded with it (the integer encoder above), and the 32
+// code bytes and the scale byte go to the token's own row (pos null: token order, rows [T, H]) or
+// to each of its k permuted rows pos[t k + j] (the permute step with the encoding on its gather;
+// slots whose row lies outside [0, M) are skipped).
+__global__ __launch_bounds__(kThreads) void mx_encode_bf16_rows_kernel(
+    const uint16_t* __restrict__ x, int64_t T, int64_t blocks_per_row, const int32_t* __restrict__ pos,
+    int k, int64_t M, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales)
+{
+    const int64_t total = T * blocks_per_row;
+    const int64_t H = blocks_per_row * 32;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < total;
+         i += static_cast<int64_t>(gridDim.x) * kThreads) {
+        const int64_t t = i / blocks_per_row;
+        const int64_t b = i - t * blocks_per_row;
+        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + t * H + 32 * b);
+        u32x4_t raw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            raw[q] = src[q];
+        uint32_t amax = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                amax = max(amax, max((raw[q][w] << 16) & 0x7fffffffu, raw[q][w] & 0x7fff0000u));
+        const int e = mx_shared_exponent(amax);
+        u32x4_t out[2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+                const uint32_t lo = raw[q][2 * w], hi = raw[q][2 * w + 1];
+                out[q / 2][2 * (q % 2) + w] =
+                    e4m3_encode_scaled(__uint_as_float(lo << 16), e) |
+                    (e4m3_encode_scaled(__uint_as_float(lo & 0xffff0000u), e) << 8) |
+                    (e4m3_encode_scaled(__uint_as_float(hi << 16), e) << 16) |
+                    (e4m3_encode_scaled(__uint_as_float(hi & 0xffff0000u), e) << 24);
+            }
+        const uint8_t sc = static_cast<uint8_t>(e + 127);
+        if (pos == nullptr) {
+            u32x4_t* dst = reinterpret_cast<u32x4_t*>(codes + t * H + 32 * b);
+            dst[0] = out[0];
+            dst[1] = out[1];
+            scales[t * blocks_per_row + b] = sc;
+        } else {
+            for (int j = 0; j < k; ++j) {
+                const int64_t p = pos[t * k + j];
+                if (p < 0 || p >= M)
+                    continue;
+                u32x4_t* dst = reinterpret_cast<u32x4_t*>(codes + p * H + 32 * b);
+                dst[0] = out[0];
+                dst[1] = out[1];
+                scales[p * blocks_per_row + b] = sc;
+            }
+        }
+    }
+}
+
 // ----------------------------------------------------------------------------------- grouped GEMM
 
 constexpr int BM = kBmMx;          // 128 rows per task
@@ -1078,6 +1138,19 @@ hipError_t launch_mx_quantize(const float* v, int64_t rows, int64_t cols, uint8_
     const int64_t cap = static_cast<int64_t>(device_info().cu_count) * 8;
     mx_quantize_kernel<<<dim3(static_cast<unsigned>(want < cap ? (want > 0 ? want : 1) : cap)),
                          dim3(kThreads), 0, s>>>(v, nblocks, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_encode_bf16_rows(const uint16_t* x, int64_t T, int64_t H, const int32_t* pos,
+                                     int64_t k, int64_t M, uint8_t* codes, uint8_t* scales, hipStream_t s)
+{
+    const int64_t total = T * (H / 32);
+    if (total <= 0)
+        return hipSuccess;
+    const int64_t want = (total + kThreads - 1) / kThreads;
+    const int64_t cap = static_cast<int64_t>(device_info().cu_count) * 16;
+    mx_encode_bf16_rows_kernel<<<dim3(static_cast<unsigned>(want < cap ? want : cap)), dim3(kThreads), 0, s>>>(
+        x, T, H / 32, pos, static_cast<int>(k), M, codes, scales);
     return hipGetLastError();
 }
 

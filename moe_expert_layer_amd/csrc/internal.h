@@ -78,6 +78,7 @@ struct ForwardLayout {
     FfnLayout ffn;                     // offsets relative to the workspace base
     size_t counts = 0, offsets = 0, perm = 0, pos = 0;
     size_t x_perm = 0, x_perm_scale = 0, y_perm = 0;
+    size_t x_q = 0, x_q_scale = 0;     // MX-encoded x in token order [T, H] + [T, H/32] (bf16 input)
     size_t total = 0;
 };
 
@@ -85,7 +86,7 @@ RouteLayout route_layout(int64_t T, int64_t k, int64_t E, size_t base);
 FfnLayout ffn_layout(int dtype, int64_t M, int64_t G, int64_t H, int64_t F, int64_t chunk,
                      size_t base);
 ForwardLayout forward_layout(int dtype, int64_t T, int64_t H, int64_t F, int64_t E, int64_t k,
-                             int64_t chunk);
+                             int64_t chunk, bool quantize_x = false);
 
 // ---------------------------------------------------------------------------------------------
 // Launchers (defined in the .hip files).  Each returns the hipError_t of its launch.
@@ -217,6 +218,11 @@ hipError_t launch_router(const float* logits, int64_t T, int64_t E, int64_t k, i
                          float* probs, hipStream_t s);
 hipError_t launch_mx_quantize(const float* v, int64_t rows, int64_t cols, uint8_t* codes,
                               uint8_t* scales, hipStream_t s);
+// bfloat16 rows x [T, H] -> OCP-MX codes and scales (H a multiple of 32): in token order (pos null;
+// codes [T, H], scales [T, H/32]) or written to each token's k permuted rows pos[t k + j] (codes
+// [M, H], scales [M, H/32]; rows outside [0, M) skipped).
+hipError_t launch_mx_encode_bf16_rows(const uint16_t* x, int64_t T, int64_t H, const int32_t* pos,
+                                     int64_t k, int64_t M, uint8_t* codes, uint8_t* scales, hipStream_t s);
 // The MX fc1 epilogue's encoder (large_tiles: the 256-row kernel's, else the 128-row kernel's) on
 // float32 values v [rows, cols] in place of the SwiGLU output; cols a multiple of 128 (64), rows * cols
 // <= 2^28.

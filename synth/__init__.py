@@ -121,6 +121,7 @@ class LayerInputs:
     expert_ids: np.ndarray          # [T,k] int32
     probs: np.ndarray               # [T,k] float32
     x_scale: np.ndarray | None = None    # [T,H/32]  (mxfp8)
+    x_bf16: np.ndarray | None = None     # [T,H] bfloat16 bits of the x draw (mxfp8 workloads)
     wg_scale: np.ndarray | None = None   # [E,H/32,F]
     wu_scale: np.ndarray | None = None   # [E,H/32,F]
     wd_scale: np.ndarray | None = None   # [E,F/32,H]
@@ -209,7 +210,12 @@ def make_layer(T: int, H: int, F: int, E: int, k: int, dtype: str = "bf16",
         raise ValueError("mxfp8 needs H and F multiples of 32")
     st = _streams(seed, 2 + 3 * E)
     ids, probs = _route(st[0], T, E, k, routing, **routing_kw)
-    x, xs = _store(_normal_f32(st[1], (T, H), x_std), dtype, 1)
+    x32 = _normal_f32(st[1], (T, H), x_std)
+    x, xs = _store(x32, dtype, 1)
+    # MX workloads also carry the same draw rounded to bfloat16: activations as a bf16 producer
+    # hands them over, for the path that encodes x itself
+    x_bf16 = to_bf16_bits(x32) if dtype == "mxfp8" else None
+    del x32
 
     u8 = dtype == "mxfp8"
     edt = {"f32": np.float32, "bf16": np.uint16, "mxfp8": np.uint8}[dtype]
@@ -229,7 +235,7 @@ def make_layer(T: int, H: int, F: int, E: int, k: int, dtype: str = "bf16",
     with ThreadPoolExecutor(_WORKERS) as ex:
         list(ex.map(one, jobs))
     return LayerInputs(T=T, H=H, F=F, E=E, k=k, dtype=dtype, x=x, w_gate=mats[0], w_up=mats[1],
-                       w_down=mats[2], expert_ids=ids, probs=probs, x_scale=xs,
+                       w_down=mats[2], expert_ids=ids, probs=probs, x_scale=xs, x_bf16=x_bf16,
                        wg_scale=scl[0], wu_scale=scl[1], wd_scale=scl[2],
                        meta=dict(seed=seed, routing=routing, **routing_kw))
 
