@@ -171,3 +171,29 @@ def test_route_noalloc_rejects_before_touching_the_gpu(mel):
     assert b"scratch" in lib.moe_last_error()
     assert lib.moe_route_noalloc(None, 16, 3, 2, None, None, None, None, None) == 1     # k > E
     assert lib.moe_route_noalloc(None, 16, 2, 8, None, None, None, None, None) == 1     # null outputs
+
+
+def test_quantize_x_flag(mel):
+    """MOE_FLAG_QUANTIZE_X is an MX-only flag; its workspace adds the token-order encoded x
+    (T*H codes + T*H/32 scales), and the offsets query needs the flag."""
+    lib = mel.library()
+    n0, n1 = ctypes.c_size_t(), ctypes.c_size_t()
+    bf = mel.problem(64, 128, 128, 4, 2, mel.BF16, 0, mel.FLAG_QUANTIZE_X)
+    assert lib.moe_workspace_size(ctypes.byref(bf), ctypes.byref(n0)) == 1
+    T, H = 300, 1024
+    mx = mel.problem(T, H, 1024, 5, 2, mel.MXFP8, 0, 0)
+    mxq = mel.problem(T, H, 1024, 5, 2, mel.MXFP8, 0, mel.FLAG_QUANTIZE_X)
+    assert lib.moe_workspace_size(ctypes.byref(mx), ctypes.byref(n0)) == 0
+    assert lib.moe_workspace_size(ctypes.byref(mxq), ctypes.byref(n1)) == 0
+    assert n1.value >= n0.value + T * H + T * H // 32
+    co, so, pm = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int32()
+    assert lib.moe_quantized_x_offsets(ctypes.byref(mx), ctypes.byref(co), ctypes.byref(so),
+                                       ctypes.byref(pm)) == 1
+    assert lib.moe_quantized_x_offsets(ctypes.byref(mxq), ctypes.byref(co), ctypes.byref(so),
+                                       ctypes.byref(pm)) == 0
+    assert pm.value == 0 and so.value >= co.value + T * H and so.value + T * H // 32 <= n1.value
+    # a bfloat16 x with a scale pointer is refused before anything is enqueued
+    st = lib.moe_expert_forward_mx(ctypes.byref(mxq), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1000),
+                                   *([ctypes.c_void_p(0x1000)] * 10), ctypes.c_void_p(0x1000), n1.value,
+                                   None)
+    assert st == 1 and b"x_scale" in lib.moe_last_error()
