@@ -194,6 +194,6 @@ def test_quantize_x_flag(mel):
     assert pm.value == 0 and so.value >= co.value + T * H and so.value + T * H // 32 <= n1.value
     # a bfloat16 x with a scale pointer is refused before anything is enqueued
     st = lib.moe_expert_forward_mx(ctypes.byref(mxq), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1000),
-                                   *([ctypes.c_void_p(0x1000)] * 10), ctypes.c_void_p(0x1000), n1.value,
+                                   *([ctypes.c_void_p(0x1000)] * 9), ctypes.c_void_p(0x1000), n1.value,
                                    None)
     assert st == 1 and b"x_scale" in lib.moe_last_error()
