@@ -253,6 +253,8 @@ FfnLayout ffn_layout(int dtype, int64_t M, int64_t G, int64_t H, int64_t F, int6
         L.tiles2 = off;
         off = align_up(off + sizeof(MTile) * static_cast<size_t>(L.max_tiles2));
     }
+    L.tiles_run = off;
+    off = align_up(off + sizeof(MTile) * static_cast<size_t>(L.max_tiles1));
     L.h = off;
     off = align_up(off + static_cast<size_t>(M * F * elem_bytes(dtype)));
     L.h_scale = off;
@@ -368,15 +370,22 @@ moe_status run_ffn(int dtype, const void* rows, const uint8_t* rows_scale, int64
     int32_t* chunk_done = head_m_size > 0 ? at<int32_t>(ws, L.chunk_done) : nullptr;
     int32_t* chunk_tiles = head_m_size > 0 ? at<int32_t>(ws, L.chunk_tiles) : nullptr;
     int32_t* task_ctr = at<int32_t>(ws, L.task_ctr);
+    // Unchunked large tiles: fc1 takes a table whose partial tails sit inside their expert's run, so a
+    // tail's tasks follow the full tiles of the same weight strip while the strip is still in the L2;
+    // fc2 keeps the tails last (its short ones split into half-width tasks).
+    const bool fc1_in_run = head_m_size <= 0 && L.bm1 == 256 && dtype != MOE_F32;
+    MTile* tiles_fc1 = fc1_in_run ? at<MTile>(ws, L.tiles_run) : tiles;
+    int32_t* tcount_fc1 = fc1_in_run ? tcount + 3 : tcount;
     LAUNCH(s, "build_tiles",
            launch_build_tiles(offsets, group_expert, G, E, M, chunk, L.bm1, tiles, L.max_tiles1,
                               tcount, chunk_tiles, chunk_done, L.num_chunks,
-                              fc2_col_tiles(dtype, H, F), task_ctr, status, write_status, s));
+                              fc2_col_tiles(dtype, H, F), task_ctr, status, write_status, s,
+                              fc1_in_run ? tiles_fc1 : nullptr, fc1_in_run ? tcount_fc1 : nullptr));
     if (dtype == MOE_BF16) {
         uint16_t* h = at<uint16_t>(ws, L.h);
         LAUNCH(s, "fc1_bf16",
                launch_fc1_bf16(static_cast<const uint16_t*>(rows), static_cast<const uint16_t*>(wg),
-                               static_cast<const uint16_t*>(wu), h, tiles, tcount, H, F,
+                               static_cast<const uint16_t*>(wu), h, tiles_fc1, tcount_fc1, H, F,
                                task_ctr, gather, gather_k, save_gu,
                                save_gu != nullptr ? save_gu + M * F : nullptr, s));
         LAUNCH(s, "fc2_bf16",
@@ -396,7 +405,7 @@ moe_status run_ffn(int dtype, const void* rows, const uint8_t* rows_scale, int64
         LAUNCH(s, "fc1_mx",
                launch_fc1_mx(static_cast<const uint8_t*>(rows), rows_scale,
                              static_cast<const uint8_t*>(wg), wgs, static_cast<const uint8_t*>(wu),
-                             wus, h, hs, tiles, tcount, H, F, task_ctr, gather, gather_k, s));
+                             wus, h, hs, tiles_fc1, tcount_fc1, H, F, task_ctr, gather, gather_k, s));
         LAUNCH(s, "fc2_mx",
                launch_fc2_mx(h, hs, static_cast<const uint8_t*>(wd), wds, static_cast<uint16_t*>(y),
                              tiles, tcount, H, F, chunk_done, task_ctr + kXcdCount, s));

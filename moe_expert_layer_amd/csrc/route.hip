@@ -201,9 +201,10 @@ __global__ __launch_bounds__(kThreads) void route_scatter_kernel(
 // One workgroup; groups are handled 1024 at a time.
 __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ group_expert, int G, int E,
-    int64_t M, int64_t chunk, int bm, MTile* __restrict__ tiles, int max_tiles, int32_t* __restrict__ tile_count,
+    int64_t M, int64_t chunk, int bm, MTile* __restrict__ tiles_main, int max_tiles, int32_t* __restrict__ tile_count,
     int32_t* __restrict__ chunk_tiles, int32_t* __restrict__ chunk_done, int num_chunks,
-    int col_tiles, int32_t* __restrict__ task_ctr, int32_t* __restrict__ status, int write_status)
+    int col_tiles, int32_t* __restrict__ task_ctr, int32_t* __restrict__ status, int write_status,
+    MTile* __restrict__ tiles_in_run, int32_t* __restrict__ count_in_run)
 {
     if (task_ctr != nullptr && threadIdx.x < 2 * kXcdCount)
         task_ctr[threadIdx.x] = 0;
@@ -224,122 +225,136 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
             chunk_done[c] = 0;
         }
     __syncthreads();
-    const bool tails_last = num_chunks <= 1;
-    for (int pass = 0; pass < (tails_last ? 2 : 1); ++pass) {
-        if (pass == 1 && threadIdx.x == 0)
-            full_tiles = carry;                   // read by thread 0 only, after the last barrier
-        for (int g0 = 0; g0 < G; g0 += kScanThreads) {
-            const int g = g0 + threadIdx.x;
-            int64_t rb = 0, re = 0;
-            int ex = 0, n = 0;
-            if (g < G) {
-                // clamp into [0, M] so that malformed offsets can never address rows outside the buffers
-                rb = min(max(static_cast<int64_t>(offsets[g]), int64_t{0}), M);
-                re = min(max(static_cast<int64_t>(offsets[g + 1]), rb), M);
-                ex = group_expert ? group_expert[g] : g;
-                if (ex < 0 || ex >= E) {
-                    if (re > rb)
-                        atomicOr(&bad, 1);
-                    re = rb;   // skipped
-                }
-                if (!tails_last) {
-                    for (int64_t r = rb; r < re;) {
-                        const int64_t cend = min(re, (r / chunk + 1) * chunk);
-                        n += static_cast<int>((cend - r + bm - 1) / bm);
-                        r = cend;
-                    }
-                } else if (pass == 0) {
-                    n = static_cast<int>(re - rb) / bm;
-                } else {
-                    n = static_cast<int>(re - rb) % bm != 0 ? 1 : 0;
-                }
-            }
-            int incl = block_inclusive_scan(n, buf);
-            int t = carry + incl - n;
-            if (tails_last && pass == 1 && G <= kScanThreads) {
-                // longest partial tiles first (all groups fit one pass): the rank of this group's
-                // tail among all tails, larger first, ties by group index
-                __shared__ int tail_rows[kScanThreads];
-                const int mine = n != 0 ? static_cast<int>(re - rb) % bm : -1;
-                tail_rows[threadIdx.x] = mine;
-                if (mine > kHalfWidthMaxRows)
-                    atomicAdd(&tall_tails, 1);
-                __syncthreads();
-                int rank = 0;
-                if (n != 0) {                     // groups without a tail skip the count
-#pragma unroll 8
-                    for (int q = 0; q < G; ++q) {
-                        const int other = tail_rows[q];
-                        rank += (other > mine || (other == mine && q < g)) ? 1 : 0;
-                    }
-                }
-                __syncthreads();
-                if (n != 0)
-                    t = carry + rank;
-            }
-            // c: the tile's chunk (0 unchunked), computed once per chunk piece by the caller, since a
-            // 64-bit division is a long software sequence
-            auto emit = [&](int64_t r0, int64_t r1, int run_begin, int run_len, int c) {
-                if (t < max_tiles) {
-                    MTile mt;
-                    mt.expert = ex;
-                    mt.row_begin = static_cast<int>(r0);
-                    mt.row_end = static_cast<int>(r1);
-                    mt.chunk = c;
-                    mt.run_begin = run_begin;
-                    mt.run_len = run_len;
-                    mt.pad0 = mt.pad1 = 0;
-                    tiles[t] = mt;
-                }
-                if (chunk_tiles != nullptr && c < num_chunks)
-                    atomicAdd(&chunk_tiles[c], col_tiles);
-                ++t;
-            };
-            if (!tails_last) {
-                // a run: the group's tiles inside one window of kChunkWindow chunks
-                const int64_t win = chunk * kChunkWindow;
-                for (int64_t r = rb; r < re;) {
-                    const int64_t wend = min(re, (r / win + 1) * win);
-                    int run_len = 0;
-                    for (int64_t q = r; q < wend;) {
-                        const int64_t cend = min(wend, (q / chunk + 1) * chunk);
-                        run_len += static_cast<int>((cend - q + bm - 1) / bm);
-                        q = cend;
-                    }
-                    const int run_begin = t;
-                    for (int64_t q = r; q < wend;) {
-                        const int64_t c = q / chunk;
-                        const int64_t cend = min(wend, (c + 1) * chunk);
-                        for (int64_t r0 = q; r0 < cend; r0 += bm)
-                            emit(r0, min(cend, r0 + bm), run_begin, run_len, static_cast<int>(c));
-                        q = cend;
-                    }
-                    r = wend;
-                }
-            } else if (pass == 0) {
-                const int run_begin = t;
-                for (int i = 0; i < n; ++i)
-                    emit(rb + int64_t{i} * bm, rb + int64_t{i + 1} * bm, run_begin, n, 0);
-            } else if (n != 0) {
-                emit(rb + static_cast<int>(re - rb) / bm * bm, re, t, 1, 0);
-            }
+    // layout 0: the table (unchunked: partial tails last, sorted; chunked: row order); layout 1
+    // (unchunked, when asked for): every group's tiles, its tail included, as one run
+    const int layouts = tiles_in_run != nullptr && num_chunks <= 1 ? 2 : 1;
+    for (int layout = 0; layout < layouts; ++layout) {
+        MTile* const tiles = layout == 0 ? tiles_main : tiles_in_run;
+        const bool tails_last = layout == 0 && num_chunks <= 1;
+        if (layout == 1) {
             __syncthreads();
-            if (threadIdx.x == kScanThreads - 1)
-                carry += incl;
+            if (threadIdx.x == 0)
+                carry = 0;
             __syncthreads();
         }
-    }
-    if (threadIdx.x == 0) {
-        tile_count[0] = min(carry, max_tiles);
-        // tile_count[2]: how many tiles lead the table before the short partial tiles (rows <=
-        // kHalfWidthMaxRows) that the non-gated GEMM splits into half-width tasks.  Only an unchunked
-        // table whose tails were sorted (longest first, one pass over the groups) has such a suffix.
-        const bool sorted_tails = tails_last && G <= kScanThreads;
-        tile_count[2] = sorted_tails ? min(full_tiles + tall_tails, max_tiles) : min(carry, max_tiles);
-        if (write_status)
-            *status = bad ? kStatusBadId : kStatusOk;
-        else if (bad)
-            *status = kStatusBadId;
+        for (int pass = 0; pass < (tails_last ? 2 : 1); ++pass) {
+            if (pass == 1 && threadIdx.x == 0)
+                full_tiles = carry;                   // read by thread 0 only, after the last barrier
+            for (int g0 = 0; g0 < G; g0 += kScanThreads) {
+                const int g = g0 + threadIdx.x;
+                int64_t rb = 0, re = 0;
+                int ex = 0, n = 0;
+                if (g < G) {
+                    // clamp into [0, M] so that malformed offsets can never address rows outside the buffers
+                    rb = min(max(static_cast<int64_t>(offsets[g]), int64_t{0}), M);
+                    re = min(max(static_cast<int64_t>(offsets[g + 1]), rb), M);
+                    ex = group_expert ? group_expert[g] : g;
+                    if (ex < 0 || ex >= E) {
+                        if (re > rb)
+                            atomicOr(&bad, 1);
+                        re = rb;   // skipped
+                    }
+                    if (!tails_last) {
+                        for (int64_t r = rb; r < re;) {
+                            const int64_t cend = min(re, (r / chunk + 1) * chunk);
+                            n += static_cast<int>((cend - r + bm - 1) / bm);
+                            r = cend;
+                        }
+                    } else if (pass == 0) {
+                        n = static_cast<int>(re - rb) / bm;
+                    } else {
+                        n = static_cast<int>(re - rb) % bm != 0 ? 1 : 0;
+                    }
+                }
+                int incl = block_inclusive_scan(n, buf);
+                int t = carry + incl - n;
+                if (tails_last && pass == 1 && G <= kScanThreads) {
+                    // longest partial tiles first (all groups fit one pass): the rank of this group's
+                    // tail among all tails, larger first, ties by group index
+                    __shared__ int tail_rows[kScanThreads];
+                    const int mine = n != 0 ? static_cast<int>(re - rb) % bm : -1;
+                    tail_rows[threadIdx.x] = mine;
+                    if (mine > kHalfWidthMaxRows)
+                        atomicAdd(&tall_tails, 1);
+                    __syncthreads();
+                    int rank = 0;
+                    if (n != 0) {                     // groups without a tail skip the count
+    #pragma unroll 8
+                        for (int q = 0; q < G; ++q) {
+                            const int other = tail_rows[q];
+                            rank += (other > mine || (other == mine && q < g)) ? 1 : 0;
+                        }
+                    }
+                    __syncthreads();
+                    if (n != 0)
+                        t = carry + rank;
+                }
+                // c: the tile's chunk (0 unchunked), computed once per chunk piece by the caller, since a
+                // 64-bit division is a long software sequence
+                auto emit = [&](int64_t r0, int64_t r1, int run_begin, int run_len, int c) {
+                    if (t < max_tiles) {
+                        MTile mt;
+                        mt.expert = ex;
+                        mt.row_begin = static_cast<int>(r0);
+                        mt.row_end = static_cast<int>(r1);
+                        mt.chunk = c;
+                        mt.run_begin = run_begin;
+                        mt.run_len = run_len;
+                        mt.pad0 = mt.pad1 = 0;
+                        tiles[t] = mt;
+                    }
+                    if (layout == 0 && chunk_tiles != nullptr && c < num_chunks)
+                        atomicAdd(&chunk_tiles[c], col_tiles);
+                    ++t;
+                };
+                if (!tails_last) {
+                    // a run: the group's tiles inside one window of kChunkWindow chunks
+                    const int64_t win = chunk * kChunkWindow;
+                    for (int64_t r = rb; r < re;) {
+                        const int64_t wend = min(re, (r / win + 1) * win);
+                        int run_len = 0;
+                        for (int64_t q = r; q < wend;) {
+                            const int64_t cend = min(wend, (q / chunk + 1) * chunk);
+                            run_len += static_cast<int>((cend - q + bm - 1) / bm);
+                            q = cend;
+                        }
+                        const int run_begin = t;
+                        for (int64_t q = r; q < wend;) {
+                            const int64_t c = q / chunk;
+                            const int64_t cend = min(wend, (c + 1) * chunk);
+                            for (int64_t r0 = q; r0 < cend; r0 += bm)
+                                emit(r0, min(cend, r0 + bm), run_begin, run_len, static_cast<int>(c));
+                            q = cend;
+                        }
+                        r = wend;
+                    }
+                } else if (pass == 0) {
+                    const int run_begin = t;
+                    for (int i = 0; i < n; ++i)
+                        emit(rb + int64_t{i} * bm, rb + int64_t{i + 1} * bm, run_begin, n, 0);
+                } else if (n != 0) {
+                    emit(rb + static_cast<int>(re - rb) / bm * bm, re, t, 1, 0);
+                }
+                __syncthreads();
+                if (threadIdx.x == kScanThreads - 1)
+                    carry += incl;
+                __syncthreads();
+            }
+        }
+        if (layout == 1 && threadIdx.x == 0)
+            *count_in_run = min(carry, max_tiles);
+        if (layout == 0 && threadIdx.x == 0) {
+            tile_count[0] = min(carry, max_tiles);
+            // tile_count[2]: how many tiles lead the table before the short partial tiles (rows <=
+            // kHalfWidthMaxRows) that the non-gated GEMM splits into half-width tasks.  Only an unchunked
+            // table whose tails were sorted (longest first, one pass over the groups) has such a suffix.
+            const bool sorted_tails = tails_last && G <= kScanThreads;
+            tile_count[2] = sorted_tails ? min(full_tiles + tall_tails, max_tiles) : min(carry, max_tiles);
+            if (write_status)
+                *status = bad ? kStatusBadId : kStatusOk;
+            else if (bad)
+                *status = kStatusBadId;
+        }
     }
 }
 
@@ -379,12 +394,14 @@ hipError_t launch_build_tiles(const int32_t* offsets, const int32_t* group_exper
                               int64_t E, int64_t M, int64_t chunk, int bm, MTile* tiles, int64_t max_tiles,
                               int32_t* tile_count, int32_t* chunk_tiles, int32_t* chunk_done,
                               int64_t num_chunks, int col_tiles, int32_t* task_ctr,
-                              int32_t* status, bool write_status, hipStream_t s)
+                              int32_t* status, bool write_status, hipStream_t s,
+                              MTile* tiles_in_run, int32_t* count_in_run)
 {
     build_tiles_kernel<<<dim3(1), dim3(kScanThreads), 0, s>>>(
         offsets, group_expert, static_cast<int>(G), static_cast<int>(E), M, chunk, bm, tiles,
         static_cast<int>(max_tiles), tile_count, chunk_tiles, chunk_done,
-        static_cast<int>(num_chunks), col_tiles, task_ctr, status, write_status ? 1 : 0);
+        static_cast<int>(num_chunks), col_tiles, task_ctr, status, write_status ? 1 : 0,
+        tiles_in_run, count_in_run);
     return hipGetLastError();
 }
 
