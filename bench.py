@@ -224,8 +224,24 @@ def movement_rates(torch, mel, inp, d, dev, flush, bytes_):
                         "frac": ub / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "launches": n,
                         "buffer_sets": S, "graph_equals_eager": bool(ok)}
     del ys, os_
+    # the ceiling at these sizes: a plain device copy moving the same number of bytes (half read,
+    # half written), timed the same way over its own rotating buffers
+    for name in ("permute", "unpermute"):
+        nbytes = out[name]["bytes"]
+        half = (nbytes // 2 + 15) // 16 * 16
+        S = max(2, -(-(768 << 20) // nbytes))
+        srcs = [torch.empty(half, dtype=torch.uint8, device=dev).fill_(1) for _ in range(S)]
+        dsts = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(S)]
+        launches = [lambda i=i: dsts[i].copy_(srcs[i]) for i in range(S)]
+        ms, _, _ = graph_rate(torch, launches, S, flush)
+        cgbs = 2 * half / (ms * 1e-3) / 1e9
+        out[name]["copy_same_bytes_GB/s"] = cgbs
+        out[name]["copy_same_bytes_frac"] = cgbs / HBM_PEAK_GBS
+        out[name]["frac_of_copy"] = out[name]["GB/s"] / cgbs
+        del srcs, dsts
     torch.cuda.synchronize()
-    log("standalone: " + ", ".join(f"{k_} {v['us']:.1f} us {v['GB/s']:.0f} GB/s ({100 * v['frac']:.0f}%)"
+    log("standalone: " + ", ".join(f"{k_} {v['us']:.1f} us {v['GB/s']:.0f} GB/s ({100 * v['frac']:.0f}%; "
+                                   f"a copy of the same bytes {v['copy_same_bytes_GB/s']:.0f} GB/s)"
                                    for k_, v in out.items()))
     return out
 
