@@ -269,7 +269,9 @@ moe_status moe_router_topk(const float* logits, int64_t T, int64_t E, int64_t k,
  * (cols a multiple of 32) -> codes [rows, cols] E4M3 bytes and scales [rows, cols/32] E8M0 bytes.
  * Shared exponent floor(log2 max|block|) - 8 clamped to [-127, 127] (-127 for an all-zero block);
  * elements v / 2^e rounded to nearest even on the E4M3 grid, saturated to +-448, sign kept.
- * Integer arithmetic on the float32 bits: bit-exact and deterministic. */
+ * The shared exponent is integer arithmetic on the float32 bits and the elements go through the
+ * hardware E4M3 conversion after an exact power-of-two scaling and a clamp to +-448: bit-exact and
+ * deterministic. */
 moe_status moe_mx_quantize(const float* v, int64_t rows, int64_t cols, uint8_t* codes,
                            uint8_t* scales, hipStream_t stream);
 

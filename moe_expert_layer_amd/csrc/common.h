@@ -62,54 +62,17 @@ __device__ __forceinline__ int mx_shared_exponent(uint32_t amax_bits)
     return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-// E4M3 code of v * 2^-e: round to nearest, ties to even, saturate to 448, keep the sign.
-// Pure integer arithmetic on v's bits, so the result is exact for every float input.
-__device__ __forceinline__ uint32_t e4m3_encode_scaled(float v, int e)
+// E4M3 codes of v0 .. v3 scaled by 2^-e (OCP MX: round to nearest, ties to even, saturate to 448,
+// keep the sign), packed into 32 bits with v0 in the low byte, through the hardware conversion
+// v_cvt_pk_fp8_f32.  The scaling by a power of two is exact (a result too small for a normal float
+// codes to a signed zero either way); v * 2^-e lies in [-512, 512] since 2^e is at least amax / 2^9,
+// and clamping it to +-448 before the conversion's round-to-nearest-even gives the saturation.
+__device__ __forceinline__ uint32_t e4m3_encode4_scaled(float v0, float v1, float v2, float v3, int e)
 {
-    const uint32_t bits = __float_as_uint(v);
-    const uint32_t sign = (bits >> 24) & 0x80u;
-    const uint32_t abits = bits & 0x7fffffffu;
-    if (abits == 0)
-        return sign;
-    // |v| = sig * 2^(ex - 23) with sig in [2^23, 2^24)
-    uint32_t sig;
-    int ex;
-    const int ef = static_cast<int>(abits >> 23);
-    if (ef != 0) {
-        sig = (abits & 0x7fffffu) | 0x800000u;
-        ex = ef - 127;
-    } else {
-        const int b = 31 - __clz(static_cast<int>(abits));
-        sig = abits << (23 - b);
-        ex = b - 149;
-    }
-    int ey = ex - e;                                  // exponent of |v| / 2^e
-    if (ey > 8)
-        return sign | 0x7eu;
-    if (ey >= -6) {                                   // E4M3 normal range
-        const uint32_t m23 = sig & 0x7fffffu;
-        uint32_t m3 = m23 >> 20;
-        const uint32_t rem = m23 & 0xfffffu;
-        if (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u)))
-            ++m3;
-        if (m3 == 8u) {
-            m3 = 0;
-            ++ey;
-        }
-        if (ey > 8 || (ey == 8 && m3 == 7u))
-            return sign | 0x7eu;
-        return sign | (static_cast<uint32_t>(ey + 7) << 3) | m3;
-    }
-    // subnormal range: count of 2^-9 steps, |v| / 2^e / 2^-9 = sig * 2^(ey - 14)
-    const int shift = 14 - ey;                        // >= 21
-    if (shift > 25)
-        return sign;
-    uint32_t q = sig >> shift;
-    const uint32_t rem = sig & ((1u << shift) - 1u);
-    const uint32_t half = 1u << (shift - 1);
-    if (rem > half || (rem == half && (q & 1u)))
-        ++q;
-    return sign | q;                                  // q <= 8; q == 8 is the min normal 0x08
+    const auto sc = [e](float v) { return fminf(fmaxf(ldexpf(v, -e), -448.0f), 448.0f); };
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(sc(v0), sc(v1), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(sc(v2), sc(v3), w, true);
+    return static_cast<uint32_t>(w);
 }
 
 }  // namespace moe

@@ -14,7 +14,7 @@
 // rows staged to LDS as loaded, weights ([K, N], N contiguous) transposed byte-wise in registers
 // into K-contiguous LDS rows, two LDS stages, XOR-swizzled 16-byte chunks.  The fc1 epilogue stages
 // the fp32 SwiGLU tile in LDS so each lane owns one (row, 32-column block), finds its amax, and
-// writes 32 E4M3 bytes plus one scale byte with the same integer encoder as the standalone kernel.
+// writes 32 E4M3 bytes plus one scale byte with the same encoder as the standalone kernel.
 #include <atomic>
 
 #include "common.h"
@@ -29,8 +29,8 @@ constexpr int kXcds = 8;
 
 // ----------------------------------------------------------------------------------- standalone encoder
 
-// One thread per 32-element block: shared exponent from the block's largest magnitude, then each
-// element encoded with it.  Integer arithmetic on the float bits throughout.
+// One thread per 32-element block: shared exponent from the block's largest magnitude (integer
+// arithmetic on the float bits), then each element encoded with it (e4m3_encode4_scaled).
 __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(const float* __restrict__ v,
                                                                int64_t nblocks,
                                                                uint8_t* __restrict__ codes,
@@ -52,10 +52,7 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(const float* __re
         u32x4_t out[2];
 #pragma unroll
         for (int w = 0; w < 8; ++w)
-            out[w / 4][w % 4] = e4m3_encode_scaled(x[w][0], e) |
-                                (e4m3_encode_scaled(x[w][1], e) << 8) |
-                                (e4m3_encode_scaled(x[w][2], e) << 16) |
-                                (e4m3_encode_scaled(x[w][3], e) << 24);
+            out[w / 4][w % 4] = e4m3_encode4_scaled(x[w][0], x[w][1], x[w][2], x[w][3], e);
         u32x4_t* dst = reinterpret_cast<u32x4_t*>(codes + b * 32);
         dst[0] = out[0];
         dst[1] = out[1];
@@ -65,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(const float* __re
 
 // bfloat16 activation rows -> OCP-MX, on the way into the gather.  One thread per (token, block of
 // 32 along H): the block's 64 bytes are widened exactly to float32, the shared exponent comes from
-// the largest magnitude, every element is encoded with it (the integer encoder above), and the 32
+// the largest magnitude, every element is encoded with it (the encoder above), and the 32
 // code bytes and the scale byte go to the token's own row (pos null: token order, rows [T, H]) or
 // to each of its k permuted rows pos[t k + j] (the permute step with the encoding on its gather;
 // slots whose row lies outside [0, M) are skipped).
@@ -98,10 +95,8 @@ __global__ __launch_bounds__(kThreads) void mx_encode_bf16_rows_kernel(
             for (int w = 0; w < 2; ++w) {
                 const uint32_t lo = raw[q][2 * w], hi = raw[q][2 * w + 1];
                 out[q / 2][2 * (q % 2) + w] =
-                    e4m3_encode_scaled(__uint_as_float(lo << 16), e) |
-                    (e4m3_encode_scaled(__uint_as_float(lo & 0xffff0000u), e) << 8) |
-                    (e4m3_encode_scaled(__uint_as_float(hi << 16), e) << 16) |
-                    (e4m3_encode_scaled(__uint_as_float(hi & 0xffff0000u), e) << 24);
+                    e4m3_encode4_scaled(__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
+                                        __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u), e);
             }
         const uint8_t sc = static_cast<uint8_t>(e + 127);
         if (pos == nullptr) {
@@ -246,10 +241,7 @@ __device__ __forceinline__ void store_h_small(const f32x16_t (&acc)[kTM][kTN], u
         u32x4_t out[2];
 #pragma unroll
         for (int w = 0; w < 8; ++w)
-            out[w / 4][w % 4] = e4m3_encode_scaled(x[w][0], e) |
-                                (e4m3_encode_scaled(x[w][1], e) << 8) |
-                                (e4m3_encode_scaled(x[w][2], e) << 16) |
-                                (e4m3_encode_scaled(x[w][3], e) << 24);
+            out[w / 4][w % 4] = e4m3_encode4_scaled(x[w][0], x[w][1], x[w][2], x[w][3], e);
         const int hcol = n0 + 32 * wn;         // this wave's 32 output columns
         u32x4_t* dst = reinterpret_cast<u32x4_t*>(Cq + static_cast<int64_t>(grow) * N_out + hcol);
         dst[0] = out[0];
@@ -760,7 +752,7 @@ __device__ __forceinline__ void store_y(const f32x16_t (&acc)[kTM][kTN], uint16_
 // fc1 epilogue: SwiGLU in fp32 into the staging area, 16 rows x 32 columns at a time (16-byte
 // chunks XOR-swizzled by row).  Four lanes share a row's 32-column block: each takes 8 values, the
 // block's largest magnitude is combined across the four, and each lane encodes its 8 values (OCP-MX,
-// the integer encoder) and stores 8 code bytes; the first of the four stores the scale byte.
+// e4m3_encode4_scaled) and stores 8 code bytes; the first of the four stores the scale byte.
 __device__ __forceinline__ uint32_t h_stage_off(int row, int col)
 {
     return row * 128 + 16 * (((col >> 2) ^ row) & 7) + 4 * (col & 3);
@@ -801,10 +793,8 @@ __device__ __forceinline__ void store_h(const f32x16_t (&acc)[kTM][kTN], uint8_t
                 amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 1)));
                 amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 2)));
                 const int e = mx_shared_exponent(amax);
-                const uint32_t lo = e4m3_encode_scaled(x0[0], e) | (e4m3_encode_scaled(x0[1], e) << 8) |
-                                    (e4m3_encode_scaled(x0[2], e) << 16) | (e4m3_encode_scaled(x0[3], e) << 24);
-                const uint32_t hi = e4m3_encode_scaled(x1[0], e) | (e4m3_encode_scaled(x1[1], e) << 8) |
-                                    (e4m3_encode_scaled(x1[2], e) << 16) | (e4m3_encode_scaled(x1[3], e) << 24);
+                const uint32_t lo = e4m3_encode4_scaled(x0[0], x0[1], x0[2], x0[3], e);
+                const uint32_t hi = e4m3_encode4_scaled(x1[0], x1[1], x1[2], x1[3], e);
                 const int grow = tile.row_begin + row_block<kWM>(i, wm) + 16 * half + erow;
                 const int hcol = n0 + 64 * wn + 32 * ob;
                 if (grow < tile.row_end) {

@@ -380,6 +380,43 @@ def _encoder_cases(rows, cols, seed):
     return v
 
 
+def _broad_encoder_input():
+    """[rows, 256] float32 blocks of 32 that pin the shared exponent to k (each block's first value is
+    448 * 2^k, every other value at most that in magnitude): every finite bfloat16 value of magnitude
+    at most 448, every E4M3 rounding midpoint and its float32 neighbours one ulp away on both sides,
+    and 100000 uniform values in (-448, 448), each set at k = -100, -20, 0, 37 and 100 (so the
+    encoder sees v * 2^k and must code v)."""
+    bits = np.arange(1 << 16, dtype=np.uint32) << 16
+    bf = bits.view(np.float32)
+    bf = bf[np.isfinite(bf) & (np.abs(bf) <= 448.0)]
+    vals = np.array([oracle.e4m3_value(c) for c in range(127)], np.float64)
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)
+    mids = np.concatenate([mids, -mids])
+    near = np.concatenate([mids, np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(-np.inf))])
+    near = near[np.abs(near) <= 448.0]
+    rnd = np.random.default_rng(9).uniform(-448, 448, 100000).astype(np.float32)
+    body = np.concatenate([bf, near, rnd]).astype(np.float32)
+    body = np.resize(body, -(-body.size // 31) * 31).reshape(-1, 31)
+    blocks = np.concatenate([np.full((body.shape[0], 1), 448.0, np.float32), body], axis=1)
+    flat = np.concatenate([np.ldexp(blocks, k).astype(np.float32) for k in (-100, -20, 0, 37, 100)])
+    flat = flat.reshape(-1)
+    return np.resize(flat, -(-flat.size // 256) * 256).reshape(-1, 256)
+
+
+def test_mx_encoders_bit_exact_on_every_bf16_value_and_rounding_midpoint():
+    """The library's E4M3 encoding (hardware conversion of v / 2^e, clamped to the E4M3 range) on a
+    broad input: the standalone encoder and both fc1 epilogues code every value as the oracle does."""
+    v = _broad_encoder_input()
+    q, sc = oracle.mx_quantize(v.astype(np.float64))
+    vd = dv.tensor(v)
+    codes, scales = mel.mx_quantize(vd)
+    assert np.array_equal(dv.host(scales), sc) and np.array_equal(dv.host(codes), q)
+    for large in (True, False):
+        rows = min(v.shape[0], (1 << 28) // v.shape[1])
+        c2, s2 = mel.mx_fc1_epilogue_encode(vd[:rows].contiguous(), large_tiles=large)
+        assert np.array_equal(dv.host(s2), sc[:rows]) and np.array_equal(dv.host(c2), q[:rows])
+
+
 @pytest.mark.parametrize("large,rows,cols", [(True, 300, 384), (True, 256, 128), (True, 37, 256),
                                              (False, 300, 192), (False, 128, 64), (False, 37, 128)],
                          ids=["large_ragged", "large_one_tile", "large_short", "small_ragged",
