@@ -64,8 +64,8 @@ struct FfnLayout {
     size_t status = 0;
     size_t tiles1 = 0, tiles2 = 0;     // MTile tables for fc1 / fc2 row-tile heights
     size_t tiles_run = 0;              // unchunked large tiles: fc1's table, partial tails inside their runs
-    size_t tile_count = 0;             // int32 [4]: [0] tiles in the table, [2] tiles before its short tails,
-                                       // [3] tiles in tiles_run
+    size_t tile_count = 0;             // int32 [8]: [0] tiles in the table, [2] tiles before its short tails;
+                                       // [4], [6] the same for tiles_run
     size_t task_ctr = 0;               // int32 [2][kXcdCount]: per-XCD task counters of fc1 / fc2
     size_t chunk_done = 0;             // int32 [num_chunks]: fc2 tiles finished per chunk
     size_t chunk_tiles = 0;            // int32 [num_chunks]: fc2 tiles per chunk
@@ -115,7 +115,8 @@ hipError_t launch_route_scatter(const int32_t* ids, int64_t M, int64_t E,
 // zeroes chunk_done; zeroes the 2 * kXcdCount task counters at task_ctr.  A non-empty group with an expert outside [0, E) is skipped and sets
 // *status; with write_status the status word is written either way.  tiles_in_run (may be null;
 // unchunked tables only): also the same tiles with every group's partial tail inside that group's run
-// (each run: the group's tiles in row order), their number in *count_in_run.
+// (each run: the group's tiles in row order), their number in count_in_run[0] and [2] (laid out as
+// tile_count, so either table can be handed to a GEMM with its counts).
 hipError_t launch_build_tiles(const int32_t* offsets, const int32_t* group_expert, int64_t G,
                               int64_t E, int64_t M, int64_t chunk, int bm, MTile* tiles, int64_t max_tiles,
                               int32_t* tile_count, int32_t* chunk_tiles, int32_t* chunk_done,

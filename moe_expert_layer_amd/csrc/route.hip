@@ -341,8 +341,10 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
                 __syncthreads();
             }
         }
-        if (layout == 1 && threadIdx.x == 0)
-            *count_in_run = min(carry, max_tiles);
+        if (layout == 1 && threadIdx.x == 0) {
+            count_in_run[0] = min(carry, max_tiles);
+            count_in_run[2] = count_in_run[0];    // no suffix of short tails: no half-width tasks
+        }
         if (layout == 0 && threadIdx.x == 0) {
             tile_count[0] = min(carry, max_tiles);
             // tile_count[2]: how many tiles lead the table before the short partial tiles (rows <=

@@ -201,13 +201,16 @@ def _layer_with_counts(counts, H, F, seed=11):
     return dataclasses.replace(inp, expert_ids=ids.astype(np.int32), probs=probs)
 
 
-def test_short_partial_tiles_half_width_tasks():
-    """Last row tiles of 1, 44 and 64 rows and an expert with one 64-row tile (the down projection
-    runs their column tiles as two half-width tasks) beside a 65-row one (kept whole) and an empty
-    expert: the output matches the oracle, is bitwise the chunked one (chunked tables never split),
-    and the backward that recomputes g and u (same kernel, same split) is bitwise the one that takes
-    the forward's saved values."""
-    inp = _layer_with_counts([257, 300, 320, 321, 0, 64], H=512, F=256)
+@pytest.mark.parametrize("counts", [[257, 300, 320, 321, 0, 64], [769, 812, 832, 833, 0, 64]],
+                         ids=["small_groups", "large_groups"])
+def test_short_partial_tiles_half_width_tasks(counts):
+    """Last row tiles of 1, 44 and 64 rows and an expert with one 64-row tile beside a 65-row one and
+    an empty expert.  With groups averaging at most two 256-row tiles (small_groups) both projections
+    run every group's tiles in one run; with larger groups the down projection keeps the tails last
+    and runs the short ones (at most 64 rows) as two half-width tasks each.  Either way the output
+    matches the oracle, is bitwise the chunked one (chunked tables never split), and the backward that
+    recomputes g and u (same kernel) is bitwise the one that takes the forward's saved values."""
+    inp = _layer_with_counts(counts, H=512, F=256)
     ref, *_ = oracle.forward(inp)
     d = dv.layer(inp)
     out = dv.host(dv.forward(mel, d, 0))
@@ -313,11 +316,13 @@ def test_grouped_ffn_matches_oracle():
     assert torch.equal(y, y2)
 
 
-def test_grouped_ffn_short_groups_large_tiles():
-    """Source-major groups of 257, 44, 64, 0, 65 and 300 rows at large-tile sizes: partial tiles of 1,
-    44 and 64 rows run as half-width down-projection tasks, the 65-row one whole; the output matches
-    the oracle and is bitwise the chunked one."""
-    sizes = [257, 44, 64, 0, 65, 300]
+@pytest.mark.parametrize("sizes", [[257, 44, 64, 0, 65, 300], [1281, 44, 64, 0, 65, 1836]],
+                         ids=["small_groups", "large_groups"])
+def test_grouped_ffn_short_groups_large_tiles(sizes):
+    """Source-major groups with partial tiles of 1, 44, 64 and 65 rows at large-tile sizes.  Groups
+    averaging at most two 256-row tiles run their tiles as one run in both projections; larger ones
+    (large_groups) run the down projection's short tails (at most 64 rows) as half-width tasks, the
+    65-row one whole.  The output matches the oracle and is bitwise the chunked one."""
     g = synth.make_grouped(rows=sum(sizes), H=512, F=256, E_local=2, sources=3, seed=5)
     g = dataclasses.replace(g, group_offsets=np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32),
                             recv_counts=np.asarray(sizes, np.int64).reshape(3, 2))
