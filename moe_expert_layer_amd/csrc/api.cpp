@@ -370,8 +370,8 @@ moe_status run_ffn(int dtype, const void* rows, const uint8_t* rows_scale, int64
     int32_t* chunk_done = head_m_size > 0 ? at<int32_t>(ws, L.chunk_done) : nullptr;
     int32_t* chunk_tiles = head_m_size > 0 ? at<int32_t>(ws, L.chunk_tiles) : nullptr;
     int32_t* task_ctr = at<int32_t>(ws, L.task_ctr);
-    // Unchunked large tiles: fc1 takes a table whose partial tails sit inside their expert's run, so a
-    // tail's tasks follow the full tiles of the same weight strip while the strip is still in the L2;
+    // Unchunked large tiles: fc1 takes a table in which each expert is one run of near-equal tiles, so
+    // the tasks of a weight strip run side by side, take equal time and share the strip in the L2;
     // fc2 keeps the tails last (its short ones split into half-width tasks).
     const bool fc1_in_run = head_m_size <= 0 && L.bm1 == 256 && dtype != MOE_F32;
     MTile* tiles_fc1 = fc1_in_run ? at<MTile>(ws, L.tiles_run) : tiles;

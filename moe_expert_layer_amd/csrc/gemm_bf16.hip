@@ -481,9 +481,9 @@ struct LoopArgs {
 
 // Slot M of a sub-step: MFMA M (row block M / kTN, column block M % kTN), then this slot's share of
 // the next sub-step's fragment reads (sub-step KS of step position SR) and of the sub-step's copies
-// (copy set CS into B stage SB / pair stage QA).  Reads and copies are spread evenly over the
-// MFMAs, so the wave's in-order issue never stalls on a burst of memory instructions, and no MFMA
-// waits for a read issued just before it.
+// (copy set CS into B stage SB / pair stage QA).  The reads go out over the first half of the
+// MFMAs, so they have landed well before a barrier's lgkmcnt(0) (spread over all of them, the last
+// read's latency was exposed at every barrier: 2% of the GEMM); the copies are spread over all.
 template <bool kGated, int NB, int CS, int SB, int QA, int SR, int KS, int M>
 __device__ __forceinline__ void slot(f32x16_t (&acc)[kTM][kTN], const Frags& use, Frags& load,
                                      const CopyCtx& cp, const LoopArgs& g)
@@ -491,7 +491,9 @@ __device__ __forceinline__ void slot(f32x16_t (&acc)[kTM][kTN], const Frags& use
     constexpr int NM = NB * kTN, NR = 2 * kTN + NB, NC = set_size<CS>();
     acc[M / kTN][M % kTN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(use.a[M / kTN], use.b[M % kTN],
                                                                     acc[M / kTN][M % kTN], 0, 0, 0);
-    reads<kGated, SR, KS, M * NR / NM, (M + 1) * NR / NM>(load, g.a_base, g.b_base);
+    constexpr int RF = NM / 2 > 0 ? NM / 2 : 1;                    // slots that carry the reads
+    if constexpr (M < RF)
+        reads<kGated, SR, KS, M * NR / RF, (M + 1) * NR / RF>(load, g.a_base, g.b_base);
     copies<CS, SB, QA, M * NC / NM, (M + 1) * NC / NM>(cp, g.a_voff, g.b_voff);
     __builtin_amdgcn_sched_barrier(0);
 }

@@ -493,7 +493,8 @@ __device__ __forceinline__ void copies(const Copy& cp, const Lane& ln, int SB)
     copies_impl<C0>(std::make_integer_sequence<int, C1 - C0>{}, cp, ln, SB);
 }
 
-// Slot M of a sub-step: MFMA M, then its share of the next fragment reads and of the copies.
+// Slot M of a sub-step: MFMA M, then its share of the next fragment reads (issued over the first
+// half of the MFMAs, so that they have landed before a barrier waits for them) and of the copies.
 template <int NC, int SB, int SR, int KS, int M>
 __device__ __forceinline__ void slot(f32x16_t (&acc)[kTM][kTN], const Frags& use, Frags& load,
                                      const Copy& cp, const Lane& ln)
@@ -501,7 +502,9 @@ __device__ __forceinline__ void slot(f32x16_t (&acc)[kTM][kTN], const Frags& use
     constexpr int NM = kTM * kTN, NR = 2 * (kTM + kTN);
     acc[M / kTN][M % kTN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(use.a[M / kTN], use.b[M % kTN],
                                                                     acc[M / kTN][M % kTN], 0, 0, 0);
-    reads<SR, KS, M * NR / NM, (M + 1) * NR / NM>(load, ln);
+    constexpr int RF = NM / 2;                                      // slots that carry the reads
+    if constexpr (M < RF)
+        reads<SR, KS, M * NR / RF, (M + 1) * NR / RF>(load, ln);
     copies<M * NC / NM, (M + 1) * NC / NM>(cp, ln, SB);
     __builtin_amdgcn_sched_barrier(0);
 }
@@ -792,7 +795,9 @@ __device__ __forceinline__ void slot(f32x16_t (&acc)[kTM][kTN], const Frags& use
     constexpr int NM = kTM * kTN, NR = kTM + kTN;
     acc[M / kTN][M % kTN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(use.a[M / kTN], use.b[M % kTN],
                                                                     acc[M / kTN][M % kTN], 0, 0, 0);
-    reads<SR, KS, M * NR / NM, (M + 1) * NR / NM>(load, ln);
+    constexpr int RF = NM / 2;                                      // slots that carry the reads
+    if constexpr (M < RF)
+        reads<SR, KS, M * NR / RF, (M + 1) * NR / RF>(load, ln);
     copies<M * NC / NM, (M + 1) * NC / NM>(cp, ln, SB);
     __builtin_amdgcn_sched_barrier(0);
 }

@@ -196,8 +196,12 @@ __global__ __launch_bounds__(kThreads) void route_scatter_kernel(
 // `chunk` rows) and each piece into tiles of at most bm rows; a run is the tiles of one piece.
 // Chunked (num_chunks > 1): tiles in row order (chunk-major); a run spans a group's tiles within a
 // window of kChunkWindow chunks, so the tasks sharing a weight strip stay together across the
-// window's chunks, and chunks complete in order window by window.  Unchunked: first every group's full tiles (row order), then the partial tail tiles, each
-// its own run, so that the short tasks come last and even out the workgroups' finishing times.
+// window's chunks, and chunks complete in order window by window.  Unchunked: first every group's
+// full tiles (row order), then the partial tail tiles, each its own run, so that the short tasks
+// come last and even out the workgroups' finishing times.  The second table (tiles_in_run,
+// unchunked calls only) keeps each group as one run of R = ceil(rows / bm) tiles of near-equal
+// height (their 32-row blocks differ by at most one): the tasks that share a weight strip then
+// take equal time, so the workgroups of an XCD stay in step and share the strip in its L2.
 // One workgroup; groups are handled 1024 at a time.
 __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ group_expert, int G, int E,
@@ -226,7 +230,7 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
         }
     __syncthreads();
     // layout 0: the table (unchunked: partial tails last, sorted; chunked: row order); layout 1
-    // (unchunked, when asked for): every group's tiles, its tail included, as one run
+    // (unchunked, when asked for): every group as one run of balanced tiles
     const int layouts = tiles_in_run != nullptr && num_chunks <= 1 ? 2 : 1;
     for (int layout = 0; layout < layouts; ++layout) {
         MTile* const tiles = layout == 0 ? tiles_main : tiles_in_run;
@@ -322,6 +326,20 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
                         for (int64_t q = r; q < wend;) {
                             const int64_t c = q / chunk;
                             const int64_t cend = min(wend, (c + 1) * chunk);
+                            if (layout == 1 && bm % 32 == 0) {
+                                // balanced: the piece's 32-row blocks spread over its R tiles as evenly
+                                // as possible (at most one block apart; the last tile ends the piece)
+                                const int len = static_cast<int>(cend - q);
+                                const int nblk = (len + 31) / 32, R = (len + bm - 1) / bm;
+                                int64_t r0 = q;
+                                for (int i = 0; i < R; ++i) {
+                                    const int64_t r1 = i == R - 1 ? cend : r0 + 32 * (nblk / R + (i < nblk % R ? 1 : 0));
+                                    emit(r0, r1, run_begin, run_len, static_cast<int>(c));
+                                    r0 = r1;
+                                }
+                                q = cend;
+                                continue;
+                            }
                             for (int64_t r0 = q; r0 < cend; r0 += bm)
                                 emit(r0, min(cend, r0 + bm), run_begin, run_len, static_cast<int>(c));
                             q = cend;
