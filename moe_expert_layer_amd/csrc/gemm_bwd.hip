@@ -688,13 +688,16 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_dma(WgradArgs g)
 // ------------------------------------------------------------------------------------------------
 // dgrads with LDS DMA (256 x 256 tiles over the 256-row tile table; N a multiple of 256, K of 128).
 //
-// Both operands are K-contiguous rows (activation rows of the tile, weight rows of the expert), so
-// each K step of 32 moves [256 rows][32 k] of each into a four-stage ring: 64-byte rows, 16-byte
-// chunk c of row r at position c ^ ((r >> 2) & 3), so the 16 rows one fragment read serves per
-// chunk cover all 16 bank groups; fragments are single ds_read_b128.  Copy schedule, waits, task
-// claiming and the overlap of the next task's first copies with the epilogue are those of the
-// weight-gradient kernel above.  Rows past a partial tile's end re-read its last row and are never
-// stored.  The gate/up dgrad's weight source switches from Wg[e] to Wu[e] at k = F.
+// Both operands are K-contiguous rows (activation rows of the tile, weight rows of the expert).
+// They move in pairs of K steps: two pair stages per operand of [256 rows][64 k], rows of 128 bytes
+// (whole cache lines; with one K step per stage every line was fetched in two halves), 16-byte chunk
+// c of row r at position c ^ ((r >> 1) & 7), so the 16 rows one fragment read serves per chunk
+// cover all 16 bank groups; fragments are single ds_read_b128.  Pair p (steps 2p, 2p + 1) goes out
+// in two halves: the first after the barrier of step 2p - 3 (which frees the stage of pair p - 2),
+// the second before the barrier of step 2p - 2; the barrier of step 2p - 1 waits for it whole.
+// Task claiming and the overlap of the next task's first copies with the epilogue are those of
+// the weight-gradient kernel above.  Rows past a partial tile's end re-read its last row and are
+// never stored.  The gate/up dgrad's weight source switches from Wg[e] to Wu[e] at k = F.
 namespace nt {
 
 constexpr int kWM = 4, kWN = 2, kTM = 2, kTN = 4;
@@ -702,14 +705,14 @@ constexpr int kWaves = kWM * kWN;
 constexpr int kThreads = kWaves * 64;
 constexpr int BM = kWM * kTM * 32;                 // 256 rows (the tile table's height)
 constexpr int BN = kWN * kTN * 32;                 // 256 output columns
-constexpr int BK = 32;
-constexpr int kStages = 4;
-constexpr int kRowBytes = BK * 2;                  // 64
-constexpr int kStageBytes = BM * kRowBytes;        // 16 KiB per operand
-constexpr int kBRing = kStages * kStageBytes;      // A stages in the first 64 KiB, B in the next
+constexpr int BK = 32;                             // one K step (two MFMA sub-steps)
+constexpr int kStages = 4;                         // K steps per unrolled loop body: two pairs
+constexpr int kRowBytes = 2 * BK * 2;              // 128: a pair stage row holds two K steps
+constexpr int kPairBytes = BM * kRowBytes;         // 32 KiB per operand
+constexpr int kBRing = 2 * kPairBytes;             // A pair stages in the first 64 KiB, B in the next
 constexpr int kSmemBytes = 2 * kBRing + 256;
-constexpr int kCopies = kStageBytes / 1024 / kWaves;   // 2: rows 16 (2 wave + j) .. + 15
-constexpr int kStepCopies = 2 * kCopies;
+constexpr int kCopies = kPairBytes / 1024 / kWaves;   // 4 per operand and pair: rows 8 (4 wave + j) .. + 7
+constexpr int kHalfCopies = kCopies;               // a half pair: two copies of A, then two of B
 static_assert(BM == BN, "one stage layout serves both operands");
 
 using tn::step_barrier;
@@ -720,46 +723,51 @@ struct Frags {
 };
 
 struct Copy {
-    const uint16_t* a;       // A at the next step's first k (row offsets in a_voff)
-    const uint16_t* b;       // the expert's weights at the next step's first k
+    const uint16_t* a;       // A at the first k of the pair being copied (row offsets in a_voff)
+    const uint16_t* b;       // the expert's weights at the same k
     const uint16_t* b1;      // segment 1's weights at k = kseg
-    int step, kseg_steps;    // next step to copy; the step at which the weights switch to b1
-    uint32_t a_lds, b_lds;
+    int pair, kseg_pairs;    // the pair being copied; the pair at which the weights switch to b1
+    uint32_t a_lds, b_lds;   // this wave's first copy in pair stage 0
 };
 
 struct Lane {
     uint32_t a_voff[kCopies], b_voff[kCopies];
-    uint32_t a_base[2], b_base[2];     // fragment-read addresses in stage 0 for sub-steps 0, 1
+    uint32_t a_base[2][2], b_base[2][2];   // fragment reads in pair stage 0: [pair half][sub-step]
 };
 
-template <int C>
-__device__ __forceinline__ void copy_one(const Copy& cp, const Lane& ln, int SB)
+// Copy C (0 .. 3) of half H of a pair into pair stage QA: C = 0, 1 move A copies 2H + C, C = 2, 3
+// weight copies 2H + C - 2.
+template <int H, int C>
+__device__ __forceinline__ void copy_one(const Copy& cp, const Lane& ln, int QA)
 {
-    constexpr int j = C % kCopies;
-    if constexpr (C < kCopies)
-        lds_copy16(cp.a, ln.a_voff[j], cp.a_lds + SB * kStageBytes + j * 1024);
+    constexpr int j = 2 * H + C % 2;
+    if constexpr (C < 2)
+        lds_copy16(cp.a, ln.a_voff[j], cp.a_lds + QA * kPairBytes + j * 1024);
     else
-        lds_copy16(cp.b, ln.b_voff[j], cp.b_lds + SB * kStageBytes + j * 1024);
+        lds_copy16(cp.b, ln.b_voff[j], cp.b_lds + QA * kPairBytes + j * 1024);
 }
 
+// After a pair's second half: the sources move on to the next pair.
 __device__ __forceinline__ void advance(Copy& cp)
 {
-    cp.a += BK;
-    ++cp.step;
-    cp.b = cp.step == cp.kseg_steps ? cp.b1 : cp.b + BK;
+    cp.a += 2 * BK;
+    ++cp.pair;
+    cp.b = cp.pair == cp.kseg_pairs ? cp.b1 : cp.b + 2 * BK;
 }
 
-// Read Q of sub-step KS of stage S: A block 0, weight blocks 0 .. kTN - 1, then A blocks 1 ...
+// Read Q of sub-step KS of step position S (pair stage S / 2, pair half S % 2): A block 0, weight
+// blocks 0 .. kTN - 1, then A blocks 1 ...
 template <int S, int KS, int Q>
 __device__ __forceinline__ void read_one(Frags& f, const Lane& ln)
 {
     using LdsV = const __attribute__((address_space(3))) bf16x8_t;
+    constexpr int q = S / 2, h = S % 2;
     if constexpr (Q >= 1 && Q <= kTN) {
         constexpr int j = Q - 1;
-        f.b[j] = *reinterpret_cast<LdsV*>(ln.b_base[KS] + S * kStageBytes + j * 32 * kRowBytes);
+        f.b[j] = *reinterpret_cast<LdsV*>(ln.b_base[h][KS] + q * kPairBytes + j * 32 * kRowBytes);
     } else {
         constexpr int i = Q == 0 ? 0 : Q - kTN;
-        f.a[i] = *reinterpret_cast<LdsV*>(ln.a_base[KS] + S * kStageBytes + i * kWM * 32 * kRowBytes);
+        f.a[i] = *reinterpret_cast<LdsV*>(ln.a_base[h][KS] + q * kPairBytes + i * kWM * 32 * kRowBytes);
     }
 }
 
@@ -775,20 +783,21 @@ __device__ __forceinline__ void reads(Frags& f, const Lane& ln)
     reads_impl<S, KS, Q0>(std::make_integer_sequence<int, Q1 - Q0>{}, f, ln);
 }
 
-template <int C0, int... Is>
+template <int H, int C0, int... Is>
 __device__ __forceinline__ void copies_impl(std::integer_sequence<int, Is...>, const Copy& cp,
-                                            const Lane& ln, int SB)
+                                            const Lane& ln, int QA)
 {
-    (copy_one<C0 + Is>(cp, ln, SB), ...);
+    (copy_one<H, C0 + Is>(cp, ln, QA), ...);
 }
 
-template <int C0, int C1>
-__device__ __forceinline__ void copies(const Copy& cp, const Lane& ln, int SB)
+// Copies C0 .. C1 - 1 of half H into pair stage QA.
+template <int H, int C0, int C1>
+__device__ __forceinline__ void copies(const Copy& cp, const Lane& ln, int QA)
 {
-    copies_impl<C0>(std::make_integer_sequence<int, C1 - C0>{}, cp, ln, SB);
+    copies_impl<H, C0>(std::make_integer_sequence<int, C1 - C0>{}, cp, ln, QA);
 }
 
-template <int NC, int SB, int SR, int KS, int M>
+template <int NC, int H, int QA, int SR, int KS, int M>
 __device__ __forceinline__ void slot(f32x16_t (&acc)[kTM][kTN], const Frags& use, Frags& load,
                                      const Copy& cp, const Lane& ln)
 {
@@ -798,50 +807,62 @@ __device__ __forceinline__ void slot(f32x16_t (&acc)[kTM][kTN], const Frags& use
     constexpr int RF = NM / 2;                                      // slots that carry the reads
     if constexpr (M < RF)
         reads<SR, KS, M * NR / RF, (M + 1) * NR / RF>(load, ln);
-    copies<M * NC / NM, (M + 1) * NC / NM>(cp, ln, SB);
+    copies<H, M * NC / NM, (M + 1) * NC / NM>(cp, ln, QA);
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int NC, int SB, int SR, int KS, int... Ms>
+template <int NC, int H, int QA, int SR, int KS, int... Ms>
 __device__ __forceinline__ void slots(std::integer_sequence<int, Ms...>, f32x16_t (&acc)[kTM][kTN],
                                       const Frags& use, Frags& load, const Copy& cp, const Lane& ln)
 {
-    (slot<NC, SB, SR, KS, Ms>(acc, use, load, cp, ln), ...);
+    (slot<NC, H, QA, SR, KS, Ms>(acc, use, load, cp, ln), ...);
 }
 
-template <int S, bool kCopy, int W>
+// K step t at position S = t % 4: sub-step 1 of step t on f0 (reading step t's second sub-step into
+// f1), with the second half of pair t / 2 + 1 when S is even and kPre; the barrier (at most W copies
+// in flight; none when W < 0); sub-step 0 of step t + 1 on f1 (reading step t + 1's first sub-step
+// into f0), with the first half of pair (t + 3) / 2 when S is odd and kPost.
+template <int S, bool kPre, bool kPost, int W>
 __device__ __forceinline__ void k_step(f32x16_t (&acc)[kTM][kTN], Frags& f0, Frags& f1, Copy& cp,
                                        const Lane& ln)
 {
+    static_assert(!(kPre && S % 2 == 1) && !(kPost && S % 2 == 0), "copy points");
     __builtin_amdgcn_sched_barrier(0);
-    slots<0, 0, S, 1>(std::make_integer_sequence<int, kTM * kTN>{}, acc, f0, f1, cp, ln);
+    slots<kPre ? kHalfCopies : 0, 1, (S / 2 + 1) % 2, S, 1>(std::make_integer_sequence<int, kTM * kTN>{},
+                                                            acc, f0, f1, cp, ln);
+    if constexpr (kPre)
+        advance(cp);
     if constexpr (W >= 0)
         step_barrier<W>();
     __builtin_amdgcn_sched_barrier(0);
-    slots<kCopy ? kStepCopies : 0, S, (S + 1) % kStages, 0>(std::make_integer_sequence<int, kTM * kTN>{},
-                                                             acc, f1, f0, cp, ln);
+    slots<kPost ? kHalfCopies : 0, 0, ((S + 3) / 2) % 2, (S + 1) % kStages, 0>(
+        std::make_integer_sequence<int, kTM * kTN>{}, acc, f1, f0, cp, ln);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kCopy)
-        advance(cp);
 }
 
-constexpr int kTopWait = 3 * kStepCopies;
+// Copies a task's setup leaves in flight once pair 0 has landed: the first half of pair 1.
+constexpr int kTopWait = kHalfCopies;
 
+// The K loop of one task.  KT is a multiple of 4; the caller issued pair 0 and the first half of
+// pair 1, cp points at pair 1, and the caller has waited for pair 0 (step_barrier<kTopWait>).  At
+// an even step's barrier the halves of the next pair may be in flight (the step after it lies in
+// the current pair); at an odd step's barrier the next pair must have landed.
 __device__ __forceinline__ void k_loop(f32x16_t (&acc)[kTM][kTN], Copy cp, const Lane& ln, int KT)
 {
-    constexpr int W = 2 * kStepCopies;
+    constexpr int WE = 2 * kHalfCopies;
     Frags f0, f1;
     reads<0, 0, 0, kTM + kTN>(f0, ln);
     for (int kt = 0; kt < KT - kStages; kt += kStages) {
-        k_step<0, true, W>(acc, f0, f1, cp, ln);
-        k_step<1, true, W>(acc, f0, f1, cp, ln);
-        k_step<2, true, W>(acc, f0, f1, cp, ln);
-        k_step<3, true, W>(acc, f0, f1, cp, ln);
+        k_step<0, true, false, WE>(acc, f0, f1, cp, ln);
+        k_step<1, false, true, 0>(acc, f0, f1, cp, ln);
+        k_step<2, true, false, WE>(acc, f0, f1, cp, ln);
+        k_step<3, false, true, 0>(acc, f0, f1, cp, ln);
     }
-    k_step<0, false, W>(acc, f0, f1, cp, ln);
-    k_step<1, false, kStepCopies>(acc, f0, f1, cp, ln);
-    k_step<2, false, 0>(acc, f0, f1, cp, ln);
-    k_step<3, false, -1>(acc, f0, f1, cp, ln);
+    // the last four steps: only the second half of the last pair is still to be copied
+    k_step<0, true, false, WE>(acc, f0, f1, cp, ln);
+    k_step<1, false, false, 0>(acc, f0, f1, cp, ln);
+    k_step<2, false, false, 0>(acc, f0, f1, cp, ln);
+    k_step<3, false, false, -1>(acc, f0, f1, cp, ln);
 }
 
 // kParts (gate/up only): 1, one pass over k < 2F storing bf16 rows; 2, tasks [0, T0) take dg Wg^T
@@ -867,27 +888,31 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_dma(BwdArgs g, int32_t* __r
     Lane ln;
     {
         const int r = lane & 31;
-        const int swz = (r >> 2) & 3;
+        const int swz = (r >> 1) & 7;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int pos = (2 * ks + (lane >> 5)) ^ swz;
-            ln.a_base[ks] = lds0 + (32 * wm + r) * kRowBytes + 16 * pos;
-            ln.b_base[ks] = lds0 + kBRing + (32 * kTN * wn + r) * kRowBytes + 16 * pos;
-            asm volatile("" : "+v"(ln.a_base[ks]));
-            asm volatile("" : "+v"(ln.b_base[ks]));
-        }
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int pos = (4 * h + 2 * ks + (lane >> 5)) ^ swz;
+                ln.a_base[h][ks] = lds0 + (32 * wm + r) * kRowBytes + 16 * pos;
+                ln.b_base[h][ks] = lds0 + kBRing + (32 * kTN * wn + r) * kRowBytes + 16 * pos;
+                asm volatile("" : "+v"(ln.a_base[h][ks]));
+                asm volatile("" : "+v"(ln.b_base[h][ks]));
+            }
     }
+    // copy j of this wave moves stage rows 8 (kCopies wave + j) .. + 7, eight lanes per row; the
+    // lane at position p of its row fetches logical chunk p ^ ((row >> 1) & 7)
     uint32_t c16[kCopies];
     int crow[kCopies];
 #pragma unroll
     for (int j = 0; j < kCopies; ++j) {
-        crow[j] = 16 * (kCopies * wave + j) + lane / 4;
-        c16[j] = 16u * static_cast<uint32_t>((lane & 3) ^ ((crow[j] >> 2) & 3));
+        crow[j] = 8 * (kCopies * wave + j) + lane / 8;
+        c16[j] = 16u * static_cast<uint32_t>((lane & 7) ^ ((crow[j] >> 1) & 7));
     }
     Copy cp;
     cp.a_lds = lds0 + kCopies * wave * 1024;
     cp.b_lds = lds0 + kBRing + kCopies * wave * 1024;
-    cp.kseg_steps = kParts == 2 ? KT : g.kseg / BK;      // parts: one weight matrix per task
+    cp.kseg_pairs = kParts == 2 ? KT / 2 : g.kseg / (2 * BK);   // parts: one weight matrix per task
 
     const int xcd = blockIdx.x % kXcdCount;
     const int blk = gridDim.x / kXcdCount;
@@ -909,12 +934,12 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_dma(BwdArgs g, int32_t* __r
         cp.a = g.a + part * g.kseg;
         cp.b = (part ? g.b1 : g.b0) + eoff;
         cp.b1 = g.b1 + eoff;
-        cp.step = 0;
-#pragma unroll
-        for (int S = 0; S < kStages; ++S) {
-            copies<0, kStepCopies>(cp, ln, S);
-            advance(cp);
-        }
+        cp.pair = 0;
+        // pair 0 whole, then the first half of pair 1 (k_loop's order)
+        copies<0, 0, kHalfCopies>(cp, ln, 0);
+        copies<1, 0, kHalfCopies>(cp, ln, 0);
+        advance(cp);
+        copies<0, 0, kHalfCopies>(cp, ln, 1);
     };
 
     int t = claim_task(claimed, task_ctr, xcd, blk, wave, lane);
