@@ -132,9 +132,12 @@ def cpu_baseline(inp, budget_s: float):
         if dt >= budget_s / 2 or n >= inp.T:
             break
         n = min(inp.T, max(2 * n, int(n * budget_s / 2 / max(dt, 1e-3))))
+    # the expert arithmetic those tokens carry: gate, up and down, 2 H F each, for each of k slots
+    gflops = n * inp.k * 6.0 * inp.H * inp.F / dt / 1e9
     return {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "gflops": gflops,
             "sample": f"{n} of {inp.T} tokens through the per-token definition (all k experts of each, "
-                      f"weights decoded per call), {dt:.1f} s, fp64"}
+                      f"weights decoded per call), {dt:.1f} s, fp64; gflops counts 6 H F per slot"}
 
 
 def cpu_baseline_grouped(g, budget_s: float):
@@ -151,9 +154,11 @@ def cpu_baseline_grouped(g, budget_s: float):
         if dt >= budget_s / 2 or n >= M:
             break
         n = min(M, max(2 * n, int(n * budget_s / 2 / max(dt, 1e-3))))
+    gflops = n * 6.0 * g.H * g.F / dt / 1e9                  # gate, up and down per row
     return {"value": n / dt, "unit": "rows/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "gflops": gflops,
             "sample": f"{n} of {M} received rows through their experts (weights decoded per call), "
-                      f"{dt:.1f} s, fp64"}
+                      f"{dt:.1f} s, fp64; gflops counts 6 H F per row"}
 
 
 def graph_rate(torch, launches, sets, flush, repeats=3):

@@ -28,9 +28,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f)
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Two floats to bfloat16 (rounded as f32_to_bf16), lo in the low half: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
 }
 
 // SwiGLU ("NPU Training Operators - MC2", 执行路径 step 8): silu(g) * u with silu(z) = z / (1 + e^-z).
