@@ -63,7 +63,7 @@ struct RouteLayout {
 struct FfnLayout {
     size_t status = 0;
     size_t tiles1 = 0, tiles2 = 0;     // MTile tables for fc1 / fc2 row-tile heights
-    size_t tiles_run = 0;              // unchunked large tiles: fc1's table, partial tails inside their runs
+    size_t tiles_run = 0;              // unchunked large tiles: fc1's table, each group one run of balanced tiles
     size_t tile_count = 0;             // int32 [8]: [0] tiles in the table, [2] tiles before its short tails;
                                        // [4], [6] the same for tiles_run
     size_t task_ctr = 0;               // int32 [2][kXcdCount]: per-XCD task counters of fc1 / fc2
@@ -114,9 +114,10 @@ hipError_t launch_route_scatter(const int32_t* ids, int64_t M, int64_t E,
 // null also the expected (row tile x column tile) tasks per chunk (row tiles * col_tiles) and
 // zeroes chunk_done; zeroes the 2 * kXcdCount task counters at task_ctr.  A non-empty group with an expert outside [0, E) is skipped and sets
 // *status; with write_status the status word is written either way.  tiles_in_run (may be null;
-// unchunked tables only): also the same tiles with every group's partial tail inside that group's run
-// (each run: the group's tiles in row order), their number in count_in_run[0] and [2] (laid out as
-// tile_count, so either table can be handed to a GEMM with its counts).
+// unchunked tables only): also a table in which each group is one run of R = ceil(rows / bm) tiles
+// of near-equal height in row order (their 32-row blocks differ by at most one; the last tile ends
+// the group), its number in count_in_run[0] and [2] (laid out as tile_count, so either table can be
+// handed to a GEMM with its counts).
 hipError_t launch_build_tiles(const int32_t* offsets, const int32_t* group_expert, int64_t G,
                               int64_t E, int64_t M, int64_t chunk, int bm, MTile* tiles, int64_t max_tiles,
                               int32_t* tile_count, int32_t* chunk_tiles, int32_t* chunk_done,
