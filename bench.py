@@ -63,14 +63,23 @@ def byte_model(inp, M):
     return {"permute": (1 + k) * T * H * b + 4 * M, "unpermute": (k * T * H * b + T * H * b + 8 * M)}
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and blank lines (a comment edit does not change a kernel)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", line).rstrip() for line in text.splitlines())
+    return "\n".join(line for line in lines if line.strip())
+
+
 def kernel_source_digest(files) -> str:
-    """sha256 over the named kernel sources, the shared headers and the tile-table builder (task
-    order changes the traffic), to tie counter figures to code."""
+    """sha256 over the code (comments and blank lines dropped) of the named kernel sources, the
+    shared headers and the tile-table builder (task order changes the traffic), to tie counter
+    figures to code."""
     import hashlib
     h = hashlib.sha256()
     for f in list(files) + ["common.h", "internal.h", "gemm_common.h", "route.hip"]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
