@@ -196,7 +196,8 @@ __global__ __launch_bounds__(kThreads) void route_scatter_kernel(
 // `chunk` rows) and each piece into tiles of at most bm rows; a run is the tiles of one piece.
 // Chunked (num_chunks > 1): tiles in row order (chunk-major); a run spans a group's tiles within a
 // window of kChunkWindow chunks, so the tasks sharing a weight strip stay together across the
-// window's chunks, and chunks complete in order window by window.  Unchunked: first every group's
+// window's chunks, and chunks complete in order window by window; each group's piece inside one
+// chunk is cut into balanced tiles (as below).  Unchunked: first every group's
 // full tiles (row order), then the partial tail tiles, each its own run, so that the short tasks
 // come last and even out the workgroups' finishing times.  The second table (tiles_in_run,
 // unchunked calls only) keeps each group as one run of R = ceil(rows / bm) tiles of near-equal
@@ -326,9 +327,10 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
                         for (int64_t q = r; q < wend;) {
                             const int64_t c = q / chunk;
                             const int64_t cend = min(wend, (c + 1) * chunk);
-                            if (layout == 1 && bm % 32 == 0) {
-                                // balanced: the piece's 32-row blocks spread over its R tiles as evenly
-                                // as possible (at most one block apart; the last tile ends the piece)
+                            if ((layout == 1 || num_chunks > 1) && bm % 32 == 0) {
+                                // balanced (the in-run table, and the chunked table's pieces): the
+                                // piece's 32-row blocks spread over its R tiles as evenly as possible
+                                // (at most one block apart; the last tile ends the piece)
                                 const int len = static_cast<int>(cend - q);
                                 const int nblk = (len + 31) / 32, R = (len + bm - 1) / bm;
                                 int64_t r0 = q;
