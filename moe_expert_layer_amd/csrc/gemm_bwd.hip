@@ -1112,12 +1112,13 @@ __global__ __launch_bounds__(kSmallThreads) void sum_slot_rows_kernel(
             const int64_t p = pos[static_cast<int64_t>(t) * k + j];
             if (p < 0 || p >= M)
                 continue;
-            const float4 a = static_cast<const float4*>(rows)[p * row_vecs + c];
-            const float4 b = static_cast<const float4*>(rows)[(M + p) * row_vecs + c];
-            acc[0] += a.x + b.x;
-            acc[1] += a.y + b.y;
-            acc[2] += a.z + b.z;
-            acc[3] += a.w + b.w;
+            // each part row is read once: non-temporal loads
+            const f32x4_t a = __builtin_nontemporal_load(static_cast<const f32x4_t*>(rows) + p * row_vecs + c);
+            const f32x4_t b = __builtin_nontemporal_load(static_cast<const f32x4_t*>(rows) + (M + p) * row_vecs + c);
+            acc[0] += a[0] + b[0];
+            acc[1] += a[1] + b[1];
+            acc[2] += a[2] + b[2];
+            acc[3] += a[3] + b[3];
         }
     }
     for (int j0 = 0; kParts == 0 && j0 < k; j0 += 8) {
@@ -1128,8 +1129,9 @@ __global__ __launch_bounds__(kSmallThreads) void sum_slot_rows_kernel(
             const bool ok = p >= 0 && p < M;
             const int64_t at = (ok ? p : 0) * row_vecs + c;
             if constexpr (kParts == 0) {
-                const uint4 b = ok ? static_cast<const uint4*>(rows)[at] : make_uint4(0, 0, 0, 0);
-                const uint32_t d[4] = {b.x, b.y, b.z, b.w};
+                const u32x4_t b = ok ? __builtin_nontemporal_load(static_cast<const u32x4_t*>(rows) + at)
+                                     : u32x4_t{0u, 0u, 0u, 0u};
+                const uint32_t d[4] = {b[0], b[1], b[2], b[3]};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     v[j][2 * e] = __uint_as_float(d[e] << 16);
