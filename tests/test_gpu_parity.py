@@ -336,6 +336,30 @@ def test_grouped_ffn_short_groups_large_tiles(sizes):
     assert torch.equal(y, mel.grouped_ffn(*args, head_m_size=256))
 
 
+@pytest.mark.parametrize("sizes", [[1, 31, 32, 33, 255, 256, 257, 0, 511, 512, 513, 1025],
+                                   [767, 768, 769, 1023, 1024, 1026, 2, 0, 480, 544, 96, 160]],
+                         ids=["tile_edges", "block_edges"])
+def test_grouped_ffn_balanced_tile_edges(sizes):
+    """Groups whose row counts sit at the edges of 32-row blocks and 256-row tiles, at large-tile
+    sizes.  Unchunked, fc1 cuts every group into ceil(rows / 256) tiles of near-equal height (a
+    group of 1025 rows: five tiles of 7, 7, 7, 6 and 6 blocks); fc2 does the same for the first set
+    (groups averaging at most two tiles) and runs full tiles first with short tails split in two for
+    the second.  Chunked tables cut each group's piece of a chunk the same way.  Every row matches
+    the oracle, and the chunked results (512 and 256 rows) are bitwise the unchunked ones."""
+    g = synth.make_grouped(rows=sum(sizes), H=256, F=256, E_local=3, sources=4, seed=7)
+    g = dataclasses.replace(g, group_offsets=np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32),
+                            recv_counts=np.asarray(sizes, np.int64).reshape(4, 3))
+    ref = oracle.grouped_ffn(g)
+    args = (dv.tensor(g.rows), dv.tensor(g.group_offsets), dv.tensor(g.group_expert),
+            dv.tensor(g.w_gate), dv.tensor(g.w_up), dv.tensor(g.w_down))
+    y = mel.grouped_ffn(*args)
+    err, row_err = oracle.inf_norm_rel(dv.host(y), ref), oracle.row_inf_norm_rel(dv.host(y), ref)
+    print(f"tile edges: inf-norm rel err {err:.3e}, worst row {row_err:.3e}")
+    assert err <= TOL["bf16"] and row_err <= TOL["bf16"]
+    for head in (512, 256):
+        assert torch.equal(y, mel.grouped_ffn(*args, head_m_size=head))
+
+
 def test_grouped_ffn_bad_group_expert_flagged():
     g = synth.make_grouped(rows=300, H=128, F=64, E_local=2, sources=8, seed=3)
     ge = g.group_expert.copy()
