@@ -28,9 +28,9 @@
 //   - inside a k sub-step every MFMA is followed by its share of the next sub-step's fragment reads
 //     and of the copies, and the barrier that opens K step kt + 1 sits between the two sub-steps of
 //     step kt, so neither barrier nor LDS latency idles the matrix cores;
-//   - the workgroup claims its next task while working on the current one and issues that task's
-//     first copies before the current epilogue, which writes through a per-wave LDS staging area
-//     as 16-byte stores.
+//   - the workgroup claims its tasks two ahead (the atomic's round trip overlaps a K loop) and
+//     issues the next task's first copies before the current epilogue, which writes through a
+//     per-wave LDS staging area as 16-byte stores.
 // Small tiles (128 x 128, two workgroups per CU, other sizes): register-staged copies, the weights
 // transposed in registers with v_perm_b32 and stored K-contiguous, two LDS stages.
 #include <atomic>
@@ -671,8 +671,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
     using L = BLayout<kGated>;
     constexpr int BN = kGated ? BNB / 2 : BNB;
     // dynamic LDS: the kStages-stage ring, then each wave's epilogue staging area.  The claimed-task
-    // word sits at the start of wave 0's area: it is written by wave 0 only, read by every wave
-    // before any epilogue starts, and wave 0 overwrites it only after its own epilogue.
+    // word sits at the start of wave 0's area: wave 0 writes it after its epilogue, every wave reads
+    // it after the next task's first barrier, and wave 0's next epilogue (which overwrites it) starts
+    // only after the barrier that ends that task's K loop.
     extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
     int* const claimed = reinterpret_cast<int*>(smem + kRingBytes);
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
@@ -818,17 +819,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
             copies<kBA1, 0, 1, kBCopies, kBCopies + kAHalf>(cp, a_voff, b_voff);
     };
 
+    // Claims (claim_issue: the atomic's round trip overlaps a K loop).  Launches that gather fc1 rows
+    // need the next task during the current K loop (its rows are fetched there), so they claim two
+    // ahead: t's successor is in the claim word at every top barrier, and the atomic issued there
+    // claims the task after it.  The others claim one ahead, late: the atomic issued at the top
+    // barrier claims t's successor and is read after the K loop, so the short tasks at a table's
+    // end still go to the workgroups that free up first.
+    const bool ahead2 = gather != nullptr;
     int t = claim_task(claimed, task_ctr, xcd, blk, wave, lane);
+    if (ahead2)
+        claim_task(claimed, task_ctr, xcd, blk, wave, lane);  // t's successor, left in the claim word
     if (t < total) {
         fetch_rows(t);
         setup(t);
     }
     while (t < total) {
-        // claim the following task now; the other waves read the claim after this task's barriers
-        if (wave == 0) {
-            const int v = atomicAdd(&task_ctr[xcd], lane == 0 ? 1 : 0);
-            *claimed = __builtin_amdgcn_readfirstlane(v);
-        }
         const int rows = tile.row_end - tile.row_begin;
         // a half-width task leaves the second column half (wave column 1) without work
         const bool half_task = __builtin_amdgcn_readfirstlane(half ? 1 : 0) != 0;
@@ -848,14 +853,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
                 for (int r = 0; r < 16; ++r)
                     acc[i][j][r] = 0.0f;
 
-        // step 0 has landed; past this barrier every wave sees the claim of the following task,
-        // whose gathered source rows are loaded now and used after this task's K loop
+        // step 0 has landed; past this barrier every wave sees the claim of the following task
+        // (two ahead), whose gathered source rows are loaded now and used after this task's K loop
         if (a_on)
             step_barrier<top_wait<true>()>();
         else
             step_barrier<top_wait<false>()>();
-        const int i = __builtin_amdgcn_readfirstlane(*claimed);
-        const int t_next = ((i / blk) * kXcdCount + xcd) * blk + i % blk;
+        int t_next = total;
+        if (ahead2) {
+            const int i = __builtin_amdgcn_readfirstlane(*claimed);
+            t_next = ((i / blk) * kXcdCount + xcd) * blk + i % blk;
+        }
+        const int claim_ret = claim_issue(task_ctr, xcd, wave, lane);
         if (t_next < total)
             fetch_rows(t_next);
         const LoopArgs g{a_base, b_base, a_voff, b_voff};
@@ -886,6 +895,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
             else
                 k_loop<kGated, kTM, true, false>(acc, cp, g, N_w, KT);
         }
+        const int claim_after = claim_value(claim_ret, wave);
+        if (!ahead2) {
+            // one ahead: the claim word (in wave 0's staging area, idle between its epilogues)
+            // carries t's successor across one barrier
+            if (wave == 0)
+                *claimed = claim_after;
+            __syncthreads();
+            const int i = __builtin_amdgcn_readfirstlane(*claimed);
+            t_next = ((i / blk) * kXcdCount + xcd) * blk + i % blk;
+        }
         const MTile done = tile;
         const int done_n0 = n0;
         const bool done_skip = half_task && wn == 1;          // columns of the other half task
@@ -909,6 +928,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
         }
         if (chunk_done != nullptr)
             count_done_through(chunk_done, done.chunk, wave, lane);
+        // two ahead: publish the claim after wave 0's last read of its staging area (which holds
+        // the word)
+        if (ahead2 && wave == 0)
+            *claimed = claim_after;
     }
 }
 }  // namespace big

@@ -641,14 +641,12 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_dma(WgradArgs g)
         }
     };
 
+    // tasks claimed two ahead (claim_issue): t's successor is in the claim word at every top barrier
     int t = claim_task(claimed, g.task_ctr, xcd, blk, wave, lane);
+    claim_task(claimed, g.task_ctr, xcd, blk, wave, lane);
     if (t < total)
         setup(t);
     while (t < total) {
-        if (wave == 0) {
-            const int v = atomicAdd(&g.task_ctr[xcd], lane == 0 ? 1 : 0);
-            *claimed = __builtin_amdgcn_readfirstlane(v);
-        }
         f32x16_t acc[kTM][kTN];
 #pragma unroll
         for (int i = 0; i < kTM; ++i)
@@ -660,7 +658,9 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_dma(WgradArgs g)
         step_barrier<kTopWait>();
         const int ci = __builtin_amdgcn_readfirstlane(*claimed);
         const int t_next = ((ci / blk) * kXcdCount + xcd) * blk + ci % blk;
+        const int claim_ret = claim_issue(g.task_ctr, xcd, wave, lane);    // the task after t_next
         k_loop(acc, cp, ln, KT, g.lda, g.ldb);
+        const int claim_after = claim_value(claim_ret, wave);
         const int de = e, dm0 = m0, dn0 = n0;
         t = t_next;
         // every wave is past its last read of this task's stages (and of the claim word)
@@ -680,6 +680,8 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_dma(WgradArgs g)
                     crow[32 * j] = acc[i][j][r];
             }
         }
+        if (wave == 0)
+            *claimed = claim_after;
     }
 }
 
@@ -942,14 +944,12 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_dma(BwdArgs g, int32_t* __r
         copies<0, 0, kHalfCopies>(cp, ln, 1);
     };
 
+    // tasks claimed two ahead (claim_issue): t's successor is in the claim word at every top barrier
     int t = claim_task(claimed, task_ctr, xcd, blk, wave, lane);
+    claim_task(claimed, task_ctr, xcd, blk, wave, lane);
     if (t < total)
         setup(t);
     while (t < total) {
-        if (wave == 0) {
-            const int v = atomicAdd(&task_ctr[xcd], lane == 0 ? 1 : 0);
-            *claimed = __builtin_amdgcn_readfirstlane(v);
-        }
         f32x16_t acc[kTM][kTN];
 #pragma unroll
         for (int i = 0; i < kTM; ++i)
@@ -961,7 +961,9 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_dma(BwdArgs g, int32_t* __r
         step_barrier<kTopWait>();
         const int ci = __builtin_amdgcn_readfirstlane(*claimed);
         const int t_next = ((ci / blk) * kXcdCount + xcd) * blk + ci % blk;
+        const int claim_ret = claim_issue(task_ctr, xcd, wave, lane);    // the task after t_next
         k_loop(acc, cp, ln, KT);
+        const int claim_after = claim_value(claim_ret, wave);
         const MTile done = tile;
         const int dn0 = n0, dpart = part;
         t = t_next;
@@ -1055,6 +1057,8 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_dma(BwdArgs g, int32_t* __r
                 }
             }
         }
+        if (wave == 0)
+            *claimed = claim_after;
     }
 }
 

@@ -35,6 +35,34 @@ __device__ __forceinline__ int claim_task(int* claimed, int32_t* task_ctr, int x
     return ((i / blk) * kXcdCount + xcd) * blk + i % blk;
 }
 
+// Claims two tasks ahead in the persistent kernels: while task t runs, wave 0 claims the task after
+// t's successor.  claim_issue issues the atomic on lane 0 of wave 0, its address hidden from the
+// compiler so that it stays a single-lane operation whose result is waited for only where it is
+// first used (a wave-wide form is rewritten into a scan that waits for the result at once);
+// claim_value reads that result, after the K loop, whose last barrier has waited for every load of
+// the wave.  Wave 0 then publishes the value in the claim word, and every wave reads it after the
+// next task's first barrier.
+__device__ __forceinline__ int claim_issue(int32_t* task_ctr, int xcd, int wave, int lane)
+{
+    int v = 0;
+    if (wave == 0 && lane == 0) {
+        int off = 0;
+        asm volatile("" : "+v"(off));
+        v = atomicAdd(task_ctr + xcd + off, 1);
+    }
+    return v;
+}
+
+__device__ __forceinline__ int claim_value(int v, int wave)
+{
+    int c = 0;
+    if (wave == 0) {
+        c = __builtin_amdgcn_readlane(v, 0);
+        asm volatile("" : "+s"(c));
+    }
+    return c;
+}
+
 // Task t belongs to the run holding row tile t / n_nt; inside the run, row tiles vary fastest.
 __device__ __forceinline__ MTile decode_task(int t, int n_nt, const MTile* __restrict__ tiles, int& nt)
 {

@@ -956,16 +956,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
             cp.a += 4 * BK;
     };
 
+    // claims as in the bf16 kernel: two ahead when gathering fc1 rows (t's successor is in the claim
+    // word at every top barrier), else one ahead, read after the K loop
+    const bool ahead2 = gather != nullptr;
     int t = claim_task(claimed, task_ctr, xcd, blk, wave, lane);
+    if (ahead2)
+        claim_task(claimed, task_ctr, xcd, blk, wave, lane);
     if (t < total) {
         fetch_rows(t);
         setup(t);
     }
     while (t < total) {
-        if (wave == 0) {
-            const int v = atomicAdd(&task_ctr[xcd], lane == 0 ? 1 : 0);
-            *claimed = __builtin_amdgcn_readfirstlane(v);
-        }
         const int rows = tile.row_end - tile.row_begin;
         const int nb = __builtin_amdgcn_readfirstlane(
             min(kTM, max(0, ((rows + 31) / 32 - wm + kWM - 1) / kWM)));
@@ -986,8 +987,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
             step_barrier<top_wait<true>()>();
         else
             step_barrier<top_wait<false>()>();
-        const int ci = __builtin_amdgcn_readfirstlane(*claimed);
-        const int t_next = ((ci / blk) * kXcdCount + xcd) * blk + ci % blk;
+        int t_next = total;
+        if (ahead2) {
+            const int ci = __builtin_amdgcn_readfirstlane(*claimed);
+            t_next = ((ci / blk) * kXcdCount + xcd) * blk + ci % blk;
+        }
+        const int claim_ret = claim_issue(task_ctr, xcd, wave, lane);
         if (t_next < total)
             fetch_rows(t_next);
         if (nb == 0)
@@ -998,6 +1003,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
             mx_k_loop<kGated, 1, true>(acc, la, cp, a_voff, b_voff, sc_voff, KT, N_w);
         else
             mx_k_loop<kGated, 2, true>(acc, la, cp, a_voff, b_voff, sc_voff, KT, N_w);
+        const int claim_after = claim_value(claim_ret, wave);
+        if (!ahead2) {
+            if (wave == 0)
+                *claimed = claim_after;
+            __syncthreads();
+            const int ci = __builtin_amdgcn_readfirstlane(*claimed);
+            t_next = ((ci / blk) * kXcdCount + xcd) * blk + ci % blk;
+        }
         const MTile done = tile;
         const int done_n0 = n0;
         t = t_next;
@@ -1011,6 +1024,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
             store_y(acc, Cy, done, done_n0, N_out, stg, wm, wn, lane, chunk_done != nullptr);
         if (chunk_done != nullptr)
             count_done_through(chunk_done, done.chunk, wave, lane);
+        // two ahead: publish the claim after wave 0's last read of its staging area (which holds
+        // the word)
+        if (ahead2 && wave == 0)
+            *claimed = claim_after;
     }
 }
 
