@@ -489,7 +489,10 @@ __device__ __forceinline__ void slot(f32x16_t (&acc)[kTM][kTN], const Frags& use
                                      const CopyCtx& cp, const LoopArgs& g)
 {
     constexpr int NM = NB * kTN, NR = 2 * kTN + NB, NC = set_size<CS>();
-    acc[M / kTN][M % kTN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(use.a[M / kTN], use.b[M % kTN],
+    // weights as the first operand: the accumulator block is the transposed 32 x 32 output block,
+    // so a lane holds one output row (lane % 32) and four runs of four adjacent columns, 8 (r / 4) +
+    // 4 (lane / 32) + r % 4 (the two operands' registers have the same layout)
+    acc[M / kTN][M % kTN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(use.b[M % kTN], use.a[M / kTN],
                                                                     acc[M / kTN][M % kTN], 0, 0, 0);
     constexpr int RF = NM / 2 > 0 ? NM / 2 : 1;                    // slots that carry the reads
     if constexpr (M < RF)
@@ -590,9 +593,10 @@ __device__ __forceinline__ void k_loop(f32x16_t (&acc)[kTM][kTN], CopyCtx cp, co
 }
 
 // Epilogue through LDS.  The wave's output (64 rows x 64 columns for fc1, 64 x 128 for fc2) goes
-// out in 32 x 64 pieces: the accumulators are written to the wave's staging area as bf16 (2-byte
-// LDS writes, rows of 128 bytes with 16-byte chunks XOR-swizzled by row), then read back as
-// 16-byte row chunks and stored to global memory 16 bytes per lane.  Only this wave touches its
+// out in 32 x 64 pieces: the accumulators (transposed blocks: a lane holds one row and runs of four
+// adjacent columns) are written to the wave's staging area as bf16, four columns per 8-byte LDS
+// write (rows of 128 bytes with 16-byte chunks XOR-swizzled by row), then read back as 16-byte row
+// chunks and stored to global memory 16 bytes per lane.  Only this wave touches its
 // area, and LDS operations of one wave complete in order, so no barrier is needed.
 // kVal (fc1): 0 the SwiGLU output h, 1 the gate values g, 2 the up values u (the last two saved for
 // the backward, same layout as h).
@@ -619,19 +623,24 @@ __device__ __forceinline__ void store_output_staged(const f32x16_t (&acc)[kTM][k
                 for (int jj = 0; jj < PC / 32; ++jj) {
                     const int ob = cp * (PC / 32) + jj;               // 32-column output block
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float v;
-                        if constexpr (kGated && kVal == 0)
-                            v = swiglu(acc[i][2 * ob][r], acc[i][2 * ob + 1][r]);   // gate, up blocks
-                        else if constexpr (kGated)
-                            v = acc[i][2 * ob + kVal - 1][r];
-                        else
-                            v = acc[i][ob][r];
-                        const int row = 32 * ii + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                        const int col = 32 * jj + (lane & 31);
+                    for (int q = 0; q < 4; ++q) {
+                        float v[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int r = 4 * q + e;
+                            if constexpr (kGated && kVal == 0)
+                                v[e] = swiglu(acc[i][2 * ob][r], acc[i][2 * ob + 1][r]);   // gate, up blocks
+                            else if constexpr (kGated)
+                                v[e] = acc[i][2 * ob + kVal - 1][r];
+                            else
+                                v[e] = acc[i][ob][r];
+                        }
+                        const int row = 32 * ii + (lane & 31);
+                        const int col = 32 * jj + 8 * q + 4 * (lane >> 5);          // 4 adjacent columns
                         const uint32_t a = stage + row * (2 * PC) +
                                            ((((col >> 3) ^ (row >> kSwz)) & (CPR - 1)) << 4) + 2 * (col & 7);
-                        *reinterpret_cast<__attribute__((address_space(3))) uint16_t*>(a) = f32_to_bf16(v);
+                        *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(a) =
+                            u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
                     }
                 }
             }
