@@ -784,8 +784,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
             gsrc[j] = gather[tl.row_begin + min(r, tl.row_end - tl.row_begin - 1)];   // used in setup
         }
     };
-    auto setup = [&](int t) {
-        tile = decode(t, n0, half);
+    // setup_from: the task whose tile, first column and width decode() gave
+    auto setup_from = [&](const MTile& tl, int col0, bool hf) {
+        tile = tl;
+        n0 = col0;
+        half = hf;
         // the weight chunks of the task's columns: chunk c of a 512-byte row holds columns 8c ..
         // 8c + 7, and copy lanes 0 .. 15 (32 .. 47) take chunks 0 .. 15 whatever the swizzle
         cp.b_on = !half || (lane & 16) == 0;
@@ -827,14 +830,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
         if (a_on)
             copies<kBA1, 0, 1, kBCopies, kBCopies + kAHalf>(cp, a_voff, b_voff);
     };
+    auto setup = [&](int t) {
+        int col0;
+        bool hf;
+        const MTile tl = decode(t, col0, hf);
+        setup_from(tl, col0, hf);
+    };
 
     // Claims (claim_issue: the atomic's round trip overlaps a K loop).  Launches that gather fc1 rows
-    // need the next task during the current K loop (its rows are fetched there), so they claim two
-    // ahead: t's successor is in the claim word at every top barrier, and the atomic issued there
-    // claims the task after it.  The others claim one ahead, late: the atomic issued at the top
-    // barrier claims t's successor and is read after the K loop, so the short tasks at a table's
-    // end still go to the workgroups that free up first.
-    const bool ahead2 = gather != nullptr;
+    // or run at least four tasks per workgroup claim two ahead: t's successor is in the claim word
+    // at every top barrier, the atomic issued there claims the task after it, and the successor's
+    // tile (and gathered rows) are loaded during t's K loop.  The others claim one ahead, late: the
+    // atomic issued at the top barrier claims t's successor and is read after the K loop, so with
+    // few tasks per workgroup the short tasks at a table's end still go to the workgroups that free
+    // up first.
+    const bool ahead2 = gather != nullptr || total >= 4 * static_cast<int>(gridDim.x);
     int t = claim_task(claimed, task_ctr, xcd, blk, wave, lane);
     if (ahead2)
         claim_task(claimed, task_ctr, xcd, blk, wave, lane);  // t's successor, left in the claim word
@@ -869,9 +879,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
         else
             step_barrier<top_wait<false>()>();
         int t_next = total;
+        MTile tile_next{};
+        int n0_next = 0;
+        bool half_next = false;
         if (ahead2) {
             const int i = __builtin_amdgcn_readfirstlane(*claimed);
             t_next = ((i / blk) * kXcdCount + xcd) * blk + i % blk;
+            if (t_next < total)
+                tile_next = decode(t_next, n0_next, half_next);
         }
         const int claim_ret = claim_issue(task_ctr, xcd, wave, lane);
         if (t_next < total)
@@ -920,8 +935,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
         t = t_next;
         // every wave is past its last read of this task's stages (and of the claim word)
         __syncthreads();
-        if (t < total)
-            setup(t);
+        if (t < total) {
+            if (ahead2)
+                setup_from(tile_next, n0_next, half_next);
+            else
+                setup(t);
+        }
         if (!done_skip)
             store_output_staged<kGated>(acc, C, done, done_n0, N_out, lds0 + kRingBytes + wave * kOutWaveBytes,
                                          wm, wn, lane, chunk_done != nullptr);
