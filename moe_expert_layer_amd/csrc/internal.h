@@ -115,8 +115,8 @@ hipError_t launch_route_scatter(const int32_t* ids, int64_t M, int64_t E,
 // zeroes chunk_done; zeroes the 2 * kXcdCount task counters at task_ctr.  A non-empty group with an expert outside [0, E) is skipped and sets
 // *status; with write_status the status word is written either way.  tiles_in_run (may be null;
 // unchunked tables only): also a table in which each group is one run of R = ceil(rows / bm) tiles
-// of near-equal height in row order (their pairs of 32-row blocks differ by at most one; the last
-// tile ends the group and takes an odd block), its number in count_in_run[0] and [2] (laid out as tile_count, so either table can be
+// of near-equal height in row order (their 32-row blocks differ by at most one; the last tile ends
+// the group), its number in count_in_run[0] and [2] (laid out as tile_count, so either table can be
 // handed to a GEMM with its counts).
 hipError_t launch_build_tiles(const int32_t* offsets, const int32_t* group_expert, int64_t G,
                               int64_t E, int64_t M, int64_t chunk, int bm, MTile* tiles, int64_t max_tiles,

@@ -201,9 +201,8 @@ __global__ __launch_bounds__(kThreads) void route_scatter_kernel(
 // full tiles (row order), then the partial tail tiles, each its own run, so that the short tasks
 // come last and even out the workgroups' finishing times.  The second table (tiles_in_run,
 // unchunked calls only) keeps each group as one run of R = ceil(rows / bm) tiles of near-equal
-// height (their pairs of 32-row blocks differ by at most one): the tasks that share a weight
-// strip then take near-equal time, so the workgroups of an XCD stay in step and share the strip in
-// its L2.
+// height (their 32-row blocks differ by at most one): the tasks that share a weight strip then
+// take equal time, so the workgroups of an XCD stay in step and share the strip in its L2.
 // One workgroup; groups are handled 1024 at a time.
 __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ group_expert, int G, int E,
@@ -328,18 +327,15 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
                         for (int64_t q = r; q < wend;) {
                             const int64_t c = q / chunk;
                             const int64_t cend = min(wend, (c + 1) * chunk);
-                            if ((layout == 1 || num_chunks > 1) && bm % 64 == 0) {
+                            if ((layout == 1 || num_chunks > 1) && bm % 32 == 0) {
                                 // balanced (the in-run table, and the chunked table's pieces): the
-                                // piece's 32-row blocks, taken in pairs, spread over its R tiles as
-                                // evenly as possible (at most one pair apart; the last tile ends the
-                                // piece and takes the odd block).  A tile's time follows its pairs:
-                                // its four SIMDs each take two of its 32-row x 128-column halves of
-                                // blocks, so 7 blocks cost what 8 do.
+                                // piece's 32-row blocks spread over its R tiles as evenly as possible
+                                // (at most one block apart; the last tile ends the piece)
                                 const int len = static_cast<int>(cend - q);
-                                const int nblk = (len + 31) / 32, R = (len + bm - 1) / bm, P = (nblk + 1) / 2;
+                                const int nblk = (len + 31) / 32, R = (len + bm - 1) / bm;
                                 int64_t r0 = q;
                                 for (int i = 0; i < R; ++i) {
-                                    const int64_t r1 = i == R - 1 ? cend : r0 + 64 * (P / R + (i < P % R ? 1 : 0));
+                                    const int64_t r1 = i == R - 1 ? cend : r0 + 32 * (nblk / R + (i < nblk % R ? 1 : 0));
                                     emit(r0, r1, run_begin, run_len, static_cast<int>(c));
                                     r0 = r1;
                                 }

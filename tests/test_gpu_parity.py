@@ -342,7 +342,7 @@ def test_grouped_ffn_short_groups_large_tiles(sizes):
 def test_grouped_ffn_balanced_tile_edges(sizes):
     """Groups whose row counts sit at the edges of 32-row blocks and 256-row tiles, at large-tile
     sizes.  Unchunked, fc1 cuts every group into ceil(rows / 256) tiles of near-equal height (a
-    group of 1025 rows, 33 blocks: five tiles of 8, 8, 6, 6 and 5 blocks, pairs of blocks spread evenly); fc2 does the same for the first set
+    group of 1025 rows: five tiles of 7, 7, 7, 6 and 6 blocks); fc2 does the same for the first set
     (groups averaging at most two tiles) and runs full tiles first with short tails split in two for
     the second.  Chunked tables cut each group's piece of a chunk the same way.  Every row matches
     the oracle, and the chunked results (512 and 256 rows) are bitwise the unchunked ones."""
