@@ -35,32 +35,39 @@ __device__ __forceinline__ int claim_task(int* claimed, int32_t* task_ctr, int x
     return ((i / blk) * kXcdCount + xcd) * blk + i % blk;
 }
 
-// Claims two tasks ahead in the persistent kernels: while task t runs, wave 0 claims the task after
-// t's successor.  claim_issue issues the atomic on lane 0 of wave 0, its address hidden from the
-// compiler so that it stays a single-lane operation whose result is waited for only where it is
-// first used (a wave-wide form is rewritten into a scan that waits for the result at once);
-// claim_value reads that result, after the K loop, whose last barrier has waited for every load of
-// the wave.  Wave 0 then publishes the value in the claim word, and every wave reads it after the
-// next task's first barrier.
+// Claims issued early and read late in the persistent kernels.  claim_issue: every wave runs the
+// same instruction sequence, so no lane-divergent region sits in the kernels' barrier loops (such a
+// region once let the compiler split a wave across barrier paths); inside it EXEC is narrowed to
+// lane 0 of wave 0 (none elsewhere) for one returning atomic add on the XCD's counter.  Written as
+// assembly because the compiler's atomic either becomes a scan that waits for the result at once
+// (uniform address) or, as a wave-wide operation, 64 serialised same-address atomics.  The result
+// register is written when the atomic returns: it is read only by claim_value, after the K loop,
+// whose barriers have waited for every load of the wave, and claim_value waits once more itself.
 __device__ __forceinline__ int claim_issue(int32_t* task_ctr, int xcd, int wave, int lane)
 {
-    int v = 0;
-    if (wave == 0 && lane == 0) {
-        int off = 0;
-        asm volatile("" : "+v"(off));
-        v = atomicAdd(task_ctr + xcd + off, 1);
-    }
+    (void)lane;
+    int v;
+    uint64_t saved;
+    const int mask = __builtin_amdgcn_readfirstlane(wave == 0 ? 1 : 0);
+    int32_t* const addr = task_ctr + xcd;
+    const int one = 1;
+    asm volatile("s_mov_b64 %1, exec\n\t"
+                 "s_mov_b32 exec_lo, %4\n\t"
+                 "s_mov_b32 exec_hi, 0\n\t"
+                 "global_atomic_add %0, %2, %3, off sc0\n\t"
+                 "s_mov_b64 exec, %1"
+                 : "=&v"(v), "=&s"(saved)
+                 : "v"(addr), "v"(one), "s"(mask)
+                 : "memory");
     return v;
 }
 
+// The claim of claim_issue (wave 0's lane 0; other waves get 0).
 __device__ __forceinline__ int claim_value(int v, int wave)
 {
-    int c = 0;
-    if (wave == 0) {
-        c = __builtin_amdgcn_readlane(v, 0);
-        asm volatile("" : "+s"(c));
-    }
-    return c;
+    int c;
+    asm volatile("s_waitcnt vmcnt(0)\n\tv_readlane_b32 %0, %1, 0" : "=s"(c) : "v"(v) : "memory");
+    return wave == 0 ? c : 0;
 }
 
 // Task t belongs to the run holding row tile t / n_nt; inside the run, row tiles vary fastest.
