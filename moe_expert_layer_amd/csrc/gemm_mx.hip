@@ -904,9 +904,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
         if (wave < 4)
             gsrc[kACopies] = gather[tl.row_begin + min(64 * wave + lane, last)];
     };
-    auto setup = [&](int tk) {
-        int nt;
-        tile = decode_task(tk, n_nt, tiles, nt);
+    // setup_from: the task whose tile and column tile decode_task gave
+    auto setup_from = [&](const MTile& tl, int nt) {
+        tile = tl;
         n0 = nt * BN;
         const int rows = tile.row_end - tile.row_begin;
 #pragma unroll
@@ -955,10 +955,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
         else
             cp.a += 4 * BK;
     };
+    auto setup = [&](int tk) {
+        int nt;
+        const MTile tl = decode_task(tk, n_nt, tiles, nt);
+        setup_from(tl, nt);
+    };
 
-    // claims as in the bf16 kernel: two ahead when gathering fc1 rows (t's successor is in the claim
-    // word at every top barrier), else one ahead, read after the K loop
-    const bool ahead2 = gather != nullptr;
+    // claims as in the bf16 kernel: two ahead when gathering fc1 rows or running at least four tasks
+    // per workgroup (t's successor is in the claim word at every top barrier, and its tile entry is
+    // loaded during t's K loop), else one ahead, read after the K loop
+    const bool ahead2 = gather != nullptr || total >= 4 * static_cast<int>(gridDim.x);
     int t = claim_task(claimed, task_ctr, xcd, blk, wave, lane);
     if (ahead2)
         claim_task(claimed, task_ctr, xcd, blk, wave, lane);
@@ -988,9 +994,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
         else
             step_barrier<top_wait<false>()>();
         int t_next = total;
+        MTile tile_next{};
+        int nt_next = 0;
         if (ahead2) {
             const int ci = __builtin_amdgcn_readfirstlane(*claimed);
             t_next = ((ci / blk) * kXcdCount + xcd) * blk + ci % blk;
+            if (t_next < total)
+                tile_next = decode_task(t_next, n_nt, tiles, nt_next);
         }
         const int claim_ret = claim_issue(task_ctr, xcd, wave, lane);
         if (t_next < total)
@@ -1015,8 +1025,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
         const int done_n0 = n0;
         t = t_next;
         __syncthreads();
-        if (t < total)
-            setup(t);
+        if (t < total) {
+            if (ahead2)
+                setup_from(tile_next, nt_next);
+            else
+                setup(t);
+        }
         const uint32_t stg = lds0 + kOutBase + wave * kOutWaveBytes;
         if constexpr (kGated)
             store_h<true>(acc, Cq, Cq_sc, done, done_n0, N_out, stg, wm, wn, lane);
