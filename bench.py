@@ -718,7 +718,7 @@ def main():
         bkavg = {n: tot / cnt for n, (tot, cnt) in bk.items()}
         grad_flops = 12.0 * M * H * F            # dgrad down + gate/up, wgrad down + gate/up
         rec_flops = 4.0 * M * H * F              # g and u recomputed
-        gemm_names = ("recompute_g", "recompute_u", "dgrad_down", "dgrad_gate_up", "wgrad_down",
+        gemm_names = ("recompute_gu", "dgrad_down", "dgrad_gate_up", "wgrad_down",
                       "wgrad_gate", "wgrad_up")
         gemm_ms = sum(bkavg.get(n, 0.0) for n in gemm_names)
         b_mean = float(bms.mean())

@@ -574,8 +574,8 @@ struct BackwardLayout {
     int bm_r = 0, bm_d = 0;
 };
 
-// g and u are recomputed with the plain grouped GEMM (K = H, N = F), whose row tiles are bm_r
-// high; the backward's own GEMMs use 128-row tiles.
+// g and u are recomputed with the fc1 kernel (h not stored), whose row tiles are bm_r high; the
+// backward's own GEMMs use 128-row tiles.
 BackwardLayout backward_layout(int64_t T, int64_t H, int64_t F, int64_t E, int64_t k)
 {
     const int64_t M = T * k;
@@ -594,7 +594,7 @@ BackwardLayout backward_layout(int64_t T, int64_t H, int64_t F, int64_t E, int64
     L.pos = take(4 * n(M));
     L.tile_count = take(4 * sizeof(int32_t));
     L.task_ctr = take(2 * kXcdCount * sizeof(int32_t));
-    L.bm_r = bf16_row_tile(F, H);
+    L.bm_r = bf16_row_tile(H, F);
     L.max_tiles_r = max_mtiles(M, E, 0, L.bm_r);
     L.bm_d = dgrad_row_tile(M, H, F);
     L.max_tiles_d = max_mtiles(M, E, 0, L.bm_d);
@@ -711,10 +711,9 @@ MOE_API moe_status moe_expert_backward(const moe_problem* p, const void* x, cons
         const int32_t* tcount_d = L.tiles_d != L.tiles_r ? tcount + 1 : tcount;
         // g = x_perm Wg[e], u = x_perm Wu[e]: the plain grouped GEMM with K = H and N = F
         if (saved_gu == nullptr) {
-            LAUNCH(s, "recompute_g", launch_recompute_bf16(x_perm, wg, at<uint16_t>(ws, L.g), tiles_r,
-                                                           tcount, H, F, task_ctr, s));
-            LAUNCH(s, "recompute_u", launch_recompute_bf16(x_perm, wu, at<uint16_t>(ws, L.u), tiles_r,
-                                                           tcount, H, F, task_ctr + kXcdCount, s));
+            LAUNCH(s, "recompute_gu",
+                   launch_recompute_gu_bf16(x_perm, wg, wu, at<uint16_t>(ws, L.g), at<uint16_t>(ws, L.u),
+                                            tiles_r, tcount, H, F, task_ctr, s));
         }
         LAUNCH(s, "row_probs", launch_row_probs(perm, probs, prow, M, s));
         LAUNCH(s, "dgrad_down",

@@ -198,19 +198,20 @@ __device__ __forceinline__ void store_output(const f32x16_t (&acc)[kTM][kTN], ui
                             (r & 3);
             if (row >= tile.row_end)
                 continue;
-            uint16_t* crow = C + static_cast<int64_t>(row) * N_out;
             if (kGated) {
 #pragma unroll
                 for (int j = 0; j < kTN; j += 2) {
                     const int q = (wn * kTN + j) / 2;
                     const int64_t at = static_cast<int64_t>(row) * N_out + n0 + 32 * q + (lane & 31);
-                    crow[n0 + 32 * q + (lane & 31)] = f32_to_bf16(swiglu(acc[i][j][r], acc[i][j + 1][r]));
+                    if (C != nullptr)           // null: only g and u are wanted
+                        C[at] = f32_to_bf16(swiglu(acc[i][j][r], acc[i][j + 1][r]));
                     if (save_g != nullptr) {
                         save_g[at] = f32_to_bf16(acc[i][j][r]);
                         save_u[at] = f32_to_bf16(acc[i][j + 1][r]);
                     }
                 }
             } else {
+                uint16_t* crow = C + static_cast<int64_t>(row) * N_out;
 #pragma unroll
                 for (int j = 0; j < kTN; ++j)
                     crow[n0 + wn * kTN * 32 + 32 * j + (lane & 31)] = f32_to_bf16(acc[i][j][r]);
@@ -667,6 +668,7 @@ __device__ __forceinline__ void store_output_staged(const f32x16_t (&acc)[kTM][k
 
 // gather (fc1 only, may be null): permuted row p of A is row gather[p] / gather_k of the matrix
 // A points at (the permute step folded into the row copies); null: row p of A.
+// C (gated) may be null when save_g / save_u are set: then h is not stored.
 // kRole only separates launches in profiles: 0 for the forward, 1 for the backward's recompute of g
 // and u (the same code).
 template <bool kGated, int kRole = 0>
@@ -941,7 +943,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
             else
                 setup(t);
         }
-        if (!done_skip)
+        if (!done_skip && C != nullptr)
             store_output_staged<kGated>(acc, C, done, done_n0, N_out, lds0 + kRingBytes + wave * kOutWaveBytes,
                                          wm, wn, lane, chunk_done != nullptr);
         if constexpr (kGated) {
@@ -993,7 +995,7 @@ hipError_t ensure_smem_limits()
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(&big::grouped_gemm_bf16_dma<false>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kBigSmem);
     if (e == hipSuccess)
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&big::grouped_gemm_bf16_dma<false, 1>),
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&big::grouped_gemm_bf16_dma<true, 1>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kBigSmem);
     if (e == hipSuccess && dev < 64)
         done[dev] = true;
@@ -1047,21 +1049,22 @@ hipError_t launch_fc2_bf16(const uint16_t* h, const uint16_t* wd, uint16_t* y, c
     return hipGetLastError();
 }
 
-hipError_t launch_recompute_bf16(const uint16_t* A, const uint16_t* w, uint16_t* C, const MTile* tiles,
-                                 const int32_t* tile_count, int64_t K, int64_t N, int32_t* task_ctr,
-                                 hipStream_t s)
+hipError_t launch_recompute_gu_bf16(const uint16_t* A, const uint16_t* wg, const uint16_t* wu,
+                                    uint16_t* g, uint16_t* u, const MTile* tiles,
+                                    const int32_t* tile_count, int64_t H, int64_t F, int32_t* task_ctr,
+                                    hipStream_t s)
 {
     const int cu = device_info().cu_count;
-    if (use_big(N, K)) {
+    if (use_big(H, F)) {
         if (hipError_t e = ensure_smem_limits(); e != hipSuccess)
             return e;
-        big::grouped_gemm_bf16_dma<false, 1><<<dim3(cu), dim3(big::kThreads), kBigSmem, s>>>(
-            A, w, nullptr, C, tiles, tile_count, static_cast<int>(K), static_cast<int>(N), nullptr,
-            task_ctr, nullptr, 1, nullptr, nullptr);
+        big::grouped_gemm_bf16_dma<true, 1><<<dim3(cu), dim3(big::kThreads), kBigSmem, s>>>(
+            A, wg, wu, nullptr, tiles, tile_count, static_cast<int>(H), static_cast<int>(F), nullptr,
+            task_ctr, nullptr, 1, g, u);
     } else {
-        FC2_SMALL<<<dim3(2 * cu), dim3(Fc2Small::kThreads), Fc2Small::kSmemBytes, s>>>(
-            A, w, nullptr, C, tiles, tile_count, static_cast<int>(K), static_cast<int>(N), nullptr,
-            task_ctr, nullptr, nullptr);
+        FC1_SMALL<<<dim3(2 * cu), dim3(Fc1Small::kThreads), Fc1Small::kSmemBytes, s>>>(
+            A, wg, wu, nullptr, tiles, tile_count, static_cast<int>(H), static_cast<int>(F), nullptr,
+            task_ctr, g, u);
     }
     return hipGetLastError();
 }
