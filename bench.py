@@ -491,6 +491,81 @@ def compact_layer(args, torch, mel, synth, dv, dev, name, flush):
 EXTRA_WORKLOADS = ("ep_rank_bf16", "finegrained_bf16", "mxfp8")
 
 
+PROBE_FIELDS = ("wait", "loop", "loop_full", "sync", "setup", "epilogue", "tasks", "tasks_full",
+                "total", "realtime", "workgroups")
+
+
+def phase_probe(args, torch, mel, synth, dv, dev):
+    """Per-task phases of the bf16 GEMM launches, from the probe library's cycle stamps: the forward
+    (or the EP rank's grouped FFN) run --steps times after --warmup, each call after the cache flush
+    the timed benchmark uses.  Cycles are wave 0's counter cycles; a full task's MFMA issue is
+    (K / 32) K steps x 2 waves x 16 MFMAs x 32 cycles per SIMD."""
+    import ctypes
+    lib = mel.library()
+    probe = lib.moe_probe_phases
+    probe.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    probe.restype = ctypes.c_int
+    cfg = synth.WORKLOADS[args.workload]
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev).view(torch.float32)
+    head = args.head_m_size if args.head_m_size is not None else 0
+    if cfg["kind"] == "grouped":
+        g = synth.make_workload(args.workload)
+        M, H = g.rows.shape
+        F = g.F
+        rows = dv.tensor(g.rows, dev)
+        offs, gexp = dv.tensor(g.group_offsets, dev), dv.tensor(g.group_expert, dev)
+        wg, wu, wd = (dv.tensor(w, dev) for w in (g.w_gate, g.w_up, g.w_down))
+        out = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+
+        def step():
+            mel.grouped_ffn(rows, offs, gexp, wg, wu, wd, head_m_size=head, out=out)
+    else:
+        inp = synth.make_workload(args.workload)
+        if inp.dtype != "bf16":
+            sys.exit("--phase-probe covers the bf16 GEMMs: pick a bf16 workload")
+        d = dv.layer(inp, dev)
+        H, F = inp.H, inp.F
+        out = torch.empty((inp.T, H), dtype=torch.bfloat16, device=dev)
+
+        def step():
+            mel.expert_forward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs,
+                               head_m_size=head, out=out)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if probe(None, 1) != 0:
+        raise RuntimeError("moe_probe_phases failed")
+    for _ in range(args.steps):
+        if not args.no_flush:
+            flush.sum()
+        step()
+    buf = (ctypes.c_ulonglong * (3 * len(PROBE_FIELDS)))()
+    if probe(ctypes.cast(buf, ctypes.c_void_p), 1) != 0:
+        raise RuntimeError("moe_probe_phases failed")
+    report = {"workload": args.workload, "steps": args.steps, "head_m_size": head, "kernels": {}}
+    for kind, name, K in ((1, "fc1_bf16", H), (0, "fc2_bf16", F)):
+        v = dict(zip(PROBE_FIELDS, buf[kind * len(PROBE_FIELDS):(kind + 1) * len(PROBE_FIELDS)]))
+        if v["tasks"] == 0:
+            continue
+        ideal = (K // 32) * 1024
+        r = {"tasks_per_launch": v["tasks"] / args.steps,
+             "tasks_per_workgroup": v["tasks"] / v["workgroups"],
+             "per_task_cycles": {f: v[f] / v["tasks"] for f in ("wait", "loop", "sync", "setup", "epilogue")},
+             "share_of_workgroup_cycles": {f: v[f] / v["total"] for f in ("wait", "loop", "sync", "setup", "epilogue")},
+             "loop_full_cycles": v["loop_full"] / v["tasks_full"] if v["tasks_full"] else None,
+             "full_task_mfma_issue_cycles": ideal,
+             "loop_full_mfma_fraction": ideal * v["tasks_full"] / v["loop_full"] if v["loop_full"] else None,
+             "counter_mhz": v["total"] / v["realtime"] * 100.0 if v["realtime"] else None,
+             "workgroup_us": v["realtime"] / v["workgroups"] / 100.0}
+        report["kernels"][name] = r
+        pt = r["per_task_cycles"]
+        log(f"{name}: {r['tasks_per_workgroup']:.1f} tasks per workgroup; per task wait {pt['wait']:.0f}, "
+            f"K loop {pt['loop']:.0f} (full tasks {r['loop_full_cycles'] or 0:.0f} against {ideal} of MFMA issue), "
+            f"sync {pt['sync']:.0f}, setup {pt['setup']:.0f}, epilogue {pt['epilogue']:.0f} counter cycles; "
+            f"counter {r['counter_mhz'] or 0:.0f} MHz")
+    return {"phase_probe": report}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -517,6 +592,9 @@ def main():
                     help="leave out the standalone permute / unpermute rates")
     ap.add_argument("--mx-from-bf16", action="store_true",
                     help="MX workloads: feed the bfloat16 x and let the library encode it (MOE_FLAG_QUANTIZE_X)")
+    ap.add_argument("--phase-probe", action="store_true",
+                    help="bf16 workloads: run the forward on the probe library (per-task cycle stamps in "
+                         "the bf16 GEMMs) and print a per-task phase report instead of the benchmark line")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -529,6 +607,11 @@ def main():
     import synth
     from synth import device as dv
 
+    if args.phase_probe:
+        from moe_expert_layer_amd.build import PROBE_LIB_PATH
+        if not os.path.exists(PROBE_LIB_PATH):
+            sys.exit(f"{PROBE_LIB_PATH} is missing: build it with `python -m moe_expert_layer_amd.build`")
+        mel.library(PROBE_LIB_PATH)        # loaded first, so every call below runs the probe build
     if not os.path.exists(mel.lib_path):
         from moe_expert_layer_amd.build import build
         build()
@@ -536,6 +619,9 @@ def main():
     dev = torch.device("cuda", 0)
 
     cfg = synth.WORKLOADS[args.workload]
+    if args.phase_probe:
+        print(json.dumps(phase_probe(args, torch, mel, synth, dv, dev)), flush=True)
+        return
     if cfg["kind"] == "grouped":
         print(json.dumps(bench_grouped(args, torch, mel, synth, dv, dev)), flush=True)
         return

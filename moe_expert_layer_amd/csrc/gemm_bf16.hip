@@ -39,6 +39,9 @@
 #include "common.h"
 #include "gemm_common.h"
 #include "internal.h"
+#ifdef MOE_PHASE_PROBE
+#include "moe_expert_layer_probe.h"
+#endif
 
 namespace moe {
 namespace {
@@ -309,6 +312,32 @@ __global__ __launch_bounds__(kWM * kWN * 64, kMinBlocks) void grouped_gemm_bf16(
 
 // ------------------------------------------------------------------------------------------------
 // Large tiles with LDS DMA
+
+#ifdef MOE_PHASE_PROBE
+// Per-task phase timing, compiled only into the probe library (timestamps only; every kernel does
+// the same work as in the product library).  Wave 0 of each workgroup reads the cycle counter at
+// the points of its task loop that MOE_PROBE_* names and keeps per-workgroup sums in scalar
+// registers; after its last task lane 0 adds them to g_phase[kind] (kind 0 fc2, 1 fc1, 2 the
+// backward's recompute), outside the task loop and its barriers.
+enum ProbeField {
+    kProbeWait,           // from the previous epilogue's end (or the kernel's start) past the top barrier
+    kProbeLoop,           // K loops
+    kProbeLoopFull,       // K loops of full-height, full-width tasks
+    kProbeSync,           // after the K loop: the claim's result and the barrier that ends the loop
+    kProbeSetup,          // the next task's setup (its first copies)
+    kProbeEpilogue,       // the epilogue
+    kProbeTasks,
+    kProbeTasksFull,
+    kProbeTotal,          // cycles from the kernel's start to the workgroup's end
+    kProbeRealtime,       // the same span on the 100 MHz real-time counter
+    kProbeWorkgroups,
+    kProbeFields
+};
+__device__ unsigned long long g_phase[3][kProbeFields];
+#define MOE_PROBE(...) __VA_ARGS__
+#else
+#define MOE_PROBE(...)
+#endif
 
 namespace big {
 constexpr int kWM = 4, kWN = 2, kTM = 2, kTN = 4;     // 8 waves (2 per SIMD), 64 x 128 each
@@ -847,6 +876,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
     // few tasks per workgroup the short tasks at a table's end still go to the workgroups that free
     // up first.
     const bool ahead2 = gather != nullptr || total >= 4 * static_cast<int>(gridDim.x);
+    MOE_PROBE(unsigned long long pr[kProbeFields] = {};
+              const unsigned long long pr_k0 = __builtin_readcyclecounter();
+              const unsigned long long pr_r0 = __builtin_amdgcn_s_memrealtime();
+              unsigned long long pr_t = pr_k0, pr_b = 0, pr_k = 0, pr_s = 0, pr_u = 0;)
     int t = claim_task(claimed, task_ctr, xcd, blk, wave, lane);
     if (ahead2)
         claim_task(claimed, task_ctr, xcd, blk, wave, lane);  // t's successor, left in the claim word
@@ -880,6 +913,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
             step_barrier<top_wait<true>()>();
         else
             step_barrier<top_wait<false>()>();
+        MOE_PROBE(pr_b = __builtin_readcyclecounter(); pr[kProbeWait] += pr_b - pr_t;)
         int t_next = total;
         MTile tile_next{};
         int n0_next = 0;
@@ -921,6 +955,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
             else
                 k_loop<kGated, kTM, true, false>(acc, cp, g, N_w, KT);
         }
+        MOE_PROBE(pr_k = __builtin_readcyclecounter(); pr[kProbeLoop] += pr_k - pr_b; ++pr[kProbeTasks];
+                  if (rows == BM && !half_task) { pr[kProbeLoopFull] += pr_k - pr_b; ++pr[kProbeTasksFull]; })
         const int claim_after = claim_value(claim_ret, wave);
         if (!ahead2) {
             // one ahead: the claim word (in wave 0's staging area, idle between its epilogues)
@@ -937,12 +973,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
         t = t_next;
         // every wave is past its last read of this task's stages (and of the claim word)
         __syncthreads();
+        MOE_PROBE(pr_s = __builtin_readcyclecounter(); pr[kProbeSync] += pr_s - pr_k;)
         if (t < total) {
             if (ahead2)
                 setup_from(tile_next, n0_next, half_next);
             else
                 setup(t);
         }
+        MOE_PROBE(pr_u = __builtin_readcyclecounter(); pr[kProbeSetup] += pr_u - pr_s;)
         if (!done_skip && C != nullptr)
             store_output_staged<kGated>(acc, C, done, done_n0, N_out, lds0 + kRingBytes + wave * kOutWaveBytes,
                                          wm, wn, lane, chunk_done != nullptr);
@@ -962,7 +1000,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
         // the word)
         if (ahead2 && wave == 0)
             *claimed = claim_after;
+        MOE_PROBE(pr_t = __builtin_readcyclecounter(); pr[kProbeEpilogue] += pr_t - pr_u;)
     }
+#ifdef MOE_PHASE_PROBE
+    if (wave == 0 && lane == 0) {
+        pr[kProbeTotal] = __builtin_readcyclecounter() - pr_k0;
+        pr[kProbeRealtime] = __builtin_amdgcn_s_memrealtime() - pr_r0;
+        pr[kProbeWorkgroups] = 1;
+        const int kind = kRole == 1 ? 2 : (kGated ? 1 : 0);
+#pragma unroll
+        for (int q = 0; q < kProbeFields; ++q)
+            atomicAdd(&g_phase[kind][q], pr[q]);
+    }
+#endif
 }
 }  // namespace big
 
@@ -1070,3 +1120,23 @@ hipError_t launch_recompute_gu_bf16(const uint16_t* A, const uint16_t* wg, const
 }
 
 }  // namespace moe
+
+#ifdef MOE_PHASE_PROBE
+static_assert(MOE_PROBE_FIELDS == moe::kProbeFields && MOE_PROBE_KINDS == 3, "probe layout");
+
+extern "C" __attribute__((visibility("default"))) int moe_probe_phases(unsigned long long* out, int reset)
+{
+    // the launches already enqueued are the ones counted
+    if (hipDeviceSynchronize() != hipSuccess)
+        return 1;
+    if (out != nullptr &&
+        hipMemcpyFromSymbol(out, HIP_SYMBOL(moe::g_phase), sizeof(moe::g_phase)) != hipSuccess)
+        return 1;
+    if (reset) {
+        const unsigned long long zero[3 * moe::kProbeFields] = {};
+        if (hipMemcpyToSymbol(HIP_SYMBOL(moe::g_phase), zero, sizeof(zero)) != hipSuccess)
+            return 1;
+    }
+    return hipDeviceSynchronize() != hipSuccess;
+}
+#endif

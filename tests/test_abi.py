@@ -197,3 +197,15 @@ def test_quantize_x_flag(mel):
                                    *([ctypes.c_void_p(0x1000)] * 9), ctypes.c_void_p(0x1000), n1.value,
                                    None)
     assert st == 1 and b"x_scale" in lib.moe_last_error()
+
+
+def test_probe_entry_only_in_the_probe_library(mel):
+    """moe_probe_phases (include/moe_expert_layer_probe.h) is exported by the probe build alone."""
+    from moe_expert_layer_amd.build import PROBE_LIB_PATH
+    probe_header = os.path.join(os.path.dirname(HEADER), "moe_expert_layer_probe.h")
+    text = re.sub(r"/\*.*?\*/", "", open(probe_header).read(), flags=re.S)
+    assert re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text) == ["moe_probe_phases"]
+    assert not hasattr(ctypes.CDLL(mel.lib_path), "moe_probe_phases")
+    if not os.path.exists(PROBE_LIB_PATH):
+        pytest.skip("probe library not built")
+    assert hasattr(ctypes.CDLL(PROBE_LIB_PATH), "moe_probe_phases")
