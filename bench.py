@@ -63,12 +63,48 @@ def byte_model(inp, M):
     return {"permute": (1 + k) * T * H * b + 4 * M, "unpermute": (k * T * H * b + T * H * b + 8 * M)}
 
 
+def _strip_probe(text: str) -> str:
+    """The source as the product library compiles it: without the probe build's code (the
+    `#ifdef MOE_PHASE_PROBE` blocks and their directives, keeping an `#else` part, the
+    `MOE_PROBE(...)` uses and the macro's own definition)."""
+    out, stack = [], []                 # per open #if: [probe block, in its #else part]
+    live = lambda: all(not p or e for p, e in stack)
+    for line in text.splitlines():
+        d = line.strip()
+        if d.startswith("#if"):
+            stack.append([d.split()[:2] == ["#ifdef", "MOE_PHASE_PROBE"], False])
+            if not stack[-1][0] and live():
+                out.append(line)
+        elif d.startswith("#else") and stack:
+            stack[-1][1] = True
+            if not stack[-1][0] and live():
+                out.append(line)
+        elif d.startswith("#endif") and stack:
+            probe = stack.pop()[0]
+            if not probe and live():
+                out.append(line)
+        elif live() and not d.startswith("#define MOE_PROBE"):
+            out.append(line)
+    text = "\n".join(out)
+    while True:                                   # MOE_PROBE( ... ) with nested parentheses
+        i = text.find("MOE_PROBE(")
+        if i < 0:
+            return text
+        j, n = i + len("MOE_PROBE("), 1
+        while n:
+            n += {"(": 1, ")": -1}.get(text[j], 0)
+            j += 1
+        text = text[:i] + text[j:]
+
+
 def _code_only(text: str) -> str:
-    """C++ source without its comments and blank lines (a comment edit does not change a kernel)."""
+    """C++ source without its comments, blank lines and probe-build code (a comment edit, or a
+    change to the probe build, does not change a product kernel)."""
     import re
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    lines = (re.sub(r"//.*", "", line).rstrip() for line in text.splitlines())
-    return "\n".join(line for line in lines if line.strip())
+    text = "\n".join(re.sub(r"//.*", "", line).rstrip() for line in text.splitlines())
+    text = _strip_probe(text)
+    return "\n".join(line for line in text.splitlines() if line.strip())
 
 
 def kernel_source_digest(files) -> str:
