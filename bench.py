@@ -528,14 +528,17 @@ EXTRA_WORKLOADS = ("ep_rank_bf16", "finegrained_bf16", "mxfp8")
 
 
 PROBE_FIELDS = ("wait", "loop", "loop_full", "sync", "setup", "epilogue", "tasks", "tasks_full",
-                "total", "realtime", "workgroups")
+                "total", "realtime", "workgroups", "steps")
+PROBE_KINDS = ("fc2_bf16", "fc1_bf16", "recompute_gu", "wgrad", "dgrad_down", "dgrad_gate_up")
 
 
 def phase_probe(args, torch, mel, synth, dv, dev):
-    """Per-task phases of the bf16 GEMM launches, from the probe library's cycle stamps: the forward
-    (or the EP rank's grouped FFN) run --steps times after --warmup, each call after the cache flush
-    the timed benchmark uses.  Cycles are wave 0's counter cycles; a full task's MFMA issue is
-    (K / 32) K steps x 2 waves x 16 MFMAs x 32 cycles per SIMD."""
+    """Per-task phases of the large-tile GEMM launches, from the probe library's cycle stamps: the
+    forward (or the EP rank's grouped FFN) run --steps times after --warmup, each call after the
+    cache flush the timed benchmark uses; then, for bf16 layer workloads and unless --skip-backward,
+    the backward (recomputing g and u) the same way.  Cycles are wave 0's counter cycles; a K step
+    of 32 issues 2 waves x 16 MFMAs x 32 cycles = 1024 cycles per SIMD, so loop_mfma_fraction is
+    (K steps x 1024) / K-loop cycles, over the full-height tasks where tasks differ in height."""
     import ctypes
     lib = mel.library()
     probe = lib.moe_probe_phases
@@ -544,61 +547,68 @@ def phase_probe(args, torch, mel, synth, dv, dev):
     cfg = synth.WORKLOADS[args.workload]
     flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev).view(torch.float32)
     head = args.head_m_size if args.head_m_size is not None else 0
+    legs = []
     if cfg["kind"] == "grouped":
         g = synth.make_workload(args.workload)
         M, H = g.rows.shape
-        F = g.F
         rows = dv.tensor(g.rows, dev)
         offs, gexp = dv.tensor(g.group_offsets, dev), dv.tensor(g.group_expert, dev)
         wg, wu, wd = (dv.tensor(w, dev) for w in (g.w_gate, g.w_up, g.w_down))
         out = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
-
-        def step():
-            mel.grouped_ffn(rows, offs, gexp, wg, wu, wd, head_m_size=head, out=out)
+        legs.append(("forward", lambda: mel.grouped_ffn(rows, offs, gexp, wg, wu, wd, head_m_size=head, out=out)))
     else:
         inp = synth.make_workload(args.workload)
         if inp.dtype != "bf16":
             sys.exit("--phase-probe covers the bf16 GEMMs: pick a bf16 workload")
         d = dv.layer(inp, dev)
-        H, F = inp.H, inp.F
-        out = torch.empty((inp.T, H), dtype=torch.bfloat16, device=dev)
-
-        def step():
-            mel.expert_forward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids, d.probs,
-                               head_m_size=head, out=out)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    if probe(None, 1) != 0:
-        raise RuntimeError("moe_probe_phases failed")
-    for _ in range(args.steps):
-        if not args.no_flush:
-            flush.sum()
-        step()
-    buf = (ctypes.c_ulonglong * (3 * len(PROBE_FIELDS)))()
-    if probe(ctypes.cast(buf, ctypes.c_void_p), 1) != 0:
-        raise RuntimeError("moe_probe_phases failed")
+        out = torch.empty((inp.T, inp.H), dtype=torch.bfloat16, device=dev)
+        legs.append(("forward", lambda: mel.expert_forward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids,
+                                                           d.probs, head_m_size=head, out=out)))
+        if not args.skip_backward:
+            dout = dv.tensor(synth.make_dout(inp), dev)
+            bws = torch.empty(mel.backward_workspace_size(mel.problem(inp.T, inp.H, inp.F, inp.E, inp.k, mel.BF16)),
+                              dtype=torch.uint8, device=dev)
+            legs.append(("backward", lambda: mel.expert_backward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids,
+                                                                 d.probs, dout, workspace=bws)))
     report = {"workload": args.workload, "steps": args.steps, "head_m_size": head, "kernels": {}}
-    for kind, name, K in ((1, "fc1_bf16", H), (0, "fc2_bf16", F)):
-        v = dict(zip(PROBE_FIELDS, buf[kind * len(PROBE_FIELDS):(kind + 1) * len(PROBE_FIELDS)]))
-        if v["tasks"] == 0:
-            continue
-        ideal = (K // 32) * 1024
-        r = {"tasks_per_launch": v["tasks"] / args.steps,
-             "tasks_per_workgroup": v["tasks"] / v["workgroups"],
-             "per_task_cycles": {f: v[f] / v["tasks"] for f in ("wait", "loop", "sync", "setup", "epilogue")},
-             "share_of_workgroup_cycles": {f: v[f] / v["total"] for f in ("wait", "loop", "sync", "setup", "epilogue")},
-             "loop_full_cycles": v["loop_full"] / v["tasks_full"] if v["tasks_full"] else None,
-             "full_task_mfma_issue_cycles": ideal,
-             "loop_full_mfma_fraction": ideal * v["tasks_full"] / v["loop_full"] if v["loop_full"] else None,
-             "counter_mhz": v["total"] / v["realtime"] * 100.0 if v["realtime"] else None,
-             "workgroup_us": v["realtime"] / v["workgroups"] / 100.0}
-        report["kernels"][name] = r
-        pt = r["per_task_cycles"]
-        log(f"{name}: {r['tasks_per_workgroup']:.1f} tasks per workgroup; per task wait {pt['wait']:.0f}, "
-            f"K loop {pt['loop']:.0f} (full tasks {r['loop_full_cycles'] or 0:.0f} against {ideal} of MFMA issue), "
-            f"sync {pt['sync']:.0f}, setup {pt['setup']:.0f}, epilogue {pt['epilogue']:.0f} counter cycles; "
-            f"counter {r['counter_mhz'] or 0:.0f} MHz")
+    nf = len(PROBE_FIELDS)
+    for leg, step in legs:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        if probe(None, 1) != 0:
+            raise RuntimeError("moe_probe_phases failed")
+        for _ in range(args.steps):
+            if not args.no_flush:
+                flush.sum()
+            step()
+        buf = (ctypes.c_ulonglong * (len(PROBE_KINDS) * nf))()
+        if probe(ctypes.cast(buf, ctypes.c_void_p), 1) != 0:
+            raise RuntimeError("moe_probe_phases failed")
+        for kind, name in enumerate(PROBE_KINDS):
+            v = dict(zip(PROBE_FIELDS, buf[kind * nf:(kind + 1) * nf]))
+            if v["tasks"] == 0:
+                continue
+            steps_per_task = v["steps"] / v["tasks"]
+            full = v["tasks_full"] > 0 and v["loop_full"] > 0
+            r = {"leg": leg,
+                 "tasks_per_launch": v["tasks"] / args.steps,
+                 "tasks_per_workgroup": v["tasks"] / v["workgroups"],
+                 "k_steps_per_task": steps_per_task,
+                 "per_task_cycles": {f: v[f] / v["tasks"] for f in ("wait", "loop", "sync", "setup", "epilogue")},
+                 "share_of_workgroup_cycles": {f: v[f] / v["total"] for f in ("wait", "loop", "sync", "setup", "epilogue")},
+                 "loop_full_cycles": v["loop_full"] / v["tasks_full"] if full else None,
+                 "mfma_issue_cycles_per_task": steps_per_task * 1024,
+                 "loop_mfma_fraction": (steps_per_task * 1024 * v["tasks_full"] / v["loop_full"] if full
+                                        else v["steps"] * 1024 / v["loop"]),
+                 "counter_mhz": v["total"] / v["realtime"] * 100.0 if v["realtime"] else None,
+                 "workgroup_us": v["realtime"] / v["workgroups"] / 100.0}
+            report["kernels"][name] = r
+            pt = r["per_task_cycles"]
+            log(f"{name}: {r['tasks_per_workgroup']:.1f} tasks per workgroup, {steps_per_task:.0f} K steps; per task "
+                f"wait {pt['wait']:.0f}, K loop {pt['loop']:.0f} (MFMA issue {r['loop_mfma_fraction']:.3f} of it"
+                f"{' on full tasks' if full else ''}), sync {pt['sync']:.0f}, setup {pt['setup']:.0f}, "
+                f"epilogue {pt['epilogue']:.0f} counter cycles; counter {r['counter_mhz'] or 0:.0f} MHz")
     return {"phase_probe": report}
 
 

@@ -3,9 +3,10 @@
  * (libmoe_expert_layer_probe.so), a build of the same sources with MOE_PHASE_PROBE defined.
  *
  * In that build the large-tile bf16 grouped GEMMs (fc1, fc2 and the backward's recompute of g and
- * u) read the cycle counter at fixed points of their task loop and add per-workgroup sums to a
- * device array; every kernel does the same work as in the product library (the stamps only add
- * instructions).  The product library does not export this function.
+ * u) and the backward's LDS-DMA GEMMs (weight gradients, down and gate/up dgrads) read the cycle
+ * counter at fixed points of their task loop and add per-workgroup sums to device arrays; every
+ * kernel does the same work as in the product library (the stamps only add instructions).  The
+ * product library does not export this function.
  *
  * For callers that measure where a GEMM launch spends its cycles, not for the compute path.
  */
@@ -22,11 +23,15 @@ extern "C" {
  * tasks; 3 from the K loop's end past the barrier that ends it; 4 the next task's setup (its
  * first copies); 5 epilogues; 6 tasks; 7 full-height, full-width tasks; 8 cycles from the kernel's
  * start to the workgroup's end; 9 the same span in ticks of the 100 MHz real-time counter;
- * 10 workgroups.  Counts of cycles are wave 0's, summed over workgroups and launches.
+ * 10 workgroups; 11 K steps of 32 over all tasks (a K step issues 1024 cycles of MFMAs per SIMD).
+ * Counts of cycles are wave 0's, summed over workgroups and launches.
  */
-#define MOE_PROBE_FIELDS 11
-/* Kernel kinds: 0 fc2 (down projection), 1 fc1 (gate and up), 2 the backward's recompute. */
-#define MOE_PROBE_KINDS 3
+#define MOE_PROBE_FIELDS 12
+/*
+ * Kernel kinds: 0 fc2 (down projection), 1 fc1 (gate and up), 2 the backward's recompute of g and u,
+ * 3 the weight gradients, 4 the down dgrad (with the SwiGLU backward), 5 the gate/up dgrad.
+ */
+#define MOE_PROBE_KINDS 6
 
 /*
  * Copies the sums since the last reset into out (host, MOE_PROBE_KINDS * MOE_PROBE_FIELDS

@@ -39,9 +39,6 @@
 #include "common.h"
 #include "gemm_common.h"
 #include "internal.h"
-#ifdef MOE_PHASE_PROBE
-#include "moe_expert_layer_probe.h"
-#endif
 
 namespace moe {
 namespace {
@@ -319,21 +316,7 @@ __global__ __launch_bounds__(kWM * kWN * 64, kMinBlocks) void grouped_gemm_bf16(
 // the points of its task loop that MOE_PROBE_* names and keeps per-workgroup sums in scalar
 // registers; after its last task lane 0 adds them to g_phase[kind] (kind 0 fc2, 1 fc1, 2 the
 // backward's recompute), outside the task loop and its barriers.
-enum ProbeField {
-    kProbeWait,           // from the previous epilogue's end (or the kernel's start) past the top barrier
-    kProbeLoop,           // K loops
-    kProbeLoopFull,       // K loops of full-height, full-width tasks
-    kProbeSync,           // after the K loop: the claim's result and the barrier that ends the loop
-    kProbeSetup,          // the next task's setup (its first copies)
-    kProbeEpilogue,       // the epilogue
-    kProbeTasks,
-    kProbeTasksFull,
-    kProbeTotal,          // cycles from the kernel's start to the workgroup's end
-    kProbeRealtime,       // the same span on the 100 MHz real-time counter
-    kProbeWorkgroups,
-    kProbeFields
-};
-__device__ unsigned long long g_phase[3][kProbeFields];
+__device__ unsigned long long g_phase[kProbeKindsBf16][kProbeFields];
 #define MOE_PROBE(...) __VA_ARGS__
 #else
 #define MOE_PROBE(...)
@@ -956,6 +939,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_dma(
                 k_loop<kGated, kTM, true, false>(acc, cp, g, N_w, KT);
         }
         MOE_PROBE(pr_k = __builtin_readcyclecounter(); pr[kProbeLoop] += pr_k - pr_b; ++pr[kProbeTasks];
+                  pr[kProbeSteps] += KT;
                   if (rows == BM && !half_task) { pr[kProbeLoopFull] += pr_k - pr_b; ++pr[kProbeTasksFull]; })
         const int claim_after = claim_value(claim_ret, wave);
         if (!ahead2) {
@@ -1122,21 +1106,16 @@ hipError_t launch_recompute_gu_bf16(const uint16_t* A, const uint16_t* wg, const
 }  // namespace moe
 
 #ifdef MOE_PHASE_PROBE
-static_assert(MOE_PROBE_FIELDS == moe::kProbeFields && MOE_PROBE_KINDS == 3, "probe layout");
-
-extern "C" __attribute__((visibility("default"))) int moe_probe_phases(unsigned long long* out, int reset)
+int moe::probe_read_bf16(unsigned long long* out, int reset)
 {
-    // the launches already enqueued are the ones counted
-    if (hipDeviceSynchronize() != hipSuccess)
-        return 1;
     if (out != nullptr &&
-        hipMemcpyFromSymbol(out, HIP_SYMBOL(moe::g_phase), sizeof(moe::g_phase)) != hipSuccess)
+        hipMemcpyFromSymbol(out, HIP_SYMBOL(g_phase), sizeof(g_phase)) != hipSuccess)
         return 1;
     if (reset) {
-        const unsigned long long zero[3 * moe::kProbeFields] = {};
-        if (hipMemcpyToSymbol(HIP_SYMBOL(moe::g_phase), zero, sizeof(zero)) != hipSuccess)
+        const unsigned long long zero[kProbeKindsBf16 * kProbeFields] = {};
+        if (hipMemcpyToSymbol(HIP_SYMBOL(g_phase), zero, sizeof(zero)) != hipSuccess)
             return 1;
     }
-    return hipDeviceSynchronize() != hipSuccess;
+    return 0;
 }
 #endif

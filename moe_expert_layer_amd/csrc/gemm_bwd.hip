@@ -46,6 +46,17 @@ constexpr int kSmemBytes = 2 * kStageBytes;    // 64 KiB
 
 enum Epi { kEpiDown = 0, kEpiGateUp = 1, kEpiWgrad = 2 };
 
+#ifdef MOE_PHASE_PROBE
+// Per-task phase timing of the LDS-DMA kernels below, compiled only into the probe library (the
+// kernels do the same work): wave 0 of each workgroup sums cycle-counter differences in scalar
+// registers and lane 0 adds them to g_phase_bwd[kind] (0 weight gradients, 1 down dgrad, 2 gate/up
+// dgrad) after the workgroup's last task, outside the task loop and its barriers.
+__device__ unsigned long long g_phase_bwd[kProbeKindsBwd][kProbeFields];
+#define MOE_PROBE(...) __VA_ARGS__
+#else
+#define MOE_PROBE(...)
+#endif
+
 // Byte offset of element (row, k) in a [128 rows][64 k] bf16 tile, 16-byte chunks XOR-swizzled by row.
 __device__ __forceinline__ int tile_off(int row, int k)
 {
@@ -642,6 +653,10 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_dma(WgradArgs g)
     };
 
     // tasks claimed two ahead (claim_issue): t's successor is in the claim word at every top barrier
+    MOE_PROBE(unsigned long long pr[kProbeFields] = {};
+              const unsigned long long pr_k0 = __builtin_readcyclecounter();
+              const unsigned long long pr_r0 = __builtin_amdgcn_s_memrealtime();
+              unsigned long long pr_t = pr_k0, pr_b = 0, pr_k = 0, pr_s = 0, pr_u = 0;)
     int t = claim_task(claimed, g.task_ctr, xcd, blk, wave, lane);
     claim_task(claimed, g.task_ctr, xcd, blk, wave, lane);
     if (t < total)
@@ -659,14 +674,20 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_dma(WgradArgs g)
         const int ci = __builtin_amdgcn_readfirstlane(*claimed);
         const int t_next = ((ci / blk) * kXcdCount + xcd) * blk + ci % blk;
         const int claim_ret = claim_issue(g.task_ctr, xcd, wave, lane);    // the task after t_next
+        MOE_PROBE(pr_b = __builtin_readcyclecounter(); pr[kProbeWait] += pr_b - pr_t;)
         k_loop(acc, cp, ln, KT, g.lda, g.ldb);
+        MOE_PROBE(pr_k = __builtin_readcyclecounter(); pr[kProbeLoop] += pr_k - pr_b;
+                  pr[kProbeLoopFull] += pr_k - pr_b; ++pr[kProbeTasks]; ++pr[kProbeTasksFull];
+                  pr[kProbeSteps] += KT;)
         const int claim_after = claim_value(claim_ret, wave);
         const int de = e, dm0 = m0, dn0 = n0;
         t = t_next;
         // every wave is past its last read of this task's stages (and of the claim word)
         __syncthreads();
+        MOE_PROBE(pr_s = __builtin_readcyclecounter(); pr[kProbeSync] += pr_s - pr_k;)
         if (t < total)
             setup(t);
+        MOE_PROBE(pr_u = __builtin_readcyclecounter(); pr[kProbeSetup] += pr_u - pr_s;)
         float* C = g.c + static_cast<int64_t>(de) * g.Mo * g.No;
 #pragma unroll
         for (int i = 0; i < kTM; ++i) {
@@ -682,7 +703,18 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_dma(WgradArgs g)
         }
         if (wave == 0)
             *claimed = claim_after;
+        MOE_PROBE(pr_t = __builtin_readcyclecounter(); pr[kProbeEpilogue] += pr_t - pr_u;)
     }
+#ifdef MOE_PHASE_PROBE
+    if (wave == 0 && lane == 0) {
+        pr[kProbeTotal] = __builtin_readcyclecounter() - pr_k0;
+        pr[kProbeRealtime] = __builtin_amdgcn_s_memrealtime() - pr_r0;
+        pr[kProbeWorkgroups] = 1;
+#pragma unroll
+        for (int q = 0; q < kProbeFields; ++q)
+            atomicAdd(&g_phase_bwd[0][q], pr[q]);
+    }
+#endif
 }
 
 }  // namespace tn
@@ -945,6 +977,10 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_dma(BwdArgs g, int32_t* __r
     };
 
     // tasks claimed two ahead (claim_issue): t's successor is in the claim word at every top barrier
+    MOE_PROBE(unsigned long long pr[kProbeFields] = {};
+              const unsigned long long pr_k0 = __builtin_readcyclecounter();
+              const unsigned long long pr_r0 = __builtin_amdgcn_s_memrealtime();
+              unsigned long long pr_t = pr_k0, pr_b = 0, pr_k = 0, pr_s = 0, pr_u = 0;)
     int t = claim_task(claimed, task_ctr, xcd, blk, wave, lane);
     claim_task(claimed, task_ctr, xcd, blk, wave, lane);
     if (t < total)
@@ -962,14 +998,20 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_dma(BwdArgs g, int32_t* __r
         const int ci = __builtin_amdgcn_readfirstlane(*claimed);
         const int t_next = ((ci / blk) * kXcdCount + xcd) * blk + ci % blk;
         const int claim_ret = claim_issue(task_ctr, xcd, wave, lane);    // the task after t_next
+        MOE_PROBE(pr_b = __builtin_readcyclecounter(); pr[kProbeWait] += pr_b - pr_t;)
         k_loop(acc, cp, ln, KT);
+        MOE_PROBE(pr_k = __builtin_readcyclecounter(); pr[kProbeLoop] += pr_k - pr_b; ++pr[kProbeTasks];
+                  pr[kProbeSteps] += KT;
+                  if (tile.row_end - tile.row_begin == BM) { pr[kProbeLoopFull] += pr_k - pr_b; ++pr[kProbeTasksFull]; })
         const int claim_after = claim_value(claim_ret, wave);
         const MTile done = tile;
         const int dn0 = n0, dpart = part;
         t = t_next;
         __syncthreads();
+        MOE_PROBE(pr_s = __builtin_readcyclecounter(); pr[kProbeSync] += pr_s - pr_k;)
         if (t < total)
             setup(t);
+        MOE_PROBE(pr_u = __builtin_readcyclecounter(); pr[kProbeSetup] += pr_u - pr_s;)
         // Lane holds column lane % 32 of each 32 x 32 block, rows 8 (r / 4) + 4 (lane / 32) + r % 4.
         const int col0 = dn0 + 32 * kTN * wn + (lane & 31);
 #pragma unroll
@@ -1059,7 +1101,18 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_dma(BwdArgs g, int32_t* __r
         }
         if (wave == 0)
             *claimed = claim_after;
+        MOE_PROBE(pr_t = __builtin_readcyclecounter(); pr[kProbeEpilogue] += pr_t - pr_u;)
     }
+#ifdef MOE_PHASE_PROBE
+    if (wave == 0 && lane == 0) {
+        pr[kProbeTotal] = __builtin_readcyclecounter() - pr_k0;
+        pr[kProbeRealtime] = __builtin_amdgcn_s_memrealtime() - pr_r0;
+        pr[kProbeWorkgroups] = 1;
+#pragma unroll
+        for (int q = 0; q < kProbeFields; ++q)
+            atomicAdd(&g_phase_bwd[kEpi == kEpiDown ? 1 : 2][q], pr[q]);
+    }
+#endif
 }
 
 template <int kEpi, int kParts>
@@ -1375,3 +1428,18 @@ hipError_t launch_wgrad(const uint16_t* a_rows, int64_t lda, const uint16_t* b_r
 }
 
 }  // namespace moe
+
+#ifdef MOE_PHASE_PROBE
+int moe::probe_read_bwd(unsigned long long* out, int reset)
+{
+    if (out != nullptr &&
+        hipMemcpyFromSymbol(out, HIP_SYMBOL(g_phase_bwd), sizeof(g_phase_bwd)) != hipSuccess)
+        return 1;
+    if (reset) {
+        const unsigned long long zero[kProbeKindsBwd * kProbeFields] = {};
+        if (hipMemcpyToSymbol(HIP_SYMBOL(g_phase_bwd), zero, sizeof(zero)) != hipSuccess)
+            return 1;
+    }
+    return 0;
+}
+#endif

@@ -236,4 +236,29 @@ hipError_t launch_mx_encode_bf16_rows(const uint16_t* x, int64_t T, int64_t H, c
 hipError_t launch_mx_epilogue_probe(const float* v, int64_t rows, int64_t cols, bool large_tiles,
                                    uint8_t* codes, uint8_t* scales, hipStream_t s);
 
+#ifdef MOE_PHASE_PROBE
+// The probe build's per-task cycle sums (one row of kProbeFields per kernel kind; the layout of
+// moe_probe_phases).  Kinds 0 fc2, 1 fc1, 2 the backward's recompute (gemm_bf16.hip); 3 weight
+// gradients, 4 down dgrad, 5 gate/up dgrad (gemm_bwd.hip).
+enum ProbeField {
+    kProbeWait,           // from the previous epilogue's end (or the kernel's start) past the top barrier
+    kProbeLoop,           // K loops
+    kProbeLoopFull,       // K loops of full-height, full-width tasks
+    kProbeSync,           // after the K loop: the claim's result and the barrier that ends the loop
+    kProbeSetup,          // the next task's setup (its first copies)
+    kProbeEpilogue,       // the epilogue
+    kProbeTasks,
+    kProbeTasksFull,
+    kProbeTotal,          // cycles from the kernel's start to the workgroup's end
+    kProbeRealtime,       // the same span on the 100 MHz real-time counter
+    kProbeWorkgroups,
+    kProbeSteps,          // K steps of 32 over all tasks
+    kProbeFields
+};
+constexpr int kProbeKindsBf16 = 3, kProbeKindsBwd = 3;
+// Copy one file's sums into out (unless null), then zero them when reset is set.
+int probe_read_bf16(unsigned long long* out, int reset);
+int probe_read_bwd(unsigned long long* out, int reset);
+#endif
+
 }  // namespace moe
