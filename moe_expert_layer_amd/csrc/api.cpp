@@ -722,8 +722,13 @@ MOE_API moe_status moe_expert_backward(const moe_problem* p, const void* x, cons
         }
         // g = x_perm Wg[e], u = x_perm Wu[e]: the plain grouped GEMM with K = H and N = F
         if (saved_gu == nullptr) {
+            // the large-tile kernel reads each row from x through perm, as the forward's fc1 does:
+            // a token's row then serves its k slots from the caches (x_perm is k times larger)
+            const bool gather = L.bm_r == 256;
             LAUNCH(s, "recompute_gu",
-                   launch_recompute_gu_bf16(x_perm, wg, wu, at<uint16_t>(ws, L.g), at<uint16_t>(ws, L.u),
+                   launch_recompute_gu_bf16(gather ? static_cast<const uint16_t*>(x) : x_perm,
+                                            gather ? perm : nullptr, static_cast<int>(k), wg, wu,
+                                            at<uint16_t>(ws, L.g), at<uint16_t>(ws, L.u),
                                             tiles_run != nullptr ? tiles_run : tiles_r,
                                             tiles_run != nullptr ? tcount + 4 : tcount, H, F, task_ctr, s));
         }

@@ -1083,18 +1083,20 @@ hipError_t launch_fc2_bf16(const uint16_t* h, const uint16_t* wd, uint16_t* y, c
     return hipGetLastError();
 }
 
-hipError_t launch_recompute_gu_bf16(const uint16_t* A, const uint16_t* wg, const uint16_t* wu,
-                                    uint16_t* g, uint16_t* u, const MTile* tiles,
-                                    const int32_t* tile_count, int64_t H, int64_t F, int32_t* task_ctr,
-                                    hipStream_t s)
+hipError_t launch_recompute_gu_bf16(const uint16_t* A, const int32_t* gather, int gather_k,
+                                    const uint16_t* wg, const uint16_t* wu, uint16_t* g, uint16_t* u,
+                                    const MTile* tiles, const int32_t* tile_count, int64_t H, int64_t F,
+                                    int32_t* task_ctr, hipStream_t s)
 {
     const int cu = device_info().cu_count;
+    if (gather != nullptr && !use_big(H, F))
+        return hipErrorInvalidValue;              // only the large-tile kernel gathers rows
     if (use_big(H, F)) {
         if (hipError_t e = ensure_smem_limits(); e != hipSuccess)
             return e;
         big::grouped_gemm_bf16_dma<true, 1><<<dim3(cu), dim3(big::kThreads), kBigSmem, s>>>(
             A, wg, wu, nullptr, tiles, tile_count, static_cast<int>(H), static_cast<int>(F), nullptr,
-            task_ctr, nullptr, 1, g, u);
+            task_ctr, gather, gather_k, g, u);
     } else {
         FC1_SMALL<<<dim3(2 * cu), dim3(Fc1Small::kThreads), Fc1Small::kSmemBytes, s>>>(
             A, wg, wu, nullptr, tiles, tile_count, static_cast<int>(H), static_cast<int>(F), nullptr,

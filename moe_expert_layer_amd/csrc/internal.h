@@ -149,10 +149,12 @@ hipError_t launch_fc2_bf16(const uint16_t* h, const uint16_t* wd, uint16_t* y, c
 
 // g = A Wg[e], u = A Wu[e] as bf16 [M, F]: the fc1 kernels with h not stored (the backward's
 // recompute of g and u, launched under its own kernel name).  Row tiles of bf16_row_tile(H, F) rows.
-hipError_t launch_recompute_gu_bf16(const uint16_t* A, const uint16_t* wg, const uint16_t* wu,
-                                    uint16_t* g, uint16_t* u, const MTile* tiles,
-                                    const int32_t* tile_count, int64_t H, int64_t F, int32_t* task_ctr,
-                                    hipStream_t s);
+// gather (large tiles only, may be null) as for launch_fc1_bf16: permuted row p of A is row
+// gather[p] / gather_k of A.
+hipError_t launch_recompute_gu_bf16(const uint16_t* A, const int32_t* gather, int gather_k,
+                                    const uint16_t* wg, const uint16_t* wu, uint16_t* g, uint16_t* u,
+                                    const MTile* tiles, const int32_t* tile_count, int64_t H, int64_t F,
+                                    int32_t* task_ctr, hipStream_t s);
 
 // gemm_f32.hip: float32 grouped GEMMs (plain FMA).
 hipError_t launch_fc1_f32(const float* A, const float* wg, const float* wu, float* h,
