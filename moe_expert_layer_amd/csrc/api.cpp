@@ -720,7 +720,7 @@ MOE_API moe_status moe_expert_backward(const moe_problem* p, const void* x, cons
             tiles_d = tiles_run;
             tcount_d = tcount + 4;
         }
-        // g = x_perm Wg[e], u = x_perm Wu[e]: the plain grouped GEMM with K = H and N = F
+        // g = x_perm Wg[e], u = x_perm Wu[e] (K = H, N = F): one launch of fc1's kernel, h not stored
         if (saved_gu == nullptr) {
             // the large-tile kernel reads each row from x through perm, as the forward's fc1 does:
             // a token's row then serves its k slots from the caches (x_perm is k times larger)
