@@ -313,8 +313,9 @@ __global__ __launch_bounds__(kWM * kWN * 64, kMinBlocks) void grouped_gemm_bf16(
 #ifdef MOE_PHASE_PROBE
 // Per-task phase timing, compiled only into the probe library (timestamps only; every kernel does
 // the same work as in the product library).  Wave 0 of each workgroup reads the cycle counter at
-// the points of its task loop marked MOE_PROBE and keeps per-workgroup sums in scalar registers; after its last task lane 0 adds them to g_phase[kind] (kind 0 fc2, 1 fc1, 2 the
-// backward's recompute), outside the task loop and its barriers.
+// the points of its task loop marked MOE_PROBE and keeps per-workgroup sums in scalar registers;
+// after its last task lane 0 adds them to g_phase[kind] (kind 0 fc2, 1 fc1, 2 the backward's
+// recompute), outside the task loop and its barriers.
 __device__ unsigned long long g_phase[kProbeKindsBf16][kProbeFields];
 #define MOE_PROBE(...) __VA_ARGS__
 #else
