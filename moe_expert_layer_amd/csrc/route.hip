@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void route_scatter_kernel(
 // unchunked calls only) keeps each group as one run of R = ceil(rows / bm) tiles of near-equal
 // height (their 32-row blocks differ by at most one): the tasks that share a weight strip then
 // take equal time, so the workgroups of an XCD stay in step and share the strip in its L2.
-// One workgroup; groups are handled 1024 at a time.
+// One workgroup per table (two when the in-run table is asked for); groups are handled 1024 at a time.
 __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ group_expert, int G, int E,
     int64_t M, int64_t chunk, int bm, MTile* __restrict__ tiles_main, int max_tiles, int32_t* __restrict__ tile_count,
@@ -211,7 +211,11 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
     int col_tiles, int32_t* __restrict__ task_ctr, int32_t* __restrict__ status, int write_status,
     MTile* __restrict__ tiles_in_run, int32_t* __restrict__ count_in_run)
 {
-    if (task_ctr != nullptr && threadIdx.x < 2 * kXcdCount)
+    // one workgroup per layout: 0 the table (unchunked: partial tails last, sorted; chunked: row
+    // order), 1 (unchunked, when asked for; the launch's second workgroup) every group as one run
+    // of balanced tiles.  Workgroup 0 alone clears the counters and writes the status.
+    const int layout = blockIdx.x;
+    if (layout == 0 && task_ctr != nullptr && threadIdx.x < 2 * kXcdCount)
         task_ctr[threadIdx.x] = 0;
     __shared__ int buf[2 * (kScanThreads / 64)];
     __shared__ int carry;
@@ -224,24 +228,15 @@ __global__ __launch_bounds__(kScanThreads) void build_tiles_kernel(
         full_tiles = 0;
         tall_tails = 0;
     }
-    if (chunk_tiles != nullptr)
+    if (layout == 0 && chunk_tiles != nullptr)
         for (int c = threadIdx.x; c < num_chunks; c += kScanThreads) {
             chunk_tiles[c] = 0;
             chunk_done[c] = 0;
         }
     __syncthreads();
-    // layout 0: the table (unchunked: partial tails last, sorted; chunked: row order); layout 1
-    // (unchunked, when asked for): every group as one run of balanced tiles
-    const int layouts = tiles_in_run != nullptr && num_chunks <= 1 ? 2 : 1;
-    for (int layout = 0; layout < layouts; ++layout) {
+    {
         MTile* const tiles = layout == 0 ? tiles_main : tiles_in_run;
         const bool tails_last = layout == 0 && num_chunks <= 1;
-        if (layout == 1) {
-            __syncthreads();
-            if (threadIdx.x == 0)
-                carry = 0;
-            __syncthreads();
-        }
         for (int pass = 0; pass < (tails_last ? 2 : 1); ++pass) {
             if (pass == 1 && threadIdx.x == 0)
                 full_tiles = carry;                   // read by thread 0 only, after the last barrier
@@ -419,7 +414,8 @@ hipError_t launch_build_tiles(const int32_t* offsets, const int32_t* group_exper
                               int32_t* status, bool write_status, hipStream_t s,
                               MTile* tiles_in_run, int32_t* count_in_run)
 {
-    build_tiles_kernel<<<dim3(1), dim3(kScanThreads), 0, s>>>(
+    const unsigned layouts = tiles_in_run != nullptr && num_chunks <= 1 ? 2 : 1;
+    build_tiles_kernel<<<dim3(layouts), dim3(kScanThreads), 0, s>>>(
         offsets, group_expert, static_cast<int>(G), static_cast<int>(E), M, chunk, bm, tiles,
         static_cast<int>(max_tiles), tile_count, chunk_tiles, chunk_done,
         static_cast<int>(num_chunks), col_tiles, task_ctr, status, write_status ? 1 : 0,
