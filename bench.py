@@ -529,16 +529,18 @@ EXTRA_WORKLOADS = ("ep_rank_bf16", "finegrained_bf16", "mxfp8")
 
 PROBE_FIELDS = ("wait", "loop", "loop_full", "sync", "setup", "epilogue", "tasks", "tasks_full",
                 "total", "realtime", "workgroups", "steps")
-PROBE_KINDS = ("fc2_bf16", "fc1_bf16", "recompute_gu", "wgrad", "dgrad_down", "dgrad_gate_up")
+PROBE_KINDS = ("fc2_bf16", "fc1_bf16", "recompute_gu", "wgrad", "dgrad_down", "dgrad_gate_up",
+               "fc2_mx", "fc1_mx")
 
 
 def phase_probe(args, torch, mel, synth, dv, dev):
     """Per-task phases of the large-tile GEMM launches, from the probe library's cycle stamps: the
     forward (or the EP rank's grouped FFN) run --steps times after --warmup, each call after the
     cache flush the timed benchmark uses; then, for bf16 layer workloads and unless --skip-backward,
-    the backward (recomputing g and u) the same way.  Cycles are wave 0's counter cycles; a K step
-    of 32 issues 2 waves x 16 MFMAs x 32 cycles = 1024 cycles per SIMD, so loop_mfma_fraction is
-    (K steps x 1024) / K-loop cycles, over the full-height tasks where tasks differ in height."""
+    the backward (recomputing g and u) the same way.  Cycles are wave 0's counter cycles; a bf16 K
+    step (32) issues 2 waves x 16 MFMAs x 32 cycles and an MX one (64) 2 waves x 8 MFMAs x 64
+    cycles, 1024 cycles per SIMD either way, so loop_mfma_fraction is (K steps x 1024) / K-loop
+    cycles, over the full-height tasks where tasks differ in height."""
     import ctypes
     lib = mel.library()
     probe = lib.moe_probe_phases
@@ -558,13 +560,18 @@ def phase_probe(args, torch, mel, synth, dv, dev):
         legs.append(("forward", lambda: mel.grouped_ffn(rows, offs, gexp, wg, wu, wd, head_m_size=head, out=out)))
     else:
         inp = synth.make_workload(args.workload)
-        if inp.dtype != "bf16":
-            sys.exit("--phase-probe covers the bf16 GEMMs: pick a bf16 workload")
+        if inp.dtype not in ("bf16", "mxfp8"):
+            sys.exit("--phase-probe covers the bf16 and MX-FP8 GEMMs: pick such a workload")
         d = dv.layer(inp, dev)
         out = torch.empty((inp.T, inp.H), dtype=torch.bfloat16, device=dev)
-        legs.append(("forward", lambda: mel.expert_forward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids,
-                                                           d.probs, head_m_size=head, out=out)))
-        if not args.skip_backward:
+        if inp.dtype == "mxfp8":
+            legs.append(("forward", lambda: mel.expert_forward_mx(
+                d.x, d.x_scale, d.w_gate, d.wg_scale, d.w_up, d.wu_scale, d.w_down, d.wd_scale,
+                d.expert_ids, d.probs, head_m_size=head, out=out)))
+        else:
+            legs.append(("forward", lambda: mel.expert_forward(d.x, d.w_gate, d.w_up, d.w_down, d.expert_ids,
+                                                               d.probs, head_m_size=head, out=out)))
+        if not args.skip_backward and inp.dtype == "bf16":
             dout = dv.tensor(synth.make_dout(inp), dev)
             bws = torch.empty(mel.backward_workspace_size(mel.problem(inp.T, inp.H, inp.F, inp.E, inp.k, mel.BF16)),
                               dtype=torch.uint8, device=dev)

@@ -1143,7 +1143,7 @@ MOE_API moe_status moe_route_noalloc(const int32_t* expert_ids, int64_t T, int64
 #include "moe_expert_layer_probe.h"
 
 static_assert(MOE_PROBE_FIELDS == moe::kProbeFields &&
-                  MOE_PROBE_KINDS == moe::kProbeKindsBf16 + moe::kProbeKindsBwd,
+                  MOE_PROBE_KINDS == moe::kProbeKindsBf16 + moe::kProbeKindsBwd + moe::kProbeKindsMx,
               "probe layout");
 
 MOE_API int moe_probe_phases(unsigned long long* out, int reset)
@@ -1155,6 +1155,11 @@ MOE_API int moe_probe_phases(unsigned long long* out, int reset)
         return 1;
     if (moe::probe_read_bwd(out != nullptr ? out + moe::kProbeKindsBf16 * moe::kProbeFields : nullptr,
                             reset) != 0)
+        return 1;
+    if (moe::probe_read_mx(out != nullptr
+                               ? out + (moe::kProbeKindsBf16 + moe::kProbeKindsBwd) * moe::kProbeFields
+                               : nullptr,
+                           reset) != 0)
         return 1;
     return hipDeviceSynchronize() != hipSuccess;
 }

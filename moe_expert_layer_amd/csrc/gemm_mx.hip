@@ -399,6 +399,17 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_mx(
 // 2e + i / 8, byte i % 8, so 16 source lanes reading 8 rows x 16 columns hand every lane 8
 // consecutive k of one column).  Block scales ride in their own two-slot LDS ring, one slot per 8
 // K steps (16 scale blocks): A scales [256 rows][16] and weight scales [16][columns].
+#ifdef MOE_PHASE_PROBE
+// Per-task phase timing of the large-tile kernel below, compiled only into the probe library (the
+// kernel does the same work): wave 0 of each workgroup sums cycle-counter differences at the
+// points marked MOE_PROBE in scalar registers, and lane 0 adds them to g_phase_mx[kind] (0 fc2,
+// 1 fc1) after the workgroup's last task, outside the task loop and its barriers.
+__device__ unsigned long long g_phase_mx[kProbeKindsMx][kProbeFields];
+#define MOE_PROBE(...) __VA_ARGS__
+#else
+#define MOE_PROBE(...)
+#endif
+
 namespace big {
 
 constexpr int kWM = 4, kWN = 2, kTM = 2, kTN = 4;
@@ -965,6 +976,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
     // per workgroup (t's successor is in the claim word at every top barrier, and its tile entry is
     // loaded during t's K loop), else one ahead, read after the K loop
     const bool ahead2 = gather != nullptr || total >= 4 * static_cast<int>(gridDim.x);
+    MOE_PROBE(unsigned long long pr[kProbeFields] = {};
+              const unsigned long long pr_k0 = __builtin_readcyclecounter();
+              const unsigned long long pr_r0 = __builtin_amdgcn_s_memrealtime();
+              unsigned long long pr_t = pr_k0, pr_b = 0, pr_k = 0, pr_s = 0, pr_u = 0;)
     int t = claim_task(claimed, task_ctr, xcd, blk, wave, lane);
     if (ahead2)
         claim_task(claimed, task_ctr, xcd, blk, wave, lane);
@@ -993,6 +1008,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
             step_barrier<top_wait<true>()>();
         else
             step_barrier<top_wait<false>()>();
+        MOE_PROBE(pr_b = __builtin_readcyclecounter(); pr[kProbeWait] += pr_b - pr_t;)
         int t_next = total;
         MTile tile_next{};
         int nt_next = 0;
@@ -1013,6 +1029,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
             mx_k_loop<kGated, 1, true>(acc, la, cp, a_voff, b_voff, sc_voff, KT, N_w);
         else
             mx_k_loop<kGated, 2, true>(acc, la, cp, a_voff, b_voff, sc_voff, KT, N_w);
+        MOE_PROBE(pr_k = __builtin_readcyclecounter(); pr[kProbeLoop] += pr_k - pr_b; ++pr[kProbeTasks];
+                  pr[kProbeSteps] += KT;
+                  if (rows == BM) { pr[kProbeLoopFull] += pr_k - pr_b; ++pr[kProbeTasksFull]; })
         const int claim_after = claim_value(claim_ret, wave);
         if (!ahead2) {
             if (wave == 0)
@@ -1025,12 +1044,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
         const int done_n0 = n0;
         t = t_next;
         __syncthreads();
+        MOE_PROBE(pr_s = __builtin_readcyclecounter(); pr[kProbeSync] += pr_s - pr_k;)
         if (t < total) {
             if (ahead2)
                 setup_from(tile_next, nt_next);
             else
                 setup(t);
         }
+        MOE_PROBE(pr_u = __builtin_readcyclecounter(); pr[kProbeSetup] += pr_u - pr_s;)
         const uint32_t stg = lds0 + kOutBase + wave * kOutWaveBytes;
         if constexpr (kGated)
             store_h<true>(acc, Cq, Cq_sc, done, done_n0, N_out, stg, wm, wn, lane);
@@ -1042,7 +1063,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
         // the word)
         if (ahead2 && wave == 0)
             *claimed = claim_after;
+        MOE_PROBE(pr_t = __builtin_readcyclecounter(); pr[kProbeEpilogue] += pr_t - pr_u;)
     }
+#ifdef MOE_PHASE_PROBE
+    if (wave == 0 && lane == 0) {
+        pr[kProbeTotal] = __builtin_readcyclecounter() - pr_k0;
+        pr[kProbeRealtime] = __builtin_amdgcn_s_memrealtime() - pr_r0;
+        pr[kProbeWorkgroups] = 1;
+#pragma unroll
+        for (int q = 0; q < kProbeFields; ++q)
+            atomicAdd(&g_phase_mx[kGated ? 1 : 0][q], pr[q]);
+    }
+#endif
 }
 
 // The fc1 epilogue's encoder on caller values: workgroup (x, y) takes output columns [128 x, 128 x +
@@ -1239,3 +1271,18 @@ hipError_t launch_fc2_mx(const uint8_t* h, const uint8_t* h_scale, const uint8_t
 }
 
 }  // namespace moe
+
+#ifdef MOE_PHASE_PROBE
+int moe::probe_read_mx(unsigned long long* out, int reset)
+{
+    if (out != nullptr &&
+        hipMemcpyFromSymbol(out, HIP_SYMBOL(g_phase_mx), sizeof(g_phase_mx)) != hipSuccess)
+        return 1;
+    if (reset) {
+        const unsigned long long zero[kProbeKindsMx * kProbeFields] = {};
+        if (hipMemcpyToSymbol(HIP_SYMBOL(g_phase_mx), zero, sizeof(zero)) != hipSuccess)
+            return 1;
+    }
+    return 0;
+}
+#endif

@@ -241,7 +241,7 @@ hipError_t launch_mx_epilogue_probe(const float* v, int64_t rows, int64_t cols, 
 #ifdef MOE_PHASE_PROBE
 // The probe build's per-task cycle sums (one row of kProbeFields per kernel kind; the layout of
 // moe_probe_phases).  Kinds 0 fc2, 1 fc1, 2 the backward's recompute (gemm_bf16.hip); 3 weight
-// gradients, 4 down dgrad, 5 gate/up dgrad (gemm_bwd.hip).
+// gradients, 4 down dgrad, 5 gate/up dgrad (gemm_bwd.hip); 6 MX fc2, 7 MX fc1 (gemm_mx.hip).
 enum ProbeField {
     kProbeWait,           // from the previous epilogue's end (or the kernel's start) past the top barrier
     kProbeLoop,           // K loops
@@ -257,10 +257,11 @@ enum ProbeField {
     kProbeSteps,          // K steps of 32 over all tasks
     kProbeFields
 };
-constexpr int kProbeKindsBf16 = 3, kProbeKindsBwd = 3;
+constexpr int kProbeKindsBf16 = 3, kProbeKindsBwd = 3, kProbeKindsMx = 2;
 // Copy one file's sums into out (unless null), then zero them when reset is set.
 int probe_read_bf16(unsigned long long* out, int reset);
 int probe_read_bwd(unsigned long long* out, int reset);
+int probe_read_mx(unsigned long long* out, int reset);
 #endif
 
 }  // namespace moe

@@ -14,7 +14,7 @@ from synth import device as dv
 
 pytestmark = pytest.mark.gpu
 
-FIELDS, KINDS = 12, 6           # include/moe_expert_layer_probe.h
+FIELDS, KINDS = 12, 8           # include/moe_expert_layer_probe.h
 TASKS = 6                       # field index of the task count
 
 
@@ -60,5 +60,5 @@ def test_probe_build_matches_the_product_and_counts_tasks():
     buf = (ctypes.c_ulonglong * (KINDS * FIELDS))()
     assert probe.moe_probe_phases(ctypes.cast(buf, ctypes.c_void_p), 1) == 0
     tasks = [buf[kind * FIELDS + TASKS] for kind in range(KINDS)]
-    # fc2, fc1, recompute, weight gradients, down dgrad, gate/up dgrad all ran tasks
-    assert all(t > 0 for t in tasks), tasks
+    # fc2, fc1, recompute, weight gradients, down dgrad, gate/up dgrad all ran tasks; MX none
+    assert all(t > 0 for t in tasks[:6]) and tasks[6:] == [0, 0], tasks
