@@ -552,18 +552,6 @@ struct MxFrags {
     int sa[kTM];
 };
 
-template <int NB>
-__device__ __forceinline__ void mfma_pair(f32x16_t (&acc)[kTM][kTN], const MxFrags& A, const i32x8_t (&b)[2],
-                                          const int (&sb)[2], int j0)
-{
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-            acc[i][j0 + jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                A.a[i], b[jj], acc[i][j0 + jj], 0, 0, 0, A.sa[i], 0, sb[jj]);
-}
-
 // Fragments of K step position p (stage p % 4, scale slot P): A row blocks and their scales.
 template <int NB, int P, int p>
 __device__ __forceinline__ void read_a_frags(MxFrags& A, const LaneAddr& la)
@@ -618,12 +606,153 @@ constexpr int mx_wait_no_a()
     return (!kLast || p + 2 < kUnitSteps ? kBCopies : 0) + (!kLast || p + 3 < kUnitSteps ? kBCopies : 0);
 }
 
+// Copy C of one K step's copy list (the scales of the block it opens into slot Q when kScale, its
+// weights into B stage SB when SB >= 0, the A of a pair into pair stage QA when QA >= 0, in that
+// order; the copy waits count on that order).  The sources move on in mx_advance, after the list.
+template <bool kScale, int Q, int SB, int QA>
+constexpr int mx_copy_count()
+{
+    return (kScale ? 1 : 0) + (SB >= 0 ? kBCopies : 0) + (QA >= 0 ? kACopies : 0);
+}
+template <bool kScale, int Q, int SB, int QA, int C>
+__device__ __forceinline__ void mx_copy_one(const MxCopy& c, const uint32_t (&a_voff)[kACopies],
+                                            const uint32_t (&b_voff)[kBCopies], uint32_t sc_voff)
+{
+    constexpr int c0 = kScale ? 1 : 0, c1 = c0 + (SB >= 0 ? kBCopies : 0);
+    if constexpr (C < c0)
+        lds_copy16(c.sc, sc_voff, c.sc_lds + Q * kScSlotBytes);
+    else if constexpr (C < c1)
+        lds_copy16(c.b, b_voff[C - c0], c.b_lds + SB * kBBytes + (C - c0) * 1024);
+    else
+        lds_copy16(c.a, a_voff[C - c1], c.a_lds + QA * kAPairBytes + (C - c1) * 1024);
+}
+template <bool kScale, int Q, int SB, int QA, int C0, int... Is>
+__device__ __forceinline__ void mx_copies_impl(std::integer_sequence<int, Is...>, const MxCopy& c,
+                                               const uint32_t (&a_voff)[kACopies],
+                                               const uint32_t (&b_voff)[kBCopies], uint32_t sc_voff)
+{
+    (mx_copy_one<kScale, Q, SB, QA, C0 + Is>(c, a_voff, b_voff, sc_voff), ...);
+}
+// Copies C0 .. C1 - 1 of the list.
+template <bool kScale, int Q, int SB, int QA, int C0, int C1>
+__device__ __forceinline__ void mx_copies(const MxCopy& c, const uint32_t (&a_voff)[kACopies],
+                                          const uint32_t (&b_voff)[kBCopies], uint32_t sc_voff)
+{
+    mx_copies_impl<kScale, Q, SB, QA, C0>(std::make_integer_sequence<int, C1 - C0>{}, c, a_voff, b_voff,
+                                          sc_voff);
+}
+template <bool kScale, int SB, int QA>
+__device__ __forceinline__ void mx_advance(MxCopy& c, int64_t N_w)
+{
+    if constexpr (kScale)
+        c.sc += c.sc_step;
+    if constexpr (SB >= 0)
+        c.b += BK * N_w;
+    if constexpr (QA >= 0)
+        c.a += 2 * BK;
+}
+
+// Fragment read R of the next step (K step position p, scale slot P), in the order its first MFMAs
+// consume them: R = 0 A row block 0, R = 1, 2 weight blocks 0, 1, R = 2 + i (i >= 1) A row block i.
+template <bool kGated, int NB, int P, int p, int R>
+__device__ __forceinline__ void mx_read_next(MxFrags& A, i32x8_t (&b01)[2], int (&sb01)[2], const LaneAddr& la)
+{
+    using L = BLayout<kGated>;
+    constexpr int S = p % kStages;
+    if constexpr (R == 1 || R == 2) {
+        constexpr int jj = R - 1;
+        b01[jj] = read_b<L::kRowBytes>(la.b[jj] + S * kBBytes);
+        sb01[jj] = read_u8(la.bsc + bsc_off<kGated>(jj) + P * kScSlotBytes + 2 * p * L::kRowBytes);
+    } else {
+        constexpr int i = R == 0 ? 0 : R - 2;
+        constexpr int kRowBlock = kWM * 32 * 128;
+        A.a[i] = read_a(la.a[S % 2][0] + (S / 2) * kAPairBytes + i * kRowBlock,
+                        la.a[S % 2][1] + (S / 2) * kAPairBytes + i * kRowBlock);
+        A.sa[i] = read_u8(la.asc + P * kScSlotBytes + row_block<kWM>(i, 0) * 16 + 2 * p);
+    }
+}
+template <bool kGated, int NB, int P, int p, int R0, int... Is>
+__device__ __forceinline__ void mx_reads_impl(std::integer_sequence<int, Is...>, MxFrags& A, i32x8_t (&b01)[2],
+                                              int (&sb01)[2], const LaneAddr& la)
+{
+    (mx_read_next<kGated, NB, P, p, R0 + Is>(A, b01, sb01, la), ...);
+}
+
+// Weight block 2 + jj of the current step (position p, slot P).
+template <bool kGated, int P, int p, int jj>
+__device__ __forceinline__ void mx_read_b23(i32x8_t (&b23)[2], int (&sb23)[2], const LaneAddr& la)
+{
+    using L = BLayout<kGated>;
+    constexpr int S = p % kStages;
+    b23[jj] = read_b<L::kRowBytes>(la.b[2 + jj] + S * kBBytes);
+    sb23[jj] = read_u8(la.bsc + bsc_off<kGated>(2 + jj) + P * kScSlotBytes + 2 * p * L::kRowBytes);
+}
+
+__device__ __forceinline__ void mx_mfma(f32x16_t& acc, const i32x8_t& a, int sa, const i32x8_t& b, int sb)
+{
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, sa, 0, sb);
+}
+
+// Slot m before the barrier: MFMA m on weight blocks 0-1 (row block m / 2, block m % 2), then, in
+// the first two slots, the read of weight block 2 + m of the current step.
+template <bool kGated, int NB, int P, int q, int m>
+__device__ __forceinline__ void mx_pre_slot(f32x16_t (&acc)[kTM][kTN], const MxFrags& Acur,
+                                            const i32x8_t (&b01)[2], const int (&sb01)[2], i32x8_t (&b23)[2],
+                                            int (&sb23)[2], const LaneAddr& la)
+{
+    mx_mfma(acc[m / 2][m % 2], Acur.a[m / 2], Acur.sa[m / 2], b01[m % 2], sb01[m % 2]);
+    if constexpr (m < 2)
+        mx_read_b23<kGated, P, q, m>(b23, sb23, la);
+    __builtin_amdgcn_sched_barrier(0);
+}
+template <bool kGated, int NB, int P, int q, int... Ms>
+__device__ __forceinline__ void mx_pre_slots(std::integer_sequence<int, Ms...>, f32x16_t (&acc)[kTM][kTN],
+                                             const MxFrags& Acur, const i32x8_t (&b01)[2], const int (&sb01)[2],
+                                             i32x8_t (&b23)[2], int (&sb23)[2], const LaneAddr& la)
+{
+    (mx_pre_slot<kGated, NB, P, q, Ms>(acc, Acur, b01, sb01, b23, sb23, la), ...);
+}
+
+// Slot m after the barrier: MFMA m on weight blocks 2-3, then this slot's share of the step's
+// copies and of the next step's fragment reads (both spread over the first half of the slots, so
+// the reads land well before the next step's first MFMAs).
+template <bool kGated, int NB, int P, int q, int Pn, int qn, bool kScale, int Q, int SB, int QA, int m>
+__device__ __forceinline__ void mx_post_slot(f32x16_t (&acc)[kTM][kTN], const MxFrags& Acur, MxFrags& Anext,
+                                             const i32x8_t (&b23)[2], const int (&sb23)[2], i32x8_t (&b01)[2],
+                                             int (&sb01)[2], const LaneAddr& la, const MxCopy& cp,
+                                             const uint32_t (&a_voff)[kACopies],
+                                             const uint32_t (&b_voff)[kBCopies], uint32_t sc_voff)
+{
+    constexpr int M = 2 * NB, RF = M / 2 > 0 ? M / 2 : 1;
+    constexpr int NC = mx_copy_count<kScale, Q, SB, QA>(), NR = NB + 2;
+    mx_mfma(acc[m / 2][2 + m % 2], Acur.a[m / 2], Acur.sa[m / 2], b23[m % 2], sb23[m % 2]);
+    if constexpr (m < RF) {
+        mx_copies<kScale, Q, SB, QA, m * NC / RF, (m + 1) * NC / RF>(cp, a_voff, b_voff, sc_voff);
+        mx_reads_impl<kGated, NB, Pn, qn, m * NR / RF>(
+            std::make_integer_sequence<int, (m + 1) * NR / RF - m * NR / RF>{}, Anext, b01, sb01, la);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+template <bool kGated, int NB, int P, int q, int Pn, int qn, bool kScale, int Q, int SB, int QA, int... Ms>
+__device__ __forceinline__ void mx_post_slots(std::integer_sequence<int, Ms...>, f32x16_t (&acc)[kTM][kTN],
+                                              const MxFrags& Acur, MxFrags& Anext, const i32x8_t (&b23)[2],
+                                              const int (&sb23)[2], i32x8_t (&b01)[2], int (&sb01)[2],
+                                              const LaneAddr& la, const MxCopy& cp,
+                                              const uint32_t (&a_voff)[kACopies],
+                                              const uint32_t (&b_voff)[kBCopies], uint32_t sc_voff)
+{
+    (mx_post_slot<kGated, NB, P, q, Pn, qn, kScale, Q, SB, QA, Ms>(acc, Acur, Anext, b23, sb23, b01, sb01, la,
+                                                                  cp, a_voff, b_voff, sc_voff),
+     ...);
+}
+
 // K step kt at position p of a 16-step unit (stage p % 4, pair stage p % 4 / 2; scales of the
 // 8-step block in slot p / 8): the MFMAs of weight blocks 0-1 (fragments loaded during the
-// previous step) while the fragments of blocks 2-3 are read; the barrier after which step kt + 1
-// has landed (W copies may stay in flight; none when W < 0); the copies (weights and scales of
-// step kt + 4 when kCopyB, A of pair (kt + 3) / 2 when kCopyA); the next step's A and blocks 0-1
-// fragments; the MFMAs of blocks 2-3.
+// previous step), each followed by a share of the reads of blocks 2-3; the barrier after which
+// step kt + 1 has landed (W copies may stay in flight; none when W < 0); the MFMAs of blocks 2-3,
+// each followed by a share of the copies (scales and weights of step kt + 4 when kCopyB, A of pair
+// (kt + 3) / 2 when kCopyA) and of the next step's A and blocks 0-1 fragments.  Interleaving keeps
+// the matrix pipe fed while a step's copies and reads issue.
 template <bool kGated, int NB, int p, bool kCopyB, bool kCopyA, int W>
 __device__ __forceinline__ void mx_step(f32x16_t (&acc)[kTM][kTN], const MxFrags& Acur, MxFrags& Anext,
                                         i32x8_t (&b01)[2], int (&sb01)[2], i32x8_t (&b23)[2],
@@ -634,23 +763,23 @@ __device__ __forceinline__ void mx_step(f32x16_t (&acc)[kTM][kTN], const MxFrags
     constexpr int P = p / kScaleSteps, q = p % kScaleSteps;                  // slot, step in block
     constexpr int pn = (p + 1) % (2 * kScaleSteps);                          // the next step
     constexpr int Pn = pn / kScaleSteps, qn = pn % kScaleSteps;
-    if constexpr (NB > 0) {
-        __builtin_amdgcn_sched_barrier(0);
-        read_b_frags<kGated, P, q, 2>(b23, sb23, la);
-        mfma_pair<NB>(acc, Acur, b01, sb01, 0);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    constexpr bool kScale = kCopyB && q == 4;
+    constexpr int Q = 1 - P, SB = kCopyB ? p % kStages : -1, QA = kCopyA ? ((p + 3) / 2) % 2 : -1;
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NB > 0)
+        mx_pre_slots<kGated, NB, P, q>(std::make_integer_sequence<int, 2 * NB>{}, acc, Acur, b01, sb01, b23,
+                                       sb23, la);
     if constexpr (W >= 0)
         step_barrier<W>();
     __builtin_amdgcn_sched_barrier(0);
-    mx_issue<kCopyB && q == 4, 1 - P, kCopyB ? p % kStages : -1, kCopyA ? ((p + 3) / 2) % 2 : -1>(
-        cp, a_voff, b_voff, sc_voff, N_w);
-    if constexpr (NB > 0) {
-        // after the last step these read a stale stage whose fragments are never used
-        read_a_frags<NB, Pn, qn>(Anext, la);
-        mfma_pair<NB>(acc, Acur, b23, sb23, 2);
-        read_b_frags<kGated, Pn, qn, 0>(b01, sb01, la);
-    }
+    // after the last step the reads below read a stale stage whose fragments are never used
+    if constexpr (NB > 0)
+        mx_post_slots<kGated, NB, P, q, Pn, qn, kScale, Q, SB, QA>(std::make_integer_sequence<int, 2 * NB>{},
+                                                                   acc, Acur, Anext, b23, sb23, b01, sb01, la,
+                                                                   cp, a_voff, b_voff, sc_voff);
+    else
+        mx_copies<kScale, Q, SB, QA, 0, mx_copy_count<kScale, Q, SB, QA>()>(cp, a_voff, b_voff, sc_voff);
+    mx_advance<kScale, SB, QA>(cp, N_w);
     __builtin_amdgcn_sched_barrier(0);
 }
 
