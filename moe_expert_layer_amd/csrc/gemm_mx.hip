@@ -688,9 +688,12 @@ __device__ __forceinline__ void mx_read_b23(i32x8_t (&b23)[2], int (&sb23)[2], c
     sb23[jj] = read_u8(la.bsc + bsc_off<kGated>(2 + jj) + P * kScSlotBytes + 2 * p * L::kRowBytes);
 }
 
+// Weights as the first operand: the accumulator block is the transposed 32 x 32 output block, so a
+// lane holds one output row (lane % 32) and four runs of four adjacent columns, 8 (r / 4) +
+// 4 (lane / 32) + r % 4 (both operands have the same register layout, scale bytes included).
 __device__ __forceinline__ void mx_mfma(f32x16_t& acc, const i32x8_t& a, int sa, const i32x8_t& b, int sb)
 {
-    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, sa, 0, sb);
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, acc, 0, 0, 0, sb, 0, sa);
 }
 
 // Slot m before the barrier: MFMA m on weight blocks 0-1 (row block m / 2, block m % 2), then, in
@@ -847,103 +850,92 @@ __device__ __forceinline__ void mx_k_loop(f32x16_t (&acc)[kTM][kTN], const LaneA
     mx_unit<kGated, NB, true, kA>(acc, A0, A1, b01, sb01, b23, sb23, la, cp, a_voff, b_voff, sc_voff, N_w);
 }
 
-// fc2 epilogue: bf16 rows through the wave's 2 KiB staging area in pieces of 16 rows x 64 columns.
+// fc2 epilogue: bf16 rows through the wave's 2 KiB staging area, one 32 x 32 output block at a time
+// (transposed accumulator blocks: a lane holds one row and four runs of four adjacent columns, each
+// written as one 8-byte LDS store; rows of 64 bytes with 16-byte chunks XOR-swizzled by row / 4),
+// read back as 16-byte row chunks and stored 16 bytes per lane.
 __device__ __forceinline__ void store_y(const f32x16_t (&acc)[kTM][kTN], uint16_t* __restrict__ C,
                                         const MTile& tile, int n0, int N_out, uint32_t stage, int wm,
                                         int wn, int lane, bool through)
 {
+    const int lrow = lane & 31, lh = lane >> 5;
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
+        for (int j = 0; j < kTN; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int cp = 0; cp < 2; ++cp) {
-                __builtin_amdgcn_sched_barrier(0);
+            for (int g = 0; g < 4; ++g) {
+                const int c = g;                                    // 16-byte chunk of columns 8g .. 8g + 7
+                const uint32_t a = stage + lrow * 64 + (((c ^ (lrow >> 2)) & 3) << 4) + 8 * lh;
+                *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(a) =
+                    u32x2_t{pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
+                            pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3])};
+            }
+            const int chunk = lane & 3;
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-                    for (int rr = 0; rr < 8; ++rr) {
-                        const int r = 8 * half + rr;
-                        const int row = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);   // 0..15
-                        const int col = 32 * jj + (lane & 31);
-                        const uint32_t a = stage + row * 128 + ((((col >> 3) ^ row) & 7) << 4) + 2 * (col & 7);
-                        *reinterpret_cast<__attribute__((address_space(3))) uint16_t*>(a) =
-                            f32_to_bf16(acc[i][2 * cp + jj][r]);
-                    }
-                const int chunk = lane & 7;
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    const int row = (lane >> 3) + 8 * m;
-                    const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
-                        stage + row * 128 + (((chunk ^ row) & 7) << 4));
-                    const int brow = 16 * half + row;          // row inside the 32-row block
-                    const int grow = tile.row_begin + row_block<kWM>(i, wm) + brow;
-                    if (grow < tile.row_end) {
-                        uint16_t* dst = C + static_cast<int64_t>(grow) * N_out + n0 + 128 * wn + 64 * cp + 8 * chunk;
-                        if (through)
-                            store16_through(dst, v);
-                        else
-                            *reinterpret_cast<u32x4_t*>(dst) = v;
-                    }
+            for (int m = 0; m < 2; ++m) {
+                const int row = (lane >> 2) + 16 * m;
+                const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
+                    stage + row * 64 + (((chunk ^ (row >> 2)) & 3) << 4));
+                const int grow = tile.row_begin + row_block<kWM>(i, wm) + row;
+                if (grow < tile.row_end) {
+                    uint16_t* dst = C + static_cast<int64_t>(grow) * N_out + n0 + 128 * wn + 32 * j + 8 * chunk;
+                    if (through)
+                        store16_through(dst, v);
+                    else
+                        *reinterpret_cast<u32x4_t*>(dst) = v;
                 }
             }
+        }
 }
 
-// fc1 epilogue: SwiGLU in fp32 into the staging area, 16 rows x 32 columns at a time (16-byte
-// chunks XOR-swizzled by row).  Four lanes share a row's 32-column block: each takes 8 values, the
-// block's largest magnitude is combined across the four, and each lane encodes its 8 values (OCP-MX,
-// e4m3_encode4_scaled) and stores 8 code bytes; the first of the four stores the scale byte.
-__device__ __forceinline__ uint32_t h_stage_off(int row, int col)
-{
-    return row * 128 + 16 * (((col >> 2) ^ row) & 7) + 4 * (col & 3);
-}
-
+// fc1 epilogue, in registers (transposed accumulator blocks): for output block ob of row block i a
+// lane holds 16 of the 32 values of one row's MX block (runs of four columns 8 g + 4 (lane / 32) ..
+// + 3), lane l + 32 the other 16.  The block's largest magnitude comes from the lane's 16 and one
+// exchange with lane l ^ 32; each lane encodes its 16 values (OCP-MX, e4m3_encode4_scaled) into
+// four words, the two halves swap two words so that each holds 16 consecutive code bytes (lane l
+// columns 0 .. 15, lane l + 32 columns 16 .. 31), and lane l stores the scale byte.
+//
 // kSwiGLU: the value of output (row, column) is swiglu(gate accumulator, up accumulator) (the GEMM);
 // otherwise the gate accumulator itself (the encoder probe, which loads caller values there).
 template <bool kSwiGLU>
 __device__ __forceinline__ void store_h(const f32x16_t (&acc)[kTM][kTN], uint8_t* __restrict__ Cq,
                                         uint8_t* __restrict__ Cq_sc, const MTile& tile, int n0,
-                                        int N_out, uint32_t stage, int wm, int wn, int lane)
+                                        int N_out, int wm, int wn, int lane)
 {
-    const int erow = lane >> 2;                   // row of the piece this lane encodes
-    const int eq = lane & 3;                      // its quarter of the 32 columns
+    const int lrow = lane & 31, lh = lane >> 5;
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
+        for (int ob = 0; ob < 2; ++ob) {          // output block: gate block 2 ob, up block 2 ob + 1
+            __builtin_amdgcn_sched_barrier(0);
+            float v[16];
+            uint32_t amax = 0;
 #pragma unroll
-            for (int ob = 0; ob < 2; ++ob) {      // output block: gate block 2 ob, up block 2 ob + 1
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int rr = 0; rr < 8; ++rr) {
-                    const int r = 8 * half + rr;
-                    const int row = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
-                    *reinterpret_cast<__attribute__((address_space(3))) float*>(
-                        stage + h_stage_off(row, lane & 31)) =
-                        kSwiGLU ? swiglu(acc[i][2 * ob][r], acc[i][2 * ob + 1][r]) : acc[i][2 * ob][r];
-                }
-                const f32x4_t x0 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(
-                    stage + h_stage_off(erow, 8 * eq));
-                const f32x4_t x1 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(
-                    stage + h_stage_off(erow, 8 * eq + 4));
-                uint32_t amax = 0;
-#pragma unroll
-                for (int z = 0; z < 4; ++z)
-                    amax = max(amax, max(__float_as_uint(x0[z]) & 0x7fffffffu, __float_as_uint(x1[z]) & 0x7fffffffu));
-                amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 1)));
-                amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 2)));
-                const int e = mx_shared_exponent(amax);
-                const uint32_t lo = e4m3_encode4_scaled(x0[0], x0[1], x0[2], x0[3], e);
-                const uint32_t hi = e4m3_encode4_scaled(x1[0], x1[1], x1[2], x1[3], e);
-                const int grow = tile.row_begin + row_block<kWM>(i, wm) + 16 * half + erow;
-                const int hcol = n0 + 64 * wn + 32 * ob;
-                if (grow < tile.row_end) {
-                    *reinterpret_cast<u32x2_t*>(Cq + static_cast<int64_t>(grow) * N_out + hcol + 8 * eq) =
-                        u32x2_t{lo, hi};
-                    if (eq == 0)
-                        Cq_sc[static_cast<int64_t>(grow) * (N_out / 32) + hcol / 32] = static_cast<uint8_t>(e + 127);
-                }
+            for (int r = 0; r < 16; ++r) {
+                v[r] = kSwiGLU ? swiglu(acc[i][2 * ob][r], acc[i][2 * ob + 1][r]) : acc[i][2 * ob][r];
+                amax = max(amax, __float_as_uint(v[r]) & 0x7fffffffu);
             }
+            amax = max(amax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), 32)));
+            const int e = mx_shared_exponent(amax);
+            uint32_t w[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                w[g] = e4m3_encode4_scaled(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3], e);
+            // lane l keeps words 0, 1 (columns 0-3, 8-11) and takes lane l + 32's (4-7, 12-15);
+            // lane l + 32 keeps words 2, 3 (20-23, 28-31) and takes lane l's (16-19, 24-27)
+            const uint32_t x = static_cast<uint32_t>(__shfl_xor(static_cast<int>(lh ? w[0] : w[2]), 32));
+            const uint32_t y = static_cast<uint32_t>(__shfl_xor(static_cast<int>(lh ? w[1] : w[3]), 32));
+            const u32x4_t out = lh ? u32x4_t{x, w[2], y, w[3]} : u32x4_t{w[0], x, w[1], y};
+            const int grow = tile.row_begin + row_block<kWM>(i, wm) + lrow;
+            const int hcol = n0 + 64 * wn + 32 * ob;
+            if (grow < tile.row_end) {
+                *reinterpret_cast<u32x4_t*>(Cq + static_cast<int64_t>(grow) * N_out + hcol + 16 * lh) = out;
+                if (lh == 0)
+                    Cq_sc[static_cast<int64_t>(grow) * (N_out / 32) + hcol / 32] = static_cast<uint8_t>(e + 127);
+            }
+        }
 }
 
 template <bool kGated>
@@ -1183,7 +1175,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
         MOE_PROBE(pr_u = __builtin_readcyclecounter(); pr[kProbeSetup] += pr_u - pr_s;)
         const uint32_t stg = lds0 + kOutBase + wave * kOutWaveBytes;
         if constexpr (kGated)
-            store_h<true>(acc, Cq, Cq_sc, done, done_n0, N_out, stg, wm, wn, lane);
+            store_h<true>(acc, Cq, Cq_sc, done, done_n0, N_out, wm, wn, lane);
         else
             store_y(acc, Cy, done, done_n0, N_out, stg, wm, wn, lane, chunk_done != nullptr);
         if (chunk_done != nullptr)
@@ -1208,15 +1200,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mx_dma(
 
 // The fc1 epilogue's encoder on caller values: workgroup (x, y) takes output columns [128 x, 128 x +
 // 128) and rows [256 y, 256 y + 256) of v [rows, cols], puts each value in the gate accumulator
-// register that holds that output in the GEMM (32 x 32 block layout: lane column lane % 32, rows
-// 8 (r / 4) + 4 (lane / 32) + r % 4), and runs store_h on them without the SwiGLU.
+// register that holds that output in the GEMM (transposed 32 x 32 blocks: lane row lane % 32,
+// columns 8 (r / 4) + 4 (lane / 32) + r % 4), and runs store_h on them without the SwiGLU.
 __global__ __launch_bounds__(kThreads, 1) void mx_epilogue_probe(const float* __restrict__ v, int rows,
                                                                  int cols, uint8_t* __restrict__ codes,
                                                                  uint8_t* __restrict__ scales)
 {
-    __shared__ __attribute__((aligned(256))) unsigned char stg[kWaves * kOutWaveBytes];
-    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-        (__attribute__((address_space(3))) unsigned char*)(stg)));
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / kWN, wn = wave % kWN;
@@ -1238,11 +1227,11 @@ __global__ __launch_bounds__(kThreads, 1) void mx_epilogue_probe(const float* __
         for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = tile.row_begin + row_block<kWM>(i, wm) + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const int col = n0 + 64 * wn + 32 * ob + (lane & 31);
+                const int row = tile.row_begin + row_block<kWM>(i, wm) + (lane & 31);
+                const int col = n0 + 64 * wn + 32 * ob + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 acc[i][2 * ob][r] = row < tile.row_end ? v[static_cast<int64_t>(row) * cols + col] : 0.0f;
             }
-    store_h<false>(acc, codes, scales, tile, n0, cols, lds0 + wave * kOutWaveBytes, wm, wn, lane);
+    store_h<false>(acc, codes, scales, tile, n0, cols, wm, wn, lane);
 }
 
 }  // namespace big
