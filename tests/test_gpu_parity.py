@@ -136,6 +136,33 @@ def test_unpermute_weighted_sum_matches_definition():
     assert oracle.inf_norm_rel(out, ref) < 1e-6
 
 
+@pytest.mark.parametrize("k,H", [(8, 4096), (12, 2176)])
+def test_unpermute_bf16_many_slots_matches_definition(k, H):
+    """bfloat16 unpermute with k >= 8 slots per token (one workgroup per row; k = 12 takes two
+    batches of loads, H = 2176 gives rows of 272 vectors, more than one per lane for some lanes),
+    some slots dropped (pos = -1): within one bfloat16 rounding of the fp64 weighted sum."""
+    rng = np.random.default_rng(12)
+    T = 97
+    y_bits = synth.to_bf16_bits(rng.standard_normal((T * k, H)).astype(np.float32))
+    perm = rng.permutation(T * k).astype(np.int32)
+    pos = np.empty_like(perm)
+    pos[perm] = np.arange(T * k, dtype=np.int32)
+    pos[rng.random(T * k) < 0.1] = -1
+    probs = rng.random((T, k)).astype(np.float32)
+    out = dv.host(mel.unpermute(dv.tensor(y_bits), dv.tensor(pos), dv.tensor(probs)))
+    y = synth.bf16_bits_to_f32(y_bits).astype(np.float64)
+    ref = np.zeros((T, H))
+    mag = np.zeros((T, H))                      # sum of |terms|: bounds the fp32 accumulation error
+    pk = pos.reshape(T, k)
+    for j in range(k):
+        ok = pk[:, j] >= 0
+        term = probs[ok, j:j + 1].astype(np.float64) * y[pk[ok, j]]
+        ref[ok] += term
+        mag[ok] += np.abs(term)
+    # one bfloat16 rounding of the output (2^-9 relative) plus k fp32 roundings of the running sum
+    assert (np.abs(out - ref) <= 2.0 ** -8 * np.abs(ref) + 2.0 ** -18 * mag).all()
+
+
 # ------------------------------------------------------------------------------------------ whole layer
 
 CASES = [
