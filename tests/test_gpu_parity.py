@@ -87,9 +87,12 @@ def test_route_out_of_range_ids_flagged_and_dropped():
 
 # ------------------------------------------------------------------------------------------ permute / unpermute
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "mxfp8"])
-def test_permute_bit_exact(dtype):
-    inp = synth.make_layer(T=300, H=256, F=128, E=7, k=3, dtype=dtype)
+@pytest.mark.parametrize("dtype,H", [("f32", 256), ("bf16", 256), ("mxfp8", 256),
+                                     ("bf16", 384), ("mxfp8", 7168), ("bf16", 8192)])
+def test_permute_bit_exact(dtype, H):
+    """Row widths whose 16-byte vectors divide a workgroup's 1024 (four per thread: 256, 8192) and
+    ones that do not (one per thread: bf16 384 = 48 vectors, MX 7168 = 448), with a ragged end."""
+    inp = synth.make_layer(T=300, H=H, F=128, E=7, k=3, dtype=dtype)
     _, _, perm, pos = oracle.route(inp.expert_ids, 7)
     d = dv.layer(inp)
     pos_d = dv.tensor(pos)
