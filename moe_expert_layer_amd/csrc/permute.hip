@@ -10,6 +10,8 @@
 // thread, so a launch keeps as many independent loads in flight as the machine can hold; rows are
 // contiguous in the thread index, so every access is coalesced.  Grid-stride versions cover sizes
 // whose pair count does not fit 32 bits.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -171,6 +173,62 @@ __global__ __launch_bounds__(kThreads) void unpermute_bf16_row_kernel(
     }
 }
 
+// Grid-stride over output rows, one workgroup per row at a time: the row's k slot indices and weights
+// are scalar loads; each lane takes kCols 16-byte columns c, c + kThreads, ... and issues their loads
+// (at most 4 slots per batch) before using any, then sums them in j order.
+template <int kCols>
+__global__ __launch_bounds__(kThreads) void unpermute_bf16_rows_gs_kernel(
+    const uint4* __restrict__ y, const int32_t* __restrict__ pos, const float* __restrict__ probs,
+    uint4* __restrict__ out, int64_t T, int k, int64_t M, int row_vecs)
+{
+    for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+        const int32_t* tp = pos + t * k;
+        const float* pp = probs + t * k;
+        for (int c0 = threadIdx.x; c0 < row_vecs; c0 += kThreads * kCols) {
+            float acc[kCols][8];
+#pragma unroll
+            for (int q = 0; q < kCols; ++q)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[q][e] = 0.0f;
+            for (int j0 = 0; j0 < k; j0 += 4) {
+                uint4 v[4][kCols];
+                float w[4];
+                bool ok[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t p = j0 + j < k ? tp[j0 + j] : -1;
+                    ok[j] = p >= 0 && p < M;
+                    w[j] = ok[j] ? pp[j0 + j] : 0.0f;
+#pragma unroll
+                    for (int q = 0; q < kCols; ++q) {
+                        const int c = c0 + q * kThreads;
+                        v[j][q] = ok[j] && c < row_vecs ? nt_load(y + p * row_vecs + c) : make_uint4(0, 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (ok[j])
+#pragma unroll
+                        for (int q = 0; q < kCols; ++q)
+                            fma_bf16x8(acc[q], w[j], v[j][q]);
+            }
+#pragma unroll
+            for (int q = 0; q < kCols; ++q) {
+                const int c = c0 + q * kThreads;
+                if (c < row_vecs) {
+                    uint4 o;
+                    o.x = pack_bf16x2(acc[q][0], acc[q][1]);
+                    o.y = pack_bf16x2(acc[q][2], acc[q][3]);
+                    o.z = pack_bf16x2(acc[q][4], acc[q][5]);
+                    o.w = pack_bf16x2(acc[q][6], acc[q][7]);
+                    out[t * row_vecs + c] = o;
+                }
+            }
+        }
+    }
+}
+
 // bfloat16 rows: 8 values per 16-byte vector.
 __global__ __launch_bounds__(kThreads) void unpermute_bf16_kernel(
     const uint4* __restrict__ y, const int32_t* __restrict__ pos, const float* __restrict__ probs,
@@ -287,9 +345,16 @@ hipError_t launch_unpermute(int dtype, const void* y_perm, const int32_t* pos, c
     if (dtype != 0 && T * (H / 8) < (int64_t{1} << 31)) {
         const uint32_t total = static_cast<uint32_t>(T * (H / 8));
         // k >= 8: one workgroup per row, the k slot indices and weights read once per workgroup
-        // (fine-grained k = 8: 68% -> 71% of HBM bandwidth); for k = 2 and 4 the flat kernel is as
-        // fast or faster (Mixtral-shaped 64% either way, MX-shaped 73% against 67%)
-        if (k >= 8 && T <= 0x7fffffff)
+        // (fine-grained k = 8: 68% -> 71% of HBM bandwidth); k <= 2: the same over a grid-stride
+        // loop of 4 workgroups per CU, two columns per lane (Mixtral-shaped 64% -> 65%, 25 -> 23 us
+        // inside the layer); k = 4: the flat kernel (MX-shaped 73% against 67% for either)
+        if (k <= 2 && T <= 0x7fffffff)
+            unpermute_bf16_rows_gs_kernel<2><<<dim3(static_cast<unsigned>(
+                                                    std::min<int64_t>(T, int64_t{device_info().cu_count} * 4))),
+                                                block, 0, s>>>(
+                static_cast<const uint4*>(y_perm), pos, probs, static_cast<uint4*>(out), T,
+                static_cast<int>(k), M, static_cast<int>(H / 8));
+        else if (k >= 8 && T <= 0x7fffffff)
             unpermute_bf16_row_kernel<<<dim3(static_cast<unsigned>(T)), block, 0, s>>>(
                 static_cast<const uint4*>(y_perm), pos, probs, static_cast<uint4*>(out),
                 static_cast<int>(k), M, static_cast<int>(H / 8));
